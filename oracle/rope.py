@@ -1,0 +1,36 @@
+"""Rotary position encoding in float64 (test infrastructure only).
+
+The LazyAttention summary names RoPE as the positional encoding that is
+deferred into the attention kernel ("Core Concept: Deferred Positional
+Encoding") and relies on RoPE attention depending only on the relative offset
+n - m ("Mathematical Equivalence"). The pages do not fix the RoPE variant; this
+oracle takes the rotate-half form used by Llama-family models (the models the
+summary's "Experimental Results" evaluate): dimension k is paired with k + D/2,
+the pair is rotated by the angle n * theta_k, theta_k = base ** (-2k / D).
+Equivalently, z_k = x_k + i x_{k+D/2} is multiplied by exp(i n theta_k).
+"""
+import numpy as np
+
+
+def inv_freq(D: int, base: float) -> np.ndarray:
+    """theta_k = base^(-2k/D) for k = 0 .. D/2-1, float64."""
+    if D % 2:
+        raise ValueError("head dim must be even")
+    k = np.arange(D // 2, dtype=np.float64)
+    return np.power(np.float64(base), -2.0 * k / D)
+
+
+def rotate(x: np.ndarray, pos, base: float) -> np.ndarray:
+    """Apply R(pos) to the last axis of x (float64).
+
+    x: [..., D]; pos: integer array broadcastable to x.shape[:-1].
+    y_k        = x_k cos(pos theta_k) - x_{k+D/2} sin(pos theta_k)
+    y_{k+D/2}  = x_k sin(pos theta_k) + x_{k+D/2} cos(pos theta_k)
+    """
+    x = np.asarray(x, dtype=np.float64)
+    D = x.shape[-1]
+    h = D // 2
+    ang = np.asarray(pos, dtype=np.float64)[..., None] * inv_freq(D, base)
+    c, s = np.cos(ang), np.sin(ang)
+    a, b = x[..., :h], x[..., h:]
+    return np.concatenate([a * c - b * s, a * s + b * c], axis=-1)

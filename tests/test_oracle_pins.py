@@ -1,0 +1,255 @@
+"""Pins of the float64 oracle to things other than itself (CPU only).
+
+Each test targets a plausible mistake: a wrong frequency exponent, a swapped
+pair convention or sign, a dropped scale, a wrong GQA head map, a mask on table
+order instead of logical position, a materialisation that depends on block ids,
+or a packing error.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import rope, meta, overhead
+from tests.brute import brute_attention, rope_matrix
+from tests.util import small, oracle_out, dense_request, rel
+from workload import Segment, RequestLayout, build
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------- RoPE
+
+def test_inv_freq_closed_form():
+    assert np.allclose(rope.inv_freq(4, 10000.0), [1.0, 0.01], rtol=0, atol=1e-15)
+    assert np.allclose(rope.inv_freq(8, 100.0),
+                       [1.0, 0.31622776601683794, 0.1, 0.031622776601683794], rtol=1e-15)
+
+
+def test_rotate_two_dims_is_plane_rotation():
+    # D = 2: theta_0 = 1 rad per position, (1, 0) rotated by n = 1
+    y = rope.rotate(np.array([1.0, 0.0]), 1, 10000.0)
+    assert abs(y[0] - 0.5403023058681398) < 1e-15 and abs(y[1] - 0.8414709848078965) < 1e-15
+
+
+def test_rotate_matches_complex_form():
+    rng = np.random.default_rng(0)
+    D, base = 16, 10000.0
+    x = rng.standard_normal((5, D))
+    pos = np.array([0, 1, 17, 4096, 35001])
+    z = x[:, : D // 2] + 1j * x[:, D // 2:]
+    th = base ** (-np.arange(D // 2) * 2.0 / D)
+    zr = z * np.exp(1j * pos[:, None] * th[None, :])
+    want = np.concatenate([zr.real, zr.imag], axis=1)
+    got = rope.rotate(x, pos, base)
+    assert np.max(np.abs(got - want)) < 1e-11
+
+
+def test_rotate_matches_explicit_matrix():
+    rng = np.random.default_rng(1)
+    for D in (8, 64, 128):
+        x = rng.standard_normal(D)
+        for n in (0, 3, 511, 20000):
+            assert np.max(np.abs(rope.rotate(x, n, 10000.0) - rope_matrix(n, D, 10000.0) @ x)) < 1e-11
+
+
+def test_rotation_group_identities():
+    rng = np.random.default_rng(2)
+    D, base = 128, 10000.0
+    x = rng.standard_normal(D)
+    assert np.array_equal(rope.rotate(x, 0, base), x)
+    for a, b in [(3, 5), (1000, -77), (123456, 654321)]:
+        lhs = rope.rotate(rope.rotate(x, b, base), a, base)
+        assert np.max(np.abs(lhs - rope.rotate(x, a + b, base))) < 1e-8
+        assert abs(np.linalg.norm(rope.rotate(x, a, base)) - np.linalg.norm(x)) < 1e-12
+
+
+def test_relative_position_identity():
+    """<R(a) q, R(b) k> = <R(a - b) q, k> (the relative-offset property)."""
+    rng = np.random.default_rng(3)
+    D, base = 128, 10000.0
+    for _ in range(50):
+        q, k = rng.standard_normal(D), rng.standard_normal(D)
+        a, b = rng.integers(-10**6, 10**6, size=2)
+        lhs = rope.rotate(q, a, base) @ rope.rotate(k, b, base)
+        rhs = rope.rotate(q, a - b, base) @ k
+        assert abs(lhs - rhs) < 1e-8 * max(1.0, abs(rhs))
+
+
+# ---------------------------------------------------------------- attention
+
+@pytest.mark.parametrize("Hq,Hkv,D", [(4, 2, 16), (4, 1, 8), (2, 2, 16), (8, 1, 8)])
+def test_oracle_equals_brute_force(Hq, Hkv, D):
+    wl = small(Hq=Hq, Hkv=Hkv, D=D, seed=11 + Hq + D)
+    got = oracle_out(wl)
+    want = brute_attention(wl)
+    assert np.all(np.isfinite(got))
+    assert np.max(np.abs(got - want)) < 1e-12
+
+
+def test_brute_force_with_gaps_overlap_and_partial_block():
+    # overlapping documents, a gap, an unaligned start, 5-token partial tail,
+    # and a query set spanning all of them
+    segs = [Segment("doc", 3, doc=1), Segment("doc", 20, doc=0),
+            Segment("doc", 100, doc=1), Segment("private", 140, tokens=21)]
+    wl = small(segs=segs, q_len=21, seed=5, q_scale=4.0)
+    assert np.max(np.abs(oracle_out(wl) - brute_attention(wl))) < 1e-12
+
+
+def test_sdpa_special_case_dense_from_zero():
+    """Dense layout from position 0 equals torch SDPA (causal) over eagerly rotated q, k."""
+    torch = pytest.importorskip("torch")
+    Hq, Hkv, D, n = 8, 2, 32, 45
+    wl = build("dense", Hq, Hkv, D, 16, 10000.0, 1, 16, [dense_request(n)], seed=9)
+    got = oracle_out(wl)
+    q = oracle.bf16_bits_to_f64(wl.q_bits)                       # [n, Hq, D]
+    ids = wl.compact_ids(0)
+    k = np.concatenate([oracle.bf16_bits_to_f64(wl.k_bits[i]) for i in ids], axis=1)[:, :n]
+    v = np.concatenate([oracle.bf16_bits_to_f64(wl.v_bits[i]) for i in ids], axis=1)[:, :n]
+    th = 10000.0 ** (-np.arange(D // 2) * 2.0 / D)
+    pos = np.arange(n)
+
+    def crot(x):  # complex-form RoPE over the token axis (second to last)
+        z = x[..., : D // 2] + 1j * x[..., D // 2:]
+        z = z * np.exp(1j * pos[:, None] * th[None, :])
+        return np.concatenate([z.real, z.imag], axis=-1)
+    qt = torch.from_numpy(crot(q.transpose(1, 0, 2)))             # [Hq, n, D]
+    kt = torch.from_numpy(crot(k)).repeat_interleave(Hq // Hkv, dim=0)
+    vt = torch.from_numpy(v).repeat_interleave(Hq // Hkv, dim=0)
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True)
+    ref = ref.numpy().transpose(1, 0, 2)
+    assert np.max(np.abs(got - ref)) < 1e-12
+
+
+def test_single_visible_key_returns_its_value():
+    segs = [Segment("private", 10, tokens=16)]
+    wl = small(segs=segs, q_len=1, q_pos=np.array([10]))
+    out = oracle_out(wl)
+    blk = wl.compact_ids(0)[0]
+    v0 = oracle.bf16_bits_to_f64(wl.v_bits[blk, :, 0, :])           # [Hkv, D]
+    G = wl.Hq // wl.Hkv
+    for h in range(wl.Hq):
+        assert np.array_equal(out[0, h], v0[h // G])
+
+
+def test_zero_keys_give_mean_of_visible_values():
+    wl = small(seed=13)
+    wl.k_bits[:] = 0                                                # all scores 0
+    out = oracle_out(wl)
+    G = wl.Hq // wl.Hkv
+    for r in range(wl.total_q):
+        p = wl.q_pos[r]
+        vals, pos = [], []
+        for t, (bid, off) in enumerate(zip(wl.compact_ids(0), wl.seq_offsets[0])):
+            n_t = 16 if t < len(wl.seq_offsets[0]) - 1 else wl.kv_lens[0] - 16 * t
+            for j in range(n_t):
+                if off + j <= p:
+                    vals.append(oracle.bf16_bits_to_f64(wl.v_bits[bid, :, j, :]))
+        mean = np.mean(vals, axis=0)
+        for h in range(wl.Hq):
+            assert np.max(np.abs(out[r, h] - mean[h // G])) < 1e-13
+
+
+def test_no_visible_key_outputs_zero():
+    segs = [Segment("doc", 50, doc=0), Segment("private", 90, tokens=3)]
+    wl = small(segs=segs, q_len=2, q_pos=np.array([0, 49]))
+    assert np.array_equal(oracle_out(wl), np.zeros_like(oracle_out(wl)))
+
+
+def test_reuse_equals_copies():
+    """One physical block at two offsets == two physical copies (each used once)."""
+    lay_reuse = RequestLayout([Segment("doc", 0, doc=0), Segment("doc", 77, doc=0),
+                               Segment("private", 140, tokens=9)], 9)
+    wl = build("reuse", 4, 2, 16, 16, 10000.0, 2, 32, [lay_reuse], seed=21)
+    out_reuse = oracle_out(wl)
+    # copy: second placement reads doc 1, made an exact copy of doc 0
+    lay_copy = RequestLayout([Segment("doc", 0, doc=0), Segment("doc", 77, doc=1),
+                              Segment("private", 140, tokens=9)], 9)
+    wc = build("copy", 4, 2, 16, 16, 10000.0, 2, 32, [lay_copy], seed=21)
+    ids0 = wc.compact_ids(0)
+    wc.k_bits[ids0[2:4]] = wc.k_bits[ids0[0:2]]
+    wc.v_bits[ids0[2:4]] = wc.v_bits[ids0[0:2]]
+    assert np.array_equal(oracle_out(wc), out_reuse)
+    assert np.max(np.abs(brute_attention(wc) - out_reuse)) < 1e-12
+
+
+def test_translation_invariance():
+    wl = small(seed=31, q_scale=4.0)
+    base_out = oracle_out(wl)
+    for c in (1, 12345, 100000):
+        wl2 = small(seed=31, q_scale=4.0)
+        wl2.seq_offsets = [o + c for o in wl2.seq_offsets]
+        wl2.q_pos = wl2.q_pos + c
+        assert np.max(np.abs(oracle_out(wl2) - base_out)) < 1e-9
+
+
+def test_block_table_permutation_invariance():
+    segs = [Segment("doc", 0, doc=0), Segment("doc", 64, doc=1), Segment("doc", 96, doc=2),
+            Segment("private", 128, tokens=32)]
+    wl = small(segs=segs, q_len=32, seed=41)
+    out = oracle_out(wl)
+    perm = np.array([5, 0, 3, 1, 4, 2, 7, 6])      # all entries are full blocks
+    wl.seq_block_ids = [wl.seq_block_ids[0][perm]]
+    wl.seq_offsets = [wl.seq_offsets[0][perm]]
+    assert np.max(np.abs(oracle_out(wl) - out)) < 1e-12
+
+
+def test_position_matters():
+    """Negative control: moving one document changes the output."""
+    wl = small(seed=51, q_scale=4.0)
+    out = oracle_out(wl)
+    wl.seq_offsets = [wl.seq_offsets[0] + np.array([1, 1, 0, 0, 0, 0])]
+    assert np.max(np.abs(oracle_out(wl) - out)) > 1e-3
+
+
+# ---------------------------------------------------------------- packed words
+
+def _golden_words():
+    with open(os.path.join(GOLDEN, "packed_words.json")) as f:
+        return json.load(f)
+
+
+def test_packed_word_golden_bits():
+    g = _golden_words()
+    for c in g["cases"]:
+        t = c["t"]
+        ids = [0] * t + [c["block_id"]]
+        offs = [16 * i for i in range(t)] + [c["offset"]]
+        bt = np.array([0, t + 1])
+        w = meta.encode_meta(ids, offs, bt, g["B"])
+        assert int(w[-1]) == int(c["word"], 16), c
+        dids, doffs = meta.decode_meta(w, bt, g["B"])
+        assert int(dids[-1]) == c["block_id"] and int(doffs[-1]) == c["offset"]
+
+
+def test_packed_word_roundtrip_and_range():
+    rng = np.random.default_rng(4)
+    bt = np.array([0, 300, 301, 1000])
+    t = np.concatenate([np.arange(300), [0], np.arange(699)])
+    ids = rng.integers(0, 1 << 17, size=1000)
+    offs = t * 16 + rng.integers(-16384, 16384, size=1000)
+    w = meta.encode_meta(ids, offs, bt, 16)
+    di, do = meta.decode_meta(w, bt, 16)
+    assert np.array_equal(di, ids) and np.array_equal(do, offs)
+    with pytest.raises(ValueError):
+        meta.encode_meta([1 << 17], [0], [0, 1], 16)
+    with pytest.raises(ValueError):
+        meta.encode_meta([0], [16384], [0, 1], 16)
+    with pytest.raises(ValueError):
+        meta.encode_meta([0], [-16385], [0, 1], 16)
+
+
+# ---------------------------------------------------------------- overhead
+
+def test_rotation_overhead_printed_value():
+    with open(os.path.join(GOLDEN, "rotation_overhead.json")) as f:
+        g = json.load(f)
+    pct = 100.0 * overhead.rotation_overhead(g["M"])
+    assert round(pct, g["printed_digits"]) == g["overhead_percent_printed"]
+    assert abs(overhead.rotation_overhead(g["M"]) - 3.0 / (4 * g["M"])) < 1e-15
+    # rotating twice (reset to zero, then to the target) would not match the printed figure
+    twice = 100.0 * overhead.rotation_overhead(g["M"], rotations_per_key=2)
+    assert round(twice, 2) != g["overhead_percent_printed"]

@@ -1,0 +1,41 @@
+"""Small-workload builders shared by CPU and GPU tests (no attention arithmetic)."""
+import numpy as np
+
+from workload import RequestLayout, Segment, build
+
+
+def oracle_out(wl, rows=None, seq=None):
+    import oracle
+    if rows is None:
+        return oracle.lazy_attention(wl.q_bits, wl.k_bits, wl.v_bits,
+                                     [wl.compact_ids(s) for s in range(wl.num_seqs)],
+                                     wl.seq_offsets, wl.kv_lens, wl.q_indptr, wl.q_pos,
+                                     wl.rope_base, wl.B)
+    return oracle.attention_rows(wl.q_bits, wl.k_bits, wl.v_bits,
+                                 [wl.compact_ids(s) if s == seq else None
+                                  for s in range(wl.num_seqs)],
+                                 wl.seq_offsets, wl.kv_lens, wl.q_indptr, wl.q_pos,
+                                 wl.rope_base, wl.B, seq, rows)
+
+
+def small(Hq=4, Hkv=2, D=16, B=16, base=10000.0, seed=7, segs=None, q_len=None,
+          q_pos=None, n_docs=3, doc_tokens=32, q_scale=1.0, requests=None):
+    """One or more requests from explicit segment lists (default: 2 docs + 20 new tokens)."""
+    if requests is None:
+        if segs is None:
+            segs = [Segment("doc", 5, doc=0), Segment("doc", 40, doc=2),
+                    Segment("private", 72, tokens=20)]
+        last = segs[-1]
+        ntok = last.tokens if last.kind == "private" else doc_tokens
+        requests = [RequestLayout(segs, q_len if q_len is not None else ntok, q_pos)]
+    return build("small", Hq, Hkv, D, B, base, n_docs, doc_tokens, requests, seed,
+                 q_scale=q_scale)
+
+
+def dense_request(n_tokens, start=0):
+    """A request whose tokens are all new and all queried, positions start..start+n-1."""
+    return RequestLayout([Segment("private", start, tokens=n_tokens)], n_tokens)
+
+
+def rel(a, b):
+    return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300))
