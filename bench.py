@@ -1,0 +1,227 @@
+#!/usr/bin/env python3
+"""Benchmark of the LazyAttention hot path on one MI355X.
+
+Workload: the mixed continuous batch "mixed-64q8kv-4p96d" (64 q / 8 KV heads, head dim
+128, bf16, block size 16, one 2000-document position-free pool): 4 prefill requests
+(16 Zipf(1.1) documents x 1024 tokens + 512-token suffix prefilled causally) and 96 decode
+requests (12 documents x 1024 tokens + 1 token). One step = the prefill half through
+lazyattn_prefill plus the decode half through lazyattn_decode, on the current HIP stream,
+each call bracketed by HIP events. Inputs are resident in HBM before timing.
+
+Reported (one JSON line): prefill attention TFLOP/s (algorithmic: 4*D FLOP per visible
+(query, key, q-head) pair) as `value`, decode attention GB/s (algorithmic: K+V bytes of
+every (sequence, key) plus q, out and 4 B per block entry) in `decode`, the roofline of
+the dominant kernel, and the float64 oracle timed on a bounded sample on the host cores.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "prefill attn TFLOP/s (% MFMA peak) + decode attn HBM GB/s, Zipf RAG batch"
+WORKLOAD = "mixed-64q8kv-4p96d"
+PEAK_MFMA_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+
+def visible_pairs(wl, seqs):
+    """Sum over query rows of the number of keys at logical position <= the row's."""
+    total = 0
+    for s in seqs:
+        T = len(wl.seq_offsets[s])
+        kv = int(wl.kv_lens[s])
+        pos = np.concatenate([wl.seq_offsets[s][t] + np.arange(16 if t < T - 1 else kv - 16 * t)
+                              for t in range(T)])
+        pos.sort()
+        qp = wl.q_pos[wl.q_indptr[s]: wl.q_indptr[s + 1]]
+        total += int(np.searchsorted(pos, qp, side="right").sum())
+    return total
+
+
+def prefill_flops(wl, seqs):
+    return 4.0 * wl.D * wl.Hq * visible_pairs(wl, seqs)
+
+
+def decode_bytes(wl, seqs):
+    kv = sum(int(wl.kv_lens[s]) for s in seqs) * 2 * wl.Hkv * wl.D * 2
+    rows = sum(int(wl.q_indptr[s + 1] - wl.q_indptr[s]) for s in seqs)
+    entries = sum(len(wl.seq_offsets[s]) for s in seqs)
+    return float(kv + 2 * rows * wl.Hq * wl.D * 2 + 4 * entries)
+
+
+def half_inputs(wl, seqs, dev, pool):
+    """CSR arrays, queries and packed words of a subset of sequences (shares the pool)."""
+    import torch
+    import position_agnostic_kv_paged_amd as L
+    ids = [wl.seq_block_ids[s] for s in seqs]
+    offs = [wl.seq_offsets[s] for s in seqs]
+    bt = np.concatenate([[0], np.cumsum([len(x) for x in ids])]).astype(np.int32)
+    words = L.encode_meta(np.concatenate(ids), np.concatenate(offs), bt)
+    rows = [np.arange(wl.q_indptr[s], wl.q_indptr[s + 1]) for s in seqs]
+    qcnt = [len(r) for r in rows]
+    rows = np.concatenate(rows)
+    q = torch.from_numpy(wl.q_bits[rows].view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def i32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+    return dict(q=q, k_pool=pool["k_pool"], v_pool=pool["v_pool"], block_table=i32(bt),
+                block_meta=torch.from_numpy(words.view(np.int32)).to(dev),
+                kv_lens=i32(wl.kv_lens[seqs]),
+                q_indptr=i32(np.concatenate([[0], np.cumsum(qcnt)])),
+                q_pos=i32(wl.q_pos[rows]), max_entries=max(len(x) for x in ids),
+                out=torch.empty_like(q))
+
+
+def cpu_baseline(wl, pre_seqs, dec_seqs, budget_s=15.0):
+    """The float64 oracle (as it stands) on a bounded sample of the same batch."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas = 1
+    cores = len(os.sched_getaffinity(0))
+    k_bits, v_bits = wl.k_bits, wl.v_bits
+    # prefill sample: 32 query rows of the first prefill request (all 64 heads)
+    s = pre_seqs[0]
+    q0 = int(wl.q_indptr[s])
+    rows = q0 + np.linspace(0, int(wl.q_indptr[s + 1]) - q0 - 1, 32).astype(np.int64)
+    t0 = time.perf_counter()
+    ids = [None] * wl.num_seqs
+    ids[s] = wl.compact_ids(s)
+    oracle.attention_rows(wl.q_bits, k_bits, v_bits, ids, wl.seq_offsets, wl.kv_lens,
+                          wl.q_indptr, wl.q_pos, wl.rope_base, wl.B, s, rows)
+    t_pre = time.perf_counter() - t0
+    qp = wl.q_pos[rows]
+    T = len(wl.seq_offsets[s])
+    kv = int(wl.kv_lens[s])
+    pos = np.sort(np.concatenate([wl.seq_offsets[s][t] + np.arange(16 if t < T - 1 else kv - 16 * t)
+                                  for t in range(T)]))
+    pre_flops = 4.0 * wl.D * wl.Hq * float(np.searchsorted(pos, qp, side="right").sum())
+    # decode sample: whole decode requests until the time budget is used
+    t0 = time.perf_counter()
+    done, dbytes = 0, 0.0
+    for s in dec_seqs:
+        ids = [None] * wl.num_seqs
+        ids[s] = wl.compact_ids(s)
+        oracle.attention_rows(wl.q_bits, k_bits, v_bits, ids, wl.seq_offsets, wl.kv_lens,
+                              wl.q_indptr, wl.q_pos, wl.rope_base, wl.B, s,
+                              np.array([wl.q_indptr[s]]))
+        done += 1
+        dbytes += decode_bytes(wl, [s])
+        if time.perf_counter() - t0 > budget_s:
+            break
+    t_dec = time.perf_counter() - t0
+    return {"value": pre_flops / t_pre / 1e12, "unit": "TFLOP/s", "cores": cores,
+            "blas_threads": blas, "kind": "oracle",
+            "decode": {"value": dbytes / t_dec / 1e9, "unit": "GB/s"},
+            "sample": f"prefill: 32 query rows x 64 heads of one 16896-key prefill request "
+                      f"({t_pre:.1f} s); decode: {done} whole decode requests "
+                      f"({t_dec:.1f} s); float64 numpy, one sequence at a time"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build runs the attention path on a "
+              "single MI355X (no multi-GPU sharding); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import position_agnostic_kv_paged_amd as L
+    from workload import make
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    L.lib()
+    dev = "cuda:0"
+    wl = make(WORKLOAD)
+    qlen = np.diff(wl.q_indptr)
+    pre_seqs = [s for s in range(wl.num_seqs) if qlen[s] > 1]
+    dec_seqs = [s for s in range(wl.num_seqs) if qlen[s] == 1]
+    pool = wl.to_device(dev)
+    pre = half_inputs(wl, pre_seqs, dev, pool)
+    dec = half_inputs(wl, dec_seqs, dev, pool)
+    ws_pre = torch.empty(L.workspace_bytes("prefill", len(pre_seqs), pre["q"].shape[0],
+                                           pre["max_entries"], wl.Hq, wl.Hkv, wl.D),
+                         dtype=torch.uint8, device=dev)
+    ws_dec = torch.empty(L.workspace_bytes("decode", len(dec_seqs), dec["q"].shape[0],
+                                           dec["max_entries"], wl.Hq, wl.Hkv, wl.D),
+                         dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def call(fn, a, ws):
+        fn(a["q"], a["k_pool"], a["v_pool"], a["block_table"], a["block_meta"], a["kv_lens"],
+           a["q_indptr"], a["q_pos"], wl.rope_base, a["max_entries"], out=a["out"],
+           workspace=ws, stream=stream)
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+          for _ in range(args.steps)]
+
+    def step(e=None):
+        if e: e[0].record(stream)
+        call(L.prefill, pre, ws_pre)
+        if e: e[1].record(stream)
+        call(L.decode, dec, ws_dec)
+        if e: e[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(ev[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_pre = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) / 1e3
+    t_dec = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) / 1e3
+    flops = prefill_flops(wl, pre_seqs)
+    dbytes = decode_bytes(wl, dec_seqs)
+    pre_tflops = flops / t_pre / 1e12
+    dec_gbs = dbytes / t_dec / 1e9
+
+    if t_pre >= t_dec:
+        roof = {"kernel": "prefill_kernel", "bound": "mfma", "achieved": pre_tflops,
+                "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        roof = {"kernel": "decode_kernel", "bound": "hbm", "achieved": dec_gbs,
+                "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["launch_ms"] = (t_pre if roof["bound"] == "mfma" else t_dec) * 1e3
+
+    line = {
+        "metric": METRIC, "value": pre_tflops, "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 in/out; fp16 rotated QK operands; fp32 accumulate",
+        "data": "synthetic (seeded N(0,1) bf16, Zipf document reuse)",
+        "config": {"workload": WORKLOAD, "Hq": wl.Hq, "Hkv": wl.Hkv, "head_dim": wl.D,
+                   "block": wl.B, "prefill_requests": len(pre_seqs),
+                   "decode_requests": len(dec_seqs), "pool_blocks": wl.num_blocks},
+        "prefill": {"value": pre_tflops, "unit": "TFLOP/s", "ms": t_pre * 1e3,
+                    "frac_mfma_peak": pre_tflops / PEAK_MFMA_TFLOPS,
+                    "algorithmic_tflop": flops / 1e12},
+        "decode": {"value": dec_gbs, "unit": "GB/s", "ms": t_dec * 1e3,
+                   "frac_hbm_peak": dec_gbs / PEAK_HBM_GBS,
+                   "algorithmic_gb": dbytes / 1e9},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, pre_seqs, dec_seqs)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,158 @@
+/*
+ * lazyattn.h -- C ABI of the LazyAttention library for AMD Instinct MI355X (gfx950).
+ *
+ * LazyAttention (Xia, Pamnani, Fang, Chockchowwat, Park, "LazyAttention: Efficient
+ * Retrieval-Augmented Generation with Deferred Positional Encoding", arXiv 2606.04302)
+ * keeps a KV cache whose keys carry NO positional encoding, so one physical copy of a
+ * document's KV blocks can back many logical requests at arbitrary positions (abstract;
+ * technical summary, "Core Concept: Deferred Positional Encoding"). RoPE is applied inside
+ * the attention kernels while scores are computed. The technical summary's "Technical
+ * Implementation" section describes the two kernels this library provides:
+ *   - prefill (compute-bound): cached KV blocks are loaded and each key tile receives ONE
+ *     relative rotation per query tile, from the query-to-document offset;
+ *   - decode (M = 1, bandwidth-bound): the rotation is fused into the inner loop, the query
+ *     is re-rotated only when the relative offset changes (a new document), and block id
+ *     and offset are bit-packed in one 32-bit word.
+ * "Mathematical Equivalence": the result equals attention over materialised copies whose
+ * keys carry RoPE at their absolute logical positions.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Device pointers are owned by the caller; the library never allocates, frees or keeps
+ *    them. Compute calls are asynchronous on `stream` (a hipStream_t passed as void*; NULL
+ *    is the default stream) and never read device memory on the host, so argument checks
+ *    are limited to pointers, alignment and scalar sizes.
+ *  - bf16 is IEEE-754 binary32 truncated to its upper 16 bits (round to nearest even).
+ *  - Supported shapes: head dim D in {64, 128}; block size B = 16 tokens; Hq % Hkv == 0 with
+ *    G = Hq / Hkv in {1, 2, 4, 8}; rope_base > 1.
+ *  - RoPE: rotate-half pairing (dim k with k + D/2), angle n * theta_k,
+ *    theta_k = rope_base^(-2k/D); softmax scale 1/sqrt(D).
+ *  - Query head h reads key/value head floor(h / G).
+ *  - Causality is on LOGICAL positions: key at position L is visible to a query at p iff
+ *    L <= p. A query with no visible key outputs zeros.
+ *  - Return value: LAZYATTN_OK (0) or a negative LAZYATTN_ERR_* code; no exception, abort
+ *    or other failure leaves the ABI.
+ */
+#ifndef LAZYATTN_H
+#define LAZYATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LAZYATTN_OK             0
+#define LAZYATTN_ERR_NULL      -1  /* a required pointer is NULL */
+#define LAZYATTN_ERR_ALIGN     -2  /* q / pools / out / workspace not 16-byte aligned */
+#define LAZYATTN_ERR_SHAPE     -3  /* unsupported D, B, G, or negative / inconsistent sizes */
+#define LAZYATTN_ERR_RANGE     -4  /* encoder: block id >= 2^17 or offset delta outside 15 bits */
+#define LAZYATTN_ERR_WORKSPACE -5  /* workspace smaller than the matching *_workspace_bytes */
+#define LAZYATTN_ERR_LAUNCH    -6  /* a kernel launch failed (hipGetLastError after launch) */
+#define LAZYATTN_ERR_ARG       -7  /* other invalid scalar argument (rope_base, counts) */
+
+/*
+ * Packed block metadata word (one per block-table entry).
+ *   bits [16:0]  physical block id            0 .. 131071
+ *   bits [31:17] delta = offset - t * B        15-bit two's complement, -16384 .. 16383
+ * t is the entry's index inside its own sequence and offset the logical position of the
+ * block's slot 0, so slot j of entry t sits at logical position t*B + delta + j. delta is
+ * constant across blocks placed back-to-back, so it changes exactly at document
+ * boundaries (where the decode kernel re-anchors its rotated query). The summary only
+ * says (block ID, offset) are bit-packed into a single register; this layout is the
+ * library's own, chosen because 17 id bits (~128k-block pools) plus an absolute 16-bit
+ * position would need 33 bits.
+ */
+#define LAZYATTN_ID_BITS    17
+#define LAZYATTN_DELTA_BITS 15
+
+/*
+ * lazyattn_prefill -- attention for a batch of sequences with any number of query rows
+ * (technical summary, "Technical Implementation", prefilling phase).
+ *
+ *  q           bf16 [total_q, Hq, D], contiguous (un-rotated queries)
+ *  k_pool      bf16 [num_blocks, Hkv, B, D] UN-ROTATED keys (position-free pool)
+ *  v_pool      bf16 [num_blocks, Hkv, B, D]
+ *  block_table int32 [num_seqs + 1]: CSR row pointers into block_meta; sequence s owns
+ *              entries block_table[s] .. block_table[s+1]-1 (T_s entries, in any order)
+ *  block_meta  uint32 [block_table[num_seqs]] packed words (see above)
+ *  kv_lens     int32 [num_seqs]: keys of sequence s; (T_s-1)*B < kv_lens[s] <= T_s*B, i.e.
+ *              only a sequence's LAST entry may be partial; its unused slots are never read
+ *              into the result (they may hold NaN)
+ *  q_indptr    int32 [num_seqs + 1]: CSR rows of q per sequence (q_len_s >= 0; mixed OK)
+ *  q_positions int32 [total_q]: logical position of each query row
+ *  rope_base   RoPE base (e.g. 10000.0)
+ *  max_entries an upper bound on T_s used to size split-K work (a wrong bound costs
+ *              balance, never memory safety)
+ *  out         bf16 [total_q, Hq, D]; every row is written
+ *  workspace   device scratch of at least lazyattn_prefill_workspace_bytes(...) bytes,
+ *              16-byte aligned; its contents on entry do not matter; concurrent calls must
+ *              not share one workspace
+ *
+ * Sequences with q_len_s > 1 run the tiled prefill kernel (one relative key rotation per
+ * query tile); sequences with q_len_s == 1 run the split-K decode kernel and a merge, all
+ * inside this call, so a continuous batch mixing prefill and decode requests is one call.
+ */
+int lazyattn_prefill(const void* q, const void* k_pool, const void* v_pool,
+                     const int32_t* block_table, const uint32_t* block_meta,
+                     const int32_t* kv_lens, const int32_t* q_indptr,
+                     const int32_t* q_positions, double rope_base,
+                     int32_t num_seqs, int32_t total_q, int32_t Hq, int32_t Hkv, int32_t D,
+                     int32_t B, int32_t num_blocks, int32_t max_entries,
+                     void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * lazyattn_decode -- same arguments and result as lazyattn_prefill, executed entirely by
+ * the split-K decode kernel (technical summary, "Technical Implementation", decoding
+ * phase): every query row is an M = 1 problem; the query is re-rotated only where the
+ * offset delta changes. Intended for q_len_s == 1; larger q_len_s are computed correctly,
+ * row by row. Workspace: lazyattn_decode_workspace_bytes(...).
+ */
+int lazyattn_decode(const void* q, const void* k_pool, const void* v_pool,
+                    const int32_t* block_table, const uint32_t* block_meta,
+                    const int32_t* kv_lens, const int32_t* q_indptr,
+                    const int32_t* q_positions, double rope_base,
+                    int32_t num_seqs, int32_t total_q, int32_t Hq, int32_t Hkv, int32_t D,
+                    int32_t B, int32_t num_blocks, int32_t max_entries,
+                    void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace sizes (bytes) for the calls above; 0 on invalid sizes. */
+size_t lazyattn_prefill_workspace_bytes(int32_t num_seqs, int32_t total_q, int32_t max_entries,
+                                        int32_t Hq, int32_t Hkv, int32_t D);
+size_t lazyattn_decode_workspace_bytes(int32_t num_seqs, int32_t total_q, int32_t max_entries,
+                                       int32_t Hq, int32_t Hkv, int32_t D);
+
+/*
+ * lazyattn_encode_meta -- HOST function: pack per-entry (block id, logical offset) into
+ * words (layout above). block_ids int32 [n], offsets int64 [n], block_table int32
+ * [num_seqs+1] with n = block_table[num_seqs]; words_out uint32 [n]. On LAZYATTN_ERR_RANGE
+ * *first_bad_entry receives the first offending flat entry index (else -1); words_out is
+ * then fully written with the in-range entries encoded and the bad ones set to 0.
+ * Returns LAZYATTN_ERR_SHAPE if block_table is not non-decreasing from 0.
+ */
+int lazyattn_encode_meta(const int32_t* block_ids, const int64_t* offsets,
+                         const int32_t* block_table, int32_t num_seqs, int32_t B,
+                         uint32_t* words_out, int64_t* first_bad_entry);
+
+/*
+ * lazyattn_debug_decode_meta -- DEVICE, for tests: decodes every word with the same device
+ * routine the attention kernels use. words uint32 [n], block_table int32 [num_seqs+1]
+ * (device), ids_out int32 [n], offsets_out int32 [n] (device); n = block_table[num_seqs]
+ * must be passed as n_entries.
+ */
+int lazyattn_debug_decode_meta(const uint32_t* words, const int32_t* block_table,
+                               int32_t num_seqs, int32_t n_entries, int32_t B,
+                               int32_t* ids_out, int32_t* offsets_out, void* stream);
+
+/* Static description of a status code. */
+const char* lazyattn_status_str(int status);
+
+/* Library version string. */
+const char* lazyattn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LAZYATTN_H */

@@ -1,0 +1,5 @@
+"""LazyAttention on AMD Instinct MI355X: deferred-RoPE paged attention over a
+position-free KV pool (HIP/gfx950 kernels behind a C ABI, include/lazyattn.h)."""
+from ._lib import lib, LazyAttnError, EXPORTED, LIB_PATH  # noqa: F401
+from .api import (prefill, decode, encode_meta, debug_decode_meta,  # noqa: F401
+                  workspace_bytes, BLOCK)

@@ -1,0 +1,60 @@
+"""ctypes loader for liblazyattn.so (the HIP/gfx950 library); argument marshalling only."""
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblazyattn.so")
+
+OK, ERR_NULL, ERR_ALIGN, ERR_SHAPE, ERR_RANGE, ERR_WORKSPACE, ERR_LAUNCH, ERR_ARG = \
+    0, -1, -2, -3, -4, -5, -6, -7
+
+# every symbol include/lazyattn.h declares
+EXPORTED = [
+    "lazyattn_prefill", "lazyattn_decode", "lazyattn_prefill_workspace_bytes",
+    "lazyattn_decode_workspace_bytes", "lazyattn_encode_meta", "lazyattn_debug_decode_meta",
+    "lazyattn_status_str", "lazyattn_version",
+]
+
+_lib = None
+
+
+class LazyAttnError(RuntimeError):
+    def __init__(self, code, where):
+        self.code = code
+        super().__init__(f"{where}: {status_str(code)} ({code})")
+
+
+def lib():
+    """Load the library once; fail loudly if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                          "(hipcc, gfx950)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, u64, dbl = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_double
+    attn = [vp, vp, vp, vp, vp, vp, vp, vp, dbl, i32, i32, i32, i32, i32, i32, i32, i32,
+            vp, vp, u64, vp]
+    for name in ("lazyattn_prefill", "lazyattn_decode"):
+        f = getattr(L, name)
+        f.argtypes, f.restype = attn, ctypes.c_int
+    for name in ("lazyattn_prefill_workspace_bytes", "lazyattn_decode_workspace_bytes"):
+        f = getattr(L, name)
+        f.argtypes, f.restype = [i32] * 6, ctypes.c_size_t
+    L.lazyattn_encode_meta.argtypes = [vp, vp, vp, i32, i32, vp, vp]
+    L.lazyattn_encode_meta.restype = ctypes.c_int
+    L.lazyattn_debug_decode_meta.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp]
+    L.lazyattn_debug_decode_meta.restype = ctypes.c_int
+    L.lazyattn_status_str.argtypes, L.lazyattn_status_str.restype = [ctypes.c_int], ctypes.c_char_p
+    L.lazyattn_version.argtypes, L.lazyattn_version.restype = [], ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def status_str(code: int) -> str:
+    return lib().lazyattn_status_str(int(code)).decode()
+
+
+def check(code: int, where: str):
+    if code != OK:
+        raise LazyAttnError(code, where)

@@ -1,0 +1,96 @@
+"""Thin torch-facing wrappers over the C ABI (include/lazyattn.h).
+
+Only argument marshalling happens here: device pointers from torch tensors, the current
+HIP stream, workspace allocation through torch. Every step of the attention path runs in
+the HIP kernels of liblazyattn.so.
+"""
+import ctypes
+
+import numpy as np
+
+from ._lib import lib, check
+
+BLOCK = 16
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dims(q, k_pool):
+    total_q, Hq, D = q.shape
+    num_blocks, Hkv, B, D2 = k_pool.shape
+    if D2 != D:
+        raise ValueError("q and k_pool head dims differ")
+    return total_q, Hq, D, num_blocks, Hkv, B
+
+
+def workspace_bytes(kind, num_seqs, total_q, max_entries, Hq, Hkv, D):
+    f = lib().lazyattn_prefill_workspace_bytes if kind == "prefill" else \
+        lib().lazyattn_decode_workspace_bytes
+    return int(f(num_seqs, total_q, max_entries, Hq, Hkv, D))
+
+
+def _attention(kind, q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indptr, q_pos,
+               rope_base, max_entries, out=None, workspace=None, stream=None):
+    import torch
+    total_q, Hq, D, num_blocks, Hkv, B = _dims(q, k_pool)
+    num_seqs = kv_lens.numel()
+    if out is None:
+        out = torch.empty_like(q)
+    need = workspace_bytes(kind, num_seqs, total_q, max_entries, Hq, Hkv, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    fn = lib().lazyattn_prefill if kind == "prefill" else lib().lazyattn_decode
+    rc = fn(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(block_meta),
+            _ptr(kv_lens), _ptr(q_indptr), _ptr(q_pos), float(rope_base), num_seqs, total_q,
+            Hq, Hkv, D, B, num_blocks, int(max_entries), _ptr(out), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(stream))
+    check(rc, "lazyattn_" + kind)
+    return out
+
+
+def prefill(q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indptr, q_pos, rope_base,
+            max_entries, out=None, workspace=None, stream=None):
+    """lazyattn_prefill on torch tensors (all on one HIP device); returns out."""
+    return _attention("prefill", q, k_pool, v_pool, block_table, block_meta, kv_lens,
+                      q_indptr, q_pos, rope_base, max_entries, out, workspace, stream)
+
+
+def decode(q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indptr, q_pos, rope_base,
+           max_entries, out=None, workspace=None, stream=None):
+    """lazyattn_decode on torch tensors; returns out."""
+    return _attention("decode", q, k_pool, v_pool, block_table, block_meta, kv_lens,
+                      q_indptr, q_pos, rope_base, max_entries, out, workspace, stream)
+
+
+def encode_meta(block_ids, offsets, block_table, B=BLOCK):
+    """Host encoder: (int32 ids, int64 offsets, int32 CSR) -> uint32 words (numpy)."""
+    ids = np.ascontiguousarray(block_ids, dtype=np.int32)
+    offs = np.ascontiguousarray(offsets, dtype=np.int64)
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    words = np.zeros(len(ids), dtype=np.uint32)
+    bad = ctypes.c_int64(-1)
+    rc = lib().lazyattn_encode_meta(ids.ctypes.data, offs.ctypes.data, bt.ctypes.data,
+                                    len(bt) - 1, B, words.ctypes.data, ctypes.byref(bad))
+    check(rc, f"lazyattn_encode_meta (first bad entry {bad.value})")
+    return words
+
+
+def debug_decode_meta(words, block_table, stream=None):
+    """Device decoder of packed words (tests): returns (ids, offsets) int32 tensors."""
+    import torch
+    n = words.numel()
+    ids = torch.empty(n, dtype=torch.int32, device=words.device)
+    offs = torch.empty(n, dtype=torch.int32, device=words.device)
+    rc = lib().lazyattn_debug_decode_meta(_ptr(words), _ptr(block_table),
+                                          block_table.numel() - 1, n, BLOCK, _ptr(ids),
+                                          _ptr(offs), _stream(stream))
+    check(rc, "lazyattn_debug_decode_meta")
+    return ids, offs

@@ -1,0 +1,202 @@
+// C ABI of the LazyAttention library: argument validation, RoPE frequency table,
+// work sizing and kernel launches. Declarations and contracts: include/lazyattn.h.
+#include "lazyattn.h"
+#include "lazyattn_common.h"
+#include "lazyattn_kernels.h"
+
+#include <cmath>
+#include <cstdint>
+
+using namespace lazyattn;
+
+namespace {
+
+constexpr int kTargetDecodeWaves = 4096;   // split-K target: ~16 waves per CU
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool shape_ok(int32_t Hq, int32_t Hkv, int32_t D, int32_t B) {
+  if (D != 64 && D != 128) return false;
+  if (B != kBlock) return false;
+  if (Hkv <= 0 || Hq <= 0 || Hq % Hkv) return false;
+  const int G = Hq / Hkv;
+  return G == 1 || G == 2 || G == 4 || G == 8;
+}
+
+// Split-K factor of a decode row: enough (row, kv-head, split) waves to fill the GPU,
+// at least ~8 blocks per split.
+int decode_splits(int rows_bound, int Hkv, int max_entries) {
+  long long pairs = (long long)(rows_bound > 0 ? rows_bound : 1) * Hkv;
+  long long s = (kTargetDecodeWaves + pairs - 1) / pairs;
+  long long cap = (max_entries + 7) / 8;
+  if (cap < 1) cap = 1;
+  if (s > cap) s = cap;
+  if (s > 256) s = 256;
+  if (s < 1) s = 1;
+  return (int)s;
+}
+
+size_t workspace_for(int num_seqs, int rows_bound, int max_entries, int Hq, int Hkv, int D) {
+  const int S = decode_splits(rows_bound, Hkv, max_entries);
+  return ws_layout(num_seqs, (long long)rows_bound * S, Hq, D).total;
+}
+
+int run(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_table,
+        const uint32_t* block_meta, const int32_t* kv_lens, const int32_t* q_indptr,
+        const int32_t* q_positions, double rope_base, int32_t num_seqs, int32_t total_q,
+        int32_t Hq, int32_t Hkv, int32_t D, int32_t B, int32_t num_blocks,
+        int32_t max_entries, void* out, void* workspace, size_t workspace_bytes,
+        void* stream, int mode) {
+  if (!q || !k_pool || !v_pool || !block_table || !block_meta || !kv_lens || !q_indptr ||
+      !q_positions || !out || !workspace)
+    return LAZYATTN_ERR_NULL;
+  if (num_seqs < 0 || total_q < 0 || num_blocks < 0 || max_entries < 0 ||
+      num_blocks > (1 << kIdBits) || !shape_ok(Hq, Hkv, D, B))
+    return LAZYATTN_ERR_SHAPE;
+  if (!(rope_base > 1.0) || !std::isfinite(rope_base)) return LAZYATTN_ERR_ARG;
+  if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(out, 16) ||
+      !aligned(workspace, 16) || !aligned(block_table, 4) || !aligned(block_meta, 4) ||
+      !aligned(kv_lens, 4) || !aligned(q_indptr, 4) || !aligned(q_positions, 4))
+    return LAZYATTN_ERR_ALIGN;
+  const int rows_bound = mode == kPlanDecodeOnly ? total_q : num_seqs;
+  if (workspace_bytes < workspace_for(num_seqs, rows_bound, max_entries, Hq, Hkv, D))
+    return LAZYATTN_ERR_WORKSPACE;
+  if (num_seqs == 0 || total_q == 0) return LAZYATTN_OK;
+
+  hipStream_t st = (hipStream_t)stream;
+  const int G = Hq / Hkv;
+  const int S = decode_splits(rows_bound, Hkv, max_entries);
+  const WsLayout L = ws_layout(num_seqs, (long long)rows_bound * S, Hq, D);
+  char* ws = (char*)workspace;
+  double* freqs = (double*)(ws + L.off_freqs);
+  int32_t* pf_prefix = (int32_t*)(ws + L.off_pf_prefix);
+  int32_t* dec_prefix = (int32_t*)(ws + L.off_dec_prefix);
+  float* partials = (float*)(ws + L.off_partials);
+
+  RopeFreqs fr{};
+  for (int k = 0; k < D / 2; ++k)
+    fr.f[k] = std::pow(rope_base, -2.0 * k / D) / (2.0 * M_PI);
+  const float scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
+
+  PlanParams pp{q_indptr, block_table, freqs, pf_prefix, dec_prefix, num_seqs,
+                prefill_positions_per_tile(G), S, mode, D / 2, fr};
+  if (launch_plan(pp, st) != hipSuccess) return LAZYATTN_ERR_LAUNCH;
+
+  if (mode == kPlanMixed) {
+    PrefillParams P{(const uint16_t*)q, (const uint16_t*)k_pool, (const uint16_t*)v_pool,
+                    block_table, block_meta, kv_lens, q_indptr, q_positions,
+                    (uint16_t*)out, pf_prefix, num_seqs, Hq, Hkv, num_blocks, scale_log2, freqs};
+    const int pos = prefill_positions_per_tile(G);
+    const long long tiles = ((long long)total_q + pos - 1) / pos + num_seqs;
+    if (tiles > INT32_MAX) return LAZYATTN_ERR_SHAPE;
+    if (launch_prefill(P, D, G, (int)tiles, true, st) != hipSuccess) return LAZYATTN_ERR_LAUNCH;
+  }
+  DecodeParams Dp{(const uint16_t*)q, (const uint16_t*)k_pool, (const uint16_t*)v_pool,
+                  block_table, block_meta, kv_lens, q_indptr, q_positions, dec_prefix,
+                  partials, num_seqs, Hq, Hkv, num_blocks, S, scale_log2, freqs};
+  if (launch_decode(Dp, D, G, (long long)rows_bound * S, st) != hipSuccess)
+    return LAZYATTN_ERR_LAUNCH;
+  MergeParams Mp{q_indptr, block_table, dec_prefix, partials, (uint16_t*)out,
+                 num_seqs, Hq, S, mode};
+  if (launch_merge(Mp, total_q, D, st) != hipSuccess) return LAZYATTN_ERR_LAUNCH;
+  return LAZYATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int lazyattn_prefill(const void* q, const void* k_pool, const void* v_pool,
+                     const int32_t* block_table, const uint32_t* block_meta,
+                     const int32_t* kv_lens, const int32_t* q_indptr,
+                     const int32_t* q_positions, double rope_base, int32_t num_seqs,
+                     int32_t total_q, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
+                     int32_t num_blocks, int32_t max_entries, void* out, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  return run(q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indptr, q_positions,
+             rope_base, num_seqs, total_q, Hq, Hkv, D, B, num_blocks, max_entries, out,
+             workspace, workspace_bytes, stream, kPlanMixed);
+}
+
+int lazyattn_decode(const void* q, const void* k_pool, const void* v_pool,
+                    const int32_t* block_table, const uint32_t* block_meta,
+                    const int32_t* kv_lens, const int32_t* q_indptr,
+                    const int32_t* q_positions, double rope_base, int32_t num_seqs,
+                    int32_t total_q, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
+                    int32_t num_blocks, int32_t max_entries, void* out, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  return run(q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indptr, q_positions,
+             rope_base, num_seqs, total_q, Hq, Hkv, D, B, num_blocks, max_entries, out,
+             workspace, workspace_bytes, stream, kPlanDecodeOnly);
+}
+
+size_t lazyattn_prefill_workspace_bytes(int32_t num_seqs, int32_t total_q, int32_t max_entries,
+                                        int32_t Hq, int32_t Hkv, int32_t D) {
+  if (num_seqs < 0 || total_q < 0 || max_entries < 0 || !shape_ok(Hq, Hkv, D, kBlock)) return 0;
+  return workspace_for(num_seqs, num_seqs, max_entries, Hq, Hkv, D);
+}
+
+size_t lazyattn_decode_workspace_bytes(int32_t num_seqs, int32_t total_q, int32_t max_entries,
+                                       int32_t Hq, int32_t Hkv, int32_t D) {
+  if (num_seqs < 0 || total_q < 0 || max_entries < 0 || !shape_ok(Hq, Hkv, D, kBlock)) return 0;
+  return workspace_for(num_seqs, total_q, max_entries, Hq, Hkv, D);
+}
+
+int lazyattn_encode_meta(const int32_t* block_ids, const int64_t* offsets,
+                         const int32_t* block_table, int32_t num_seqs, int32_t B,
+                         uint32_t* words_out, int64_t* first_bad_entry) {
+  if (first_bad_entry) *first_bad_entry = -1;
+  if (!block_table || num_seqs < 0) return !block_table ? LAZYATTN_ERR_NULL : LAZYATTN_ERR_SHAPE;
+  if (B != kBlock) return LAZYATTN_ERR_SHAPE;
+  if (block_table[0] != 0) return LAZYATTN_ERR_SHAPE;
+  for (int s = 0; s < num_seqs; ++s)
+    if (block_table[s + 1] < block_table[s]) return LAZYATTN_ERR_SHAPE;
+  const int64_t n = block_table[num_seqs];
+  if (n > 0 && (!block_ids || !offsets || !words_out)) return LAZYATTN_ERR_NULL;
+  int rc = LAZYATTN_OK;
+  const int64_t dmin = -(1ll << (LAZYATTN_DELTA_BITS - 1)), dmax = (1ll << (LAZYATTN_DELTA_BITS - 1)) - 1;
+  for (int s = 0; s < num_seqs; ++s) {
+    for (int64_t e = block_table[s]; e < block_table[s + 1]; ++e) {
+      const int64_t t = e - block_table[s];
+      const int64_t id = block_ids[e];
+      const int64_t delta = offsets[e] - t * B;
+      if (id < 0 || id > (int64_t)kIdMask || delta < dmin || delta > dmax) {
+        words_out[e] = 0;
+        if (rc == LAZYATTN_OK && first_bad_entry) *first_bad_entry = e;
+        rc = LAZYATTN_ERR_RANGE;
+        continue;
+      }
+      words_out[e] = (uint32_t)id | ((uint32_t)(delta & ((1 << LAZYATTN_DELTA_BITS) - 1)) << kIdBits);
+    }
+  }
+  return rc;
+}
+
+int lazyattn_debug_decode_meta(const uint32_t* words, const int32_t* block_table,
+                               int32_t num_seqs, int32_t n_entries, int32_t B,
+                               int32_t* ids_out, int32_t* offsets_out, void* stream) {
+  if (!words || !block_table || !ids_out || !offsets_out) return LAZYATTN_ERR_NULL;
+  if (num_seqs <= 0 || n_entries < 0 || B != kBlock) return LAZYATTN_ERR_SHAPE;
+  if (launch_debug_decode(words, block_table, num_seqs, n_entries, ids_out, offsets_out,
+                          (hipStream_t)stream) != hipSuccess)
+    return LAZYATTN_ERR_LAUNCH;
+  return LAZYATTN_OK;
+}
+
+const char* lazyattn_status_str(int status) {
+  switch (status) {
+    case LAZYATTN_OK: return "ok";
+    case LAZYATTN_ERR_NULL: return "null pointer argument";
+    case LAZYATTN_ERR_ALIGN: return "misaligned pointer argument";
+    case LAZYATTN_ERR_SHAPE: return "unsupported or inconsistent shape";
+    case LAZYATTN_ERR_RANGE: return "block id or offset delta out of the packed word's range";
+    case LAZYATTN_ERR_WORKSPACE: return "workspace too small";
+    case LAZYATTN_ERR_LAUNCH: return "kernel launch failed";
+    case LAZYATTN_ERR_ARG: return "invalid scalar argument";
+  }
+  return "unknown status";
+}
+
+const char* lazyattn_version(void) { return "lazyattn-gfx950 0.1"; }
+
+}  // extern "C"

@@ -1,0 +1,137 @@
+// Shared device helpers of the LazyAttention kernels (gfx950 only).
+//
+// Packed words, RoPE phase arithmetic, bf16 packing and MFMA operand types used by the
+// prefill, decode and merge kernels. Nothing here is shared with the float64 oracle.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lazyattn {
+
+constexpr int kBlock = 16;                 // tokens per KV block
+constexpr int kIdBits = 17;
+constexpr uint32_t kIdMask = (1u << kIdBits) - 1u;
+constexpr int kMaxHalfDim = 64;            // D <= 128
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// RoPE frequencies in revolutions per position: f_k = base^(-2k/D) / (2 pi), computed on
+// the host in double precision and passed by value (kernel argument segment).
+struct RopeFreqs {
+  double f[kMaxHalfDim];
+};
+
+// ---- packed (block id, delta) word ------------------------------------------------------
+// bits [16:0] id, bits [31:17] delta = offset - t*B (two's complement). One AND and one
+// arithmetic shift; this is the only device decoder, used by every kernel.
+__host__ __device__ __forceinline__ int word_id(uint32_t w) { return (int)(w & kIdMask); }
+__host__ __device__ __forceinline__ int word_delta(uint32_t w) { return ((int32_t)w) >> kIdBits; }
+__host__ __device__ __forceinline__ int word_offset(uint32_t w, int t) {
+  return t * kBlock + word_delta(w);
+}
+
+// ---- exact RoPE phase --------------------------------------------------------------------
+// cos/sin of n * theta_k for an integer n (|n| < 2^31): the angle is reduced in revolutions
+// in double precision (n * f_k is exact to ~2^-53 relative, frac() is exact), then the
+// hardware sin/cos take the reduced revolution count in [0, 1).
+__device__ __forceinline__ void rope_cos_sin(int n, double f, float& c, float& s) {
+  double x = (double)n * f;
+  x = x - __builtin_floor(x);
+  float r = (float)x;
+  s = __builtin_amdgcn_sinf(r);
+  c = __builtin_amdgcn_cosf(r);
+}
+
+// ---- bf16 helpers --------------------------------------------------------------------------
+__device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+// Round two floats to bf16 (nearest even) and pack: a -> low half, b -> high half.
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  __bf16 x = (__bf16)a, y = (__bf16)b;
+  uint16_t ux = __builtin_bit_cast(uint16_t, x), uy = __builtin_bit_cast(uint16_t, y);
+  return (uint32_t)ux | ((uint32_t)uy << 16);
+}
+
+// Round two floats to fp16 (nearest even) and pack. The rotated query/key operands of the
+// score products are carried in fp16: they come out of fp32 rotation arithmetic anyway,
+// and fp16 keeps 3 more mantissa bits than bf16 at the same MFMA rate (element magnitudes
+// must stay below 65504).
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
+  _Float16 x = (_Float16)a, y = (_Float16)b;
+  uint16_t ux = __builtin_bit_cast(uint16_t, x), uy = __builtin_bit_cast(uint16_t, y);
+  return (uint32_t)ux | ((uint32_t)uy << 16);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32h(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16h(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16). Within each 16-lane group, lane i
+// receives element e = the 16-bit value at (address given by lane 4e + i/4) + (i % 4).
+// With lane m supplying &M[k0 + m/4][n0 + 4 (m%4)] of a row-major bf16 matrix M, lane i
+// receives M[k0 .. k0+3][n0 + i]: four consecutive rows of one column.
+__device__ __forceinline__ u32x2 lds_read_tr(const uint16_t* p) {
+  s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(p));
+  return __builtin_bit_cast(u32x2, r);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// Binary search: largest s in [0, n) with prefix[s] <= x (prefix non-decreasing, prefix[0]=0).
+__device__ __forceinline__ int upper_seq(const int32_t* prefix, int n, int x) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (prefix[mid] <= x) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// ---- workspace layout -----------------------------------------------------------------------
+// [0, 512)                RoPE frequency table, double [64] (revolutions per position)
+// [512, ...)              prefix arrays: prefill tiles, decode items, each num_seqs + 1 int32
+// aligned 256             split-K partials: float [items][Hq][D + 4]  (o[D], m, l, -, -)
+struct WsLayout {
+  size_t off_freqs, off_pf_prefix, off_dec_prefix, off_partials, total;
+};
+
+__host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+__host__ __device__ inline WsLayout ws_layout(int num_seqs, long long max_items, int Hq, int D) {
+  WsLayout L;
+  L.off_freqs = 0;
+  L.off_pf_prefix = 512;
+  L.off_dec_prefix = align_up(L.off_pf_prefix + 4ull * (num_seqs + 1), 256);
+  L.off_partials = align_up(L.off_dec_prefix + 4ull * (num_seqs + 1), 256);
+  L.total = L.off_partials + (size_t)max_items * Hq * (D + 4) * 4ull;
+  return L;
+}
+
+// Plan modes.
+enum PlanMode : int { kPlanMixed = 0, kPlanDecodeOnly = 1 };
+
+}  // namespace lazyattn

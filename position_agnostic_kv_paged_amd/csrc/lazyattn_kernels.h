@@ -1,0 +1,74 @@
+// Kernel parameter blocks and launchers (internal to the library).
+#pragma once
+
+#include "lazyattn_common.h"
+
+namespace lazyattn {
+
+struct PlanParams {
+  const int32_t* q_indptr;
+  const int32_t* block_table;
+  double* freqs_out;         // [D/2] workspace copy of the frequency table
+  int32_t* pf_prefix;        // [num_seqs + 1] prefill tiles
+  int32_t* dec_prefix;       // [num_seqs + 1] decode items (row, split)
+  int num_seqs;
+  int pos_per_tile;          // query positions per prefill tile
+  int splits;                // maximum split-K factor of a decode row
+  int mode;                  // PlanMode
+  int half_dim;
+  RopeFreqs fr;              // host-computed table (kernel argument)
+};
+
+struct PrefillParams {
+  const uint16_t* q;
+  const uint16_t* k_pool;
+  const uint16_t* v_pool;
+  const int32_t* block_table;
+  const uint32_t* block_meta;
+  const int32_t* kv_lens;
+  const int32_t* q_indptr;
+  const int32_t* q_pos;
+  uint16_t* out;
+  const int32_t* pf_prefix;
+  int num_seqs, Hq, Hkv, num_blocks;
+  float scale_log2;          // log2(e) / sqrt(D)
+  const double* freqs;       // [D/2] RoPE frequencies (revolutions per position)
+};
+
+struct DecodeParams {
+  const uint16_t* q;
+  const uint16_t* k_pool;
+  const uint16_t* v_pool;
+  const int32_t* block_table;
+  const uint32_t* block_meta;
+  const int32_t* kv_lens;
+  const int32_t* q_indptr;
+  const int32_t* q_pos;
+  const int32_t* dec_prefix;
+  float* partials;           // [items][Hq][D + 4]
+  int num_seqs, Hq, Hkv, num_blocks, splits;
+  float scale_log2;
+  const double* freqs;
+};
+
+struct MergeParams {
+  const int32_t* q_indptr;
+  const int32_t* block_table;
+  const int32_t* dec_prefix;
+  const float* partials;
+  uint16_t* out;
+  int num_seqs, Hq, splits, mode;
+};
+
+hipError_t launch_plan(const PlanParams& p, hipStream_t st);
+hipError_t launch_merge(const MergeParams& p, int total_q, int D, hipStream_t st);
+hipError_t launch_debug_decode(const uint32_t* words, const int32_t* bt, int num_seqs, int n,
+                               int32_t* ids, int32_t* offs, hipStream_t st);
+// grid_tiles: upper bound of prefill tiles (extra workgroups exit at once)
+hipError_t launch_prefill(const PrefillParams& p, int D, int G, int grid_tiles, bool rotate,
+                          hipStream_t st);
+int prefill_positions_per_tile(int G);
+hipError_t launch_decode(const DecodeParams& p, int D, int G, long long grid_items,
+                         hipStream_t st);
+
+}  // namespace lazyattn

@@ -1,0 +1,133 @@
+// Device-side planning, split-K merge and the debug word decoder.
+//
+// The host never reads device memory (calls stay asynchronous), so the per-sequence work
+// counts are derived on the device: one workgroup scans q_indptr / block_table and writes
+// prefix sums that the attention kernels binary-search to find their sequence.
+#include "lazyattn_common.h"
+#include "lazyattn_kernels.h"
+
+namespace lazyattn {
+
+__device__ __forceinline__ int decode_splits(int T, int S) {
+  int s = T < S ? T : S;
+  return s < 1 ? 1 : s;
+}
+
+// One workgroup of 1024 threads; chunked exclusive scan over sequences.
+__global__ __launch_bounds__(1024) void plan_kernel(PlanParams P) {
+  __shared__ int sa[1024], sb[1024];
+  __shared__ int carry_a, carry_b;
+  const int tid = threadIdx.x;
+  if (tid == 0) { carry_a = 0; carry_b = 0; }
+#pragma unroll
+  for (int i = 0; i < kMaxHalfDim; ++i)
+    if (tid == i && i < P.half_dim) P.freqs_out[i] = P.fr.f[i];
+  __syncthreads();
+  for (int base = 0; base < P.num_seqs; base += 1024) {
+    const int s = base + tid;
+    int a = 0, b = 0;
+    if (s < P.num_seqs) {
+      const int qlen = P.q_indptr[s + 1] - P.q_indptr[s];
+      const int T = P.block_table[s + 1] - P.block_table[s];
+      const bool dec = (P.mode == kPlanDecodeOnly) || qlen == 1;
+      if (dec) b = qlen * decode_splits(T, P.splits);
+      else a = (qlen + P.pos_per_tile - 1) / P.pos_per_tile;
+    }
+    sa[tid] = a; sb[tid] = b;
+    __syncthreads();
+    for (int o = 1; o < 1024; o <<= 1) {          // inclusive Hillis-Steele scan
+      int xa = tid >= o ? sa[tid - o] : 0;
+      int xb = tid >= o ? sb[tid - o] : 0;
+      __syncthreads();
+      sa[tid] += xa; sb[tid] += xb;
+      __syncthreads();
+    }
+    if (s < P.num_seqs) {
+      P.pf_prefix[s] = carry_a + sa[tid] - a;
+      P.dec_prefix[s] = carry_b + sb[tid] - b;
+    }
+    __syncthreads();
+    if (tid == 1023) { carry_a += sa[1023]; carry_b += sb[1023]; }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    P.pf_prefix[P.num_seqs] = carry_a;
+    P.dec_prefix[P.num_seqs] = carry_b;
+  }
+}
+
+// Split-K merge: one thread per 4 output dims of one (row, head). Partials hold the
+// running max m (log2 domain), the sum l and the unnormalised o of each split.
+template <int D>
+__global__ __launch_bounds__(256) void merge_kernel(MergeParams P) {
+  constexpr int TPH = D / 4;                  // threads per head
+  constexpr int HPB = 256 / TPH;              // heads per block
+  const int r = blockIdx.x;
+  const int h = blockIdx.y * HPB + threadIdx.x / TPH;
+  const int d0 = (threadIdx.x % TPH) * 4;
+  if (h >= P.Hq) return;
+  const int seq = upper_seq(P.q_indptr, P.num_seqs, r);
+  const int q0 = P.q_indptr[seq], qlen = P.q_indptr[seq + 1] - q0;
+  const bool dec = (P.mode == kPlanDecodeOnly) || qlen == 1;
+  if (!dec) return;                           // written by the prefill kernel
+  const int T = P.block_table[seq + 1] - P.block_table[seq];
+  const int splits = decode_splits(T, P.splits);
+  const long long item0 = (long long)P.dec_prefix[seq] + (long long)(r - q0) * splits;
+  float M = -INFINITY;
+  for (int s = 0; s < splits; ++s) {
+    const float* part = P.partials + ((item0 + s) * P.Hq + h) * (D + 4);
+    M = fmaxf(M, part[D]);
+  }
+  float L = 0.f, o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+  if (M != -INFINITY) {
+    for (int s = 0; s < splits; ++s) {
+      const float* part = P.partials + ((item0 + s) * P.Hq + h) * (D + 4);
+      const float m = part[D];
+      if (m == -INFINITY) continue;
+      const float sc = exp2f(m - M);
+      L += part[D + 1] * sc;
+      const f32x4 v = *(const f32x4*)(part + d0);
+      o0 += v[0] * sc; o1 += v[1] * sc; o2 += v[2] * sc; o3 += v[3] * sc;
+    }
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  uint32_t* dst = (uint32_t*)(P.out + ((size_t)r * P.Hq + h) * D + d0);
+  dst[0] = pack_bf16(o0 * inv, o1 * inv);
+  dst[1] = pack_bf16(o2 * inv, o3 * inv);
+}
+
+__global__ void debug_decode_meta_kernel(const uint32_t* words, const int32_t* block_table,
+                                         int num_seqs, int n, int32_t* ids, int32_t* offs) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= n) return;
+  const int s = upper_seq(block_table, num_seqs, e);
+  const int t = e - block_table[s];
+  const uint32_t w = words[e];
+  ids[e] = word_id(w);
+  offs[e] = word_offset(w, t);
+}
+
+hipError_t launch_plan(const PlanParams& p, hipStream_t st) {
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(const MergeParams& p, int total_q, int D, hipStream_t st) {
+  if (total_q == 0) return hipSuccess;
+  if (D == 128) {
+    hipLaunchKernelGGL(merge_kernel<128>, dim3(total_q, (p.Hq + 7) / 8), dim3(256), 0, st, p);
+  } else {
+    hipLaunchKernelGGL(merge_kernel<64>, dim3(total_q, (p.Hq + 15) / 16), dim3(256), 0, st, p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_debug_decode(const uint32_t* words, const int32_t* bt, int num_seqs, int n,
+                               int32_t* ids, int32_t* offs, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(debug_decode_meta_kernel, dim3((n + 255) / 256), dim3(256), 0, st,
+                     words, bt, num_seqs, n, ids, offs);
+  return hipGetLastError();
+}
+
+}  // namespace lazyattn

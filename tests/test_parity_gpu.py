@@ -1,0 +1,211 @@
+"""Parity of the HIP path (through the C ABI) with the float64 oracle on the same inputs.
+
+Tolerance on bf16 outputs: max |diff| <= 2e-2 and mean |diff| <= 2e-3; packed-word
+decoding bit-exact. Small cases compare every output element; the full-size workloads
+compare sampled rows (every head and dim of each sampled row) and check that all outputs
+are finite (unreferenced pool blocks and padding slots hold NaN).
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import oracle  # noqa: E402
+from workload import make, Segment, RequestLayout, build  # noqa: E402
+from tests.util import small, oracle_out  # noqa: E402
+from tests.gpu_util import run_hip, compare, say, words_for  # noqa: E402
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import position_agnostic_kv_paged_amd as L
+    L.lib()
+
+
+def _oracle_rows(wl, seq, rows):
+    return oracle_out(wl, rows=rows, seq=seq)
+
+
+# ------------------------------------------------------------------ packed words
+
+def test_device_word_decode_bit_exact():
+    import position_agnostic_kv_paged_amd as L
+    wl = make("decode-32q8kv-b8-ctx32769")
+    words = words_for(wl)
+    bt = wl.block_table
+    say("device decode of words: long-decode workload")
+    ids, offs = L.debug_decode_meta(torch.from_numpy(words.view(np.int32)).cuda(),
+                                    torch.from_numpy(bt).cuda())
+    torch.cuda.synchronize()
+    want_ids, want_offs = oracle.decode_meta(words, bt, 16)
+    assert np.array_equal(ids.cpu().numpy(), want_ids)
+    assert np.array_equal(offs.cpu().numpy(), want_offs)
+    # boundary words
+    cases_ids = np.array([0, 1, 131071, 5, 0, 131071], np.int32)
+    cases_off = np.array([0, 16 - 16384, 32 + 16383, 48 - 1, 64 + 7, 80], np.int64)
+    bt2 = np.array([0, 6], np.int32)
+    w2 = L.encode_meta(cases_ids, cases_off, bt2)
+    ids, offs = L.debug_decode_meta(torch.from_numpy(w2.view(np.int32)).cuda(),
+                                    torch.from_numpy(bt2).cuda())
+    torch.cuda.synchronize()
+    assert np.array_equal(ids.cpu().numpy(), cases_ids)
+    assert np.array_equal(offs.cpu().numpy(), cases_off)
+
+
+# ------------------------------------------------------------------ tiny configuration
+
+@pytest.mark.parametrize("kind", ["prefill", "decode"])
+def test_tiny_prefill_config(kind):
+    wl = make("tiny-prefill-4q1kv-d64")
+    say(f"tiny prefill config via {kind}")
+    compare(run_hip(wl, kind), oracle_out(wl), f"tiny/{kind}")
+
+
+@pytest.mark.parametrize("kind", ["prefill", "decode"])
+def test_tiny_decode_variant(kind):
+    wl = make("tiny-prefill-4q1kv-d64", decode_variant=True)
+    say(f"tiny decode variant via {kind}")
+    compare(run_hip(wl, kind), oracle_out(wl), f"tiny-decode/{kind}")
+
+
+# ------------------------------------------------------------------ adversarial mini-cases
+
+def _mini_cases():
+    cases = []
+    for D in (64, 128):
+        for Hq, Hkv in ((4, 4), (4, 2), (8, 2), (8, 1)):
+            cases.append((f"gaps-D{D}-G{Hq // Hkv}", dict(Hq=Hq, Hkv=Hkv, D=D, seed=D + Hq)))
+    segs_overlap = [Segment("doc", 3, doc=1), Segment("doc", 20, doc=0),
+                    Segment("doc", 100, doc=1), Segment("private", 140, tokens=21)]
+    cases.append(("overlap-repeat-partial", dict(Hq=8, Hkv=2, D=128, segs=segs_overlap,
+                                                 q_len=21, seed=3, q_scale=4.0)))
+    # 550 two-block placements back-to-back from 16000 (delta = 16000 stays in the word's
+    # 15-bit range): key and query positions run past 2^15
+    segs_far = [Segment("doc", 16000 + 32 * i, doc=i % 3) for i in range(550)] + \
+        [Segment("private", 16000 + 32 * 550, tokens=37)]
+    cases.append(("positions-above-2^15", dict(Hq=4, Hkv=1, D=128, segs=segs_far, q_len=37,
+                                               seed=4, q_scale=4.0)))
+    segs_zero = [Segment("doc", 50, doc=0), Segment("private", 90, tokens=3)]
+    cases.append(("no-visible-key", dict(Hq=4, Hkv=2, D=64, segs=segs_zero, q_len=2,
+                                         q_pos=np.array([0, 49]), seed=5)))
+    segs_long = [Segment("doc", 7 + 32 * i, doc=i % 3) for i in range(9)] + \
+        [Segment("private", 7 + 32 * 9, tokens=150)]
+    cases.append(("many-tiles-ragged", dict(Hq=8, Hkv=2, D=128, segs=segs_long, q_len=150,
+                                            seed=6)))
+    return cases
+
+
+@pytest.mark.parametrize("kind", ["prefill", "decode"])
+@pytest.mark.parametrize("name,kw", _mini_cases(), ids=[c[0] for c in _mini_cases()])
+def test_mini_cases(name, kw, kind):
+    wl = small(**kw)
+    say(f"mini case {name} via {kind}")
+    compare(run_hip(wl, kind), oracle_out(wl), f"{name}/{kind}")
+
+
+def test_mixed_batch_small():
+    """One call with prefill (q_len > 1), decode (q_len = 1) and empty (q_len = 0) requests."""
+    reqs = [RequestLayout([Segment("doc", 11, doc=0), Segment("doc", 60, doc=1),
+                           Segment("private", 100, tokens=70)], 70),
+            RequestLayout([Segment("doc", 0, doc=2), Segment("private", 32, tokens=5)], 1),
+            RequestLayout([Segment("doc", 0, doc=1), Segment("private", 32, tokens=2)], 0),
+            RequestLayout([Segment("doc", 500, doc=2), Segment("doc", 5, doc=0),
+                           Segment("private", 600, tokens=17)], 1)]
+    wl = build("mixed-small", 8, 1, 128, 16, 10000.0, 3, 32, reqs, seed=8)
+    say("mixed small batch via prefill")
+    compare(run_hip(wl, "prefill"), oracle_out(wl), "mixed-small/prefill")
+    compare(run_hip(wl, "decode"), oracle_out(wl), "mixed-small/decode")
+
+
+# ------------------------------------------------------------------ properties
+
+def test_reuse_equals_copy_bitwise_on_gpu():
+    lay_reuse = RequestLayout([Segment("doc", 0, doc=0), Segment("doc", 77, doc=0),
+                               Segment("private", 140, tokens=9)], 9)
+    lay_copy = RequestLayout([Segment("doc", 0, doc=0), Segment("doc", 77, doc=1),
+                              Segment("private", 140, tokens=9)], 9)
+    w1 = build("reuse", 8, 2, 128, 16, 10000.0, 2, 32, [lay_reuse], seed=21)
+    w2 = build("copy", 8, 2, 128, 16, 10000.0, 2, 32, [lay_copy], seed=21)
+    ids = w2.compact_ids(0)
+    w2.k_bits[ids[2:4]] = w2.k_bits[ids[0:2]]
+    w2.v_bits[ids[2:4]] = w2.v_bits[ids[0:2]]
+    for kind in ("prefill", "decode"):
+        say(f"reuse vs copy via {kind}")
+        a, b = run_hip(w1, kind), run_hip(w2, kind)
+        assert np.array_equal(a, b)
+        compare(a, oracle_out(w1), f"reuse/{kind}")
+
+
+def test_run_to_run_bitwise_determinism():
+    wl = make("prefill-32q8kv-b16-ctx5376")
+    say("determinism: prefill workload twice")
+    a, b = run_hip(wl, "prefill", repeat=2)
+    assert np.array_equal(a, b)
+    wd = make("decode-32q8kv-b64-ctx4161")
+    say("determinism: decode workload twice")
+    a, b = run_hip(wd, "decode", repeat=2)
+    assert np.array_equal(a, b)
+
+
+def test_shifted_document_is_detected():
+    """The comparison sees a one-position error in a document placement."""
+    wl = small(Hq=8, Hkv=2, D=128, seed=77, q_scale=4.0)
+    good = oracle_out(wl)
+    wl.seq_offsets = [wl.seq_offsets[0] + np.array([1, 1, 0, 0, 0, 0])]
+    got = run_hip(wl, "prefill")
+    assert np.max(np.abs(got - good)) > 2e-2
+
+
+# ------------------------------------------------------------------ full-size workloads
+
+def _sampled(wl, kind, seqs, rows_of):
+    out = run_hip(wl, kind)
+    assert np.all(np.isfinite(out)), "non-finite outputs"
+    got, want = [], []
+    for s in seqs:
+        rows = rows_of(s)
+        got.append(out[rows])
+        want.append(oracle_out(wl, rows=rows, seq=s))
+    return np.concatenate(got), np.concatenate(want)
+
+
+def test_decode_llama8b_batch64():
+    wl = make("decode-32q8kv-b64-ctx4161")
+    say("decode-32q8kv-b64-ctx4161 via decode")
+    seqs = [0, 9, 21, 40, 63]
+    g, w = _sampled(wl, "decode", seqs, lambda s: np.array([wl.q_indptr[s]]))
+    compare(g, w, "decode-b64")
+
+
+def test_prefill_llama8b_batch16():
+    wl = make("prefill-32q8kv-b16-ctx5376")
+    say("prefill-32q8kv-b16-ctx5376 via prefill")
+
+    def rows(s):
+        q0 = wl.q_indptr[s]
+        return q0 + np.array([0, 1, 63, 64, 127, 128, 200, 255])
+    g, w = _sampled(wl, "prefill", [0, 7, 15], rows)
+    compare(g, w, "prefill-b16")
+
+
+def test_long_decode_batch8():
+    wl = make("decode-32q8kv-b8-ctx32769")
+    say("decode-32q8kv-b8-ctx32769 via decode")
+    g, w = _sampled(wl, "decode", [0, 3, 7], lambda s: np.array([wl.q_indptr[s]]))
+    compare(g, w, "long-decode")
+
+
+def test_mixed_70b_batch():
+    wl = make("mixed-64q8kv-4p96d")
+    say("mixed-64q8kv-4p96d via prefill (one call)")
+
+    def rows(s):
+        q0, q1 = wl.q_indptr[s], wl.q_indptr[s + 1]
+        if q1 - q0 == 1:
+            return np.array([q0])
+        return q0 + np.array([0, 31, 32, 255, 256, 511])
+    g, w = _sampled(wl, "prefill", [0, 3, 4, 50, 99], rows)
+    compare(g, w, "mixed")
