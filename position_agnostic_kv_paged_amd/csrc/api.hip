@@ -11,7 +11,7 @@ using namespace lazyattn;
 
 namespace {
 
-constexpr int kTargetDecodeWaves = 4096;   // split-K target: ~16 waves per CU
+constexpr long long kTargetDecodeItems = 16384;   // ~8 (row-split, kv-head) items per resident wave
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -23,22 +23,27 @@ bool shape_ok(int32_t Hq, int32_t Hkv, int32_t D, int32_t B) {
   return G == 1 || G == 2 || G == 4 || G == 8;
 }
 
-// Split-K factor of a decode row: enough (row, kv-head, split) waves to fill the GPU,
-// at least ~8 blocks per split.
-int decode_splits(int rows_bound, int Hkv, int max_entries) {
-  long long pairs = (long long)(rows_bound > 0 ? rows_bound : 1) * Hkv;
-  long long s = (kTargetDecodeWaves + pairs - 1) / pairs;
-  long long cap = (max_entries + 7) / 8;
-  if (cap < 1) cap = 1;
-  if (s > cap) s = cap;
-  if (s > 256) s = 256;
-  if (s < 1) s = 1;
-  return (int)s;
+// Decode split size (blocks, even): enough (row-split, kv-head) items to balance the
+// persistent waves' queue, 4 .. 64 blocks per item.
+struct DecodeSplit {
+  int bps, smax;
+};
+DecodeSplit decode_split(int rows_bound, int Hkv, int max_entries) {
+  const long long work = (long long)(rows_bound > 0 ? rows_bound : 1) * Hkv *
+                         (max_entries > 0 ? max_entries : 1);
+  long long b = (work + kTargetDecodeItems - 1) / kTargetDecodeItems;
+  if (b < 4) b = 4;
+  if (b > 64) b = 64;
+  b += b & 1;
+  DecodeSplit d;
+  d.bps = (int)b;
+  d.smax = max_entries > 0 ? (int)((max_entries + b - 1) / b) : 1;
+  return d;
 }
 
 size_t workspace_for(int num_seqs, int rows_bound, int max_entries, int Hq, int Hkv, int D) {
-  const int S = decode_splits(rows_bound, Hkv, max_entries);
-  return ws_layout(num_seqs, (long long)rows_bound * S, Hq, D).total;
+  const DecodeSplit ds = decode_split(rows_bound, Hkv, max_entries);
+  return ws_layout(num_seqs, (long long)rows_bound * ds.smax, Hq, D).total;
 }
 
 int run(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_table,
@@ -65,10 +70,12 @@ int run(const void* q, const void* k_pool, const void* v_pool, const int32_t* bl
 
   hipStream_t st = (hipStream_t)stream;
   const int G = Hq / Hkv;
-  const int S = decode_splits(rows_bound, Hkv, max_entries);
-  const WsLayout L = ws_layout(num_seqs, (long long)rows_bound * S, Hq, D);
+  const DecodeSplit ds = decode_split(rows_bound, Hkv, max_entries);
+  const WsLayout L = ws_layout(num_seqs, (long long)rows_bound * ds.smax, Hq, D);
   char* ws = (char*)workspace;
   double* freqs = (double*)(ws + L.off_freqs);
+  int32_t* counter = (int32_t*)(ws + L.off_counter);
+  uint32_t* zero = (uint32_t*)(ws + L.off_zero);
   int32_t* pf_prefix = (int32_t*)(ws + L.off_pf_prefix);
   int32_t* dec_prefix = (int32_t*)(ws + L.off_dec_prefix);
   float* partials = (float*)(ws + L.off_partials);
@@ -78,26 +85,27 @@ int run(const void* q, const void* k_pool, const void* v_pool, const int32_t* bl
     fr.f[k] = std::pow(rope_base, -2.0 * k / D) / (2.0 * M_PI);
   const float scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
 
-  PlanParams pp{q_indptr, block_table, freqs, pf_prefix, dec_prefix, num_seqs,
-                prefill_positions_per_tile(G), S, mode, D / 2, fr};
+  PlanParams pp{q_indptr, block_table, freqs, pf_prefix, dec_prefix, counter, zero, num_seqs,
+                prefill_positions_per_tile(G), ds.bps, ds.smax, mode, D / 2, fr};
   if (launch_plan(pp, st) != hipSuccess) return LAZYATTN_ERR_LAUNCH;
 
   if (mode == kPlanMixed) {
-    PrefillParams P{(const uint16_t*)q, (const uint16_t*)k_pool, (const uint16_t*)v_pool,
-                    block_table, block_meta, kv_lens, q_indptr, q_positions,
-                    (uint16_t*)out, pf_prefix, num_seqs, Hq, Hkv, num_blocks, scale_log2, freqs};
     const int pos = prefill_positions_per_tile(G);
     const long long tiles = ((long long)total_q + pos - 1) / pos + num_seqs;
-    if (tiles > INT32_MAX) return LAZYATTN_ERR_SHAPE;
-    if (launch_prefill(P, D, G, (int)tiles, true, st) != hipSuccess) return LAZYATTN_ERR_LAUNCH;
+    if (tiles * Hkv > INT32_MAX / 2) return LAZYATTN_ERR_SHAPE;
+    PrefillParams P{(const uint16_t*)q, (const uint16_t*)k_pool, (const uint16_t*)v_pool,
+                    block_table, block_meta, kv_lens, q_indptr, q_positions,
+                    (uint16_t*)out, pf_prefix, (const uint16_t*)zero, num_seqs, Hq, Hkv,
+                    num_blocks, (int)tiles, scale_log2, freqs};
+    if (launch_prefill(P, D, G, true, st) != hipSuccess) return LAZYATTN_ERR_LAUNCH;
   }
   DecodeParams Dp{(const uint16_t*)q, (const uint16_t*)k_pool, (const uint16_t*)v_pool,
                   block_table, block_meta, kv_lens, q_indptr, q_positions, dec_prefix,
-                  partials, num_seqs, Hq, Hkv, num_blocks, S, scale_log2, freqs};
-  if (launch_decode(Dp, D, G, (long long)rows_bound * S, st) != hipSuccess)
-    return LAZYATTN_ERR_LAUNCH;
+                  counter, (const uint16_t*)zero, partials, num_seqs, Hq, Hkv, num_blocks,
+                  ds.bps, ds.smax, scale_log2, freqs};
+  if (launch_decode(Dp, D, G, st) != hipSuccess) return LAZYATTN_ERR_LAUNCH;
   MergeParams Mp{q_indptr, block_table, dec_prefix, partials, (uint16_t*)out,
-                 num_seqs, Hq, S, mode};
+                 num_seqs, Hq, ds.bps, ds.smax, mode};
   if (launch_merge(Mp, total_q, D, st) != hipSuccess) return LAZYATTN_ERR_LAUNCH;
   return LAZYATTN_OK;
 }

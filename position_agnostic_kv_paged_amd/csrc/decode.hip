@@ -10,20 +10,27 @@
 // position off_t + j. The score of a query at p is
 //   <R(p) q, R(off_t + j) k> = <R(p - off_t) q, R(j) k>.
 // R(j), j < 16, is a per-lane constant (lane = slot), so keys are rotated with loop-invariant
-// cos/sin; q' = R(p - off_t) q changes by the constant R(-16) from one block to the next
-// while delta stays constant, and is recomputed exactly (double-precision phase) only
-// where delta changes and at the start of each split.
+// cos/sin. q' = R(p - off_t) q is carried in the 16 columns of a 16x16x32 MFMA as
+// (head g, block phase ph) pairs: a group of two consecutive blocks is scored against
+// R(p - off_t0) q and R(p - off_t0 - 16) q at once, and from one group to the next (delta
+// unchanged) every column advances by the constant R(-32); where delta changes (a document
+// boundary) and at the start of each work item q' is recomputed exactly from the
+// double-precision phase.
 //
-// One wave per (query row, KV head, split); G query heads are the columns of 16x16x32 bf16
-// MFMAs: S^T = K~ q'^T per block, O^T += V^T P^T per pair of blocks (V staged in the
-// wave's own LDS slice, transposed on read). Partial (m, l, o) per split go to the
-// workspace; merge_kernel combines them.
+// Work: a persistent grid of waves takes (row-split, kv-head) items from an atomic queue
+// (balanced tail). Keys are prefetched one group ahead into registers; values go straight
+// from global memory into a double-buffered, XOR-swizzled LDS slice of the wave
+// (global_load_lds) and are read back transposed (ds_read_b64_tr_b16) as the A operand of
+// O^T += V^T P^T. Rows that must contribute nothing (padding, missing blocks) are fetched
+// from a zeroed workspace chunk so that 0 * NaN never enters the sum. Each item writes a
+// partial (o, m, l); merge_kernel combines the splits of a row.
 #include "lazyattn_common.h"
 #include "lazyattn_kernels.h"
 
 namespace lazyattn {
 
-constexpr int kDecodeWaves = 4;
+constexpr int kDecodeWaves = 4;        // waves per workgroup
+constexpr int kDecodeWgPerCu = 4;      // workgroups launched per CU (residency set by VGPRs)
 
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -31,93 +38,154 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// 16-byte global -> LDS copy: lane l writes lds_wave_base + 16 l (the base is wave-uniform).
+__device__ __forceinline__ void g2lds16(const void* g, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base,
+                                   16, 0, 0);
+}
+
+// LDS layout of a group's values (32 rows of D bf16): 16-byte chunk c of row R sits at chunk
+// position c ^ swz(R), so the four rows read by one 16-lane transposed read hit disjoint banks.
+__device__ __forceinline__ int vswz(int R) { return (R & 3) * 2; }
+
+struct GroupMeta {
+  int id[2], delta[2], nval[2];
+};
+
 template <int D, int G>
-__global__ __launch_bounds__(kDecodeWaves * 64) void decode_kernel(DecodeParams P) {
-  constexpr int NC = D / 32;                  // 32-dim k-steps (16x16x32)
+__global__ __launch_bounds__(kDecodeWaves * 64, 2) void decode_kernel(DecodeParams P) {
+  constexpr int NC = D / 32;                  // 32-dim k-steps of the score MFMA
   constexpr int HC = NC / 2;                  // chunk c pairs with chunk c + HC (dims + D/2)
-  constexpr int VS = D + 16;                  // LDS row stride (bf16 elements)
-  constexpr int VCH = D / 8;                  // 16-byte chunks per value row
-  __shared__ __align__(16) uint16_t Vs_all[kDecodeWaves][32 * VS];
+  constexpr int ROWB = D * 2;                 // bytes per value row
+  constexpr int BUF = 32 * ROWB;              // one group: 2 blocks x 16 rows
+  constexpr int LOADS = BUF / 1024;           // global_load_lds instructions per group
+  __shared__ __align__(16) uint8_t lds_all[kDecodeWaves][2][BUF];
+  // R(32) of every frequency: (cos, sin) interleaved, shared by the workgroup
+  __shared__ __align__(16) float adv_all[D];
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  uint16_t* Vs = Vs_all[w];
-  const long long item = (long long)blockIdx.x * kDecodeWaves + w;
-  const int kvh = blockIdx.y;
-  if (item >= P.dec_prefix[P.num_seqs]) return;      // per wave; no workgroup barriers below
-  const int it = (int)item;
-  const int seq = upper_seq(P.dec_prefix, P.num_seqs, it);
-  const int local = it - P.dec_prefix[seq];
-  const int q0 = P.q_indptr[seq];
-  const int e0 = P.block_table[seq], T = P.block_table[seq + 1] - e0;
-  const int kvlen = P.kv_lens[seq];
-  int splits = T < P.splits ? T : P.splits;
-  if (splits < 1) splits = 1;
-  const int row = local / splits, sp = local % splits;
-  const int bps = (T + splits - 1) / splits;
-  const int eb = sp * bps;
-  const int ee = min(T, eb + bps);
-  const int r = q0 + row;
-  const int p = P.q_pos[r];
-
+  uint8_t* lds = lds_all[w][0];
   const int i16 = lane & 15, q4 = lane >> 4;
-  const bool head_ok = i16 < G;
-  const int h = kvh * G + (head_ok ? i16 : 0);
+  const int col = i16, g = col % G, ph = col / G;
+  const bool col_ok = col < 2 * G;
 
-  // lane's frequencies: k = 32c + 8 q4 + e for c < HC, e < 8 (same set for K and q')
-  // R(j) with j = i16 (slot of this lane's key row) and R(16)
-  float cj[HC][8], sj[HC][8], c16[HC][8], s16[HC][8];
+  // loop-invariant rotation constants of this lane's frequencies k = 32c + 8 q4 + e:
+  // R(i16) for its key row in registers; R(32) for the per-group advance of q' in LDS
+  float cj[HC][8], sj[HC][8];
 #pragma unroll
   for (int c = 0; c < HC; ++c)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const double f = P.freqs[32 * c + 8 * q4 + e];
-      rope_cos_sin(i16, f, cj[c][e], sj[c][e]);
-      rope_cos_sin(16, f, c16[c][e], s16[c][e]);
-    }
-  const uint16_t* qrow = P.q + ((size_t)r * P.Hq + h) * D;
+    for (int e = 0; e < 8; ++e)
+      rope_cos_sin(i16, P.freqs[32 * c + 8 * q4 + e], cj[c][e], sj[c][e]);
+  if (threadIdx.x < D / 2) {
+    float cs, sn;
+    rope_cos_sin(32, P.freqs[threadIdx.x], cs, sn);
+    adv_all[2 * threadIdx.x] = cs;
+    adv_all[2 * threadIdx.x + 1] = sn;
+  }
+  __syncthreads();
 
-  float qr[NC][8];                 // q' = R(p - off_t) q in fp32
-  u32x4 qb[NC];                    // fp16 B operand of q'
-  int cur_delta = 0;
-  bool anchored = false;
+  const int n_items = P.dec_prefix[P.num_seqs] * P.Hkv;
+  for (;;) {
+    int it = 0;
+    if (lane == 0) it = atomicAdd(P.counter, 1);
+    it = __shfl(it, 0);
+    if (it >= n_items) break;
+    const int rs = it / P.Hkv, kvh = it % P.Hkv;
+    const int seq = upper_seq(P.dec_prefix, P.num_seqs, rs);
+    const int local = rs - P.dec_prefix[seq];
+    const int q0 = P.q_indptr[seq];
+    const int e0 = P.block_table[seq], T = P.block_table[seq + 1] - e0;
+    const int kvlen = P.kv_lens[seq];
+    const int splits = row_splits(T, P.bps, P.smax);
+    const int bpsr = row_bps(T, P.bps, P.smax);
+    const int row = local / splits, sp = local % splits;
+    const int eb = sp * bpsr;
+    const int ee = min(T, eb + bpsr);
+    const int r = q0 + row;
+    const int p = P.q_pos[r];
+    const int h = kvh * G + g;
+    const uint16_t* qrow = P.q + ((size_t)r * P.Hq + h) * D;
 
-  float m = -INFINITY, l = 0.f;
-  f32x4 o[D / 16];
+    float m = -INFINITY, l = 0.f;
+    f32x4 o[D / 16];
 #pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4{};
+    for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4{};
+    float qr[NC][8];
+    bool have_q = false;
+    int cur_delta = 0;
 
-  for (int t0 = eb; t0 < ee; t0 += 2) {
-    f32x4 sc[2];
+    // issue the loads of the group starting at entry t0 into LDS buffer `buf`
+    auto issue = [&](int t0, int buf, u32x4 (&kreg)[2][NC], GroupMeta& gm) {
 #pragma unroll
-    for (int bb = 0; bb < 2; ++bb) {
-      const int t = t0 + bb;
-      sc[bb] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-      const bool blk = t < ee;
-      const uint32_t wd = blk ? P.block_meta[e0 + t] : 0u;
-      const int id = word_id(wd), delta = word_delta(wd);
-      const int off = t * kBlock + delta;
-      const int rem = kvlen - t * kBlock;
-      const int nval = (blk && id < P.num_blocks) ? (rem < kBlock ? (rem > 0 ? rem : 0) : kBlock)
-                                                  : 0;
-      const size_t base = ((size_t)id * P.Hkv + kvh) * kBlock;
-      // value rows -> LDS slice rows 16*bb .. 16*bb+15 (zero where the slot is not valid)
+      for (int b = 0; b < 2; ++b) {
+        const int t = t0 + b;
+        const bool blk = t < ee;
+        const uint32_t wd = blk ? P.block_meta[e0 + t] : 0u;
+        const int id = word_id(wd);
+        const int rem = kvlen - t * kBlock;
+        gm.id[b] = id;
+        gm.delta[b] = word_delta(wd);
+        gm.nval[b] = (blk && id < P.num_blocks) ? (rem < kBlock ? (rem > 0 ? rem : 0) : kBlock) : 0;
+        const size_t base = ((size_t)id * P.Hkv + kvh) * kBlock;
 #pragma unroll
-      for (int u0 = 0; u0 < 16 * VCH; u0 += 64) {
-        const int u = u0 + lane;
-        const int j = u / VCH, c8 = u % VCH;
-        u32x4 v = {0, 0, 0, 0};
-        if (j < nval) v = *(const u32x4*)(P.v_pool + (base + j) * D + 8 * c8);
-        *(u32x4*)(Vs + (16 * bb + j) * VS + 8 * c8) = v;
+        for (int c = 0; c < NC; ++c)
+          kreg[b][c] = i16 < gm.nval[b]
+                           ? *(const u32x4*)(P.k_pool + (base + i16) * D + 32 * c + 8 * q4)
+                           : u32x4{0, 0, 0, 0};
       }
-      if (!blk) continue;                      // uniform
-      // q' for this block: exact re-anchor on a delta change, else advance by R(-16)
-      if (!anchored || delta != cur_delta) {
-        const int n = p - off;
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        const int off = i * 1024 + 16 * lane;
+        const int R = off / ROWB, cs = (off % ROWB) / 16;
+        const int b = R >> 4, j = R & 15;
+        const int c = cs ^ vswz(R);
+        const void* src = P.zero;
+        if (j < gm.nval[b])
+          src = P.v_pool + (((size_t)gm.id[b] * P.Hkv + kvh) * kBlock + j) * D + 8 * c;
+        g2lds16(src, lds + buf * BUF + i * 1024);
+      }
+    };
+
+    u32x4 kcur[2][NC], knext[2][NC];
+    GroupMeta gcur, gnext;
+    int buf = 0;
+    if (eb < ee) issue(eb, 0, knext, gnext);
+    for (int t0 = eb; t0 < ee; t0 += 2) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);       // vmcnt(0): this group's keys and values
+      asm volatile("" ::: "memory");
+      wave_sync();
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) kcur[b][c] = knext[b][c];
+      gcur = gnext;
+      if (t0 + 2 < ee) issue(t0 + 2, buf ^ 1, knext, gnext);
+
+      // ---- q' of this lane's column: R(p - off_{t0+ph}) q_g ---------------------------
+      const int d0 = gcur.delta[0];
+      const int d1 = (t0 + 1 < ee) ? gcur.delta[1] : d0;
+      if (have_q && d0 == cur_delta && d1 == cur_delta) {
+#pragma unroll
+        for (int c = 0; c < HC; ++c)
+#pragma unroll
+          for (int e2 = 0; e2 < 4; ++e2) {           // R(-32)
+            const f32x4 cs = *(const f32x4*)(adv_all + 2 * (32 * c + 8 * q4 + 2 * e2));
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              const int e = 2 * e2 + u;
+              const float a = qr[c][e], b = qr[c + HC][e];
+              qr[c][e] = a * cs[2 * u] + b * cs[2 * u + 1];
+              qr[c + HC][e] = b * cs[2 * u] - a * cs[2 * u + 1];
+            }
+          }
+      } else {
+        const int n = p - ((t0 + ph) * kBlock + (ph ? d1 : d0));
 #pragma unroll
         for (int c = 0; c < HC; ++c) {
-          const u32x4 va = head_ok ? *(const u32x4*)(qrow + 32 * c + 8 * q4) : u32x4{0, 0, 0, 0};
-          const u32x4 vb = head_ok ? *(const u32x4*)(qrow + 32 * (c + HC) + 8 * q4)
-                                   : u32x4{0, 0, 0, 0};
+          const u32x4 va = col_ok ? *(const u32x4*)(qrow + 32 * c + 8 * q4) : u32x4{0, 0, 0, 0};
+          const u32x4 vb = col_ok ? *(const u32x4*)(qrow + 32 * (c + HC) + 8 * q4)
+                                  : u32x4{0, 0, 0, 0};
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             float cs, sn;
@@ -128,103 +196,113 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_kernel(DecodeParams 
             qr[c + HC][e] = a * sn + b * cs;
           }
         }
-        anchored = true;
-        cur_delta = delta;
-      } else {
-#pragma unroll
-        for (int c = 0; c < HC; ++c)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {   // R(-16): angle -16 theta_k
-            const float a = qr[c][e], b = qr[c + HC][e];
-            qr[c][e] = a * c16[c][e] + b * s16[c][e];
-            qr[c + HC][e] = b * c16[c][e] - a * s16[c][e];
-          }
+        have_q = (d0 == d1);
+        cur_delta = d1;
       }
-#pragma unroll
-      for (int c = 0; c < NC; ++c)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) qb[c][i] = pack_f16(qr[c][2 * i], qr[c][2 * i + 1]);
-
-      // keys of this block: lane row = slot i16, dims 32c + 8 q4 + e, rotated by R(i16)
-      u32x4 kr[NC];
-#pragma unroll
-      for (int c = 0; c < NC; ++c)
-        kr[c] = i16 < nval ? *(const u32x4*)(P.k_pool + (base + i16) * D + 32 * c + 8 * q4)
-                           : u32x4{0, 0, 0, 0};
-      f32x4 acc = f32x4{};
+      // ---- scores of both blocks; each lane keeps its own phase's block ------------------
+      f32x4 S[2] = {f32x4{}, f32x4{}};
 #pragma unroll
       for (int c = 0; c < HC; ++c) {
-        u32x4 lo, hi;
+        u32x4 qlo, qhi;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float a0 = bf_lo(kr[c][i]), a1 = bf_hi(kr[c][i]);
-          const float b0 = bf_lo(kr[c + HC][i]), b1 = bf_hi(kr[c + HC][i]);
-          const float c0 = cj[c][2 * i], s0 = sj[c][2 * i], c1 = cj[c][2 * i + 1], s1 = sj[c][2 * i + 1];
-          lo[i] = pack_f16(a0 * c0 - b0 * s0, a1 * c1 - b1 * s1);
-          hi[i] = pack_f16(a0 * s0 + b0 * c0, a1 * s1 + b1 * c1);
+          qlo[i] = pack_f16(qr[c][2 * i], qr[c][2 * i + 1]);
+          qhi[i] = pack_f16(qr[c + HC][2 * i], qr[c + HC][2 * i + 1]);
         }
-        acc = mfma16h(as_f16x8(lo), as_f16x8(qb[c]), acc);
-        acc = mfma16h(as_f16x8(hi), as_f16x8(qb[c + HC]), acc);
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          u32x4 lo, hi;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float a0 = bf_lo(kcur[b][c][i]), a1 = bf_hi(kcur[b][c][i]);
+            const float b0 = bf_lo(kcur[b][c + HC][i]), b1 = bf_hi(kcur[b][c + HC][i]);
+            const float c0 = cj[c][2 * i], s0 = sj[c][2 * i];
+            const float c1 = cj[c][2 * i + 1], s1 = sj[c][2 * i + 1];
+            lo[i] = pack_f16(a0 * c0 - b0 * s0, a1 * c1 - b1 * s1);
+            hi[i] = pack_f16(a0 * s0 + b0 * c0, a1 * s1 + b1 * c1);
+          }
+          S[b] = mfma16h(as_f16x8(lo), as_f16x8(qlo), S[b]);
+          S[b] = mfma16h(as_f16x8(hi), as_f16x8(qhi), S[b]);
+        }
       }
-      // acc[i]: slot 4 q4 + i, head column i16
+      const int nv = ph ? gcur.nval[1] : gcur.nval[0];
+      const int offp = (t0 + ph) * kBlock + (ph ? d1 : d0);
+      float sc[4];
+      float mx = -INFINITY;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int j = 4 * q4 + i;
-        const bool ok = j < nval && off + j <= p;
-        sc[bb][i] = ok ? acc[i] * P.scale_log2 : -INFINITY;
+        const float v = ph ? S[1][i] : S[0][i];
+        const bool ok = col_ok && j < nv && offp + j <= p;
+        sc[i] = ok ? v * P.scale_log2 : -INFINITY;
+        mx = fmaxf(mx, sc[i]);
       }
-    }
-    // online softmax over the 8 scores of this lane's head; row max across the 4 slot groups
-    float mx = -INFINITY;
+      // row max over the 8 lanes of head g: slot groups (q4) and both phases
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = fmaxf(mx, __shfl_xor(mx, G));
+      const float m_new = fmaxf(m, mx);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = exp2f(m - m_use);
+      float pr[4];
+      float rsum = 0.f;
 #pragma unroll
-    for (int bb = 0; bb < 2; ++bb)
+      for (int i = 0; i < 4; ++i) { pr[i] = exp2f(sc[i] - m_use); rsum += pr[i]; }
+      l = l * alpha + rsum;
+      m = m_new;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[bb][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = exp2f(m - m_use);
-    float pr[2][4];
-    float rs = 0.f;
-#pragma unroll
-    for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) { pr[bb][i] = exp2f(sc[bb][i] - m_use); rs += pr[bb][i]; }
-    l = l * alpha + rs;
-    m = m_new;
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) o[dt] *= alpha;
+      for (int dt = 0; dt < D / 16; ++dt) o[dt] *= alpha;
+      const uint32_t p01 = pack_bf16(pr[0], pr[1]), p23 = pack_bf16(pr[2], pr[3]);
+      const u32x4 bp = ph ? u32x4{0u, 0u, p01, p23} : u32x4{p01, p23, 0u, 0u};
 
-    const u32x4 bp = {pack_bf16(pr[0][0], pr[0][1]), pack_bf16(pr[0][2], pr[0][3]),
-                      pack_bf16(pr[1][0], pr[1][1]), pack_bf16(pr[1][2], pr[1][3])};
-    wave_sync();                                 // value rows written by other lanes
+      // ---- O^T += V^T P^T over the group's 32 keys ------------------------------------------
+      const uint8_t* vb = lds + buf * BUF;
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) {
-      const int n0 = 16 * dt + 4 * (i16 & 3);
-      const u32x2 r1 = lds_read_tr(Vs + (4 * q4 + (i16 >> 2)) * VS + n0);
-      const u32x2 r2 = lds_read_tr(Vs + (16 + 4 * q4 + (i16 >> 2)) * VS + n0);
-      const u32x4 a = {r1[0], r1[1], r2[0], r2[1]};
-      o[dt] = mfma16(as_bf16x8(a), as_bf16x8(bp), o[dt]);
+      for (int dt = 0; dt < D / 16; ++dt) {
+        const int x = 16 * dt + 4 * (i16 & 3);
+        const int cchunk = x >> 3, half = (x >> 2) & 1;
+        const int R1 = 4 * q4 + (i16 >> 2), R2 = 16 + R1;
+        const u32x2 r1 = lds_read_tr(
+            (const uint16_t*)(vb + R1 * ROWB + 16 * (cchunk ^ vswz(R1)) + 8 * half));
+        const u32x2 r2 = lds_read_tr(
+            (const uint16_t*)(vb + R2 * ROWB + 16 * (cchunk ^ vswz(R2)) + 8 * half));
+        const u32x4 a = {r1[0], r1[1], r2[0], r2[1]};
+        o[dt] = mfma16(as_bf16x8(a), as_bf16x8(bp), o[dt]);
+      }
+      buf ^= 1;
     }
-    wave_sync();                                 // before the next pair overwrites the slice
-  }
+    wave_sync();
 
-  // partial (o, m, l) of this split: lane holds head i16, dims 16 dt + 4 q4 + (0..3)
-  float lt = l + __shfl_xor(l, 16);
-  lt += __shfl_xor(lt, 32);
-  if (head_ok) {
-    float* part = P.partials + ((size_t)item * P.Hq + h) * (D + 4);
+    // ---- partial of this item: add both phases of head g -----------------------------------
+    float lt = l + __shfl_xor(l, 16);
+    lt += __shfl_xor(lt, 32);
+    lt += __shfl_xor(lt, G);
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) *(f32x4*)(part + 16 * dt + 4 * q4) = o[dt];
-    if (q4 == 0) { part[D] = m; part[D + 1] = lt; }
+    for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[dt][i] += __shfl_xor(o[dt][i], G);
+    if (col < G) {
+      float* part = P.partials + ((size_t)rs * P.Hq + h) * (D + 4);
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) *(f32x4*)(part + 16 * dt + 4 * q4) = o[dt];
+      if (q4 == 0) { part[D] = m; part[D + 1] = lt; }
+    }
   }
 }
 
+static int g_num_cus = 0;
+
 template <int D>
-static hipError_t launch_d(const DecodeParams& p, int G, long long grid_items, hipStream_t st) {
-  dim3 grid((unsigned)((grid_items + kDecodeWaves - 1) / kDecodeWaves), p.Hkv);
-  dim3 block(kDecodeWaves * 64);
+static hipError_t launch_d(const DecodeParams& p, int G, hipStream_t st) {
+  if (g_num_cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    g_num_cus = n;
+  }
+  dim3 grid(g_num_cus * kDecodeWgPerCu), block(kDecodeWaves * 64);
   switch (G) {
     case 1: hipLaunchKernelGGL((decode_kernel<D, 1>), grid, block, 0, st, p); break;
     case 2: hipLaunchKernelGGL((decode_kernel<D, 2>), grid, block, 0, st, p); break;
@@ -235,10 +313,8 @@ static hipError_t launch_d(const DecodeParams& p, int G, long long grid_items, h
   return hipGetLastError();
 }
 
-hipError_t launch_decode(const DecodeParams& p, int D, int G, long long grid_items,
-                         hipStream_t st) {
-  if (grid_items <= 0) return hipSuccess;
-  return D == 128 ? launch_d<128>(p, G, grid_items, st) : launch_d<64>(p, G, grid_items, st);
+hipError_t launch_decode(const DecodeParams& p, int D, int G, hipStream_t st) {
+  return D == 128 ? launch_d<128>(p, G, st) : launch_d<64>(p, G, st);
 }
 
 }  // namespace lazyattn

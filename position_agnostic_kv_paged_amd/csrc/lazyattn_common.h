@@ -113,22 +113,40 @@ __device__ __forceinline__ int upper_seq(const int32_t* prefix, int n, int x) {
 
 // ---- workspace layout -----------------------------------------------------------------------
 // [0, 512)                RoPE frequency table, double [64] (revolutions per position)
-// [512, ...)              prefix arrays: prefill tiles, decode items, each num_seqs + 1 int32
-// aligned 256             split-K partials: float [items][Hq][D + 4]  (o[D], m, l, -, -)
+// [512, 768)              int32 decode work-queue counter at 512; 16-byte zero rows at 576..767
+// [768, ...)              prefix arrays: prefill tiles, decode row-splits, each num_seqs + 1 int32
+// aligned 256             split-K partials: float [row-splits][Hq][D + 4]  (o[D], m, l, -, -)
 struct WsLayout {
-  size_t off_freqs, off_pf_prefix, off_dec_prefix, off_partials, total;
+  size_t off_freqs, off_counter, off_zero, off_pf_prefix, off_dec_prefix, off_partials, total;
 };
 
 __host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-__host__ __device__ inline WsLayout ws_layout(int num_seqs, long long max_items, int Hq, int D) {
+__host__ __device__ inline WsLayout ws_layout(int num_seqs, long long max_rowsplits, int Hq, int D) {
   WsLayout L;
   L.off_freqs = 0;
-  L.off_pf_prefix = 512;
+  L.off_counter = 512;
+  L.off_zero = 576;
+  L.off_pf_prefix = 768;
   L.off_dec_prefix = align_up(L.off_pf_prefix + 4ull * (num_seqs + 1), 256);
   L.off_partials = align_up(L.off_dec_prefix + 4ull * (num_seqs + 1), 256);
-  L.total = L.off_partials + (size_t)max_items * Hq * (D + 4) * 4ull;
+  L.total = L.off_partials + (size_t)max_rowsplits * Hq * (D + 4) * 4ull;
   return L;
+}
+
+// Split-K of a decode row with T block-table entries: the host picks a base split size
+// `bps` (even) and a cap `smax` on splits per row; a sequence longer than the caller's
+// max_entries bound gets larger splits instead of more, so the partial buffer sized from
+// smax is never exceeded.
+__host__ __device__ inline int row_bps(int T, int bps, int smax) {
+  int need = (T + smax - 1) / smax;
+  need += need & 1;
+  return need > bps ? need : bps;
+}
+__host__ __device__ inline int row_splits(int T, int bps, int smax) {
+  if (T <= 0) return 1;
+  const int b = row_bps(T, bps, smax);
+  return (T + b - 1) / b;
 }
 
 // Plan modes.

@@ -10,10 +10,12 @@ struct PlanParams {
   const int32_t* block_table;
   double* freqs_out;         // [D/2] workspace copy of the frequency table
   int32_t* pf_prefix;        // [num_seqs + 1] prefill tiles
-  int32_t* dec_prefix;       // [num_seqs + 1] decode items (row, split)
+  int32_t* dec_prefix;       // [num_seqs + 1] decode row-splits
+  int32_t* counter;          // decode work queue (zeroed here)
+  uint32_t* zero;            // 192 bytes set to zero here
   int num_seqs;
   int pos_per_tile;          // query positions per prefill tile
-  int splits;                // maximum split-K factor of a decode row
+  int bps, smax;             // decode split size (blocks) and splits-per-row cap
   int mode;                  // PlanMode
   int half_dim;
   RopeFreqs fr;              // host-computed table (kernel argument)
@@ -30,7 +32,9 @@ struct PrefillParams {
   const int32_t* q_pos;
   uint16_t* out;
   const int32_t* pf_prefix;
+  const uint16_t* zero;      // zero bytes: source of V rows that must read as 0
   int num_seqs, Hq, Hkv, num_blocks;
+  int tiles_bound;           // upper bound of prefill tiles per KV head (grid sizing)
   float scale_log2;          // log2(e) / sqrt(D)
   const double* freqs;       // [D/2] RoPE frequencies (revolutions per position)
 };
@@ -45,8 +49,10 @@ struct DecodeParams {
   const int32_t* q_indptr;
   const int32_t* q_pos;
   const int32_t* dec_prefix;
-  float* partials;           // [items][Hq][D + 4]
-  int num_seqs, Hq, Hkv, num_blocks, splits;
+  int32_t* counter;          // work queue over (row-split, kv-head) items
+  const uint16_t* zero;      // zero bytes: source of V rows that must read as 0
+  float* partials;           // [row-splits][Hq][D + 4]
+  int num_seqs, Hq, Hkv, num_blocks, bps, smax;
   float scale_log2;
   const double* freqs;
 };
@@ -57,18 +63,16 @@ struct MergeParams {
   const int32_t* dec_prefix;
   const float* partials;
   uint16_t* out;
-  int num_seqs, Hq, splits, mode;
+  int num_seqs, Hq, bps, smax, mode;
 };
 
 hipError_t launch_plan(const PlanParams& p, hipStream_t st);
 hipError_t launch_merge(const MergeParams& p, int total_q, int D, hipStream_t st);
 hipError_t launch_debug_decode(const uint32_t* words, const int32_t* bt, int num_seqs, int n,
                                int32_t* ids, int32_t* offs, hipStream_t st);
-// grid_tiles: upper bound of prefill tiles (extra workgroups exit at once)
-hipError_t launch_prefill(const PrefillParams& p, int D, int G, int grid_tiles, bool rotate,
-                          hipStream_t st);
+// p.tiles_bound: upper bound of prefill tiles (extra workgroups exit at once)
+hipError_t launch_prefill(const PrefillParams& p, int D, int G, bool rotate, hipStream_t st);
 int prefill_positions_per_tile(int G);
-hipError_t launch_decode(const DecodeParams& p, int D, int G, long long grid_items,
-                         hipStream_t st);
+hipError_t launch_decode(const DecodeParams& p, int D, int G, hipStream_t st);
 
 }  // namespace lazyattn

@@ -8,17 +8,13 @@
 
 namespace lazyattn {
 
-__device__ __forceinline__ int decode_splits(int T, int S) {
-  int s = T < S ? T : S;
-  return s < 1 ? 1 : s;
-}
-
 // One workgroup of 1024 threads; chunked exclusive scan over sequences.
 __global__ __launch_bounds__(1024) void plan_kernel(PlanParams P) {
   __shared__ int sa[1024], sb[1024];
   __shared__ int carry_a, carry_b;
   const int tid = threadIdx.x;
-  if (tid == 0) { carry_a = 0; carry_b = 0; }
+  if (tid == 0) { carry_a = 0; carry_b = 0; *P.counter = 0; }
+  if (tid < 48) P.zero[tid] = 0u;
 #pragma unroll
   for (int i = 0; i < kMaxHalfDim; ++i)
     if (tid == i && i < P.half_dim) P.freqs_out[i] = P.fr.f[i];
@@ -30,7 +26,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanParams P) {
       const int qlen = P.q_indptr[s + 1] - P.q_indptr[s];
       const int T = P.block_table[s + 1] - P.block_table[s];
       const bool dec = (P.mode == kPlanDecodeOnly) || qlen == 1;
-      if (dec) b = qlen * decode_splits(T, P.splits);
+      if (dec) b = qlen * row_splits(T, P.bps, P.smax);
       else a = (qlen + P.pos_per_tile - 1) / P.pos_per_tile;
     }
     sa[tid] = a; sb[tid] = b;
@@ -71,7 +67,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams P) {
   const bool dec = (P.mode == kPlanDecodeOnly) || qlen == 1;
   if (!dec) return;                           // written by the prefill kernel
   const int T = P.block_table[seq + 1] - P.block_table[seq];
-  const int splits = decode_splits(T, P.splits);
+  const int splits = row_splits(T, P.bps, P.smax);
   const long long item0 = (long long)P.dec_prefix[seq] + (long long)(r - q0) * splits;
   float M = -INFINITY;
   for (int s = 0; s < splits; ++s) {

@@ -1,4 +1,4 @@
-// LazyAttention prefill kernel for gfx950 (bf16 MFMA, online softmax).
+// LazyAttention prefill kernel for gfx950 (MFMA, online softmax, pipelined key tiles).
 //
 // Technical summary of LazyAttention (arXiv 2606.04302), "Technical Implementation",
 // prefilling phase: cached KV blocks are loaded from the position-free cache and, instead
@@ -8,14 +8,23 @@
 //   <R(p) q, R(L) k> = <R(p - p_ref) q, R(L - p_ref) k>
 // for any reference position p_ref; the kernel takes p_ref = the tile's first query
 // position, rotates the tile's queries by R(p - p_ref) once, and rotates each staged key by
-// R(L - p_ref) once per (query tile, key tile) -- the key rotation is shared by all
-// 32 * NW rows of the workgroup tile, which is what keeps it a small overhead.
+// R(L - p_ref) once per (query tile, key tile) -- shared by all 32 * NW rows of the
+// workgroup, which is what keeps it a small overhead.
+//
+// Key rotation cost: for key slot j of a block with offset off_b,
+//   R(off_b + j - p_ref) = R(off_b - p_ref) R(j).
+// R(j) is a per-thread constant (each thread always stages the same slot and frequencies);
+// cos/sin of (off_b - p_ref) theta_k are computed once per (block, frequency) per key tile
+// from an exact double-precision phase and shared through LDS; combining the two is four
+// multiply-adds per (key, frequency).
 //
 // Workgroup tile: NW waves x 32 rows; rows are (query position, head-in-group) pairs so the
 // G query heads of one KV head share every staged key/value tile (grouped-query packing).
-// Per wave, S^T = K~ Q~^T and O^T += V^T P^T on 32x32x16 bf16 MFMA: each lane owns one
-// query row (MFMA column), so row max / row sum are in-lane plus one cross-half exchange.
-// V is staged row-major in LDS and transposed on read by ds_read_b64_tr_b16.
+// Per wave, S^T = K~ Q~^T (fp16 operands) and O^T += V^T P^T (bf16) on 32x32x16 MFMA: each
+// lane owns one query row (MFMA column), so row max / row sum are in-lane plus one
+// cross-half exchange. Values go straight from global memory into a swizzled LDS tile
+// (global_load_lds) and are transposed on read (ds_read_b64_tr_b16). The next key tile's
+// loads are in flight while the current one is multiplied; one barrier per key tile.
 #include "lazyattn_common.h"
 #include "lazyattn_kernels.h"
 #include <limits.h>
@@ -23,6 +32,56 @@
 namespace lazyattn {
 
 constexpr int kPrefillWaves = 8;
+
+__device__ __forceinline__ void g2lds16p(const void* g, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base,
+                                   16, 0, 0);
+}
+
+// value tile row R: 16-byte chunk c stored at chunk position c ^ swz(R) (bank-conflict-free
+// transposed reads of four consecutive rows)
+__device__ __forceinline__ int pswz(int R) { return (R & 3) * 2; }
+
+struct TileWords {
+  int id[4], off[4], nval[4];
+  int kmin, kmax;
+  bool full;
+};
+
+// a[b] for a runtime b in 0..3 without dynamic register indexing
+__device__ __forceinline__ int sel4(const int (&a)[4], int b) {
+  return b == 0 ? a[0] : b == 1 ? a[1] : b == 2 ? a[2] : a[3];
+}
+
+__device__ __forceinline__ TileWords tile_words(const PrefillParams& P, int e0, int T, int kvlen,
+                                                int kt) {
+  TileWords tw;
+  tw.kmin = INT_MAX;
+  tw.kmax = INT_MIN;
+  tw.full = true;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int ent = 4 * kt + b;
+    int nv = 0, id = 0, off = 0;
+    if (ent < T) {
+      const uint32_t w = P.block_meta[e0 + ent];
+      id = word_id(w);
+      off = word_offset(w, ent);
+      const int rem = kvlen - ent * kBlock;
+      nv = rem < kBlock ? (rem > 0 ? rem : 0) : kBlock;
+      if (id >= P.num_blocks) nv = 0;                   // out-of-pool id: never read
+    }
+    tw.id[b] = id;
+    tw.off[b] = off;
+    tw.nval[b] = nv;
+    if (nv > 0) {
+      tw.kmin = min(tw.kmin, off);
+      tw.kmax = max(tw.kmax, off + nv - 1);
+    }
+    if (nv != kBlock) tw.full = false;
+  }
+  return tw;
+}
 
 template <int D, int G, bool ROTATE>
 __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillParams P) {
@@ -33,20 +92,32 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
   constexpr int NK = 64;                      // keys per key tile (4 blocks)
   constexpr int HALF = D / 2;
   constexpr int NCH = D / 16;                 // 16-dim k-steps of QK^T
-  constexpr int KS = D + 8;                   // LDS row strides (bf16 elements)
-  constexpr int VS = D + 16;
-  constexpr int KU = NK * (HALF / 8);         // key staging units: (key, 8-dim pair chunk)
-  constexpr int VU = NK * (D / 8);            // value staging units: (key, 8-dim chunk)
+  constexpr int KS = D + 8;                   // K~ LDS row stride (16-bit elements)
+  constexpr int ROWB = D * 2;                 // V row bytes (unpadded, swizzled)
+  constexpr int VBYTES = NK * ROWB;
+  constexpr int VLOADS = VBYTES / (NT * 16);  // global_load_lds per thread per tile
+  constexpr int CPT = HALF / 8;               // 8-frequency chunks per key
+  constexpr int KUNITS = NK * CPT;            // (key, frequency chunk) staging units
+  static_assert(KUNITS <= NT, "one key unit per thread");
+  static_assert(VLOADS >= 1 && VBYTES % (NT * 16) == 0, "value tile split");
 
-  __shared__ __align__(16) uint16_t Ks[NK * KS];
-  __shared__ __align__(16) uint16_t Vs[NK * VS];
+  __shared__ __align__(16) uint16_t Ks[2][NK * KS];
+  __shared__ __align__(16) uint8_t Vs[2][VBYTES];
+  __shared__ __align__(16) float2 tbl[2][4 * HALF];      // cos/sin((off_b - p_ref) theta_k)
   __shared__ double fr_s[HALF];
   __shared__ int pmax_s;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int kvh = blockIdx.y;
-  const int tile_id = blockIdx.x;
-  if (tile_id >= P.pf_prefix[P.num_seqs]) return;          // uniform per workgroup
+
+  // XCD-aware order: consecutive workgroups land on different XCDs, so hand each XCD a
+  // contiguous range of tiles (tiles of one sequence and KV head share their key tiles).
+  const int nwg = gridDim.x;                                  // multiple of 8
+  const int Lb = blockIdx.x;
+  const int Lp = (Lb & 7) * (nwg >> 3) + (Lb >> 3);
+  const int tiles_bound = P.tiles_bound;
+  const int kvh = Lp / tiles_bound;
+  const int tile_id = Lp - kvh * tiles_bound;
+  if (kvh >= P.Hkv || tile_id >= P.pf_prefix[P.num_seqs]) return;   // uniform
   const int seq = upper_seq(P.pf_prefix, P.num_seqs, tile_id);
   const int qt = tile_id - P.pf_prefix[seq];
   const int q0 = P.q_indptr[seq], qlen = P.q_indptr[seq + 1] - q0;
@@ -91,15 +162,88 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
     }
   }
 
-  // wave / workgroup extents of the query positions (for tile skipping and masking)
+  // wave / workgroup extents of the query positions (tile skipping and masking)
   int pmax_w = p, pmin_w = row_ok ? p : INT_MAX;
   for (int o = 32; o >= 1; o >>= 1) {
     pmax_w = max(pmax_w, __shfl_xor(pmax_w, o));
     pmin_w = min(pmin_w, __shfl_xor(pmin_w, o));
   }
   if (lane == 0) atomicMax(&pmax_s, pmax_w);
-  __syncthreads();
-  const int pmax_g = pmax_s;
+
+  // ---- this thread's key staging unit: key n (slot j of block b), frequencies 8cp..8cp+7
+  const bool kunit = tid < KUNITS;
+  const int kn = tid / CPT, cp = tid % CPT;
+  const int kb = (kn >> 4) & 3, kj = kn & 15;
+  float cj[8], sj[8];                                       // R(j), loop invariant
+#pragma unroll
+  for (int i = 0; i < 8; ++i) rope_cos_sin(kj, fr_s[(8 * cp + i) % HALF], cj[i], sj[i]);
+
+  // table of a key tile: thread (b, k) computes cos/sin((off_b - p_ref) theta_k)
+  auto make_table = [&](const TileWords& tw, int buf) {
+    if (tid < 4 * HALF) {
+      const int b = tid / HALF, k = tid % HALF;
+      float c, s;
+      rope_cos_sin(sel4(tw.off, b) - p_ref, fr_s[k], c, s);
+      tbl[buf][tid] = make_float2(c, s);
+    }
+  };
+  auto issue_v = [&](const TileWords& tw, int buf) {
+#pragma unroll
+    for (int i = 0; i < VLOADS; ++i) {
+      const int base = (w * VLOADS + i) * 1024;
+      const int off = base + 16 * lane;
+      const int R = off / ROWB, cs = (off % ROWB) / 16;
+      const int b = R >> 4, j = R & 15;
+      const void* src = P.zero;
+      if (j < sel4(tw.nval, b))
+        src = P.v_pool + (((size_t)sel4(tw.id, b) * P.Hkv + kvh) * kBlock + j) * D +
+              8 * (cs ^ pswz(R));
+      g2lds16p(src, Vs[buf] + base);
+    }
+  };
+  auto load_k = [&](const TileWords& tw, u32x4& lo, u32x4& hi) {
+    lo = u32x4{0, 0, 0, 0};
+    hi = u32x4{0, 0, 0, 0};
+    if (kunit && kj < sel4(tw.nval, kb)) {
+      const uint16_t* src =
+          P.k_pool + (((size_t)sel4(tw.id, kb) * P.Hkv + kvh) * kBlock + kj) * D + 8 * cp;
+      lo = *(const u32x4*)src;
+      hi = *(const u32x4*)(src + HALF);
+    }
+  };
+  auto store_k = [&](u32x4 lo, u32x4 hi, int buf) {
+    if (!kunit) return;
+    u32x4 ol, oh;
+    if (ROTATE) {
+      const float4* t4 = (const float4*)&tbl[buf][kb * HALF + 8 * cp];
+#pragma unroll
+      for (int i2 = 0; i2 < 4; ++i2) {
+        const float4 cs = t4[i2];                           // two (cos, sin) pairs
+        float ra[2], rb[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int i = 2 * i2 + u;
+          const float cb = u ? cs.z : cs.x, sb = u ? cs.w : cs.y;
+          const float c = cb * cj[i] - sb * sj[i];
+          const float s = sb * cj[i] + cb * sj[i];
+          const float a = u ? bf_hi(lo[i2]) : bf_lo(lo[i2]);
+          const float b = u ? bf_hi(hi[i2]) : bf_lo(hi[i2]);
+          ra[u] = a * c - b * s;
+          rb[u] = a * s + b * c;
+        }
+        ol[i2] = pack_f16(ra[0], ra[1]);
+        oh[i2] = pack_f16(rb[0], rb[1]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ol[i] = pack_f16(bf_lo(lo[i]), bf_hi(lo[i]));
+        oh[i] = pack_f16(bf_lo(hi[i]), bf_hi(hi[i]));
+      }
+    }
+    *(u32x4*)(Ks[buf] + kn * KS + 8 * cp) = ol;
+    *(u32x4*)(Ks[buf] + kn * KS + HALF + 8 * cp) = oh;
+  };
 
   float m = -INFINITY, l = 0.f;
   f32x16 o[D / 32];
@@ -107,83 +251,45 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
   for (int dt = 0; dt < D / 32; ++dt) o[dt] = f32x16{};
 
   const int n_kt = (T + 3) / 4;
+  // prologue: tile 0 staged (values, rotated keys), table of tile 1 ready
+  TileWords tw_cur = tile_words(P, e0, T, kvlen, 0);
+  TileWords tw_nxt = tile_words(P, e0, T, kvlen, 1);
+  u32x4 klo, khi;
+  if (n_kt > 0) {
+    make_table(tw_cur, 0);
+    issue_v(tw_cur, 0);
+    load_k(tw_cur, klo, khi);
+    __syncthreads();                                         // table of tile 0 visible
+    store_k(klo, khi, 0);
+    if (n_kt > 1) make_table(tw_nxt, 1);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);                        // vmcnt(0)
+  __syncthreads();
+  const int pmax_g = pmax_s;
+
   for (int kt = 0; kt < n_kt; ++kt) {
-    // the tile's four words (uniform loads)
-    uint32_t wd[4];
-    int off[4], nval[4];
-    int kmin = INT_MAX, kmax = INT_MIN;
-    bool tile_full = true;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int ent = 4 * kt + b;
-      if (ent < T) {
-        wd[b] = P.block_meta[e0 + ent];
-        off[b] = word_offset(wd[b], ent);
-        const int rem = kvlen - ent * kBlock;
-        nval[b] = rem < kBlock ? (rem > 0 ? rem : 0) : kBlock;
-        if (word_id(wd[b]) >= P.num_blocks) nval[b] = 0;      // out-of-pool id: never read
-      } else {
-        wd[b] = 0; off[b] = 0; nval[b] = 0;
-      }
-      if (nval[b] > 0) {
-        kmin = min(kmin, off[b]);
-        kmax = max(kmax, off[b] + nval[b] - 1);
-      }
-      if (nval[b] != kBlock) tile_full = false;
+    const int cur = kt & 1, nxt = cur ^ 1;
+    const bool has_next = kt + 1 < n_kt;
+    TileWords tw_n2 = tw_nxt;
+    if (has_next) {
+      issue_v(tw_nxt, nxt);
+      load_k(tw_nxt, klo, khi);
     }
-    if (kmin > pmax_g) continue;                                // nothing visible: skip tile
+    if (kt + 2 < n_kt) {
+      tw_n2 = tile_words(P, e0, T, kvlen, kt + 2);
+      make_table(tw_n2, cur);                                // table of tile kt+2
+    }
 
-    // ---- stage: rotated keys and raw values into LDS ---------------------------------
-    for (int u = tid; u < KU; u += NT) {
-      const int n = u / (HALF / 8), cp = u % (HALF / 8);
-      const int b = n >> 4, j = n & 15;
-      u32x4 lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
-      if (j < nval[b]) {
-        const uint16_t* src = P.k_pool +
-            (((size_t)word_id(wd[b]) * P.Hkv + kvh) * kBlock + j) * D + 8 * cp;
-        lo = *(const u32x4*)src;
-        hi = *(const u32x4*)(src + HALF);
-        const int nrel = off[b] + j - p_ref;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float a0 = bf_lo(lo[i]), a1 = bf_hi(lo[i]);
-          float b0 = bf_lo(hi[i]), b1 = bf_hi(hi[i]);
-          if (ROTATE) {
-            float c0, s0, c1, s1;
-            rope_cos_sin(nrel, fr_s[8 * cp + 2 * i], c0, s0);
-            rope_cos_sin(nrel, fr_s[8 * cp + 2 * i + 1], c1, s1);
-            lo[i] = pack_f16(a0 * c0 - b0 * s0, a1 * c1 - b1 * s1);
-            hi[i] = pack_f16(a0 * s0 + b0 * c0, a1 * s1 + b1 * c1);
-          } else {
-            lo[i] = pack_f16(a0, a1);
-            hi[i] = pack_f16(b0, b1);
-          }
-        }
-      }
-      *(u32x4*)(Ks + n * KS + 8 * cp) = lo;
-      *(u32x4*)(Ks + n * KS + HALF + 8 * cp) = hi;
-    }
-    for (int u = tid; u < VU; u += NT) {
-      const int n = u / (D / 8), c8 = u % (D / 8);
-      const int b = n >> 4, j = n & 15;
-      u32x4 v = {0, 0, 0, 0};
-      if (j < nval[b])
-        v = *(const u32x4*)(P.v_pool +
-                            (((size_t)word_id(wd[b]) * P.Hkv + kvh) * kBlock + j) * D + 8 * c8);
-      *(u32x4*)(Vs + n * VS + 8 * c8) = v;
-    }
-    __syncthreads();
-
-    // ---- compute (per wave) ---------------------------------------------------------------
-    if (kmin <= pmax_w) {
-      const bool nomask = tile_full && kmax <= pmin_w;
+    // ---- compute tile kt (per wave) -------------------------------------------------------
+    if (tw_cur.kmin <= pmax_w && tw_cur.kmin <= pmax_g) {
+      const bool nomask = tw_cur.full && tw_cur.kmax <= pmin_w;
       f32x16 s[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         s[t] = f32x16{};
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
-          const u32x4 a = *(const u32x4*)(Ks + (32 * t + col) * KS + 16 * c + 8 * hh);
+          const u32x4 a = *(const u32x4*)(Ks[cur] + (32 * t + col) * KS + 16 * c + 8 * hh);
           s[t] = mfma32h(as_f16x8(a), as_f16x8(qb[c]), s[t]);
         }
       }
@@ -197,7 +303,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
           if (!nomask) {
             const int b = 2 * t + (r >> 3);
             const int j = ((r >> 2) & 1) * 8 + 4 * hh + (r & 3);
-            const bool ok = j < nval[b] && off[b] + j <= p;
+            const bool ok = j < tw_cur.nval[b] && tw_cur.off[b] + j <= p;
             v = ok ? v : -INFINITY;
           }
           s[t][r] = v;
@@ -205,23 +311,27 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
         }
       }
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m, mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = exp2f(m - m_use);
+      // lazy rescale: the running max moves only when a row's max exceeds it by 2^8
+      if (__any(mx > m + 8.f)) {
+        const float m_new = fmaxf(m, mx);
+        const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m - m_new);
+        l *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
+        m = m_new;
+      }
+      const float m_use = m == -INFINITY ? 0.f : m;
       float rs = 0.f;
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float e = exp2f(s[t][r] - m_use);
+          const float e = __builtin_amdgcn_exp2f(s[t][r] - m_use);
           s[t][r] = e;
           rs += e;
         }
       }
-      l = l * alpha + rs;
-      m = m_new;
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
+      l += rs;
 
       const int gi = lane >> 4, i16 = lane & 15;
 #pragma unroll
@@ -230,20 +340,30 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
         for (int kk = 0; kk < 2; ++kk) {
           u32x4 bp;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) bp[i] = pack_bf16(s[t][8 * kk + 2 * i], s[t][8 * kk + 2 * i + 1]);
-          const int k0 = 32 * t + 16 * kk + 4 * hh + (i16 >> 2);
+          for (int i = 0; i < 4; ++i)
+            bp[i] = pack_bf16(s[t][8 * kk + 2 * i], s[t][8 * kk + 2 * i + 1]);
+          const int R1 = 32 * t + 16 * kk + 4 * hh + (i16 >> 2), R2 = R1 + 8;
 #pragma unroll
           for (int dt = 0; dt < D / 32; ++dt) {
-            const int n0 = 32 * dt + 16 * (gi & 1) + 4 * (i16 & 3);
-            const u32x2 r1 = lds_read_tr(Vs + k0 * VS + n0);
-            const u32x2 r2 = lds_read_tr(Vs + (k0 + 8) * VS + n0);
+            const int x = 32 * dt + 16 * (gi & 1) + 4 * (i16 & 3);
+            const int c8 = x >> 3, half = (x >> 2) & 1;
+            const u32x2 r1 = lds_read_tr(
+                (const uint16_t*)(Vs[cur] + R1 * ROWB + 16 * (c8 ^ pswz(R1)) + 8 * half));
+            const u32x2 r2 = lds_read_tr(
+                (const uint16_t*)(Vs[cur] + R2 * ROWB + 16 * (c8 ^ pswz(R2)) + 8 * half));
             const u32x4 a = {r1[0], r1[1], r2[0], r2[1]};
             o[dt] = mfma32(as_bf16x8(a), as_bf16x8(bp), o[dt]);
           }
         }
       }
     }
+
+    // ---- finish staging tile kt+1 -------------------------------------------------------------
+    if (has_next) store_k(klo, khi, nxt);
+    __builtin_amdgcn_s_waitcnt(0x0F70);                      // vmcnt(0): values of tile kt+1
     __syncthreads();
+    tw_cur = tw_nxt;
+    tw_nxt = tw_n2;
   }
 
   // ---- epilogue: O / l -> bf16 ----------------------------------------------------------
@@ -267,30 +387,28 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
 int prefill_positions_per_tile(int G) { return 32 * kPrefillWaves / G; }
 
 template <int D, int G>
-static hipError_t launch_dg(const PrefillParams& p, int grid_tiles, bool rotate, hipStream_t st) {
-  dim3 grid(grid_tiles, p.Hkv), block(kPrefillWaves * 64);
+static hipError_t launch_dg(const PrefillParams& p, bool rotate, hipStream_t st) {
+  const long long n = (long long)p.tiles_bound * p.Hkv;
+  dim3 grid((unsigned)((n + 7) / 8 * 8)), block(kPrefillWaves * 64);
   if (rotate) hipLaunchKernelGGL((prefill_kernel<D, G, true>), grid, block, 0, st, p);
   else hipLaunchKernelGGL((prefill_kernel<D, G, false>), grid, block, 0, st, p);
   return hipGetLastError();
 }
 
 template <int D>
-static hipError_t launch_d(const PrefillParams& p, int G, int grid_tiles, bool rotate,
-                           hipStream_t st) {
+static hipError_t launch_d(const PrefillParams& p, int G, bool rotate, hipStream_t st) {
   switch (G) {
-    case 1: return launch_dg<D, 1>(p, grid_tiles, rotate, st);
-    case 2: return launch_dg<D, 2>(p, grid_tiles, rotate, st);
-    case 4: return launch_dg<D, 4>(p, grid_tiles, rotate, st);
-    case 8: return launch_dg<D, 8>(p, grid_tiles, rotate, st);
+    case 1: return launch_dg<D, 1>(p, rotate, st);
+    case 2: return launch_dg<D, 2>(p, rotate, st);
+    case 4: return launch_dg<D, 4>(p, rotate, st);
+    case 8: return launch_dg<D, 8>(p, rotate, st);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_prefill(const PrefillParams& p, int D, int G, int grid_tiles, bool rotate,
-                          hipStream_t st) {
-  if (grid_tiles <= 0) return hipSuccess;
-  return D == 128 ? launch_d<128>(p, G, grid_tiles, rotate, st)
-                  : launch_d<64>(p, G, grid_tiles, rotate, st);
+hipError_t launch_prefill(const PrefillParams& p, int D, int G, bool rotate, hipStream_t st) {
+  if (p.tiles_bound <= 0) return hipSuccess;
+  return D == 128 ? launch_d<128>(p, G, rotate, st) : launch_d<64>(p, G, rotate, st);
 }
 
 }  // namespace lazyattn
