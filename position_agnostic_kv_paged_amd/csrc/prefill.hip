@@ -107,7 +107,8 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
   __shared__ double fr_s[HALF];
   __shared__ int pmax_s;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);    // wave index (uniform)
 
   // XCD-aware order: consecutive workgroups land on different XCDs, so hand each XCD a
   // contiguous range of tiles (tiles of one sequence and KV head share their key tiles).
@@ -171,47 +172,65 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
   if (lane == 0) atomicMax(&pmax_s, pmax_w);
 
   // ---- this thread's key staging unit: key n (slot j of block b), frequencies 8cp..8cp+7
+  // (a wave's 64 threads stage keys of one block: b is wave-uniform)
   const bool kunit = tid < KUNITS;
   const int kn = tid / CPT, cp = tid % CPT;
-  const int kb = (kn >> 4) & 3, kj = kn & 15;
+  const int kb = __builtin_amdgcn_readfirstlane((kn >> 4) & 3), kj = kn & 15;
   float cj[8], sj[8];                                       // R(j), loop invariant
 #pragma unroll
-  for (int i = 0; i < 8; ++i) rope_cos_sin(kj, fr_s[(8 * cp + i) % HALF], cj[i], sj[i]);
+  for (int i = 0; i < 8; ++i) rope_cos_sin(kj, fr_s[8 * cp + i], cj[i], sj[i]);
+
+  float m = -INFINITY, l = 0.f;
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) o[dt] = f32x16{};
 
   // table of a key tile: thread (b, k) computes cos/sin((off_b - p_ref) theta_k)
-  auto make_table = [&](const TileWords& tw, int buf) {
-    if (tid < 4 * HALF) {
-      const int b = tid / HALF, k = tid % HALF;
-      float c, s;
-      rope_cos_sin(sel4(tw.off, b) - p_ref, fr_s[k], c, s);
-      tbl[buf][tid] = make_float2(c, s);
+#define LA_MAKE_TABLE(TW, BUF)                                                        \
+  if (tid < 4 * HALF) {                                                               \
+    const int b_ = tid / HALF, k_ = tid % HALF;                                       \
+    const int o_ = b_ == 0 ? (TW).off[0] : b_ == 1 ? (TW).off[1]                      \
+                 : b_ == 2 ? (TW).off[2] : (TW).off[3];                               \
+    float c_, s_;                                                                     \
+    rope_cos_sin(o_ - p_ref, fr_s[k_], c_, s_);                                       \
+    tbl[BUF][tid] = make_float2(c_, s_);                                              \
+  }
+  // values of a key tile straight into LDS (the block of each load is wave-uniform)
+#define LA_ISSUE_V(TW, BUF)                                                           \
+  _Pragma("unroll") for (int i_ = 0; i_ < VLOADS; ++i_) {                             \
+    const int base_ = (w * VLOADS + i_) * 1024;                                       \
+    const int b_ = (base_ / ROWB) >> 4;                                               \
+    const int off_ = base_ + 16 * lane;                                               \
+    const int R_ = off_ / ROWB, cs_ = (off_ % ROWB) / 16;                             \
+    const int j_ = R_ & 15;                                                           \
+    const int nv_ = b_ == 0 ? (TW).nval[0] : b_ == 1 ? (TW).nval[1]                   \
+                  : b_ == 2 ? (TW).nval[2] : (TW).nval[3];                            \
+    const int id_ = b_ == 0 ? (TW).id[0] : b_ == 1 ? (TW).id[1]                       \
+                  : b_ == 2 ? (TW).id[2] : (TW).id[3];                                \
+    const void* src_ = P.zero;                                                        \
+    if (j_ < nv_)                                                                     \
+      src_ = P.v_pool + (((size_t)id_ * P.Hkv + kvh) * kBlock + j_) * D +             \
+             8 * (cs_ ^ pswz(R_));                                                    \
+    g2lds16p(src_, Vs[BUF] + base_);                                                  \
+  }
+
+  const int n_kt = (T + 3) / 4;
+  u32x4 klo = {0, 0, 0, 0}, khi = {0, 0, 0, 0};
+  // raw keys of tile kt into (klo, khi)
+  auto load_k = [&](int kt) {
+    const TileWords tw = tile_words(P, e0, T, kvlen, kt);
+    const int nv = kb == 0 ? tw.nval[0] : kb == 1 ? tw.nval[1] : kb == 2 ? tw.nval[2] : tw.nval[3];
+    const int id = kb == 0 ? tw.id[0] : kb == 1 ? tw.id[1] : kb == 2 ? tw.id[2] : tw.id[3];
+    klo = u32x4{0, 0, 0, 0};
+    khi = u32x4{0, 0, 0, 0};
+    if (kunit && kj < nv) {
+      const uint16_t* src = P.k_pool + (((size_t)id * P.Hkv + kvh) * kBlock + kj) * D + 8 * cp;
+      klo = *(const u32x4*)src;
+      khi = *(const u32x4*)(src + HALF);
     }
   };
-  auto issue_v = [&](const TileWords& tw, int buf) {
-#pragma unroll
-    for (int i = 0; i < VLOADS; ++i) {
-      const int base = (w * VLOADS + i) * 1024;
-      const int off = base + 16 * lane;
-      const int R = off / ROWB, cs = (off % ROWB) / 16;
-      const int b = R >> 4, j = R & 15;
-      const void* src = P.zero;
-      if (j < sel4(tw.nval, b))
-        src = P.v_pool + (((size_t)sel4(tw.id, b) * P.Hkv + kvh) * kBlock + j) * D +
-              8 * (cs ^ pswz(R));
-      g2lds16p(src, Vs[buf] + base);
-    }
-  };
-  auto load_k = [&](const TileWords& tw, u32x4& lo, u32x4& hi) {
-    lo = u32x4{0, 0, 0, 0};
-    hi = u32x4{0, 0, 0, 0};
-    if (kunit && kj < sel4(tw.nval, kb)) {
-      const uint16_t* src =
-          P.k_pool + (((size_t)sel4(tw.id, kb) * P.Hkv + kvh) * kBlock + kj) * D + 8 * cp;
-      lo = *(const u32x4*)src;
-      hi = *(const u32x4*)(src + HALF);
-    }
-  };
-  auto store_k = [&](u32x4 lo, u32x4 hi, int buf) {
+  // rotate (klo, khi) with table `buf` and store them as fp16 into Ks[buf]
+  auto store_k = [&](int buf) {
     if (!kunit) return;
     u32x4 ol, oh;
     if (ROTATE) {
@@ -226,8 +245,8 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
           const float cb = u ? cs.z : cs.x, sb = u ? cs.w : cs.y;
           const float c = cb * cj[i] - sb * sj[i];
           const float s = sb * cj[i] + cb * sj[i];
-          const float a = u ? bf_hi(lo[i2]) : bf_lo(lo[i2]);
-          const float b = u ? bf_hi(hi[i2]) : bf_lo(hi[i2]);
+          const float a = u ? bf_hi(klo[i2]) : bf_lo(klo[i2]);
+          const float b = u ? bf_hi(khi[i2]) : bf_lo(khi[i2]);
           ra[u] = a * c - b * s;
           rb[u] = a * s + b * c;
         }
@@ -237,31 +256,26 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        ol[i] = pack_f16(bf_lo(lo[i]), bf_hi(lo[i]));
-        oh[i] = pack_f16(bf_lo(hi[i]), bf_hi(hi[i]));
+        ol[i] = pack_f16(bf_lo(klo[i]), bf_hi(klo[i]));
+        oh[i] = pack_f16(bf_lo(khi[i]), bf_hi(khi[i]));
       }
     }
     *(u32x4*)(Ks[buf] + kn * KS + 8 * cp) = ol;
     *(u32x4*)(Ks[buf] + kn * KS + HALF + 8 * cp) = oh;
   };
 
-  float m = -INFINITY, l = 0.f;
-  f32x16 o[D / 32];
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) o[dt] = f32x16{};
-
-  const int n_kt = (T + 3) / 4;
   // prologue: tile 0 staged (values, rotated keys), table of tile 1 ready
-  TileWords tw_cur = tile_words(P, e0, T, kvlen, 0);
-  TileWords tw_nxt = tile_words(P, e0, T, kvlen, 1);
-  u32x4 klo, khi;
   if (n_kt > 0) {
-    make_table(tw_cur, 0);
-    issue_v(tw_cur, 0);
-    load_k(tw_cur, klo, khi);
+    const TileWords t0 = tile_words(P, e0, T, kvlen, 0);
+    LA_MAKE_TABLE(t0, 0);
+    LA_ISSUE_V(t0, 0);
+    load_k(0);
     __syncthreads();                                         // table of tile 0 visible
-    store_k(klo, khi, 0);
-    if (n_kt > 1) make_table(tw_nxt, 1);
+    store_k(0);
+    if (n_kt > 1) {
+      const TileWords t1 = tile_words(P, e0, T, kvlen, 1);
+      LA_MAKE_TABLE(t1, 1);
+    }
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);                        // vmcnt(0)
   __syncthreads();
@@ -270,15 +284,16 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
   for (int kt = 0; kt < n_kt; ++kt) {
     const int cur = kt & 1, nxt = cur ^ 1;
     const bool has_next = kt + 1 < n_kt;
-    TileWords tw_n2 = tw_nxt;
     if (has_next) {
-      issue_v(tw_nxt, nxt);
-      load_k(tw_nxt, klo, khi);
+      const TileWords tn = tile_words(P, e0, T, kvlen, kt + 1);
+      LA_ISSUE_V(tn, nxt);
+      load_k(kt + 1);
     }
     if (kt + 2 < n_kt) {
-      tw_n2 = tile_words(P, e0, T, kvlen, kt + 2);
-      make_table(tw_n2, cur);                                // table of tile kt+2
+      const TileWords tn2 = tile_words(P, e0, T, kvlen, kt + 2);
+      LA_MAKE_TABLE(tn2, cur);                               // table of tile kt+2
     }
+    const TileWords tw_cur = tile_words(P, e0, T, kvlen, kt);
 
     // ---- compute tile kt (per wave) -------------------------------------------------------
     if (tw_cur.kmin <= pmax_w && tw_cur.kmin <= pmax_g) {
@@ -303,7 +318,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
           if (!nomask) {
             const int b = 2 * t + (r >> 3);
             const int j = ((r >> 2) & 1) * 8 + 4 * hh + (r & 3);
-            const bool ok = j < tw_cur.nval[b] && tw_cur.off[b] + j <= p;
+            const bool ok = (j < tw_cur.nval[b]) & (tw_cur.off[b] + j <= p);
             v = ok ? v : -INFINITY;
           }
           s[t][r] = v;
@@ -359,12 +374,12 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
     }
 
     // ---- finish staging tile kt+1 -------------------------------------------------------------
-    if (has_next) store_k(klo, khi, nxt);
+    if (has_next) store_k(nxt);
     __builtin_amdgcn_s_waitcnt(0x0F70);                      // vmcnt(0): values of tile kt+1
     __syncthreads();
-    tw_cur = tw_nxt;
-    tw_nxt = tw_n2;
   }
+#undef LA_MAKE_TABLE
+#undef LA_ISSUE_V
 
   // ---- epilogue: O / l -> bf16 ----------------------------------------------------------
   const float lt = l + __shfl_xor(l, 32);
