@@ -158,6 +158,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
+                    help="profiling aid: run only one half (the JSON line then reports it alone)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build runs the attention path on a "
@@ -197,9 +199,11 @@ def main():
 
     def step(e=None):
         if e: e[0].record(stream)
-        call(L.prefill, pre, ws_pre)
+        if args.only != "decode":
+            call(L.prefill, pre, ws_pre)
         if e: e[1].record(stream)
-        call(L.decode, dec, ws_dec)
+        if args.only != "prefill":
+            call(L.decode, dec, ws_dec)
         if e: e[2].record(stream)
 
     # a plain copy of known size, once, so that FETCH_SIZE / WRITE_SIZE counter runs over
@@ -222,8 +226,8 @@ def main():
     t_dec = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) / 1e3
     flops = prefill_flops(wl, pre_seqs)
     dbytes = decode_bytes(wl, dec_seqs)
-    pre_tflops = flops / t_pre / 1e12
-    dec_gbs = dbytes / t_dec / 1e9
+    pre_tflops = flops / t_pre / 1e12 if t_pre > 0 else 0.0
+    dec_gbs = dbytes / t_dec / 1e9 if t_dec > 0 else 0.0
 
     if t_pre >= t_dec:
         roof = {"kernel": "prefill_kernel", "bound": "mfma", "achieved": pre_tflops,

@@ -96,6 +96,33 @@ __device__ __forceinline__ u32x2 lds_read_tr(const uint16_t* p) {
   return __builtin_bit_cast(u32x2, r);
 }
 
+// Combine each lane with lane l ^ 32 (v_permlane32_swap, no LDS round trip). With both
+// operands equal, the swap returns {x[l mod 32], x[32 + l mod 32]} in either order, so a
+// symmetric combination of the pair needs no lane select.
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_add(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Tree reductions of 32 values (no long dependency chains).
+__device__ __forceinline__ float max32(const f32x16& a, const f32x16& b) {
+  float m[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    m[i] = fmaxf(fmaxf(a[2 * i], a[2 * i + 1]), fmaxf(b[2 * i], b[2 * i + 1]));
+#pragma unroll
+  for (int w = 4; w >= 1; w >>= 1)
+#pragma unroll
+    for (int i = 0; i < w; ++i) m[i] = fmaxf(m[i], m[i + w]);
+  return m[0];
+}
+
 __device__ __forceinline__ float wave_max(float v) {
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
   return v;

@@ -22,7 +22,7 @@
 // G query heads of one KV head share every staged key/value tile (grouped-query packing).
 // Per wave, S^T = K~ Q~^T (fp16 operands) and O^T += V^T P^T (bf16) on 32x32x16 MFMA: each
 // lane owns one query row (MFMA column), so row max / row sum are in-lane plus one
-// cross-half exchange. Values go straight from global memory into a swizzled LDS tile
+// cross-half exchange. Values go straight from global memory into a padded LDS tile
 // (global_load_lds) and are transposed on read (ds_read_b64_tr_b16). The next key tile's
 // loads are in flight while the current one is multiplied; one barrier per key tile.
 #include "lazyattn_common.h"
@@ -38,9 +38,6 @@ __device__ __forceinline__ void g2lds16p(const void* g, void* lds_wave_base) {
                                    16, 0, 0);
 }
 
-// value tile row R: 16-byte chunk c stored at chunk position c ^ swz(R) (bank-conflict-free
-// transposed reads of four consecutive rows)
-__device__ __forceinline__ int pswz(int R) { return (R & 3) * 2; }
 
 struct TileWords {
   int id[4], off[4], nval[4];
@@ -64,7 +61,7 @@ __device__ __forceinline__ TileWords tile_words(const PrefillParams& P, int e0, 
     const int ent = 4 * kt + b;
     int nv = 0, id = 0, off = 0;
     if (ent < T) {
-      const uint32_t w = P.block_meta[e0 + ent];
+      const uint32_t w = P.block_meta[__builtin_amdgcn_readfirstlane(e0 + ent)];
       id = word_id(w);
       off = word_offset(w, ent);
       const int rem = kvlen - ent * kBlock;
@@ -93,17 +90,21 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
   constexpr int HALF = D / 2;
   constexpr int NCH = D / 16;                 // 16-dim k-steps of QK^T
   constexpr int KS = D + 8;                   // K~ LDS row stride (16-bit elements)
-  constexpr int ROWB = D * 2;                 // V row bytes (unpadded, swizzled)
-  constexpr int VBYTES = NK * ROWB;
-  constexpr int VLOADS = VBYTES / (NT * 16);  // global_load_lds per thread per tile
+  constexpr int ROWB = D * 2;                 // V row bytes
+  constexpr int VROW = ROWB + 32;             // padded LDS row: 4 consecutive rows -> disjoint banks
+  constexpr int SPR = VROW / 16;              // 16-byte slots per padded row
+  constexpr int VBYTES = NK * VROW;
+  constexpr int VINST = VBYTES / 1024;        // wave-wide global_load_lds per tile
+  static_assert(VBYTES % 1024 == 0, "value tile = whole wave loads");
   constexpr int CPT = HALF / 8;               // 8-frequency chunks per key
   constexpr int KUNITS = NK * CPT;            // (key, frequency chunk) staging units
   static_assert(KUNITS <= NT, "one key unit per thread");
-  static_assert(VLOADS >= 1 && VBYTES % (NT * 16) == 0, "value tile split");
 
   __shared__ __align__(16) uint16_t Ks[2][NK * KS];
   __shared__ __align__(16) uint8_t Vs[2][VBYTES];
   __shared__ __align__(16) float2 tbl[2][4 * HALF];      // cos/sin((off_b - p_ref) theta_k)
+  __shared__ __align__(16) float2 slot_cs[16 * HALF];    // cos/sin(j theta_k), j < 16
+  __shared__ __align__(16) uint16_t Qs[NW][32 * KS];     // each wave's rotated queries (fp16)
   __shared__ double fr_s[HALF];
   __shared__ int pmax_s;
 
@@ -119,12 +120,14 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
   const int kvh = Lp / tiles_bound;
   const int tile_id = Lp - kvh * tiles_bound;
   if (kvh >= P.Hkv || tile_id >= P.pf_prefix[P.num_seqs]) return;   // uniform
-  const int seq = upper_seq(P.pf_prefix, P.num_seqs, tile_id);
-  const int qt = tile_id - P.pf_prefix[seq];
-  const int q0 = P.q_indptr[seq], qlen = P.q_indptr[seq + 1] - q0;
-  const int e0 = P.block_table[seq], T = P.block_table[seq + 1] - e0;
-  const int kvlen = P.kv_lens[seq];
-  const int p_ref = ROTATE ? P.q_pos[q0 + qt * POS] : 0;
+  const int seq = __builtin_amdgcn_readfirstlane(upper_seq(P.pf_prefix, P.num_seqs, tile_id));
+  const int qt = __builtin_amdgcn_readfirstlane(tile_id - P.pf_prefix[seq]);
+  const int q0 = __builtin_amdgcn_readfirstlane(P.q_indptr[seq]);
+  const int qlen = __builtin_amdgcn_readfirstlane(P.q_indptr[seq + 1] - q0);
+  const int e0 = __builtin_amdgcn_readfirstlane(P.block_table[seq]);
+  const int T = __builtin_amdgcn_readfirstlane(P.block_table[seq + 1] - e0);
+  const int kvlen = __builtin_amdgcn_readfirstlane(P.kv_lens[seq]);
+  const int p_ref = ROTATE ? __builtin_amdgcn_readfirstlane(P.q_pos[q0 + qt * POS]) : 0;
 
   for (int i = tid; i < HALF; i += NT) fr_s[i] = P.freqs[i];
   if (tid == 0) pmax_s = INT_MIN;
@@ -138,9 +141,9 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
   const bool row_ok = qi < qlen;
   const int p = row_ok ? P.q_pos[q0 + qi] : INT_MIN;       // invalid rows see no key
 
-  // B operand chunks: lane holds dims 16c + 8hh + e (e < 8) of its row; the rotate-half
-  // partner of chunk c is chunk c + NCH/2 (dims + D/2), in the same lane.
-  u32x4 qb[NCH];
+  // Q~ rows of this wave -> LDS (fp16, row-major): lane holds dims 16c + 8hh + e (e < 8) of
+  // its row; the rotate-half partner of chunk c is chunk c + NCH/2 (dims + D/2), same lane.
+  uint16_t* qs = Qs[w];
   {
     u32x4 raw[NCH];
     const uint16_t* qrow = P.q + ((size_t)(q0 + (row_ok ? qi : 0)) * P.Hq + h) * D;
@@ -148,18 +151,22 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
     for (int c = 0; c < NCH; ++c)
       raw[c] = row_ok ? *(const u32x4*)(qrow + 16 * c + 8 * hh) : u32x4{0, 0, 0, 0};
     const int n = row_ok ? p - p_ref : 0;
+    const float sc = P.scale_log2;                  // softmax scale folded into Q~
 #pragma unroll
     for (int c = 0; c < NCH / 2; ++c) {
+      u32x4 lo, hi;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float a0 = bf_lo(raw[c][i]), a1 = bf_hi(raw[c][i]);
-        float b0 = bf_lo(raw[c + NCH / 2][i]), b1 = bf_hi(raw[c + NCH / 2][i]);
+        float a0 = bf_lo(raw[c][i]) * sc, a1 = bf_hi(raw[c][i]) * sc;
+        float b0 = bf_lo(raw[c + NCH / 2][i]) * sc, b1 = bf_hi(raw[c + NCH / 2][i]) * sc;
         float c0, s0, c1, s1;
         rope_cos_sin(n, fr_s[16 * c + 8 * hh + 2 * i], c0, s0);
         rope_cos_sin(n, fr_s[16 * c + 8 * hh + 2 * i + 1], c1, s1);
-        qb[c][i] = pack_f16(a0 * c0 - b0 * s0, a1 * c1 - b1 * s1);
-        qb[c + NCH / 2][i] = pack_f16(a0 * s0 + b0 * c0, a1 * s1 + b1 * c1);
+        lo[i] = pack_f16(a0 * c0 - b0 * s0, a1 * c1 - b1 * s1);
+        hi[i] = pack_f16(a0 * s0 + b0 * c0, a1 * s1 + b1 * c1);
       }
+      *(u32x4*)(qs + col * KS + 16 * c + 8 * hh) = lo;
+      *(u32x4*)(qs + col * KS + 16 * (c + NCH / 2) + 8 * hh) = hi;
     }
   }
 
@@ -176,11 +183,18 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
   const bool kunit = tid < KUNITS;
   const int kn = tid / CPT, cp = tid % CPT;
   const int kb = __builtin_amdgcn_readfirstlane((kn >> 4) & 3), kj = kn & 15;
-  float cj[8], sj[8];                                       // R(j), loop invariant
-#pragma unroll
-  for (int i = 0; i < 8; ++i) rope_cos_sin(kj, fr_s[8 * cp + i], cj[i], sj[i]);
+  for (int i = tid; i < 16 * HALF; i += NT) {               // R(j) table, loop invariant
+    float c, sn;
+    rope_cos_sin(i / HALF, fr_s[i % HALF], c, sn);
+    slot_cs[i] = make_float2(c, sn);
+  }
 
-  float m = -INFINITY, l = 0.f;
+  // The running max m rides on the matrix cores: an extra 16-wide k-step with
+  // K~ = (1, 0, ...) and Q~ = (-m, 0, ...) makes S^T = K~ Q~^T - m directly.
+  const bool e0lane = hh == 0;
+  const u32x4 ones_a = e0lane ? u32x4{0x3C00u, 0u, 0u, 0u} : u32x4{0u, 0u, 0u, 0u};   // fp16 1.0
+  float m = -INFINITY, l = 0.f;                              // l: this lane's half of the row sum
+  u32x4 qm = {0u, 0u, 0u, 0u};                               // (-m, 0, ...) as fp16
   f32x16 o[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) o[dt] = f32x16{};
@@ -195,23 +209,24 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
     rope_cos_sin(o_ - p_ref, fr_s[k_], c_, s_);                                       \
     tbl[BUF][tid] = make_float2(c_, s_);                                              \
   }
-  // values of a key tile straight into LDS (the block of each load is wave-uniform)
+  // values of a key tile straight into LDS: slot (row R, chunk c) of the padded tile; pad
+  // slots and invalid rows read the zeroed workspace chunk
 #define LA_ISSUE_V(TW, BUF)                                                           \
-  _Pragma("unroll") for (int i_ = 0; i_ < VLOADS; ++i_) {                             \
-    const int base_ = (w * VLOADS + i_) * 1024;                                       \
-    const int b_ = (base_ / ROWB) >> 4;                                               \
-    const int off_ = base_ + 16 * lane;                                               \
-    const int R_ = off_ / ROWB, cs_ = (off_ % ROWB) / 16;                             \
-    const int j_ = R_ & 15;                                                           \
-    const int nv_ = b_ == 0 ? (TW).nval[0] : b_ == 1 ? (TW).nval[1]                   \
-                  : b_ == 2 ? (TW).nval[2] : (TW).nval[3];                            \
-    const int id_ = b_ == 0 ? (TW).id[0] : b_ == 1 ? (TW).id[1]                       \
-                  : b_ == 2 ? (TW).id[2] : (TW).id[3];                                \
-    const void* src_ = P.zero;                                                        \
-    if (j_ < nv_)                                                                     \
-      src_ = P.v_pool + (((size_t)id_ * P.Hkv + kvh) * kBlock + j_) * D +             \
-             8 * (cs_ ^ pswz(R_));                                                    \
-    g2lds16p(src_, Vs[BUF] + base_);                                                  \
+  _Pragma("unroll") for (int i_ = 0; i_ < (VINST + NW - 1) / NW; ++i_) {              \
+    const int I_ = w + NW * i_;                                                       \
+    if (I_ < VINST) {                                                                 \
+      const int slot_ = I_ * 64 + lane;                                               \
+      const int R_ = slot_ / SPR, c_ = slot_ % SPR;                                   \
+      const int b_ = R_ >> 4, j_ = R_ & 15;                                           \
+      const int nv_ = b_ == 0 ? (TW).nval[0] : b_ == 1 ? (TW).nval[1]                 \
+                    : b_ == 2 ? (TW).nval[2] : (TW).nval[3];                          \
+      const int id_ = b_ == 0 ? (TW).id[0] : b_ == 1 ? (TW).id[1]                     \
+                    : b_ == 2 ? (TW).id[2] : (TW).id[3];                              \
+      const void* src_ = P.zero;                                                      \
+      if ((c_ < D / 8) & (j_ < nv_))                                                  \
+        src_ = P.v_pool + (((size_t)id_ * P.Hkv + kvh) * kBlock + j_) * D + 8 * c_;   \
+      g2lds16p(src_, Vs[BUF] + I_ * 1024);                                            \
+    }                                                                                 \
   }
 
   const int n_kt = (T + 3) / 4;
@@ -235,16 +250,18 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
     u32x4 ol, oh;
     if (ROTATE) {
       const float4* t4 = (const float4*)&tbl[buf][kb * HALF + 8 * cp];
+      const float4* j4 = (const float4*)&slot_cs[kj * HALF + 8 * cp];
 #pragma unroll
       for (int i2 = 0; i2 < 4; ++i2) {
-        const float4 cs = t4[i2];                           // two (cos, sin) pairs
+        const float4 cs = t4[i2];                           // two (cos, sin) pairs: block
+        const float4 js = j4[i2];                           // two (cos, sin) pairs: slot
         float ra[2], rb[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          const int i = 2 * i2 + u;
           const float cb = u ? cs.z : cs.x, sb = u ? cs.w : cs.y;
-          const float c = cb * cj[i] - sb * sj[i];
-          const float s = sb * cj[i] + cb * sj[i];
+          const float cj = u ? js.z : js.x, sj = u ? js.w : js.y;
+          const float c = cb * cj - sb * sj;
+          const float s = sb * cj + cb * sj;
           const float a = u ? bf_hi(klo[i2]) : bf_lo(klo[i2]);
           const float b = u ? bf_hi(khi[i2]) : bf_lo(khi[i2]);
           ra[u] = a * c - b * s;
@@ -264,119 +281,163 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
     *(u32x4*)(Ks[buf] + kn * KS + HALF + 8 * cp) = oh;
   };
 
-  // prologue: tile 0 staged (values, rotated keys), table of tile 1 ready
+  // S^T = K~ Q~^T - m for the key tile in Ks[buf] (scores in log2 units)
+  auto qk = [&](int buf, f32x16 (&sc)[2]) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) sc[t] = mfma32h(as_f16x8(ones_a), as_f16x8(qm), f32x16{});
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const u32x4 b = *(const u32x4*)(qs + col * KS + 16 * c + 8 * hh);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const u32x4 a = *(const u32x4*)(Ks[buf] + (32 * t + col) * KS + 16 * c + 8 * hh);
+        sc[t] = mfma32h(as_f16x8(a), as_f16x8(b), sc[t]);
+      }
+    }
+  };
+
+  // Software pipeline over key tiles. Iteration kt holds S(kt) on entry; it
+  //   A) exponentiates S(kt) into P(kt) while the matrix cores compute S(kt+1);
+  //   B) runs O += V(kt)^T P(kt)^T while the vector ALUs rotate keys of tile kt+2;
+  // keys are staged two tiles ahead, values one tile ahead (both double-buffered), the
+  // (block, frequency) phase tables three tiles ahead. Work on tiles past the end reads
+  // empty blocks (zeros) and is discarded.
   if (n_kt > 0) {
     const TileWords t0 = tile_words(P, e0, T, kvlen, 0);
+    const TileWords t1 = tile_words(P, e0, T, kvlen, 1);
     LA_MAKE_TABLE(t0, 0);
+    LA_MAKE_TABLE(t1, 1);
     LA_ISSUE_V(t0, 0);
+    load_k(1);
+    const u32x4 k1lo = klo, k1hi = khi;
     load_k(0);
-    __syncthreads();                                         // table of tile 0 visible
+    __syncthreads();                                         // tables 0, 1 visible
     store_k(0);
-    if (n_kt > 1) {
-      const TileWords t1 = tile_words(P, e0, T, kvlen, 1);
-      LA_MAKE_TABLE(t1, 1);
-    }
+    klo = k1lo;
+    khi = k1hi;
+    store_k(1);
+    __syncthreads();                                         // tables 0, 1 consumed
+    const TileWords t2 = tile_words(P, e0, T, kvlen, 2);
+    LA_MAKE_TABLE(t2, 0);
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);                        // vmcnt(0)
   __syncthreads();
   const int pmax_g = pmax_s;
+  f32x16 S0[2], S1[2];
+  if (n_kt > 0) qk(0, S0);
 
-  for (int kt = 0; kt < n_kt; ++kt) {
+  // one pipeline iteration: S(kt) in Sc on entry, S(kt+1) left in Sn
+  auto step = [&](const int kt, f32x16 (&Sc)[2], f32x16 (&Sn)[2]) {
     const int cur = kt & 1, nxt = cur ^ 1;
-    const bool has_next = kt + 1 < n_kt;
-    if (has_next) {
-      const TileWords tn = tile_words(P, e0, T, kvlen, kt + 1);
-      LA_ISSUE_V(tn, nxt);
-      load_k(kt + 1);
-    }
-    if (kt + 2 < n_kt) {
-      const TileWords tn2 = tile_words(P, e0, T, kvlen, kt + 2);
-      LA_MAKE_TABLE(tn2, cur);                               // table of tile kt+2
-    }
-    const TileWords tw_cur = tile_words(P, e0, T, kvlen, kt);
-
-    // ---- compute tile kt (per wave) -------------------------------------------------------
-    if (tw_cur.kmin <= pmax_w && tw_cur.kmin <= pmax_g) {
-      const bool nomask = tw_cur.full && tw_cur.kmax <= pmin_w;
-      f32x16 s[2];
+    // ---- rare paths: causal / ragged mask of S(kt), lazy rescale --------------------------
+    {
+      const TileWords tw = tile_words(P, e0, T, kvlen, kt);
+      const bool visible = tw.kmin <= pmax_w && tw.kmin <= pmax_g;
+      if (!(visible && tw.full && tw.kmax <= pmin_w)) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        s[t] = f32x16{};
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-          const u32x4 a = *(const u32x4*)(Ks[cur] + (32 * t + col) * KS + 16 * c + 8 * hh);
-          s[t] = mfma32h(as_f16x8(a), as_f16x8(qb[c]), s[t]);
-        }
-      }
-      // s[t][r]: key n = 32t + (r/4)*8 + 4hh + r%4 of this lane's row
-      float mx = -INFINITY;
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float v = s[t][r] * P.scale_log2;
-          if (!nomask) {
+          for (int r = 0; r < 16; ++r) {
             const int b = 2 * t + (r >> 3);
             const int j = ((r >> 2) & 1) * 8 + 4 * hh + (r & 3);
-            const bool ok = (j < tw_cur.nval[b]) & (tw_cur.off[b] + j <= p);
-            v = ok ? v : -INFINITY;
+            const bool ok = visible & (j < tw.nval[b]) & (tw.off[b] + j <= p);
+            Sc[t][r] = ok ? Sc[t][r] : -INFINITY;
           }
-          s[t][r] = v;
-          mx = fmaxf(mx, v);
-        }
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      // lazy rescale: the running max moves only when a row's max exceeds it by 2^8
-      if (__any(mx > m + 8.f)) {
-        const float m_new = fmaxf(m, mx);
-        const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m - m_new);
-        l *= alpha;
+    }
+    float mx = -INFINITY;
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
-        m = m_new;
-      }
-      const float m_use = m == -INFINITY ? 0.f : m;
-      float rs = 0.f;
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, Sc[t][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    // the running max moves only when a row's max exceeds it by 2^8 (or on the row's first
+    // visible key), so P = exp2(S) stays below 256; m is kept as the exact fp16 value the
+    // matrix cores subtract, so the offset cancels in O / l
+    const bool first = (m == -INFINITY) & (mx != -INFINITY);
+    if (__any(first | (mx > 8.f))) {
+      const float m_old = m == -INFINITY ? 0.f : m;
+      float m_new = m;
+      if (first | (mx > 0.f)) m_new = (float)(_Float16)(m_old + mx);
+      const float delta = m_new == -INFINITY ? 0.f : m_new - m_old;
+      const float alpha = first ? 1.f : __builtin_amdgcn_exp2f(-delta);
+      m = m_new;
+      qm[0] = e0lane ? (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(m == -INFINITY ? 0.f : -m))
+                     : 0u;
+      l *= alpha;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = __builtin_amdgcn_exp2f(s[t][r] - m_use);
-          s[t][r] = e;
-          rs += e;
-        }
-      }
-      l += rs;
+      for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) Sc[t][r] -= delta;
+    }
 
+    // ---- staging issue: values of tile kt+1, raw keys of tile kt+2, table of tile kt+3 ----
+    {
+      const TileWords tn1 = tile_words(P, e0, T, kvlen, kt + 1);
+      LA_ISSUE_V(tn1, nxt);
+      load_k(kt + 2);
+      const TileWords tn3 = tile_words(P, e0, T, kvlen, kt + 3);
+      LA_MAKE_TABLE(tn3, nxt);
+    }
+
+    // ---- A: P(kt) = exp2(S(kt)) on the VALU, S(kt+1) on the matrix cores --------------
+    u32x4 bp[2][2];
+    float rs = 0.f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float e0 = __builtin_amdgcn_exp2f(Sc[t][8 * kk + 2 * i]);
+          const float e1 = __builtin_amdgcn_exp2f(Sc[t][8 * kk + 2 * i + 1]);
+          rs += e0 + e1;
+          bp[t][kk][i] = pack_bf16(e0, e1);
+        }
+    l += rs;
+    qk(nxt, Sn);
+#pragma unroll
+    for (int i = 0; i < 2 * (NCH + 1); ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // 1 LDS read
+      __builtin_amdgcn_sched_group_barrier(0x402, 3, 0);     // 3 VALU / transcendental
+    }
+
+    // ---- B: O += V(kt)^T P(kt)^T on the matrix cores, keys of tile kt+2 on the VALU -----
+    {
       const int gi = lane >> 4, i16 = lane & 15;
+      const uint8_t* vbase = Vs[cur] + (4 * hh + (i16 >> 2)) * VROW +
+                             16 * (2 * (gi & 1) + ((i16 & 3) >> 1)) + 8 * (i16 & 1);
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-          u32x4 bp;
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            bp[i] = pack_bf16(s[t][8 * kk + 2 * i], s[t][8 * kk + 2 * i + 1]);
-          const int R1 = 32 * t + 16 * kk + 4 * hh + (i16 >> 2), R2 = R1 + 8;
 #pragma unroll
           for (int dt = 0; dt < D / 32; ++dt) {
-            const int x = 32 * dt + 16 * (gi & 1) + 4 * (i16 & 3);
-            const int c8 = x >> 3, half = (x >> 2) & 1;
-            const u32x2 r1 = lds_read_tr(
-                (const uint16_t*)(Vs[cur] + R1 * ROWB + 16 * (c8 ^ pswz(R1)) + 8 * half));
-            const u32x2 r2 = lds_read_tr(
-                (const uint16_t*)(Vs[cur] + R2 * ROWB + 16 * (c8 ^ pswz(R2)) + 8 * half));
+            const uint8_t* a1 = vbase + (32 * t + 16 * kk) * VROW + 64 * dt;
+            const u32x2 r1 = lds_read_tr((const uint16_t*)a1);
+            const u32x2 r2 = lds_read_tr((const uint16_t*)(a1 + 8 * VROW));
             const u32x4 a = {r1[0], r1[1], r2[0], r2[1]};
-            o[dt] = mfma32(as_bf16x8(a), as_bf16x8(bp), o[dt]);
+            o[dt] = mfma32(as_bf16x8(a), as_bf16x8(bp[t][kk]), o[dt]);
           }
         }
       }
     }
-
-    // ---- finish staging tile kt+1 -------------------------------------------------------------
-    if (has_next) store_k(nxt);
+    store_k(cur);                                            // keys of tile kt+2
+#pragma unroll
+    for (int i = 0; i < 4 * (D / 32); ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);     // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);     // 2 LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x402, 4, 1);     // 4 VALU
+    }
     __builtin_amdgcn_s_waitcnt(0x0F70);                      // vmcnt(0): values of tile kt+1
     __syncthreads();
+  };
+  for (int kt = 0; kt < n_kt; kt += 2) {                     // unrolled x2: S0 <-> S1
+    step(kt, S0, S1);
+    if (kt + 1 < n_kt) step(kt + 1, S1, S0);
   }
 #undef LA_MAKE_TABLE
 #undef LA_ISSUE_V
