@@ -50,18 +50,29 @@ __device__ __forceinline__ int sel4(const int (&a)[4], int b) {
   return b == 0 ? a[0] : b == 1 ? a[1] : b == 2 ? a[2] : a[3];
 }
 
-__device__ __forceinline__ TileWords tile_words(const PrefillParams& P, int e0, int T, int kvlen,
-                                                int kt) {
+// Words of key tiles kt .. kt+3 live in one VGPR ("window"): lane i < 16 holds the word of
+// entry 4 kt + i. Tile kt + d (d a compile-time 0..3) is decoded from lanes 4d .. 4d+3 with
+// readlane, so the loop issues one small vector load per key tile (for the next window)
+// instead of a dependent memory round trip per word.
+__device__ __forceinline__ uint32_t load_window(const PrefillParams& P, int e0, int T, int kt,
+                                                int lane) {
+  const int ent = 4 * kt + lane;
+  return (lane < 16 && ent < T) ? P.block_meta[e0 + ent] : 0u;
+}
+
+template <int d>
+__device__ __forceinline__ TileWords tile_words(const PrefillParams& P, uint32_t win, int T,
+                                                int kvlen, int kt0) {
   TileWords tw;
   tw.kmin = INT_MAX;
   tw.kmax = INT_MIN;
   tw.full = true;
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
-    const int ent = 4 * kt + b;
+    const int ent = 4 * (kt0 + d) + b;
     int nv = 0, id = 0, off = 0;
     if (ent < T) {
-      const uint32_t w = P.block_meta[__builtin_amdgcn_readfirstlane(e0 + ent)];
+      const uint32_t w = (uint32_t)__builtin_amdgcn_readlane((int)win, 4 * d + b);
       id = word_id(w);
       off = word_offset(w, ent);
       const int rem = kvlen - ent * kBlock;
@@ -232,8 +243,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
   const int n_kt = (T + 3) / 4;
   u32x4 klo = {0, 0, 0, 0}, khi = {0, 0, 0, 0};
   // raw keys of tile kt into (klo, khi)
-  auto load_k = [&](int kt) {
-    const TileWords tw = tile_words(P, e0, T, kvlen, kt);
+  auto load_k = [&](const TileWords& tw) {
     const int nv = kb == 0 ? tw.nval[0] : kb == 1 ? tw.nval[1] : kb == 2 ? tw.nval[2] : tw.nval[3];
     const int id = kb == 0 ? tw.id[0] : kb == 1 ? tw.id[1] : kb == 2 ? tw.id[2] : tw.id[3];
     klo = u32x4{0, 0, 0, 0};
@@ -302,22 +312,23 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
   // keys are staged two tiles ahead, values one tile ahead (both double-buffered), the
   // (block, frequency) phase tables three tiles ahead. Work on tiles past the end reads
   // empty blocks (zeros) and is discarded.
+  uint32_t win = load_window(P, e0, T, 0, lane);           // words of tiles 0 .. 3
   if (n_kt > 0) {
-    const TileWords t0 = tile_words(P, e0, T, kvlen, 0);
-    const TileWords t1 = tile_words(P, e0, T, kvlen, 1);
+    const TileWords t0 = tile_words<0>(P, win, T, kvlen, 0);
+    const TileWords t1 = tile_words<1>(P, win, T, kvlen, 0);
     LA_MAKE_TABLE(t0, 0);
     LA_MAKE_TABLE(t1, 1);
     LA_ISSUE_V(t0, 0);
-    load_k(1);
+    load_k(t1);
     const u32x4 k1lo = klo, k1hi = khi;
-    load_k(0);
+    load_k(t0);
     __syncthreads();                                         // tables 0, 1 visible
     store_k(0);
     klo = k1lo;
     khi = k1hi;
     store_k(1);
     __syncthreads();                                         // tables 0, 1 consumed
-    const TileWords t2 = tile_words(P, e0, T, kvlen, 2);
+    const TileWords t2 = tile_words<2>(P, win, T, kvlen, 0);
     LA_MAKE_TABLE(t2, 0);
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);                        // vmcnt(0)
@@ -329,9 +340,10 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
   // one pipeline iteration: S(kt) in Sc on entry, S(kt+1) left in Sn
   auto step = [&](const int kt, f32x16 (&Sc)[2], f32x16 (&Sn)[2]) {
     const int cur = kt & 1, nxt = cur ^ 1;
+    const uint32_t win_next = load_window(P, e0, T, kt + 1, lane);   // used from step kt+1
     // ---- rare paths: causal / ragged mask of S(kt), lazy rescale --------------------------
     {
-      const TileWords tw = tile_words(P, e0, T, kvlen, kt);
+      const TileWords tw = tile_words<0>(P, win, T, kvlen, kt);
       const bool visible = tw.kmin <= pmax_w && tw.kmin <= pmax_g;
       if (!(visible && tw.full && tw.kmax <= pmin_w)) {
 #pragma unroll
@@ -375,10 +387,10 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
 
     // ---- staging issue: values of tile kt+1, raw keys of tile kt+2, table of tile kt+3 ----
     {
-      const TileWords tn1 = tile_words(P, e0, T, kvlen, kt + 1);
+      const TileWords tn1 = tile_words<1>(P, win, T, kvlen, kt);
       LA_ISSUE_V(tn1, nxt);
-      load_k(kt + 2);
-      const TileWords tn3 = tile_words(P, e0, T, kvlen, kt + 3);
+      load_k(tile_words<2>(P, win, T, kvlen, kt));
+      const TileWords tn3 = tile_words<3>(P, win, T, kvlen, kt);
       LA_MAKE_TABLE(tn3, nxt);
     }
 
@@ -434,6 +446,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);                      // vmcnt(0): values of tile kt+1
     __syncthreads();
+    win = win_next;
   };
   for (int kt = 0; kt < n_kt; kt += 2) {                     // unrolled x2: S0 <-> S1
     step(kt, S0, S1);
