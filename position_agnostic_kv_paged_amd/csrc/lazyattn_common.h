@@ -96,6 +96,13 @@ __device__ __forceinline__ u32x2 lds_read_tr(const uint16_t* p) {
   return __builtin_bit_cast(u32x2, r);
 }
 
+// c + x.lo + x.hi for two packed bf16 values (v_dot2_f32_bf16 against (1, 1))
+__device__ __forceinline__ float sum2_bf16(uint32_t x, float c) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, x),
+                                         __builtin_bit_cast(bf16x2_t, 0x3F803F80u), c, false);
+}
+
 // Combine each lane with lane l ^ 32 (v_permlane32_swap, no LDS round trip). With both
 // operands equal, the swap returns {x[l mod 32], x[32 + l mod 32]} in either order, so a
 // symmetric combination of the pair needs no lane select.

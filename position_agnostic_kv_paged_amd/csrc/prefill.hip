@@ -68,25 +68,19 @@ __device__ __forceinline__ TileWords tile_words(const PrefillParams& P, uint32_t
   tw.kmax = INT_MIN;
   tw.full = true;
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
+  for (int b = 0; b < 4; ++b) {                        // branch-free: scalar selects only
     const int ent = 4 * (kt0 + d) + b;
-    int nv = 0, id = 0, off = 0;
-    if (ent < T) {
-      const uint32_t w = (uint32_t)__builtin_amdgcn_readlane((int)win, 4 * d + b);
-      id = word_id(w);
-      off = word_offset(w, ent);
-      const int rem = kvlen - ent * kBlock;
-      nv = rem < kBlock ? (rem > 0 ? rem : 0) : kBlock;
-      if (id >= P.num_blocks) nv = 0;                   // out-of-pool id: never read
-    }
+    const uint32_t w = (uint32_t)__builtin_amdgcn_readlane((int)win, 4 * d + b);
+    const int id = word_id(w);
+    const int off = word_offset(w, ent);
+    const int nv = (ent < T) & (id < P.num_blocks)       // out-of-pool id: never read
+                   ? min(max(kvlen - ent * kBlock, 0), kBlock) : 0;
     tw.id[b] = id;
     tw.off[b] = off;
     tw.nval[b] = nv;
-    if (nv > 0) {
-      tw.kmin = min(tw.kmin, off);
-      tw.kmax = max(tw.kmax, off + nv - 1);
-    }
-    if (nv != kBlock) tw.full = false;
+    tw.kmin = nv > 0 ? min(tw.kmin, off) : tw.kmin;
+    tw.kmax = nv > 0 ? max(tw.kmax, off + nv - 1) : tw.kmax;
+    tw.full = tw.full & (nv == kBlock);
   }
   return tw;
 }
@@ -191,7 +185,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
 
   // ---- this thread's key staging unit: key n (slot j of block b), frequencies 8cp..8cp+7
   // (a wave's 64 threads stage keys of one block: b is wave-uniform)
-  const bool kunit = tid < KUNITS;
+  const bool kunit = KUNITS == NT || tid < KUNITS;
   const int kn = tid / CPT, cp = tid % CPT;
   const int kb = __builtin_amdgcn_readfirstlane((kn >> 4) & 3), kj = kn & 15;
   for (int i = tid; i < 16 * HALF; i += NT) {               // R(j) table, loop invariant
@@ -395,8 +389,9 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
     }
 
     // ---- A: P(kt) = exp2(S(kt)) on the VALU, S(kt+1) on the matrix cores --------------
+    // the row sum adds the bf16-rounded P that the matrix cores multiply (v_dot2 with 1, 1)
     u32x4 bp[2][2];
-    float rs = 0.f;
+    float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -405,10 +400,11 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
         for (int i = 0; i < 4; ++i) {
           const float e0 = __builtin_amdgcn_exp2f(Sc[t][8 * kk + 2 * i]);
           const float e1 = __builtin_amdgcn_exp2f(Sc[t][8 * kk + 2 * i + 1]);
-          rs += e0 + e1;
           bp[t][kk][i] = pack_bf16(e0, e1);
+          if (i & 1) rs1 = sum2_bf16(bp[t][kk][i], rs1);
+          else rs0 = sum2_bf16(bp[t][kk][i], rs0);
         }
-    l += rs;
+    l += rs0 + rs1;
     qk(nxt, Sn);
 #pragma unroll
     for (int i = 0; i < 2 * (NCH + 1); ++i) {
