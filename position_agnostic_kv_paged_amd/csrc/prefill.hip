@@ -28,6 +28,7 @@
 #include "lazyattn_common.h"
 #include "lazyattn_kernels.h"
 #include <limits.h>
+#include <type_traits>
 
 namespace lazyattn {
 
@@ -101,9 +102,10 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
   constexpr int VBYTES = NK * VROW;
   constexpr int VINST = VBYTES / 1024;        // wave-wide global_load_lds per tile
   static_assert(VBYTES % 1024 == 0, "value tile = whole wave loads");
-  constexpr int CPT = HALF / 8;               // 8-frequency chunks per key
-  constexpr int KUNITS = NK * CPT;            // (key, frequency chunk) staging units
-  static_assert(KUNITS <= NT, "one key unit per thread");
+  constexpr int FPT = NK * HALF / NT;         // frequencies each thread rotates per key tile
+  constexpr int CPT = HALF / FPT;             // threads per key
+  static_assert(FPT == 4 || FPT == 8, "staging unit = 4 or 8 frequencies of one key");
+  using KRaw = typename std::conditional<FPT == 8, u32x4, u32x2>::type;
 
   __shared__ __align__(16) uint16_t Ks[2][NK * KS];
   __shared__ __align__(16) uint8_t Vs[2][VBYTES];
@@ -183,9 +185,8 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
   }
   if (lane == 0) atomicMax(&pmax_s, pmax_w);
 
-  // ---- this thread's key staging unit: key n (slot j of block b), frequencies 8cp..8cp+7
-  // (a wave's 64 threads stage keys of one block: b is wave-uniform)
-  const bool kunit = KUNITS == NT || tid < KUNITS;
+  // ---- this thread's key staging unit: key kn (slot kj of block kb), frequencies
+  // FPT*cp .. FPT*cp+FPT-1 (a wave's 64 threads stage keys of one block: kb is uniform)
   const int kn = tid / CPT, cp = tid % CPT;
   const int kb = __builtin_amdgcn_readfirstlane((kn >> 4) & 3), kj = kn & 15;
   for (int i = tid; i < 16 * HALF; i += NT) {               // R(j) table, loop invariant
@@ -235,57 +236,86 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
   }
 
   const int n_kt = (T + 3) / 4;
-  u32x4 klo = {0, 0, 0, 0}, khi = {0, 0, 0, 0};
-  // raw keys of tile kt into (klo, khi)
+  KRaw klo{}, khi{};
+  // raw keys of a tile into (klo, khi); empty slots read as zero
   auto load_k = [&](const TileWords& tw) {
     const int nv = kb == 0 ? tw.nval[0] : kb == 1 ? tw.nval[1] : kb == 2 ? tw.nval[2] : tw.nval[3];
     const int id = kb == 0 ? tw.id[0] : kb == 1 ? tw.id[1] : kb == 2 ? tw.id[2] : tw.id[3];
-    klo = u32x4{0, 0, 0, 0};
-    khi = u32x4{0, 0, 0, 0};
-    if (kunit && kj < nv) {
-      const uint16_t* src = P.k_pool + (((size_t)id * P.Hkv + kvh) * kBlock + kj) * D + 8 * cp;
-      klo = *(const u32x4*)src;
-      khi = *(const u32x4*)(src + HALF);
+    klo = KRaw{};
+    khi = KRaw{};
+    if (kj < nv) {
+      const uint16_t* src = P.k_pool + (((size_t)id * P.Hkv + kvh) * kBlock + kj) * D + FPT * cp;
+      klo = *(const KRaw*)src;
+      khi = *(const KRaw*)(src + HALF);
     }
   };
-  // rotate (klo, khi) with table `buf` and store them as fp16 into Ks[buf]
-  auto store_k = [&](int buf) {
-    if (!kunit) return;
-    u32x4 ol, oh;
-    if (ROTATE) {
-      const float4* t4 = (const float4*)&tbl[buf][kb * HALF + 8 * cp];
-      const float4* j4 = (const float4*)&slot_cs[kj * HALF + 8 * cp];
+  // rotation of frequencies 2 i2, 2 i2 + 1 of the staged key by R(off_b - p_ref) R(kj),
+  // from (cos, sin) pairs read out of the tables; results packed as fp16
+  auto rot_pair = [&](const float4 cs, const float4 js, uint32_t xlo, uint32_t xhi) -> u32x2 {
+    float ra[2], rb[2];
 #pragma unroll
-      for (int i2 = 0; i2 < 4; ++i2) {
-        const float4 cs = t4[i2];                           // two (cos, sin) pairs: block
-        const float4 js = j4[i2];                           // two (cos, sin) pairs: slot
-        float ra[2], rb[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const float cb = u ? cs.z : cs.x, sb = u ? cs.w : cs.y;
-          const float cj = u ? js.z : js.x, sj = u ? js.w : js.y;
-          const float c = cb * cj - sb * sj;
-          const float s = sb * cj + cb * sj;
-          const float a = u ? bf_hi(klo[i2]) : bf_lo(klo[i2]);
-          const float b = u ? bf_hi(khi[i2]) : bf_lo(khi[i2]);
-          ra[u] = a * c - b * s;
-          rb[u] = a * s + b * c;
-        }
-        ol[i2] = pack_f16(ra[0], ra[1]);
-        oh[i2] = pack_f16(rb[0], rb[1]);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        ol[i] = pack_f16(bf_lo(klo[i]), bf_hi(klo[i]));
-        oh[i] = pack_f16(bf_lo(khi[i]), bf_hi(khi[i]));
-      }
+    for (int u = 0; u < 2; ++u) {
+      const float cb = u ? cs.z : cs.x, sb = u ? cs.w : cs.y;
+      const float cj = u ? js.z : js.x, sj = u ? js.w : js.y;
+      const float c = cb * cj - sb * sj;
+      const float sn = sb * cj + cb * sj;
+      const float a = u ? bf_hi(xlo) : bf_lo(xlo);
+      const float b = u ? bf_hi(xhi) : bf_lo(xhi);
+      ra[u] = a * c - b * sn;
+      rb[u] = a * sn + b * c;
     }
-    *(u32x4*)(Ks[buf] + kn * KS + 8 * cp) = ol;
-    *(u32x4*)(Ks[buf] + kn * KS + HALF + 8 * cp) = oh;
+    return u32x2{pack_f16(ra[0], ra[1]), pack_f16(rb[0], rb[1])};
   };
 
-  // S^T = K~ Q~^T - m for the key tile in Ks[buf] (scores in log2 units)
+  // Software pipeline over key tiles. Iteration kt holds S(kt) on entry; it
+  //   A) exponentiates S(kt) into P(kt) while the matrix cores compute S(kt+1);
+  //   B) runs O += V(kt)^T P(kt)^T while the vector ALUs rotate keys of tile kt+2;
+  // keys are staged two tiles ahead, values one tile ahead (both double-buffered), the
+  // (block, frequency) phase tables three tiles ahead. Work on tiles past the end reads
+  // empty blocks (zeros) and is discarded. Inside A and B the order of matrix, vector and
+  // LDS instructions is fixed by scheduling fences: each MFMA is followed by the vector
+  // work that hides under it, and LDS operands are fetched one MFMA group ahead.
+  uint32_t win = load_window(P, e0, T, 0, lane);           // words of tiles 0 .. 3
+  if (n_kt > 0) {
+    const TileWords t0 = tile_words<0>(P, win, T, kvlen, 0);
+    const TileWords t1 = tile_words<1>(P, win, T, kvlen, 0);
+    LA_MAKE_TABLE(t0, 0);
+    LA_MAKE_TABLE(t1, 1);
+    LA_ISSUE_V(t0, 0);
+    __syncthreads();                                         // tables 0, 1 visible
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {                         // keys of tiles 0 and 1
+      load_k(tt == 0 ? t0 : t1);
+      KRaw ol, oh;
+      if (ROTATE) {
+        const float4* t4 = (const float4*)&tbl[tt][kb * HALF + FPT * cp];
+        const float4* j4 = (const float4*)&slot_cs[kj * HALF + FPT * cp];
+#pragma unroll
+        for (int i2 = 0; i2 < FPT / 2; ++i2) {
+          const u32x2 r = rot_pair(t4[i2], j4[i2], klo[i2], khi[i2]);
+          ol[i2] = r[0];
+          oh[i2] = r[1];
+        }
+      } else {
+#pragma unroll
+        for (int i2 = 0; i2 < FPT / 2; ++i2) {
+          ol[i2] = pack_f16(bf_lo(klo[i2]), bf_hi(klo[i2]));
+          oh[i2] = pack_f16(bf_lo(khi[i2]), bf_hi(khi[i2]));
+        }
+      }
+      *(KRaw*)(Ks[tt] + kn * KS + FPT * cp) = ol;
+      *(KRaw*)(Ks[tt] + kn * KS + HALF + FPT * cp) = oh;
+    }
+    __syncthreads();                                         // tables 0, 1 consumed
+    const TileWords t2 = tile_words<2>(P, win, T, kvlen, 0);
+    LA_MAKE_TABLE(t2, 0);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);                        // vmcnt(0)
+  __syncthreads();
+  const int pmax_g = pmax_s;
+  f32x16 S0[2], S1[2];
+
+  // S^T = K~ Q~^T - m for the key tile in Ks[buf] (prologue only; the loop interleaves it)
   auto qk = [&](int buf, f32x16 (&sc)[2]) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) sc[t] = mfma32h(as_f16x8(ones_a), as_f16x8(qm), f32x16{});
@@ -299,43 +329,29 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
       }
     }
   };
-
-  // Software pipeline over key tiles. Iteration kt holds S(kt) on entry; it
-  //   A) exponentiates S(kt) into P(kt) while the matrix cores compute S(kt+1);
-  //   B) runs O += V(kt)^T P(kt)^T while the vector ALUs rotate keys of tile kt+2;
-  // keys are staged two tiles ahead, values one tile ahead (both double-buffered), the
-  // (block, frequency) phase tables three tiles ahead. Work on tiles past the end reads
-  // empty blocks (zeros) and is discarded.
-  uint32_t win = load_window(P, e0, T, 0, lane);           // words of tiles 0 .. 3
-  if (n_kt > 0) {
-    const TileWords t0 = tile_words<0>(P, win, T, kvlen, 0);
-    const TileWords t1 = tile_words<1>(P, win, T, kvlen, 0);
-    LA_MAKE_TABLE(t0, 0);
-    LA_MAKE_TABLE(t1, 1);
-    LA_ISSUE_V(t0, 0);
-    load_k(t1);
-    const u32x4 k1lo = klo, k1hi = khi;
-    load_k(t0);
-    __syncthreads();                                         // tables 0, 1 visible
-    store_k(0);
-    klo = k1lo;
-    khi = k1hi;
-    store_k(1);
-    __syncthreads();                                         // tables 0, 1 consumed
-    const TileWords t2 = tile_words<2>(P, win, T, kvlen, 0);
-    LA_MAKE_TABLE(t2, 0);
-  }
-  __builtin_amdgcn_s_waitcnt(0x0F70);                        // vmcnt(0)
-  __syncthreads();
-  const int pmax_g = pmax_s;
-  f32x16 S0[2], S1[2];
   if (n_kt > 0) qk(0, S0);
+
+  const int gi = lane >> 4, i16 = lane & 15;
+  const uint8_t* vlane = (const uint8_t*)Vs + (4 * hh + (i16 >> 2)) * VROW +
+                         16 * (2 * (gi & 1) + ((i16 & 3) >> 1)) + 8 * (i16 & 1);
+  const uint16_t* klane = Ks[0] + col * KS + 8 * hh;        // + buf * NK * KS
+  const uint16_t* qlane = qs + col * KS + 8 * hh;
 
   // one pipeline iteration: S(kt) in Sc on entry, S(kt+1) left in Sn
   auto step = [&](const int kt, f32x16 (&Sc)[2], f32x16 (&Sn)[2]) {
     const int cur = kt & 1, nxt = cur ^ 1;
+    // ---- staging issue: raw keys of tile kt+2, values of tile kt+1, words, table of kt+3 --
+    load_k(tile_words<2>(P, win, T, kvlen, kt));
+    {
+      const TileWords tn1 = tile_words<1>(P, win, T, kvlen, kt);
+      LA_ISSUE_V(tn1, nxt);
+    }
     const uint32_t win_next = load_window(P, e0, T, kt + 1, lane);   // used from step kt+1
-    // ---- rare paths: causal / ragged mask of S(kt), lazy rescale --------------------------
+    {
+      const TileWords tn3 = tile_words<3>(P, win, T, kvlen, kt);
+      LA_MAKE_TABLE(tn3, nxt);
+    }
+    // ---- rare paths: causal / ragged mask of S(kt) ------------------------------------
     {
       const TileWords tw = tile_words<0>(P, win, T, kvlen, kt);
       const bool visible = tw.kmin <= pmax_w && tw.kmin <= pmax_g;
@@ -351,12 +367,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
           }
       }
     }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, Sc[t][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mx = xor32_max(max32(Sc[0], Sc[1]));
     // the running max moves only when a row's max exceeds it by 2^8 (or on the row's first
     // visible key), so P = exp2(S) stays below 256; m is kept as the exact fp16 value the
     // matrix cores subtract, so the offset cancels in O / l
@@ -378,67 +389,142 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
 #pragma unroll
         for (int r = 0; r < 16; ++r) Sc[t][r] -= delta;
     }
+    __builtin_amdgcn_sched_barrier(0);
 
-    // ---- staging issue: values of tile kt+1, raw keys of tile kt+2, table of tile kt+3 ----
-    {
-      const TileWords tn1 = tile_words<1>(P, win, T, kvlen, kt);
-      LA_ISSUE_V(tn1, nxt);
-      load_k(tile_words<2>(P, win, T, kvlen, kt));
-      const TileWords tn3 = tile_words<3>(P, win, T, kvlen, kt);
-      LA_MAKE_TABLE(tn3, nxt);
-    }
-
-    // ---- A: P(kt) = exp2(S(kt)) on the VALU, S(kt+1) on the matrix cores --------------
-    // the row sum adds the bf16-rounded P that the matrix cores multiply (v_dot2 with 1, 1)
+    // ---- A: S(kt+1) on the matrix cores, P(kt) = exp2(S(kt)) on the VALU ---------------
+    // score pair q (0..15) of this lane: t = q / 8, kk = (q / 4) % 2, i = q % 4
     u32x4 bp[2][2];
     float rs0 = 0.f, rs1 = 0.f;
+    constexpr int SLOTS = 2 * NCH + 2;                        // MFMAs of S(kt+1)
+    constexpr int PPS = (16 + SLOTS - 1) / SLOTS;             // score pairs per MFMA slot
+    auto exp_slot = [&](const int slot) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float e0 = __builtin_amdgcn_exp2f(Sc[t][8 * kk + 2 * i]);
-          const float e1 = __builtin_amdgcn_exp2f(Sc[t][8 * kk + 2 * i + 1]);
-          bp[t][kk][i] = pack_bf16(e0, e1);
+      for (int u = 0; u < PPS; ++u) {
+        const int q = slot * PPS + u;
+        if (q < 16) {
+          const int t = q >> 3, kk = (q >> 2) & 1, i = q & 3;
+          const float x0 = __builtin_amdgcn_exp2f(Sc[t][8 * kk + 2 * i]);
+          const float x1 = __builtin_amdgcn_exp2f(Sc[t][8 * kk + 2 * i + 1]);
+          bp[t][kk][i] = pack_bf16(x0, x1);
           if (i & 1) rs1 = sum2_bf16(bp[t][kk][i], rs1);
           else rs0 = sum2_bf16(bp[t][kk][i], rs0);
         }
-    l += rs0 + rs1;
-    qk(nxt, Sn);
-#pragma unroll
-    for (int i = 0; i < 2 * (NCH + 1); ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // 1 MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // 1 LDS read
-      __builtin_amdgcn_sched_group_barrier(0x402, 3, 0);     // 3 VALU / transcendental
-    }
-
-    // ---- B: O += V(kt)^T P(kt)^T on the matrix cores, keys of tile kt+2 on the VALU -----
+      }
+    };
     {
-      const int gi = lane >> 4, i16 = lane & 15;
-      const uint8_t* vbase = Vs[cur] + (4 * hh + (i16 >> 2)) * VROW +
-                             16 * (2 * (gi & 1) + ((i16 & 3) >> 1)) + 8 * (i16 & 1);
+      const uint16_t* ka = klane + nxt * (NK * KS);
+      u32x4 a0 = *(const u32x4*)ka, a1 = *(const u32x4*)(ka + 32 * KS);
+      u32x4 b = *(const u32x4*)qlane;
+      Sn[0] = mfma32h(as_f16x8(ones_a), as_f16x8(qm), f32x16{});
+      exp_slot(0);
+      Sn[1] = mfma32h(as_f16x8(ones_a), as_f16x8(qm), f32x16{});
+      exp_slot(1);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-          for (int dt = 0; dt < D / 32; ++dt) {
-            const uint8_t* a1 = vbase + (32 * t + 16 * kk) * VROW + 64 * dt;
-            const u32x2 r1 = lds_read_tr((const uint16_t*)a1);
-            const u32x2 r2 = lds_read_tr((const uint16_t*)(a1 + 8 * VROW));
-            const u32x4 a = {r1[0], r1[1], r2[0], r2[1]};
-            o[dt] = mfma32(as_bf16x8(a), as_bf16x8(bp[t][kk]), o[dt]);
-          }
+      for (int c = 0; c < NCH; ++c) {
+        u32x4 na0 = a0, na1 = a1, nb = b;
+        if (c + 1 < NCH) {
+          na0 = *(const u32x4*)(ka + 16 * (c + 1));
+          na1 = *(const u32x4*)(ka + 32 * KS + 16 * (c + 1));
+          nb = *(const u32x4*)(qlane + 16 * (c + 1));
         }
+        Sn[0] = mfma32h(as_f16x8(a0), as_f16x8(b), Sn[0]);
+        exp_slot(2 + 2 * c);
+        Sn[1] = mfma32h(as_f16x8(a1), as_f16x8(b), Sn[1]);
+        exp_slot(3 + 2 * c);
+        __builtin_amdgcn_sched_barrier(0);
+        a0 = na0;
+        a1 = na1;
+        b = nb;
       }
     }
-    store_k(cur);                                            // keys of tile kt+2
+    l += rs0 + rs1;
+
+    // ---- B: O += V(kt)^T P(kt)^T on the matrix cores, keys of tile kt+2 on the VALU -----
+    // MFMA group g = (t, kk) = (g / 2, g % 2) takes D/32 MFMAs; rotation chunk g (two
+    // frequencies of the staged key) is cut into four pieces spread over those MFMAs.
+    {
+      const uint8_t* vb = vlane + cur * VBYTES;
+      auto vread = [&](int g, u32x4 (&va)[D / 32]) {
+        const int t = g >> 1, kk = g & 1;
 #pragma unroll
-    for (int i = 0; i < 4 * (D / 32); ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);     // 1 MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);     // 2 LDS reads
-      __builtin_amdgcn_sched_group_barrier(0x402, 4, 1);     // 4 VALU
+        for (int dt = 0; dt < D / 32; ++dt) {
+          const uint8_t* a1 = vb + (32 * t + 16 * kk) * VROW + 64 * dt;
+          const u32x2 r1 = lds_read_tr((const uint16_t*)a1);
+          const u32x2 r2 = lds_read_tr((const uint16_t*)(a1 + 8 * VROW));
+          va[dt] = u32x4{r1[0], r1[1], r2[0], r2[1]};
+        }
+      };
+      const float4* t4 = (const float4*)&tbl[cur][kb * HALF + FPT * cp];
+      const float4* j4 = (const float4*)&slot_cs[kj * HALF + FPT * cp];
+      KRaw ol, oh;
+      float rc[2], rsn[2], ra[2], rb[2];
+      // piece 0/1: angle of frequency u = piece; piece 2/3: rotate frequency u = piece - 2
+      auto piece = [&](const int g, const int pc, const float4 cs, const float4 js) {
+        if (pc < 2) {
+          const int u = pc;
+          const float cb = u ? cs.z : cs.x, sb = u ? cs.w : cs.y;
+          const float cj = u ? js.z : js.x, sj = u ? js.w : js.y;
+          rc[u] = cb * cj - sb * sj;
+          rsn[u] = sb * cj + cb * sj;
+          asm volatile("" ::"v"(rc[u]), "v"(rsn[u]));
+        } else {
+          const int u = pc - 2;
+          const float x = u ? bf_hi(klo[g]) : bf_lo(klo[g]);
+          const float y = u ? bf_hi(khi[g]) : bf_lo(khi[g]);
+          ra[u] = x * rc[u] - y * rsn[u];
+          rb[u] = x * rsn[u] + y * rc[u];
+          if (u == 1) {
+            ol[g] = pack_f16(ra[0], ra[1]);
+            oh[g] = pack_f16(rb[0], rb[1]);
+            asm volatile("" ::"v"(ol[g]), "v"(oh[g]));
+          }
+        }
+      };
+      auto plain = [&](const int g) {
+        ol[g] = pack_f16(bf_lo(klo[g]), bf_hi(klo[g]));
+        oh[g] = pack_f16(bf_lo(khi[g]), bf_hi(khi[g]));
+        asm volatile("" ::"v"(ol[g]), "v"(oh[g]));
+      };
+      u32x4 va[D / 32];
+      vread(0, va);
+      float4 cs = ROTATE ? t4[0] : float4{}, js = ROTATE ? j4[0] : float4{};
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        u32x4 vn[D / 32];
+        float4 csn = cs, jsn = js;
+        if (g + 1 < 4) {
+          vread(g + 1, vn);
+          if (ROTATE && g + 1 < FPT / 2) {
+            csn = t4[g + 1];
+            jsn = j4[g + 1];
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+          o[dt] = mfma32(as_bf16x8(va[dt]), as_bf16x8(bp[g >> 1][g & 1]), o[dt]);
+          if (g < FPT / 2) {
+            if (ROTATE) {
+#pragma unroll
+              for (int pc = dt * 4 / (D / 32); pc < (dt + 1) * 4 / (D / 32); ++pc)
+                piece(g, pc, cs, js);
+            } else if (dt == 0) {
+              plain(g);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (g + 1 < 4) {
+#pragma unroll
+          for (int dt = 0; dt < D / 32; ++dt) va[dt] = vn[dt];
+          cs = csn;
+          js = jsn;
+        }
+      }
+      *(KRaw*)(Ks[cur] + kn * KS + FPT * cp) = ol;           // keys of tile kt+2
+      *(KRaw*)(Ks[cur] + kn * KS + HALF + FPT * cp) = oh;
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);                      // vmcnt(0): values of tile kt+1
     __syncthreads();
@@ -452,7 +538,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
 #undef LA_ISSUE_V
 
   // ---- epilogue: O / l -> bf16 ----------------------------------------------------------
-  const float lt = l + __shfl_xor(l, 32);
+  const float lt = xor32_add(l);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   if (row_ok) {
     uint16_t* dst = P.out + ((size_t)(q0 + qi) * P.Hq + h) * D;
