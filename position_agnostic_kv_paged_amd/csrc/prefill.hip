@@ -52,30 +52,41 @@ __device__ __forceinline__ int sel4(const int (&a)[4], int b) {
 }
 
 // Words of key tiles kt .. kt+3 live in one VGPR ("window"): lane i < 16 holds the word of
-// entry 4 kt + i. Tile kt + d (d a compile-time 0..3) is decoded from lanes 4d .. 4d+3 with
-// readlane, so the loop issues one small vector load per key tile (for the next window)
-// instead of a dependent memory round trip per word.
+// entry 4 kt + i. The loop issues one small vector load per key tile (the next window);
+// each lane decodes its own word (block id, logical offset, valid keys) on the VALU, and
+// the scalars a step needs are read out of lanes 4d .. 4d+3 (tile kt + d) with readlane.
 __device__ __forceinline__ uint32_t load_window(const PrefillParams& P, int e0, int T, int kt,
                                                 int lane) {
   const int ent = 4 * kt + lane;
   return (lane < 16 && ent < T) ? P.block_meta[e0 + ent] : 0u;
 }
 
+struct WinDec {
+  int id, off, nv;                                       // this lane's entry, decoded
+};
+
+__device__ __forceinline__ WinDec decode_window(const PrefillParams& P, uint32_t win, int T,
+                                                int kvlen, int kt, int lane) {
+  const int ent = 4 * kt + lane;
+  WinDec d;
+  d.id = word_id(win);
+  d.off = word_offset(win, ent);
+  d.nv = (lane < 16) & (ent < T) & (d.id < P.num_blocks)     // out-of-pool id: never read
+             ? min(max(kvlen - ent * kBlock, 0), kBlock) : 0;
+  return d;
+}
+
+__device__ __forceinline__ int rl(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
+
 template <int d>
-__device__ __forceinline__ TileWords tile_words(const PrefillParams& P, uint32_t win, int T,
-                                                int kvlen, int kt0) {
+__device__ __forceinline__ TileWords tile_words(const WinDec& wd) {
   TileWords tw;
   tw.kmin = INT_MAX;
   tw.kmax = INT_MIN;
   tw.full = true;
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {                        // branch-free: scalar selects only
-    const int ent = 4 * (kt0 + d) + b;
-    const uint32_t w = (uint32_t)__builtin_amdgcn_readlane((int)win, 4 * d + b);
-    const int id = word_id(w);
-    const int off = word_offset(w, ent);
-    const int nv = (ent < T) & (id < P.num_blocks)       // out-of-pool id: never read
-                   ? min(max(kvlen - ent * kBlock, 0), kBlock) : 0;
+  for (int b = 0; b < 4; ++b) {
+    const int id = rl(wd.id, 4 * d + b), off = rl(wd.off, 4 * d + b), nv = rl(wd.nv, 4 * d + b);
     tw.id[b] = id;
     tw.off[b] = off;
     tw.nval[b] = nv;
@@ -109,8 +120,10 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
 
   __shared__ __align__(16) uint16_t Ks[2][NK * KS];
   __shared__ __align__(16) uint8_t Vs[2][VBYTES];
-  __shared__ __align__(16) float2 tbl[2][4 * HALF];      // cos/sin((off_b - p_ref) theta_k)
-  __shared__ __align__(16) float2 slot_cs[16 * HALF];    // cos/sin(j theta_k), j < 16
+  // (cos, sin) tables as float4 = two frequencies, laid out [block or slot][pair][thread]
+  // so that the staging threads of a wave read consecutive 16-byte words
+  __shared__ __align__(16) float4 tbl[2][4 * HALF / 2];  // cos/sin((off_b - p_ref) theta_k)
+  __shared__ __align__(16) float4 slot_cs[16 * HALF / 2]; // cos/sin(j theta_k), j < 16
   __shared__ __align__(16) uint16_t Qs[NW][32 * KS];     // each wave's rotated queries (fp16)
   __shared__ double fr_s[HALF];
   __shared__ int pmax_s;
@@ -189,10 +202,14 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
   // FPT*cp .. FPT*cp+FPT-1 (a wave's 64 threads stage keys of one block: kb is uniform)
   const int kn = tid / CPT, cp = tid % CPT;
   const int kb = __builtin_amdgcn_readfirstlane((kn >> 4) & 3), kj = kn & 15;
+  // float2 position of frequency f of row r (a block or a slot) in the tables
+  auto tpos = [&](int r, int f) {
+    return ((r * (FPT / 2) + (f % FPT) / 2) * CPT + f / FPT) * 2 + (f & 1);
+  };
   for (int i = tid; i < 16 * HALF; i += NT) {               // R(j) table, loop invariant
     float c, sn;
     rope_cos_sin(i / HALF, fr_s[i % HALF], c, sn);
-    slot_cs[i] = make_float2(c, sn);
+    ((float2*)slot_cs)[tpos(i / HALF, i % HALF)] = make_float2(c, sn);
   }
 
   // The running max m rides on the matrix cores: an extra 16-wide k-step with
@@ -213,7 +230,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
                  : b_ == 2 ? (TW).off[2] : (TW).off[3];                               \
     float c_, s_;                                                                     \
     rope_cos_sin(o_ - p_ref, fr_s[k_], c_, s_);                                       \
-    tbl[BUF][tid] = make_float2(c_, s_);                                              \
+    ((float2*)tbl[BUF])[tpos(b_, k_)] = make_float2(c_, s_);                          \
   }
   // values of a key tile straight into LDS: slot (row R, chunk c) of the padded tile; pad
   // slots and invalid rows read the zeroed workspace chunk
@@ -238,9 +255,9 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
   const int n_kt = (T + 3) / 4;
   KRaw klo{}, khi{};
   // raw keys of a tile into (klo, khi); empty slots read as zero
-  auto load_k = [&](const TileWords& tw) {
-    const int nv = kb == 0 ? tw.nval[0] : kb == 1 ? tw.nval[1] : kb == 2 ? tw.nval[2] : tw.nval[3];
-    const int id = kb == 0 ? tw.id[0] : kb == 1 ? tw.id[1] : kb == 2 ? tw.id[2] : tw.id[3];
+  // (key staging reads block kb of tile kt + d: lane 4 d + kb of the decoded window)
+  auto load_k = [&](const WinDec& wd, int d) {
+    const int nv = rl(wd.nv, 4 * d + kb), id = rl(wd.id, 4 * d + kb);
     klo = KRaw{};
     khi = KRaw{};
     if (kj < nv) {
@@ -277,22 +294,23 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
   // work that hides under it, and LDS operands are fetched one MFMA group ahead.
   uint32_t win = load_window(P, e0, T, 0, lane);           // words of tiles 0 .. 3
   if (n_kt > 0) {
-    const TileWords t0 = tile_words<0>(P, win, T, kvlen, 0);
-    const TileWords t1 = tile_words<1>(P, win, T, kvlen, 0);
+    const WinDec wd = decode_window(P, win, T, kvlen, 0, lane);
+    const TileWords t0 = tile_words<0>(wd);
+    const TileWords t1 = tile_words<1>(wd);
     LA_MAKE_TABLE(t0, 0);
     LA_MAKE_TABLE(t1, 1);
     LA_ISSUE_V(t0, 0);
     __syncthreads();                                         // tables 0, 1 visible
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {                         // keys of tiles 0 and 1
-      load_k(tt == 0 ? t0 : t1);
+      load_k(wd, tt);
       KRaw ol, oh;
       if (ROTATE) {
-        const float4* t4 = (const float4*)&tbl[tt][kb * HALF + FPT * cp];
-        const float4* j4 = (const float4*)&slot_cs[kj * HALF + FPT * cp];
+        const float4* t4 = &tbl[tt][kb * (FPT / 2) * CPT + cp];
+        const float4* j4 = &slot_cs[kj * (FPT / 2) * CPT + cp];
 #pragma unroll
         for (int i2 = 0; i2 < FPT / 2; ++i2) {
-          const u32x2 r = rot_pair(t4[i2], j4[i2], klo[i2], khi[i2]);
+          const u32x2 r = rot_pair(t4[i2 * CPT], j4[i2 * CPT], klo[i2], khi[i2]);
           ol[i2] = r[0];
           oh[i2] = r[1];
         }
@@ -307,7 +325,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
       *(KRaw*)(Ks[tt] + kn * KS + HALF + FPT * cp) = oh;
     }
     __syncthreads();                                         // tables 0, 1 consumed
-    const TileWords t2 = tile_words<2>(P, win, T, kvlen, 0);
+    const TileWords t2 = tile_words<2>(wd);
     LA_MAKE_TABLE(t2, 0);
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);                        // vmcnt(0)
@@ -341,19 +359,20 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
   auto step = [&](const int kt, f32x16 (&Sc)[2], f32x16 (&Sn)[2]) {
     const int cur = kt & 1, nxt = cur ^ 1;
     // ---- staging issue: raw keys of tile kt+2, values of tile kt+1, words, table of kt+3 --
-    load_k(tile_words<2>(P, win, T, kvlen, kt));
+    const WinDec wd = decode_window(P, win, T, kvlen, kt, lane);
+    load_k(wd, 2);
     {
-      const TileWords tn1 = tile_words<1>(P, win, T, kvlen, kt);
+      const TileWords tn1 = tile_words<1>(wd);
       LA_ISSUE_V(tn1, nxt);
     }
     const uint32_t win_next = load_window(P, e0, T, kt + 1, lane);   // used from step kt+1
     {
-      const TileWords tn3 = tile_words<3>(P, win, T, kvlen, kt);
+      const TileWords tn3 = tile_words<3>(wd);
       LA_MAKE_TABLE(tn3, nxt);
     }
     // ---- rare paths: causal / ragged mask of S(kt) ------------------------------------
     {
-      const TileWords tw = tile_words<0>(P, win, T, kvlen, kt);
+      const TileWords tw = tile_words<0>(wd);
       const bool visible = tw.kmin <= pmax_w && tw.kmin <= pmax_g;
       if (!(visible && tw.full && tw.kmax <= pmin_w)) {
 #pragma unroll
@@ -455,8 +474,8 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
           va[dt] = u32x4{r1[0], r1[1], r2[0], r2[1]};
         }
       };
-      const float4* t4 = (const float4*)&tbl[cur][kb * HALF + FPT * cp];
-      const float4* j4 = (const float4*)&slot_cs[kj * HALF + FPT * cp];
+      const float4* t4 = &tbl[cur][kb * (FPT / 2) * CPT + cp];
+      const float4* j4 = &slot_cs[kj * (FPT / 2) * CPT + cp];
       KRaw ol, oh;
       float rc[2], rsn[2], ra[2], rb[2];
       // piece 0/1: angle of frequency u = piece; piece 2/3: rotate frequency u = piece - 2
@@ -497,8 +516,8 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
         if (g + 1 < 4) {
           vread(g + 1, vn);
           if (ROTATE && g + 1 < FPT / 2) {
-            csn = t4[g + 1];
-            jsn = j4[g + 1];
+            csn = t4[(g + 1) * CPT];
+            jsn = j4[(g + 1) * CPT];
           }
         }
         __builtin_amdgcn_sched_barrier(0);
