@@ -54,20 +54,22 @@ __device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u <<
 __device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 
 // Round two floats to bf16 (nearest even) and pack: a -> low half, b -> high half.
+// One v_cvt_pk_bf16_f32 on gfx950.
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-  __bf16 x = (__bf16)a, y = (__bf16)b;
-  uint16_t ux = __builtin_bit_cast(uint16_t, x), uy = __builtin_bit_cast(uint16_t, y);
-  return (uint32_t)ux | ((uint32_t)uy << 16);
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 h2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){a, b}, h2));
 }
 
 // Round two floats to fp16 (nearest even) and pack. The rotated query/key operands of the
 // score products are carried in fp16: they come out of fp32 rotation arithmetic anyway,
 // and fp16 keeps 3 more mantissa bits than bf16 at the same MFMA rate (element magnitudes
 // must stay below 65504).
+// One v_cvt_pk_f16_f32 on gfx950.
 __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
-  _Float16 x = (_Float16)a, y = (_Float16)b;
-  uint16_t ux = __builtin_bit_cast(uint16_t, x), uy = __builtin_bit_cast(uint16_t, y);
-  return (uint32_t)ux | ((uint32_t)uy << 16);
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){a, b}, h2));
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -117,17 +119,29 @@ __device__ __forceinline__ float xor32_add(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Tree reductions of 32 values (no long dependency chains).
+// max(a, b, c) in one v_max3_f32. Written as inline asm: fmaxf must quiet signalling NaNs,
+// so the compiler adds a canonicalising v_max per operand it cannot prove canonical (every
+// MFMA result); scores here are finite or -inf.
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// Max of 32 values: four independent chains of v_max3 (two values per instruction).
 __device__ __forceinline__ float max32(const f32x16& a, const f32x16& b) {
-  float m[8];
+  float c[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    m[i] = fmaxf(fmaxf(a[2 * i], a[2 * i + 1]), fmaxf(b[2 * i], b[2 * i + 1]));
-#pragma unroll
-  for (int w = 4; w >= 1; w >>= 1)
-#pragma unroll
-    for (int i = 0; i < w; ++i) m[i] = fmaxf(m[i], m[i + w]);
-  return m[0];
+  for (int j = 0; j < 4; ++j) {
+    const f32x16& v = j < 2 ? a : b;
+    const int o = (j & 1) * 8;
+    float x = max3f(v[o], v[o + 1], v[o + 2]);
+    x = max3f(x, v[o + 3], v[o + 4]);
+    x = max3f(x, v[o + 5], v[o + 6]);
+    c[j] = x;
+  }
+  const float t0 = max3f(c[0], c[1], a[7]), t1 = max3f(c[2], c[3], b[7]);
+  return max3f(max3f(t0, t1, a[15]), b[15], b[15]);
 }
 
 __device__ __forceinline__ float wave_max(float v) {

@@ -71,7 +71,7 @@ __device__ __forceinline__ WinDec decode_window(const PrefillParams& P, uint32_t
   WinDec d;
   d.id = word_id(win);
   d.off = word_offset(win, ent);
-  d.nv = (lane < 16) & (ent < T) & (d.id < P.num_blocks)     // out-of-pool id: never read
+  d.nv = ((lane < 16) & (ent < T) & (d.id < P.num_blocks))   // out-of-pool id: never read
              ? min(max(kvlen - ent * kBlock, 0), kBlock) : 0;
   return d;
 }
