@@ -49,6 +49,14 @@ __device__ __forceinline__ void rope_cos_sin(int n, double f, float& c, float& s
   c = __builtin_amdgcn_cosf(r);
 }
 
+// sin(2 pi (frac(n f) + quarter)) from an exact double-precision phase; quarter = 0.25
+// gives the cosine.
+__device__ __forceinline__ float rope_sin_rev(int n, double f, float quarter) {
+  double x = (double)n * f;
+  x = x - __builtin_floor(x);
+  return __builtin_amdgcn_sinf((float)x + quarter);
+}
+
 // ---- bf16 helpers --------------------------------------------------------------------------
 __device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
@@ -126,6 +134,16 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
   float r;
   asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
   return r;
+}
+
+// Max of 16 values: two chains of v_max3.
+__device__ __forceinline__ float max16(const f32x16& v) {
+  float x = max3f(v[0], v[1], v[2]), y = max3f(v[8], v[9], v[10]);
+  x = max3f(x, v[3], v[4]);
+  y = max3f(y, v[11], v[12]);
+  x = max3f(x, v[5], v[6]);
+  y = max3f(y, v[13], v[14]);
+  return max3f(max3f(x, v[7], v[15]), y, y);
 }
 
 // Max of 32 values: four independent chains of v_max3 (two values per instruction).

@@ -57,8 +57,10 @@ __device__ __forceinline__ int sel4(const int (&a)[4], int b) {
 // the scalars a step needs are read out of lanes 4d .. 4d+3 (tile kt + d) with readlane.
 __device__ __forceinline__ uint32_t load_window(const PrefillParams& P, int e0, int T, int kt,
                                                 int lane) {
-  const int ent = 4 * kt + lane;
-  return (lane < 16 && ent < T) ? P.block_meta[e0 + ent] : 0u;
+  // every lane loads (no branch): lanes past the table read its last word, which the
+  // decode marks empty (T >= 1 whenever a key tile exists)
+  const int ent = min(4 * kt + lane, T - 1);
+  return P.block_meta[e0 + max(ent, 0)];
 }
 
 struct WinDec {
@@ -77,6 +79,13 @@ __device__ __forceinline__ WinDec decode_window(const PrefillParams& P, uint32_t
 }
 
 __device__ __forceinline__ int rl(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
+
+// c ? a : b for pointers as an integer blend: a plain select of an expensive address may be
+// turned into a branch, which would split the interleaved MFMA block it sits in
+__device__ __forceinline__ const void* blend_ptr(bool c, const void* a, const void* b) {
+  const uint64_t m = 0 - (uint64_t)c;
+  return (const void*)(((uint64_t)a & m) | ((uint64_t)b & ~m));
+}
 
 template <int d>
 __device__ __forceinline__ TileWords tile_words(const WinDec& wd) {
@@ -222,35 +231,41 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) o[dt] = f32x16{};
 
-  // table of a key tile: thread (b, k) computes cos/sin((off_b - p_ref) theta_k)
-#define LA_MAKE_TABLE(TW, BUF)                                                        \
-  if (tid < 4 * HALF) {                                                               \
-    const int b_ = tid / HALF, k_ = tid % HALF;                                       \
-    const int o_ = b_ == 0 ? (TW).off[0] : b_ == 1 ? (TW).off[1]                      \
-                 : b_ == 2 ? (TW).off[2] : (TW).off[3];                               \
-    float c_, s_;                                                                     \
-    rope_cos_sin(o_ - p_ref, fr_s[k_], c_, s_);                                       \
-    ((float2*)tbl[BUF])[tpos(b_, k_)] = make_float2(c_, s_);                          \
-  }
-  // values of a key tile straight into LDS: slot (row R, chunk c) of the padded tile; pad
-  // slots and invalid rows read the zeroed workspace chunk
-#define LA_ISSUE_V(TW, BUF)                                                           \
-  _Pragma("unroll") for (int i_ = 0; i_ < (VINST + NW - 1) / NW; ++i_) {              \
-    const int I_ = w + NW * i_;                                                       \
-    if (I_ < VINST) {                                                                 \
-      const int slot_ = I_ * 64 + lane;                                               \
-      const int R_ = slot_ / SPR, c_ = slot_ % SPR;                                   \
-      const int b_ = R_ >> 4, j_ = R_ & 15;                                           \
-      const int nv_ = b_ == 0 ? (TW).nval[0] : b_ == 1 ? (TW).nval[1]                 \
-                    : b_ == 2 ? (TW).nval[2] : (TW).nval[3];                          \
-      const int id_ = b_ == 0 ? (TW).id[0] : b_ == 1 ? (TW).id[1]                     \
-                    : b_ == 2 ? (TW).id[2] : (TW).id[3];                              \
-      const void* src_ = P.zero;                                                      \
-      if ((c_ < D / 8) & (j_ < nv_))                                                  \
-        src_ = P.v_pool + (((size_t)id_ * P.Hkv + kvh) * kBlock + j_) * D + 8 * c_;   \
-      g2lds16p(src_, Vs[BUF] + I_ * 1024);                                            \
-    }                                                                                 \
-  }
+  // table of a key tile: cos and sin((off_b - p_ref) theta_k) for 4 blocks x HALF
+  // frequencies = 8 HALF values, one per thread (threads beyond repeat a value and store
+  // the same bits): value v is entry v / 2, cosine if v is even (cos x = sin(x + 1/4 rev)).
+  // Branch-free so that it can sit between MFMAs of one basic block.
+  const int tab_v = tid % (8 * HALF);
+  const int tab_b = __builtin_amdgcn_readfirstlane((tab_v >> 1) / HALF);   // wave-uniform
+  const double tab_f = fr_s[(tab_v >> 1) % HALF];          // this thread's frequency
+  const float tab_quarter = (tab_v & 1) ? 0.f : 0.25f;
+  const int tab_pos = 2 * tpos(tab_b, (tab_v >> 1) % HALF) + (tab_v & 1);
+  // (the per-lane block choice selects among readlane results, never indexes an array)
+  auto make_table = [&](const WinDec& wd, int d, int buf) __attribute__((always_inline)) {
+    const int o = rl(wd.off, 4 * d + tab_b);
+    ((float*)tbl[buf])[tab_pos] = rope_sin_rev(o - p_ref, tab_f, tab_quarter);
+  };
+  // values of tile kt + d straight into LDS, wave-wide instruction i of this wave: slot
+  // (row R, chunk c) of the padded tile; pad slots and invalid rows read the zeroed chunk
+  auto issue_v = [&](const WinDec& wd, int d, int buf, int i) __attribute__((always_inline)) {
+    const int I = w + NW * i;
+    const int slot = I * 64 + lane;
+    const int R = slot / SPR, c = slot % SPR;
+    const int b = R >> 4, j = R & 15;
+    const int n0 = rl(wd.nv, 4 * d), n1 = rl(wd.nv, 4 * d + 1);
+    const int n2 = rl(wd.nv, 4 * d + 2), n3 = rl(wd.nv, 4 * d + 3);
+    const int i0 = rl(wd.id, 4 * d), i1 = rl(wd.id, 4 * d + 1);
+    const int i2 = rl(wd.id, 4 * d + 2), i3 = rl(wd.id, 4 * d + 3);
+    const int nv = b == 0 ? n0 : b == 1 ? n1 : b == 2 ? n2 : n3;
+    const int id = b == 0 ? i0 : b == 1 ? i1 : b == 2 ? i2 : i3;
+    const void* src = blend_ptr((c < D / 8) & (j < nv),
+                                P.v_pool + (((size_t)id * P.Hkv + kvh) * kBlock + j) * D + 8 * c,
+                                P.zero);
+    g2lds16p(src, Vs[buf] + I * 1024);
+  };
+  constexpr int VPW = VINST / NW;                           // value loads every wave issues
+  constexpr int VREM = VINST % NW;                          // + one more on waves < VREM
+  static_assert(VPW >= 1 && VPW <= 3, "value loads are placed in the first score k-steps");
 
   const int n_kt = (T + 3) / 4;
   KRaw klo{}, khi{};
@@ -258,13 +273,11 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
   // (key staging reads block kb of tile kt + d: lane 4 d + kb of the decoded window)
   auto load_k = [&](const WinDec& wd, int d) {
     const int nv = rl(wd.nv, 4 * d + kb), id = rl(wd.id, 4 * d + kb);
-    klo = KRaw{};
-    khi = KRaw{};
-    if (kj < nv) {
-      const uint16_t* src = P.k_pool + (((size_t)id * P.Hkv + kvh) * kBlock + kj) * D + FPT * cp;
-      klo = *(const KRaw*)src;
-      khi = *(const KRaw*)(src + HALF);
-    }
+    // branch-free: empty slots load from the zeroed workspace chunk
+    const uint16_t* src = (const uint16_t*)blend_ptr(
+        kj < nv, P.k_pool + (((size_t)id * P.Hkv + kvh) * kBlock + kj) * D + FPT * cp, P.zero);
+    klo = *(const KRaw*)src;
+    khi = *(const KRaw*)(src + HALF);
   };
   // rotation of frequencies 2 i2, 2 i2 + 1 of the staged key by R(off_b - p_ref) R(kj),
   // from (cos, sin) pairs read out of the tables; results packed as fp16
@@ -289,17 +302,19 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
   //   B) runs O += V(kt)^T P(kt)^T while the vector ALUs rotate keys of tile kt+2;
   // keys are staged two tiles ahead, values one tile ahead (both double-buffered), the
   // (block, frequency) phase tables three tiles ahead. Work on tiles past the end reads
-  // empty blocks (zeros) and is discarded. Inside A and B the order of matrix, vector and
-  // LDS instructions is fixed by scheduling fences: each MFMA is followed by the vector
-  // work that hides under it, and LDS operands are fetched one MFMA group ahead.
+  // empty blocks (zeros) and is discarded. Inside A and B the order of matrix, vector,
+  // memory and LDS instructions is fixed by scheduling fences: each MFMA is followed by the
+  // vector work that hides under it, LDS operands are fetched one MFMA group ahead, and the
+  // loads for later tiles are spread over A's k-steps so that the vector memory path
+  // overlaps the matrix cores instead of stalling every wave right after the barrier.
   uint32_t win = load_window(P, e0, T, 0, lane);           // words of tiles 0 .. 3
   if (n_kt > 0) {
     const WinDec wd = decode_window(P, win, T, kvlen, 0, lane);
-    const TileWords t0 = tile_words<0>(wd);
-    const TileWords t1 = tile_words<1>(wd);
-    LA_MAKE_TABLE(t0, 0);
-    LA_MAKE_TABLE(t1, 1);
-    LA_ISSUE_V(t0, 0);
+    make_table(wd, 0, 0);
+    make_table(wd, 1, 1);
+#pragma unroll
+    for (int i = 0; i < VPW; ++i) issue_v(wd, 0, 0, i);
+    if (w < VREM) issue_v(wd, 0, 0, VPW);
     __syncthreads();                                         // tables 0, 1 visible
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {                         // keys of tiles 0 and 1
@@ -325,8 +340,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
       *(KRaw*)(Ks[tt] + kn * KS + HALF + FPT * cp) = oh;
     }
     __syncthreads();                                         // tables 0, 1 consumed
-    const TileWords t2 = tile_words<2>(wd);
-    LA_MAKE_TABLE(t2, 0);
+    make_table(wd, 2, 0);
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);                        // vmcnt(0)
   __syncthreads();
@@ -348,6 +362,8 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
     }
   };
   if (n_kt > 0) qk(0, S0);
+  WinDec wdc = decode_window(P, win, T, kvlen, 0, lane);
+  float mxc = xor32_max(max32(S0[0], S0[1]));
 
   const int gi = lane >> 4, i16 = lane & 15;
   const uint8_t* vlane = (const uint8_t*)Vs + (4 * hh + (i16 >> 2)) * VROW +
@@ -358,18 +374,14 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
   // one pipeline iteration: S(kt) in Sc on entry, S(kt+1) left in Sn
   auto step = [&](const int kt, f32x16 (&Sc)[2], f32x16 (&Sn)[2]) {
     const int cur = kt & 1, nxt = cur ^ 1;
-    // ---- staging issue: raw keys of tile kt+2, values of tile kt+1, words, table of kt+3 --
-    const WinDec wd = decode_window(P, win, T, kvlen, kt, lane);
-    load_k(wd, 2);
-    {
-      const TileWords tn1 = tile_words<1>(wd);
-      LA_ISSUE_V(tn1, nxt);
-    }
-    const uint32_t win_next = load_window(P, e0, T, kt + 1, lane);   // used from step kt+1
-    {
-      const TileWords tn3 = tile_words<3>(wd);
-      LA_MAKE_TABLE(tn3, nxt);
-    }
+    // wdc (decoded words of tiles kt .. kt+3) and mxc (row max of S(kt) before masking)
+    // were computed under the MFMAs of the previous iteration
+    const WinDec wd = wdc;
+    uint32_t win_next = 0;
+    WinDec wdn;
+    float h0 = 0.f, h1 = 0.f;
+    if (w < VREM) issue_v(wd, 1, nxt, VPW);                   // the odd value loads
+    float mx = mxc;
     // ---- rare paths: causal / ragged mask of S(kt) ------------------------------------
     {
       const TileWords tw = tile_words<0>(wd);
@@ -384,9 +396,9 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
             const bool ok = visible & (j < tw.nval[b]) & (tw.off[b] + j <= p);
             Sc[t][r] = ok ? Sc[t][r] : -INFINITY;
           }
+        mx = xor32_max(max32(Sc[0], Sc[1]));
       }
     }
-    const float mx = xor32_max(max32(Sc[0], Sc[1]));
     // the running max moves only when a row's max exceeds it by 2^8 (or on the row's first
     // visible key), so P = exp2(S) stays below 256; m is kept as the exact fp16 value the
     // matrix cores subtract, so the offset cancels in O / l
@@ -427,6 +439,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
           bp[t][kk][i] = pack_bf16(x0, x1);
           if (i & 1) rs1 = sum2_bf16(bp[t][kk][i], rs1);
           else rs0 = sum2_bf16(bp[t][kk][i], rs0);
+          asm volatile("" ::"v"(bp[t][kk][i]));                // keep it in this MFMA slot
         }
       }
     };
@@ -436,6 +449,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
       u32x4 b = *(const u32x4*)qlane;
       Sn[0] = mfma32h(as_f16x8(ones_a), as_f16x8(qm), f32x16{});
       exp_slot(0);
+      load_k(wd, 2);                                        // raw keys of tile kt+2
       Sn[1] = mfma32h(as_f16x8(ones_a), as_f16x8(qm), f32x16{});
       exp_slot(1);
       __builtin_amdgcn_sched_barrier(0);
@@ -449,6 +463,12 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
         }
         Sn[0] = mfma32h(as_f16x8(a0), as_f16x8(b), Sn[0]);
         exp_slot(2 + 2 * c);
+        // staging for later tiles, spread over the k-steps so that the vector memory
+        // path works while the matrix cores do: values of tile kt+1 (k-steps 0..2), the
+        // next word window (k-step 2), the phase table of tile kt+3 (k-step 3)
+        if (c < VPW) issue_v(wd, 1, nxt, c);
+        if (c == 2) win_next = load_window(P, e0, T, kt + 1, lane);
+        if (c == 3) make_table(wd, 3, nxt);
         Sn[1] = mfma32h(as_f16x8(a1), as_f16x8(b), Sn[1]);
         exp_slot(3 + 2 * c);
         __builtin_amdgcn_sched_barrier(0);
@@ -521,6 +541,20 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
           }
         }
         __builtin_amdgcn_sched_barrier(0);
+        // next iteration's inputs, under these MFMAs: decoded words of tiles kt+1 ..
+        // kt+4 (group 1) and the row max of S(kt+1) (groups 2, 3)
+        if (g == 1) {
+          wdn = decode_window(P, win_next, T, kvlen, kt + 1, lane);
+          asm volatile("" ::"v"(wdn.id), "v"(wdn.off), "v"(wdn.nv));
+        }
+        if (g == 2) {
+          h0 = max16(Sn[0]);
+          asm volatile("" ::"v"(h0));
+        }
+        if (g == 3) {
+          h1 = max16(Sn[1]);
+          asm volatile("" ::"v"(h1));
+        }
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
           o[dt] = mfma32(as_bf16x8(va[dt]), as_bf16x8(bp[g >> 1][g & 1]), o[dt]);
@@ -545,16 +579,15 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
       *(KRaw*)(Ks[cur] + kn * KS + FPT * cp) = ol;           // keys of tile kt+2
       *(KRaw*)(Ks[cur] + kn * KS + HALF + FPT * cp) = oh;
     }
+    wdc = wdn;
+    mxc = xor32_max(max3f(h0, h1, h1));
     __builtin_amdgcn_s_waitcnt(0x0F70);                      // vmcnt(0): values of tile kt+1
     __syncthreads();
-    win = win_next;
   };
   for (int kt = 0; kt < n_kt; kt += 2) {                     // unrolled x2: S0 <-> S1
     step(kt, S0, S1);
     if (kt + 1 < n_kt) step(kt + 1, S1, S0);
   }
-#undef LA_MAKE_TABLE
-#undef LA_ISSUE_V
 
   // ---- epilogue: O / l -> bf16 ----------------------------------------------------------
   const float lt = xor32_add(l);
