@@ -422,6 +422,10 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
     }
     __builtin_amdgcn_sched_barrier(0);
 
+    // Waves w and w + NW/2 share a SIMD and run the same phase; the issue arbiter favours
+    // the older one, which then idles at the barrier while the other finishes alone.
+    // Alternating wave priorities between the two blocks lets both finish together.
+    if (w < NW / 2) __builtin_amdgcn_s_setprio(2); else __builtin_amdgcn_s_setprio(1);
     // ---- A: S(kt+1) on the matrix cores, P(kt) = exp2(S(kt)) on the VALU ---------------
     // score pair q (0..15) of this lane: t = q / 8, kk = (q / 4) % 2, i = q % 4
     u32x4 bp[2][2];
@@ -479,6 +483,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
     }
     l += rs0 + rs1;
 
+    if (w < NW / 2) __builtin_amdgcn_s_setprio(1); else __builtin_amdgcn_s_setprio(2);
     // ---- B: O += V(kt)^T P(kt)^T on the matrix cores, keys of tile kt+2 on the VALU -----
     // MFMA group g = (t, kk) = (g / 2, g % 2) takes D/32 MFMAs; rotation chunk g (two
     // frequencies of the staged key) is cut into four pieces spread over those MFMAs.
@@ -579,6 +584,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
       *(KRaw*)(Ks[cur] + kn * KS + FPT * cp) = ol;           // keys of tile kt+2
       *(KRaw*)(Ks[cur] + kn * KS + HALF + FPT * cp) = oh;
     }
+    __builtin_amdgcn_s_setprio(0);
     wdc = wdn;
     mxc = xor32_max(max3f(h0, h1, h1));
     __builtin_amdgcn_s_waitcnt(0x0F70);                      // vmcnt(0): values of tile kt+1
