@@ -104,6 +104,70 @@ def half_inputs(wl, seqs, dev, pool):
                 out=torch.empty_like(q))
 
 
+def _counter_rows(run_dir):
+    """Rows of the rocprofv3 --pmc csv output under run_dir."""
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"),
+                              recursive=True)):
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    if not rows:
+        raise SystemExit(f"no *counter_collection.csv under {run_dir}")
+    return rows
+
+
+def record_traffic(fetch_dir, write_dir):
+    """Write profiles/traffic.json from one FETCH_SIZE and one WRITE_SIZE rocprofv3 run of
+    this script: per-launch KiB of each attention kernel, scaled by what the same counter
+    reads on the calibration copy of COPY_CALIBRATION_BYTES (found as the dispatch whose
+    WRITE_SIZE is closest to that size; both runs dispatch in the same order)."""
+    fetch, write = _counter_rows(fetch_dir), _counter_rows(write_dir)
+
+    def per_dispatch(rows, counter):
+        out = {}
+        for r in rows:
+            if r["Counter_Name"] == counter:
+                key = (int(r["Dispatch_Id"]), r["Kernel_Name"])
+                out[key] = out.get(key, 0.0) + float(r["Counter_Value"])
+        return out
+    f, w = per_dispatch(fetch, "FETCH_SIZE"), per_dispatch(write, "WRITE_SIZE")
+    target_kib = COPY_CALIBRATION_BYTES / 1024
+    # the copy writes the calibration size and, unlike the fill of its source, reads it too
+    near = [k for k in w if abs(w[k] - target_kib) < 0.05 * target_kib and k in f]
+    if not near:
+        raise SystemExit("calibration copy not found in the counter runs")
+    cal = max(near, key=lambda k: f[k])
+    rec = {"_about": "HBM-side bytes per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE "
+                     "(KiB per dispatch), each scaled by the factor that maps the same counter "
+                     "on a plain device copy of known size (run once inside bench.py) to that "
+                     "size. Valid while the kernel sources hash to source_hash.",
+           "workload": WORKLOAD,
+           "calibration": {"copy_bytes": COPY_CALIBRATION_BYTES, "fetch_kib_on_copy": f[cal],
+                           "write_kib_on_copy": w[cal],
+                           "fetch_factor": target_kib / f[cal],
+                           "write_factor": target_kib / w[cal]}}
+    for kernel, tag in (("prefill_kernel", "lazyattn::prefill_kernel<"),
+                        ("decode_kernel", "lazyattn::decode_kernel<")):
+        # launches of the half under test: a prefill call also launches the decode kernel
+        # (for its single-row sequences, none here), which then finds no work
+        keys = [k for k in f if tag in k[1] and k in w]
+        if not keys:
+            continue
+        top = max(f[k] for k in keys)
+        keys = [k for k in keys if f[k] > 0.01 * top]
+        fk, wk = [f[k] for k in keys], [w[k] for k in keys]
+        fkib, wkib = float(np.mean(fk)), float(np.mean(wk))
+        rec[kernel] = {"source_hash": kernel_source_hash(kernel), "dispatches": len(fk),
+                       "fetch_kib": fkib, "write_kib": wkib,
+                       "hbm_bytes_per_launch": 1024 * (fkib * rec["calibration"]["fetch_factor"]
+                                                       + wkib * rec["calibration"]["write_factor"])}
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec, indent=1))
+
+
 def cpu_baseline(wl, pre_seqs, dec_seqs, budget_s=15.0):
     """The float64 oracle (as it stands) on a bounded sample of the same batch."""
     import oracle
@@ -114,10 +178,9 @@ def cpu_baseline(wl, pre_seqs, dec_seqs, budget_s=15.0):
         blas = 1
     cores = len(os.sched_getaffinity(0))
     k_bits, v_bits = wl.k_bits, wl.v_bits
-    # prefill sample: 32 query rows of the first prefill request (all 64 heads)
+    # prefill sample: the whole first prefill request (all its query rows, all 64 heads)
     s = pre_seqs[0]
-    q0 = int(wl.q_indptr[s])
-    rows = q0 + np.linspace(0, int(wl.q_indptr[s + 1]) - q0 - 1, 32).astype(np.int64)
+    rows = np.arange(int(wl.q_indptr[s]), int(wl.q_indptr[s + 1]), dtype=np.int64)
     t0 = time.perf_counter()
     ids = [None] * wl.num_seqs
     ids[s] = wl.compact_ids(s)
@@ -147,8 +210,8 @@ def cpu_baseline(wl, pre_seqs, dec_seqs, budget_s=15.0):
     return {"value": pre_flops / t_pre / 1e12, "unit": "TFLOP/s", "cores": cores,
             "blas_threads": blas, "kind": "oracle",
             "decode": {"value": dbytes / t_dec / 1e9, "unit": "GB/s"},
-            "sample": f"prefill: 32 query rows x 64 heads of one 16896-key prefill request "
-                      f"({t_pre:.1f} s); decode: {done} whole decode requests "
+            "sample": f"prefill: one whole request ({len(rows)} query rows x {wl.Hq} heads "
+                      f"against {kv} keys, {t_pre:.1f} s); decode: {done} whole decode requests "
                       f"({t_dec:.1f} s); float64 numpy, one sequence at a time"}
 
 
@@ -160,7 +223,13 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode"], default=None,
                     help="profiling aid: run only one half (the JSON line then reports it alone)")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/traffic.json from two rocprofv3 --pmc runs of this "
+                         "script (FETCH_SIZE, then WRITE_SIZE) and exit; needs no GPU")
     args = ap.parse_args()
+    if args.record_traffic:
+        record_traffic(*args.record_traffic)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build runs the attention path on a "
               "single MI355X (no multi-GPU sharding); use --gpus 1", file=sys.stderr)
@@ -243,9 +312,11 @@ def main():
         "metric": METRIC, "value": pre_tflops, "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall / args.steps * 1e3,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16 in/out; fp16 rotated QK operands; fp32 accumulate",
+        "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) bf16, Zipf document reuse)",
         "config": {"workload": WORKLOAD, "Hq": wl.Hq, "Hkv": wl.Hkv, "head_dim": wl.D,
+                   "operands": "bf16 in/out, fp16 rotated q/k and bf16 p/v on MFMA, fp32 "
+                               "accumulation",
                    "block": wl.B, "prefill_requests": len(pre_seqs),
                    "decode_requests": len(dec_seqs), "pool_blocks": wl.num_blocks},
         "prefill": {"value": pre_tflops, "unit": "TFLOP/s", "ms": t_pre * 1e3,

@@ -63,6 +63,10 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 2) void decode_kernel(DecodePara
   // R(32) of every frequency: (cos, sin) interleaved, shared by the workgroup
   __shared__ __align__(16) float adv_all[D];
 
+  // a call whose batch has no single-row sequence (a pure prefill batch) leaves no work:
+  // leave before the per-workgroup constants and the queue atomic
+  const int n_items = P.dec_prefix[P.num_seqs] * P.Hkv;
+  if (n_items == 0) return;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   uint8_t* lds = lds_all[w][0];
   const int i16 = lane & 15, q4 = lane >> 4;
@@ -85,7 +89,6 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 2) void decode_kernel(DecodePara
   }
   __syncthreads();
 
-  const int n_items = P.dec_prefix[P.num_seqs] * P.Hkv;
   for (;;) {
     int it = 0;
     if (lane == 0) it = atomicAdd(P.counter, 1);
