@@ -206,6 +206,8 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
     pmin_w = min(pmin_w, __shfl_xor(pmin_w, o));
   }
   if (lane == 0) atomicMax(&pmax_s, pmax_w);
+  pmax_w = __builtin_amdgcn_readfirstlane(pmax_w);           // wave-uniform after the reduction
+  pmin_w = __builtin_amdgcn_readfirstlane(pmin_w);
 
   // ---- this thread's key staging unit: key kn (slot kj of block kb), frequencies
   // FPT*cp .. FPT*cp+FPT-1 (a wave's 64 threads stage keys of one block: kb is uniform)
@@ -344,7 +346,13 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);                        // vmcnt(0)
   __syncthreads();
-  const int pmax_g = pmax_s;
+  const int pmax_g = __builtin_amdgcn_readfirstlane(pmax_s);
+  // does tile d of a decoded window need the causal / ragged mask for this wave's rows?
+  auto needs_mask = [&](const WinDec& wd) __attribute__((always_inline)) {
+    const TileWords tw = tile_words<0>(wd);
+    const bool visible = tw.kmin <= pmax_w && tw.kmin <= pmax_g;
+    return !(visible && tw.full && tw.kmax <= pmin_w);
+  };
   f32x16 S0[2], S1[2];
 
   // S^T = K~ Q~^T - m for the key tile in Ks[buf] (prologue only; the loop interleaves it)
@@ -363,6 +371,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
   };
   if (n_kt > 0) qk(0, S0);
   WinDec wdc = decode_window(P, win, T, kvlen, 0, lane);
+  bool maskc = needs_mask(wdc);
   float mxc = xor32_max(max32(S0[0], S0[1]));
 
   const int gi = lane >> 4, i16 = lane & 15;
@@ -379,14 +388,15 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
     const WinDec wd = wdc;
     uint32_t win_next = 0;
     WinDec wdn;
+    bool maskn = false;
     float h0 = 0.f, h1 = 0.f;
     if (w < VREM) issue_v(wd, 1, nxt, VPW);                   // the odd value loads
     float mx = mxc;
     // ---- rare paths: causal / ragged mask of S(kt) ------------------------------------
-    {
+    if (maskc) {
       const TileWords tw = tile_words<0>(wd);
       const bool visible = tw.kmin <= pmax_w && tw.kmin <= pmax_g;
-      if (!(visible && tw.full && tw.kmax <= pmin_w)) {
+      {
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -551,6 +561,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
         if (g == 1) {
           wdn = decode_window(P, win_next, T, kvlen, kt + 1, lane);
           asm volatile("" ::"v"(wdn.id), "v"(wdn.off), "v"(wdn.nv));
+          maskn = needs_mask(wdn);
         }
         if (g == 2) {
           h0 = max16(Sn[0]);
@@ -586,6 +597,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
     }
     __builtin_amdgcn_s_setprio(0);
     wdc = wdn;
+    maskc = maskn;
     mxc = xor32_max(max3f(h0, h1, h1));
     __builtin_amdgcn_s_waitcnt(0x0F70);                      // vmcnt(0): values of tile kt+1
     __syncthreads();
