@@ -10,8 +10,12 @@ each call bracketed by HIP events. Inputs are resident in HBM before timing.
 
 Reported (one JSON line): prefill attention TFLOP/s (algorithmic: 4*D FLOP per visible
 (query, key, q-head) pair) as `value`, decode attention GB/s (algorithmic: K+V bytes of
-every (sequence, key) plus q, out and 4 B per block entry) in `decode`, the roofline of
+every (sequence, key) plus q, out and 4 B per block entry) in `decode`, also as unique-block
+bytes and counter-measured HBM bytes per second, p10/median/p90 call times, the roofline of
 the dominant kernel, and the float64 oracle timed on a bounded sample on the host cores.
+
+Other configurations (--workload), a no-reuse control (--no-reuse) and cold-cache steps
+(--cold) are for reference runs; the default line is the mixed batch, warm.
 """
 import argparse
 import json
@@ -215,6 +219,22 @@ def cpu_baseline(wl, pre_seqs, dec_seqs, budget_s=15.0):
                       f"({t_dec:.1f} s); float64 numpy, one sequence at a time"}
 
 
+def unique_decode_bytes(wl, seqs):
+    """K+V bytes of the distinct pool blocks the sequences reference (each read once) plus
+    q, out and the words: what an ideal cache would fetch."""
+    ids = np.unique(np.concatenate([wl.seq_block_ids[s] for s in seqs]))
+    kv = len(ids) * wl.B * 2 * wl.Hkv * wl.D * 2
+    rows = sum(int(wl.q_indptr[s + 1] - wl.q_indptr[s]) for s in seqs)
+    entries = sum(len(wl.seq_offsets[s]) for s in seqs)
+    return float(kv + 2 * rows * wl.Hq * wl.D * 2 + 4 * entries)
+
+
+def pct(xs):
+    xs = np.sort(np.asarray(xs))
+    return {"p10": float(np.percentile(xs, 10)), "median": float(np.median(xs)),
+            "p90": float(np.percentile(xs, 90))}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -223,6 +243,14 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode"], default=None,
                     help="profiling aid: run only one half (the JSON line then reports it alone)")
+    ap.add_argument("--workload", default=WORKLOAD,
+                    help="configuration to time (default: the mixed batch); the others are "
+                         "the parity configurations, timed for reference")
+    ap.add_argument("--no-reuse", action="store_true",
+                    help="control of the same shape in which every document appears once")
+    ap.add_argument("--cold", action="store_true",
+                    help="overwrite a 1 GiB buffer before every step (flushes L2 and MALL; "
+                         "outside the timed calls)")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/traffic.json from two rocprofv3 --pmc runs of this "
                          "script (FETCH_SIZE, then WRITE_SIZE) and exit; needs no GPU")
@@ -243,19 +271,23 @@ def main():
         sys.exit(2)
     L.lib()
     dev = "cuda:0"
-    wl = make(WORKLOAD)
+    wl = make(args.workload, no_reuse=args.no_reuse)
     qlen = np.diff(wl.q_indptr)
     pre_seqs = [s for s in range(wl.num_seqs) if qlen[s] > 1]
     dec_seqs = [s for s in range(wl.num_seqs) if qlen[s] == 1]
+    if args.only == "prefill":
+        dec_seqs = []
+    if args.only == "decode":
+        pre_seqs = []
     pool = wl.to_device(dev)
-    pre = half_inputs(wl, pre_seqs, dev, pool)
-    dec = half_inputs(wl, dec_seqs, dev, pool)
-    ws_pre = torch.empty(L.workspace_bytes("prefill", len(pre_seqs), pre["q"].shape[0],
-                                           pre["max_entries"], wl.Hq, wl.Hkv, wl.D),
-                         dtype=torch.uint8, device=dev)
-    ws_dec = torch.empty(L.workspace_bytes("decode", len(dec_seqs), dec["q"].shape[0],
-                                           dec["max_entries"], wl.Hq, wl.Hkv, wl.D),
-                         dtype=torch.uint8, device=dev)
+    halves = []
+    for kind, seqs, fn in (("prefill", pre_seqs, L.prefill), ("decode", dec_seqs, L.decode)):
+        if not seqs:
+            continue
+        a = half_inputs(wl, seqs, dev, pool)
+        ws = torch.empty(L.workspace_bytes(kind, len(seqs), a["q"].shape[0], a["max_entries"],
+                                           wl.Hq, wl.Hkv, wl.D), dtype=torch.uint8, device=dev)
+        halves.append((kind, seqs, fn, a, ws))
     stream = torch.cuda.current_stream()
 
     def call(fn, a, ws):
@@ -263,17 +295,18 @@ def main():
            a["q_indptr"], a["q_pos"], wl.rope_base, a["max_entries"], out=a["out"],
            workspace=ws, stream=stream)
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    nh = len(halves)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nh + 1)]
           for _ in range(args.steps)]
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev) if args.cold else None
 
     def step(e=None):
-        if e: e[0].record(stream)
-        if args.only != "decode":
-            call(L.prefill, pre, ws_pre)
-        if e: e[1].record(stream)
-        if args.only != "prefill":
-            call(L.decode, dec, ws_dec)
-        if e: e[2].record(stream)
+        if flush is not None:
+            flush.fill_(1.0)
+        for i, (kind, seqs, fn, a, ws) in enumerate(halves):
+            if e: e[i].record(stream)
+            call(fn, a, ws)
+        if e: e[nh].record(stream)
 
     # a plain copy of known size, once, so that FETCH_SIZE / WRITE_SIZE counter runs over
     # this program can be scaled to bytes (the factor is recorded with the counters)
@@ -291,43 +324,60 @@ def main():
         step(ev[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    t_pre = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) / 1e3
-    t_dec = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) / 1e3
-    flops = prefill_flops(wl, pre_seqs)
-    dbytes = decode_bytes(wl, dec_seqs)
-    pre_tflops = flops / t_pre / 1e12 if t_pre > 0 else 0.0
-    dec_gbs = dbytes / t_dec / 1e9 if t_dec > 0 else 0.0
 
-    if t_pre >= t_dec:
-        roof = {"kernel": "prefill_kernel", "bound": "mfma", "achieved": pre_tflops,
-                "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s"}
+    line = {"metric": METRIC, "value": 0.0, "unit": "TFLOP/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": wall / args.steps * 1e3, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic (seeded N(0,1) bf16, Zipf document reuse)"
+                    + (", no-reuse control" if args.no_reuse else "")
+                    + (", cold L2/MALL before every step" if args.cold else ""),
+            "config": {"workload": wl.name, "Hq": wl.Hq, "Hkv": wl.Hkv, "head_dim": wl.D,
+                       "operands": "bf16 in/out, fp16 rotated q/k and bf16 p/v on MFMA, fp32 "
+                                   "accumulation",
+                       "block": wl.B, "prefill_requests": len(pre_seqs),
+                       "decode_requests": len(dec_seqs), "pool_blocks": wl.num_blocks}}
+    roofs = []
+    for i, (kind, seqs, fn, a, ws) in enumerate(halves):
+        ts = [e[i].elapsed_time(e[i + 1]) / 1e3 for e in ev]
+        t = float(np.mean(ts))
+        stats = {k: v * 1e3 for k, v in pct(ts).items()}
+        if kind == "prefill":
+            flops = prefill_flops(wl, seqs)
+            val = flops / t / 1e12
+            line["prefill"] = {"value": val, "unit": "TFLOP/s", "ms": t * 1e3, "ms_pct": stats,
+                               "frac_mfma_peak": val / PEAK_MFMA_TFLOPS,
+                               "algorithmic_tflop": flops / 1e12}
+            roofs.append((t, {"kernel": "prefill_kernel", "bound": "mfma", "achieved": val,
+                              "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s"}))
+        else:
+            dbytes, ubytes = decode_bytes(wl, seqs), unique_decode_bytes(wl, seqs)
+            val = dbytes / t / 1e9
+            line["decode"] = {"value": val, "unit": "GB/s", "ms": t * 1e3, "ms_pct": stats,
+                              "frac_hbm_peak": val / PEAK_HBM_GBS,
+                              "algorithmic_gb": dbytes / 1e9,
+                              "unique_gb": ubytes / 1e9, "unique_gbs": ubytes / t / 1e9}
+            roofs.append((t, {"kernel": "decode_kernel", "bound": "hbm", "achieved": val,
+                              "peak": PEAK_HBM_GBS, "unit": "GB/s"}))
+    # `value` is the prefill half's TFLOP/s when the batch has one, else the decode GB/s
+    if "prefill" in line:
+        line["value"] = line["prefill"]["value"]
     else:
-        roof = {"kernel": "decode_kernel", "bound": "hbm", "achieved": dec_gbs,
-                "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+        line["metric"] = "decode attn HBM GB/s (logical K+V bytes), Zipf RAG batch"
+        line["value"], line["unit"] = line["decode"]["value"], "GB/s"
+    t_dom, roof = max(roofs, key=lambda r: r[0])
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = recorded_traffic(roof["kernel"])
-    roof["launch_ms"] = (t_pre if roof["bound"] == "mfma" else t_dec) * 1e3
-
-    line = {
-        "metric": METRIC, "value": pre_tflops, "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall / args.steps * 1e3,
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) bf16, Zipf document reuse)",
-        "config": {"workload": WORKLOAD, "Hq": wl.Hq, "Hkv": wl.Hkv, "head_dim": wl.D,
-                   "operands": "bf16 in/out, fp16 rotated q/k and bf16 p/v on MFMA, fp32 "
-                               "accumulation",
-                   "block": wl.B, "prefill_requests": len(pre_seqs),
-                   "decode_requests": len(dec_seqs), "pool_blocks": wl.num_blocks},
-        "prefill": {"value": pre_tflops, "unit": "TFLOP/s", "ms": t_pre * 1e3,
-                    "frac_mfma_peak": pre_tflops / PEAK_MFMA_TFLOPS,
-                    "algorithmic_tflop": flops / 1e12},
-        "decode": {"value": dec_gbs, "unit": "GB/s", "ms": t_dec * 1e3,
-                   "frac_hbm_peak": dec_gbs / PEAK_HBM_GBS,
-                   "algorithmic_gb": dbytes / 1e9},
-        "roofline": roof,
-    }
-    if not args.no_cpu_baseline:
+    roof["traffic"] = (recorded_traffic(roof["kernel"])
+                       if wl.name == WORKLOAD and not args.cold else None)
+    roof["launch_ms"] = t_dom * 1e3
+    line["roofline"] = roof
+    # decode GB/s three ways: logical (value), unique blocks, and counter-measured HBM bytes
+    # (from the committed counter record, while it matches this kernel and workload)
+    if "decode" in line and wl.name == WORKLOAD and not args.cold:
+        rec = recorded_traffic("decode_kernel")
+        line["decode"]["hbm_counter_gbs"] = (rec / (line["decode"]["ms"] / 1e3) / 1e9
+                                             if rec else None)
+    if not args.no_cpu_baseline and wl.name == WORKLOAD and pre_seqs and dec_seqs:
         line["cpu_baseline"] = cpu_baseline(wl, pre_seqs, dec_seqs)
     print(json.dumps(line), flush=True)
 

@@ -17,8 +17,12 @@
 // boundary) and at the start of each work item q' is recomputed exactly from the
 // double-precision phase.
 //
-// Work: a persistent grid of waves takes (row-split, kv-head) items from an atomic queue
-// (balanced tail). Keys are prefetched one group ahead into registers; values go straight
+// Work: (row-split, kv-head) items are dealt round-robin to the waves of a grid that is
+// exactly resident (item i goes to wave i mod W). Each wave first describes all of its items
+// at once, one item per lane (sequence, query row and position, entry range), so starting
+// an item costs no dependent memory round trips; the first key/value group of the next
+// item is fetched while the last group of the current one is multiplied. Keys are
+// prefetched one group ahead into registers; values go straight
 // from global memory into a double-buffered, XOR-swizzled LDS slice of the wave
 // (global_load_lds) and are read back transposed (ds_read_b64_tr_b16) as the A operand of
 // O^T += V^T P^T. Rows that must contribute nothing (padding, missing blocks) are fetched
@@ -30,7 +34,7 @@
 namespace lazyattn {
 
 constexpr int kDecodeWaves = 4;        // waves per workgroup
-constexpr int kDecodeWgPerCu = 4;      // workgroups launched per CU (residency set by VGPRs)
+constexpr int kDecodeWgPerCu = 2;      // workgroups per CU = the resident count (VGPRs, LDS)
 
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -62,6 +66,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 2) void decode_kernel(DecodePara
   __shared__ __align__(16) uint8_t lds_all[kDecodeWaves][2][BUF];
   // R(32) of every frequency: (cos, sin) interleaved, shared by the workgroup
   __shared__ __align__(16) float adv_all[D];
+  __shared__ __align__(16) f32x4 slot_tab[HC * 4 * 4 * 16];
 
   // a call whose batch has no single-row sequence (a pure prefill batch) leaves no work:
   // leave before the per-workgroup constants and the queue atomic
@@ -73,14 +78,18 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 2) void decode_kernel(DecodePara
   const int col = i16, g = col % G, ph = col / G;
   const bool col_ok = col < 2 * G;
 
-  // loop-invariant rotation constants of this lane's frequencies k = 32c + 8 q4 + e:
-  // R(i16) for its key row in registers; R(32) for the per-group advance of q' in LDS
-  float cj[HC][8], sj[HC][8];
-#pragma unroll
-  for (int c = 0; c < HC; ++c)
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      rope_cos_sin(i16, P.freqs[32 * c + 8 * q4 + e], cj[c][e], sj[c][e]);
+  // loop-invariant rotation constants, shared by the workgroup in LDS: R(j) of slot j for
+  // frequencies k = 32c + 8 q4 + 2 e2 + u as float4 (cos, sin of u = 0, 1) at
+  // [c][q4][e2][j] -- the 16 slots of a 16-lane read are consecutive 16-byte words; and
+  // R(32) for the per-group advance of q'
+  for (int i = threadIdx.x; i < HC * 4 * 4 * 16; i += kDecodeWaves * 64) {
+    const int j = i & 15, e2 = (i >> 4) & 3, qq = (i >> 6) & 3, c = i >> 8;
+    const int f0 = 32 * c + 8 * qq + 2 * e2;
+    float c0, s0, c1, s1;
+    rope_cos_sin(j, P.freqs[f0], c0, s0);
+    rope_cos_sin(j, P.freqs[f0 + 1], c1, s1);
+    slot_tab[i] = f32x4{c0, s0, c1, s1};
+  }
   if (threadIdx.x < D / 2) {
     float cs, sn;
     rope_cos_sin(32, P.freqs[threadIdx.x], cs, sn);
@@ -89,24 +98,40 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 2) void decode_kernel(DecodePara
   }
   __syncthreads();
 
-  for (;;) {
-    int it = 0;
-    if (lane == 0) it = atomicAdd(P.counter, 1);
-    it = __shfl(it, 0);
-    if (it >= n_items) break;
-    const int rs = it / P.Hkv, kvh = it % P.Hkv;
-    const int seq = upper_seq(P.dec_prefix, P.num_seqs, rs);
-    const int local = rs - P.dec_prefix[seq];
-    const int q0 = P.q_indptr[seq];
-    const int e0 = P.block_table[seq], T = P.block_table[seq + 1] - e0;
-    const int kvlen = P.kv_lens[seq];
-    const int splits = row_splits(T, P.bps, P.smax);
-    const int bpsr = row_bps(T, P.bps, P.smax);
-    const int row = local / splits, sp = local % splits;
-    const int eb = sp * bpsr;
-    const int ee = min(T, eb + bpsr);
-    const int r = q0 + row;
-    const int p = P.q_pos[r];
+  const int W = gridDim.x * kDecodeWaves;           // waves of the grid
+  const int gw = blockIdx.x * kDecodeWaves + w;      // this wave's index
+  // items gw + i W, i = 0, 1, ...; described 64 at a time, item gw + (64 rd + k) W by lane k
+  for (int base = gw; base < n_items; base += 64 * W) {
+    int x_rs = 0, x_kvh = 0, x_r = 0, x_p = 0, x_e0 = 0, x_kvlen = 0, x_eb = 0, x_ee = 0;
+    {
+      const int itl = base + lane * W;
+      if (itl < n_items) {
+        x_rs = itl / P.Hkv;
+        x_kvh = itl - x_rs * P.Hkv;
+        const int seq = upper_seq(P.dec_prefix, P.num_seqs, x_rs);
+        const int local = x_rs - P.dec_prefix[seq];
+        x_e0 = P.block_table[seq];
+        const int T = P.block_table[seq + 1] - x_e0;
+        x_kvlen = P.kv_lens[seq];
+        const int splits = row_splits(T, P.bps, P.smax);
+        const int bpsr = row_bps(T, P.bps, P.smax);
+        const int row = local / splits, sp = local - row * splits;
+        x_eb = sp * bpsr;
+        x_ee = min(T, x_eb + bpsr);
+        x_r = P.q_indptr[seq] + row;
+        x_p = P.q_pos[x_r];
+      }
+    }
+    const int n_here = min(64, (n_items - base + W - 1) / W);
+    int buf = 0;
+    bool pre = false;                                 // first group already in flight
+    u32x4 kcur[2][NC], knext[2][NC];
+    GroupMeta gcur, gnext;
+    for (int k = 0; k < n_here; ++k) {
+    const int rs = rl(x_rs, k), kvh = rl(x_kvh, k);
+    const int e0 = rl(x_e0, k), kvlen = rl(x_kvlen, k);
+    const int eb = rl(x_eb, k), ee = rl(x_ee, k);
+    const int r = rl(x_r, k), p = rl(x_p, k);
     const int h = kvh * G + g;
     const uint16_t* qrow = P.q + ((size_t)r * P.Hq + h) * D;
 
@@ -118,23 +143,25 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 2) void decode_kernel(DecodePara
     bool have_q = false;
     int cur_delta = 0;
 
-    // issue the loads of the group starting at entry t0 into LDS buffer `buf`
-    auto issue = [&](int t0, int buf, u32x4 (&kreg)[2][NC], GroupMeta& gm) {
+    // issue the loads of the group starting at entry t0 of an item (entries below i_ee,
+    // words from i_e0, kv-head i_kvh, i_kvlen keys) into LDS buffer `buf`
+    auto issue = [&](int t0, int i_ee, int i_e0, int i_kvh, int i_kvlen, int buf,
+                     u32x4 (&kreg)[2][NC], GroupMeta& gm) {
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
         const int t = t0 + b;
-        const bool blk = t < ee;
-        const uint32_t wd = blk ? P.block_meta[e0 + t] : 0u;
+        const bool blk = t < i_ee;
+        const uint32_t wd = blk ? P.block_meta[i_e0 + t] : 0u;
         const int id = word_id(wd);
-        const int rem = kvlen - t * kBlock;
+        const int rem = i_kvlen - t * kBlock;
         gm.id[b] = id;
         gm.delta[b] = word_delta(wd);
         gm.nval[b] = (blk && id < P.num_blocks) ? (rem < kBlock ? (rem > 0 ? rem : 0) : kBlock) : 0;
-        const size_t base = ((size_t)id * P.Hkv + kvh) * kBlock;
+        const size_t kb = ((size_t)id * P.Hkv + i_kvh) * kBlock;
 #pragma unroll
         for (int c = 0; c < NC; ++c)
           kreg[b][c] = i16 < gm.nval[b]
-                           ? *(const u32x4*)(P.k_pool + (base + i16) * D + 32 * c + 8 * q4)
+                           ? *(const u32x4*)(P.k_pool + (kb + i16) * D + 32 * c + 8 * q4)
                            : u32x4{0, 0, 0, 0};
       }
 #pragma unroll
@@ -145,15 +172,13 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 2) void decode_kernel(DecodePara
         const int c = cs ^ vswz(R);
         const void* src = P.zero;
         if (j < gm.nval[b])
-          src = P.v_pool + (((size_t)gm.id[b] * P.Hkv + kvh) * kBlock + j) * D + 8 * c;
+          src = P.v_pool + (((size_t)gm.id[b] * P.Hkv + i_kvh) * kBlock + j) * D + 8 * c;
         g2lds16(src, lds + buf * BUF + i * 1024);
       }
     };
 
-    u32x4 kcur[2][NC], knext[2][NC];
-    GroupMeta gcur, gnext;
-    int buf = 0;
-    if (eb < ee) issue(eb, 0, knext, gnext);
+    if (!pre && eb < ee) issue(eb, ee, e0, kvh, kvlen, buf, knext, gnext);
+    pre = false;
     for (int t0 = eb; t0 < ee; t0 += 2) {
       __builtin_amdgcn_s_waitcnt(0x0F70);       // vmcnt(0): this group's keys and values
       asm volatile("" ::: "memory");
@@ -163,7 +188,16 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 2) void decode_kernel(DecodePara
 #pragma unroll
         for (int c = 0; c < NC; ++c) kcur[b][c] = knext[b][c];
       gcur = gnext;
-      if (t0 + 2 < ee) issue(t0 + 2, buf ^ 1, knext, gnext);
+      if (t0 + 2 < ee) {
+        issue(t0 + 2, ee, e0, kvh, kvlen, buf ^ 1, knext, gnext);
+      } else if (k + 1 < n_here) {                    // the next item's first group
+        const int n_eb = rl(x_eb, k + 1), n_ee = rl(x_ee, k + 1);
+        if (n_eb < n_ee) {
+          issue(n_eb, n_ee, rl(x_e0, k + 1), rl(x_kvh, k + 1), rl(x_kvlen, k + 1), buf ^ 1,
+                knext, gnext);
+          pre = true;
+        }
+      }
 
       // ---- q' of this lane's column: R(p - off_{t0+ph}) q_g ---------------------------
       const int d0 = gcur.delta[0];
@@ -219,8 +253,8 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 2) void decode_kernel(DecodePara
           for (int i = 0; i < 4; ++i) {
             const float a0 = bf_lo(kcur[b][c][i]), a1 = bf_hi(kcur[b][c][i]);
             const float b0 = bf_lo(kcur[b][c + HC][i]), b1 = bf_hi(kcur[b][c + HC][i]);
-            const float c0 = cj[c][2 * i], s0 = sj[c][2 * i];
-            const float c1 = cj[c][2 * i + 1], s1 = sj[c][2 * i + 1];
+            const f32x4 t = slot_tab[((c * 4 + q4) * 4 + i) * 16 + i16];
+            const float c0 = t[0], s0 = t[1], c1 = t[2], s1 = t[3];
             lo[i] = pack_f16(a0 * c0 - b0 * s0, a1 * c1 - b1 * s1);
             hi[i] = pack_f16(a0 * s0 + b0 * c0, a1 * s1 + b1 * c1);
           }
@@ -289,6 +323,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 2) void decode_kernel(DecodePara
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt) *(f32x4*)(part + 16 * dt + 4 * q4) = o[dt];
       if (q4 == 0) { part[D] = m; part[D + 1] = lt; }
+    }
     }
   }
 }

@@ -106,6 +106,9 @@ __device__ __forceinline__ u32x2 lds_read_tr(const uint16_t* p) {
   return __builtin_bit_cast(u32x2, r);
 }
 
+// value of v in lane `lane` (a wave-uniform index)
+__device__ __forceinline__ int rl(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
+
 // c + x.lo + x.hi for two packed bf16 values (v_dot2_f32_bf16 against (1, 1))
 __device__ __forceinline__ float sum2_bf16(uint32_t x, float c) {
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));

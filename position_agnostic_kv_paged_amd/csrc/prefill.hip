@@ -78,8 +78,6 @@ __device__ __forceinline__ WinDec decode_window(const PrefillParams& P, uint32_t
   return d;
 }
 
-__device__ __forceinline__ int rl(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
-
 // c ? a : b for pointers as an integer blend: a plain select of an expensive address may be
 // turned into a branch, which would split the interleaved MFMA block it sits in
 __device__ __forceinline__ const void* blend_ptr(bool c, const void* a, const void* b) {

@@ -292,15 +292,26 @@ class Config:
     description: str = ""
 
 
-def layouts_for(cfg: Config, seed: int) -> List[RequestLayout]:
+def layouts_for(cfg: Config, seed: int, no_reuse: bool = False) -> List[RequestLayout]:
+    """Request layouts of a configuration. no_reuse builds the control of the same shape in
+    which every document appears once in the whole batch (documents taken in the order of a
+    seeded permutation instead of Zipf draws), so no K/V block is read twice."""
     rng = np.random.default_rng([seed, 0])
     rank_to_doc = rng.permutation(cfg.n_docs)
     cdf = _zipf_cdf(cfg.n_docs, cfg.zipf_s)
+    distinct = np.random.default_rng([seed, 5]).permutation(cfg.n_docs)
+    if no_reuse and sum(g.count * g.n_docs for g in cfg.groups) > cfg.n_docs:
+        raise ValueError(f"{cfg.name}: not enough documents for a no-reuse batch")
+    used = 0
     lays = []
     for grp in cfg.groups:
         for _ in range(grp.count):
-            docs = _draw_docs(rng, grp.n_docs, cfg.n_docs, cfg.zipf_s, grp.replace,
-                              rank_to_doc, cdf)
+            if no_reuse:
+                docs = [int(d) for d in distinct[used:used + grp.n_docs]]
+                used += grp.n_docs
+            else:
+                docs = _draw_docs(rng, grp.n_docs, cfg.n_docs, cfg.zipf_s, grp.replace,
+                                  rank_to_doc, cdf)
             pos = int(rng.integers(0, cfg.start_max + 1)) if cfg.start_max > 0 else 0
             segs = []
             for d in docs:
@@ -354,7 +365,8 @@ def _tiny_layouts(decode: bool) -> List[RequestLayout]:
     return [RequestLayout(segs, 32)]
 
 
-def make(name: str, seed: Optional[int] = None, decode_variant: bool = False) -> Workload:
+def make(name: str, seed: Optional[int] = None, decode_variant: bool = False,
+         no_reuse: bool = False) -> Workload:
     """Build a named configuration. Master seed defaults to 1000 + its 1-based index."""
     cfg = CONFIGS[name]
     if seed is None:
@@ -362,8 +374,9 @@ def make(name: str, seed: Optional[int] = None, decode_variant: bool = False) ->
     if name.startswith("tiny-prefill"):
         lays = _tiny_layouts(decode_variant)
     else:
-        lays = layouts_for(cfg, seed)
-    wl = build(cfg.name + ("-decode" if decode_variant else ""), cfg.Hq, cfg.Hkv, cfg.D, cfg.B,
+        lays = layouts_for(cfg, seed, no_reuse)
+    suffix = ("-decode" if decode_variant else "") + ("-noreuse" if no_reuse else "")
+    wl = build(cfg.name + suffix, cfg.Hq, cfg.Hkv, cfg.D, cfg.B,
                cfg.rope_base, cfg.n_docs, cfg.doc_tokens, lays, seed)
     wl.info["description"] = cfg.description
     return wl
