@@ -11,7 +11,6 @@ using namespace lazyattn;
 
 namespace {
 
-constexpr long long kTargetDecodeItems = 16384;   // ~8 (row-split, kv-head) items per resident wave
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -23,21 +22,36 @@ bool shape_ok(int32_t Hq, int32_t Hkv, int32_t D, int32_t B) {
   return G == 1 || G == 2 || G == 4 || G == 8;
 }
 
-// Decode split size (blocks, even): enough (row-split, kv-head) items to balance the
-// persistent waves' queue, 4 .. 64 blocks per item.
+// Decode split size (blocks per item, even, at least 8). The (row-split, kv-head) items are
+// dealt round-robin to the W resident decode waves, so the choice aims at an item count that
+// is a whole multiple of W -- every wave gets the same number of equal items -- assuming each
+// row holds about max_entries blocks. Among 1 .. 8 items per wave the candidate with the
+// least idle share wins; ties go to fewer, longer items (fewer partials to merge).
 struct DecodeSplit {
   int bps, smax;
 };
 DecodeSplit decode_split(int rows_bound, int Hkv, int max_entries) {
-  const long long work = (long long)(rows_bound > 0 ? rows_bound : 1) * Hkv *
-                         (max_entries > 0 ? max_entries : 1);
-  long long b = (work + kTargetDecodeItems - 1) / kTargetDecodeItems;
-  if (b < 4) b = 4;
-  if (b > 64) b = 64;
-  b += b & 1;
+  const long long W = decode_resident_waves();
+  const long long T = max_entries > 0 ? max_entries : 1;
+  const long long pairs = (long long)(rows_bound > 0 ? rows_bound : 1) * Hkv;
+  long long best_b = 0;
+  double best_eff = -1.0;
+  for (long long k = 1; k <= 8; ++k) {
+    long long s = k * W / pairs;                     // splits per row
+    if (s < 1) s = 1;
+    long long b = (T + s - 1) / s;
+    if (b < 8) b = 8;
+    b += b & 1;
+    const long long items = pairs * ((T + b - 1) / b);
+    const double eff = (double)items / (double)(((items + W - 1) / W) * W);
+    if (eff > best_eff + 1e-9) {
+      best_eff = eff;
+      best_b = b;
+    }
+  }
   DecodeSplit d;
-  d.bps = (int)b;
-  d.smax = max_entries > 0 ? (int)((max_entries + b - 1) / b) : 1;
+  d.bps = (int)best_b;
+  d.smax = (int)((T + best_b - 1) / best_b);
   return d;
 }
 

@@ -330,17 +330,23 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 2) void decode_kernel(DecodePara
 
 static int g_num_cus = 0;
 
-template <int D>
-static hipError_t launch_d(const DecodeParams& p, int G, hipStream_t st) {
+static int num_cus() {
   if (g_num_cus == 0) {
     int dev = 0, n = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         n <= 0)
-      n = 256;
+      n = 256;                                       // MI355X (also when no device is visible)
     g_num_cus = n;
   }
-  dim3 grid(g_num_cus * kDecodeWgPerCu), block(kDecodeWaves * 64);
+  return g_num_cus;
+}
+
+int decode_resident_waves() { return num_cus() * kDecodeWgPerCu * kDecodeWaves; }
+
+template <int D>
+static hipError_t launch_d(const DecodeParams& p, int G, hipStream_t st) {
+  dim3 grid(num_cus() * kDecodeWgPerCu), block(kDecodeWaves * 64);
   switch (G) {
     case 1: hipLaunchKernelGGL((decode_kernel<D, 1>), grid, block, 0, st, p); break;
     case 2: hipLaunchKernelGGL((decode_kernel<D, 2>), grid, block, 0, st, p); break;
