@@ -88,7 +88,6 @@ int run(const void* q, const void* k_pool, const void* v_pool, const int32_t* bl
   const WsLayout L = ws_layout(num_seqs, (long long)rows_bound * ds.smax, Hq, D);
   char* ws = (char*)workspace;
   double* freqs = (double*)(ws + L.off_freqs);
-  int32_t* counter = (int32_t*)(ws + L.off_counter);
   uint32_t* zero = (uint32_t*)(ws + L.off_zero);
   int32_t* pf_prefix = (int32_t*)(ws + L.off_pf_prefix);
   int32_t* dec_prefix = (int32_t*)(ws + L.off_dec_prefix);
@@ -99,7 +98,7 @@ int run(const void* q, const void* k_pool, const void* v_pool, const int32_t* bl
     fr.f[k] = std::pow(rope_base, -2.0 * k / D) / (2.0 * M_PI);
   const float scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
 
-  PlanParams pp{q_indptr, block_table, freqs, pf_prefix, dec_prefix, counter, zero, num_seqs,
+  PlanParams pp{q_indptr, block_table, freqs, pf_prefix, dec_prefix, zero, num_seqs,
                 prefill_positions_per_tile(G), ds.bps, ds.smax, mode, D / 2, fr};
   if (launch_plan(pp, st) != hipSuccess) return LAZYATTN_ERR_LAUNCH;
 
@@ -115,7 +114,7 @@ int run(const void* q, const void* k_pool, const void* v_pool, const int32_t* bl
   }
   DecodeParams Dp{(const uint16_t*)q, (const uint16_t*)k_pool, (const uint16_t*)v_pool,
                   block_table, block_meta, kv_lens, q_indptr, q_positions, dec_prefix,
-                  counter, (const uint16_t*)zero, partials, num_seqs, Hq, Hkv, num_blocks,
+                  (const uint16_t*)zero, partials, num_seqs, Hq, Hkv, num_blocks,
                   ds.bps, ds.smax, scale_log2, freqs};
   if (launch_decode(Dp, D, G, st) != hipSuccess) return LAZYATTN_ERR_LAUNCH;
   MergeParams Mp{q_indptr, block_table, dec_prefix, partials, (uint16_t*)out,

@@ -182,11 +182,11 @@ __device__ __forceinline__ int upper_seq(const int32_t* prefix, int n, int x) {
 
 // ---- workspace layout -----------------------------------------------------------------------
 // [0, 512)                RoPE frequency table, double [64] (revolutions per position)
-// [512, 768)              int32 decode work-queue counter at 512; 16-byte zero rows at 576..767
+// [512, 768)              reserved; 16-byte zero rows at 576..767
 // [768, ...)              prefix arrays: prefill tiles, decode row-splits, each num_seqs + 1 int32
 // aligned 256             split-K partials: float [row-splits][Hq][D + 4]  (o[D], m, l, -, -)
 struct WsLayout {
-  size_t off_freqs, off_counter, off_zero, off_pf_prefix, off_dec_prefix, off_partials, total;
+  size_t off_freqs, off_zero, off_pf_prefix, off_dec_prefix, off_partials, total;
 };
 
 __host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -194,7 +194,6 @@ __host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a -
 __host__ __device__ inline WsLayout ws_layout(int num_seqs, long long max_rowsplits, int Hq, int D) {
   WsLayout L;
   L.off_freqs = 0;
-  L.off_counter = 512;
   L.off_zero = 576;
   L.off_pf_prefix = 768;
   L.off_dec_prefix = align_up(L.off_pf_prefix + 4ull * (num_seqs + 1), 256);

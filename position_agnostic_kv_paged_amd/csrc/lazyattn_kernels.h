@@ -11,7 +11,6 @@ struct PlanParams {
   double* freqs_out;         // [D/2] workspace copy of the frequency table
   int32_t* pf_prefix;        // [num_seqs + 1] prefill tiles
   int32_t* dec_prefix;       // [num_seqs + 1] decode row-splits
-  int32_t* counter;          // decode work queue (zeroed here)
   uint32_t* zero;            // 192 bytes set to zero here
   int num_seqs;
   int pos_per_tile;          // query positions per prefill tile
@@ -49,7 +48,6 @@ struct DecodeParams {
   const int32_t* q_indptr;
   const int32_t* q_pos;
   const int32_t* dec_prefix;
-  int32_t* counter;          // work queue over (row-split, kv-head) items
   const uint16_t* zero;      // zero bytes: source of V rows that must read as 0
   float* partials;           // [row-splits][Hq][D + 4]
   int num_seqs, Hq, Hkv, num_blocks, bps, smax;

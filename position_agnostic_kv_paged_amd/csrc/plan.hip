@@ -13,7 +13,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanParams P) {
   __shared__ int sa[1024], sb[1024];
   __shared__ int carry_a, carry_b;
   const int tid = threadIdx.x;
-  if (tid == 0) { carry_a = 0; carry_b = 0; *P.counter = 0; }
+  if (tid == 0) { carry_a = 0; carry_b = 0; }
   if (tid < 48) P.zero[tid] = 0u;
 #pragma unroll
   for (int i = 0; i < kMaxHalfDim; ++i)

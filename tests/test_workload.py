@@ -96,3 +96,17 @@ def test_mixed_layout():
     qlen = np.diff(wl.q_indptr)
     assert list(qlen[:4]) == [512] * 4 and np.all(qlen[4:] == 1) and wl.num_seqs == 100
     assert np.all(wl.kv_lens[:4] == 16 * 1024 + 512) and np.all(wl.kv_lens[4:] == 12 * 1024 + 1)
+
+
+def test_no_reuse_control_has_distinct_documents():
+    """The no-reuse control keeps the shape (requests, documents per request, lengths) and
+    references every pool block at most once (private blocks are unique anyway)."""
+    base = make("decode-32q8kv-b64-ctx4161")
+    ctl = make("decode-32q8kv-b64-ctx4161", no_reuse=True)
+    assert ctl.num_seqs == base.num_seqs
+    assert np.array_equal(ctl.kv_lens, base.kv_lens)
+    assert np.array_equal(ctl.q_indptr, base.q_indptr)
+    ids = np.concatenate([ctl.seq_block_ids[s] for s in range(ctl.num_seqs)])
+    assert len(np.unique(ids)) == len(ids)
+    base_ids = np.concatenate([base.seq_block_ids[s] for s in range(base.num_seqs)])
+    assert len(np.unique(base_ids)) < len(base_ids)          # the Zipf batch does reuse
