@@ -251,6 +251,9 @@ def main():
     ap.add_argument("--cold", action="store_true",
                     help="overwrite a 1 GiB buffer before every step (flushes L2 and MALL; "
                          "outside the timed calls)")
+    ap.add_argument("--no-ablation", action="store_true",
+                    help="skip the rotation ablation (the materialised-baseline entry points "
+                         "timed on the same inputs)")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/traffic.json from two rocprofv3 --pmc runs of this "
                          "script (FETCH_SIZE, then WRITE_SIZE) and exit; needs no GPU")
@@ -281,6 +284,7 @@ def main():
         pre_seqs = []
     pool = wl.to_device(dev)
     halves = []
+    baseline = {"prefill": L.prefill_rotated_pool, "decode": L.decode_rotated_pool}
     for kind, seqs, fn in (("prefill", pre_seqs, L.prefill), ("decode", dec_seqs, L.decode)):
         if not seqs:
             continue
@@ -377,6 +381,26 @@ def main():
         rec = recorded_traffic("decode_kernel")
         line["decode"]["hbm_counter_gbs"] = (rec / (line["decode"]["ms"] / 1e3) / 1e9
                                              if rec else None)
+    # rotation ablation: the same calls with the key rotation compiled out (the materialised
+    # baseline's kernels), timed on the same inputs -- only the time is used, the values
+    # differ because this pool is not pre-rotated
+    if not args.no_ablation:
+        abl = {}
+        for kind, seqs, fn, a, ws in halves:
+            for _ in range(args.warmup):
+                call(baseline[kind], a, ws)
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
+            for k in range(args.steps):
+                e[2 * k].record(stream)
+                call(baseline[kind], a, ws)
+                e[2 * k + 1].record(stream)
+            torch.cuda.synchronize()
+            t_base = float(np.median([e[2 * k].elapsed_time(e[2 * k + 1])
+                                      for k in range(args.steps)]))
+            t_lazy = line[kind]["ms_pct"]["median"]
+            abl[kind] = {"baseline_ms": t_base, "lazy_ms": t_lazy,
+                         "rotation_overhead": t_lazy / t_base - 1.0}
+        line["rotation_ablation"] = abl
     if not args.no_cpu_baseline and wl.name == WORKLOAD and pre_seqs and dec_seqs:
         line["cpu_baseline"] = cpu_baseline(wl, pre_seqs, dec_seqs)
     print(json.dumps(line), flush=True)

@@ -117,6 +117,34 @@ int lazyattn_decode(const void* q, const void* k_pool, const void* v_pool,
                     int32_t B, int32_t num_blocks, int32_t max_entries,
                     void* out, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * lazyattn_prefill_rotated_pool / lazyattn_decode_rotated_pool -- the materialised baseline
+ * the method is measured against (technical summary: "Mathematical Equivalence"; the
+ * "rotate keys twice" copy it avoids). Same arguments, layouts, workspace sizes and errors as
+ * lazyattn_prefill / lazyattn_decode, but k_pool must hold keys ALREADY rotated to the
+ * absolute logical position they are referenced at (slot j of entry t holds R(off_t + j) k),
+ * so each block can serve only one position; queries are rotated by R(p) and keys are used
+ * as stored -- plain paged RoPE attention. Same kernels with the per-tile key rotation
+ * (prefill) and the per-slot key rotation and query re-anchoring (decode) compiled out; the
+ * pair measures what the deferred rotation costs.
+ */
+int lazyattn_prefill_rotated_pool(const void* q, const void* k_pool, const void* v_pool,
+                                  const int32_t* block_table, const uint32_t* block_meta,
+                                  const int32_t* kv_lens, const int32_t* q_indptr,
+                                  const int32_t* q_positions, double rope_base,
+                                  int32_t num_seqs, int32_t total_q, int32_t Hq, int32_t Hkv,
+                                  int32_t D, int32_t B, int32_t num_blocks,
+                                  int32_t max_entries, void* out, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+int lazyattn_decode_rotated_pool(const void* q, const void* k_pool, const void* v_pool,
+                                 const int32_t* block_table, const uint32_t* block_meta,
+                                 const int32_t* kv_lens, const int32_t* q_indptr,
+                                 const int32_t* q_positions, double rope_base,
+                                 int32_t num_seqs, int32_t total_q, int32_t Hq, int32_t Hkv,
+                                 int32_t D, int32_t B, int32_t num_blocks,
+                                 int32_t max_entries, void* out, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
 /* Workspace sizes (bytes) for the calls above; 0 on invalid sizes. */
 size_t lazyattn_prefill_workspace_bytes(int32_t num_seqs, int32_t total_q, int32_t max_entries,
                                         int32_t Hq, int32_t Hkv, int32_t D);

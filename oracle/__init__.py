@@ -33,5 +33,5 @@ the summary's printed 0.59% overhead at M = 128. No function here is
 "parity unpinned".
 """
 from . import rope, meta, attention, overhead  # noqa: F401
-from .attention import lazy_attention, attention_rows, bf16_bits_to_f64  # noqa: F401
+from .attention import lazy_attention, attention_rows, bf16_bits_to_f64, rotated_pool  # noqa: F401
 from .meta import encode_meta, decode_meta  # noqa: F401

@@ -29,11 +29,13 @@ def bf16_bits_to_f64(bits) -> np.ndarray:
     return b.view(np.float32).astype(np.float64)
 
 
-def materialise(k_pool, v_pool, block_ids, offsets, kv_len, B, base):
+def materialise(k_pool, v_pool, block_ids, offsets, kv_len, B, base, rotate_keys=True):
     """Copy a sequence's blocks into logical order with eager RoPE on keys.
 
     k_pool, v_pool: uint16 bf16 bits [num_blocks, Hkv, B, D] (or float arrays).
     block_ids, offsets: per-entry physical block id and logical offset of slot 0.
+    rotate_keys=False reads a pool whose keys already carry R(L) (the materialised
+    baseline the method is compared with): keys are then used as stored.
     Returns K_hat [Hkv, n, D] float64 (rotated), V_hat [Hkv, n, D], key_pos [n].
     """
     T = len(block_ids)
@@ -46,9 +48,12 @@ def materialise(k_pool, v_pool, block_ids, offsets, kv_len, B, base):
         kb = k_pool[blk][:, :n_t, :]
         vb = v_pool[blk][:, :n_t, :]
         if kb.dtype == np.uint16:
-            kb, vb = bf16_bits_to_f64(kb), bf16_bits_to_f64(vb)
+            kb = bf16_bits_to_f64(kb)
+        if vb.dtype == np.uint16:
+            vb = bf16_bits_to_f64(vb)
         pos = int(offsets[t]) + np.arange(n_t, dtype=np.int64)
-        ks.append(rotate(kb, pos[None, :], base))
+        ks.append(rotate(kb, pos[None, :], base) if rotate_keys
+                  else np.asarray(kb, dtype=np.float64))
         vs.append(np.asarray(vb, dtype=np.float64))
         ps.append(pos)
     return (np.concatenate(ks, axis=1), np.concatenate(vs, axis=1),
@@ -86,7 +91,7 @@ def _rot_queries(q, q_pos, base):
 
 
 def lazy_attention(q, k_pool, v_pool, seq_block_ids, seq_offsets, kv_lens,
-                   q_indptr, q_pos, base, B):
+                   q_indptr, q_pos, base, B, rotate_keys=True):
     """Whole-batch reference output, float64 [total_q, Hq, D].
 
     q: bf16 bits [total_q, Hq, D]; seq_block_ids / seq_offsets: one array per
@@ -100,20 +105,42 @@ def lazy_attention(q, k_pool, v_pool, seq_block_ids, seq_offsets, kv_lens,
         if r1 == r0:
             continue
         K_hat, V_hat, key_pos = materialise(
-            k_pool, v_pool, seq_block_ids[s], seq_offsets[s], int(kv_lens[s]), B, base)
+            k_pool, v_pool, seq_block_ids[s], seq_offsets[s], int(kv_lens[s]), B, base,
+            rotate_keys)
         qr = _rot_queries(q[r0:r1], q_pos[r0:r1], base)
         out[r0:r1] = attend(qr, q_pos[r0:r1], K_hat, V_hat, key_pos)
     return out
 
 
 def attention_rows(q, k_pool, v_pool, seq_block_ids, seq_offsets, kv_lens,
-                   q_indptr, q_pos, base, B, seq, rows):
+                   q_indptr, q_pos, base, B, seq, rows, rotate_keys=True):
     """Reference output of selected query rows (global row indices) of one sequence."""
     rows = np.asarray(rows, dtype=np.int64)
     r0, r1 = int(q_indptr[seq]), int(q_indptr[seq + 1])
     if np.any(rows < r0) or np.any(rows >= r1):
         raise ValueError("rows must belong to the sequence")
     K_hat, V_hat, key_pos = materialise(
-        k_pool, v_pool, seq_block_ids[seq], seq_offsets[seq], int(kv_lens[seq]), B, base)
+        k_pool, v_pool, seq_block_ids[seq], seq_offsets[seq], int(kv_lens[seq]), B, base,
+        rotate_keys)
     qr = _rot_queries(q[rows], q_pos[rows], base)
     return attend(qr, q_pos[rows], K_hat, V_hat, key_pos)
+
+
+def rotated_pool(k_pool, seq_block_ids, seq_offsets, kv_lens, B, base):
+    """Float64 copy of k_pool in which every referenced key slot holds R(L) k at the
+    logical position L it is referenced at (the materialised baseline's pool). Each block
+    may be referenced once; unreferenced blocks are copied unrotated."""
+    kp = bf16_bits_to_f64(k_pool) if k_pool.dtype == np.uint16 else np.array(k_pool, np.float64)
+    out = kp.copy()
+    seen = set()
+    for s in range(len(kv_lens)):
+        T = len(seq_block_ids[s])
+        for t in range(T):
+            blk = int(seq_block_ids[s][t])
+            if blk in seen:
+                raise ValueError("a block referenced twice cannot hold one rotation")
+            seen.add(blk)
+            n_t = B if t < T - 1 else int(kv_lens[s]) - (T - 1) * B
+            pos = int(seq_offsets[s][t]) + np.arange(n_t, dtype=np.int64)
+            out[blk][:, :n_t, :] = rotate(kp[blk][:, :n_t, :], pos[None, :], base)
+    return out

@@ -9,7 +9,8 @@ OK, ERR_NULL, ERR_ALIGN, ERR_SHAPE, ERR_RANGE, ERR_WORKSPACE, ERR_LAUNCH, ERR_AR
 
 # every symbol include/lazyattn.h declares
 EXPORTED = [
-    "lazyattn_prefill", "lazyattn_decode", "lazyattn_prefill_workspace_bytes",
+    "lazyattn_prefill", "lazyattn_decode", "lazyattn_prefill_rotated_pool",
+    "lazyattn_decode_rotated_pool", "lazyattn_prefill_workspace_bytes",
     "lazyattn_decode_workspace_bytes", "lazyattn_encode_meta", "lazyattn_debug_decode_meta",
     "lazyattn_status_str", "lazyattn_version",
 ]
@@ -35,7 +36,8 @@ def lib():
     vp, i32, u64, dbl = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_double
     attn = [vp, vp, vp, vp, vp, vp, vp, vp, dbl, i32, i32, i32, i32, i32, i32, i32, i32,
             vp, vp, u64, vp]
-    for name in ("lazyattn_prefill", "lazyattn_decode"):
+    for name in ("lazyattn_prefill", "lazyattn_decode", "lazyattn_prefill_rotated_pool",
+                 "lazyattn_decode_rotated_pool"):
         f = getattr(L, name)
         f.argtypes, f.restype = attn, ctypes.c_int
     for name in ("lazyattn_prefill_workspace_bytes", "lazyattn_decode_workspace_bytes"):

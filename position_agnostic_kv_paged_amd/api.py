@@ -38,7 +38,8 @@ def workspace_bytes(kind, num_seqs, total_q, max_entries, Hq, Hkv, D):
 
 
 def _attention(kind, q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indptr, q_pos,
-               rope_base, max_entries, out=None, workspace=None, stream=None):
+               rope_base, max_entries, out=None, workspace=None, stream=None,
+               rotated_pool=False):
     import torch
     total_q, Hq, D, num_blocks, Hkv, B = _dims(q, k_pool)
     num_seqs = kv_lens.numel()
@@ -47,12 +48,13 @@ def _attention(kind, q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indp
     need = workspace_bytes(kind, num_seqs, total_q, max_entries, Hq, Hkv, D)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    fn = lib().lazyattn_prefill if kind == "prefill" else lib().lazyattn_decode
+    name = "lazyattn_" + kind + ("_rotated_pool" if rotated_pool else "")
+    fn = getattr(lib(), name)
     rc = fn(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(block_meta),
             _ptr(kv_lens), _ptr(q_indptr), _ptr(q_pos), float(rope_base), num_seqs, total_q,
             Hq, Hkv, D, B, num_blocks, int(max_entries), _ptr(out), _ptr(workspace),
             workspace.numel() * workspace.element_size(), _stream(stream))
-    check(rc, "lazyattn_" + kind)
+    check(rc, name)
     return out
 
 
@@ -68,6 +70,21 @@ def decode(q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indptr, q_pos,
     """lazyattn_decode on torch tensors; returns out."""
     return _attention("decode", q, k_pool, v_pool, block_table, block_meta, kv_lens,
                       q_indptr, q_pos, rope_base, max_entries, out, workspace, stream)
+
+
+def prefill_rotated_pool(q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indptr, q_pos,
+                         rope_base, max_entries, out=None, workspace=None, stream=None):
+    """lazyattn_prefill_rotated_pool: the materialised baseline (k_pool holds keys already
+    rotated to the positions they are referenced at); returns out."""
+    return _attention("prefill", q, k_pool, v_pool, block_table, block_meta, kv_lens,
+                      q_indptr, q_pos, rope_base, max_entries, out, workspace, stream, True)
+
+
+def decode_rotated_pool(q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indptr, q_pos,
+                        rope_base, max_entries, out=None, workspace=None, stream=None):
+    """lazyattn_decode_rotated_pool (materialised baseline); returns out."""
+    return _attention("decode", q, k_pool, v_pool, block_table, block_meta, kv_lens,
+                      q_indptr, q_pos, rope_base, max_entries, out, workspace, stream, True)
 
 
 def encode_meta(block_ids, offsets, block_table, B=BLOCK):

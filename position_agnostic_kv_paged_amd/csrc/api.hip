@@ -65,7 +65,7 @@ int run(const void* q, const void* k_pool, const void* v_pool, const int32_t* bl
         const int32_t* q_positions, double rope_base, int32_t num_seqs, int32_t total_q,
         int32_t Hq, int32_t Hkv, int32_t D, int32_t B, int32_t num_blocks,
         int32_t max_entries, void* out, void* workspace, size_t workspace_bytes,
-        void* stream, int mode) {
+        void* stream, int mode, bool rotate) {
   if (!q || !k_pool || !v_pool || !block_table || !block_meta || !kv_lens || !q_indptr ||
       !q_positions || !out || !workspace)
     return LAZYATTN_ERR_NULL;
@@ -110,13 +110,13 @@ int run(const void* q, const void* k_pool, const void* v_pool, const int32_t* bl
                     block_table, block_meta, kv_lens, q_indptr, q_positions,
                     (uint16_t*)out, pf_prefix, (const uint16_t*)zero, num_seqs, Hq, Hkv,
                     num_blocks, (int)tiles, scale_log2, freqs};
-    if (launch_prefill(P, D, G, true, st) != hipSuccess) return LAZYATTN_ERR_LAUNCH;
+    if (launch_prefill(P, D, G, rotate, st) != hipSuccess) return LAZYATTN_ERR_LAUNCH;
   }
   DecodeParams Dp{(const uint16_t*)q, (const uint16_t*)k_pool, (const uint16_t*)v_pool,
                   block_table, block_meta, kv_lens, q_indptr, q_positions, dec_prefix,
                   (const uint16_t*)zero, partials, num_seqs, Hq, Hkv, num_blocks,
                   ds.bps, ds.smax, scale_log2, freqs};
-  if (launch_decode(Dp, D, G, st) != hipSuccess) return LAZYATTN_ERR_LAUNCH;
+  if (launch_decode(Dp, D, G, rotate, st) != hipSuccess) return LAZYATTN_ERR_LAUNCH;
   MergeParams Mp{q_indptr, block_table, dec_prefix, partials, (uint16_t*)out,
                  num_seqs, Hq, ds.bps, ds.smax, mode};
   if (launch_merge(Mp, total_q, D, st) != hipSuccess) return LAZYATTN_ERR_LAUNCH;
@@ -136,7 +136,7 @@ int lazyattn_prefill(const void* q, const void* k_pool, const void* v_pool,
                      size_t workspace_bytes, void* stream) {
   return run(q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indptr, q_positions,
              rope_base, num_seqs, total_q, Hq, Hkv, D, B, num_blocks, max_entries, out,
-             workspace, workspace_bytes, stream, kPlanMixed);
+             workspace, workspace_bytes, stream, kPlanMixed, true);
 }
 
 int lazyattn_decode(const void* q, const void* k_pool, const void* v_pool,
@@ -148,7 +148,33 @@ int lazyattn_decode(const void* q, const void* k_pool, const void* v_pool,
                     size_t workspace_bytes, void* stream) {
   return run(q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indptr, q_positions,
              rope_base, num_seqs, total_q, Hq, Hkv, D, B, num_blocks, max_entries, out,
-             workspace, workspace_bytes, stream, kPlanDecodeOnly);
+             workspace, workspace_bytes, stream, kPlanDecodeOnly, true);
+}
+
+int lazyattn_prefill_rotated_pool(const void* q, const void* k_pool, const void* v_pool,
+                                  const int32_t* block_table, const uint32_t* block_meta,
+                                  const int32_t* kv_lens, const int32_t* q_indptr,
+                                  const int32_t* q_positions, double rope_base,
+                                  int32_t num_seqs, int32_t total_q, int32_t Hq, int32_t Hkv,
+                                  int32_t D, int32_t B, int32_t num_blocks,
+                                  int32_t max_entries, void* out, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  return run(q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indptr, q_positions,
+             rope_base, num_seqs, total_q, Hq, Hkv, D, B, num_blocks, max_entries, out,
+             workspace, workspace_bytes, stream, kPlanMixed, false);
+}
+
+int lazyattn_decode_rotated_pool(const void* q, const void* k_pool, const void* v_pool,
+                                 const int32_t* block_table, const uint32_t* block_meta,
+                                 const int32_t* kv_lens, const int32_t* q_indptr,
+                                 const int32_t* q_positions, double rope_base,
+                                 int32_t num_seqs, int32_t total_q, int32_t Hq, int32_t Hkv,
+                                 int32_t D, int32_t B, int32_t num_blocks,
+                                 int32_t max_entries, void* out, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  return run(q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indptr, q_positions,
+             rope_base, num_seqs, total_q, Hq, Hkv, D, B, num_blocks, max_entries, out,
+             workspace, workspace_bytes, stream, kPlanDecodeOnly, false);
 }
 
 size_t lazyattn_prefill_workspace_bytes(int32_t num_seqs, int32_t total_q, int32_t max_entries,

@@ -56,7 +56,9 @@ struct GroupMeta {
   int id[2], delta[2], nval[2];
 };
 
-template <int D, int G>
+// ROT = false is the materialised baseline: the pool's keys already carry R(L) at their
+// logical positions, so keys are read as stored and q' = R(p) q for the whole item.
+template <int D, int G, bool ROT>
 __global__ __launch_bounds__(kDecodeWaves * 64, 2) void decode_kernel(DecodeParams P) {
   constexpr int NC = D / 32;                  // 32-dim k-steps of the score MFMA
   constexpr int HC = NC / 2;                  // chunk c pairs with chunk c + HC (dims + D/2)
@@ -82,7 +84,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 2) void decode_kernel(DecodePara
   // frequencies k = 32c + 8 q4 + 2 e2 + u as float4 (cos, sin of u = 0, 1) at
   // [c][q4][e2][j] -- the 16 slots of a 16-lane read are consecutive 16-byte words; and
   // R(32) for the per-group advance of q'
-  for (int i = threadIdx.x; i < HC * 4 * 4 * 16; i += kDecodeWaves * 64) {
+  for (int i = threadIdx.x; ROT && i < HC * 4 * 4 * 16; i += kDecodeWaves * 64) {
     const int j = i & 15, e2 = (i >> 4) & 3, qq = (i >> 6) & 3, c = i >> 8;
     const int f0 = 32 * c + 8 * qq + 2 * e2;
     float c0, s0, c1, s1;
@@ -202,7 +204,9 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 2) void decode_kernel(DecodePara
       // ---- q' of this lane's column: R(p - off_{t0+ph}) q_g ---------------------------
       const int d0 = gcur.delta[0];
       const int d1 = (t0 + 1 < ee) ? gcur.delta[1] : d0;
-      if (have_q && d0 == cur_delta && d1 == cur_delta) {
+      if (!ROT && have_q) {
+        // keys carry their absolute rotation: q' = R(p) q stays fixed
+      } else if (ROT && have_q && d0 == cur_delta && d1 == cur_delta) {
 #pragma unroll
         for (int c = 0; c < HC; ++c)
 #pragma unroll
@@ -217,7 +221,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 2) void decode_kernel(DecodePara
             }
           }
       } else {
-        const int n = p - ((t0 + ph) * kBlock + (ph ? d1 : d0));
+        const int n = ROT ? p - ((t0 + ph) * kBlock + (ph ? d1 : d0)) : p;
 #pragma unroll
         for (int c = 0; c < HC; ++c) {
           const u32x4 va = col_ok ? *(const u32x4*)(qrow + 32 * c + 8 * q4) : u32x4{0, 0, 0, 0};
@@ -233,7 +237,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 2) void decode_kernel(DecodePara
             qr[c + HC][e] = a * sn + b * cs;
           }
         }
-        have_q = (d0 == d1);
+        have_q = !ROT || (d0 == d1);
         cur_delta = d1;
       }
       // ---- scores of both blocks; each lane keeps its own phase's block ------------------
@@ -253,10 +257,15 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 2) void decode_kernel(DecodePara
           for (int i = 0; i < 4; ++i) {
             const float a0 = bf_lo(kcur[b][c][i]), a1 = bf_hi(kcur[b][c][i]);
             const float b0 = bf_lo(kcur[b][c + HC][i]), b1 = bf_hi(kcur[b][c + HC][i]);
-            const f32x4 t = slot_tab[((c * 4 + q4) * 4 + i) * 16 + i16];
-            const float c0 = t[0], s0 = t[1], c1 = t[2], s1 = t[3];
-            lo[i] = pack_f16(a0 * c0 - b0 * s0, a1 * c1 - b1 * s1);
-            hi[i] = pack_f16(a0 * s0 + b0 * c0, a1 * s1 + b1 * c1);
+            if (ROT) {
+              const f32x4 t = slot_tab[((c * 4 + q4) * 4 + i) * 16 + i16];
+              const float c0 = t[0], s0 = t[1], c1 = t[2], s1 = t[3];
+              lo[i] = pack_f16(a0 * c0 - b0 * s0, a1 * c1 - b1 * s1);
+              hi[i] = pack_f16(a0 * s0 + b0 * c0, a1 * s1 + b1 * c1);
+            } else {
+              lo[i] = pack_f16(a0, a1);
+              hi[i] = pack_f16(b0, b1);
+            }
           }
           S[b] = mfma16h(as_f16x8(lo), as_f16x8(qlo), S[b]);
           S[b] = mfma16h(as_f16x8(hi), as_f16x8(qhi), S[b]);
@@ -344,21 +353,22 @@ static int num_cus() {
 
 int decode_resident_waves() { return num_cus() * kDecodeWgPerCu * kDecodeWaves; }
 
-template <int D>
-static hipError_t launch_d(const DecodeParams& p, int G, hipStream_t st) {
+template <int D, bool ROT>
+static hipError_t launch_dr(const DecodeParams& p, int G, hipStream_t st) {
   dim3 grid(num_cus() * kDecodeWgPerCu), block(kDecodeWaves * 64);
   switch (G) {
-    case 1: hipLaunchKernelGGL((decode_kernel<D, 1>), grid, block, 0, st, p); break;
-    case 2: hipLaunchKernelGGL((decode_kernel<D, 2>), grid, block, 0, st, p); break;
-    case 4: hipLaunchKernelGGL((decode_kernel<D, 4>), grid, block, 0, st, p); break;
-    case 8: hipLaunchKernelGGL((decode_kernel<D, 8>), grid, block, 0, st, p); break;
+    case 1: hipLaunchKernelGGL((decode_kernel<D, 1, ROT>), grid, block, 0, st, p); break;
+    case 2: hipLaunchKernelGGL((decode_kernel<D, 2, ROT>), grid, block, 0, st, p); break;
+    case 4: hipLaunchKernelGGL((decode_kernel<D, 4, ROT>), grid, block, 0, st, p); break;
+    case 8: hipLaunchKernelGGL((decode_kernel<D, 8, ROT>), grid, block, 0, st, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_decode(const DecodeParams& p, int D, int G, hipStream_t st) {
-  return D == 128 ? launch_d<128>(p, G, st) : launch_d<64>(p, G, st);
+hipError_t launch_decode(const DecodeParams& p, int D, int G, bool rotate, hipStream_t st) {
+  if (D == 128) return rotate ? launch_dr<128, true>(p, G, st) : launch_dr<128, false>(p, G, st);
+  return rotate ? launch_dr<64, true>(p, G, st) : launch_dr<64, false>(p, G, st);
 }
 
 }  // namespace lazyattn

@@ -73,6 +73,6 @@ hipError_t launch_prefill(const PrefillParams& p, int D, int G, bool rotate, hip
 int prefill_positions_per_tile(int G);
 // waves of the decode grid (all resident at once); decode items are dealt round-robin to them
 int decode_resident_waves();
-hipError_t launch_decode(const DecodeParams& p, int D, int G, hipStream_t st);
+hipError_t launch_decode(const DecodeParams& p, int D, int G, bool rotate, hipStream_t st);
 
 }  // namespace lazyattn

@@ -242,6 +242,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
   const int tab_pos = 2 * tpos(tab_b, (tab_v >> 1) % HALF) + (tab_v & 1);
   // (the per-lane block choice selects among readlane results, never indexes an array)
   auto make_table = [&](const WinDec& wd, int d, int buf) __attribute__((always_inline)) {
+    if (!ROTATE) return;                                    // keys need no phase table
     const int o = rl(wd.off, 4 * d + tab_b);
     ((float*)tbl[buf])[tab_pos] = rope_sin_rev(o - p_ref, tab_f, tab_quarter);
   };

@@ -176,6 +176,25 @@ def test_reuse_equals_copies():
     assert np.max(np.abs(brute_attention(wc) - out_reuse)) < 1e-12
 
 
+def test_rotated_pool_baseline_equals_lazy():
+    """The materialised baseline -- a pool whose keys already carry R(L) at the position
+    they are referenced at, read as stored -- gives the same attention as the position-free
+    pool with rotation applied ("Mathematical Equivalence"); checked against the
+    independent brute force too."""
+    segs = [Segment("doc", 3, doc=0), Segment("doc", 47, doc=1), Segment("private", 90, tokens=12)]
+    wl = small(segs=segs, q_len=12, seed=23, q_scale=3.0)
+    ids = [wl.compact_ids(s) for s in range(wl.num_seqs)]
+    kp = oracle.rotated_pool(wl.k_bits, ids, wl.seq_offsets, wl.kv_lens, wl.B, wl.rope_base)
+    base_out = oracle.lazy_attention(wl.q_bits, kp, wl.v_bits, ids, wl.seq_offsets, wl.kv_lens,
+                                     wl.q_indptr, wl.q_pos, wl.rope_base, wl.B, rotate_keys=False)
+    assert np.max(np.abs(base_out - oracle_out(wl))) < 1e-12
+    assert np.max(np.abs(base_out - brute_attention(wl))) < 1e-12
+    # and the baseline really depends on where the rotation was applied
+    wrong = oracle.lazy_attention(wl.q_bits, kp, wl.v_bits, ids, wl.seq_offsets, wl.kv_lens,
+                                  wl.q_indptr, wl.q_pos, wl.rope_base, wl.B)
+    assert np.max(np.abs(wrong - base_out)) > 1e-3
+
+
 def test_translation_invariance():
     wl = small(seed=31, q_scale=4.0)
     base_out = oracle_out(wl)

@@ -120,6 +120,50 @@ def test_mixed_batch_small():
     compare(run_hip(wl, "decode"), oracle_out(wl), "mixed-small/decode")
 
 
+def _distinct_cases():
+    """Layouts in which every pool block is referenced once (a rotated pool can hold it)."""
+    segs = [Segment("doc", 7 + 32 * i + 3 * (i % 2), doc=i) for i in range(9)] + \
+        [Segment("private", 7 + 32 * 9 + 5, tokens=150)]
+    one = dict(Hq=8, Hkv=2, D=128, n_docs=9, segs=segs, q_len=150, seed=12, q_scale=3.0)
+    reqs = [RequestLayout([Segment("doc", 11, doc=0), Segment("doc", 60, doc=1),
+                           Segment("private", 100, tokens=9)], 1),
+            RequestLayout([Segment("doc", 400, doc=2), Segment("doc", 3, doc=3),
+                           Segment("private", 700, tokens=33)], 1),
+            RequestLayout([Segment("doc", 1000, doc=4), Segment("private", 1040, tokens=5)], 5)]
+    multi = dict(Hq=4, Hkv=1, D=64, n_docs=5, requests=reqs, seed=13)
+    return [("distinct-one-request-D128", one), ("distinct-multi-request-D64", multi)]
+
+
+@pytest.mark.parametrize("kind", ["prefill", "decode"])
+@pytest.mark.parametrize("name,kw", _distinct_cases(), ids=[c[0] for c in _distinct_cases()])
+def test_rotated_pool_baseline(name, kw, kind):
+    """The materialised-baseline entry points over a pool that holds every key rotated to
+    the position it is referenced at (built on the host in float64, rounded to bf16)
+    against the oracle reading that pool as stored."""
+    import torch
+    import oracle
+    import position_agnostic_kv_paged_amd as L
+    from workload import f32_to_bf16_bits
+    wl = small(**kw)
+    ids = [wl.compact_ids(s) for s in range(wl.num_seqs)]
+    kp = oracle.rotated_pool(wl.k_bits, ids, wl.seq_offsets, wl.kv_lens, wl.B, wl.rope_base)
+    kp_bits = wl.k_bits.copy()                  # unreferenced slots keep their NaN fill
+    fin = np.isfinite(kp)
+    kp_bits[fin] = f32_to_bf16_bits(kp[fin].astype(np.float32))
+    want = oracle.lazy_attention(wl.q_bits, kp_bits, wl.v_bits, ids, wl.seq_offsets,
+                                 wl.kv_lens, wl.q_indptr, wl.q_pos, wl.rope_base, wl.B,
+                                 rotate_keys=False)
+    t = wl.to_device("cuda")
+    t["k_pool"] = torch.from_numpy(kp_bits.view(np.int16)).to("cuda").view(torch.bfloat16)
+    meta = torch.from_numpy(np.ascontiguousarray(words_for(wl)).view(np.int32)).to("cuda")
+    fn = L.prefill_rotated_pool if kind == "prefill" else L.decode_rotated_pool
+    say(f"rotated-pool baseline {name} via {kind}")
+    out = fn(t["q"], t["k_pool"], t["v_pool"], t["block_table"], meta, t["kv_lens"],
+             t["q_indptr"], t["q_pos"], wl.rope_base, max(len(x) for x in wl.seq_block_ids))
+    torch.cuda.synchronize()
+    compare(out.float().cpu().numpy().astype(np.float64), want, f"{name}/{kind}-baseline")
+
+
 # ------------------------------------------------------------------ properties
 
 def test_reuse_equals_copy_bitwise_on_gpu():
