@@ -145,6 +145,30 @@ int lazyattn_decode_rotated_pool(const void* q, const void* k_pool, const void* 
                                  int32_t max_entries, void* out, void* workspace,
                                  size_t workspace_bytes, void* stream);
 
+/*
+ * lazyattn_materialize_rotated -- the position-adjusted copy the method avoids (technical
+ * summary: "Mathematical Equivalence"; reuse schemes that store rotated copies), for
+ * measurement. For every block-table entry e (flat index, e < min(n_entries,
+ * block_table[num_seqs])) of sequence s with word (id, delta) and offset off_e = t*B + delta
+ * it writes private block e of the destination pools:
+ *   dst_k[e, g, j, :] = R(off_e + j) k_pool[id, g, j, :]  (bf16, round to nearest even)
+ *   dst_v[e, g, j, :] = v_pool[id, g, j, :]
+ * for the slots j holding keys of the sequence (slots at or past kv_lens[s], and entries with
+ * id >= num_blocks, are written as zeros), and dst_meta[e] = the word with block id e and the
+ * same delta. dst_k / dst_v: bf16 [n_entries, Hkv, B, D], dst_meta: uint32 [n_entries], all
+ * device memory owned by the caller; n_entries should equal block_table[num_seqs] and must be
+ * <= 2^17 (the new ids must fit the word; else LAZYATTN_ERR_RANGE). Then
+ * lazyattn_*_rotated_pool over (dst_k, dst_v, dst_meta, block_table, ...) computes the same
+ * attention as lazyattn_* over the position-free pool. Asynchronous on `stream`; errors as
+ * above (NULL, ALIGN for 16-byte pools / 4-byte arrays, SHAPE, RANGE, ARG, LAUNCH).
+ */
+int lazyattn_materialize_rotated(const void* k_pool, const void* v_pool,
+                                 const int32_t* block_table, const uint32_t* block_meta,
+                                 const int32_t* kv_lens, double rope_base, int32_t num_seqs,
+                                 int32_t n_entries, int32_t Hkv, int32_t D, int32_t B,
+                                 int32_t num_blocks, void* dst_k, void* dst_v,
+                                 uint32_t* dst_meta, void* stream);
+
 /* Workspace sizes (bytes) for the calls above; 0 on invalid sizes. */
 size_t lazyattn_prefill_workspace_bytes(int32_t num_seqs, int32_t total_q, int32_t max_entries,
                                         int32_t Hq, int32_t Hkv, int32_t D);

@@ -10,7 +10,8 @@ OK, ERR_NULL, ERR_ALIGN, ERR_SHAPE, ERR_RANGE, ERR_WORKSPACE, ERR_LAUNCH, ERR_AR
 # every symbol include/lazyattn.h declares
 EXPORTED = [
     "lazyattn_prefill", "lazyattn_decode", "lazyattn_prefill_rotated_pool",
-    "lazyattn_decode_rotated_pool", "lazyattn_prefill_workspace_bytes",
+    "lazyattn_decode_rotated_pool", "lazyattn_materialize_rotated",
+    "lazyattn_prefill_workspace_bytes",
     "lazyattn_decode_workspace_bytes", "lazyattn_encode_meta", "lazyattn_debug_decode_meta",
     "lazyattn_status_str", "lazyattn_version",
 ]
@@ -43,6 +44,9 @@ def lib():
     for name in ("lazyattn_prefill_workspace_bytes", "lazyattn_decode_workspace_bytes"):
         f = getattr(L, name)
         f.argtypes, f.restype = [i32] * 6, ctypes.c_size_t
+    L.lazyattn_materialize_rotated.argtypes = [vp, vp, vp, vp, vp, dbl, i32, i32, i32, i32, i32,
+                                               i32, vp, vp, vp, vp]
+    L.lazyattn_materialize_rotated.restype = ctypes.c_int
     L.lazyattn_encode_meta.argtypes = [vp, vp, vp, i32, i32, vp, vp]
     L.lazyattn_encode_meta.restype = ctypes.c_int
     L.lazyattn_debug_decode_meta.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp]

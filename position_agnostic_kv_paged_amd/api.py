@@ -87,6 +87,27 @@ def decode_rotated_pool(q, k_pool, v_pool, block_table, block_meta, kv_lens, q_i
                       q_indptr, q_pos, rope_base, max_entries, out, workspace, stream, True)
 
 
+def materialize_rotated(k_pool, v_pool, block_table, block_meta, kv_lens, rope_base, n_entries,
+                        dst_k=None, dst_v=None, dst_meta=None, stream=None):
+    """lazyattn_materialize_rotated: private rotated copies of every entry's block; returns
+    (dst_k, dst_v, dst_meta) (allocated with torch when not given)."""
+    import torch
+    num_blocks, Hkv, B, D = k_pool.shape
+    if dst_k is None:
+        dst_k = torch.empty((max(n_entries, 1), Hkv, B, D), dtype=k_pool.dtype,
+                            device=k_pool.device)
+    if dst_v is None:
+        dst_v = torch.empty_like(dst_k)
+    if dst_meta is None:
+        dst_meta = torch.empty(max(n_entries, 1), dtype=torch.int32, device=k_pool.device)
+    rc = lib().lazyattn_materialize_rotated(
+        _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(block_meta), _ptr(kv_lens),
+        float(rope_base), kv_lens.numel(), int(n_entries), Hkv, D, B, num_blocks, _ptr(dst_k),
+        _ptr(dst_v), _ptr(dst_meta), _stream(stream))
+    check(rc, "lazyattn_materialize_rotated")
+    return dst_k, dst_v, dst_meta
+
+
 def encode_meta(block_ids, offsets, block_table, B=BLOCK):
     """Host encoder: (int32 ids, int64 offsets, int32 CSR) -> uint32 words (numpy)."""
     ids = np.ascontiguousarray(block_ids, dtype=np.int32)

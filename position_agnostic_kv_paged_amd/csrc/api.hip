@@ -219,6 +219,35 @@ int lazyattn_encode_meta(const int32_t* block_ids, const int64_t* offsets,
   return rc;
 }
 
+int lazyattn_materialize_rotated(const void* k_pool, const void* v_pool,
+                                 const int32_t* block_table, const uint32_t* block_meta,
+                                 const int32_t* kv_lens, double rope_base, int32_t num_seqs,
+                                 int32_t n_entries, int32_t Hkv, int32_t D, int32_t B,
+                                 int32_t num_blocks, void* dst_k, void* dst_v,
+                                 uint32_t* dst_meta, void* stream) {
+  if (!k_pool || !v_pool || !block_table || !block_meta || !kv_lens || !dst_k || !dst_v ||
+      !dst_meta)
+    return LAZYATTN_ERR_NULL;
+  if (!aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(dst_k, 16) ||
+      !aligned(dst_v, 16) || !aligned(block_table, 4) || !aligned(block_meta, 4) ||
+      !aligned(kv_lens, 4) || !aligned(dst_meta, 4))
+    return LAZYATTN_ERR_ALIGN;
+  if (num_seqs <= 0 || Hkv <= 0 || num_blocks <= 0 || B != kBlock || (D != 64 && D != 128) ||
+      n_entries < 0)
+    return LAZYATTN_ERR_SHAPE;
+  if (n_entries > (int32_t)kIdMask + 1) return LAZYATTN_ERR_RANGE;   // new ids must fit a word
+  if (!(rope_base > 1.0)) return LAZYATTN_ERR_ARG;
+  MaterializeParams P{(const uint16_t*)k_pool, (const uint16_t*)v_pool, block_table,
+                      block_meta, kv_lens, (uint16_t*)dst_k, (uint16_t*)dst_v, dst_meta,
+                      num_seqs, n_entries, Hkv, num_blocks, {}};
+  for (int k = 0; k < D / 2; ++k)
+    P.fr.f[k] = std::pow(rope_base, -2.0 * k / D) / (2.0 * M_PI);
+  if (launch_materialize(P, D, 8 * decode_resident_waves() / 8, (hipStream_t)stream) !=
+      hipSuccess)
+    return LAZYATTN_ERR_LAUNCH;
+  return LAZYATTN_OK;
+}
+
 int lazyattn_debug_decode_meta(const uint32_t* words, const int32_t* block_table,
                                int32_t num_seqs, int32_t n_entries, int32_t B,
                                int32_t* ids_out, int32_t* offsets_out, void* stream) {

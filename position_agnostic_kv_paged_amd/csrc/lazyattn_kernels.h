@@ -71,6 +71,20 @@ hipError_t launch_debug_decode(const uint32_t* words, const int32_t* bt, int num
 // p.tiles_bound: upper bound of prefill tiles (extra workgroups exit at once)
 hipError_t launch_prefill(const PrefillParams& p, int D, int G, bool rotate, hipStream_t st);
 int prefill_positions_per_tile(int G);
+struct MaterializeParams {
+  const uint16_t* k_pool;
+  const uint16_t* v_pool;
+  const int32_t* block_table;
+  const uint32_t* block_meta;
+  const int32_t* kv_lens;
+  uint16_t* dst_k;           // [n_entries, Hkv, B, D]
+  uint16_t* dst_v;
+  uint32_t* dst_meta;        // [n_entries]
+  int num_seqs, n_entries, Hkv, num_blocks;
+  RopeFreqs fr;              // host-computed table (kernel argument)
+};
+hipError_t launch_materialize(const MaterializeParams& p, int D, int num_wg, hipStream_t st);
+
 // waves of the decode grid (all resident at once); decode items are dealt round-robin to them
 int decode_resident_waves();
 hipError_t launch_decode(const DecodeParams& p, int D, int G, bool rotate, hipStream_t st);

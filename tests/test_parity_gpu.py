@@ -14,7 +14,7 @@ pytestmark = pytest.mark.gpu
 import oracle  # noqa: E402
 from workload import make, Segment, RequestLayout, build  # noqa: E402
 from tests.util import small, oracle_out  # noqa: E402
-from tests.gpu_util import run_hip, compare, say, words_for  # noqa: E402
+from tests.gpu_util import run_hip, compare, say, words_for, MAX_ABS  # noqa: E402
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -162,6 +162,78 @@ def test_rotated_pool_baseline(name, kw, kind):
              t["q_indptr"], t["q_pos"], wl.rope_base, max(len(x) for x in wl.seq_block_ids))
     torch.cuda.synchronize()
     compare(out.float().cpu().numpy().astype(np.float64), want, f"{name}/{kind}-baseline")
+
+
+def _materialize_cases():
+    segs_overlap = [Segment("doc", 3, doc=1), Segment("doc", 20, doc=0),
+                    Segment("doc", 100, doc=1), Segment("private", 140, tokens=21)]
+    return _distinct_cases() + [
+        ("overlap-repeat-partial", dict(Hq=8, Hkv=2, D=128, segs=segs_overlap, q_len=21,
+                                        seed=3, q_scale=4.0))]
+
+
+@pytest.mark.parametrize("name,kw", _materialize_cases(), ids=[c[0] for c in _materialize_cases()])
+def test_materialize_rotated(name, kw):
+    """lazyattn_materialize_rotated writes, for every entry, its keys rotated to their
+    logical positions (within one bf16 ulp of the oracle's float64 rotation), its values
+    (bit for bit) and a word naming the private block; attention over that copy through the
+    baseline entry points matches the oracle on the original position-free inputs (blocks
+    reused at several offsets get one copy per placement)."""
+    import torch
+    import oracle
+    import position_agnostic_kv_paged_amd as L
+    from oracle.attention import bf16_bits_to_f64
+    from workload import f32_to_bf16_bits
+    wl = small(**kw)
+    t = wl.to_device("cuda")
+    words = words_for(wl)
+    meta = torch.from_numpy(np.ascontiguousarray(words).view(np.int32)).to("cuda")
+    n = int(wl.block_table[-1])
+    say(f"materialize {name}: {n} entries")
+    dk, dv, dm = L.materialize_rotated(t["k_pool"], t["v_pool"], t["block_table"], meta,
+                                       t["kv_lens"], wl.rope_base, n)
+    torch.cuda.synchronize()
+    got_k = dk.view(torch.int16).cpu().numpy().view(np.uint16)
+    got_v = dv.view(torch.int16).cpu().numpy().view(np.uint16)
+    got_m = dm.cpu().numpy().view(np.uint32)
+    # expected, from the oracle's definitions (host only)
+    exp_k = np.zeros_like(got_k)
+    exp_v = np.zeros_like(got_v)
+    for s_ in range(wl.num_seqs):
+        ids = wl.compact_ids(s_)
+        T = len(ids)
+        for t_ in range(T):
+            e = int(wl.block_table[s_]) + t_
+            n_t = wl.B if t_ < T - 1 else int(wl.kv_lens[s_]) - (T - 1) * wl.B
+            pos = int(wl.seq_offsets[s_][t_]) + np.arange(n_t)
+            kk = bf16_bits_to_f64(wl.k_bits[ids[t_]][:, :n_t, :])
+            rot = oracle.rope.rotate(kk, pos[None, :], wl.rope_base)
+            exp_k[e, :, :n_t] = f32_to_bf16_bits(rot.astype(np.float32))
+            exp_v[e, :, :n_t] = wl.v_bits[ids[t_]][:, :n_t, :]
+    diff = np.abs(got_k.astype(np.int32) - exp_k.astype(np.int32))
+    say(f"  keys: {np.count_nonzero(diff)} of {diff.size} bit patterns differ, max {diff.max()}")
+    assert diff.max() <= 1 and np.count_nonzero(diff) <= 1e-3 * diff.size
+    assert np.array_equal(got_v, exp_v)
+    exp_m = oracle.encode_meta(np.arange(n), np.concatenate(wl.seq_offsets), wl.block_table, wl.B)
+    assert np.array_equal(got_m, np.asarray(exp_m, dtype=np.uint32))
+    # attention over the copy: to parity with the oracle reading the host-built copy as
+    # stored; against LazyAttention's definition the copy's bf16 rounding of rotated keys
+    # (8 mantissa bits, where the lazy kernels keep rotated keys in fp16) costs up to about
+    # 2.5e-2 on the x4-query stress layout, so that comparison gets a looser bound
+    host_copy_k = exp_k
+    want_copy = oracle.lazy_attention(wl.q_bits, host_copy_k, exp_v, [np.arange(n)[int(wl.block_table[s_]):int(wl.block_table[s_ + 1])] for s_ in range(wl.num_seqs)],
+                                      wl.seq_offsets, wl.kv_lens, wl.q_indptr, wl.q_pos,
+                                      wl.rope_base, wl.B, rotate_keys=False)
+    want_lazy = oracle_out(wl)
+    for kind, fn in (("prefill", L.prefill_rotated_pool), ("decode", L.decode_rotated_pool)):
+        out = fn(t["q"], dk, dv, t["block_table"], dm, t["kv_lens"], t["q_indptr"], t["q_pos"],
+                 wl.rope_base, max(len(x) for x in wl.seq_block_ids))
+        torch.cuda.synchronize()
+        got = out.float().cpu().numpy().astype(np.float64)
+        compare(got, want_copy, f"{name}/copy+{kind}")
+        d = float(np.abs(got - want_lazy).max())
+        say(f"  {name}/copy+{kind} vs the position-free definition: max_abs={d:.3e}")
+        assert d <= 3 * MAX_ABS
 
 
 # ------------------------------------------------------------------ properties
