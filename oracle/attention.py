@@ -41,6 +41,9 @@ def materialise(k_pool, v_pool, block_ids, offsets, kv_len, B, base, rotate_keys
     T = len(block_ids)
     if kv_len <= (T - 1) * B or kv_len > T * B:
         raise ValueError("kv_len inconsistent with the number of entries")
+    if T == 0:                                   # no entries: no keys
+        Hkv, D = k_pool.shape[1], k_pool.shape[3]
+        return (np.zeros((Hkv, 0, D)), np.zeros((Hkv, 0, D)), np.zeros(0, dtype=np.int64))
     ks, vs, ps = [], [], []
     for t in range(T):
         n_t = B if t < T - 1 else kv_len - (T - 1) * B
@@ -69,6 +72,8 @@ def attend(q_rot, q_pos, K_hat, V_hat, key_pos):
     Hkv = K_hat.shape[0]
     G = Hq // Hkv
     out = np.zeros((n_q, Hq, D), dtype=np.float64)
+    if K_hat.shape[1] == 0:                      # no key at all: every row sees none
+        return out
     visible = key_pos[None, :] <= np.asarray(q_pos, dtype=np.int64)[:, None]
     scale = 1.0 / np.sqrt(D)
     for h in range(Hq):

@@ -51,6 +51,13 @@ __device__ __forceinline__ int sel4(const int (&a)[4], int b) {
   return b == 0 ? a[0] : b == 1 ? a[1] : b == 2 ? a[2] : a[3];
 }
 
+// c ? a : b for pointers as an integer blend: a plain select of an expensive address may be
+// turned into a branch, which would split the interleaved MFMA block it sits in
+__device__ __forceinline__ const void* blend_ptr(bool c, const void* a, const void* b) {
+  const uint64_t m = 0 - (uint64_t)c;
+  return (const void*)(((uint64_t)a & m) | ((uint64_t)b & ~m));
+}
+
 // Words of key tiles kt .. kt+3 live in one VGPR ("window"): lane i < 16 holds the word of
 // entry 4 kt + i. The loop issues one small vector load per key tile (the next window);
 // each lane decodes its own word (block id, logical offset, valid keys) on the VALU, and
@@ -58,9 +65,9 @@ __device__ __forceinline__ int sel4(const int (&a)[4], int b) {
 __device__ __forceinline__ uint32_t load_window(const PrefillParams& P, int e0, int T, int kt,
                                                 int lane) {
   // every lane loads (no branch): lanes past the table read its last word, which the
-  // decode marks empty (T >= 1 whenever a key tile exists)
+  // decode marks empty; a sequence without entries reads the zeroed workspace chunk
   const int ent = min(4 * kt + lane, T - 1);
-  return P.block_meta[e0 + max(ent, 0)];
+  return *(const uint32_t*)blend_ptr(T > 0, P.block_meta + e0 + max(ent, 0), P.zero);
 }
 
 struct WinDec {
@@ -76,13 +83,6 @@ __device__ __forceinline__ WinDec decode_window(const PrefillParams& P, uint32_t
   d.nv = ((lane < 16) & (ent < T) & (d.id < P.num_blocks))   // out-of-pool id: never read
              ? min(max(kvlen - ent * kBlock, 0), kBlock) : 0;
   return d;
-}
-
-// c ? a : b for pointers as an integer blend: a plain select of an expensive address may be
-// turned into a branch, which would split the interleaved MFMA block it sits in
-__device__ __forceinline__ const void* blend_ptr(bool c, const void* a, const void* b) {
-  const uint64_t m = 0 - (uint64_t)c;
-  return (const void*)(((uint64_t)a & m) | ((uint64_t)b & ~m));
 }
 
 template <int d>

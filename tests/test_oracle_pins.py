@@ -159,6 +159,19 @@ def test_no_visible_key_outputs_zero():
     assert np.array_equal(oracle_out(wl), np.zeros_like(oracle_out(wl)))
 
 
+def test_sequence_without_entries_outputs_zero():
+    """A sequence with no block-table entries has no key, so its rows are 0; the other
+    sequences of the batch are unaffected (each equals its own single-request oracle)."""
+    r1 = RequestLayout([Segment("doc", 5, doc=0), Segment("private", 40, tokens=20)], 20)
+    empty = RequestLayout([], 3, np.array([7, 8, 9]))
+    both = build("small", 4, 2, 64, 16, 10000.0, 3, 32, [r1, empty], 11)
+    alone = build("small", 4, 2, 64, 16, 10000.0, 3, 32, [r1], 11)
+    out = oracle_out(both)
+    assert both.kv_lens[1] == 0 and both.block_table[2] == both.block_table[1]
+    assert np.array_equal(out[20:], np.zeros_like(out[20:]))
+    assert np.array_equal(out[:20], oracle_out(alone))
+
+
 def test_reuse_equals_copies():
     """One physical block at two offsets == two physical copies (each used once)."""
     lay_reuse = RequestLayout([Segment("doc", 0, doc=0), Segment("doc", 77, doc=0),

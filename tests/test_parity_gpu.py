@@ -106,6 +106,26 @@ def test_mini_cases(name, kw, kind):
     compare(run_hip(wl, kind), oracle_out(wl), f"{name}/{kind}")
 
 
+@pytest.mark.parametrize("kind", ["prefill", "decode"])
+def test_sequences_without_entries(kind):
+    """Sequences with no block-table entries (first, middle and last of the batch) give 0
+    rows and leave the others exact; the last one's table starts at the end of the words."""
+    segs = [Segment("doc", 5, doc=0), Segment("doc", 40, doc=2),
+            Segment("private", 72, tokens=20)]
+    nq = 20 if kind == "prefill" else 1
+    ne = 2 if kind == "prefill" else 1
+    full = RequestLayout(segs, nq)
+    empty = RequestLayout([], ne, np.array([7, 9][:ne]))
+    wl = build("small", 8, 2, 128, 16, 10000.0, 3, 32, [empty, full, empty, full, empty], 12)
+    say(f"sequences without entries via {kind}")
+    assert wl.kv_lens[-1] == 0 and wl.block_table[-1] == wl.block_table[-2]
+    got, want = run_hip(wl, kind), oracle_out(wl)
+    compare(got, want, f"empty-sequences/{kind}")
+    for s in (0, 2, 4):
+        r0, r1 = int(wl.q_indptr[s]), int(wl.q_indptr[s + 1])
+        assert np.array_equal(got[r0:r1], np.zeros_like(got[r0:r1]))
+
+
 def test_mixed_batch_small():
     """One call with prefill (q_len > 1), decode (q_len = 1) and empty (q_len = 0) requests."""
     reqs = [RequestLayout([Segment("doc", 11, doc=0), Segment("doc", 60, doc=1),
@@ -325,3 +345,21 @@ def test_mixed_70b_batch():
         return q0 + np.array([0, 31, 32, 255, 256, 511])
     g, w = _sampled(wl, "prefill", [0, 3, 4, 50, 99], rows)
     compare(g, w, "mixed")
+
+
+@pytest.mark.gpu
+def test_probes():
+    """The ceiling probes run and read what they claim to: the read probe's XOR fold equals
+    the buffer's, and the MFMA probe reports positive cycle spans."""
+    import torch
+    import position_agnostic_kv_paged_amd as L
+    g = torch.Generator().manual_seed(31)
+    host = torch.randint(-2**31, 2**31 - 1, (3 * 2**20 + 4,), generator=g, dtype=torch.int64)
+    host = host.to(torch.int32)
+    buf = host.cuda()
+    got = L.probe_read(buf).cpu().numpy().view(np.uint32)
+    want = np.bitwise_xor.reduce(host.numpy().view(np.uint32))
+    assert np.bitwise_xor.reduce(got) == want
+    cyc, flops = L.probe_mfma(4)
+    torch.cuda.synchronize()
+    assert flops > 0 and int(cyc.min().item()) > 0
