@@ -169,6 +169,22 @@ int lazyattn_materialize_rotated(const void* k_pool, const void* v_pool,
                                  int32_t num_blocks, void* dst_k, void* dst_v,
                                  uint32_t* dst_meta, void* stream);
 
+/*
+ * Measured ceilings (for reporting; not part of the attention path):
+ *  lazyattn_probe_cus -- compute units the probes and the decode grid are sized for.
+ *  lazyattn_probe_mfma -- one workgroup of 8 waves per CU; every wave issues iters x 16
+ *    independent 32x32x16 fp16 MFMAs (32768 FLOP each) and writes its s_memtime span
+ *    (shader cycles) to cycles_out (uint64 [probe_cus * 8]); scratch_out: float
+ *    [probe_cus * 512] (results folded there). Time it with events: FLOP / time is the
+ *    matrix-core rate reachable in practice; cycles / time is the sustained shader clock.
+ *  lazyattn_probe_read -- reads `bytes` (a multiple of 16, 16-byte aligned) of device memory
+ *    once with 16-byte non-temporal loads; scratch_out: uint32 [8 * probe_cus * 256].
+ * Errors: NULL, ALIGN, ARG (iters <= 0), SHAPE (bytes), LAUNCH.
+ */
+int32_t lazyattn_probe_cus(void);
+int lazyattn_probe_mfma(int32_t iters, void* cycles_out, void* scratch_out, void* stream);
+int lazyattn_probe_read(const void* buf, size_t bytes, void* scratch_out, void* stream);
+
 /* Workspace sizes (bytes) for the calls above; 0 on invalid sizes. */
 size_t lazyattn_prefill_workspace_bytes(int32_t num_seqs, int32_t total_q, int32_t max_entries,
                                         int32_t Hq, int32_t Hkv, int32_t D);

@@ -10,7 +10,8 @@ OK, ERR_NULL, ERR_ALIGN, ERR_SHAPE, ERR_RANGE, ERR_WORKSPACE, ERR_LAUNCH, ERR_AR
 # every symbol include/lazyattn.h declares
 EXPORTED = [
     "lazyattn_prefill", "lazyattn_decode", "lazyattn_prefill_rotated_pool",
-    "lazyattn_decode_rotated_pool", "lazyattn_materialize_rotated",
+    "lazyattn_decode_rotated_pool", "lazyattn_materialize_rotated", "lazyattn_probe_cus",
+    "lazyattn_probe_mfma", "lazyattn_probe_read",
     "lazyattn_prefill_workspace_bytes",
     "lazyattn_decode_workspace_bytes", "lazyattn_encode_meta", "lazyattn_debug_decode_meta",
     "lazyattn_status_str", "lazyattn_version",
@@ -47,6 +48,9 @@ def lib():
     L.lazyattn_materialize_rotated.argtypes = [vp, vp, vp, vp, vp, dbl, i32, i32, i32, i32, i32,
                                                i32, vp, vp, vp, vp]
     L.lazyattn_materialize_rotated.restype = ctypes.c_int
+    L.lazyattn_probe_cus.argtypes, L.lazyattn_probe_cus.restype = [], i32
+    L.lazyattn_probe_mfma.argtypes, L.lazyattn_probe_mfma.restype = [i32, vp, vp, vp], ctypes.c_int
+    L.lazyattn_probe_read.argtypes, L.lazyattn_probe_read.restype = [vp, u64, vp, vp], ctypes.c_int
     L.lazyattn_encode_meta.argtypes = [vp, vp, vp, i32, i32, vp, vp]
     L.lazyattn_encode_meta.restype = ctypes.c_int
     L.lazyattn_debug_decode_meta.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp]

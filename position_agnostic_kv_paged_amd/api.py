@@ -132,3 +132,34 @@ def debug_decode_meta(words, block_table, stream=None):
                                           _ptr(offs), _stream(stream))
     check(rc, "lazyattn_debug_decode_meta")
     return ids, offs
+
+
+def probe_cus():
+    """Compute units the probes (and the decode grid) are sized for."""
+    return int(lib().lazyattn_probe_cus())
+
+
+def probe_mfma(iters, cycles=None, scratch=None, stream=None):
+    """lazyattn_probe_mfma: launches the MFMA loop; returns (cycles uint64-as-int64 tensor,
+    flops of the launch). Time it with events on `stream`."""
+    import torch
+    n = probe_cus()
+    if cycles is None:
+        cycles = torch.empty(n * 8, dtype=torch.int64, device="cuda")
+    if scratch is None:
+        scratch = torch.empty(n * 512, dtype=torch.float32, device=cycles.device)
+    rc = lib().lazyattn_probe_mfma(int(iters), _ptr(cycles), _ptr(scratch), _stream(stream))
+    check(rc, "lazyattn_probe_mfma")
+    return cycles, float(n) * 8 * iters * 16 * 2 * 32 * 32 * 16
+
+
+def probe_read(buf, scratch=None, stream=None):
+    """lazyattn_probe_read: reads every byte of the device tensor `buf` once; returns the
+    uint32 scratch whose XOR is the XOR of buf's 32-bit words."""
+    import torch
+    if scratch is None:
+        scratch = torch.empty(8 * probe_cus() * 256, dtype=torch.int32, device=buf.device)
+    rc = lib().lazyattn_probe_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(scratch),
+                                   _stream(stream))
+    check(rc, "lazyattn_probe_read")
+    return scratch

@@ -248,6 +248,28 @@ int lazyattn_materialize_rotated(const void* k_pool, const void* v_pool,
   return LAZYATTN_OK;
 }
 
+int32_t lazyattn_probe_cus(void) { return decode_resident_waves() / 8; }
+
+int lazyattn_probe_mfma(int32_t iters, void* cycles_out, void* scratch_out, void* stream) {
+  if (!cycles_out || !scratch_out) return LAZYATTN_ERR_NULL;
+  if (!aligned(cycles_out, 8) || !aligned(scratch_out, 4)) return LAZYATTN_ERR_ALIGN;
+  if (iters <= 0) return LAZYATTN_ERR_ARG;
+  if (launch_probe_mfma(lazyattn_probe_cus(), iters, (unsigned long long*)cycles_out,
+                        (float*)scratch_out, (hipStream_t)stream) != hipSuccess)
+    return LAZYATTN_ERR_LAUNCH;
+  return LAZYATTN_OK;
+}
+
+int lazyattn_probe_read(const void* buf, size_t bytes, void* scratch_out, void* stream) {
+  if (!buf || !scratch_out) return LAZYATTN_ERR_NULL;
+  if (!aligned(buf, 16) || !aligned(scratch_out, 4)) return LAZYATTN_ERR_ALIGN;
+  if (bytes == 0 || bytes % 16) return LAZYATTN_ERR_SHAPE;
+  if (launch_probe_read(buf, bytes, 8 * lazyattn_probe_cus(), (uint32_t*)scratch_out,
+                        (hipStream_t)stream) != hipSuccess)
+    return LAZYATTN_ERR_LAUNCH;
+  return LAZYATTN_OK;
+}
+
 int lazyattn_debug_decode_meta(const uint32_t* words, const int32_t* block_table,
                                int32_t num_seqs, int32_t n_entries, int32_t B,
                                int32_t* ids_out, int32_t* offsets_out, void* stream) {

@@ -85,6 +85,11 @@ struct MaterializeParams {
 };
 hipError_t launch_materialize(const MaterializeParams& p, int D, int num_wg, hipStream_t st);
 
+hipError_t launch_probe_mfma(int num_cus, int iters, unsigned long long* cyc, float* out,
+                             hipStream_t st);
+hipError_t launch_probe_read(const void* buf, size_t bytes, int num_wg, uint32_t* out,
+                             hipStream_t st);
+
 // waves of the decode grid (all resident at once); decode items are dealt round-robin to them
 int decode_resident_waves();
 hipError_t launch_decode(const DecodeParams& p, int D, int G, bool rotate, hipStream_t st);

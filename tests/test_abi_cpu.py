@@ -23,7 +23,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     hdr = open(os.path.join(ROOT, "include", "lazyattn.h")).read()
-    declared = sorted(set(re.findall(r"^(?:int|size_t|const char\*)\s+(lazyattn_\w+)\(",
+    declared = sorted(set(re.findall(r"^(?:int|int32_t|size_t|const char\*)\s+(lazyattn_\w+)\(",
                                      hdr, flags=re.M)))
     assert declared == sorted(L.EXPORTED)
     raw = ctypes.CDLL(L.LIB_PATH)
