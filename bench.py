@@ -236,6 +236,35 @@ def pct(xs):
             "p90": float(np.percentile(xs, 90))}
 
 
+def measure_ingest(torch, L, wl, stream, reps, n_tokens=1 << 17):
+    """lazyattn_ingest_kv writing n_tokens new (K, V) rows of this workload's head shape into
+    distinct slots of a scratch pool, in a seeded random block order: bytes moved = read +
+    write of K and V."""
+    nb = n_tokens // wl.B
+    pool_k = torch.empty((nb, wl.Hkv, wl.B, wl.D), dtype=torch.bfloat16, device="cuda")
+    pool_v = torch.empty_like(pool_k)
+    kn = torch.randn((n_tokens, wl.Hkv, wl.D), device="cuda").to(torch.bfloat16)
+    vn = torch.randn_like(kn)
+    g = torch.Generator(device="cpu").manual_seed(5)
+    blocks = torch.randperm(nb, generator=g).to(torch.int32)
+    slots = (blocks[:, None] * wl.B + torch.arange(wl.B, dtype=torch.int32)[None, :]).reshape(-1)
+    slots = slots.cuda()
+    for _ in range(3):
+        L.ingest_kv(kn, vn, slots, pool_k, pool_v, stream=stream)
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps)]
+    for k in range(reps):
+        e[2 * k].record(stream)
+        L.ingest_kv(kn, vn, slots, pool_k, pool_v, stream=stream)
+        e[2 * k + 1].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.median([e[2 * k].elapsed_time(e[2 * k + 1]) for k in range(reps)]))
+    moved = 4.0 * n_tokens * wl.Hkv * wl.D * 2 + 4.0 * n_tokens
+    del pool_k, pool_v, kn, vn
+    return {"tokens": n_tokens, "ms": ms, "gbs": moved / (ms / 1e3) / 1e9,
+            "frac_hbm_peak": moved / (ms / 1e3) / 1e9 / PEAK_HBM_GBS,
+            "bytes": "read + write of K and V rows, plus the 4-byte slot of each token"}
+
+
 def measured_ceilings(torch, L, stream, reps=5):
     """What the chip sustains here: the MFMA loop's TFLOP/s and shader clock (s_memtime
     cycles over event time), and a plain 2 GiB stream read's GB/s (medians over reps)."""
@@ -454,6 +483,8 @@ def main():
                          "materialize_then_attend_ms": t_mat + t_base,
                          "lazy_speedup_vs_materialize": (t_mat + t_base) / t_lazy}
         line["rotation_ablation"] = abl
+    # ingest of new tokens' K/V into pool slots (separate scratch pool; not part of a step)
+    line["ingest"] = measure_ingest(torch, L, wl, stream, args.steps)
     # the same kernels' rates against what the chip sustains on plain probes
     ceil = measured_ceilings(torch, L, stream)
     line["measured_ceilings"] = ceil

@@ -51,6 +51,8 @@ extern "C" {
 #define LAZYATTN_ERR_WORKSPACE -5  /* workspace smaller than the matching *_workspace_bytes */
 #define LAZYATTN_ERR_LAUNCH    -6  /* a kernel launch failed (hipGetLastError after launch) */
 #define LAZYATTN_ERR_ARG       -7  /* other invalid scalar argument (rope_base, counts) */
+#define LAZYATTN_ERR_NOSPACE   -8  /* pool index: not enough free or evictable blocks */
+#define LAZYATTN_ERR_STATE     -9  /* pool index: unknown document, reference underflow, block not owned */
 
 /*
  * Packed block metadata word (one per block-table entry).
@@ -168,6 +170,58 @@ int lazyattn_materialize_rotated(const void* k_pool, const void* v_pool,
                                  int32_t n_entries, int32_t Hkv, int32_t D, int32_t B,
                                  int32_t num_blocks, void* dst_k, void* dst_v,
                                  uint32_t* dst_meta, void* stream);
+
+/*
+ * lazyattn_ingest_kv -- writes the keys and values of new tokens (a prefill suffix, a decode
+ * token, a document seen for the first time) into the position-free pool, keys exactly as
+ * projected, without rotation (technical summary, "Core Concept": the cache holds
+ * content-only keys; position is applied later inside the attention kernels).
+ *   k_new, v_new   bf16 [n_tokens, Hkv, D], contiguous, 16-byte aligned (device)
+ *   slot_mapping   int32 [n_tokens] (device): block_id * B + slot for each token; a negative
+ *                  value or a block_id >= num_blocks leaves that token unwritten
+ *   k_pool, v_pool bf16 [num_blocks, Hkv, B, D] (device), written in place
+ * Tokens must map to distinct slots (two tokens writing one slot race). D in {64, 128}, B = 16.
+ * Asynchronous on `stream`; errors: SHAPE, NULL, ALIGN, LAUNCH (n_tokens = 0 is a no-op).
+ */
+int lazyattn_ingest_kv(const void* k_new, const void* v_new, const int32_t* slot_mapping,
+                       int32_t n_tokens, int32_t Hkv, int32_t D, int32_t B, int32_t num_blocks,
+                       void* k_pool, void* v_pool, void* stream);
+
+/*
+ * Pool index (host only, no device memory): which physical blocks of the position-free pool
+ * hold which document. Technical summary, "Core Concept" / "Problem Statement": cached keys
+ * carry no position, so one physical copy serves every request containing the document at
+ * any offset; the index is keyed by document alone (a caller-chosen 64-bit key, e.g. a
+ * content hash). Documents used by no live request stay cached in LRU order and are
+ * evicted oldest first when an allocation needs room. The handle is internally locked;
+ * calls from several threads are serialised.
+ *   lazyattn_pool_create(num_blocks, B, &h) -- all blocks free; ids handed out from 0 up
+ *     at first. ARG if num_blocks not in 1 .. 2^17 or B <= 0.
+ *   lazyattn_pool_acquire(h, key, n_tokens, blocks_out, cap, &n, &hit) -- n =
+ *     ceil(n_tokens / B). Cached: the same block ids, hit = 1 (STATE if n_tokens differs
+ *     from the cached document's). Otherwise n blocks are taken (evicting as needed), hit =
+ *     0, and the caller writes the document's K/V into them (lazyattn_ingest_kv). Either
+ *     way the document gains one reference. ARG if cap < n (n is still returned); NOSPACE if
+ *     free plus evictable blocks are fewer than n (nothing is evicted then).
+ *   lazyattn_pool_release(h, key) -- drops one reference; at zero the document becomes
+ *     evictable (most recently used). STATE for an unknown key or no reference held.
+ *   lazyattn_pool_alloc_private / lazyattn_pool_free_private -- blocks owned by one request
+ *     (its question, suffix, decode tokens); freeing a block that is not a private block in
+ *     use gives STATE and frees nothing.
+ *   lazyattn_pool_stats -- counters and occupancy.
+ */
+typedef struct LazyattnPoolStats {
+  int64_t hits, misses, evictions, evicted_blocks;
+  int32_t num_blocks, free_blocks, cached_docs, pinned_docs, private_blocks, evictable_blocks;
+} LazyattnPoolStats;
+int lazyattn_pool_create(int32_t num_blocks, int32_t block_size, void** pool_out);
+int lazyattn_pool_destroy(void* pool);
+int lazyattn_pool_acquire(void* pool, uint64_t doc_key, int32_t n_tokens, int32_t* blocks_out,
+                          int32_t blocks_cap, int32_t* n_blocks_out, int32_t* hit_out);
+int lazyattn_pool_release(void* pool, uint64_t doc_key);
+int lazyattn_pool_alloc_private(void* pool, int32_t n_blocks, int32_t* blocks_out);
+int lazyattn_pool_free_private(void* pool, const int32_t* blocks, int32_t n_blocks);
+int lazyattn_pool_stats(void* pool, LazyattnPoolStats* out);
 
 /*
  * Measured ceilings (for reporting; not part of the attention path):

@@ -23,6 +23,8 @@ Modules
   meta       independent encoder/decoder of the packed (block id, offset) word.
   attention  materialise + attend; sampled-row variant for large batches.
   overhead   the rotation-FLOP accounting of the prefill tile (3/(4M)).
+  pool       ingest of new keys/values into pool slots; a plain model of the
+             document-keyed block index (LRU among unreferenced documents).
 
 Pins (tests marked "not gpu"): closed-form rotation identities and the complex
 (RoFormer) form of RoPE, a brute-force attention with explicit D x D rotation
@@ -32,6 +34,6 @@ translation and permutation invariance, bit patterns of the packed word, and
 the summary's printed 0.59% overhead at M = 128. No function here is
 "parity unpinned".
 """
-from . import rope, meta, attention, overhead  # noqa: F401
+from . import rope, meta, attention, overhead, pool  # noqa: F401
 from .attention import lazy_attention, attention_rows, bf16_bits_to_f64, rotated_pool  # noqa: F401
 from .meta import encode_meta, decode_meta  # noqa: F401

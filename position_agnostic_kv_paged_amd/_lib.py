@@ -6,18 +6,30 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblazyattn
 
 OK, ERR_NULL, ERR_ALIGN, ERR_SHAPE, ERR_RANGE, ERR_WORKSPACE, ERR_LAUNCH, ERR_ARG = \
     0, -1, -2, -3, -4, -5, -6, -7
+ERR_NOSPACE, ERR_STATE = -8, -9
 
 # every symbol include/lazyattn.h declares
 EXPORTED = [
     "lazyattn_prefill", "lazyattn_decode", "lazyattn_prefill_rotated_pool",
     "lazyattn_decode_rotated_pool", "lazyattn_materialize_rotated", "lazyattn_probe_cus",
-    "lazyattn_probe_mfma", "lazyattn_probe_read",
+    "lazyattn_probe_mfma", "lazyattn_probe_read", "lazyattn_ingest_kv", "lazyattn_pool_create",
+    "lazyattn_pool_destroy", "lazyattn_pool_acquire", "lazyattn_pool_release",
+    "lazyattn_pool_alloc_private", "lazyattn_pool_free_private", "lazyattn_pool_stats",
     "lazyattn_prefill_workspace_bytes",
     "lazyattn_decode_workspace_bytes", "lazyattn_encode_meta", "lazyattn_debug_decode_meta",
     "lazyattn_status_str", "lazyattn_version",
 ]
 
 _lib = None
+
+
+class PoolStats(ctypes.Structure):
+    """LazyattnPoolStats (include/lazyattn.h)."""
+    _fields_ = [("hits", ctypes.c_int64), ("misses", ctypes.c_int64),
+                ("evictions", ctypes.c_int64), ("evicted_blocks", ctypes.c_int64),
+                ("num_blocks", ctypes.c_int32), ("free_blocks", ctypes.c_int32),
+                ("cached_docs", ctypes.c_int32), ("pinned_docs", ctypes.c_int32),
+                ("private_blocks", ctypes.c_int32), ("evictable_blocks", ctypes.c_int32)]
 
 
 class LazyAttnError(RuntimeError):
@@ -51,6 +63,18 @@ def lib():
     L.lazyattn_probe_cus.argtypes, L.lazyattn_probe_cus.restype = [], i32
     L.lazyattn_probe_mfma.argtypes, L.lazyattn_probe_mfma.restype = [i32, vp, vp, vp], ctypes.c_int
     L.lazyattn_probe_read.argtypes, L.lazyattn_probe_read.restype = [vp, u64, vp, vp], ctypes.c_int
+    L.lazyattn_ingest_kv.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp]
+    L.lazyattn_ingest_kv.restype = ctypes.c_int
+    P32 = ctypes.POINTER(ctypes.c_int32)
+    for name, args in (("lazyattn_pool_create", [i32, i32, ctypes.POINTER(vp)]),
+                       ("lazyattn_pool_destroy", [vp]),
+                       ("lazyattn_pool_acquire", [vp, ctypes.c_uint64, i32, P32, i32, P32, P32]),
+                       ("lazyattn_pool_release", [vp, ctypes.c_uint64]),
+                       ("lazyattn_pool_alloc_private", [vp, i32, P32]),
+                       ("lazyattn_pool_free_private", [vp, P32, i32]),
+                       ("lazyattn_pool_stats", [vp, ctypes.POINTER(PoolStats)])):
+        f = getattr(L, name)
+        f.argtypes, f.restype = args, ctypes.c_int
     L.lazyattn_encode_meta.argtypes = [vp, vp, vp, i32, i32, vp, vp]
     L.lazyattn_encode_meta.restype = ctypes.c_int
     L.lazyattn_debug_decode_meta.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp]

@@ -8,7 +8,7 @@ import ctypes
 
 import numpy as np
 
-from ._lib import lib, check
+from ._lib import lib, check, PoolStats
 
 BLOCK = 16
 
@@ -163,3 +163,66 @@ def probe_read(buf, scratch=None, stream=None):
                                    _stream(stream))
     check(rc, "lazyattn_probe_read")
     return scratch
+
+
+def ingest_kv(k_new, v_new, slot_mapping, k_pool, v_pool, stream=None):
+    """lazyattn_ingest_kv: scatter new tokens' K/V (bf16 [n, Hkv, D], unrotated) into the pool
+    slots slot_mapping (int32 [n], block_id * B + slot; negative = skip)."""
+    n, Hkv, D = k_new.shape
+    num_blocks, _, B, _ = k_pool.shape
+    rc = lib().lazyattn_ingest_kv(_ptr(k_new), _ptr(v_new), _ptr(slot_mapping), n, Hkv, D, B,
+                                  num_blocks, _ptr(k_pool), _ptr(v_pool), _stream(stream))
+    check(rc, "lazyattn_ingest_kv")
+
+
+class PoolIndex:
+    """Host index of the position-free pool (lazyattn_pool_*): document key -> block ids,
+    references, LRU eviction of unreferenced documents, private blocks."""
+
+    def __init__(self, num_blocks, block_size=BLOCK):
+        self._h = ctypes.c_void_p()
+        check(lib().lazyattn_pool_create(int(num_blocks), int(block_size), ctypes.byref(self._h)),
+              "lazyattn_pool_create")
+        self.block_size = int(block_size)
+
+    def close(self):
+        if self._h:
+            lib().lazyattn_pool_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def acquire(self, key, n_tokens):
+        """-> (block ids int32 array, hit)."""
+        cap = (int(n_tokens) + self.block_size - 1) // self.block_size
+        buf = (ctypes.c_int32 * max(cap, 1))()
+        n, hit = ctypes.c_int32(), ctypes.c_int32()
+        check(lib().lazyattn_pool_acquire(self._h, ctypes.c_uint64(int(key)), int(n_tokens), buf,
+                                          cap, ctypes.byref(n), ctypes.byref(hit)),
+              "lazyattn_pool_acquire")
+        return np.frombuffer(buf, dtype=np.int32, count=n.value).copy(), bool(hit.value)
+
+    def release(self, key):
+        check(lib().lazyattn_pool_release(self._h, ctypes.c_uint64(int(key))),
+              "lazyattn_pool_release")
+
+    def alloc_private(self, n_blocks):
+        buf = (ctypes.c_int32 * max(int(n_blocks), 1))()
+        check(lib().lazyattn_pool_alloc_private(self._h, int(n_blocks), buf),
+              "lazyattn_pool_alloc_private")
+        return np.frombuffer(buf, dtype=np.int32, count=int(n_blocks)).copy()
+
+    def free_private(self, blocks):
+        b = np.ascontiguousarray(blocks, dtype=np.int32)
+        check(lib().lazyattn_pool_free_private(
+            self._h, b.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), len(b)),
+              "lazyattn_pool_free_private")
+
+    def stats(self):
+        st = PoolStats()
+        check(lib().lazyattn_pool_stats(self._h, ctypes.byref(st)), "lazyattn_pool_stats")
+        return {name: getattr(st, name) for name, _ in PoolStats._fields_}

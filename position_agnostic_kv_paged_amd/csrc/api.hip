@@ -248,6 +248,26 @@ int lazyattn_materialize_rotated(const void* k_pool, const void* v_pool,
   return LAZYATTN_OK;
 }
 
+int lazyattn_ingest_kv(const void* k_new, const void* v_new, const int32_t* slot_mapping,
+                       int32_t n_tokens, int32_t Hkv, int32_t D, int32_t B, int32_t num_blocks,
+                       void* k_pool, void* v_pool, void* stream) {
+  if (n_tokens < 0 || Hkv <= 0 || num_blocks <= 0) return LAZYATTN_ERR_SHAPE;
+  if ((D != 64 && D != 128) || B != kBlock) return LAZYATTN_ERR_SHAPE;
+  if (n_tokens == 0) return LAZYATTN_OK;
+  if (!k_new || !v_new || !slot_mapping || !k_pool || !v_pool) return LAZYATTN_ERR_NULL;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_pool, 16) ||
+      !aligned(v_pool, 16) || !aligned(slot_mapping, 4))
+    return LAZYATTN_ERR_ALIGN;
+  IngestParams p{(const uint16_t*)k_new, (const uint16_t*)v_new, slot_mapping,
+                 (uint16_t*)k_pool, (uint16_t*)v_pool, n_tokens, Hkv, D, B, num_blocks};
+  const long long chunks = (long long)n_tokens * Hkv * (D / 8);
+  const long long want = (chunks + 255) / 256;
+  const int cap = 8 * (decode_resident_waves() / 8) * 4;      // 4 x (8 workgroups per CU)
+  const int num_wg = (int)(want < cap ? want : cap);
+  if (launch_ingest(p, num_wg, (hipStream_t)stream) != hipSuccess) return LAZYATTN_ERR_LAUNCH;
+  return LAZYATTN_OK;
+}
+
 int32_t lazyattn_probe_cus(void) { return decode_resident_waves() / 8; }
 
 int lazyattn_probe_mfma(int32_t iters, void* cycles_out, void* scratch_out, void* stream) {
@@ -291,6 +311,8 @@ const char* lazyattn_status_str(int status) {
     case LAZYATTN_ERR_WORKSPACE: return "workspace too small";
     case LAZYATTN_ERR_LAUNCH: return "kernel launch failed";
     case LAZYATTN_ERR_ARG: return "invalid scalar argument";
+    case LAZYATTN_ERR_NOSPACE: return "pool index: not enough free or evictable blocks";
+    case LAZYATTN_ERR_STATE: return "pool index: unknown document, reference underflow or block not owned";
   }
   return "unknown status";
 }

@@ -85,6 +85,16 @@ struct MaterializeParams {
 };
 hipError_t launch_materialize(const MaterializeParams& p, int D, int num_wg, hipStream_t st);
 
+struct IngestParams {
+  const uint16_t* k_new;     // [n_tokens][Hkv][D] bf16, as projected (no rotation)
+  const uint16_t* v_new;
+  const int32_t* slot_mapping;   // [n_tokens] block_id * B + slot, or -1
+  uint16_t* k_pool;          // [num_blocks][Hkv][B][D]
+  uint16_t* v_pool;
+  int n_tokens, Hkv, D, B, num_blocks;
+};
+hipError_t launch_ingest(const IngestParams& p, int num_wg, hipStream_t st);
+
 hipError_t launch_probe_mfma(int num_cus, int iters, unsigned long long* cyc, float* out,
                              hipStream_t st);
 hipError_t launch_probe_read(const void* buf, size_t bytes, int num_wg, uint32_t* out,
