@@ -148,6 +148,31 @@ int lazyattn_decode_rotated_pool(const void* q, const void* k_pool, const void* 
                                  size_t workspace_bytes, void* stream);
 
 /*
+ * lazyattn_prefill_freqs / lazyattn_decode_freqs -- the same calls with the RoPE frequency of
+ * every rotate-half pair given instead of derived from a base: inv_freq is a HOST array of
+ * D/2 doubles, theta_k in radians per position for the pair (k, k + D/2), each finite and
+ * >= 0 (0 leaves that pair unrotated). Covers frequency-scaled RoPE variants (technical
+ * summary, "Key Contributions": compatibility with RoPE variants), e.g. Llama-3.1's scaled
+ * table, position interpolation (theta_k / s), other bases. Read during the call only; the
+ * device work is the same. Errors as lazyattn_prefill / lazyattn_decode (NULL if inv_freq
+ * is NULL, ARG for a negative or non-finite entry).
+ */
+int lazyattn_prefill_freqs(const void* q, const void* k_pool, const void* v_pool,
+                           const int32_t* block_table, const uint32_t* block_meta,
+                           const int32_t* kv_lens, const int32_t* q_indptr,
+                           const int32_t* q_positions, const double* inv_freq,
+                           int32_t num_seqs, int32_t total_q, int32_t Hq, int32_t Hkv,
+                           int32_t D, int32_t B, int32_t num_blocks, int32_t max_entries,
+                           void* out, void* workspace, size_t workspace_bytes, void* stream);
+int lazyattn_decode_freqs(const void* q, const void* k_pool, const void* v_pool,
+                          const int32_t* block_table, const uint32_t* block_meta,
+                          const int32_t* kv_lens, const int32_t* q_indptr,
+                          const int32_t* q_positions, const double* inv_freq,
+                          int32_t num_seqs, int32_t total_q, int32_t Hq, int32_t Hkv,
+                          int32_t D, int32_t B, int32_t num_blocks, int32_t max_entries,
+                          void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * lazyattn_materialize_rotated -- the position-adjusted copy the method avoids (technical
  * summary: "Mathematical Equivalence"; reuse schemes that store rotated copies), for
  * measurement. For every block-table entry e (flat index, e < min(n_entries,

@@ -12,16 +12,44 @@ Equivalently, z_k = x_k + i x_{k+D/2} is multiplied by exp(i n theta_k).
 import numpy as np
 
 
-def inv_freq(D: int, base: float) -> np.ndarray:
-    """theta_k = base^(-2k/D) for k = 0 .. D/2-1, float64."""
+def inv_freq(D: int, base) -> np.ndarray:
+    """theta_k = base^(-2k/D) for k = 0 .. D/2-1, float64. `base` may instead be the table
+    theta_k itself (D/2 values): a frequency-scaled RoPE variant given explicitly."""
     if D % 2:
         raise ValueError("head dim must be even")
+    if np.ndim(base) == 1:
+        t = np.asarray(base, dtype=np.float64)
+        if t.shape != (D // 2,):
+            raise ValueError("frequency table must hold D/2 values")
+        return t
     k = np.arange(D // 2, dtype=np.float64)
     return np.power(np.float64(base), -2.0 * k / D)
 
 
-def rotate(x: np.ndarray, pos, base: float) -> np.ndarray:
-    """Apply R(pos) to the last axis of x (float64).
+def llama31_scale(theta, factor=8.0, low_freq_factor=1.0, high_freq_factor=4.0,
+                  original_context=8192):
+    """Frequency scaling of the Llama 3.1 models, applied to each theta separately.
+
+    With wavelength w = 2 pi / theta: w below original_context / high_freq_factor keeps
+    theta; w above original_context / low_freq_factor gives theta / factor; in between,
+    with r = original_context / w, the weight s = (r - low) / (high - low) mixes the two:
+    (1 - s) theta / factor + s theta.
+    """
+    out = []
+    for t in np.asarray(theta, dtype=np.float64):
+        w = 2.0 * np.pi / t
+        if w < original_context / high_freq_factor:
+            out.append(t)
+        elif w > original_context / low_freq_factor:
+            out.append(t / factor)
+        else:
+            s = (original_context / w - low_freq_factor) / (high_freq_factor - low_freq_factor)
+            out.append((1.0 - s) * t / factor + s * t)
+    return np.array(out)
+
+
+def rotate(x: np.ndarray, pos, base) -> np.ndarray:
+    """Apply R(pos) to the last axis of x (float64); base: a RoPE base or the theta table.
 
     x: [..., D]; pos: integer array broadcastable to x.shape[:-1].
     y_k        = x_k cos(pos theta_k) - x_{k+D/2} sin(pos theta_k)

@@ -11,7 +11,8 @@ ERR_NOSPACE, ERR_STATE = -8, -9
 # every symbol include/lazyattn.h declares
 EXPORTED = [
     "lazyattn_prefill", "lazyattn_decode", "lazyattn_prefill_rotated_pool",
-    "lazyattn_decode_rotated_pool", "lazyattn_materialize_rotated", "lazyattn_probe_cus",
+    "lazyattn_decode_rotated_pool", "lazyattn_prefill_freqs", "lazyattn_decode_freqs",
+    "lazyattn_materialize_rotated", "lazyattn_probe_cus",
     "lazyattn_probe_mfma", "lazyattn_probe_read", "lazyattn_ingest_kv", "lazyattn_pool_create",
     "lazyattn_pool_destroy", "lazyattn_pool_acquire", "lazyattn_pool_release",
     "lazyattn_pool_alloc_private", "lazyattn_pool_free_private", "lazyattn_pool_stats",
@@ -54,6 +55,9 @@ def lib():
                  "lazyattn_decode_rotated_pool"):
         f = getattr(L, name)
         f.argtypes, f.restype = attn, ctypes.c_int
+    for name in ("lazyattn_prefill_freqs", "lazyattn_decode_freqs"):
+        f = getattr(L, name)
+        f.argtypes, f.restype = attn[:8] + [vp] + attn[9:], ctypes.c_int
     for name in ("lazyattn_prefill_workspace_bytes", "lazyattn_decode_workspace_bytes"):
         f = getattr(L, name)
         f.argtypes, f.restype = [i32] * 6, ctypes.c_size_t

@@ -39,7 +39,7 @@ def workspace_bytes(kind, num_seqs, total_q, max_entries, Hq, Hkv, D):
 
 def _attention(kind, q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indptr, q_pos,
                rope_base, max_entries, out=None, workspace=None, stream=None,
-               rotated_pool=False):
+               rotated_pool=False, inv_freq=None):
     import torch
     total_q, Hq, D, num_blocks, Hkv, B = _dims(q, k_pool)
     num_seqs = kv_lens.numel()
@@ -48,10 +48,19 @@ def _attention(kind, q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indp
     need = workspace_bytes(kind, num_seqs, total_q, max_entries, Hq, Hkv, D)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    name = "lazyattn_" + kind + ("_rotated_pool" if rotated_pool else "")
+    if inv_freq is not None:
+        if rotated_pool:
+            raise ValueError("a frequency table applies to the position-free pool only")
+        fr = np.ascontiguousarray(inv_freq, dtype=np.float64)
+        if fr.shape != (D // 2,):
+            raise ValueError(f"inv_freq must hold D/2 = {D // 2} frequencies")
+        name, pe = "lazyattn_" + kind + "_freqs", ctypes.c_void_p(fr.ctypes.data)
+    else:
+        name = "lazyattn_" + kind + ("_rotated_pool" if rotated_pool else "")
+        pe = float(rope_base)
     fn = getattr(lib(), name)
     rc = fn(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(block_meta),
-            _ptr(kv_lens), _ptr(q_indptr), _ptr(q_pos), float(rope_base), num_seqs, total_q,
+            _ptr(kv_lens), _ptr(q_indptr), _ptr(q_pos), pe, num_seqs, total_q,
             Hq, Hkv, D, B, num_blocks, int(max_entries), _ptr(out), _ptr(workspace),
             workspace.numel() * workspace.element_size(), _stream(stream))
     check(rc, name)
@@ -59,17 +68,34 @@ def _attention(kind, q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indp
 
 
 def prefill(q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indptr, q_pos, rope_base,
-            max_entries, out=None, workspace=None, stream=None):
-    """lazyattn_prefill on torch tensors (all on one HIP device); returns out."""
+            max_entries, out=None, workspace=None, stream=None, inv_freq=None):
+    """lazyattn_prefill on torch tensors (all on one HIP device); returns out. With inv_freq
+    (D/2 radians per position), lazyattn_prefill_freqs and rope_base is not used."""
     return _attention("prefill", q, k_pool, v_pool, block_table, block_meta, kv_lens,
-                      q_indptr, q_pos, rope_base, max_entries, out, workspace, stream)
+                      q_indptr, q_pos, rope_base, max_entries, out, workspace, stream,
+                      inv_freq=inv_freq)
 
 
 def decode(q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indptr, q_pos, rope_base,
-           max_entries, out=None, workspace=None, stream=None):
-    """lazyattn_decode on torch tensors; returns out."""
+           max_entries, out=None, workspace=None, stream=None, inv_freq=None):
+    """lazyattn_decode on torch tensors; returns out (inv_freq as for prefill)."""
     return _attention("decode", q, k_pool, v_pool, block_table, block_meta, kv_lens,
-                      q_indptr, q_pos, rope_base, max_entries, out, workspace, stream)
+                      q_indptr, q_pos, rope_base, max_entries, out, workspace, stream,
+                      inv_freq=inv_freq)
+
+
+def llama31_inv_freq(D, base=500000.0, factor=8.0, low_freq_factor=1.0, high_freq_factor=4.0,
+                     original_context=8192):
+    """Frequency-scaled RoPE table of the Llama 3.1 models (host, float64, D/2 entries):
+    pairs whose wavelength 2 pi / theta is shorter than original_context / high_freq_factor
+    keep theta, those longer than original_context / low_freq_factor use theta / factor, and
+    in between theta is interpolated linearly in original_context / wavelength."""
+    theta = np.power(float(base), -np.arange(0, D, 2, dtype=np.float64) / D)
+    wavelen = 2.0 * np.pi / theta
+    smooth = (original_context / wavelen - low_freq_factor) / (high_freq_factor - low_freq_factor)
+    mid = (1.0 - smooth) * theta / factor + smooth * theta
+    out = np.where(wavelen < original_context / high_freq_factor, theta, mid)
+    return np.where(wavelen > original_context / low_freq_factor, theta / factor, out)
 
 
 def prefill_rotated_pool(q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indptr, q_pos,

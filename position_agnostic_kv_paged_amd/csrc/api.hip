@@ -65,14 +65,20 @@ int run(const void* q, const void* k_pool, const void* v_pool, const int32_t* bl
         const int32_t* q_positions, double rope_base, int32_t num_seqs, int32_t total_q,
         int32_t Hq, int32_t Hkv, int32_t D, int32_t B, int32_t num_blocks,
         int32_t max_entries, void* out, void* workspace, size_t workspace_bytes,
-        void* stream, int mode, bool rotate) {
+        void* stream, int mode, bool rotate, const double* inv_freq = nullptr) {
   if (!q || !k_pool || !v_pool || !block_table || !block_meta || !kv_lens || !q_indptr ||
       !q_positions || !out || !workspace)
     return LAZYATTN_ERR_NULL;
   if (num_seqs < 0 || total_q < 0 || num_blocks < 0 || max_entries < 0 ||
       num_blocks > (1 << kIdBits) || !shape_ok(Hq, Hkv, D, B))
     return LAZYATTN_ERR_SHAPE;
-  if (!(rope_base > 1.0) || !std::isfinite(rope_base)) return LAZYATTN_ERR_ARG;
+  if (inv_freq) {
+    if (!shape_ok(Hq, Hkv, D, B)) return LAZYATTN_ERR_SHAPE;
+    for (int k = 0; k < D / 2; ++k)
+      if (!(inv_freq[k] >= 0.0) || !std::isfinite(inv_freq[k])) return LAZYATTN_ERR_ARG;
+  } else if (!(rope_base > 1.0) || !std::isfinite(rope_base)) {
+    return LAZYATTN_ERR_ARG;
+  }
   if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(out, 16) ||
       !aligned(workspace, 16) || !aligned(block_table, 4) || !aligned(block_meta, 4) ||
       !aligned(kv_lens, 4) || !aligned(q_indptr, 4) || !aligned(q_positions, 4))
@@ -95,7 +101,7 @@ int run(const void* q, const void* k_pool, const void* v_pool, const int32_t* bl
 
   RopeFreqs fr{};
   for (int k = 0; k < D / 2; ++k)
-    fr.f[k] = std::pow(rope_base, -2.0 * k / D) / (2.0 * M_PI);
+    fr.f[k] = (inv_freq ? inv_freq[k] : std::pow(rope_base, -2.0 * k / D)) / (2.0 * M_PI);
   const float scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
 
   PlanParams pp{q_indptr, block_table, freqs, pf_prefix, dec_prefix, zero, num_seqs,
@@ -175,6 +181,32 @@ int lazyattn_decode_rotated_pool(const void* q, const void* k_pool, const void* 
   return run(q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indptr, q_positions,
              rope_base, num_seqs, total_q, Hq, Hkv, D, B, num_blocks, max_entries, out,
              workspace, workspace_bytes, stream, kPlanDecodeOnly, false);
+}
+
+int lazyattn_prefill_freqs(const void* q, const void* k_pool, const void* v_pool,
+                           const int32_t* block_table, const uint32_t* block_meta,
+                           const int32_t* kv_lens, const int32_t* q_indptr,
+                           const int32_t* q_positions, const double* inv_freq,
+                           int32_t num_seqs, int32_t total_q, int32_t Hq, int32_t Hkv,
+                           int32_t D, int32_t B, int32_t num_blocks, int32_t max_entries,
+                           void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!inv_freq) return LAZYATTN_ERR_NULL;
+  return run(q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indptr, q_positions, 0.0,
+             num_seqs, total_q, Hq, Hkv, D, B, num_blocks, max_entries, out, workspace,
+             workspace_bytes, stream, kPlanMixed, true, inv_freq);
+}
+
+int lazyattn_decode_freqs(const void* q, const void* k_pool, const void* v_pool,
+                          const int32_t* block_table, const uint32_t* block_meta,
+                          const int32_t* kv_lens, const int32_t* q_indptr,
+                          const int32_t* q_positions, const double* inv_freq,
+                          int32_t num_seqs, int32_t total_q, int32_t Hq, int32_t Hkv,
+                          int32_t D, int32_t B, int32_t num_blocks, int32_t max_entries,
+                          void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!inv_freq) return LAZYATTN_ERR_NULL;
+  return run(q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indptr, q_positions, 0.0,
+             num_seqs, total_q, Hq, Hkv, D, B, num_blocks, max_entries, out, workspace,
+             workspace_bytes, stream, kPlanDecodeOnly, true, inv_freq);
 }
 
 size_t lazyattn_prefill_workspace_bytes(int32_t num_seqs, int32_t total_q, int32_t max_entries,

@@ -285,3 +285,52 @@ def test_rotation_overhead_printed_value():
     # rotating twice (reset to zero, then to the target) would not match the printed figure
     twice = 100.0 * overhead.rotation_overhead(g["M"], rotations_per_key=2)
     assert round(twice, 2) != g["overhead_percent_printed"]
+
+
+# ------------------------------------------------------------------ RoPE frequency tables
+
+def test_frequency_table_equals_base_form():
+    """Passing the table theta_k = base^(-2k/D) explicitly gives the same rotation."""
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal((5, 64))
+    pos = np.array([0, 1, 77, 4000, 40000])
+    assert np.array_equal(rope.rotate(x, pos, rope.inv_freq(64, 10000.0)),
+                          rope.rotate(x, pos, 10000.0))
+
+
+def test_zero_frequency_pairs_are_unrotated():
+    theta = rope.inv_freq(32, 10000.0).copy()
+    theta[::2] = 0.0
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((3, 32))
+    y = rope.rotate(x, np.array([5, 900, 31000]), theta)
+    k = np.arange(0, 16, 2)
+    assert np.array_equal(y[:, k], x[:, k]) and np.array_equal(y[:, k + 16], x[:, k + 16])
+    assert not np.allclose(y[:, k + 1], x[:, k + 1])
+
+
+def test_llama31_scaling_bands_and_continuity():
+    """High frequencies (wavelength < 8192/4) unchanged, low (> 8192/1) divided by 8, the
+    band between interpolated continuously; the 128-dim, base 500000 table has all three."""
+    t_hi = 2 * np.pi / np.array([2047.0, 100.0, 2 * np.pi])      # w < 2048
+    t_lo = 2 * np.pi / np.array([8193.0, 1e5, 3e6])              # w > 8192
+    assert np.array_equal(rope.llama31_scale(t_hi), t_hi)
+    assert np.array_equal(rope.llama31_scale(t_lo), t_lo / 8)
+    for w in (2048.0, 8192.0):                                  # band edges: continuous
+        t = 2 * np.pi / np.array([w * (1 - 1e-12), w, w * (1 + 1e-12)])
+        v = rope.llama31_scale(t)
+        assert np.allclose(v, v[1], rtol=1e-9)
+    mid = 2 * np.pi / 4096.0                                    # r = 2: s = 1/3
+    assert np.isclose(rope.llama31_scale([mid])[0], (2 / 3) * mid / 8 + (1 / 3) * mid, rtol=1e-15)
+    th = rope.inv_freq(128, 500000.0)
+    sc = rope.llama31_scale(th)
+    w = 2 * np.pi / th
+    assert (sc == th)[w < 2048].all() and (sc == th / 8)[w > 8192].all()
+    assert ((w >= 2048) & (w <= 8192)).any() and (np.diff(sc) < 0).all()
+
+
+def test_package_llama31_table_equals_oracle():
+    from position_agnostic_kv_paged_amd.api import llama31_inv_freq
+    for D in (64, 128):
+        want = rope.llama31_scale(rope.inv_freq(D, 500000.0))
+        assert np.allclose(llama31_inv_freq(D), want, rtol=1e-15, atol=0)

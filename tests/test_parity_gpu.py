@@ -106,6 +106,28 @@ def test_mini_cases(name, kw, kind):
     compare(run_hip(wl, kind), oracle_out(wl), f"{name}/{kind}")
 
 
+def _freq_tables(D):
+    import position_agnostic_kv_paged_amd as L
+    half_zero = oracle.rope.inv_freq(D, 10000.0).copy()
+    half_zero[::2] = 0.0                                 # every other pair unrotated
+    interp = oracle.rope.inv_freq(D, 10000.0) / 4.0      # position interpolation by 4
+    return {"llama31": L.llama31_inv_freq(D), "half-zero": half_zero, "interp4": interp}
+
+
+@pytest.mark.parametrize("kind", ["prefill", "decode"])
+@pytest.mark.parametrize("table", ["llama31", "half-zero", "interp4"])
+@pytest.mark.parametrize("name", ["gaps-D128-G4", "gaps-D64-G2", "positions-above-2^15",
+                                  "many-tiles-ragged"])
+def test_frequency_tables(name, table, kind):
+    """lazyattn_*_freqs with frequency-scaled RoPE tables against the oracle with the same
+    table (Llama 3.1 scaling at base 500000, zero-frequency pairs, position interpolation)."""
+    kw = dict(_mini_cases())[name]
+    wl = small(**kw)
+    th = _freq_tables(wl.D)[table]
+    say(f"frequency table {table} on {name} via {kind}")
+    compare(run_hip(wl, kind, inv_freq=th), oracle_out(wl, base=th), f"{name}/{table}/{kind}")
+
+
 @pytest.mark.parametrize("kind", ["prefill", "decode"])
 def test_sequences_without_entries(kind):
     """Sequences with no block-table entries (first, middle and last of the batch) give 0

@@ -4,13 +4,14 @@ import numpy as np
 from workload import RequestLayout, Segment, build
 
 
-def oracle_out(wl, rows=None, seq=None):
+def oracle_out(wl, rows=None, seq=None, base=None):
+    """The oracle on a workload; `base` overrides its RoPE base (a number or a table)."""
     import oracle
     if rows is None:
         return oracle.lazy_attention(wl.q_bits, wl.k_bits, wl.v_bits,
                                      [wl.compact_ids(s) for s in range(wl.num_seqs)],
                                      wl.seq_offsets, wl.kv_lens, wl.q_indptr, wl.q_pos,
-                                     wl.rope_base, wl.B)
+                                     wl.rope_base if base is None else base, wl.B)
     return oracle.attention_rows(wl.q_bits, wl.k_bits, wl.v_bits,
                                  [wl.compact_ids(s) if s == seq else None
                                   for s in range(wl.num_seqs)],
