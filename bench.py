@@ -156,8 +156,8 @@ def record_traffic(fetch_dir, write_dir):
                         ("decode_kernel", "lazyattn::decode_kernel<")):
         # launches of the half under test: a prefill call also launches the decode kernel
         # (for its single-row sequences, none here), which then finds no work
-        # the lazy (rotating) instantiation only; the materialised baseline's is `false`
-        keys = [k for k in f if tag in k[1] and ", true>(" in k[1] and k in w]
+        # the lazy (RoPE, mode 0) instantiation only; the materialised baseline's is mode 1
+        keys = [k for k in f if tag in k[1] and ", 0>(" in k[1] and k in w]
         if not keys:
             continue
         top = max(f[k] for k in keys)

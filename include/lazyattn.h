@@ -173,6 +173,34 @@ int lazyattn_decode_freqs(const void* q, const void* k_pool, const void* v_pool,
                           void* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * lazyattn_prefill_alibi / lazyattn_decode_alibi -- the same calls over the same
+ * position-free pool with ALiBi instead of RoPE (technical summary, "Key Contributions":
+ * compatibility with ALiBi). Nothing is rotated; a query of head h at logical position p
+ * scores key slot j of entry t (logical position L = off_t + j from the packed word) as
+ *   q . k / sqrt(D) - slopes[h] * (p - L),
+ * with the same causal rule (L <= p), softmax and output. slopes: DEVICE float32 [Hq],
+ * caller-owned (e.g. Press et al.'s 2^(-8 i / H)). The bias is computed in fp32 (prefill
+ * carries slope * log2(e) for the part within a block, at most 15 slots, as the sum of two
+ * fp16 values on the matrix cores). Errors as lazyattn_prefill /
+ * lazyattn_decode (NULL if slopes is NULL, ALIGN if it is not 4-byte aligned); rope_base is
+ * not an argument.
+ */
+int lazyattn_prefill_alibi(const void* q, const void* k_pool, const void* v_pool,
+                           const int32_t* block_table, const uint32_t* block_meta,
+                           const int32_t* kv_lens, const int32_t* q_indptr,
+                           const int32_t* q_positions, const float* slopes,
+                           int32_t num_seqs, int32_t total_q, int32_t Hq, int32_t Hkv,
+                           int32_t D, int32_t B, int32_t num_blocks, int32_t max_entries,
+                           void* out, void* workspace, size_t workspace_bytes, void* stream);
+int lazyattn_decode_alibi(const void* q, const void* k_pool, const void* v_pool,
+                          const int32_t* block_table, const uint32_t* block_meta,
+                          const int32_t* kv_lens, const int32_t* q_indptr,
+                          const int32_t* q_positions, const float* slopes,
+                          int32_t num_seqs, int32_t total_q, int32_t Hq, int32_t Hkv,
+                          int32_t D, int32_t B, int32_t num_blocks, int32_t max_entries,
+                          void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * lazyattn_materialize_rotated -- the position-adjusted copy the method avoids (technical
  * summary: "Mathematical Equivalence"; reuse schemes that store rotated copies), for
  * measurement. For every block-table entry e (flat index, e < min(n_entries,

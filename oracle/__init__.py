@@ -25,6 +25,7 @@ Modules
   overhead   the rotation-FLOP accounting of the prefill tile (3/(4M)).
   pool       ingest of new keys/values into pool slots; a plain model of the
              document-keyed block index (LRU among unreferenced documents).
+  alibi      ALiBi (linear bias on logical distances, no rotation) over the same pool.
 
 Pins (tests marked "not gpu"): closed-form rotation identities and the complex
 (RoFormer) form of RoPE, a brute-force attention with explicit D x D rotation
@@ -34,6 +35,6 @@ translation and permutation invariance, bit patterns of the packed word, and
 the summary's printed 0.59% overhead at M = 128. No function here is
 "parity unpinned".
 """
-from . import rope, meta, attention, overhead, pool  # noqa: F401
+from . import rope, meta, attention, overhead, pool, alibi  # noqa: F401
 from .attention import lazy_attention, attention_rows, bf16_bits_to_f64, rotated_pool  # noqa: F401
 from .meta import encode_meta, decode_meta  # noqa: F401

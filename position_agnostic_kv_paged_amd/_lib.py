@@ -12,6 +12,7 @@ ERR_NOSPACE, ERR_STATE = -8, -9
 EXPORTED = [
     "lazyattn_prefill", "lazyattn_decode", "lazyattn_prefill_rotated_pool",
     "lazyattn_decode_rotated_pool", "lazyattn_prefill_freqs", "lazyattn_decode_freqs",
+    "lazyattn_prefill_alibi", "lazyattn_decode_alibi",
     "lazyattn_materialize_rotated", "lazyattn_probe_cus",
     "lazyattn_probe_mfma", "lazyattn_probe_read", "lazyattn_ingest_kv", "lazyattn_pool_create",
     "lazyattn_pool_destroy", "lazyattn_pool_acquire", "lazyattn_pool_release",
@@ -55,7 +56,8 @@ def lib():
                  "lazyattn_decode_rotated_pool"):
         f = getattr(L, name)
         f.argtypes, f.restype = attn, ctypes.c_int
-    for name in ("lazyattn_prefill_freqs", "lazyattn_decode_freqs"):
+    for name in ("lazyattn_prefill_freqs", "lazyattn_decode_freqs", "lazyattn_prefill_alibi",
+                 "lazyattn_decode_alibi"):
         f = getattr(L, name)
         f.argtypes, f.restype = attn[:8] + [vp] + attn[9:], ctypes.c_int
     for name in ("lazyattn_prefill_workspace_bytes", "lazyattn_decode_workspace_bytes"):

@@ -39,7 +39,7 @@ def workspace_bytes(kind, num_seqs, total_q, max_entries, Hq, Hkv, D):
 
 def _attention(kind, q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indptr, q_pos,
                rope_base, max_entries, out=None, workspace=None, stream=None,
-               rotated_pool=False, inv_freq=None):
+               rotated_pool=False, inv_freq=None, slopes=None):
     import torch
     total_q, Hq, D, num_blocks, Hkv, B = _dims(q, k_pool)
     num_seqs = kv_lens.numel()
@@ -48,7 +48,13 @@ def _attention(kind, q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indp
     need = workspace_bytes(kind, num_seqs, total_q, max_entries, Hq, Hkv, D)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    if inv_freq is not None:
+    if slopes is not None:
+        if rotated_pool or inv_freq is not None:
+            raise ValueError("ALiBi slopes exclude RoPE options")
+        if slopes.dtype != torch.float32 or slopes.numel() != Hq or not slopes.is_contiguous():
+            raise ValueError(f"slopes must be a contiguous float32 device tensor of Hq = {Hq}")
+        name, pe = "lazyattn_" + kind + "_alibi", _ptr(slopes)
+    elif inv_freq is not None:
         if rotated_pool:
             raise ValueError("a frequency table applies to the position-free pool only")
         fr = np.ascontiguousarray(inv_freq, dtype=np.float64)
@@ -68,20 +74,21 @@ def _attention(kind, q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indp
 
 
 def prefill(q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indptr, q_pos, rope_base,
-            max_entries, out=None, workspace=None, stream=None, inv_freq=None):
+            max_entries, out=None, workspace=None, stream=None, inv_freq=None, slopes=None):
     """lazyattn_prefill on torch tensors (all on one HIP device); returns out. With inv_freq
-    (D/2 radians per position), lazyattn_prefill_freqs and rope_base is not used."""
+    (D/2 radians per position), lazyattn_prefill_freqs; with slopes (float32 device [Hq]),
+    lazyattn_prefill_alibi; rope_base is then not used."""
     return _attention("prefill", q, k_pool, v_pool, block_table, block_meta, kv_lens,
                       q_indptr, q_pos, rope_base, max_entries, out, workspace, stream,
-                      inv_freq=inv_freq)
+                      inv_freq=inv_freq, slopes=slopes)
 
 
 def decode(q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indptr, q_pos, rope_base,
-           max_entries, out=None, workspace=None, stream=None, inv_freq=None):
-    """lazyattn_decode on torch tensors; returns out (inv_freq as for prefill)."""
+           max_entries, out=None, workspace=None, stream=None, inv_freq=None, slopes=None):
+    """lazyattn_decode on torch tensors; returns out (inv_freq, slopes as for prefill)."""
     return _attention("decode", q, k_pool, v_pool, block_table, block_meta, kv_lens,
                       q_indptr, q_pos, rope_base, max_entries, out, workspace, stream,
-                      inv_freq=inv_freq)
+                      inv_freq=inv_freq, slopes=slopes)
 
 
 def llama31_inv_freq(D, base=500000.0, factor=8.0, low_freq_factor=1.0, high_freq_factor=4.0,

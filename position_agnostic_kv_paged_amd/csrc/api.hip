@@ -65,14 +65,18 @@ int run(const void* q, const void* k_pool, const void* v_pool, const int32_t* bl
         const int32_t* q_positions, double rope_base, int32_t num_seqs, int32_t total_q,
         int32_t Hq, int32_t Hkv, int32_t D, int32_t B, int32_t num_blocks,
         int32_t max_entries, void* out, void* workspace, size_t workspace_bytes,
-        void* stream, int mode, bool rotate, const double* inv_freq = nullptr) {
+        void* stream, int mode, int pe, const double* inv_freq = nullptr,
+        const float* slopes = nullptr) {
   if (!q || !k_pool || !v_pool || !block_table || !block_meta || !kv_lens || !q_indptr ||
       !q_positions || !out || !workspace)
     return LAZYATTN_ERR_NULL;
   if (num_seqs < 0 || total_q < 0 || num_blocks < 0 || max_entries < 0 ||
       num_blocks > (1 << kIdBits) || !shape_ok(Hq, Hkv, D, B))
     return LAZYATTN_ERR_SHAPE;
-  if (inv_freq) {
+  if (pe == kAlibi) {
+    if (!slopes) return LAZYATTN_ERR_NULL;
+    if (!aligned(slopes, 4)) return LAZYATTN_ERR_ALIGN;
+  } else if (inv_freq) {
     if (!shape_ok(Hq, Hkv, D, B)) return LAZYATTN_ERR_SHAPE;
     for (int k = 0; k < D / 2; ++k)
       if (!(inv_freq[k] >= 0.0) || !std::isfinite(inv_freq[k])) return LAZYATTN_ERR_ARG;
@@ -99,8 +103,8 @@ int run(const void* q, const void* k_pool, const void* v_pool, const int32_t* bl
   int32_t* dec_prefix = (int32_t*)(ws + L.off_dec_prefix);
   float* partials = (float*)(ws + L.off_partials);
 
-  RopeFreqs fr{};
-  for (int k = 0; k < D / 2; ++k)
+  RopeFreqs fr{};                                   // (unused with ALiBi: all zero)
+  for (int k = 0; pe != kAlibi && k < D / 2; ++k)
     fr.f[k] = (inv_freq ? inv_freq[k] : std::pow(rope_base, -2.0 * k / D)) / (2.0 * M_PI);
   const float scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
 
@@ -115,14 +119,14 @@ int run(const void* q, const void* k_pool, const void* v_pool, const int32_t* bl
     PrefillParams P{(const uint16_t*)q, (const uint16_t*)k_pool, (const uint16_t*)v_pool,
                     block_table, block_meta, kv_lens, q_indptr, q_positions,
                     (uint16_t*)out, pf_prefix, (const uint16_t*)zero, num_seqs, Hq, Hkv,
-                    num_blocks, (int)tiles, scale_log2, freqs};
-    if (launch_prefill(P, D, G, rotate, st) != hipSuccess) return LAZYATTN_ERR_LAUNCH;
+                    num_blocks, (int)tiles, scale_log2, freqs, slopes};
+    if (launch_prefill(P, D, G, pe, st) != hipSuccess) return LAZYATTN_ERR_LAUNCH;
   }
   DecodeParams Dp{(const uint16_t*)q, (const uint16_t*)k_pool, (const uint16_t*)v_pool,
                   block_table, block_meta, kv_lens, q_indptr, q_positions, dec_prefix,
                   (const uint16_t*)zero, partials, num_seqs, Hq, Hkv, num_blocks,
-                  ds.bps, ds.smax, scale_log2, freqs};
-  if (launch_decode(Dp, D, G, rotate, st) != hipSuccess) return LAZYATTN_ERR_LAUNCH;
+                  ds.bps, ds.smax, scale_log2, freqs, slopes};
+  if (launch_decode(Dp, D, G, pe, st) != hipSuccess) return LAZYATTN_ERR_LAUNCH;
   MergeParams Mp{q_indptr, block_table, dec_prefix, partials, (uint16_t*)out,
                  num_seqs, Hq, ds.bps, ds.smax, mode};
   if (launch_merge(Mp, total_q, D, st) != hipSuccess) return LAZYATTN_ERR_LAUNCH;
@@ -142,7 +146,7 @@ int lazyattn_prefill(const void* q, const void* k_pool, const void* v_pool,
                      size_t workspace_bytes, void* stream) {
   return run(q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indptr, q_positions,
              rope_base, num_seqs, total_q, Hq, Hkv, D, B, num_blocks, max_entries, out,
-             workspace, workspace_bytes, stream, kPlanMixed, true);
+             workspace, workspace_bytes, stream, kPlanMixed, kRope);
 }
 
 int lazyattn_decode(const void* q, const void* k_pool, const void* v_pool,
@@ -154,7 +158,7 @@ int lazyattn_decode(const void* q, const void* k_pool, const void* v_pool,
                     size_t workspace_bytes, void* stream) {
   return run(q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indptr, q_positions,
              rope_base, num_seqs, total_q, Hq, Hkv, D, B, num_blocks, max_entries, out,
-             workspace, workspace_bytes, stream, kPlanDecodeOnly, true);
+             workspace, workspace_bytes, stream, kPlanDecodeOnly, kRope);
 }
 
 int lazyattn_prefill_rotated_pool(const void* q, const void* k_pool, const void* v_pool,
@@ -167,7 +171,7 @@ int lazyattn_prefill_rotated_pool(const void* q, const void* k_pool, const void*
                                   size_t workspace_bytes, void* stream) {
   return run(q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indptr, q_positions,
              rope_base, num_seqs, total_q, Hq, Hkv, D, B, num_blocks, max_entries, out,
-             workspace, workspace_bytes, stream, kPlanMixed, false);
+             workspace, workspace_bytes, stream, kPlanMixed, kStored);
 }
 
 int lazyattn_decode_rotated_pool(const void* q, const void* k_pool, const void* v_pool,
@@ -180,7 +184,7 @@ int lazyattn_decode_rotated_pool(const void* q, const void* k_pool, const void* 
                                  size_t workspace_bytes, void* stream) {
   return run(q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indptr, q_positions,
              rope_base, num_seqs, total_q, Hq, Hkv, D, B, num_blocks, max_entries, out,
-             workspace, workspace_bytes, stream, kPlanDecodeOnly, false);
+             workspace, workspace_bytes, stream, kPlanDecodeOnly, kStored);
 }
 
 int lazyattn_prefill_freqs(const void* q, const void* k_pool, const void* v_pool,
@@ -193,7 +197,7 @@ int lazyattn_prefill_freqs(const void* q, const void* k_pool, const void* v_pool
   if (!inv_freq) return LAZYATTN_ERR_NULL;
   return run(q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indptr, q_positions, 0.0,
              num_seqs, total_q, Hq, Hkv, D, B, num_blocks, max_entries, out, workspace,
-             workspace_bytes, stream, kPlanMixed, true, inv_freq);
+             workspace_bytes, stream, kPlanMixed, kRope, inv_freq);
 }
 
 int lazyattn_decode_freqs(const void* q, const void* k_pool, const void* v_pool,
@@ -206,7 +210,31 @@ int lazyattn_decode_freqs(const void* q, const void* k_pool, const void* v_pool,
   if (!inv_freq) return LAZYATTN_ERR_NULL;
   return run(q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indptr, q_positions, 0.0,
              num_seqs, total_q, Hq, Hkv, D, B, num_blocks, max_entries, out, workspace,
-             workspace_bytes, stream, kPlanDecodeOnly, true, inv_freq);
+             workspace_bytes, stream, kPlanDecodeOnly, kRope, inv_freq);
+}
+
+int lazyattn_prefill_alibi(const void* q, const void* k_pool, const void* v_pool,
+                           const int32_t* block_table, const uint32_t* block_meta,
+                           const int32_t* kv_lens, const int32_t* q_indptr,
+                           const int32_t* q_positions, const float* slopes,
+                           int32_t num_seqs, int32_t total_q, int32_t Hq, int32_t Hkv,
+                           int32_t D, int32_t B, int32_t num_blocks, int32_t max_entries,
+                           void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  return run(q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indptr, q_positions, 0.0,
+             num_seqs, total_q, Hq, Hkv, D, B, num_blocks, max_entries, out, workspace,
+             workspace_bytes, stream, kPlanMixed, kAlibi, nullptr, slopes);
+}
+
+int lazyattn_decode_alibi(const void* q, const void* k_pool, const void* v_pool,
+                          const int32_t* block_table, const uint32_t* block_meta,
+                          const int32_t* kv_lens, const int32_t* q_indptr,
+                          const int32_t* q_positions, const float* slopes,
+                          int32_t num_seqs, int32_t total_q, int32_t Hq, int32_t Hkv,
+                          int32_t D, int32_t B, int32_t num_blocks, int32_t max_entries,
+                          void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  return run(q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indptr, q_positions, 0.0,
+             num_seqs, total_q, Hq, Hkv, D, B, num_blocks, max_entries, out, workspace,
+             workspace_bytes, stream, kPlanDecodeOnly, kAlibi, nullptr, slopes);
 }
 
 size_t lazyattn_prefill_workspace_bytes(int32_t num_seqs, int32_t total_q, int32_t max_entries,

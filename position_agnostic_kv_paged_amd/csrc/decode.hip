@@ -56,10 +56,14 @@ struct GroupMeta {
   int id[2], delta[2], nval[2];
 };
 
-// ROT = false is the materialised baseline: the pool's keys already carry R(L) at their
+// PE = kStored is the materialised baseline: the pool's keys already carry R(L) at their
 // logical positions, so keys are read as stored and q' = R(p) q for the whole item.
-template <int D, int G, bool ROT>
+// PE = kAlibi rotates nothing (q' = q, keys as stored) and adds slope_h (L - p) to each
+// score, L = off_t + j from the packed word.
+template <int D, int G, int PE>
 __global__ __launch_bounds__(kDecodeWaves * 64, 2) void decode_kernel(DecodeParams P) {
+  constexpr bool ROT = PE == kRope;
+  constexpr bool ALIBI = PE == kAlibi;
   constexpr int NC = D / 32;                  // 32-dim k-steps of the score MFMA
   constexpr int HC = NC / 2;                  // chunk c pairs with chunk c + HC (dims + D/2)
   constexpr int ROWB = D * 2;                 // bytes per value row
@@ -136,6 +140,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 2) void decode_kernel(DecodePara
     const int r = rl(x_r, k), p = rl(x_p, k);
     const int h = kvh * G + g;
     const uint16_t* qrow = P.q + ((size_t)r * P.Hq + h) * D;
+    const float sl2 = ALIBI ? P.slopes[h] * 1.4426950408889634f : 0.f;   // log2 units
 
     float m = -INFINITY, l = 0.f;
     f32x4 o[D / 16];
@@ -221,7 +226,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 2) void decode_kernel(DecodePara
             }
           }
       } else {
-        const int n = ROT ? p - ((t0 + ph) * kBlock + (ph ? d1 : d0)) : p;
+        const int n = ROT ? p - ((t0 + ph) * kBlock + (ph ? d1 : d0)) : (ALIBI ? 0 : p);
 #pragma unroll
         for (int c = 0; c < HC; ++c) {
           const u32x4 va = col_ok ? *(const u32x4*)(qrow + 32 * c + 8 * q4) : u32x4{0, 0, 0, 0};
@@ -280,7 +285,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 2) void decode_kernel(DecodePara
         const int j = 4 * q4 + i;
         const float v = ph ? S[1][i] : S[0][i];
         const bool ok = col_ok && j < nv && offp + j <= p;
-        sc[i] = ok ? v * P.scale_log2 : -INFINITY;
+        sc[i] = ok ? v * P.scale_log2 + (ALIBI ? sl2 * (float)(offp + j - p) : 0.f) : -INFINITY;
         mx = fmaxf(mx, sc[i]);
       }
       // row max over the 8 lanes of head g: slot groups (q4) and both phases
@@ -353,22 +358,31 @@ static int num_cus() {
 
 int decode_resident_waves() { return num_cus() * kDecodeWgPerCu * kDecodeWaves; }
 
-template <int D, bool ROT>
+template <int D, int PE>
 static hipError_t launch_dr(const DecodeParams& p, int G, hipStream_t st) {
   dim3 grid(num_cus() * kDecodeWgPerCu), block(kDecodeWaves * 64);
   switch (G) {
-    case 1: hipLaunchKernelGGL((decode_kernel<D, 1, ROT>), grid, block, 0, st, p); break;
-    case 2: hipLaunchKernelGGL((decode_kernel<D, 2, ROT>), grid, block, 0, st, p); break;
-    case 4: hipLaunchKernelGGL((decode_kernel<D, 4, ROT>), grid, block, 0, st, p); break;
-    case 8: hipLaunchKernelGGL((decode_kernel<D, 8, ROT>), grid, block, 0, st, p); break;
+    case 1: hipLaunchKernelGGL((decode_kernel<D, 1, PE>), grid, block, 0, st, p); break;
+    case 2: hipLaunchKernelGGL((decode_kernel<D, 2, PE>), grid, block, 0, st, p); break;
+    case 4: hipLaunchKernelGGL((decode_kernel<D, 4, PE>), grid, block, 0, st, p); break;
+    case 8: hipLaunchKernelGGL((decode_kernel<D, 8, PE>), grid, block, 0, st, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_decode(const DecodeParams& p, int D, int G, bool rotate, hipStream_t st) {
-  if (D == 128) return rotate ? launch_dr<128, true>(p, G, st) : launch_dr<128, false>(p, G, st);
-  return rotate ? launch_dr<64, true>(p, G, st) : launch_dr<64, false>(p, G, st);
+template <int D>
+static hipError_t launch_d(const DecodeParams& p, int G, int pe, hipStream_t st) {
+  switch (pe) {
+    case kRope: return launch_dr<D, kRope>(p, G, st);
+    case kStored: return launch_dr<D, kStored>(p, G, st);
+    case kAlibi: return launch_dr<D, kAlibi>(p, G, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode(const DecodeParams& p, int D, int G, int pe, hipStream_t st) {
+  return D == 128 ? launch_d<128>(p, G, pe, st) : launch_d<64>(p, G, pe, st);
 }
 
 }  // namespace lazyattn

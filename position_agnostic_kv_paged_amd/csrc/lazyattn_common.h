@@ -217,6 +217,16 @@ __host__ __device__ inline int row_splits(int T, int bps, int smax) {
   return (T + b - 1) / b;
 }
 
+// Positional encoding applied inside the attention kernels.
+//   kRope    position-free pool: keys and queries rotated by RoPE from logical positions
+//   kStored  materialised baseline: keys already carry R(L); queries rotated by R(p)
+//   kAlibi   position-free pool, no rotation: score + slope_h (L - p) (linear bias)
+enum PosEnc : int { kRope = 0, kStored = 1, kAlibi = 2 };
+
+__device__ __forceinline__ uint32_t f16_bits(float x) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
+}
+
 // Plan modes.
 enum PlanMode : int { kPlanMixed = 0, kPlanDecodeOnly = 1 };
 

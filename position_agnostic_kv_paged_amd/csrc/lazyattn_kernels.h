@@ -36,6 +36,7 @@ struct PrefillParams {
   int tiles_bound;           // upper bound of prefill tiles per KV head (grid sizing)
   float scale_log2;          // log2(e) / sqrt(D)
   const double* freqs;       // [D/2] RoPE frequencies (revolutions per position)
+  const float* slopes;       // [Hq] ALiBi slopes (positional encoding kAlibi only)
 };
 
 struct DecodeParams {
@@ -53,6 +54,7 @@ struct DecodeParams {
   int num_seqs, Hq, Hkv, num_blocks, bps, smax;
   float scale_log2;
   const double* freqs;
+  const float* slopes;       // [Hq] ALiBi slopes (positional encoding kAlibi only)
 };
 
 struct MergeParams {
@@ -69,7 +71,7 @@ hipError_t launch_merge(const MergeParams& p, int total_q, int D, hipStream_t st
 hipError_t launch_debug_decode(const uint32_t* words, const int32_t* bt, int num_seqs, int n,
                                int32_t* ids, int32_t* offs, hipStream_t st);
 // p.tiles_bound: upper bound of prefill tiles (extra workgroups exit at once)
-hipError_t launch_prefill(const PrefillParams& p, int D, int G, bool rotate, hipStream_t st);
+hipError_t launch_prefill(const PrefillParams& p, int D, int G, int pe, hipStream_t st);
 int prefill_positions_per_tile(int G);
 struct MaterializeParams {
   const uint16_t* k_pool;
@@ -102,6 +104,6 @@ hipError_t launch_probe_read(const void* buf, size_t bytes, int num_wg, uint32_t
 
 // waves of the decode grid (all resident at once); decode items are dealt round-robin to them
 int decode_resident_waves();
-hipError_t launch_decode(const DecodeParams& p, int D, int G, bool rotate, hipStream_t st);
+hipError_t launch_decode(const DecodeParams& p, int D, int G, int pe, hipStream_t st);
 
 }  // namespace lazyattn

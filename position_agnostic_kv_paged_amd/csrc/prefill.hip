@@ -104,8 +104,10 @@ __device__ __forceinline__ TileWords tile_words(const WinDec& wd) {
   return tw;
 }
 
-template <int D, int G, bool ROTATE>
+template <int D, int G, int PE>
 __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillParams P) {
+  constexpr bool ROTATE = PE == kRope;        // keys rotated per tile (position-free pool)
+  constexpr bool ALIBI = PE == kAlibi;        // no rotation; linear bias on the scores
   constexpr int NW = kPrefillWaves;
   constexpr int NT = NW * 64;
   constexpr int ROWS = 32 * NW;
@@ -186,6 +188,11 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
       for (int i = 0; i < 4; ++i) {
         float a0 = bf_lo(raw[c][i]) * sc, a1 = bf_hi(raw[c][i]) * sc;
         float b0 = bf_lo(raw[c + NCH / 2][i]) * sc, b1 = bf_hi(raw[c + NCH / 2][i]) * sc;
+        if (ALIBI) {                                // queries are not rotated
+          lo[i] = pack_f16(a0, a1);
+          hi[i] = pack_f16(b0, b1);
+          continue;
+        }
         float c0, s0, c1, s1;
         rope_cos_sin(n, fr_s[16 * c + 8 * hh + 2 * i], c0, s0);
         rope_cos_sin(n, fr_s[16 * c + 8 * hh + 2 * i + 1], c1, s1);
@@ -222,11 +229,30 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
   }
 
   // The running max m rides on the matrix cores: an extra 16-wide k-step with
-  // K~ = (1, 0, ...) and Q~ = (-m, 0, ...) makes S^T = K~ Q~^T - m directly.
+  // K~ = (1, 0, ...) and Q~ = (-m, 0, ...) makes S^T = K~ Q~^T - m directly. With ALiBi the
+  // same k-step also carries the bias within a block: K~ = (1, j, j, 0, ...) for slot j
+  // and Q~ = (-m, c_hi, c_lo, 0, ...) with c = slope_h log2(e) = c_hi + c_lo split into two
+  // fp16 values, so S^T gets + c j; the rest of the bias, c (off_b - p) per block b, is
+  // added on the vector ALUs in fp32.
   const bool e0lane = hh == 0;
-  const u32x4 ones_a = e0lane ? u32x4{0x3C00u, 0u, 0u, 0u} : u32x4{0u, 0u, 0u, 0u};   // fp16 1.0
+  const float cslope = ALIBI ? P.slopes[h] * 1.4426950408889634f : 0.f;
+  const float c_hi = (float)(_Float16)cslope;
+  const uint32_t slope_hi = ALIBI ? f16_bits(c_hi) << 16 : 0u;
+  const uint32_t jbits = ALIBI ? f16_bits((float)(col & 15)) : 0u;
+  const u32x4 ones_a = e0lane ? u32x4{0x3C00u | (jbits << 16), jbits, 0u, 0u}
+                              : u32x4{0u, 0u, 0u, 0u};      // fp16 (1, j, j, 0, ...)
   float m = -INFINITY, l = 0.f;                              // l: this lane's half of the row sum
-  u32x4 qm = {0u, 0u, 0u, 0u};                               // (-m, 0, ...) as fp16
+  u32x4 qm = {e0lane ? slope_hi : 0u,                        // (-m, c_hi, c_lo, 0...) as fp16
+              e0lane && ALIBI ? f16_bits(cslope - c_hi) : 0u, 0u, 0u};
+  const int p_bias = row_ok ? p : 0;                         // rows past the tile see no key
+  // ALiBi bias of score half t of the tile whose words are at window index 0 of wd
+  auto add_bias = [&](f32x16& s, const WinDec& wd, int t) __attribute__((always_inline)) {
+    if (!ALIBI) return;
+    const float b0 = cslope * (float)(rl(wd.off, 2 * t) - p_bias);
+    const float b1 = cslope * (float)(rl(wd.off, 2 * t + 1) - p_bias);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] += (r < 8) ? b0 : b1;
+  };
   f32x16 o[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) o[dt] = f32x16{};
@@ -370,6 +396,8 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
   };
   if (n_kt > 0) qk(0, S0);
   WinDec wdc = decode_window(P, win, T, kvlen, 0, lane);
+  add_bias(S0[0], wdc, 0);
+  add_bias(S0[1], wdc, 1);
   bool maskc = needs_mask(wdc);
   float mxc = xor32_max(max32(S0[0], S0[1]));
 
@@ -419,8 +447,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
       const float delta = m_new == -INFINITY ? 0.f : m_new - m_old;
       const float alpha = first ? 1.f : __builtin_amdgcn_exp2f(-delta);
       m = m_new;
-      qm[0] = e0lane ? (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(m == -INFINITY ? 0.f : -m))
-                     : 0u;
+      qm[0] = e0lane ? f16_bits(m == -INFINITY ? 0.f : -m) | slope_hi : 0u;
       l *= alpha;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
@@ -563,10 +590,12 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
           maskn = needs_mask(wdn);
         }
         if (g == 2) {
+          add_bias(Sn[0], wdn, 0);
           h0 = max16(Sn[0]);
           asm volatile("" ::"v"(h0));
         }
         if (g == 3) {
+          add_bias(Sn[1], wdn, 1);
           h1 = max16(Sn[1]);
           asm volatile("" ::"v"(h1));
         }
@@ -627,28 +656,32 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
 int prefill_positions_per_tile(int G) { return 32 * kPrefillWaves / G; }
 
 template <int D, int G>
-static hipError_t launch_dg(const PrefillParams& p, bool rotate, hipStream_t st) {
+static hipError_t launch_dg(const PrefillParams& p, int pe, hipStream_t st) {
   const long long n = (long long)p.tiles_bound * p.Hkv;
   dim3 grid((unsigned)((n + 7) / 8 * 8)), block(kPrefillWaves * 64);
-  if (rotate) hipLaunchKernelGGL((prefill_kernel<D, G, true>), grid, block, 0, st, p);
-  else hipLaunchKernelGGL((prefill_kernel<D, G, false>), grid, block, 0, st, p);
+  switch (pe) {
+    case kRope: hipLaunchKernelGGL((prefill_kernel<D, G, kRope>), grid, block, 0, st, p); break;
+    case kStored: hipLaunchKernelGGL((prefill_kernel<D, G, kStored>), grid, block, 0, st, p); break;
+    case kAlibi: hipLaunchKernelGGL((prefill_kernel<D, G, kAlibi>), grid, block, 0, st, p); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
 template <int D>
-static hipError_t launch_d(const PrefillParams& p, int G, bool rotate, hipStream_t st) {
+static hipError_t launch_d(const PrefillParams& p, int G, int pe, hipStream_t st) {
   switch (G) {
-    case 1: return launch_dg<D, 1>(p, rotate, st);
-    case 2: return launch_dg<D, 2>(p, rotate, st);
-    case 4: return launch_dg<D, 4>(p, rotate, st);
-    case 8: return launch_dg<D, 8>(p, rotate, st);
+    case 1: return launch_dg<D, 1>(p, pe, st);
+    case 2: return launch_dg<D, 2>(p, pe, st);
+    case 4: return launch_dg<D, 4>(p, pe, st);
+    case 8: return launch_dg<D, 8>(p, pe, st);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_prefill(const PrefillParams& p, int D, int G, bool rotate, hipStream_t st) {
+hipError_t launch_prefill(const PrefillParams& p, int D, int G, int pe, hipStream_t st) {
   if (p.tiles_bound <= 0) return hipSuccess;
-  return D == 128 ? launch_d<128>(p, G, rotate, st) : launch_d<64>(p, G, rotate, st);
+  return D == 128 ? launch_d<128>(p, G, pe, st) : launch_d<64>(p, G, pe, st);
 }
 
 }  // namespace lazyattn

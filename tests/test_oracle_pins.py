@@ -334,3 +334,68 @@ def test_package_llama31_table_equals_oracle():
     for D in (64, 128):
         want = rope.llama31_scale(rope.inv_freq(D, 500000.0))
         assert np.allclose(llama31_inv_freq(D), want, rtol=1e-15, atol=0)
+
+
+# ------------------------------------------------------------------ ALiBi
+
+def _alibi_out(wl, slopes):
+    from oracle.alibi import alibi_attention
+    return alibi_attention(wl.q_bits, wl.k_bits, wl.v_bits,
+                           [wl.compact_ids(s) for s in range(wl.num_seqs)], wl.seq_offsets,
+                           wl.kv_lens, wl.q_indptr, wl.q_pos, slopes, wl.B)
+
+
+def test_alibi_slopes_published_values():
+    from oracle.alibi import alibi_slopes
+    assert np.array_equal(alibi_slopes(8), 2.0 ** -np.arange(1, 9))        # 1/2 .. 1/256
+    assert np.allclose(alibi_slopes(4), [2 ** -2, 2 ** -4, 2 ** -6, 2 ** -8], rtol=0, atol=0)
+    s12 = alibi_slopes(12)                    # 8 of H = 8, then slopes 1, 3, 5, 7 of H = 16
+    assert np.array_equal(s12[:8], alibi_slopes(8))
+    assert np.allclose(s12[8:], 2.0 ** (-np.array([1, 3, 5, 7]) * 0.5), rtol=1e-15)
+
+
+def test_alibi_equals_sdpa_with_explicit_bias():
+    """A layout with gaps, reuse and a partial tail against torch's scaled_dot_product_attention
+    given the bias -m_h (p - L) and the causal mask as an explicit additive matrix."""
+    torch = pytest.importorskip("torch")
+    from oracle.alibi import alibi_slopes
+    segs = [Segment("doc", 3, doc=1), Segment("doc", 40, doc=0), Segment("doc", 100, doc=1),
+            Segment("private", 140, tokens=21)]
+    wl = small(Hq=8, Hkv=2, D=32, segs=segs, q_len=21, seed=13)
+    sl = alibi_slopes(8) * 3.0
+    got = _alibi_out(wl, sl)
+    ids = wl.compact_ids(0)
+    T = len(ids)
+    n_t = [16] * (T - 1) + [int(wl.kv_lens[0]) - 16 * (T - 1)]
+    k = np.concatenate([oracle.bf16_bits_to_f64(wl.k_bits[ids[t]][:, :n_t[t]]) for t in range(T)], 1)
+    v = np.concatenate([oracle.bf16_bits_to_f64(wl.v_bits[ids[t]][:, :n_t[t]]) for t in range(T)], 1)
+    L = np.concatenate([wl.seq_offsets[0][t] + np.arange(n_t[t]) for t in range(T)])
+    p = wl.q_pos.astype(np.int64)
+    bias = np.where(L[None, :] <= p[:, None], -(p[:, None] - L[None, :]).astype(float), -np.inf)
+    q = torch.from_numpy(oracle.bf16_bits_to_f64(wl.q_bits).transpose(1, 0, 2).copy())
+    kt = torch.from_numpy(k).repeat_interleave(4, dim=0)
+    vt = torch.from_numpy(v).repeat_interleave(4, dim=0)
+    mask = torch.from_numpy(sl[:, None, None] * bias[None])
+    ref = torch.nn.functional.scaled_dot_product_attention(q, kt, vt, attn_mask=mask)
+    assert np.max(np.abs(got - ref.numpy().transpose(1, 0, 2))) < 1e-12
+
+
+def test_alibi_translation_invariance_and_limits():
+    from oracle.alibi import alibi_slopes
+    segs = [Segment("doc", 10, doc=0), Segment("doc", 60, doc=2), Segment("private", 95, tokens=9)]
+    wl = small(Hq=4, Hkv=1, D=16, segs=segs, q_len=9, seed=14)
+    shifted = [Segment(s.kind, s.start + 5000, doc=s.doc, tokens=s.tokens) for s in segs]
+    wl2 = small(Hq=4, Hkv=1, D=16, segs=shifted, q_len=9, seed=14)
+    sl = alibi_slopes(4)
+    assert np.allclose(_alibi_out(wl, sl), _alibi_out(wl2, sl), rtol=0, atol=1e-13)
+    # zero slopes: plain causal attention without position (independent of any placement
+    # that keeps the visible set)
+    assert np.allclose(_alibi_out(wl, np.zeros(4)), _alibi_out(wl2, np.zeros(4)), atol=1e-13)
+    # a very steep slope: each row returns the value of its nearest visible key, the
+    # private token at the row's own position
+    out = _alibi_out(wl, np.full(4, 60.0))
+    ids, offs = wl.compact_ids(0), wl.seq_offsets[0]
+    for r, p in enumerate(wl.q_pos):
+        t = max(i for i in range(len(offs)) if offs[i] <= p)
+        want = oracle.bf16_bits_to_f64(wl.v_bits[ids[t], 0, p - offs[t]])
+        assert np.allclose(out[r], want[None, :], atol=1e-12)

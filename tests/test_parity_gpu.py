@@ -128,6 +128,40 @@ def test_frequency_tables(name, table, kind):
     compare(run_hip(wl, kind, inv_freq=th), oracle_out(wl, base=th), f"{name}/{table}/{kind}")
 
 
+def _alibi_ref(wl, slopes):
+    from oracle.alibi import alibi_attention
+    return alibi_attention(wl.q_bits, wl.k_bits, wl.v_bits,
+                           [wl.compact_ids(s) for s in range(wl.num_seqs)], wl.seq_offsets,
+                           wl.kv_lens, wl.q_indptr, wl.q_pos, slopes, wl.B)
+
+
+@pytest.mark.parametrize("kind", ["prefill", "decode"])
+@pytest.mark.parametrize("name,kw", _mini_cases(), ids=[c[0] for c in _mini_cases()])
+def test_alibi_mini_cases(name, kw, kind):
+    """lazyattn_*_alibi over the position-free pool against the float64 ALiBi definition:
+    the paper's slopes, four times steeper on the peaky (x4 query scale) cases."""
+    from oracle.alibi import alibi_slopes
+    wl = small(**kw)
+    sl = alibi_slopes(wl.Hq) * (4.0 if kw.get("q_scale", 1.0) > 1.0 else 1.0)
+    say(f"ALiBi mini case {name} via {kind}")
+    compare(run_hip(wl, kind, slopes=sl), _alibi_ref(wl, sl), f"alibi/{name}/{kind}")
+
+
+def test_alibi_mixed_batch_and_zero_slopes():
+    """A mixed batch through lazyattn_prefill_alibi, and zero slopes (no positional term)."""
+    from oracle.alibi import alibi_slopes
+    reqs = [RequestLayout([Segment("doc", 11, doc=0), Segment("doc", 60, doc=1),
+                           Segment("private", 100, tokens=70)], 70),
+            RequestLayout([Segment("doc", 0, doc=2), Segment("private", 32, tokens=5)], 1),
+            RequestLayout([Segment("doc", 500, doc=2), Segment("doc", 5, doc=0),
+                           Segment("private", 600, tokens=17)], 1)]
+    wl = build("mixed-small", 8, 2, 128, 16, 10000.0, 3, 32, reqs, seed=18)
+    for sl in (alibi_slopes(8), np.zeros(8)):
+        say(f"ALiBi mixed batch, slopes {sl[:2]}")
+        compare(run_hip(wl, "prefill", slopes=sl), _alibi_ref(wl, sl), "alibi/mixed/prefill")
+        compare(run_hip(wl, "decode", slopes=sl), _alibi_ref(wl, sl), "alibi/mixed/decode")
+
+
 @pytest.mark.parametrize("kind", ["prefill", "decode"])
 def test_sequences_without_entries(kind):
     """Sequences with no block-table entries (first, middle and last of the batch) give 0
