@@ -125,8 +125,8 @@ def _counter_rows(run_dir):
 def record_traffic(fetch_dir, write_dir):
     """Write profiles/traffic.json from one FETCH_SIZE and one WRITE_SIZE rocprofv3 run of
     this script: per-launch KiB of each attention kernel, scaled by what the same counter
-    reads on the calibration copy of COPY_CALIBRATION_BYTES (found as the dispatch whose
-    WRITE_SIZE is closest to that size; both runs dispatch in the same order)."""
+    reads on the calibration copy of COPY_CALIBRATION_BYTES (the runtime copy kernel that
+    writes exactly that size; both runs dispatch in the same order)."""
     fetch, write = _counter_rows(fetch_dir), _counter_rows(write_dir)
 
     def per_dispatch(rows, counter):
@@ -138,11 +138,13 @@ def record_traffic(fetch_dir, write_dir):
         return out
     f, w = per_dispatch(fetch, "FETCH_SIZE"), per_dispatch(write, "WRITE_SIZE")
     target_kib = COPY_CALIBRATION_BYTES / 1024
-    # the copy writes the calibration size and, unlike the fill of its source, reads it too
-    near = [k for k in w if abs(w[k] - target_kib) < 0.05 * target_kib and k in f]
-    if not near:
-        raise SystemExit("calibration copy not found in the counter runs")
-    cal = max(near, key=lambda k: f[k])
+    # the calibration copy is the runtime's device-to-device copy kernel writing exactly the
+    # calibration size (other kernels of the run may write as much: fills, conversions)
+    near = [k for k in w if "copyBuffer" in k[1] and abs(w[k] - target_kib) < 0.01 * target_kib
+            and k in f]
+    if len(near) != 1:
+        raise SystemExit(f"calibration copy not found uniquely in the counter runs ({near})")
+    cal = near[0]
     rec = {"_about": "HBM-side bytes per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE "
                      "(KiB per dispatch), each scaled by the factor that maps the same counter "
                      "on a plain device copy of known size (run once inside bench.py) to that "
@@ -483,6 +485,27 @@ def main():
                          "materialize_then_attend_ms": t_mat + t_base,
                          "lazy_speedup_vs_materialize": (t_mat + t_base) / t_lazy}
         line["rotation_ablation"] = abl
+        # the ALiBi variant on the same pool and rows (Press et al.'s slopes)
+        slopes = torch.tensor([2.0 ** (-8.0 * i / wl.Hq) for i in range(1, wl.Hq + 1)],
+                              dtype=torch.float32, device=dev)
+        var = {}
+        for kind, seqs, fn, a, ws in halves:
+            def run_alibi():
+                fn(a["q"], a["k_pool"], a["v_pool"], a["block_table"], a["block_meta"],
+                   a["kv_lens"], a["q_indptr"], a["q_pos"], wl.rope_base, a["max_entries"],
+                   out=a["out"], workspace=ws, stream=stream, slopes=slopes)
+            for _ in range(args.warmup):
+                run_alibi()
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
+            for k in range(args.steps):
+                e[2 * k].record(stream)
+                run_alibi()
+                e[2 * k + 1].record(stream)
+            torch.cuda.synchronize()
+            var[kind] = {"ms": float(np.median([e[2 * k].elapsed_time(e[2 * k + 1])
+                                                for k in range(args.steps)])),
+                         "rope_ms": line[kind]["ms_pct"]["median"]}
+        line["alibi"] = var
     # ingest of new tokens' K/V into pool slots (separate scratch pool; not part of a step)
     line["ingest"] = measure_ingest(torch, L, wl, stream, args.steps)
     # the same kernels' rates against what the chip sustains on plain probes

@@ -53,43 +53,87 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanParams P) {
 }
 
 // Split-K merge: one thread per 4 output dims of one (row, head). Partials hold the
-// running max m (log2 domain), the sum l and the unnormalised o of each split.
+// running max m (log2 domain), the sum l and the unnormalised o of each split. The row's
+// sequence is found once per workgroup by its first wave (a 64-way search: one round of
+// loads per factor of 64 sequences), and the partials of up to 8 splits are loaded at once,
+// so the kernel waits for a few memory round trips rather than one per split.
 template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(MergeParams P) {
   constexpr int TPH = D / 4;                  // threads per head
   constexpr int HPB = 256 / TPH;              // heads per block
+  constexpr int CH = 8;                       // splits loaded together
+  __shared__ long long s_item0;
+  __shared__ int s_splits;
   const int r = blockIdx.x;
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    int lo = 0, hi = P.num_seqs;              // q_indptr[lo] <= r < q_indptr[hi]
+    while (hi - lo > 64) {                    // 64 probes spread over [lo, hi)
+      const int span = hi - lo;
+      const int idx = lo + (int)(((long long)lane * span) / 64);
+      const unsigned long long bal = __ballot(P.q_indptr[idx] <= r);   // lane 0 always set
+      const int top = 63 - __builtin_clzll(bal);
+      const int nlo = lo + (int)(((long long)top * span) / 64);
+      if (top < 63) hi = lo + (int)(((long long)(top + 1) * span) / 64);
+      lo = nlo;
+    }
+    {                                         // the last <= 64 candidates, one per lane
+      const int span = hi - lo;
+      const bool le = lane < span && P.q_indptr[lo + min(lane, span - 1)] <= r;
+      lo += 63 - __builtin_clzll(__ballot(le));
+    }
+    if (lane == 0) {
+      const int seq = lo;
+      const int q0 = P.q_indptr[seq], qlen = P.q_indptr[seq + 1] - q0;
+      const bool dec = (P.mode == kPlanDecodeOnly) || qlen == 1;
+      const int T = P.block_table[seq + 1] - P.block_table[seq];
+      const int splits = row_splits(T, P.bps, P.smax);
+      s_splits = dec ? splits : 0;            // prefill rows are written by the prefill kernel
+      s_item0 = (long long)P.dec_prefix[seq] + (long long)(r - q0) * splits;
+    }
+  }
+  __syncthreads();
+  const int splits = s_splits;
+  const long long item0 = s_item0;
   const int h = blockIdx.y * HPB + threadIdx.x / TPH;
   const int d0 = (threadIdx.x % TPH) * 4;
-  if (h >= P.Hq) return;
-  const int seq = upper_seq(P.q_indptr, P.num_seqs, r);
-  const int q0 = P.q_indptr[seq], qlen = P.q_indptr[seq + 1] - q0;
-  const bool dec = (P.mode == kPlanDecodeOnly) || qlen == 1;
-  if (!dec) return;                           // written by the prefill kernel
-  const int T = P.block_table[seq + 1] - P.block_table[seq];
-  const int splits = row_splits(T, P.bps, P.smax);
-  const long long item0 = (long long)P.dec_prefix[seq] + (long long)(r - q0) * splits;
+  if (splits == 0 || h >= P.Hq) return;
+  auto part = [&](int sp) { return P.partials + ((item0 + sp) * P.Hq + h) * (D + 4); };
   float M = -INFINITY;
-  for (int s = 0; s < splits; ++s) {
-    const float* part = P.partials + ((item0 + s) * P.Hq + h) * (D + 4);
-    M = fmaxf(M, part[D]);
+  for (int s0 = 0; s0 < splits; s0 += CH) {
+    float mm[CH];
+#pragma unroll
+    for (int u = 0; u < CH; ++u) mm[u] = s0 + u < splits ? part(s0 + u)[D] : -INFINITY;
+#pragma unroll
+    for (int u = 0; u < CH; ++u) M = fmaxf(M, mm[u]);
   }
-  float L = 0.f, o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+  float L = 0.f;
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
   if (M != -INFINITY) {
-    for (int s = 0; s < splits; ++s) {
-      const float* part = P.partials + ((item0 + s) * P.Hq + h) * (D + 4);
-      const float m = part[D];
-      if (m == -INFINITY) continue;
-      const float sc = exp2f(m - M);
-      L += part[D + 1] * sc;
-      const f32x4 v = *(const f32x4*)(part + d0);
-      o0 += v[0] * sc; o1 += v[1] * sc; o2 += v[2] * sc; o3 += v[3] * sc;
+    for (int s0 = 0; s0 < splits; s0 += CH) {
+      float mm[CH], ll[CH];
+      f32x4 vv[CH];
+#pragma unroll
+      for (int u = 0; u < CH; ++u) {
+        const bool in = s0 + u < splits;
+        const float* pp = part(in ? s0 + u : 0);
+        mm[u] = in ? pp[D] : -INFINITY;
+        ll[u] = in ? pp[D + 1] : 0.f;
+        vv[u] = in ? *(const f32x4*)(pp + d0) : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int u = 0; u < CH; ++u) {
+        if (mm[u] == -INFINITY) continue;
+        const float sc = exp2f(mm[u] - M);
+        L += ll[u] * sc;
+        o += vv[u] * sc;
+      }
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   uint32_t* dst = (uint32_t*)(P.out + ((size_t)r * P.Hq + h) * D + d0);
-  dst[0] = pack_bf16(o0 * inv, o1 * inv);
-  dst[1] = pack_bf16(o2 * inv, o3 * inv);
+  dst[0] = pack_bf16(o[0] * inv, o[1] * inv);
+  dst[1] = pack_bf16(o[2] * inv, o[3] * inv);
 }
 
 __global__ void debug_decode_meta_kernel(const uint32_t* words, const int32_t* block_table,
