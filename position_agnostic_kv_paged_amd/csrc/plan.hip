@@ -8,18 +8,16 @@
 
 namespace lazyattn {
 
-// One workgroup of 1024 threads; chunked exclusive scan over sequences.
-__global__ __launch_bounds__(1024) void plan_kernel(PlanParams P) {
-  __shared__ int sa[1024], sb[1024];
-  __shared__ int carry_a, carry_b;
-  const int tid = threadIdx.x;
-  if (tid == 0) { carry_a = 0; carry_b = 0; }
+// One workgroup of 256 threads; exclusive scan over sequences in chunks of 256: each wave
+// scans its 64 counts with shuffles, the four wave totals go through LDS (two barriers per
+// chunk).
+__global__ __launch_bounds__(256) void plan_kernel(PlanParams P) {
+  __shared__ int wa[4], wb[4];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   if (tid < 48) P.zero[tid] = 0u;
-#pragma unroll
-  for (int i = 0; i < kMaxHalfDim; ++i)
-    if (tid == i && i < P.half_dim) P.freqs_out[i] = P.fr.f[i];
-  __syncthreads();
-  for (int base = 0; base < P.num_seqs; base += 1024) {
+  if (tid < P.half_dim) P.freqs_out[tid] = P.fr.f[tid];
+  int carry_a = 0, carry_b = 0;                 // identical in every thread
+  for (int base = 0; base < P.num_seqs; base += 256) {
     const int s = base + tid;
     int a = 0, b = 0;
     if (s < P.num_seqs) {
@@ -29,22 +27,28 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanParams P) {
       if (dec) b = qlen * row_splits(T, P.bps, P.smax);
       else a = (qlen + P.pos_per_tile - 1) / P.pos_per_tile;
     }
-    sa[tid] = a; sb[tid] = b;
+    int ia = a, ib = b;                          // inclusive scan within the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int xa = __shfl_up(ia, o), xb = __shfl_up(ib, o);
+      if (lane >= o) { ia += xa; ib += xb; }
+    }
+    if (lane == 63) { wa[w] = ia; wb[w] = ib; }
     __syncthreads();
-    for (int o = 1; o < 1024; o <<= 1) {          // inclusive Hillis-Steele scan
-      int xa = tid >= o ? sa[tid - o] : 0;
-      int xb = tid >= o ? sb[tid - o] : 0;
-      __syncthreads();
-      sa[tid] += xa; sb[tid] += xb;
-      __syncthreads();
+    int oa = 0, ob = 0, ta = 0, tb = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (k < w) { oa += wa[k]; ob += wb[k]; }
+      ta += wa[k];
+      tb += wb[k];
     }
     if (s < P.num_seqs) {
-      P.pf_prefix[s] = carry_a + sa[tid] - a;
-      P.dec_prefix[s] = carry_b + sb[tid] - b;
+      P.pf_prefix[s] = carry_a + oa + ia - a;
+      P.dec_prefix[s] = carry_b + ob + ib - b;
     }
-    __syncthreads();
-    if (tid == 1023) { carry_a += sa[1023]; carry_b += sb[1023]; }
-    __syncthreads();
+    carry_a += ta;
+    carry_b += tb;
+    __syncthreads();                             // wa / wb are rewritten next chunk
   }
   if (tid == 0) {
     P.pf_prefix[P.num_seqs] = carry_a;
@@ -55,13 +59,14 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanParams P) {
 // Split-K merge: one thread per 4 output dims of one (row, head). Partials hold the
 // running max m (log2 domain), the sum l and the unnormalised o of each split. The row's
 // sequence is found once per workgroup by its first wave (a 64-way search: one round of
-// loads per factor of 64 sequences), and the partials of up to 8 splits are loaded at once,
-// so the kernel waits for a few memory round trips rather than one per split.
+// loads per factor of 64 sequences), and the partials of up to 16 splits are loaded at once
+// and folded in with online rescaling, so the kernel waits for a few memory round trips
+// rather than one per split.
 template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(MergeParams P) {
   constexpr int TPH = D / 4;                  // threads per head
   constexpr int HPB = 256 / TPH;              // heads per block
-  constexpr int CH = 8;                       // splits loaded together
+  constexpr int CH = 16;                      // splits loaded together
   __shared__ long long s_item0;
   __shared__ int s_splits;
   const int r = blockIdx.x;
@@ -99,36 +104,36 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams P) {
   const int d0 = (threadIdx.x % TPH) * 4;
   if (splits == 0 || h >= P.Hq) return;
   auto part = [&](int sp) { return P.partials + ((item0 + sp) * P.Hq + h) * (D + 4); };
-  float M = -INFINITY;
-  for (int s0 = 0; s0 < splits; s0 += CH) {
-    float mm[CH];
-#pragma unroll
-    for (int u = 0; u < CH; ++u) mm[u] = s0 + u < splits ? part(s0 + u)[D] : -INFINITY;
-#pragma unroll
-    for (int u = 0; u < CH; ++u) M = fmaxf(M, mm[u]);
-  }
-  float L = 0.f;
+  // one pass with online rescaling, CH splits per round of loads
+  float M = -INFINITY, L = 0.f;
   f32x4 o = {0.f, 0.f, 0.f, 0.f};
-  if (M != -INFINITY) {
-    for (int s0 = 0; s0 < splits; s0 += CH) {
-      float mm[CH], ll[CH];
-      f32x4 vv[CH];
+  for (int s0 = 0; s0 < splits; s0 += CH) {
+    float mm[CH], ll[CH];
+    f32x4 vv[CH];
 #pragma unroll
-      for (int u = 0; u < CH; ++u) {
-        const bool in = s0 + u < splits;
-        const float* pp = part(in ? s0 + u : 0);
-        mm[u] = in ? pp[D] : -INFINITY;
-        ll[u] = in ? pp[D + 1] : 0.f;
-        vv[u] = in ? *(const f32x4*)(pp + d0) : f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-#pragma unroll
-      for (int u = 0; u < CH; ++u) {
-        if (mm[u] == -INFINITY) continue;
-        const float sc = exp2f(mm[u] - M);
-        L += ll[u] * sc;
-        o += vv[u] * sc;
-      }
+    for (int u = 0; u < CH; ++u) {
+      const bool in = s0 + u < splits;
+      const float* pp = part(in ? s0 + u : 0);
+      mm[u] = in ? pp[D] : -INFINITY;
+      ll[u] = in ? pp[D + 1] : 0.f;
+      vv[u] = in ? *(const f32x4*)(pp + d0) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    float cm = mm[0];
+#pragma unroll
+    for (int u = 1; u < CH; ++u) cm = fmaxf(cm, mm[u]);
+    if (cm == -INFINITY) continue;                // no visible key in these splits
+    const float Mn = fmaxf(M, cm);
+    const float al = M == -INFINITY ? 0.f : exp2f(M - Mn);
+    L *= al;
+    o *= al;
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      if (mm[u] == -INFINITY) continue;
+      const float sc = exp2f(mm[u] - Mn);
+      L += ll[u] * sc;
+      o += vv[u] * sc;
+    }
+    M = Mn;
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   uint32_t* dst = (uint32_t*)(P.out + ((size_t)r * P.Hq + h) * D + d0);
@@ -148,7 +153,7 @@ __global__ void debug_decode_meta_kernel(const uint32_t* words, const int32_t* b
 }
 
 hipError_t launch_plan(const PlanParams& p, hipStream_t st) {
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, st, p);
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
