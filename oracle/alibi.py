@@ -74,3 +74,13 @@ def alibi_attention(q, k_pool, v_pool, seq_block_ids, seq_offsets, kv_lens, q_in
         qf = bf16_bits_to_f64(q[r0:r1]) if q.dtype == np.uint16 else np.asarray(q[r0:r1], float)
         out[r0:r1] = attend_alibi(qf, q_pos[r0:r1], K, V, key_pos, slopes)
     return out
+
+
+def alibi_rows(q, k_pool, v_pool, seq_block_ids, seq_offsets, kv_lens, q_indptr, q_pos,
+               slopes, B, seq, rows):
+    """Output rows `rows` (global row indices of sequence `seq`), float64 [len(rows), Hq, D]."""
+    rows = np.asarray(rows, dtype=np.int64)
+    K, V, key_pos = materialise(k_pool, v_pool, seq_block_ids[seq], seq_offsets[seq],
+                                int(kv_lens[seq]), B, 10000.0, rotate_keys=False)
+    qf = bf16_bits_to_f64(q[rows]) if q.dtype == np.uint16 else np.asarray(q[rows], float)
+    return attend_alibi(qf, q_pos[rows], K, V, key_pos, slopes)

@@ -353,14 +353,22 @@ def test_shifted_document_is_detected():
 
 # ------------------------------------------------------------------ full-size workloads
 
-def _sampled(wl, kind, seqs, rows_of):
-    out = run_hip(wl, kind)
+def _sampled(wl, kind, seqs, rows_of, inv_freq=None, slopes=None):
+    out = run_hip(wl, kind, inv_freq=inv_freq, slopes=slopes)
     assert np.all(np.isfinite(out)), "non-finite outputs"
     got, want = [], []
     for s in seqs:
         rows = rows_of(s)
         got.append(out[rows])
-        want.append(oracle_out(wl, rows=rows, seq=s))
+        if slopes is not None:
+            from oracle.alibi import alibi_rows
+            want.append(alibi_rows(wl.q_bits, wl.k_bits, wl.v_bits,
+                                   [wl.compact_ids(x) if x == s else None
+                                    for x in range(wl.num_seqs)],
+                                   wl.seq_offsets, wl.kv_lens, wl.q_indptr, wl.q_pos,
+                                   slopes, wl.B, s, rows))
+        else:
+            want.append(oracle_out(wl, rows=rows, seq=s, base=inv_freq))
     return np.concatenate(got), np.concatenate(want)
 
 
@@ -401,6 +409,31 @@ def test_mixed_70b_batch():
         return q0 + np.array([0, 31, 32, 255, 256, 511])
     g, w = _sampled(wl, "prefill", [0, 3, 4, 50, 99], rows)
     compare(g, w, "mixed")
+
+
+@pytest.mark.parametrize("variant", ["alibi", "llama31"])
+@pytest.mark.parametrize("name,kind", [("decode-32q8kv-b64-ctx4161", "decode"),
+                                       ("prefill-32q8kv-b16-ctx5376", "prefill"),
+                                       ("decode-32q8kv-b8-ctx32769", "decode")])
+def test_full_size_variants(name, kind, variant):
+    """The ALiBi and frequency-table entry points on the full-size workloads (positions up
+    to ~35k), sampled rows against the oracle, all outputs finite."""
+    import position_agnostic_kv_paged_amd as L
+    from oracle.alibi import alibi_slopes
+    wl = make(name)
+    say(f"{name} via {kind}, {variant}")
+    opt = dict(slopes=alibi_slopes(wl.Hq)) if variant == "alibi" else \
+        dict(inv_freq=L.llama31_inv_freq(wl.D))
+    if kind == "prefill":
+        def rows(s):
+            return wl.q_indptr[s] + np.array([0, 63, 64, 200, 255])
+        seqs = [0, 15]
+    else:
+        def rows(s):
+            return np.array([wl.q_indptr[s]])
+        seqs = [0, wl.num_seqs - 1]
+    g, w = _sampled(wl, kind, seqs, rows, **opt)
+    compare(g, w, f"{name}/{variant}")
 
 
 @pytest.mark.gpu

@@ -16,7 +16,7 @@ def oracle_out(wl, rows=None, seq=None, base=None):
                                  [wl.compact_ids(s) if s == seq else None
                                   for s in range(wl.num_seqs)],
                                  wl.seq_offsets, wl.kv_lens, wl.q_indptr, wl.q_pos,
-                                 wl.rope_base, wl.B, seq, rows)
+                                 wl.rope_base if base is None else base, wl.B, seq, rows)
 
 
 def small(Hq=4, Hkv=2, D=16, B=16, base=10000.0, seed=7, segs=None, q_len=None,
