@@ -19,7 +19,7 @@ bool shape_ok(int32_t Hq, int32_t Hkv, int32_t D, int32_t B) {
   if (B != kBlock) return false;
   if (Hkv <= 0 || Hq <= 0 || Hq % Hkv) return false;
   const int G = Hq / Hkv;
-  return G == 1 || G == 2 || G == 4 || G == 8;
+  return G == 1 || G == 2 || G == 4 || G == 8 || G == 16;
 }
 
 // Decode split size (blocks per item, even, at least 8). The (row-split, kv-head) items are

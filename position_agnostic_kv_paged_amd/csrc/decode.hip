@@ -64,6 +64,11 @@ template <int D, int G, int PE>
 __global__ __launch_bounds__(kDecodeWaves * 64, 2) void decode_kernel(DecodeParams P) {
   constexpr bool ROT = PE == kRope;
   constexpr bool ALIBI = PE == kAlibi;
+  // PHC: the 16 columns of the score MFMA hold (head, block phase) pairs (2 G <= 16), so
+  // both blocks of a group are scored against one q' operand. Otherwise (G = 16) the
+  // columns are the 16 heads and q' is set to each block's phase in turn.
+  constexpr bool PHC = 2 * G <= 16;
+  static_assert(PHC || G == 16, "decode supports G in {1, 2, 4, 8, 16}");
   constexpr int NC = D / 32;                  // 32-dim k-steps of the score MFMA
   constexpr int HC = NC / 2;                  // chunk c pairs with chunk c + HC (dims + D/2)
   constexpr int ROWB = D * 2;                 // bytes per value row
@@ -96,9 +101,9 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 2) void decode_kernel(DecodePara
     rope_cos_sin(j, P.freqs[f0 + 1], c1, s1);
     slot_tab[i] = f32x4{c0, s0, c1, s1};
   }
-  if (threadIdx.x < D / 2) {
+  if (threadIdx.x < D / 2) {                 // R(32) (PHC) or R(16): q' advance
     float cs, sn;
-    rope_cos_sin(32, P.freqs[threadIdx.x], cs, sn);
+    rope_cos_sin(PHC ? 32 : 16, P.freqs[threadIdx.x], cs, sn);
     adv_all[2 * threadIdx.x] = cs;
     adv_all[2 * threadIdx.x + 1] = sn;
   }
@@ -206,105 +211,215 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 2) void decode_kernel(DecodePara
         }
       }
 
-      // ---- q' of this lane's column: R(p - off_{t0+ph}) q_g ---------------------------
       const int d0 = gcur.delta[0];
       const int d1 = (t0 + 1 < ee) ? gcur.delta[1] : d0;
-      if (!ROT && have_q) {
-        // keys carry their absolute rotation: q' = R(p) q stays fixed
-      } else if (ROT && have_q && d0 == cur_delta && d1 == cur_delta) {
+      u32x4 bp;
+      if constexpr (PHC) {
+        // ---- q' of this lane's column: R(p - off_{t0+ph}) q_g ---------------------------
+        if (!ROT && have_q) {
+          // keys carry their absolute rotation: q' = R(p) q stays fixed
+        } else if (ROT && have_q && d0 == cur_delta && d1 == cur_delta) {
 #pragma unroll
-        for (int c = 0; c < HC; ++c)
+          for (int c = 0; c < HC; ++c)
 #pragma unroll
-          for (int e2 = 0; e2 < 4; ++e2) {           // R(-32)
-            const f32x4 cs = *(const f32x4*)(adv_all + 2 * (32 * c + 8 * q4 + 2 * e2));
+            for (int e2 = 0; e2 < 4; ++e2) {           // R(-32)
+              const f32x4 cs = *(const f32x4*)(adv_all + 2 * (32 * c + 8 * q4 + 2 * e2));
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-              const int e = 2 * e2 + u;
-              const float a = qr[c][e], b = qr[c + HC][e];
-              qr[c][e] = a * cs[2 * u] + b * cs[2 * u + 1];
-              qr[c + HC][e] = b * cs[2 * u] - a * cs[2 * u + 1];
+              for (int u = 0; u < 2; ++u) {
+                const int e = 2 * e2 + u;
+                const float a = qr[c][e], b = qr[c + HC][e];
+                qr[c][e] = a * cs[2 * u] + b * cs[2 * u + 1];
+                qr[c + HC][e] = b * cs[2 * u] - a * cs[2 * u + 1];
+              }
+            }
+        } else {
+          const int n = ROT ? p - ((t0 + ph) * kBlock + (ph ? d1 : d0)) : (ALIBI ? 0 : p);
+#pragma unroll
+          for (int c = 0; c < HC; ++c) {
+            const u32x4 va = col_ok ? *(const u32x4*)(qrow + 32 * c + 8 * q4) : u32x4{0, 0, 0, 0};
+            const u32x4 vb = col_ok ? *(const u32x4*)(qrow + 32 * (c + HC) + 8 * q4)
+                                    : u32x4{0, 0, 0, 0};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              float cs, sn;
+              rope_cos_sin(n, P.freqs[32 * c + 8 * q4 + e], cs, sn);
+              const float a = (e & 1) ? bf_hi(va[e >> 1]) : bf_lo(va[e >> 1]);
+              const float b = (e & 1) ? bf_hi(vb[e >> 1]) : bf_lo(vb[e >> 1]);
+              qr[c][e] = a * cs - b * sn;
+              qr[c + HC][e] = a * sn + b * cs;
             }
           }
-      } else {
-        const int n = ROT ? p - ((t0 + ph) * kBlock + (ph ? d1 : d0)) : (ALIBI ? 0 : p);
+          have_q = !ROT || (d0 == d1);
+          cur_delta = d1;
+        }
+        // ---- scores of both blocks; each lane keeps its own phase's block ------------------
+        f32x4 S[2] = {f32x4{}, f32x4{}};
 #pragma unroll
         for (int c = 0; c < HC; ++c) {
-          const u32x4 va = col_ok ? *(const u32x4*)(qrow + 32 * c + 8 * q4) : u32x4{0, 0, 0, 0};
-          const u32x4 vb = col_ok ? *(const u32x4*)(qrow + 32 * (c + HC) + 8 * q4)
-                                  : u32x4{0, 0, 0, 0};
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            float cs, sn;
-            rope_cos_sin(n, P.freqs[32 * c + 8 * q4 + e], cs, sn);
-            const float a = (e & 1) ? bf_hi(va[e >> 1]) : bf_lo(va[e >> 1]);
-            const float b = (e & 1) ? bf_hi(vb[e >> 1]) : bf_lo(vb[e >> 1]);
-            qr[c][e] = a * cs - b * sn;
-            qr[c + HC][e] = a * sn + b * cs;
-          }
-        }
-        have_q = !ROT || (d0 == d1);
-        cur_delta = d1;
-      }
-      // ---- scores of both blocks; each lane keeps its own phase's block ------------------
-      f32x4 S[2] = {f32x4{}, f32x4{}};
-#pragma unroll
-      for (int c = 0; c < HC; ++c) {
-        u32x4 qlo, qhi;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          qlo[i] = pack_f16(qr[c][2 * i], qr[c][2 * i + 1]);
-          qhi[i] = pack_f16(qr[c + HC][2 * i], qr[c + HC][2 * i + 1]);
-        }
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          u32x4 lo, hi;
+          u32x4 qlo, qhi;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float a0 = bf_lo(kcur[b][c][i]), a1 = bf_hi(kcur[b][c][i]);
-            const float b0 = bf_lo(kcur[b][c + HC][i]), b1 = bf_hi(kcur[b][c + HC][i]);
-            if (ROT) {
-              const f32x4 t = slot_tab[((c * 4 + q4) * 4 + i) * 16 + i16];
-              const float c0 = t[0], s0 = t[1], c1 = t[2], s1 = t[3];
-              lo[i] = pack_f16(a0 * c0 - b0 * s0, a1 * c1 - b1 * s1);
-              hi[i] = pack_f16(a0 * s0 + b0 * c0, a1 * s1 + b1 * c1);
-            } else {
-              lo[i] = pack_f16(a0, a1);
-              hi[i] = pack_f16(b0, b1);
+            qlo[i] = pack_f16(qr[c][2 * i], qr[c][2 * i + 1]);
+            qhi[i] = pack_f16(qr[c + HC][2 * i], qr[c + HC][2 * i + 1]);
+          }
+#pragma unroll
+          for (int b = 0; b < 2; ++b) {
+            u32x4 lo, hi;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float a0 = bf_lo(kcur[b][c][i]), a1 = bf_hi(kcur[b][c][i]);
+              const float b0 = bf_lo(kcur[b][c + HC][i]), b1 = bf_hi(kcur[b][c + HC][i]);
+              if (ROT) {
+                const f32x4 t = slot_tab[((c * 4 + q4) * 4 + i) * 16 + i16];
+                const float c0 = t[0], s0 = t[1], c1 = t[2], s1 = t[3];
+                lo[i] = pack_f16(a0 * c0 - b0 * s0, a1 * c1 - b1 * s1);
+                hi[i] = pack_f16(a0 * s0 + b0 * c0, a1 * s1 + b1 * c1);
+              } else {
+                lo[i] = pack_f16(a0, a1);
+                hi[i] = pack_f16(b0, b1);
+              }
+            }
+            S[b] = mfma16h(as_f16x8(lo), as_f16x8(qlo), S[b]);
+            S[b] = mfma16h(as_f16x8(hi), as_f16x8(qhi), S[b]);
+          }
+        }
+        const int nv = ph ? gcur.nval[1] : gcur.nval[0];
+        const int offp = (t0 + ph) * kBlock + (ph ? d1 : d0);
+        float sc[4];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = 4 * q4 + i;
+          const float v = ph ? S[1][i] : S[0][i];
+          const bool ok = col_ok && j < nv && offp + j <= p;
+          sc[i] = ok ? v * P.scale_log2 + (ALIBI ? sl2 * (float)(offp + j - p) : 0.f) : -INFINITY;
+          mx = fmaxf(mx, sc[i]);
+        }
+        // row max over the 8 lanes of head g: slot groups (q4) and both phases
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = fmaxf(mx, __shfl_xor(mx, G));
+        const float m_new = fmaxf(m, mx);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = exp2f(m - m_use);
+        float pr[4];
+        float rsum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { pr[i] = exp2f(sc[i] - m_use); rsum += pr[i]; }
+        l = l * alpha + rsum;
+        m = m_new;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) o[dt] *= alpha;
+        const uint32_t p01 = pack_bf16(pr[0], pr[1]), p23 = pack_bf16(pr[2], pr[3]);
+        bp = ph ? u32x4{0u, 0u, p01, p23} : u32x4{p01, p23, 0u, 0u};
+      } else {
+        // ---- G = 16: q' = R(p - off_b) q_g of lane column g, set for block b in turn ------
+        auto qexact = [&](int n) {
+#pragma unroll
+          for (int c = 0; c < HC; ++c) {
+            const u32x4 va = *(const u32x4*)(qrow + 32 * c + 8 * q4);
+            const u32x4 vb = *(const u32x4*)(qrow + 32 * (c + HC) + 8 * q4);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              float cs, sn;
+              rope_cos_sin(n, P.freqs[32 * c + 8 * q4 + e], cs, sn);
+              const float a = (e & 1) ? bf_hi(va[e >> 1]) : bf_lo(va[e >> 1]);
+              const float b = (e & 1) ? bf_hi(vb[e >> 1]) : bf_lo(vb[e >> 1]);
+              qr[c][e] = a * cs - b * sn;
+              qr[c + HC][e] = a * sn + b * cs;
             }
           }
-          S[b] = mfma16h(as_f16x8(lo), as_f16x8(qlo), S[b]);
-          S[b] = mfma16h(as_f16x8(hi), as_f16x8(qhi), S[b]);
+        };
+        auto set_q = [&](int off) {              // qr := R(p - off) q (or the fixed q')
+          if (!ROT) {
+            if (!have_q) qexact(ALIBI ? 0 : p);
+          } else if (have_q && off == cur_delta + kBlock) {
+#pragma unroll
+            for (int c = 0; c < HC; ++c)
+#pragma unroll
+              for (int e2 = 0; e2 < 4; ++e2) {       // R(-16)
+                const f32x4 cs = *(const f32x4*)(adv_all + 2 * (32 * c + 8 * q4 + 2 * e2));
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                  const int e = 2 * e2 + u;
+                  const float a = qr[c][e], b = qr[c + HC][e];
+                  qr[c][e] = a * cs[2 * u] + b * cs[2 * u + 1];
+                  qr[c + HC][e] = b * cs[2 * u] - a * cs[2 * u + 1];
+                }
+              }
+          } else {
+            qexact(p - off);
+          }
+          have_q = true;
+          cur_delta = off;                         // here: the offset qr is anchored at
+        };
+        auto scores = [&](int b) {
+          f32x4 S = {};
+#pragma unroll
+          for (int c = 0; c < HC; ++c) {
+            u32x4 qlo, qhi, lo, hi;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              qlo[i] = pack_f16(qr[c][2 * i], qr[c][2 * i + 1]);
+              qhi[i] = pack_f16(qr[c + HC][2 * i], qr[c + HC][2 * i + 1]);
+              const float a0 = bf_lo(kcur[b][c][i]), a1 = bf_hi(kcur[b][c][i]);
+              const float b0 = bf_lo(kcur[b][c + HC][i]), b1 = bf_hi(kcur[b][c + HC][i]);
+              if (ROT) {
+                const f32x4 t = slot_tab[((c * 4 + q4) * 4 + i) * 16 + i16];
+                const float c0 = t[0], s0 = t[1], c1 = t[2], s1 = t[3];
+                lo[i] = pack_f16(a0 * c0 - b0 * s0, a1 * c1 - b1 * s1);
+                hi[i] = pack_f16(a0 * s0 + b0 * c0, a1 * s1 + b1 * c1);
+              } else {
+                lo[i] = pack_f16(a0, a1);
+                hi[i] = pack_f16(b0, b1);
+              }
+            }
+            S = mfma16h(as_f16x8(lo), as_f16x8(qlo), S);
+            S = mfma16h(as_f16x8(hi), as_f16x8(qhi), S);
+          }
+          return S;
+        };
+        const bool has1 = t0 + 1 < ee;
+        set_q(t0 * kBlock + d0);
+        const f32x4 S0 = scores(0);
+        f32x4 S1 = {};
+        if (has1) {
+          set_q((t0 + 1) * kBlock + d1);
+          S1 = scores(1);
         }
+        float sc[8];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          const int nv = b ? (has1 ? gcur.nval[1] : 0) : gcur.nval[0];
+          const int offb = (t0 + b) * kBlock + (b ? d1 : d0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int j = 4 * q4 + i;
+            const float v = b ? S1[i] : S0[i];
+            const bool ok = j < nv && offb + j <= p;
+            sc[4 * b + i] = ok ? v * P.scale_log2 + (ALIBI ? sl2 * (float)(offb + j - p) : 0.f)
+                               : -INFINITY;
+            mx = fmaxf(mx, sc[4 * b + i]);
+          }
+        }
+        // row max over the 4 lanes of head g (slot groups q4)
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m, mx);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = exp2f(m - m_use);
+        float pr[8];
+        float rsum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) { pr[i] = exp2f(sc[i] - m_use); rsum += pr[i]; }
+        l = l * alpha + rsum;
+        m = m_new;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) o[dt] *= alpha;
+        bp = u32x4{pack_bf16(pr[0], pr[1]), pack_bf16(pr[2], pr[3]), pack_bf16(pr[4], pr[5]),
+                   pack_bf16(pr[6], pr[7])};
       }
-      const int nv = ph ? gcur.nval[1] : gcur.nval[0];
-      const int offp = (t0 + ph) * kBlock + (ph ? d1 : d0);
-      float sc[4];
-      float mx = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = 4 * q4 + i;
-        const float v = ph ? S[1][i] : S[0][i];
-        const bool ok = col_ok && j < nv && offp + j <= p;
-        sc[i] = ok ? v * P.scale_log2 + (ALIBI ? sl2 * (float)(offp + j - p) : 0.f) : -INFINITY;
-        mx = fmaxf(mx, sc[i]);
-      }
-      // row max over the 8 lanes of head g: slot groups (q4) and both phases
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      mx = fmaxf(mx, __shfl_xor(mx, G));
-      const float m_new = fmaxf(m, mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = exp2f(m - m_use);
-      float pr[4];
-      float rsum = 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) { pr[i] = exp2f(sc[i] - m_use); rsum += pr[i]; }
-      l = l * alpha + rsum;
-      m = m_new;
-#pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) o[dt] *= alpha;
-      const uint32_t p01 = pack_bf16(pr[0], pr[1]), p23 = pack_bf16(pr[2], pr[3]);
-      const u32x4 bp = ph ? u32x4{0u, 0u, p01, p23} : u32x4{p01, p23, 0u, 0u};
 
       // ---- O^T += V^T P^T over the group's 32 keys ------------------------------------------
       const uint8_t* vb = lds + buf * BUF;
@@ -327,11 +442,11 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 2) void decode_kernel(DecodePara
     // ---- partial of this item: add both phases of head g -----------------------------------
     float lt = l + __shfl_xor(l, 16);
     lt += __shfl_xor(lt, 32);
-    lt += __shfl_xor(lt, G);
+    if (PHC) lt += __shfl_xor(lt, G);
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[dt][i] += __shfl_xor(o[dt][i], G);
+      for (int i = 0; PHC && i < 4; ++i) o[dt][i] += __shfl_xor(o[dt][i], G);
     if (col < G) {
       float* part = P.partials + ((size_t)rs * P.Hq + h) * (D + 4);
 #pragma unroll
@@ -366,6 +481,7 @@ static hipError_t launch_dr(const DecodeParams& p, int G, hipStream_t st) {
     case 2: hipLaunchKernelGGL((decode_kernel<D, 2, PE>), grid, block, 0, st, p); break;
     case 4: hipLaunchKernelGGL((decode_kernel<D, 4, PE>), grid, block, 0, st, p); break;
     case 8: hipLaunchKernelGGL((decode_kernel<D, 8, PE>), grid, block, 0, st, p); break;
+    case 16: hipLaunchKernelGGL((decode_kernel<D, 16, PE>), grid, block, 0, st, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -675,6 +675,7 @@ static hipError_t launch_d(const PrefillParams& p, int G, int pe, hipStream_t st
     case 2: return launch_dg<D, 2>(p, pe, st);
     case 4: return launch_dg<D, 4>(p, pe, st);
     case 8: return launch_dg<D, 8>(p, pe, st);
+    case 16: return launch_dg<D, 16>(p, pe, st);
   }
   return hipErrorInvalidValue;
 }

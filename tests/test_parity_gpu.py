@@ -95,6 +95,15 @@ def _mini_cases():
         [Segment("private", 7 + 32 * 9, tokens=150)]
     cases.append(("many-tiles-ragged", dict(Hq=8, Hkv=2, D=128, segs=segs_long, q_len=150,
                                             seed=6)))
+    # 16 query heads per KV head (decode: heads in the 16 MFMA columns, q' set per block)
+    cases.append(("gaps-D128-G16", dict(Hq=16, Hkv=1, D=128, seed=21)))
+    cases.append(("gaps-D64-G16", dict(Hq=32, Hkv=2, D=64, seed=22)))
+    cases.append(("overlap-repeat-partial-G16", dict(Hq=16, Hkv=1, D=128, segs=segs_overlap,
+                                                     q_len=21, seed=23, q_scale=4.0)))
+    cases.append(("positions-above-2^15-G16", dict(Hq=16, Hkv=1, D=128, segs=segs_far,
+                                                   q_len=37, seed=24, q_scale=4.0)))
+    cases.append(("many-tiles-ragged-G16", dict(Hq=32, Hkv=2, D=128, segs=segs_long,
+                                                q_len=150, seed=25)))
     return cases
 
 
@@ -434,6 +443,28 @@ def test_full_size_variants(name, kind, variant):
         seqs = [0, wl.num_seqs - 1]
     g, w = _sampled(wl, kind, seqs, rows, **opt)
     compare(g, w, f"{name}/{variant}")
+
+
+@pytest.mark.parametrize("kind", ["prefill", "decode"])
+def test_gqa16_405b_shape(kind):
+    """128 query heads over 8 KV heads (G = 16), head dim 128: 12 requests of 6 Zipf
+    documents x 512 tokens at per-request offsets plus a 48-token question; sampled rows."""
+    rng = np.random.default_rng(31)
+    reqs = []
+    for r in range(12):
+        start = int(rng.integers(0, 512))
+        docs = rng.choice(40, size=6, replace=False)
+        segs = [Segment("doc", start + 512 * i, doc=int(d)) for i, d in enumerate(docs)]
+        segs.append(Segment("private", start + 512 * 6, tokens=48))
+        reqs.append(RequestLayout(segs, 48 if kind == "prefill" else 1))
+    wl = build("gqa16", 128, 8, 128, 16, 10000.0, 40, 512, reqs, seed=32)
+    say(f"G = 16 (128 q / 8 kv heads) via {kind}")
+
+    def rows(s):
+        q0, q1 = wl.q_indptr[s], wl.q_indptr[s + 1]
+        return np.array([q0]) if q1 - q0 == 1 else q0 + np.array([0, 17, 47])
+    g, w = _sampled(wl, kind, [0, 5, 11], rows)
+    compare(g, w, f"gqa16/{kind}")
 
 
 @pytest.mark.gpu
