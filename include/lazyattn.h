@@ -24,7 +24,8 @@
  *    are limited to pointers, alignment and scalar sizes.
  *  - bf16 is IEEE-754 binary32 truncated to its upper 16 bits (round to nearest even).
  *  - Supported shapes: head dim D in {64, 128}; block size B = 16 tokens; Hq % Hkv == 0 with
- *    G = Hq / Hkv in {1, 2, 4, 8, 16}; rope_base > 1.
+ *    G = Hq / Hkv in {1, 2, 4, 8} or a multiple of 16 (16, 32, 48, 64, ...: MQA-style
+ *    groups); rope_base > 1.
  *  - RoPE: rotate-half pairing (dim k with k + D/2), angle n * theta_k,
  *    theta_k = rope_base^(-2k/D); softmax scale 1/sqrt(D).
  *  - Query head h reads key/value head floor(h / G).

@@ -19,8 +19,13 @@ bool shape_ok(int32_t Hq, int32_t Hkv, int32_t D, int32_t B) {
   if (B != kBlock) return false;
   if (Hkv <= 0 || Hq <= 0 || Hq % Hkv) return false;
   const int G = Hq / Hkv;
-  return G == 1 || G == 2 || G == 4 || G == 8 || G == 16;
+  return G == 1 || G == 2 || G == 4 || G == 8 || G % 16 == 0;
 }
+
+// Query heads per KV head as the kernels see them: G itself up to 16; G = 16 S splits each
+// KV head into S work heads of 16 query heads that read the same pool head.
+int work_group(int Hq, int Hkv) { const int G = Hq / Hkv; return G > 16 ? 16 : G; }
+int work_heads(int Hq, int Hkv) { return Hq / work_group(Hq, Hkv); }
 
 // Decode split size (blocks per item, even, at least 8). The (row-split, kv-head) items are
 // dealt round-robin to the W resident decode waves, so the choice aims at an item count that
@@ -56,7 +61,7 @@ DecodeSplit decode_split(int rows_bound, int Hkv, int max_entries) {
 }
 
 size_t workspace_for(int num_seqs, int rows_bound, int max_entries, int Hq, int Hkv, int D) {
-  const DecodeSplit ds = decode_split(rows_bound, Hkv, max_entries);
+  const DecodeSplit ds = decode_split(rows_bound, work_heads(Hq, Hkv), max_entries);
   return ws_layout(num_seqs, (long long)rows_bound * ds.smax, Hq, D).total;
 }
 
@@ -93,8 +98,8 @@ int run(const void* q, const void* k_pool, const void* v_pool, const int32_t* bl
   if (num_seqs == 0 || total_q == 0) return LAZYATTN_OK;
 
   hipStream_t st = (hipStream_t)stream;
-  const int G = Hq / Hkv;
-  const DecodeSplit ds = decode_split(rows_bound, Hkv, max_entries);
+  const int G = work_group(Hq, Hkv), Hw = work_heads(Hq, Hkv), kv_group = Hw / Hkv;
+  const DecodeSplit ds = decode_split(rows_bound, Hw, max_entries);
   const WsLayout L = ws_layout(num_seqs, (long long)rows_bound * ds.smax, Hq, D);
   char* ws = (char*)workspace;
   double* freqs = (double*)(ws + L.off_freqs);
@@ -115,17 +120,17 @@ int run(const void* q, const void* k_pool, const void* v_pool, const int32_t* bl
   if (mode == kPlanMixed) {
     const int pos = prefill_positions_per_tile(G);
     const long long tiles = ((long long)total_q + pos - 1) / pos + num_seqs;
-    if (tiles * Hkv > INT32_MAX / 2) return LAZYATTN_ERR_SHAPE;
+    if (tiles * Hw > INT32_MAX / 2) return LAZYATTN_ERR_SHAPE;
     PrefillParams P{(const uint16_t*)q, (const uint16_t*)k_pool, (const uint16_t*)v_pool,
                     block_table, block_meta, kv_lens, q_indptr, q_positions,
-                    (uint16_t*)out, pf_prefix, (const uint16_t*)zero, num_seqs, Hq, Hkv,
-                    num_blocks, (int)tiles, scale_log2, freqs, slopes};
+                    (uint16_t*)out, pf_prefix, (const uint16_t*)zero, num_seqs, Hq, Hw,
+                    num_blocks, (int)tiles, scale_log2, freqs, slopes, Hkv, kv_group};
     if (launch_prefill(P, D, G, pe, st) != hipSuccess) return LAZYATTN_ERR_LAUNCH;
   }
   DecodeParams Dp{(const uint16_t*)q, (const uint16_t*)k_pool, (const uint16_t*)v_pool,
                   block_table, block_meta, kv_lens, q_indptr, q_positions, dec_prefix,
-                  (const uint16_t*)zero, partials, num_seqs, Hq, Hkv, num_blocks,
-                  ds.bps, ds.smax, scale_log2, freqs, slopes};
+                  (const uint16_t*)zero, partials, num_seqs, Hq, Hw, num_blocks,
+                  ds.bps, ds.smax, scale_log2, freqs, slopes, Hkv, kv_group};
   if (launch_decode(Dp, D, G, pe, st) != hipSuccess) return LAZYATTN_ERR_LAUNCH;
   MergeParams Mp{q_indptr, block_table, dec_prefix, partials, (uint16_t*)out,
                  num_seqs, Hq, ds.bps, ds.smax, mode};

@@ -113,12 +113,14 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 2) void decode_kernel(DecodePara
   const int gw = blockIdx.x * kDecodeWaves + w;      // this wave's index
   // items gw + i W, i = 0, 1, ...; described 64 at a time, item gw + (64 rd + k) W by lane k
   for (int base = gw; base < n_items; base += 64 * W) {
-    int x_rs = 0, x_kvh = 0, x_r = 0, x_p = 0, x_e0 = 0, x_kvlen = 0, x_eb = 0, x_ee = 0;
+    int x_rs = 0, x_kvh = 0, x_kvp = 0, x_r = 0, x_p = 0, x_e0 = 0, x_kvlen = 0, x_eb = 0,
+        x_ee = 0;
     {
       const int itl = base + lane * W;
       if (itl < n_items) {
         x_rs = itl / P.Hkv;
         x_kvh = itl - x_rs * P.Hkv;
+        x_kvp = x_kvh / P.kv_group;                   // pool head of this work head
         const int seq = upper_seq(P.dec_prefix, P.num_seqs, x_rs);
         const int local = x_rs - P.dec_prefix[seq];
         x_e0 = P.block_table[seq];
@@ -139,7 +141,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 2) void decode_kernel(DecodePara
     u32x4 kcur[2][NC], knext[2][NC];
     GroupMeta gcur, gnext;
     for (int k = 0; k < n_here; ++k) {
-    const int rs = rl(x_rs, k), kvh = rl(x_kvh, k);
+    const int rs = rl(x_rs, k), kvh = rl(x_kvh, k), kvp = rl(x_kvp, k);
     const int e0 = rl(x_e0, k), kvlen = rl(x_kvlen, k);
     const int eb = rl(x_eb, k), ee = rl(x_ee, k);
     const int r = rl(x_r, k), p = rl(x_p, k);
@@ -156,7 +158,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 2) void decode_kernel(DecodePara
     int cur_delta = 0;
 
     // issue the loads of the group starting at entry t0 of an item (entries below i_ee,
-    // words from i_e0, kv-head i_kvh, i_kvlen keys) into LDS buffer `buf`
+    // words from i_e0, pool head i_kvh, i_kvlen keys) into LDS buffer `buf`
     auto issue = [&](int t0, int i_ee, int i_e0, int i_kvh, int i_kvlen, int buf,
                      u32x4 (&kreg)[2][NC], GroupMeta& gm) {
 #pragma unroll
@@ -169,7 +171,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 2) void decode_kernel(DecodePara
         gm.id[b] = id;
         gm.delta[b] = word_delta(wd);
         gm.nval[b] = (blk && id < P.num_blocks) ? (rem < kBlock ? (rem > 0 ? rem : 0) : kBlock) : 0;
-        const size_t kb = ((size_t)id * P.Hkv + i_kvh) * kBlock;
+        const size_t kb = ((size_t)id * P.Hkv_pool + i_kvh) * kBlock;
 #pragma unroll
         for (int c = 0; c < NC; ++c)
           kreg[b][c] = i16 < gm.nval[b]
@@ -184,12 +186,12 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 2) void decode_kernel(DecodePara
         const int c = cs ^ vswz(R);
         const void* src = P.zero;
         if (j < gm.nval[b])
-          src = P.v_pool + (((size_t)gm.id[b] * P.Hkv + i_kvh) * kBlock + j) * D + 8 * c;
+          src = P.v_pool + (((size_t)gm.id[b] * P.Hkv_pool + i_kvh) * kBlock + j) * D + 8 * c;
         g2lds16(src, lds + buf * BUF + i * 1024);
       }
     };
 
-    if (!pre && eb < ee) issue(eb, ee, e0, kvh, kvlen, buf, knext, gnext);
+    if (!pre && eb < ee) issue(eb, ee, e0, kvp, kvlen, buf, knext, gnext);
     pre = false;
     for (int t0 = eb; t0 < ee; t0 += 2) {
       __builtin_amdgcn_s_waitcnt(0x0F70);       // vmcnt(0): this group's keys and values
@@ -201,11 +203,11 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 2) void decode_kernel(DecodePara
         for (int c = 0; c < NC; ++c) kcur[b][c] = knext[b][c];
       gcur = gnext;
       if (t0 + 2 < ee) {
-        issue(t0 + 2, ee, e0, kvh, kvlen, buf ^ 1, knext, gnext);
+        issue(t0 + 2, ee, e0, kvp, kvlen, buf ^ 1, knext, gnext);
       } else if (k + 1 < n_here) {                    // the next item's first group
         const int n_eb = rl(x_eb, k + 1), n_ee = rl(x_ee, k + 1);
         if (n_eb < n_ee) {
-          issue(n_eb, n_ee, rl(x_e0, k + 1), rl(x_kvh, k + 1), rl(x_kvlen, k + 1), buf ^ 1,
+          issue(n_eb, n_ee, rl(x_e0, k + 1), rl(x_kvp, k + 1), rl(x_kvlen, k + 1), buf ^ 1,
                 knext, gnext);
           pre = true;
         }

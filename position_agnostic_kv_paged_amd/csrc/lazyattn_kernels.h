@@ -37,7 +37,12 @@ struct PrefillParams {
   float scale_log2;          // log2(e) / sqrt(D)
   const double* freqs;       // [D/2] RoPE frequencies (revolutions per position)
   const float* slopes;       // [Hq] ALiBi slopes (positional encoding kAlibi only)
+  int Hkv_pool, kv_group;    // pool KV heads; work heads per pool head (see below)
 };
+
+// More than 16 query heads per KV head (G = 16 S): the kernels run Hkv * S "work heads" of
+// 16 query heads each; work head v reads pool head v / S (kv_group = S). Otherwise
+// kv_group = 1 and Hkv_pool = Hkv.
 
 struct DecodeParams {
   const uint16_t* q;
@@ -55,6 +60,7 @@ struct DecodeParams {
   float scale_log2;
   const double* freqs;
   const float* slopes;       // [Hq] ALiBi slopes (positional encoding kAlibi only)
+  int Hkv_pool, kv_group;    // as in PrefillParams
 };
 
 struct MergeParams {

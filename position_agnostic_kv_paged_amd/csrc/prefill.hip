@@ -167,6 +167,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
   const int rho = 32 * w + col;
   const int qi = qt * POS + rho / G;
   const int h = kvh * G + rho % G;
+  const int kvp = kvh / P.kv_group;                          // pool head of this work head
   const bool row_ok = qi < qlen;
   const int p = row_ok ? P.q_pos[q0 + qi] : INT_MIN;       // invalid rows see no key
 
@@ -286,7 +287,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
     const int nv = b == 0 ? n0 : b == 1 ? n1 : b == 2 ? n2 : n3;
     const int id = b == 0 ? i0 : b == 1 ? i1 : b == 2 ? i2 : i3;
     const void* src = blend_ptr((c < D / 8) & (j < nv),
-                                P.v_pool + (((size_t)id * P.Hkv + kvh) * kBlock + j) * D + 8 * c,
+                                P.v_pool + (((size_t)id * P.Hkv_pool + kvp) * kBlock + j) * D + 8 * c,
                                 P.zero);
     g2lds16p(src, Vs[buf] + I * 1024);
   };
@@ -302,7 +303,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
     const int nv = rl(wd.nv, 4 * d + kb), id = rl(wd.id, 4 * d + kb);
     // branch-free: empty slots load from the zeroed workspace chunk
     const uint16_t* src = (const uint16_t*)blend_ptr(
-        kj < nv, P.k_pool + (((size_t)id * P.Hkv + kvh) * kBlock + kj) * D + FPT * cp, P.zero);
+        kj < nv, P.k_pool + (((size_t)id * P.Hkv_pool + kvp) * kBlock + kj) * D + FPT * cp, P.zero);
     klo = *(const KRaw*)src;
     khi = *(const KRaw*)(src + HALF);
   };

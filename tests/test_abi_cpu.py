@@ -81,7 +81,8 @@ def test_argument_validation_without_gpu(L, fn):
     assert _call(lib, fn, D=96) == -3
     assert _call(lib, fn, B=32) == -3
     assert _call(lib, fn, Hq=12, Hkv=8) == -3
-    assert _call(lib, fn, Hq=96, Hkv=3) == -3          # G = 32 unsupported
+    assert _call(lib, fn, Hq=24, Hkv=1) == -3          # G = 24: not 1, 2, 4, 8 or 16 S
+    assert _call(lib, fn, Hq=96, Hkv=2, D=96) == -3    # G = 48 is fine, D = 96 is not
     assert _call(lib, fn, S=-1) == -3
     assert _call(lib, fn, NB=(1 << 17) + 1) == -3
     assert _call(lib, fn, base=1.0) == -7

@@ -104,6 +104,14 @@ def _mini_cases():
                                                    q_len=37, seed=24, q_scale=4.0)))
     cases.append(("many-tiles-ragged-G16", dict(Hq=32, Hkv=2, D=128, segs=segs_long,
                                                 q_len=150, seed=25)))
+    # more than 16 query heads per KV head (multi-query attention): each KV head is split
+    # into 16-head groups that read the same pool head
+    cases.append(("gaps-D128-G32", dict(Hq=32, Hkv=1, D=128, seed=41)))
+    cases.append(("gaps-D64-G32-2kv", dict(Hq=64, Hkv=2, D=64, seed=42)))
+    cases.append(("overlap-repeat-partial-G64", dict(Hq=64, Hkv=1, D=128, segs=segs_overlap,
+                                                     q_len=21, seed=43, q_scale=4.0)))
+    cases.append(("many-tiles-ragged-G48", dict(Hq=48, Hkv=1, D=128, segs=segs_long,
+                                                q_len=150, seed=44)))
     return cases
 
 
