@@ -174,6 +174,32 @@ int lazyattn_decode_freqs(const void* q, const void* k_pool, const void* v_pool,
                           void* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * lazyattn_prefill_partial / lazyattn_decode_partial -- the same calls with partial rotary
+ * RoPE (technical summary, "Key Contributions": compatibility with RoPE variants): only the
+ * first rotary_dim dims of q and k are rotated, rotate-half inside them (dim k paired with
+ * k + rotary_dim/2, theta_k = rope_base^(-2k / rotary_dim), k < rotary_dim/2); dims
+ * rotary_dim .. D-1 enter the scores unrotated. This is the convention of GPT-NeoX-style
+ * models with a rotary fraction below 1. q and the pool keep the natural dim order; the
+ * softmax scale stays 1/sqrt(D). rotary_dim must be a multiple of 16 in [16, D]
+ * (LAZYATTN_ERR_ARG otherwise); rotary_dim = D gives lazyattn_prefill / lazyattn_decode.
+ * Other arguments, ownership and errors as lazyattn_prefill / lazyattn_decode.
+ */
+int lazyattn_prefill_partial(const void* q, const void* k_pool, const void* v_pool,
+                             const int32_t* block_table, const uint32_t* block_meta,
+                             const int32_t* kv_lens, const int32_t* q_indptr,
+                             const int32_t* q_positions, double rope_base, int32_t rotary_dim,
+                             int32_t num_seqs, int32_t total_q, int32_t Hq, int32_t Hkv,
+                             int32_t D, int32_t B, int32_t num_blocks, int32_t max_entries,
+                             void* out, void* workspace, size_t workspace_bytes, void* stream);
+int lazyattn_decode_partial(const void* q, const void* k_pool, const void* v_pool,
+                            const int32_t* block_table, const uint32_t* block_meta,
+                            const int32_t* kv_lens, const int32_t* q_indptr,
+                            const int32_t* q_positions, double rope_base, int32_t rotary_dim,
+                            int32_t num_seqs, int32_t total_q, int32_t Hq, int32_t Hkv,
+                            int32_t D, int32_t B, int32_t num_blocks, int32_t max_entries,
+                            void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * lazyattn_prefill_alibi / lazyattn_decode_alibi -- the same calls over the same
  * position-free pool with ALiBi instead of RoPE (technical summary, "Key Contributions":
  * compatibility with ALiBi). Nothing is rotated; a query of head h at logical position p

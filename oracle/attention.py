@@ -29,13 +29,15 @@ def bf16_bits_to_f64(bits) -> np.ndarray:
     return b.view(np.float32).astype(np.float64)
 
 
-def materialise(k_pool, v_pool, block_ids, offsets, kv_len, B, base, rotate_keys=True):
+def materialise(k_pool, v_pool, block_ids, offsets, kv_len, B, base, rotate_keys=True,
+                rotary_dim=None):
     """Copy a sequence's blocks into logical order with eager RoPE on keys.
 
     k_pool, v_pool: uint16 bf16 bits [num_blocks, Hkv, B, D] (or float arrays).
     block_ids, offsets: per-entry physical block id and logical offset of slot 0.
     rotate_keys=False reads a pool whose keys already carry R(L) (the materialised
     baseline the method is compared with): keys are then used as stored.
+    rotary_dim: partial rotary (only the first rotary_dim dims rotated; rope.rotate).
     Returns K_hat [Hkv, n, D] float64 (rotated), V_hat [Hkv, n, D], key_pos [n].
     """
     T = len(block_ids)
@@ -55,7 +57,7 @@ def materialise(k_pool, v_pool, block_ids, offsets, kv_len, B, base, rotate_keys
         if vb.dtype == np.uint16:
             vb = bf16_bits_to_f64(vb)
         pos = int(offsets[t]) + np.arange(n_t, dtype=np.int64)
-        ks.append(rotate(kb, pos[None, :], base) if rotate_keys
+        ks.append(rotate(kb, pos[None, :], base, rotary_dim) if rotate_keys
                   else np.asarray(kb, dtype=np.float64))
         vs.append(np.asarray(vb, dtype=np.float64))
         ps.append(pos)
@@ -90,13 +92,13 @@ def attend(q_rot, q_pos, K_hat, V_hat, key_pos):
     return out
 
 
-def _rot_queries(q, q_pos, base):
+def _rot_queries(q, q_pos, base, rotary_dim=None):
     qf = bf16_bits_to_f64(q) if q.dtype == np.uint16 else np.asarray(q, np.float64)
-    return rotate(qf, np.asarray(q_pos, dtype=np.int64)[:, None], base)
+    return rotate(qf, np.asarray(q_pos, dtype=np.int64)[:, None], base, rotary_dim)
 
 
 def lazy_attention(q, k_pool, v_pool, seq_block_ids, seq_offsets, kv_lens,
-                   q_indptr, q_pos, base, B, rotate_keys=True):
+                   q_indptr, q_pos, base, B, rotate_keys=True, rotary_dim=None):
     """Whole-batch reference output, float64 [total_q, Hq, D].
 
     q: bf16 bits [total_q, Hq, D]; seq_block_ids / seq_offsets: one array per
@@ -111,14 +113,14 @@ def lazy_attention(q, k_pool, v_pool, seq_block_ids, seq_offsets, kv_lens,
             continue
         K_hat, V_hat, key_pos = materialise(
             k_pool, v_pool, seq_block_ids[s], seq_offsets[s], int(kv_lens[s]), B, base,
-            rotate_keys)
-        qr = _rot_queries(q[r0:r1], q_pos[r0:r1], base)
+            rotate_keys, rotary_dim)
+        qr = _rot_queries(q[r0:r1], q_pos[r0:r1], base, rotary_dim)
         out[r0:r1] = attend(qr, q_pos[r0:r1], K_hat, V_hat, key_pos)
     return out
 
 
 def attention_rows(q, k_pool, v_pool, seq_block_ids, seq_offsets, kv_lens,
-                   q_indptr, q_pos, base, B, seq, rows, rotate_keys=True):
+                   q_indptr, q_pos, base, B, seq, rows, rotate_keys=True, rotary_dim=None):
     """Reference output of selected query rows (global row indices) of one sequence."""
     rows = np.asarray(rows, dtype=np.int64)
     r0, r1 = int(q_indptr[seq]), int(q_indptr[seq + 1])
@@ -126,8 +128,8 @@ def attention_rows(q, k_pool, v_pool, seq_block_ids, seq_offsets, kv_lens,
         raise ValueError("rows must belong to the sequence")
     K_hat, V_hat, key_pos = materialise(
         k_pool, v_pool, seq_block_ids[seq], seq_offsets[seq], int(kv_lens[seq]), B, base,
-        rotate_keys)
-    qr = _rot_queries(q[rows], q_pos[rows], base)
+        rotate_keys, rotary_dim)
+    qr = _rot_queries(q[rows], q_pos[rows], base, rotary_dim)
     return attend(qr, q_pos[rows], K_hat, V_hat, key_pos)
 
 

@@ -48,17 +48,25 @@ def llama31_scale(theta, factor=8.0, low_freq_factor=1.0, high_freq_factor=4.0,
     return np.array(out)
 
 
-def rotate(x: np.ndarray, pos, base) -> np.ndarray:
+def rotate(x: np.ndarray, pos, base, rotary_dim=None) -> np.ndarray:
     """Apply R(pos) to the last axis of x (float64); base: a RoPE base or the theta table.
 
     x: [..., D]; pos: integer array broadcastable to x.shape[:-1].
     y_k        = x_k cos(pos theta_k) - x_{k+D/2} sin(pos theta_k)
     y_{k+D/2}  = x_k sin(pos theta_k) + x_{k+D/2} cos(pos theta_k)
+
+    Partial rotary (rotary_dim = r < D; the form GPT-NeoX-style models use when only a
+    fraction of each head is rotated): the formulas above act on the first r dims alone,
+    with r in place of D (pairs k, k + r/2; theta_k = base^(-2k/r), k < r/2), and dims
+    r .. D-1 are returned unchanged. A theta table then holds r/2 values.
     """
     x = np.asarray(x, dtype=np.float64)
     D = x.shape[-1]
-    h = D // 2
-    ang = np.asarray(pos, dtype=np.float64)[..., None] * inv_freq(D, base)
+    r = D if rotary_dim is None else int(rotary_dim)
+    if r % 2 or not 0 < r <= D:
+        raise ValueError("rotary_dim must be even and in (0, D]")
+    h = r // 2
+    ang = np.asarray(pos, dtype=np.float64)[..., None] * inv_freq(r, base)
     c, s = np.cos(ang), np.sin(ang)
-    a, b = x[..., :h], x[..., h:]
-    return np.concatenate([a * c - b * s, a * s + b * c], axis=-1)
+    a, b = x[..., :h], x[..., h:r]
+    return np.concatenate([a * c - b * s, a * s + b * c, x[..., r:]], axis=-1)

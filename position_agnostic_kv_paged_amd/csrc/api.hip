@@ -71,7 +71,7 @@ int run(const void* q, const void* k_pool, const void* v_pool, const int32_t* bl
         int32_t Hq, int32_t Hkv, int32_t D, int32_t B, int32_t num_blocks,
         int32_t max_entries, void* out, void* workspace, size_t workspace_bytes,
         void* stream, int mode, int pe, const double* inv_freq = nullptr,
-        const float* slopes = nullptr) {
+        const float* slopes = nullptr, int rotary_dim = 0) {
   if (!q || !k_pool || !v_pool || !block_table || !block_meta || !kv_lens || !q_indptr ||
       !q_positions || !out || !workspace)
     return LAZYATTN_ERR_NULL;
@@ -88,6 +88,8 @@ int run(const void* q, const void* k_pool, const void* v_pool, const int32_t* bl
   } else if (!(rope_base > 1.0) || !std::isfinite(rope_base)) {
     return LAZYATTN_ERR_ARG;
   }
+  if (pe == kRopePartial && (rotary_dim < 16 || rotary_dim > D || rotary_dim % 16))
+    return LAZYATTN_ERR_ARG;
   if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(out, 16) ||
       !aligned(workspace, 16) || !aligned(block_table, 4) || !aligned(block_meta, 4) ||
       !aligned(kv_lens, 4) || !aligned(q_indptr, 4) || !aligned(q_positions, 4))
@@ -108,9 +110,15 @@ int run(const void* q, const void* k_pool, const void* v_pool, const int32_t* bl
   int32_t* dec_prefix = (int32_t*)(ws + L.off_dec_prefix);
   float* partials = (float*)(ws + L.off_partials);
 
-  RopeFreqs fr{};                                   // (unused with ALiBi: all zero)
+  // RoPE frequencies in revolutions per position (unused with ALiBi: all zero). Partial
+  // rotary: theta_k = base^(-2k/r) for the r/2 rotated pairs, zero for the pass-through
+  // pairs of the permuted dim order (nat_chunk).
+  RopeFreqs fr{};
+  const int r = pe == kRopePartial ? rotary_dim : D;
   for (int k = 0; pe != kAlibi && k < D / 2; ++k)
-    fr.f[k] = (inv_freq ? inv_freq[k] : std::pow(rope_base, -2.0 * k / D)) / (2.0 * M_PI);
+    fr.f[k] = k < r / 2 ? (inv_freq ? inv_freq[k] : std::pow(rope_base, -2.0 * k / r)) /
+                              (2.0 * M_PI)
+                        : 0.0;
   const float scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
 
   PlanParams pp{q_indptr, block_table, freqs, pf_prefix, dec_prefix, zero, num_seqs,
@@ -124,13 +132,13 @@ int run(const void* q, const void* k_pool, const void* v_pool, const int32_t* bl
     PrefillParams P{(const uint16_t*)q, (const uint16_t*)k_pool, (const uint16_t*)v_pool,
                     block_table, block_meta, kv_lens, q_indptr, q_positions,
                     (uint16_t*)out, pf_prefix, (const uint16_t*)zero, num_seqs, Hq, Hw,
-                    num_blocks, (int)tiles, scale_log2, freqs, slopes, Hkv, kv_group};
+                    num_blocks, (int)tiles, scale_log2, freqs, slopes, Hkv, kv_group, r / 16};
     if (launch_prefill(P, D, G, pe, st) != hipSuccess) return LAZYATTN_ERR_LAUNCH;
   }
   DecodeParams Dp{(const uint16_t*)q, (const uint16_t*)k_pool, (const uint16_t*)v_pool,
                   block_table, block_meta, kv_lens, q_indptr, q_positions, dec_prefix,
                   (const uint16_t*)zero, partials, num_seqs, Hq, Hw, num_blocks,
-                  ds.bps, ds.smax, scale_log2, freqs, slopes, Hkv, kv_group};
+                  ds.bps, ds.smax, scale_log2, freqs, slopes, Hkv, kv_group, r / 16};
   if (launch_decode(Dp, D, G, pe, st) != hipSuccess) return LAZYATTN_ERR_LAUNCH;
   MergeParams Mp{q_indptr, block_table, dec_prefix, partials, (uint16_t*)out,
                  num_seqs, Hq, ds.bps, ds.smax, mode};
@@ -240,6 +248,32 @@ int lazyattn_decode_alibi(const void* q, const void* k_pool, const void* v_pool,
   return run(q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indptr, q_positions, 0.0,
              num_seqs, total_q, Hq, Hkv, D, B, num_blocks, max_entries, out, workspace,
              workspace_bytes, stream, kPlanDecodeOnly, kAlibi, nullptr, slopes);
+}
+
+int lazyattn_prefill_partial(const void* q, const void* k_pool, const void* v_pool,
+                             const int32_t* block_table, const uint32_t* block_meta,
+                             const int32_t* kv_lens, const int32_t* q_indptr,
+                             const int32_t* q_positions, double rope_base, int32_t rotary_dim,
+                             int32_t num_seqs, int32_t total_q, int32_t Hq, int32_t Hkv,
+                             int32_t D, int32_t B, int32_t num_blocks, int32_t max_entries,
+                             void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  return run(q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indptr, q_positions,
+             rope_base, num_seqs, total_q, Hq, Hkv, D, B, num_blocks, max_entries, out,
+             workspace, workspace_bytes, stream, kPlanMixed, kRopePartial, nullptr, nullptr,
+             rotary_dim);
+}
+
+int lazyattn_decode_partial(const void* q, const void* k_pool, const void* v_pool,
+                            const int32_t* block_table, const uint32_t* block_meta,
+                            const int32_t* kv_lens, const int32_t* q_indptr,
+                            const int32_t* q_positions, double rope_base, int32_t rotary_dim,
+                            int32_t num_seqs, int32_t total_q, int32_t Hq, int32_t Hkv,
+                            int32_t D, int32_t B, int32_t num_blocks, int32_t max_entries,
+                            void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  return run(q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indptr, q_positions,
+             rope_base, num_seqs, total_q, Hq, Hkv, D, B, num_blocks, max_entries, out,
+             workspace, workspace_bytes, stream, kPlanDecodeOnly, kRopePartial, nullptr,
+             nullptr, rotary_dim);
 }
 
 size_t lazyattn_prefill_workspace_bytes(int32_t num_seqs, int32_t total_q, int32_t max_entries,

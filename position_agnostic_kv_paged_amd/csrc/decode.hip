@@ -62,7 +62,8 @@ struct GroupMeta {
 // score, L = off_t + j from the packed word.
 template <int D, int G, int PE>
 __global__ __launch_bounds__(kDecodeWaves * 64, 2) void decode_kernel(DecodeParams P) {
-  constexpr bool ROT = PE == kRope;
+  constexpr bool PART = PE == kRopePartial;   // dims in the permuted order of nat_chunk
+  constexpr bool ROT = PE == kRope || PART;
   constexpr bool ALIBI = PE == kAlibi;
   // PHC: the 16 columns of the score MFMA hold (head, block phase) pairs (2 G <= 16), so
   // both blocks of a group are scored against one q' operand. Otherwise (G = 16) the
@@ -88,6 +89,11 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 2) void decode_kernel(DecodePara
   const int i16 = lane & 15, q4 = lane >> 4;
   const int col = i16, g = col % G, ph = col / G;
   const bool col_ok = col < 2 * G;
+  // element offset in a q or key row of the 8 dims this lane holds in 32-dim k-step c
+  int dofs[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+    dofs[c] = PART ? 8 * nat_chunk(4 * c + q4, P.rot_chunks, D / 16) : 32 * c + 8 * q4;
 
   // loop-invariant rotation constants, shared by the workgroup in LDS: R(j) of slot j for
   // frequencies k = 32c + 8 q4 + 2 e2 + u as float4 (cos, sin of u = 0, 1) at
@@ -175,7 +181,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 2) void decode_kernel(DecodePara
 #pragma unroll
         for (int c = 0; c < NC; ++c)
           kreg[b][c] = i16 < gm.nval[b]
-                           ? *(const u32x4*)(P.k_pool + (kb + i16) * D + 32 * c + 8 * q4)
+                           ? *(const u32x4*)(P.k_pool + (kb + i16) * D + dofs[c])
                            : u32x4{0, 0, 0, 0};
       }
 #pragma unroll
@@ -238,9 +244,8 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 2) void decode_kernel(DecodePara
           const int n = ROT ? p - ((t0 + ph) * kBlock + (ph ? d1 : d0)) : (ALIBI ? 0 : p);
 #pragma unroll
           for (int c = 0; c < HC; ++c) {
-            const u32x4 va = col_ok ? *(const u32x4*)(qrow + 32 * c + 8 * q4) : u32x4{0, 0, 0, 0};
-            const u32x4 vb = col_ok ? *(const u32x4*)(qrow + 32 * (c + HC) + 8 * q4)
-                                    : u32x4{0, 0, 0, 0};
+            const u32x4 va = col_ok ? *(const u32x4*)(qrow + dofs[c]) : u32x4{0, 0, 0, 0};
+            const u32x4 vb = col_ok ? *(const u32x4*)(qrow + dofs[c + HC]) : u32x4{0, 0, 0, 0};
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
               float cs, sn;
@@ -319,8 +324,8 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 2) void decode_kernel(DecodePara
         auto qexact = [&](int n) {
 #pragma unroll
           for (int c = 0; c < HC; ++c) {
-            const u32x4 va = *(const u32x4*)(qrow + 32 * c + 8 * q4);
-            const u32x4 vb = *(const u32x4*)(qrow + 32 * (c + HC) + 8 * q4);
+            const u32x4 va = *(const u32x4*)(qrow + dofs[c]);
+            const u32x4 vb = *(const u32x4*)(qrow + dofs[c + HC]);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
               float cs, sn;
@@ -495,6 +500,7 @@ static hipError_t launch_d(const DecodeParams& p, int G, int pe, hipStream_t st)
     case kRope: return launch_dr<D, kRope>(p, G, st);
     case kStored: return launch_dr<D, kStored>(p, G, st);
     case kAlibi: return launch_dr<D, kAlibi>(p, G, st);
+    case kRopePartial: return launch_dr<D, kRopePartial>(p, G, st);
   }
   return hipErrorInvalidValue;
 }

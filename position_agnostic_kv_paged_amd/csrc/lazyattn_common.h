@@ -221,7 +221,19 @@ __host__ __device__ inline int row_splits(int T, int bps, int smax) {
 //   kRope    position-free pool: keys and queries rotated by RoPE from logical positions
 //   kStored  materialised baseline: keys already carry R(L); queries rotated by R(p)
 //   kAlibi   position-free pool, no rotation: score + slope_h (L - p) (linear bias)
-enum PosEnc : int { kRope = 0, kStored = 1, kAlibi = 2 };
+//   kRopePartial  as kRope, with rotate-half applied inside the first rotary_dim dims only
+enum PosEnc : int { kRope = 0, kStored = 1, kAlibi = 2, kRopePartial = 3 };
+
+// Partial rotary (dims k and k + r/2 paired for k < r/2, theta_k = base^(-2k/r), dims r..D-1
+// unrotated) is computed as full rotate-half over a permuted dim order whose extra pairs have
+// frequency zero: a common permutation of q's and k's dims leaves every score unchanged.
+// The permutation moves whole 8-dim chunks. With hc = r/16 and Hc = D/16, the kernels' chunk
+// kc holds natural chunk nat_chunk(kc): chunks below hc stay, the pass-through chunks
+// r/8 .. r/8 + Hc - hc - 1 fill kernel chunks hc .. Hc - 1, the rotary partners hc .. 2hc - 1
+// move to Hc .. Hc + hc - 1, and the rest stays. hc = Hc is the identity.
+__host__ __device__ inline int nat_chunk(int kc, int hc, int Hc) {
+  return kc < hc ? kc : kc < Hc ? kc + hc : kc < Hc + hc ? kc - Hc + hc : kc;
+}
 
 __device__ __forceinline__ uint32_t f16_bits(float x) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);

@@ -38,6 +38,7 @@ struct PrefillParams {
   const double* freqs;       // [D/2] RoPE frequencies (revolutions per position)
   const float* slopes;       // [Hq] ALiBi slopes (positional encoding kAlibi only)
   int Hkv_pool, kv_group;    // pool KV heads; work heads per pool head (see below)
+  int rot_chunks;            // rotary_dim / 16 (kRopePartial only; nat_chunk)
 };
 
 // More than 16 query heads per KV head (G = 16 S): the kernels run Hkv * S "work heads" of
@@ -61,6 +62,7 @@ struct DecodeParams {
   const double* freqs;
   const float* slopes;       // [Hq] ALiBi slopes (positional encoding kAlibi only)
   int Hkv_pool, kv_group;    // as in PrefillParams
+  int rot_chunks;            // as in PrefillParams
 };
 
 struct MergeParams {

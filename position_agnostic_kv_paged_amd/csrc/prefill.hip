@@ -106,7 +106,8 @@ __device__ __forceinline__ TileWords tile_words(const WinDec& wd) {
 
 template <int D, int G, int PE>
 __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillParams P) {
-  constexpr bool ROTATE = PE == kRope;        // keys rotated per tile (position-free pool)
+  constexpr bool PART = PE == kRopePartial;   // dims in the permuted order of nat_chunk
+  constexpr bool ROTATE = PE == kRope || PART; // keys rotated per tile (position-free pool)
   constexpr bool ALIBI = PE == kAlibi;        // no rotation; linear bias on the scores
   constexpr int NW = kPrefillWaves;
   constexpr int NT = NW * 64;
@@ -179,7 +180,10 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
     const uint16_t* qrow = P.q + ((size_t)(q0 + (row_ok ? qi : 0)) * P.Hq + h) * D;
 #pragma unroll
     for (int c = 0; c < NCH; ++c)
-      raw[c] = row_ok ? *(const u32x4*)(qrow + 16 * c + 8 * hh) : u32x4{0, 0, 0, 0};
+      raw[c] = row_ok ? *(const u32x4*)(qrow + (PART ? 8 * nat_chunk(2 * c + hh, P.rot_chunks,
+                                                                     D / 16)
+                                                      : 16 * c + 8 * hh))
+                      : u32x4{0, 0, 0, 0};
     const int n = row_ok ? p - p_ref : 0;
     const float sc = P.scale_log2;                  // softmax scale folded into Q~
 #pragma unroll
@@ -219,6 +223,12 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
   // FPT*cp .. FPT*cp+FPT-1 (a wave's 64 threads stage keys of one block: kb is uniform)
   const int kn = tid / CPT, cp = tid % CPT;
   const int kb = __builtin_amdgcn_readfirstlane((kn >> 4) & 3), kj = kn & 15;
+  // where those dims sit in a pool row (and their rotate-half partners, k_dhi further on)
+  const int k_lo = PART ? 8 * nat_chunk(FPT * cp / 8, P.rot_chunks, D / 16) + FPT * cp % 8
+                        : FPT * cp;
+  const int k_dhi = PART ? 8 * nat_chunk(FPT * cp / 8 + D / 16, P.rot_chunks, D / 16) +
+                               FPT * cp % 8 - k_lo
+                         : HALF;
   // float2 position of frequency f of row r (a block or a slot) in the tables
   auto tpos = [&](int r, int f) {
     return ((r * (FPT / 2) + (f % FPT) / 2) * CPT + f / FPT) * 2 + (f & 1);
@@ -301,11 +311,11 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
   // (key staging reads block kb of tile kt + d: lane 4 d + kb of the decoded window)
   auto load_k = [&](const WinDec& wd, int d) {
     const int nv = rl(wd.nv, 4 * d + kb), id = rl(wd.id, 4 * d + kb);
-    // branch-free: empty slots load from the zeroed workspace chunk
+    // branch-free: empty slots load from the zeroed workspace chunk (0 < k_dhi <= D/2)
     const uint16_t* src = (const uint16_t*)blend_ptr(
-        kj < nv, P.k_pool + (((size_t)id * P.Hkv_pool + kvp) * kBlock + kj) * D + FPT * cp, P.zero);
+        kj < nv, P.k_pool + (((size_t)id * P.Hkv_pool + kvp) * kBlock + kj) * D + k_lo, P.zero);
     klo = *(const KRaw*)src;
-    khi = *(const KRaw*)(src + HALF);
+    khi = *(const KRaw*)(src + k_dhi);
   };
   // rotation of frequencies 2 i2, 2 i2 + 1 of the staged key by R(off_b - p_ref) R(kj),
   // from (cos, sin) pairs read out of the tables; results packed as fp16
@@ -664,6 +674,9 @@ static hipError_t launch_dg(const PrefillParams& p, int pe, hipStream_t st) {
     case kRope: hipLaunchKernelGGL((prefill_kernel<D, G, kRope>), grid, block, 0, st, p); break;
     case kStored: hipLaunchKernelGGL((prefill_kernel<D, G, kStored>), grid, block, 0, st, p); break;
     case kAlibi: hipLaunchKernelGGL((prefill_kernel<D, G, kAlibi>), grid, block, 0, st, p); break;
+    case kRopePartial:
+      hipLaunchKernelGGL((prefill_kernel<D, G, kRopePartial>), grid, block, 0, st, p);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -18,7 +18,7 @@ def words_for(wl):
 
 
 def run_hip(wl, kind, dev="cuda", tensors=None, words=None, repeat=1, inv_freq=None,
-            slopes=None):
+            slopes=None, rotary_dim=None):
     """Call lazyattn_prefill / lazyattn_decode on the workload; returns float64 [total_q,Hq,D]."""
     import torch
     import position_agnostic_kv_paged_amd as L
@@ -33,7 +33,8 @@ def run_hip(wl, kind, dev="cuda", tensors=None, words=None, repeat=1, inv_freq=N
         out = fn(t["q"], t["k_pool"], t["v_pool"], t["block_table"], meta, t["kv_lens"],
                  t["q_indptr"], t["q_pos"], wl.rope_base, max_entries, inv_freq=inv_freq,
                  slopes=None if slopes is None else
-                 torch.as_tensor(np.asarray(slopes, np.float32), device=dev))
+                 torch.as_tensor(np.asarray(slopes, np.float32), device=dev),
+                 rotary_dim=rotary_dim)
         torch.cuda.synchronize()
         outs.append(out.float().cpu().numpy().astype(np.float64))
     return outs[0] if repeat == 1 else outs

@@ -94,6 +94,24 @@ def test_argument_validation_without_gpu(L, fn):
     assert _call(lib, fn, S=0, TQ=0) == 0
 
 
+@pytest.mark.parametrize("fn", ["lazyattn_prefill_partial", "lazyattn_decode_partial"])
+def test_partial_rotary_validation_without_gpu(L, fn):
+    """rotary_dim must be a multiple of 16 in [16, D]; errors return before any launch."""
+    lib = L.lib()
+    f = getattr(lib, fn)
+    vp = ctypes.c_void_p
+
+    def call(r, D=128, q=16, base=10000.0):
+        return f(vp(q) if q else None, vp(16), vp(16), vp(16), vp(16), vp(16), vp(16), vp(16),
+                 base, r, 1, 1, 32, 8, D, 16, 10, 4, vp(16), vp(16), 1 << 30, None)
+    for r in (0, 8, 24, 144, -16):
+        assert call(r) == -7
+    assert call(80, D=64) == -7
+    assert call(32, q=0) == -1
+    assert call(32, base=0.5) == -7
+    assert call(32, D=96) == -3
+
+
 def test_workspace_sizes(L):
     lib = L.lib()
     assert lib.lazyattn_prefill_workspace_bytes(4, 100, 10, 32, 8, 96) == 0

@@ -124,6 +124,67 @@ def test_sdpa_special_case_dense_from_zero():
     assert np.max(np.abs(got - ref)) < 1e-12
 
 
+# ---------------------------------------------------------------- partial rotary
+
+def test_partial_rotate_matches_complex_form():
+    """rotary_dim r: z_k = x_k + i x_{k+r/2} times exp(i n base^(-2k/r)) for k < r/2, the
+    other dims untouched (a frequency exponent over D instead of r, or pairs k, k + D/2,
+    would fail)."""
+    rng = np.random.default_rng(40)
+    base = 10000.0
+    for D, r in ((64, 16), (128, 32), (128, 64), (16, 2)):
+        x = rng.standard_normal((4, D))
+        pos = np.array([0, 3, 777, 40001])
+        z = x[:, : r // 2] + 1j * x[:, r // 2: r]
+        th = np.exp(-np.log(base) * 2.0 * np.arange(r // 2) / r)
+        zr = z * np.exp(1j * pos[:, None] * th[None, :])
+        want = np.concatenate([zr.real, zr.imag, x[:, r:]], axis=1)
+        got = rope.rotate(x, pos, base, rotary_dim=r)
+        assert np.max(np.abs(got - want)) < 1e-11
+        assert np.array_equal(got[:, r:], x[:, r:])
+    x = rng.standard_normal(32)
+    assert np.array_equal(rope.rotate(x, 99, base, rotary_dim=32), rope.rotate(x, 99, base))
+
+
+def test_partial_rotary_relative_identity():
+    """<R(a) q, R(b) k> = <R(a - b) q, k> also with partial rotary: the pass-through dims
+    add the same plain product on both sides."""
+    rng = np.random.default_rng(41)
+    for r in (16, 48):
+        q, k = rng.standard_normal(64), rng.standard_normal(64)
+        for a, b in ((5, 2), (100000, 31), (7, 900000)):
+            lhs = rope.rotate(q, a, 500000.0, r) @ rope.rotate(k, b, 500000.0, r)
+            rhs = rope.rotate(q, a - b, 500000.0, r) @ k
+            assert abs(lhs - rhs) < 1e-9 * (1 + abs(lhs))
+
+
+def test_partial_rotary_sdpa_dense_from_zero():
+    """Dense layout from position 0 with rotary_dim 16 of 64 equals torch SDPA over q, k
+    rotated in complex form on their first 16 dims (both q and k see the partial rotation,
+    the scale stays 1/sqrt(D))."""
+    torch = pytest.importorskip("torch")
+    Hq, Hkv, D, r, n = 4, 2, 64, 16, 37
+    wl = build("dense", Hq, Hkv, D, 16, 10000.0, 1, 16, [dense_request(n)], seed=45)
+    got = oracle_out(wl, rotary_dim=r)
+    q = oracle.bf16_bits_to_f64(wl.q_bits)
+    ids = wl.compact_ids(0)
+    k = np.concatenate([oracle.bf16_bits_to_f64(wl.k_bits[i]) for i in ids], axis=1)[:, :n]
+    v = np.concatenate([oracle.bf16_bits_to_f64(wl.v_bits[i]) for i in ids], axis=1)[:, :n]
+    th = 10000.0 ** (-np.arange(r // 2) * 2.0 / r)
+    pos = np.arange(n)
+
+    def crot(x):
+        z = x[..., : r // 2] + 1j * x[..., r // 2: r]
+        z = z * np.exp(1j * pos[:, None] * th[None, :])
+        return np.concatenate([z.real, z.imag, x[..., r:]], axis=-1)
+    qt = torch.from_numpy(crot(q.transpose(1, 0, 2)))
+    kt = torch.from_numpy(crot(k)).repeat_interleave(Hq // Hkv, dim=0)
+    vt = torch.from_numpy(v).repeat_interleave(Hq // Hkv, dim=0)
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True)
+    assert np.max(np.abs(got - ref.numpy().transpose(1, 0, 2))) < 1e-12
+    assert np.max(np.abs(got - oracle_out(wl))) > 1e-3      # differs from full rotary
+
+
 def test_single_visible_key_returns_its_value():
     segs = [Segment("private", 10, tokens=16)]
     wl = small(segs=segs, q_len=1, q_pos=np.array([10]))

@@ -145,6 +145,38 @@ def test_frequency_tables(name, table, kind):
     compare(run_hip(wl, kind, inv_freq=th), oracle_out(wl, base=th), f"{name}/{table}/{kind}")
 
 
+_PARTIAL = [("gaps-D128-G4", 32), ("gaps-D128-G4", 64), ("gaps-D128-G4", 112),
+            ("gaps-D64-G2", 16), ("gaps-D64-G2", 48), ("positions-above-2^15", 16),
+            ("many-tiles-ragged", 64), ("overlap-repeat-partial", 32), ("gaps-D128-G16", 32),
+            ("gaps-D128-G32", 64)]
+
+
+@pytest.mark.parametrize("kind", ["prefill", "decode"])
+@pytest.mark.parametrize("name,r", _PARTIAL, ids=[f"{n}-r{r}" for n, r in _PARTIAL])
+def test_partial_rotary(name, r, kind):
+    """lazyattn_*_partial (rotate-half inside the first r dims, the rest unrotated) against
+    the oracle's partial rotary on the same workload."""
+    wl = small(**dict(_mini_cases())[name])
+    say(f"partial rotary r = {r} on {name} via {kind}")
+    compare(run_hip(wl, kind, rotary_dim=r), oracle_out(wl, rotary_dim=r),
+            f"{name}/r{r}/{kind}")
+
+
+@pytest.mark.parametrize("kind", ["prefill", "decode"])
+def test_partial_rotary_full_size(kind):
+    """Partial rotary (r = 32 of 128) on the full-size Zipf batches, sampled rows."""
+    if kind == "decode":
+        wl = make("decode-32q8kv-b64-ctx4161")
+        g, w = _sampled(wl, "decode", [0, 33, 63], lambda s: np.array([wl.q_indptr[s]]),
+                        rotary_dim=32)
+    else:
+        wl = make("prefill-32q8kv-b16-ctx5376")
+        g, w = _sampled(wl, "prefill", [0, 15], lambda s: wl.q_indptr[s] + np.array([0, 129, 255]),
+                        rotary_dim=32)
+    say(f"partial rotary r = 32 on {wl.name} via {kind}")
+    compare(g, w, f"{wl.name}/r32")
+
+
 def _alibi_ref(wl, slopes):
     from oracle.alibi import alibi_attention
     return alibi_attention(wl.q_bits, wl.k_bits, wl.v_bits,
@@ -370,8 +402,8 @@ def test_shifted_document_is_detected():
 
 # ------------------------------------------------------------------ full-size workloads
 
-def _sampled(wl, kind, seqs, rows_of, inv_freq=None, slopes=None):
-    out = run_hip(wl, kind, inv_freq=inv_freq, slopes=slopes)
+def _sampled(wl, kind, seqs, rows_of, inv_freq=None, slopes=None, rotary_dim=None):
+    out = run_hip(wl, kind, inv_freq=inv_freq, slopes=slopes, rotary_dim=rotary_dim)
     assert np.all(np.isfinite(out)), "non-finite outputs"
     got, want = [], []
     for s in seqs:
@@ -385,7 +417,7 @@ def _sampled(wl, kind, seqs, rows_of, inv_freq=None, slopes=None):
                                    wl.seq_offsets, wl.kv_lens, wl.q_indptr, wl.q_pos,
                                    slopes, wl.B, s, rows))
         else:
-            want.append(oracle_out(wl, rows=rows, seq=s, base=inv_freq))
+            want.append(oracle_out(wl, rows=rows, seq=s, base=inv_freq, rotary_dim=rotary_dim))
     return np.concatenate(got), np.concatenate(want)
 
 

@@ -4,19 +4,22 @@ import numpy as np
 from workload import RequestLayout, Segment, build
 
 
-def oracle_out(wl, rows=None, seq=None, base=None):
-    """The oracle on a workload; `base` overrides its RoPE base (a number or a table)."""
+def oracle_out(wl, rows=None, seq=None, base=None, rotary_dim=None):
+    """The oracle on a workload; `base` overrides its RoPE base (a number or a table),
+    `rotary_dim` selects partial rotary."""
     import oracle
     if rows is None:
         return oracle.lazy_attention(wl.q_bits, wl.k_bits, wl.v_bits,
                                      [wl.compact_ids(s) for s in range(wl.num_seqs)],
                                      wl.seq_offsets, wl.kv_lens, wl.q_indptr, wl.q_pos,
-                                     wl.rope_base if base is None else base, wl.B)
+                                     wl.rope_base if base is None else base, wl.B,
+                                     rotary_dim=rotary_dim)
     return oracle.attention_rows(wl.q_bits, wl.k_bits, wl.v_bits,
                                  [wl.compact_ids(s) if s == seq else None
                                   for s in range(wl.num_seqs)],
                                  wl.seq_offsets, wl.kv_lens, wl.q_indptr, wl.q_pos,
-                                 wl.rope_base if base is None else base, wl.B, seq, rows)
+                                 wl.rope_base if base is None else base, wl.B, seq, rows,
+                                 rotary_dim=rotary_dim)
 
 
 def small(Hq=4, Hkv=2, D=16, B=16, base=10000.0, seed=7, segs=None, q_len=None,
