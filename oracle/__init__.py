@@ -26,6 +26,7 @@ Modules
   pool       ingest of new keys/values into pool slots; a plain model of the
              document-keyed block index (LRU among unreferenced documents).
   alibi      ALiBi (linear bias on logical distances, no rotation) over the same pool.
+  docrot     a pool whose keys carry RoPE at their positions inside their document.
 
 Pins (tests marked "not gpu"): closed-form rotation identities and the complex
 (RoFormer) form of RoPE, a brute-force attention with explicit D x D rotation
@@ -35,6 +36,6 @@ translation and permutation invariance, bit patterns of the packed word, and
 the summary's printed 0.59% overhead at M = 128. No function here is
 "parity unpinned".
 """
-from . import rope, meta, attention, overhead, pool, alibi  # noqa: F401
+from . import rope, meta, attention, overhead, pool, alibi, docrot  # noqa: F401
 from .attention import lazy_attention, attention_rows, bf16_bits_to_f64, rotated_pool  # noqa: F401
 from .meta import encode_meta, decode_meta  # noqa: F401

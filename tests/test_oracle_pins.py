@@ -185,6 +185,54 @@ def test_partial_rotary_sdpa_dense_from_zero():
     assert np.max(np.abs(got - oracle_out(wl))) > 1e-3      # differs from full rotary
 
 
+# ---------------------------------------------------------------- document-rotated pool
+
+def _docrot_wl():
+    segs = [Segment("doc", 5, doc=0), Segment("doc", 40, doc=2), Segment("doc", 200, doc=0),
+            Segment("private", 300, tokens=21)]
+    return small(Hq=4, Hkv=2, D=32, segs=segs, q_len=21, seed=51)
+
+
+def test_doc_rotated_pool_equals_lazy_attention():
+    """Keys stored with RoPE at their positions inside their document (float64, no
+    rounding): undoing the stored rotation and applying the logical one gives the lazy
+    oracle's output on the un-rotated pool (doc 0 appears twice at different offsets)."""
+    from oracle.docrot import doc_rotated_attention
+    from tests.util import doc_stored_offsets, doc_rotated_pool
+    wl = _docrot_wl()
+    st = doc_stored_offsets(wl)
+    kd = doc_rotated_pool(wl, st, as_bits=False)
+    got = doc_rotated_attention(wl.q_bits, kd, wl.v_bits,
+                                [wl.compact_ids(s) for s in range(wl.num_seqs)],
+                                wl.seq_offsets, st, wl.kv_lens, wl.q_indptr, wl.q_pos,
+                                wl.rope_base, wl.B)
+    assert np.max(np.abs(got - oracle_out(wl))) < 1e-12
+    bad = [x.copy() for x in st]
+    bad[0][2] += 1                                   # one block's stored offset off by one
+    worse = doc_rotated_attention(wl.q_bits, kd, wl.v_bits,
+                                  [wl.compact_ids(s) for s in range(wl.num_seqs)],
+                                  wl.seq_offsets, bad, wl.kv_lens, wl.q_indptr, wl.q_pos,
+                                  wl.rope_base, wl.B)
+    assert np.max(np.abs(worse - got)) > 1e-4
+
+
+def test_doc_rotated_translation_invariance():
+    """Shifting every logical offset and query position by c (stored offsets fixed) leaves
+    the output unchanged: only L - p and the stored rotation enter."""
+    from oracle.docrot import doc_rotated_attention
+    from tests.util import doc_stored_offsets, doc_rotated_pool
+    wl = _docrot_wl()
+    st = doc_stored_offsets(wl)
+    kd = doc_rotated_pool(wl, st)
+    ids = [wl.compact_ids(s) for s in range(wl.num_seqs)]
+    a = doc_rotated_attention(wl.q_bits, kd, wl.v_bits, ids, wl.seq_offsets, st, wl.kv_lens,
+                              wl.q_indptr, wl.q_pos, wl.rope_base, wl.B)
+    c = 123457
+    b = doc_rotated_attention(wl.q_bits, kd, wl.v_bits, ids, [o + c for o in wl.seq_offsets],
+                              st, wl.kv_lens, wl.q_indptr, wl.q_pos + c, wl.rope_base, wl.B)
+    assert np.max(np.abs(a - b)) < 1e-10
+
+
 def test_single_visible_key_returns_its_value():
     segs = [Segment("private", 10, tokens=16)]
     wl = small(segs=segs, q_len=1, q_pos=np.array([10]))

@@ -43,3 +43,43 @@ def dense_request(n_tokens, start=0):
 
 def rel(a, b):
     return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300))
+
+
+def doc_stored_offsets(wl):
+    """Per sequence, the stored rotation offset of each entry's slot 0 for a pool that keeps
+    document keys rotated at their positions inside the document (block b of a document at
+    16 b) and private keys at their logical positions."""
+    doc_blocks = wl.info["doc_tokens"] // wl.B
+    out = []
+    for lay in wl.layouts:
+        st = []
+        for sg in lay.segments:
+            if sg.kind == "doc":
+                st += [wl.B * b for b in range(doc_blocks)]
+            else:
+                st += [sg.start + wl.B * b for b in range(-(-sg.tokens // wl.B))]
+        out.append(np.array(st, dtype=np.int64))
+    return out
+
+
+def doc_rotated_pool(wl, stored, as_bits=True):
+    """wl's compact K pool with every block's keys rotated by R(stored + j) (the oracle's
+    rotation); bf16 bits (round to nearest even) or float64. A block must have one stored
+    offset wherever it is referenced."""
+    from oracle.attention import bf16_bits_to_f64
+    from oracle.rope import rotate
+    from workload.rag import f32_to_bf16_bits
+    st_of = {}
+    for s in range(wl.num_seqs):
+        for c, st in zip(wl.compact_ids(s), stored[s]):
+            if st_of.setdefault(int(c), int(st)) != int(st):
+                raise ValueError("a block is referenced with two stored offsets")
+    k = bf16_bits_to_f64(wl.k_bits)
+    j = np.arange(wl.B, dtype=np.int64)
+    for c, st in st_of.items():
+        k[c] = rotate(k[c], (st + j)[None, :], wl.rope_base)
+    if not as_bits:
+        return k
+    nan = np.isnan(k)                       # padding slots stay NaN
+    bits = f32_to_bf16_bits(np.where(nan, 0.0, k).astype(np.float32))
+    return np.where(nan, np.uint16(0x7FC0), bits).astype(np.uint16)
