@@ -506,6 +506,31 @@ def main():
                                                 for k in range(args.steps)])),
                          "rope_ms": line[kind]["ms_pct"]["median"]}
         line["alibi"] = var
+        # the document-rotated pool variant: keys stored with RoPE at their positions inside
+        # their document, so decode needs no per-key rotation. Timed on the same pool and rows
+        # (only the time is used: this pool's keys are not stored rotated, the work is the
+        # same)
+        st_all = wl.doc_stored_offsets()
+        var = {}
+        for kind, seqs, fn, a, ws in halves:
+            st = torch.from_numpy(np.concatenate([st_all[s] for s in seqs]).astype(np.int32)).to(dev)
+
+            def run_doc():
+                fn(a["q"], a["k_pool"], a["v_pool"], a["block_table"], a["block_meta"],
+                   a["kv_lens"], a["q_indptr"], a["q_pos"], wl.rope_base, a["max_entries"],
+                   out=a["out"], workspace=ws, stream=stream, stored_offsets=st)
+            for _ in range(args.warmup):
+                run_doc()
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
+            for k in range(args.steps):
+                e[2 * k].record(stream)
+                run_doc()
+                e[2 * k + 1].record(stream)
+            torch.cuda.synchronize()
+            var[kind] = {"ms": float(np.median([e[2 * k].elapsed_time(e[2 * k + 1])
+                                                for k in range(args.steps)])),
+                         "rope_ms": line[kind]["ms_pct"]["median"]}
+        line["doc_rotated_pool"] = var
     # ingest of new tokens' K/V into pool slots (separate scratch pool; not part of a step)
     line["ingest"] = measure_ingest(torch, L, wl, stream, args.steps)
     # the same kernels' rates against what the chip sustains on plain probes

@@ -200,6 +200,40 @@ int lazyattn_decode_partial(const void* q, const void* k_pool, const void* v_poo
                             void* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * lazyattn_prefill_doc_rotated / lazyattn_decode_doc_rotated -- the same calls over a pool
+ * whose keys already carry RoPE at a STORED position, typically their position inside their
+ * document as a model produced them when it encoded the document alone (technical summary,
+ * "Technical Implementation": a cached key is rotated once by the difference between where
+ * it was encoded and where it is used, and decode re-rotates the query only at a new
+ * document). stored_offsets: DEVICE int32 [block_table[num_seqs]], caller-owned, one per
+ * block-table entry: the position at which slot 0 of that entry's block was rotated when
+ * stored (slot j at stored_offsets[e] + j; 16 b for the b-th block of a document encoded from
+ * position 0). The key of entry e, slot j, is used as R(off_e - stored_offsets[e]) times the
+ * stored key, which equals R(L) k for the key k before rotation; the logical offsets of the
+ * packed words still decide causality. With stored_offsets[e] = off_e the call is the
+ * materialised baseline. Decode applies no per-key rotation: q' = R(p - off_e +
+ * stored_offsets[e]) q is recomputed only where off_e - stored_offsets[e] changes. Errors as
+ * lazyattn_prefill / lazyattn_decode (NULL if stored_offsets is NULL, ALIGN if it is not
+ * 4-byte aligned).
+ */
+int lazyattn_prefill_doc_rotated(const void* q, const void* k_pool, const void* v_pool,
+                                 const int32_t* block_table, const uint32_t* block_meta,
+                                 const int32_t* kv_lens, const int32_t* q_indptr,
+                                 const int32_t* q_positions, const int32_t* stored_offsets,
+                                 double rope_base, int32_t num_seqs, int32_t total_q,
+                                 int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
+                                 int32_t num_blocks, int32_t max_entries, void* out,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+int lazyattn_decode_doc_rotated(const void* q, const void* k_pool, const void* v_pool,
+                                const int32_t* block_table, const uint32_t* block_meta,
+                                const int32_t* kv_lens, const int32_t* q_indptr,
+                                const int32_t* q_positions, const int32_t* stored_offsets,
+                                double rope_base, int32_t num_seqs, int32_t total_q,
+                                int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
+                                int32_t num_blocks, int32_t max_entries, void* out,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * lazyattn_prefill_alibi / lazyattn_decode_alibi -- the same calls over the same
  * position-free pool with ALiBi instead of RoPE (technical summary, "Key Contributions":
  * compatibility with ALiBi). Nothing is rotated; a query of head h at logical position p

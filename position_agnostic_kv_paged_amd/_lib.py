@@ -13,7 +13,7 @@ EXPORTED = [
     "lazyattn_prefill", "lazyattn_decode", "lazyattn_prefill_rotated_pool",
     "lazyattn_decode_rotated_pool", "lazyattn_prefill_freqs", "lazyattn_decode_freqs",
     "lazyattn_prefill_alibi", "lazyattn_decode_alibi", "lazyattn_prefill_partial",
-    "lazyattn_decode_partial",
+    "lazyattn_decode_partial", "lazyattn_prefill_doc_rotated", "lazyattn_decode_doc_rotated",
     "lazyattn_materialize_rotated", "lazyattn_probe_cus",
     "lazyattn_probe_mfma", "lazyattn_probe_read", "lazyattn_ingest_kv", "lazyattn_pool_create",
     "lazyattn_pool_destroy", "lazyattn_pool_acquire", "lazyattn_pool_release",
@@ -67,6 +67,9 @@ def lib():
     for name in ("lazyattn_prefill_partial", "lazyattn_decode_partial"):
         f = getattr(L, name)
         f.argtypes, f.restype = attn[:9] + [i32] + attn[9:], ctypes.c_int
+    for name in ("lazyattn_prefill_doc_rotated", "lazyattn_decode_doc_rotated"):
+        f = getattr(L, name)
+        f.argtypes, f.restype = attn[:8] + [vp] + attn[8:], ctypes.c_int
     L.lazyattn_materialize_rotated.argtypes = [vp, vp, vp, vp, vp, dbl, i32, i32, i32, i32, i32,
                                                i32, vp, vp, vp, vp]
     L.lazyattn_materialize_rotated.restype = ctypes.c_int

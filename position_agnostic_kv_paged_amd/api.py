@@ -39,7 +39,8 @@ def workspace_bytes(kind, num_seqs, total_q, max_entries, Hq, Hkv, D):
 
 def _attention(kind, q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indptr, q_pos,
                rope_base, max_entries, out=None, workspace=None, stream=None,
-               rotated_pool=False, inv_freq=None, slopes=None, rotary_dim=None):
+               rotated_pool=False, inv_freq=None, slopes=None, rotary_dim=None,
+               stored_offsets=None):
     import torch
     total_q, Hq, D, num_blocks, Hkv, B = _dims(q, k_pool)
     num_seqs = kv_lens.numel()
@@ -48,8 +49,16 @@ def _attention(kind, q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indp
     need = workspace_bytes(kind, num_seqs, total_q, max_entries, Hq, Hkv, D)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    extra = []
-    if rotary_dim is not None and rotary_dim != D:
+    extra, pre = [], []
+    if stored_offsets is not None:
+        if rotated_pool or inv_freq is not None or slopes is not None or rotary_dim is not None:
+            raise ValueError("stored_offsets combines with rope_base only")
+        if stored_offsets.dtype != torch.int32 or not stored_offsets.is_contiguous() or \
+                stored_offsets.numel() != block_meta.numel():
+            raise ValueError("stored_offsets must be a contiguous int32 device tensor with one "
+                             "entry per block-table entry")
+        name, pe, pre = "lazyattn_" + kind + "_doc_rotated", float(rope_base), [_ptr(stored_offsets)]
+    elif rotary_dim is not None and rotary_dim != D:
         if rotated_pool or inv_freq is not None or slopes is not None:
             raise ValueError("rotary_dim combines with rope_base only")
         name, pe = "lazyattn_" + kind + "_partial", float(rope_base)
@@ -72,7 +81,7 @@ def _attention(kind, q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indp
         pe = float(rope_base)
     fn = getattr(lib(), name)
     rc = fn(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(block_meta),
-            _ptr(kv_lens), _ptr(q_indptr), _ptr(q_pos), pe, *extra, num_seqs, total_q,
+            _ptr(kv_lens), _ptr(q_indptr), _ptr(q_pos), *pre, pe, *extra, num_seqs, total_q,
             Hq, Hkv, D, B, num_blocks, int(max_entries), _ptr(out), _ptr(workspace),
             workspace.numel() * workspace.element_size(), _stream(stream))
     check(rc, name)
@@ -81,24 +90,28 @@ def _attention(kind, q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indp
 
 def prefill(q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indptr, q_pos, rope_base,
             max_entries, out=None, workspace=None, stream=None, inv_freq=None, slopes=None,
-            rotary_dim=None):
+            rotary_dim=None, stored_offsets=None):
     """lazyattn_prefill on torch tensors (all on one HIP device); returns out. With inv_freq
     (D/2 radians per position), lazyattn_prefill_freqs; with slopes (float32 device [Hq]),
     lazyattn_prefill_alibi; rope_base is then not used. With rotary_dim below D (a multiple
-    of 16), lazyattn_prefill_partial (partial rotary)."""
+    of 16), lazyattn_prefill_partial (partial rotary). With stored_offsets (int32 device,
+    one per block-table entry), lazyattn_prefill_doc_rotated (keys stored with RoPE at
+    those offsets)."""
     return _attention("prefill", q, k_pool, v_pool, block_table, block_meta, kv_lens,
                       q_indptr, q_pos, rope_base, max_entries, out, workspace, stream,
-                      inv_freq=inv_freq, slopes=slopes, rotary_dim=rotary_dim)
+                      inv_freq=inv_freq, slopes=slopes, rotary_dim=rotary_dim,
+                      stored_offsets=stored_offsets)
 
 
 def decode(q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indptr, q_pos, rope_base,
            max_entries, out=None, workspace=None, stream=None, inv_freq=None, slopes=None,
-           rotary_dim=None):
-    """lazyattn_decode on torch tensors; returns out (inv_freq, slopes, rotary_dim as for
-    prefill)."""
+           rotary_dim=None, stored_offsets=None):
+    """lazyattn_decode on torch tensors; returns out (inv_freq, slopes, rotary_dim,
+    stored_offsets as for prefill)."""
     return _attention("decode", q, k_pool, v_pool, block_table, block_meta, kv_lens,
                       q_indptr, q_pos, rope_base, max_entries, out, workspace, stream,
-                      inv_freq=inv_freq, slopes=slopes, rotary_dim=rotary_dim)
+                      inv_freq=inv_freq, slopes=slopes, rotary_dim=rotary_dim,
+                      stored_offsets=stored_offsets)
 
 
 def llama31_inv_freq(D, base=500000.0, factor=8.0, low_freq_factor=1.0, high_freq_factor=4.0,

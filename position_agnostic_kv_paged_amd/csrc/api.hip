@@ -71,7 +71,8 @@ int run(const void* q, const void* k_pool, const void* v_pool, const int32_t* bl
         int32_t Hq, int32_t Hkv, int32_t D, int32_t B, int32_t num_blocks,
         int32_t max_entries, void* out, void* workspace, size_t workspace_bytes,
         void* stream, int mode, int pe, const double* inv_freq = nullptr,
-        const float* slopes = nullptr, int rotary_dim = 0) {
+        const float* slopes = nullptr, int rotary_dim = 0,
+        const int32_t* stored_offsets = nullptr) {
   if (!q || !k_pool || !v_pool || !block_table || !block_meta || !kv_lens || !q_indptr ||
       !q_positions || !out || !workspace)
     return LAZYATTN_ERR_NULL;
@@ -90,6 +91,10 @@ int run(const void* q, const void* k_pool, const void* v_pool, const int32_t* bl
   }
   if (pe == kRopePartial && (rotary_dim < 16 || rotary_dim > D || rotary_dim % 16))
     return LAZYATTN_ERR_ARG;
+  if (pe == kDocRotated) {
+    if (!stored_offsets) return LAZYATTN_ERR_NULL;
+    if (!aligned(stored_offsets, 4)) return LAZYATTN_ERR_ALIGN;
+  }
   if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(out, 16) ||
       !aligned(workspace, 16) || !aligned(block_table, 4) || !aligned(block_meta, 4) ||
       !aligned(kv_lens, 4) || !aligned(q_indptr, 4) || !aligned(q_positions, 4))
@@ -132,13 +137,15 @@ int run(const void* q, const void* k_pool, const void* v_pool, const int32_t* bl
     PrefillParams P{(const uint16_t*)q, (const uint16_t*)k_pool, (const uint16_t*)v_pool,
                     block_table, block_meta, kv_lens, q_indptr, q_positions,
                     (uint16_t*)out, pf_prefix, (const uint16_t*)zero, num_seqs, Hq, Hw,
-                    num_blocks, (int)tiles, scale_log2, freqs, slopes, Hkv, kv_group, r / 16};
+                    num_blocks, (int)tiles, scale_log2, freqs, slopes, Hkv, kv_group, r / 16,
+                    stored_offsets};
     if (launch_prefill(P, D, G, pe, st) != hipSuccess) return LAZYATTN_ERR_LAUNCH;
   }
   DecodeParams Dp{(const uint16_t*)q, (const uint16_t*)k_pool, (const uint16_t*)v_pool,
                   block_table, block_meta, kv_lens, q_indptr, q_positions, dec_prefix,
                   (const uint16_t*)zero, partials, num_seqs, Hq, Hw, num_blocks,
-                  ds.bps, ds.smax, scale_log2, freqs, slopes, Hkv, kv_group, r / 16};
+                  ds.bps, ds.smax, scale_log2, freqs, slopes, Hkv, kv_group, r / 16,
+                  stored_offsets};
   if (launch_decode(Dp, D, G, pe, st) != hipSuccess) return LAZYATTN_ERR_LAUNCH;
   MergeParams Mp{q_indptr, block_table, dec_prefix, partials, (uint16_t*)out,
                  num_seqs, Hq, ds.bps, ds.smax, mode};
@@ -274,6 +281,34 @@ int lazyattn_decode_partial(const void* q, const void* k_pool, const void* v_poo
              rope_base, num_seqs, total_q, Hq, Hkv, D, B, num_blocks, max_entries, out,
              workspace, workspace_bytes, stream, kPlanDecodeOnly, kRopePartial, nullptr,
              nullptr, rotary_dim);
+}
+
+int lazyattn_prefill_doc_rotated(const void* q, const void* k_pool, const void* v_pool,
+                                 const int32_t* block_table, const uint32_t* block_meta,
+                                 const int32_t* kv_lens, const int32_t* q_indptr,
+                                 const int32_t* q_positions, const int32_t* stored_offsets,
+                                 double rope_base, int32_t num_seqs, int32_t total_q,
+                                 int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
+                                 int32_t num_blocks, int32_t max_entries, void* out,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  return run(q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indptr, q_positions,
+             rope_base, num_seqs, total_q, Hq, Hkv, D, B, num_blocks, max_entries, out,
+             workspace, workspace_bytes, stream, kPlanMixed, kDocRotated, nullptr, nullptr, 0,
+             stored_offsets);
+}
+
+int lazyattn_decode_doc_rotated(const void* q, const void* k_pool, const void* v_pool,
+                                const int32_t* block_table, const uint32_t* block_meta,
+                                const int32_t* kv_lens, const int32_t* q_indptr,
+                                const int32_t* q_positions, const int32_t* stored_offsets,
+                                double rope_base, int32_t num_seqs, int32_t total_q,
+                                int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
+                                int32_t num_blocks, int32_t max_entries, void* out,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  return run(q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indptr, q_positions,
+             rope_base, num_seqs, total_q, Hq, Hkv, D, B, num_blocks, max_entries, out,
+             workspace, workspace_bytes, stream, kPlanDecodeOnly, kDocRotated, nullptr,
+             nullptr, 0, stored_offsets);
 }
 
 size_t lazyattn_prefill_workspace_bytes(int32_t num_seqs, int32_t total_q, int32_t max_entries,

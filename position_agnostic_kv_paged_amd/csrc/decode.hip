@@ -54,6 +54,7 @@ __device__ __forceinline__ int vswz(int R) { return (R & 3) * 2; }
 
 struct GroupMeta {
   int id[2], delta[2], nval[2];
+  int st[2];                   // document-rotated pool: stored offset of the block's slot 0
 };
 
 // PE = kStored is the materialised baseline: the pool's keys already carry R(L) at their
@@ -63,8 +64,11 @@ struct GroupMeta {
 template <int D, int G, int PE>
 __global__ __launch_bounds__(kDecodeWaves * 64, 2) void decode_kernel(DecodeParams P) {
   constexpr bool PART = PE == kRopePartial;   // dims in the permuted order of nat_chunk
-  constexpr bool ROT = PE == kRope || PART;
+  constexpr bool ROT = PE == kRope || PART;   // keys get the per-slot rotation R(j)
   constexpr bool ALIBI = PE == kAlibi;
+  // DOC: keys carry R(stored + j); q' = R(p - (off - stored)) q is constant over entries with
+  // the same off - stored (one document) and keys are used as stored
+  constexpr bool DOC = PE == kDocRotated;
   // PHC: the 16 columns of the score MFMA hold (head, block phase) pairs (2 G <= 16), so
   // both blocks of a group are scored against one q' operand. Otherwise (G = 16) the
   // columns are the 16 heads and q' is set to each block's phase in turn.
@@ -176,6 +180,8 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 2) void decode_kernel(DecodePara
         const int rem = i_kvlen - t * kBlock;
         gm.id[b] = id;
         gm.delta[b] = word_delta(wd);
+        // (used only at the group's turn, after its loads have been waited for)
+        gm.st[b] = DOC && blk ? P.stored[i_e0 + t] : 0;
         gm.nval[b] = (blk && id < P.num_blocks) ? (rem < kBlock ? (rem > 0 ? rem : 0) : kBlock) : 0;
         const size_t kb = ((size_t)id * P.Hkv_pool + i_kvh) * kBlock;
 #pragma unroll
@@ -221,11 +227,16 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 2) void decode_kernel(DecodePara
 
       const int d0 = gcur.delta[0];
       const int d1 = (t0 + 1 < ee) ? gcur.delta[1] : d0;
+      // rotation still to apply to the stored keys of each block: off - stored
+      const int sh0 = t0 * kBlock + d0 - gcur.st[0];
+      const int sh1 = (t0 + 1 < ee) ? (t0 + 1) * kBlock + d1 - gcur.st[1] : sh0;
       u32x4 bp;
       if constexpr (PHC) {
         // ---- q' of this lane's column: R(p - off_{t0+ph}) q_g ---------------------------
-        if (!ROT && have_q) {
+        if (!ROT && !DOC && have_q) {
           // keys carry their absolute rotation: q' = R(p) q stays fixed
+        } else if (DOC && have_q && sh0 == cur_delta && sh1 == cur_delta) {
+          // same document as the previous group: q' unchanged
         } else if (ROT && have_q && d0 == cur_delta && d1 == cur_delta) {
 #pragma unroll
           for (int c = 0; c < HC; ++c)
@@ -241,7 +252,8 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 2) void decode_kernel(DecodePara
               }
             }
         } else {
-          const int n = ROT ? p - ((t0 + ph) * kBlock + (ph ? d1 : d0)) : (ALIBI ? 0 : p);
+          const int n = ROT ? p - ((t0 + ph) * kBlock + (ph ? d1 : d0))
+                        : DOC ? p - (ph ? sh1 : sh0) : (ALIBI ? 0 : p);
 #pragma unroll
           for (int c = 0; c < HC; ++c) {
             const u32x4 va = col_ok ? *(const u32x4*)(qrow + dofs[c]) : u32x4{0, 0, 0, 0};
@@ -256,8 +268,8 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 2) void decode_kernel(DecodePara
               qr[c + HC][e] = a * sn + b * cs;
             }
           }
-          have_q = !ROT || (d0 == d1);
-          cur_delta = d1;
+          have_q = ROT ? d0 == d1 : DOC ? sh0 == sh1 : true;
+          cur_delta = DOC ? sh1 : d1;
         }
         // ---- scores of both blocks; each lane keeps its own phase's block ------------------
         f32x4 S[2] = {f32x4{}, f32x4{}};
@@ -338,9 +350,11 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 2) void decode_kernel(DecodePara
           }
         };
         auto set_q = [&](int off) {              // qr := R(p - off) q (or the fixed q')
-          if (!ROT) {
+          if (!ROT && !DOC) {
             if (!have_q) qexact(ALIBI ? 0 : p);
-          } else if (have_q && off == cur_delta + kBlock) {
+          } else if (DOC && have_q && off == cur_delta) {
+            // same document: q' unchanged
+          } else if (ROT && have_q && off == cur_delta + kBlock) {
 #pragma unroll
             for (int c = 0; c < HC; ++c)
 #pragma unroll
@@ -387,11 +401,11 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 2) void decode_kernel(DecodePara
           return S;
         };
         const bool has1 = t0 + 1 < ee;
-        set_q(t0 * kBlock + d0);
+        set_q(DOC ? sh0 : t0 * kBlock + d0);
         const f32x4 S0 = scores(0);
         f32x4 S1 = {};
         if (has1) {
-          set_q((t0 + 1) * kBlock + d1);
+          set_q(DOC ? sh1 : (t0 + 1) * kBlock + d1);
           S1 = scores(1);
         }
         float sc[8];
@@ -501,6 +515,7 @@ static hipError_t launch_d(const DecodeParams& p, int G, int pe, hipStream_t st)
     case kStored: return launch_dr<D, kStored>(p, G, st);
     case kAlibi: return launch_dr<D, kAlibi>(p, G, st);
     case kRopePartial: return launch_dr<D, kRopePartial>(p, G, st);
+    case kDocRotated: return launch_dr<D, kDocRotated>(p, G, st);
   }
   return hipErrorInvalidValue;
 }

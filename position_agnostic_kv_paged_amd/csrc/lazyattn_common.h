@@ -222,7 +222,9 @@ __host__ __device__ inline int row_splits(int T, int bps, int smax) {
 //   kStored  materialised baseline: keys already carry R(L); queries rotated by R(p)
 //   kAlibi   position-free pool, no rotation: score + slope_h (L - p) (linear bias)
 //   kRopePartial  as kRope, with rotate-half applied inside the first rotary_dim dims only
-enum PosEnc : int { kRope = 0, kStored = 1, kAlibi = 2, kRopePartial = 3 };
+//   kDocRotated   keys stored with RoPE at a per-entry stored offset (e.g. their position
+//                 inside their document): the kernels rotate by off_t - stored_t only
+enum PosEnc : int { kRope = 0, kStored = 1, kAlibi = 2, kRopePartial = 3, kDocRotated = 4 };
 
 // Partial rotary (dims k and k + r/2 paired for k < r/2, theta_k = base^(-2k/r), dims r..D-1
 // unrotated) is computed as full rotate-half over a permuted dim order whose extra pairs have

@@ -39,6 +39,7 @@ struct PrefillParams {
   const float* slopes;       // [Hq] ALiBi slopes (positional encoding kAlibi only)
   int Hkv_pool, kv_group;    // pool KV heads; work heads per pool head (see below)
   int rot_chunks;            // rotary_dim / 16 (kRopePartial only; nat_chunk)
+  const int32_t* stored;     // [entries] stored rotation offset of slot 0 (kDocRotated only)
 };
 
 // More than 16 query heads per KV head (G = 16 S): the kernels run Hkv * S "work heads" of
@@ -63,6 +64,7 @@ struct DecodeParams {
   const float* slopes;       // [Hq] ALiBi slopes (positional encoding kAlibi only)
   int Hkv_pool, kv_group;    // as in PrefillParams
   int rot_chunks;            // as in PrefillParams
+  const int32_t* stored;     // as in PrefillParams
 };
 
 struct MergeParams {

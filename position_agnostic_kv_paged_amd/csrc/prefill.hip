@@ -70,16 +70,25 @@ __device__ __forceinline__ uint32_t load_window(const PrefillParams& P, int e0, 
   return *(const uint32_t*)blend_ptr(T > 0, P.block_meta + e0 + max(ent, 0), P.zero);
 }
 
+// stored rotation offsets of the same entries (document-rotated pool)
+__device__ __forceinline__ int load_stored(const PrefillParams& P, int e0, int T, int kt,
+                                           int lane) {
+  const int ent = min(4 * kt + lane, T - 1);
+  return *(const int*)blend_ptr(T > 0, P.stored + e0 + max(ent, 0), P.zero);
+}
+
 struct WinDec {
   int id, off, nv;                                       // this lane's entry, decoded
+  int sh;                                                // rotation still to apply: off - stored
 };
 
-__device__ __forceinline__ WinDec decode_window(const PrefillParams& P, uint32_t win, int T,
-                                                int kvlen, int kt, int lane) {
+__device__ __forceinline__ WinDec decode_window(const PrefillParams& P, uint32_t win, int st,
+                                                int T, int kvlen, int kt, int lane) {
   const int ent = 4 * kt + lane;
   WinDec d;
   d.id = word_id(win);
   d.off = word_offset(win, ent);
+  d.sh = d.off - st;
   d.nv = ((lane < 16) & (ent < T) & (d.id < P.num_blocks))   // out-of-pool id: never read
              ? min(max(kvlen - ent * kBlock, 0), kBlock) : 0;
   return d;
@@ -107,7 +116,8 @@ __device__ __forceinline__ TileWords tile_words(const WinDec& wd) {
 template <int D, int G, int PE>
 __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillParams P) {
   constexpr bool PART = PE == kRopePartial;   // dims in the permuted order of nat_chunk
-  constexpr bool ROTATE = PE == kRope || PART; // keys rotated per tile (position-free pool)
+  constexpr bool DOC = PE == kDocRotated;     // keys carry R(stored + j): rotate by off - stored
+  constexpr bool ROTATE = PE == kRope || PART || DOC;   // keys rotated per tile
   constexpr bool ALIBI = PE == kAlibi;        // no rotation; linear bias on the scores
   constexpr int NW = kPrefillWaves;
   constexpr int NT = NW * 64;
@@ -233,7 +243,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
   auto tpos = [&](int r, int f) {
     return ((r * (FPT / 2) + (f % FPT) / 2) * CPT + f / FPT) * 2 + (f & 1);
   };
-  for (int i = tid; i < 16 * HALF; i += NT) {               // R(j) table, loop invariant
+  for (int i = tid; !DOC && i < 16 * HALF; i += NT) {       // R(j) table, loop invariant
     float c, sn;
     rope_cos_sin(i / HALF, fr_s[i % HALF], c, sn);
     ((float2*)slot_cs)[tpos(i / HALF, i % HALF)] = make_float2(c, sn);
@@ -280,7 +290,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
   // (the per-lane block choice selects among readlane results, never indexes an array)
   auto make_table = [&](const WinDec& wd, int d, int buf) __attribute__((always_inline)) {
     if (!ROTATE) return;                                    // keys need no phase table
-    const int o = rl(wd.off, 4 * d + tab_b);
+    const int o = rl(DOC ? wd.sh : wd.off, 4 * d + tab_b);
     ((float*)tbl[buf])[tab_pos] = rope_sin_rev(o - p_ref, tab_f, tab_quarter);
   };
   // values of tile kt + d straight into LDS, wave-wide instruction i of this wave: slot
@@ -325,8 +335,8 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
     for (int u = 0; u < 2; ++u) {
       const float cb = u ? cs.z : cs.x, sb = u ? cs.w : cs.y;
       const float cj = u ? js.z : js.x, sj = u ? js.w : js.y;
-      const float c = cb * cj - sb * sj;
-      const float sn = sb * cj + cb * sj;
+      const float c = DOC ? cb : cb * cj - sb * sj;
+      const float sn = DOC ? sb : sb * cj + cb * sj;
       const float a = u ? bf_hi(xlo) : bf_lo(xlo);
       const float b = u ? bf_hi(xhi) : bf_lo(xhi);
       ra[u] = a * c - b * sn;
@@ -346,8 +356,9 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
   // loads for later tiles are spread over A's k-steps so that the vector memory path
   // overlaps the matrix cores instead of stalling every wave right after the barrier.
   uint32_t win = load_window(P, e0, T, 0, lane);           // words of tiles 0 .. 3
+  const int st0 = DOC ? load_stored(P, e0, T, 0, lane) : 0;
   if (n_kt > 0) {
-    const WinDec wd = decode_window(P, win, T, kvlen, 0, lane);
+    const WinDec wd = decode_window(P, win, st0, T, kvlen, 0, lane);
     make_table(wd, 0, 0);
     make_table(wd, 1, 1);
 #pragma unroll
@@ -363,7 +374,8 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
         const float4* j4 = &slot_cs[kj * (FPT / 2) * CPT + cp];
 #pragma unroll
         for (int i2 = 0; i2 < FPT / 2; ++i2) {
-          const u32x2 r = rot_pair(t4[i2 * CPT], j4[i2 * CPT], klo[i2], khi[i2]);
+          const u32x2 r = rot_pair(t4[i2 * CPT], DOC ? float4{} : j4[i2 * CPT], klo[i2],
+                                   khi[i2]);
           ol[i2] = r[0];
           oh[i2] = r[1];
         }
@@ -406,7 +418,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
     }
   };
   if (n_kt > 0) qk(0, S0);
-  WinDec wdc = decode_window(P, win, T, kvlen, 0, lane);
+  WinDec wdc = decode_window(P, win, st0, T, kvlen, 0, lane);
   add_bias(S0[0], wdc, 0);
   add_bias(S0[1], wdc, 1);
   bool maskc = needs_mask(wdc);
@@ -425,6 +437,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
     // were computed under the MFMAs of the previous iteration
     const WinDec wd = wdc;
     uint32_t win_next = 0;
+    int st_next = 0;
     WinDec wdn;
     bool maskn = false;
     float h0 = 0.f, h1 = 0.f;
@@ -518,7 +531,10 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
         // path works while the matrix cores do: values of tile kt+1 (k-steps 0..2), the
         // next word window (k-step 2), the phase table of tile kt+3 (k-step 3)
         if (c < VPW) issue_v(wd, 1, nxt, c);
-        if (c == 2) win_next = load_window(P, e0, T, kt + 1, lane);
+        if (c == 2) {
+          win_next = load_window(P, e0, T, kt + 1, lane);
+          if (DOC) st_next = load_stored(P, e0, T, kt + 1, lane);
+        }
         if (c == 3) make_table(wd, 3, nxt);
         Sn[1] = mfma32h(as_f16x8(a1), as_f16x8(b), Sn[1]);
         exp_slot(3 + 2 * c);
@@ -556,8 +572,8 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
           const int u = pc;
           const float cb = u ? cs.z : cs.x, sb = u ? cs.w : cs.y;
           const float cj = u ? js.z : js.x, sj = u ? js.w : js.y;
-          rc[u] = cb * cj - sb * sj;
-          rsn[u] = sb * cj + cb * sj;
+          rc[u] = DOC ? cb : cb * cj - sb * sj;
+          rsn[u] = DOC ? sb : sb * cj + cb * sj;
           asm volatile("" ::"v"(rc[u]), "v"(rsn[u]));
         } else {
           const int u = pc - 2;
@@ -579,7 +595,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
       };
       u32x4 va[D / 32];
       vread(0, va);
-      float4 cs = ROTATE ? t4[0] : float4{}, js = ROTATE ? j4[0] : float4{};
+      float4 cs = ROTATE ? t4[0] : float4{}, js = ROTATE && !DOC ? j4[0] : float4{};
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -589,14 +605,14 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
           vread(g + 1, vn);
           if (ROTATE && g + 1 < FPT / 2) {
             csn = t4[(g + 1) * CPT];
-            jsn = j4[(g + 1) * CPT];
+            if (!DOC) jsn = j4[(g + 1) * CPT];
           }
         }
         __builtin_amdgcn_sched_barrier(0);
         // next iteration's inputs, under these MFMAs: decoded words of tiles kt+1 ..
         // kt+4 (group 1) and the row max of S(kt+1) (groups 2, 3)
         if (g == 1) {
-          wdn = decode_window(P, win_next, T, kvlen, kt + 1, lane);
+          wdn = decode_window(P, win_next, st_next, T, kvlen, kt + 1, lane);
           asm volatile("" ::"v"(wdn.id), "v"(wdn.off), "v"(wdn.nv));
           maskn = needs_mask(wdn);
         }
@@ -676,6 +692,9 @@ static hipError_t launch_dg(const PrefillParams& p, int pe, hipStream_t st) {
     case kAlibi: hipLaunchKernelGGL((prefill_kernel<D, G, kAlibi>), grid, block, 0, st, p); break;
     case kRopePartial:
       hipLaunchKernelGGL((prefill_kernel<D, G, kRopePartial>), grid, block, 0, st, p);
+      break;
+    case kDocRotated:
+      hipLaunchKernelGGL((prefill_kernel<D, G, kDocRotated>), grid, block, 0, st, p);
       break;
     default: return hipErrorInvalidValue;
   }

@@ -18,7 +18,7 @@ def words_for(wl):
 
 
 def run_hip(wl, kind, dev="cuda", tensors=None, words=None, repeat=1, inv_freq=None,
-            slopes=None, rotary_dim=None):
+            slopes=None, rotary_dim=None, stored=None):
     """Call lazyattn_prefill / lazyattn_decode on the workload; returns float64 [total_q,Hq,D]."""
     import torch
     import position_agnostic_kv_paged_amd as L
@@ -28,13 +28,15 @@ def run_hip(wl, kind, dev="cuda", tensors=None, words=None, repeat=1, inv_freq=N
     meta = torch.from_numpy(np.ascontiguousarray(words).view(np.int32)).to(dev)
     max_entries = max(len(x) for x in wl.seq_block_ids)
     fn = L.prefill if kind == "prefill" else L.decode
+    st = None if stored is None else \
+        torch.from_numpy(np.concatenate(stored).astype(np.int32)).to(dev)
     outs = []
     for _ in range(repeat):
         out = fn(t["q"], t["k_pool"], t["v_pool"], t["block_table"], meta, t["kv_lens"],
                  t["q_indptr"], t["q_pos"], wl.rope_base, max_entries, inv_freq=inv_freq,
                  slopes=None if slopes is None else
                  torch.as_tensor(np.asarray(slopes, np.float32), device=dev),
-                 rotary_dim=rotary_dim)
+                 rotary_dim=rotary_dim, stored_offsets=st)
         torch.cuda.synchronize()
         outs.append(out.float().cpu().numpy().astype(np.float64))
     return outs[0] if repeat == 1 else outs

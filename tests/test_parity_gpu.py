@@ -177,6 +177,73 @@ def test_partial_rotary_full_size(kind):
     compare(g, w, f"{wl.name}/r32")
 
 
+_DOCROT = ["gaps-D128-G4", "gaps-D64-G2", "overlap-repeat-partial", "positions-above-2^15",
+           "many-tiles-ragged", "gaps-D128-G16", "many-tiles-ragged-G16", "gaps-D128-G32",
+           "gaps-D128-G1"]
+
+
+def _docrot_case(wl, stored):
+    """(workload whose K pool holds keys rotated at the stored offsets, oracle output)."""
+    import dataclasses
+    from oracle.docrot import doc_rotated_attention
+    from tests.util import doc_rotated_pool
+    kd = doc_rotated_pool(wl, stored)
+    want = doc_rotated_attention(wl.q_bits, kd, wl.v_bits,
+                                 [wl.compact_ids(s) for s in range(wl.num_seqs)],
+                                 wl.seq_offsets, stored, wl.kv_lens, wl.q_indptr, wl.q_pos,
+                                 wl.rope_base, wl.B)
+    return dataclasses.replace(wl, k_bits=kd), want
+
+
+@pytest.mark.parametrize("kind", ["prefill", "decode"])
+@pytest.mark.parametrize("name", _DOCROT)
+def test_doc_rotated_pool(name, kind):
+    """lazyattn_*_doc_rotated over a pool whose document keys carry RoPE at their positions
+    inside the document (block b at 16 b) and private keys at their logical positions."""
+    from tests.util import doc_stored_offsets
+    wl = small(**dict(_mini_cases())[name])
+    st = doc_stored_offsets(wl)
+    wd, want = _docrot_case(wl, st)
+    say(f"document-rotated pool on {name} via {kind}")
+    compare(run_hip(wd, kind, stored=st), want, f"{name}/docrot/{kind}")
+
+
+@pytest.mark.parametrize("kind", ["prefill", "decode"])
+def test_doc_rotated_pool_at_logical_offsets(kind):
+    """Stored offsets equal to the logical offsets (every block rotated where it is used):
+    the materialised pool, through the document-rotated entry points."""
+    wl = small(**dict(_mini_cases())["gaps-D128-G4"])      # every block referenced once
+    st = [np.asarray(o, dtype=np.int64) for o in wl.seq_offsets]
+    wd, want = _docrot_case(wl, st)
+    compare(run_hip(wd, kind, stored=st), want, f"docrot-logical/{kind}")
+    assert np.max(np.abs(want - oracle_out(wl))) < 1e-2          # the same attention
+
+
+def test_doc_rotated_pool_full_size_decode():
+    """Document-rotated pool on the 64-request decode batch (Zipf documents reused at
+    per-request offsets), sampled rows."""
+    from oracle.docrot import doc_rotated_rows
+    from tests.util import doc_stored_offsets
+    import dataclasses
+    from tests.util import doc_rotated_pool
+    wl = make("decode-32q8kv-b64-ctx4161")
+    st = doc_stored_offsets(wl)
+    kd = doc_rotated_pool(wl, st)
+    wd = dataclasses.replace(wl, k_bits=kd)
+    say("document-rotated pool on decode-32q8kv-b64-ctx4161 via decode")
+    out = run_hip(wd, "decode", stored=st)
+    got, want = [], []
+    for s in (0, 31, 63):
+        rows = np.array([wl.q_indptr[s]])
+        got.append(out[rows])
+        want.append(doc_rotated_rows(wl.q_bits, kd, wl.v_bits,
+                                     [wl.compact_ids(x) if x == s else None
+                                      for x in range(wl.num_seqs)],
+                                     wl.seq_offsets, st, wl.kv_lens, wl.q_indptr, wl.q_pos,
+                                     wl.rope_base, wl.B, s, rows))
+    compare(np.concatenate(got), np.concatenate(want), "decode-b64/docrot")
+
+
 def _alibi_ref(wl, slopes):
     from oracle.alibi import alibi_attention
     return alibi_attention(wl.q_bits, wl.k_bits, wl.v_bits,

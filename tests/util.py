@@ -46,20 +46,8 @@ def rel(a, b):
 
 
 def doc_stored_offsets(wl):
-    """Per sequence, the stored rotation offset of each entry's slot 0 for a pool that keeps
-    document keys rotated at their positions inside the document (block b of a document at
-    16 b) and private keys at their logical positions."""
-    doc_blocks = wl.info["doc_tokens"] // wl.B
-    out = []
-    for lay in wl.layouts:
-        st = []
-        for sg in lay.segments:
-            if sg.kind == "doc":
-                st += [wl.B * b for b in range(doc_blocks)]
-            else:
-                st += [sg.start + wl.B * b for b in range(-(-sg.tokens // wl.B))]
-        out.append(np.array(st, dtype=np.int64))
-    return out
+    """Stored offsets of a pool whose document keys were encoded per document."""
+    return wl.doc_stored_offsets()
 
 
 def doc_rotated_pool(wl, stored, as_bits=True):

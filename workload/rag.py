@@ -129,6 +129,23 @@ class Workload:
         """Entry block ids of `seq` re-indexed into the compact k_bits/v_bits arrays."""
         return np.searchsorted(self.pool_ids, self.seq_block_ids[seq]).astype(np.int64)
 
+    def doc_stored_offsets(self) -> List[np.ndarray]:
+        """Per sequence and entry, where slot 0 of the entry's block sits in the sequence the
+        block was first laid out in: 16 b for the b-th block of a document (its position
+        inside the document), the logical offset for a private block. This is the stored
+        offset of a pool whose document keys were encoded per document from position 0."""
+        doc_blocks = self.info["doc_tokens"] // self.B
+        out = []
+        for lay in self.layouts:
+            st = []
+            for sg in lay.segments:
+                if sg.kind == "doc":
+                    st += [self.B * b for b in range(doc_blocks)]
+                else:
+                    st += [sg.start + self.B * b for b in range(-(-sg.tokens // self.B))]
+            out.append(np.array(st, dtype=np.int64))
+        return out
+
     def compact_views(self):
         """(k_pool, v_pool, per-seq compact ids) for host-side references."""
         return self.k_bits, self.v_bits, [self.compact_ids(s) for s in range(self.num_seqs)]
