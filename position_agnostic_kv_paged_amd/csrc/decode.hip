@@ -61,6 +61,9 @@ struct GroupMeta {
 // logical positions, so keys are read as stored and q' = R(p) q for the whole item.
 // PE = kAlibi rotates nothing (q' = q, keys as stored) and adds slope_h (L - p) to each
 // score, L = off_t + j from the packed word.
+// PE = kRopePartial is kRope over the permuted dim order of nat_chunk (partial rotary).
+// PE = kDocRotated reads keys stored with R(stored_t + j): keys are used as stored and
+// q' = R(p - (off_t - stored_t)) q, recomputed where off_t - stored_t changes.
 template <int D, int G, int PE>
 __global__ __launch_bounds__(kDecodeWaves * 64, 2) void decode_kernel(DecodeParams P) {
   constexpr bool PART = PE == kRopePartial;   // dims in the permuted order of nat_chunk

@@ -25,6 +25,11 @@
 // cross-half exchange. Values go straight from global memory into a padded LDS tile
 // (global_load_lds) and are transposed on read (ds_read_b64_tr_b16). The next key tile's
 // loads are in flight while the current one is multiplied; one barrier per key tile.
+//
+// Positional-encoding instances: kRope (above); kStored (keys already carry R(L): no key
+// rotation); kAlibi (no rotation, linear bias); kRopePartial (kRope over the permuted dim
+// order of nat_chunk); kDocRotated (keys stored with R(stored_b + j): each key tile is
+// rotated by R(off_b - stored_b - p_ref) from the block phase table alone).
 #include "lazyattn_common.h"
 #include "lazyattn_kernels.h"
 #include <limits.h>
