@@ -119,3 +119,25 @@ def test_workspace_sizes(L):
     b = lib.lazyattn_prefill_workspace_bytes(64, 64 * 256, 261, 32, 8, 128)
     assert a > 0 and b > 0
     assert L.lib().lazyattn_status_str(-5) == b"workspace too small"
+
+
+def test_binding_rejects_mixed_or_malformed_variant_arguments(L):
+    """The torch binding checks variant arguments before any library call (CPU tensors)."""
+    torch = pytest.importorskip("torch")
+    q = torch.zeros((4, 8, 128), dtype=torch.bfloat16)
+    pool = torch.zeros((6, 2, 16, 128), dtype=torch.bfloat16)
+    i32 = lambda *v: torch.tensor(v, dtype=torch.int32)
+    args = (q, pool, pool, i32(0, 2), i32(0, 0), i32(20), i32(0, 4), i32(16, 17, 18, 19),
+            10000.0, 2)
+    with pytest.raises(ValueError):                     # stored offsets must be int32
+        L.prefill(*args, stored_offsets=torch.zeros(2, dtype=torch.int64))
+    with pytest.raises(ValueError):                     # one stored offset per entry
+        L.prefill(*args, stored_offsets=i32(0))
+    with pytest.raises(ValueError):
+        L.decode(*args, stored_offsets=i32(0, 16), rotary_dim=32)
+    with pytest.raises(ValueError):
+        L.prefill(*args, rotary_dim=32, slopes=torch.zeros(8))
+    with pytest.raises(ValueError):                     # D/2 frequencies
+        L.prefill(*args, inv_freq=np.ones(10))
+    with pytest.raises(ValueError):                     # slopes: float32 [Hq]
+        L.decode(*args, slopes=torch.zeros(4))

@@ -244,6 +244,33 @@ def test_doc_rotated_pool_full_size_decode():
     compare(np.concatenate(got), np.concatenate(want), "decode-b64/docrot")
 
 
+@pytest.mark.parametrize("variant", ["partial-r32", "doc-rotated"])
+def test_variants_mixed_batch_with_empty_sequences(variant):
+    """Partial rotary and the document-rotated pool in one call holding prefill, decode,
+    zero-query and entry-less requests (through lazyattn_prefill_*, which routes single-row
+    requests to the decode kernel)."""
+    segs = [Segment("doc", 11, doc=0), Segment("doc", 60, doc=1),
+            Segment("private", 100, tokens=70)]
+    reqs = [RequestLayout([], 1, np.array([3])),
+            RequestLayout(segs, 70),
+            RequestLayout([Segment("doc", 0, doc=2), Segment("private", 32, tokens=5)], 1),
+            RequestLayout([Segment("doc", 0, doc=1), Segment("private", 32, tokens=2)], 0),
+            RequestLayout([], 2, np.array([0, 5]))]
+    wl = build("mixed-empty", 16, 2, 128, 16, 10000.0, 3, 32, reqs, seed=61)
+    say(f"{variant} on a mixed batch with empty requests")
+    if variant == "partial-r32":
+        got, want = run_hip(wl, "prefill", rotary_dim=32), oracle_out(wl, rotary_dim=32)
+    else:
+        from tests.util import doc_stored_offsets
+        st = doc_stored_offsets(wl)
+        wd, want = _docrot_case(wl, st)
+        got = run_hip(wd, "prefill", stored=st)
+    compare(got, want, f"mixed-empty/{variant}")
+    for s in (0, 4):
+        r0, r1 = int(wl.q_indptr[s]), int(wl.q_indptr[s + 1])
+        assert np.array_equal(got[r0:r1], np.zeros_like(got[r0:r1]))
+
+
 def _alibi_ref(wl, slopes):
     from oracle.alibi import alibi_attention
     return alibi_attention(wl.q_bits, wl.k_bits, wl.v_bits,
