@@ -617,3 +617,54 @@ def test_probes():
     cyc, flops = L.probe_mfma(4)
     torch.cuda.synchronize()
     assert flops > 0 and int(cyc.min().item()) > 0
+
+
+def _random_batch(seed):
+    """A seeded random batch: 1-4 requests of random documents (repeats allowed, gaps, some
+    back-to-back), a private tail (partial last block), random query counts including
+    single-row and zero-row requests; random G in {1, 2, 4, 8, 16, 32} and D in {64, 128}."""
+    rng = np.random.default_rng(seed)
+    D = int(rng.choice([64, 128]))
+    G = int(rng.choice([1, 2, 4, 8, 16, 32]))
+    Hkv = int(rng.choice([1, 2])) if G <= 16 else 1
+    n_docs, doc_tokens = 4, int(rng.choice([16, 32, 48]))
+    reqs = []
+    for _ in range(int(rng.integers(1, 5))):
+        pos = int(rng.integers(0, 3000))
+        segs = []
+        for _ in range(int(rng.integers(0, 5))):
+            segs.append(Segment("doc", pos, doc=int(rng.integers(0, n_docs))))
+            pos += doc_tokens + int(rng.choice([0, 0, rng.integers(1, 40)]))
+        tail = int(rng.integers(1, 60))
+        segs.append(Segment("private", pos, tokens=tail))
+        nq = int(rng.choice([0, 1, int(rng.integers(1, tail + 1)), tail]))
+        reqs.append(RequestLayout(segs, nq))
+    return build(f"random-{seed}", Hkv * G, Hkv, D, 16, 10000.0, n_docs, doc_tokens, reqs,
+                 seed=seed, q_scale=float(rng.choice([1.0, 3.0])))
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_random_layouts_all_modes(seed):
+    """Seeded random layouts through every positional-encoding entry point (RoPE, partial
+    rotary, document-rotated pool, ALiBi) via the mixed prefill call and the decode call."""
+    from oracle.alibi import alibi_slopes
+    from tests.util import doc_stored_offsets
+    wl = _random_batch(seed)
+    G, D = wl.Hq // wl.Hkv, wl.D
+    say(f"random layout {seed}: {wl.num_seqs} requests, G={G}, D={D}, rows={wl.total_q}")
+    if wl.total_q == 0:
+        return
+    want = oracle_out(wl)
+    r = 32 if D == 128 else 16
+    want_p = oracle_out(wl, rotary_dim=r)
+    st = doc_stored_offsets(wl)
+    wd, want_d = _docrot_case(wl, st)
+    slopes = alibi_slopes(wl.Hq)
+    want_a = _alibi_ref(wl, slopes)
+    qlen = np.diff(wl.q_indptr)
+    kinds = ["prefill"] + (["decode"] if np.all(qlen <= 1) else [])
+    for kind in kinds:
+        compare(run_hip(wl, kind), want, f"random{seed}/rope/{kind}")
+        compare(run_hip(wl, kind, rotary_dim=r), want_p, f"random{seed}/partial/{kind}")
+        compare(run_hip(wd, kind, stored=st), want_d, f"random{seed}/doc/{kind}")
+        compare(run_hip(wl, kind, slopes=slopes), want_a, f"random{seed}/alibi/{kind}")
