@@ -18,7 +18,7 @@ def words_for(wl):
 
 
 def run_hip(wl, kind, dev="cuda", tensors=None, words=None, repeat=1, inv_freq=None,
-            slopes=None, rotary_dim=None, stored=None):
+            slopes=None, rotary_dim=None, stored=None, max_entries=None):
     """Call lazyattn_prefill / lazyattn_decode on the workload; returns float64 [total_q,Hq,D]."""
     import torch
     import position_agnostic_kv_paged_amd as L
@@ -26,7 +26,8 @@ def run_hip(wl, kind, dev="cuda", tensors=None, words=None, repeat=1, inv_freq=N
     if words is None:
         words = words_for(wl)
     meta = torch.from_numpy(np.ascontiguousarray(words).view(np.int32)).to(dev)
-    max_entries = max(len(x) for x in wl.seq_block_ids)
+    if max_entries is None:
+        max_entries = max(len(x) for x in wl.seq_block_ids)
     fn = L.prefill if kind == "prefill" else L.decode
     st = None if stored is None else \
         torch.from_numpy(np.concatenate(stored).astype(np.int32)).to(dev)

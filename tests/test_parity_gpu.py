@@ -668,3 +668,17 @@ def test_random_layouts_all_modes(seed):
         compare(run_hip(wl, kind, rotary_dim=r), want_p, f"random{seed}/partial/{kind}")
         compare(run_hip(wd, kind, stored=st), want_d, f"random{seed}/doc/{kind}")
         compare(run_hip(wl, kind, slopes=slopes), want_a, f"random{seed}/alibi/{kind}")
+
+
+@pytest.mark.parametrize("kind", ["prefill", "decode"])
+@pytest.mark.parametrize("bound", [1, 3, 1000])
+def test_max_entries_hint_is_only_a_hint(kind, bound):
+    """max_entries below or far above the real block-table length changes the split-K work
+    split and the workspace size, never the result (long rows get longer splits)."""
+    segs_long = [Segment("doc", 7 + 32 * i, doc=i % 3) for i in range(40)] + \
+        [Segment("private", 7 + 32 * 40, tokens=9)]
+    reqs = [RequestLayout(segs_long, 9 if kind == "prefill" else 1),
+            RequestLayout([Segment("doc", 0, doc=1), Segment("private", 32, tokens=3)], 1)]
+    wl = build("hint", 8, 2, 128, 16, 10000.0, 3, 32, reqs, seed=71)
+    say(f"max_entries = {bound} (real {max(len(x) for x in wl.seq_block_ids)}) via {kind}")
+    compare(run_hip(wl, kind, max_entries=bound), oracle_out(wl), f"hint{bound}/{kind}")
