@@ -52,6 +52,18 @@ __device__ __forceinline__ void g2lds16(const void* g, void* lds_wave_base) {
 // position c ^ swz(R), so the four rows read by one 16-lane transposed read hit disjoint banks.
 __device__ __forceinline__ int vswz(int R) { return (R & 3) * 2; }
 
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+
+// R(j) on two rotate-half pairs at once in packed fp16: a, b hold (x_k, x_k+1) and
+// (x_k+D/2, x_k+1+D/2), c and s the pairs' cos and sin; returns {a c - b s, a s + b c}.
+// The products are the fp16 score operands themselves (they are rounded to fp16 anyway).
+__device__ __forceinline__ u32x2 rot_h2(uint32_t a, uint32_t b, uint32_t c, uint32_t s) {
+  const h2 A = __builtin_bit_cast(h2, a), Bv = __builtin_bit_cast(h2, b);
+  const h2 C = __builtin_bit_cast(h2, c), S = __builtin_bit_cast(h2, s);
+  return u32x2{__builtin_bit_cast(uint32_t, A * C - Bv * S),
+               __builtin_bit_cast(uint32_t, A * S + Bv * C)};
+}
+
 struct GroupMeta {
   int id[2], delta[2], nval[2];
   int st[2];                   // document-rotated pool: stored offset of the block's slot 0
@@ -85,7 +97,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 2) void decode_kernel(DecodePara
   __shared__ __align__(16) uint8_t lds_all[kDecodeWaves][2][BUF];
   // R(32) of every frequency: (cos, sin) interleaved, shared by the workgroup
   __shared__ __align__(16) float adv_all[D];
-  __shared__ __align__(16) f32x4 slot_tab[HC * 4 * 4 * 16];
+  __shared__ __align__(16) u32x2 slot_tab[HC * 4 * 4 * 16];   // fp16 (cos, cos), (sin, sin)
 
   // a call whose batch has no single-row sequence (a pure prefill batch) leaves no work:
   // leave before the per-workgroup constants and the queue atomic
@@ -103,8 +115,8 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 2) void decode_kernel(DecodePara
     dofs[c] = PART ? 8 * nat_chunk(4 * c + q4, P.rot_chunks, D / 16) : 32 * c + 8 * q4;
 
   // loop-invariant rotation constants, shared by the workgroup in LDS: R(j) of slot j for
-  // frequencies k = 32c + 8 q4 + 2 e2 + u as float4 (cos, sin of u = 0, 1) at
-  // [c][q4][e2][j] -- the 16 slots of a 16-lane read are consecutive 16-byte words; and
+  // frequencies k = 32c + 8 q4 + 2 e2 + u as packed fp16 pairs (cos u = 0, 1; sin u = 0, 1)
+  // at [c][q4][e2][j] -- the 16 slots of a 16-lane read are consecutive 8-byte words; and
   // R(32) for the per-group advance of q'
   for (int i = threadIdx.x; ROT && i < HC * 4 * 4 * 16; i += kDecodeWaves * 64) {
     const int j = i & 15, e2 = (i >> 4) & 3, qq = (i >> 6) & 3, c = i >> 8;
@@ -112,7 +124,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 2) void decode_kernel(DecodePara
     float c0, s0, c1, s1;
     rope_cos_sin(j, P.freqs[f0], c0, s0);
     rope_cos_sin(j, P.freqs[f0 + 1], c1, s1);
-    slot_tab[i] = f32x4{c0, s0, c1, s1};
+    slot_tab[i] = u32x2{pack_f16(c0, c1), pack_f16(s0, s1)};
   }
   if (threadIdx.x < D / 2) {                 // R(32) (PHC) or R(16): q' advance
     float cs, sn;
@@ -292,10 +304,10 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 2) void decode_kernel(DecodePara
               const float a0 = bf_lo(kcur[b][c][i]), a1 = bf_hi(kcur[b][c][i]);
               const float b0 = bf_lo(kcur[b][c + HC][i]), b1 = bf_hi(kcur[b][c + HC][i]);
               if (ROT) {
-                const f32x4 t = slot_tab[((c * 4 + q4) * 4 + i) * 16 + i16];
-                const float c0 = t[0], s0 = t[1], c1 = t[2], s1 = t[3];
-                lo[i] = pack_f16(a0 * c0 - b0 * s0, a1 * c1 - b1 * s1);
-                hi[i] = pack_f16(a0 * s0 + b0 * c0, a1 * s1 + b1 * c1);
+                const u32x2 t = slot_tab[((c * 4 + q4) * 4 + i) * 16 + i16];
+                const u32x2 r = rot_h2(pack_f16(a0, a1), pack_f16(b0, b1), t[0], t[1]);
+                lo[i] = r[0];
+                hi[i] = r[1];
               } else {
                 lo[i] = pack_f16(a0, a1);
                 hi[i] = pack_f16(b0, b1);
@@ -389,10 +401,10 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 2) void decode_kernel(DecodePara
               const float a0 = bf_lo(kcur[b][c][i]), a1 = bf_hi(kcur[b][c][i]);
               const float b0 = bf_lo(kcur[b][c + HC][i]), b1 = bf_hi(kcur[b][c + HC][i]);
               if (ROT) {
-                const f32x4 t = slot_tab[((c * 4 + q4) * 4 + i) * 16 + i16];
-                const float c0 = t[0], s0 = t[1], c1 = t[2], s1 = t[3];
-                lo[i] = pack_f16(a0 * c0 - b0 * s0, a1 * c1 - b1 * s1);
-                hi[i] = pack_f16(a0 * s0 + b0 * c0, a1 * s1 + b1 * c1);
+                const u32x2 t = slot_tab[((c * 4 + q4) * 4 + i) * 16 + i16];
+                const u32x2 r = rot_h2(pack_f16(a0, a1), pack_f16(b0, b1), t[0], t[1]);
+                lo[i] = r[0];
+                hi[i] = r[1];
               } else {
                 lo[i] = pack_f16(a0, a1);
                 hi[i] = pack_f16(b0, b1);
