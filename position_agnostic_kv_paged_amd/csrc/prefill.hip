@@ -45,6 +45,14 @@ __device__ __forceinline__ void g2lds16p(const void* g, void* lds_wave_base) {
 }
 
 
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ h2 as_h2(uint32_t u) { return __builtin_bit_cast(h2, u); }
+__device__ __forceinline__ uint32_t h2_bits(h2 v) { return __builtin_bit_cast(uint32_t, v); }
+// two bf16 values -> two fp16 values (one packed word)
+__device__ __forceinline__ h2 bf2_to_h2(uint32_t x) {
+  return as_h2(pack_f16(__uint_as_float(x << 16), __uint_as_float(x & 0xffff0000u)));
+}
+
 struct TileWords {
   int id[4], off[4], nval[4];
   int kmin, kmax;
@@ -147,8 +155,11 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
   __shared__ __align__(16) uint8_t Vs[2][VBYTES];
   // (cos, sin) tables as float4 = two frequencies, laid out [block or slot][pair][thread]
   // so that the staging threads of a wave read consecutive 16-byte words
-  __shared__ __align__(16) float4 tbl[2][4 * HALF / 2];  // cos/sin((off_b - p_ref) theta_k)
-  __shared__ __align__(16) float4 slot_cs[16 * HALF / 2]; // cos/sin(j theta_k), j < 16
+  // rotation tables as fp16 pairs, one 8-byte entry per two frequencies: {(cos, cos),
+  // (sin, sin)}, laid out [block or slot][pair][thread] so that the staging threads of a
+  // wave read consecutive 8-byte words
+  __shared__ __align__(16) u32x2 tbl[2][4 * HALF / 2];   // (off_b - p_ref) theta_k
+  __shared__ __align__(16) u32x2 slot_cs[16 * HALF / 2]; // j theta_k, j < 16
   __shared__ __align__(16) uint16_t Qs[NW][32 * KS];     // each wave's rotated queries (fp16)
   __shared__ double fr_s[HALF];
   __shared__ int pmax_s;
@@ -244,14 +255,17 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
   const int k_dhi = PART ? 8 * nat_chunk(FPT * cp / 8 + D / 16, P.rot_chunks, D / 16) +
                                FPT * cp % 8 - k_lo
                          : HALF;
-  // float2 position of frequency f of row r (a block or a slot) in the tables
+  // fp16 position of the cosine of frequency f of row r (a block or a slot) in the tables;
+  // its sine sits 2 further on
   auto tpos = [&](int r, int f) {
-    return ((r * (FPT / 2) + (f % FPT) / 2) * CPT + f / FPT) * 2 + (f & 1);
+    return ((r * (FPT / 2) + (f % FPT) / 2) * CPT + f / FPT) * 4 + (f & 1);
   };
   for (int i = tid; !DOC && i < 16 * HALF; i += NT) {       // R(j) table, loop invariant
     float c, sn;
     rope_cos_sin(i / HALF, fr_s[i % HALF], c, sn);
-    ((float2*)slot_cs)[tpos(i / HALF, i % HALF)] = make_float2(c, sn);
+    _Float16* t = (_Float16*)slot_cs + tpos(i / HALF, i % HALF);
+    t[0] = (_Float16)c;
+    t[2] = (_Float16)sn;
   }
 
   // The running max m rides on the matrix cores: an extra 16-wide k-step with
@@ -291,12 +305,12 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
   const int tab_b = __builtin_amdgcn_readfirstlane((tab_v >> 1) / HALF);   // wave-uniform
   const double tab_f = fr_s[(tab_v >> 1) % HALF];          // this thread's frequency
   const float tab_quarter = (tab_v & 1) ? 0.f : 0.25f;
-  const int tab_pos = 2 * tpos(tab_b, (tab_v >> 1) % HALF) + (tab_v & 1);
+  const int tab_pos = tpos(tab_b, (tab_v >> 1) % HALF) + 2 * (tab_v & 1);
   // (the per-lane block choice selects among readlane results, never indexes an array)
   auto make_table = [&](const WinDec& wd, int d, int buf) __attribute__((always_inline)) {
     if (!ROTATE) return;                                    // keys need no phase table
     const int o = rl(DOC ? wd.sh : wd.off, 4 * d + tab_b);
-    ((float*)tbl[buf])[tab_pos] = rope_sin_rev(o - p_ref, tab_f, tab_quarter);
+    ((_Float16*)tbl[buf])[tab_pos] = (_Float16)rope_sin_rev(o - p_ref, tab_f, tab_quarter);
   };
   // values of tile kt + d straight into LDS, wave-wide instruction i of this wave: slot
   // (row R, chunk c) of the padded tile; pad slots and invalid rows read the zeroed chunk
@@ -333,21 +347,17 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
     khi = *(const KRaw*)(src + k_dhi);
   };
   // rotation of frequencies 2 i2, 2 i2 + 1 of the staged key by R(off_b - p_ref) R(kj),
-  // from (cos, sin) pairs read out of the tables; results packed as fp16
-  auto rot_pair = [&](const float4 cs, const float4 js, uint32_t xlo, uint32_t xhi) -> u32x2 {
-    float ra[2], rb[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const float cb = u ? cs.z : cs.x, sb = u ? cs.w : cs.y;
-      const float cj = u ? js.z : js.x, sj = u ? js.w : js.y;
-      const float c = DOC ? cb : cb * cj - sb * sj;
-      const float sn = DOC ? sb : sb * cj + cb * sj;
-      const float a = u ? bf_hi(xlo) : bf_lo(xlo);
-      const float b = u ? bf_hi(xhi) : bf_lo(xhi);
-      ra[u] = a * c - b * sn;
-      rb[u] = a * sn + b * c;
+  // in packed fp16 from the (cos, sin) pairs of the tables (the result is an fp16 operand)
+  auto rot_pair = [&](const u32x2 cs, const u32x2 js, uint32_t xlo, uint32_t xhi) -> u32x2 {
+    h2 c = as_h2(cs[0]), sn = as_h2(cs[1]);
+    if (!DOC) {
+      const h2 cj = as_h2(js[0]), sj = as_h2(js[1]);
+      const h2 cc = c * cj - sn * sj;
+      sn = sn * cj + c * sj;
+      c = cc;
     }
-    return u32x2{pack_f16(ra[0], ra[1]), pack_f16(rb[0], rb[1])};
+    const h2 a = bf2_to_h2(xlo), b = bf2_to_h2(xhi);
+    return u32x2{h2_bits(a * c - b * sn), h2_bits(a * sn + b * c)};
   };
 
   // Software pipeline over key tiles. Iteration kt holds S(kt) on entry; it
@@ -375,11 +385,11 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
       load_k(wd, tt);
       KRaw ol, oh;
       if (ROTATE) {
-        const float4* t4 = &tbl[tt][kb * (FPT / 2) * CPT + cp];
-        const float4* j4 = &slot_cs[kj * (FPT / 2) * CPT + cp];
+        const u32x2* t4 = &tbl[tt][kb * (FPT / 2) * CPT + cp];
+        const u32x2* j4 = &slot_cs[kj * (FPT / 2) * CPT + cp];
 #pragma unroll
         for (int i2 = 0; i2 < FPT / 2; ++i2) {
-          const u32x2 r = rot_pair(t4[i2 * CPT], DOC ? float4{} : j4[i2 * CPT], klo[i2],
+          const u32x2 r = rot_pair(t4[i2 * CPT], DOC ? u32x2{} : j4[i2 * CPT], klo[i2],
                                    khi[i2]);
           ol[i2] = r[0];
           oh[i2] = r[1];
@@ -567,30 +577,33 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
           va[dt] = u32x4{r1[0], r1[1], r2[0], r2[1]};
         }
       };
-      const float4* t4 = &tbl[cur][kb * (FPT / 2) * CPT + cp];
-      const float4* j4 = &slot_cs[kj * (FPT / 2) * CPT + cp];
+      const u32x2* t4 = &tbl[cur][kb * (FPT / 2) * CPT + cp];
+      const u32x2* j4 = &slot_cs[kj * (FPT / 2) * CPT + cp];
       KRaw ol, oh;
-      float rc[2], rsn[2], ra[2], rb[2];
-      // piece 0/1: angle of frequency u = piece; piece 2/3: rotate frequency u = piece - 2
-      auto piece = [&](const int g, const int pc, const float4 cs, const float4 js) {
-        if (pc < 2) {
-          const int u = pc;
-          const float cb = u ? cs.z : cs.x, sb = u ? cs.w : cs.y;
-          const float cj = u ? js.z : js.x, sj = u ? js.w : js.y;
-          rc[u] = DOC ? cb : cb * cj - sb * sj;
-          rsn[u] = DOC ? sb : sb * cj + cb * sj;
-          asm volatile("" ::"v"(rc[u]), "v"(rsn[u]));
-        } else {
-          const int u = pc - 2;
-          const float x = u ? bf_hi(klo[g]) : bf_lo(klo[g]);
-          const float y = u ? bf_hi(khi[g]) : bf_lo(khi[g]);
-          ra[u] = x * rc[u] - y * rsn[u];
-          rb[u] = x * rsn[u] + y * rc[u];
-          if (u == 1) {
-            ol[g] = pack_f16(ra[0], ra[1]);
-            oh[g] = pack_f16(rb[0], rb[1]);
-            asm volatile("" ::"v"(ol[g]), "v"(oh[g]));
+      h2 rc, rsn, xa, xb;
+      // chunk g (two frequencies) in packed fp16, four pieces: 0 the angle R(off_b - p_ref)
+      // R(kj), 1 and 2 the key halves to fp16, 3 the rotation
+      auto piece = [&](const int g, const int pc, const u32x2 cs, const u32x2 js) {
+        if (pc == 0) {
+          rc = as_h2(cs[0]);
+          rsn = as_h2(cs[1]);
+          if (!DOC) {
+            const h2 cj = as_h2(js[0]), sj = as_h2(js[1]);
+            const h2 cc = rc * cj - rsn * sj;
+            rsn = rsn * cj + rc * sj;
+            rc = cc;
           }
+          asm volatile("" ::"v"(rc), "v"(rsn));
+        } else if (pc == 1) {
+          xa = bf2_to_h2(klo[g]);
+          asm volatile("" ::"v"(xa));
+        } else if (pc == 2) {
+          xb = bf2_to_h2(khi[g]);
+          asm volatile("" ::"v"(xb));
+        } else {
+          ol[g] = h2_bits(xa * rc - xb * rsn);
+          oh[g] = h2_bits(xa * rsn + xb * rc);
+          asm volatile("" ::"v"(ol[g]), "v"(oh[g]));
         }
       };
       auto plain = [&](const int g) {
@@ -600,12 +613,12 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
       };
       u32x4 va[D / 32];
       vread(0, va);
-      float4 cs = ROTATE ? t4[0] : float4{}, js = ROTATE && !DOC ? j4[0] : float4{};
+      u32x2 cs = ROTATE ? t4[0] : u32x2{}, js = ROTATE && !DOC ? j4[0] : u32x2{};
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         u32x4 vn[D / 32];
-        float4 csn = cs, jsn = js;
+        u32x2 csn = cs, jsn = js;
         if (g + 1 < 4) {
           vread(g + 1, vn);
           if (ROTATE && g + 1 < FPT / 2) {
