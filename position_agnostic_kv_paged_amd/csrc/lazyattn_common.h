@@ -180,6 +180,30 @@ __device__ __forceinline__ int upper_seq(const int32_t* prefix, int n, int x) {
   return lo;
 }
 
+// The same search by one whole wave (every lane calls it; the result is wave-uniform): 64
+// probes per round of loads, so up to 64 sequences take one memory round trip instead of
+// log2(n) dependent ones. Requires prefix[0] <= x. Returns s and prefix[s].
+struct SeqFound {
+  int s, start;
+};
+__device__ __forceinline__ SeqFound wave_upper_seq(const int32_t* prefix, int n, int x,
+                                                   int lane) {
+  int lo = 0, hi = n;                          // prefix[lo] <= x, answer in [lo, hi)
+  while (hi - lo > 64) {
+    const int span = hi - lo;
+    const int idx = lo + (int)(((long long)lane * span) / 64);
+    const unsigned long long bal = __ballot(prefix[idx] <= x);   // lane 0 always set
+    const int top = 63 - __builtin_clzll(bal);
+    const int nlo = lo + (int)(((long long)top * span) / 64);
+    if (top < 63) hi = lo + (int)(((long long)(top + 1) * span) / 64);
+    lo = nlo;
+  }
+  const int span = hi - lo;
+  const int v = prefix[lo + min(lane, span - 1)];
+  const int top = 63 - __builtin_clzll(__ballot(lane < span && v <= x));
+  return SeqFound{__builtin_amdgcn_readfirstlane(lo + top), __builtin_amdgcn_readlane(v, top)};
+}
+
 // ---- workspace layout -----------------------------------------------------------------------
 // [0, 512)                RoPE frequency table, double [64] (revolutions per position)
 // [512, 768)              reserved; 16-byte zero rows at 576..767

@@ -68,9 +68,20 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams P) {
   constexpr int HPB = 256 / TPH;              // heads per block
   constexpr int CH = 16;                      // splits loaded together
   __shared__ long long s_item0;
-  __shared__ int s_splits;
-  const int r = blockIdx.x;
-  if (threadIdx.x < 64) {
+  __shared__ int s_splits, s_row;
+  if (P.mode != kPlanDecodeOnly) {
+    // a batch of any query lengths: only single-row sequences have partials, so workgroup
+    // x takes sequence x (no search) and prefill sequences leave at once
+    if (threadIdx.x == 0) {
+      const int seq = blockIdx.x;
+      const int q0 = P.q_indptr[seq], qlen = P.q_indptr[seq + 1] - q0;
+      const int T = P.block_table[seq + 1] - P.block_table[seq];
+      s_splits = qlen == 1 ? row_splits(T, P.bps, P.smax) : 0;
+      s_item0 = P.dec_prefix[seq];
+      s_row = q0;
+    }
+  } else if (threadIdx.x < 64) {
+    const int r = blockIdx.x;
     const int lane = threadIdx.x;
     int lo = 0, hi = P.num_seqs;              // q_indptr[lo] <= r < q_indptr[hi]
     while (hi - lo > 64) {                    // 64 probes spread over [lo, hi)
@@ -95,9 +106,11 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams P) {
       const int splits = row_splits(T, P.bps, P.smax);
       s_splits = dec ? splits : 0;            // prefill rows are written by the prefill kernel
       s_item0 = (long long)P.dec_prefix[seq] + (long long)(r - q0) * splits;
+      s_row = r;
     }
   }
   __syncthreads();
+  const int r = s_row;
   const int splits = s_splits;
   const long long item0 = s_item0;
   const int h = blockIdx.y * HPB + threadIdx.x / TPH;
@@ -159,10 +172,12 @@ hipError_t launch_plan(const PlanParams& p, hipStream_t st) {
 
 hipError_t launch_merge(const MergeParams& p, int total_q, int D, hipStream_t st) {
   if (total_q == 0) return hipSuccess;
+  // one workgroup per query row, or per sequence where only single-row sequences merge
+  const unsigned rows = p.mode == kPlanDecodeOnly ? (unsigned)total_q : (unsigned)p.num_seqs;
   if (D == 128) {
-    hipLaunchKernelGGL(merge_kernel<128>, dim3(total_q, (p.Hq + 7) / 8), dim3(256), 0, st, p);
+    hipLaunchKernelGGL(merge_kernel<128>, dim3(rows, (p.Hq + 7) / 8), dim3(256), 0, st, p);
   } else {
-    hipLaunchKernelGGL(merge_kernel<64>, dim3(total_q, (p.Hq + 15) / 16), dim3(256), 0, st, p);
+    hipLaunchKernelGGL(merge_kernel<64>, dim3(rows, (p.Hq + 15) / 16), dim3(256), 0, st, p);
   }
   return hipGetLastError();
 }

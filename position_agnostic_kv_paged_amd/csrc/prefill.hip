@@ -176,18 +176,18 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
   const int kvh = Lp / tiles_bound;
   const int tile_id = Lp - kvh * tiles_bound;
   if (kvh >= P.Hkv || tile_id >= P.pf_prefix[P.num_seqs]) return;   // uniform
-  const int seq = __builtin_amdgcn_readfirstlane(upper_seq(P.pf_prefix, P.num_seqs, tile_id));
-  const int qt = __builtin_amdgcn_readfirstlane(tile_id - P.pf_prefix[seq]);
+  // The prologue is a chain of dependent memory round trips (sequence, its CSR entries,
+  // then its queries, positions and words, then the first keys); independent loads are
+  // issued together so that each link costs one trip.
+  const SeqFound sf = wave_upper_seq(P.pf_prefix, P.num_seqs, tile_id, lane);
+  const int seq = sf.s;
+  const int qt = __builtin_amdgcn_readfirstlane(tile_id - sf.start);
   const int q0 = __builtin_amdgcn_readfirstlane(P.q_indptr[seq]);
   const int qlen = __builtin_amdgcn_readfirstlane(P.q_indptr[seq + 1] - q0);
   const int e0 = __builtin_amdgcn_readfirstlane(P.block_table[seq]);
   const int T = __builtin_amdgcn_readfirstlane(P.block_table[seq + 1] - e0);
   const int kvlen = __builtin_amdgcn_readfirstlane(P.kv_lens[seq]);
   const int p_ref = ROTATE ? __builtin_amdgcn_readfirstlane(P.q_pos[q0 + qt * POS]) : 0;
-
-  for (int i = tid; i < HALF; i += NT) fr_s[i] = P.freqs[i];
-  if (tid == 0) pmax_s = INT_MIN;
-  __syncthreads();
 
   // ---- this lane's query row -------------------------------------------------------------
   const int col = lane & 31, hh = lane >> 5;
@@ -197,19 +197,30 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
   const int kvp = kvh / P.kv_group;                          // pool head of this work head
   const bool row_ok = qi < qlen;
   const int p = row_ok ? P.q_pos[q0 + qi] : INT_MIN;       // invalid rows see no key
+  // raw query row (rotated below) and the words of key tiles 0 .. 3, in flight together
+  // with the frequency table
+  u32x4 qraw[NCH];
+  {
+    const uint16_t* qrow = P.q + ((size_t)(q0 + (row_ok ? qi : 0)) * P.Hq + h) * D;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+      qraw[c] = row_ok ? *(const u32x4*)(qrow + (PART ? 8 * nat_chunk(2 * c + hh, P.rot_chunks,
+                                                                      D / 16)
+                                                       : 16 * c + 8 * hh))
+                       : u32x4{0, 0, 0, 0};
+  }
+  uint32_t win = load_window(P, e0, T, 0, lane);           // words of tiles 0 .. 3
+  const int st0 = DOC ? load_stored(P, e0, T, 0, lane) : 0;
+
+  for (int i = tid; i < HALF; i += NT) fr_s[i] = P.freqs[i];
+  if (tid == 0) pmax_s = INT_MIN;
+  __syncthreads();
 
   // Q~ rows of this wave -> LDS (fp16, row-major): lane holds dims 16c + 8hh + e (e < 8) of
   // its row; the rotate-half partner of chunk c is chunk c + NCH/2 (dims + D/2), same lane.
   uint16_t* qs = Qs[w];
   {
-    u32x4 raw[NCH];
-    const uint16_t* qrow = P.q + ((size_t)(q0 + (row_ok ? qi : 0)) * P.Hq + h) * D;
-#pragma unroll
-    for (int c = 0; c < NCH; ++c)
-      raw[c] = row_ok ? *(const u32x4*)(qrow + (PART ? 8 * nat_chunk(2 * c + hh, P.rot_chunks,
-                                                                     D / 16)
-                                                      : 16 * c + 8 * hh))
-                      : u32x4{0, 0, 0, 0};
+    const u32x4 (&raw)[NCH] = qraw;
     const int n = row_ok ? p - p_ref : 0;
     const float sc = P.scale_log2;                  // softmax scale folded into Q~
 #pragma unroll
@@ -338,14 +349,15 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
   KRaw klo{}, khi{};
   // raw keys of a tile into (klo, khi); empty slots read as zero
   // (key staging reads block kb of tile kt + d: lane 4 d + kb of the decoded window)
-  auto load_k = [&](const WinDec& wd, int d) {
+  auto load_k_to = [&](const WinDec& wd, int d, KRaw& lo, KRaw& hi) {
     const int nv = rl(wd.nv, 4 * d + kb), id = rl(wd.id, 4 * d + kb);
     // branch-free: empty slots load from the zeroed workspace chunk (0 < k_dhi <= D/2)
     const uint16_t* src = (const uint16_t*)blend_ptr(
         kj < nv, P.k_pool + (((size_t)id * P.Hkv_pool + kvp) * kBlock + kj) * D + k_lo, P.zero);
-    klo = *(const KRaw*)src;
-    khi = *(const KRaw*)(src + k_dhi);
+    lo = *(const KRaw*)src;
+    hi = *(const KRaw*)(src + k_dhi);
   };
+  auto load_k = [&](const WinDec& wd, int d) { load_k_to(wd, d, klo, khi); };
   // rotation of frequencies 2 i2, 2 i2 + 1 of the staged key by R(off_b - p_ref) R(kj),
   // in packed fp16 from the (cos, sin) pairs of the tables (the result is an fp16 operand)
   auto rot_pair = [&](const u32x2 cs, const u32x2 js, uint32_t xlo, uint32_t xhi) -> u32x2 {
@@ -370,10 +382,11 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
   // vector work that hides under it, LDS operands are fetched one MFMA group ahead, and the
   // loads for later tiles are spread over A's k-steps so that the vector memory path
   // overlaps the matrix cores instead of stalling every wave right after the barrier.
-  uint32_t win = load_window(P, e0, T, 0, lane);           // words of tiles 0 .. 3
-  const int st0 = DOC ? load_stored(P, e0, T, 0, lane) : 0;
   if (n_kt > 0) {
     const WinDec wd = decode_window(P, win, st0, T, kvlen, 0, lane);
+    KRaw kraw[2][2];                                         // raw keys of tiles 0 and 1
+    load_k_to(wd, 0, kraw[0][0], kraw[0][1]);
+    load_k_to(wd, 1, kraw[1][0], kraw[1][1]);
     make_table(wd, 0, 0);
     make_table(wd, 1, 1);
 #pragma unroll
@@ -382,7 +395,8 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
     __syncthreads();                                         // tables 0, 1 visible
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {                         // keys of tiles 0 and 1
-      load_k(wd, tt);
+      const KRaw& klo = kraw[tt][0];
+      const KRaw& khi = kraw[tt][1];
       KRaw ol, oh;
       if (ROTATE) {
         const u32x2* t4 = &tbl[tt][kb * (FPT / 2) * CPT + cp];
