@@ -273,15 +273,19 @@ def measured_ceilings(torch, L, stream, reps=5):
     iters = 2000
     cyc = torch.empty(L.probe_cus() * 8, dtype=torch.int64, device="cuda")
     buf = torch.empty(1 << 29, dtype=torch.int32, device="cuda").fill_(7)
-    mf, ghz, rd = [], [], []
+    half = buf.numel() // 2
+    mf, ghz, rd, cp = [], [], [], []
     for r in range(reps + 1):
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
         e[0].record(stream)
         _, flops = L.probe_mfma(iters, cycles=cyc, stream=stream)
         e[1].record(stream)
         e[2].record(stream)
         L.probe_read(buf, stream=stream)
         e[3].record(stream)
+        e[4].record(stream)
+        buf[half:].copy_(buf[:half])                       # plain device copy, 1 GiB each way
+        e[5].record(stream)
         torch.cuda.synchronize()
         if r == 0:
             continue                                       # first launch: code load
@@ -289,11 +293,13 @@ def measured_ceilings(torch, L, stream, reps=5):
         mf.append(flops / t / 1e12)
         ghz.append(float(cyc.max().item()) / t / 1e9)
         rd.append(buf.numel() * 4 / (e[2].elapsed_time(e[3]) / 1e3) / 1e9)
+        cp.append(2 * half * 4 / (e[4].elapsed_time(e[5]) / 1e3) / 1e9)
     del buf
     return {"mfma_f16_tflops": float(np.median(mf)), "shader_ghz": float(np.median(ghz)),
-            "hbm_read_gbs": float(np.median(rd)),
+            "hbm_read_gbs": float(np.median(rd)), "hbm_copy_gbs": float(np.median(cp)),
             "note": "MFMA: 8 waves/CU of independent 32x32x16 fp16 products; read: 2 GiB, "
-                    "16-byte non-temporal loads, 8 workgroups of 256 per CU"}
+                    "16-byte non-temporal loads, 8 workgroups of 256 per CU; copy: torch "
+                    "device-to-device copy of 1 GiB, read + write bytes"}
 
 
 def main():
@@ -540,6 +546,7 @@ def main():
         line["prefill"]["frac_measured_mfma"] = line["prefill"]["value"] / ceil["mfma_f16_tflops"]
     if "decode" in line:
         line["decode"]["frac_measured_read"] = line["decode"]["value"] / ceil["hbm_read_gbs"]
+    line["ingest"]["frac_measured_copy"] = line["ingest"]["gbs"] / ceil["hbm_copy_gbs"]
     if not args.no_cpu_baseline and wl.name == WORKLOAD and pre_seqs and dec_seqs:
         line["cpu_baseline"] = cpu_baseline(wl, pre_seqs, dec_seqs)
     print(json.dumps(line), flush=True)

@@ -31,7 +31,8 @@ def _dev(a):
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
 
 
-@pytest.mark.parametrize("D,Hkv,n", [(128, 8, 1000), (64, 2, 37), (128, 1, 1)])
+@pytest.mark.parametrize("D,Hkv,n", [(128, 8, 1000), (64, 2, 37), (128, 1, 1), (128, 3, 333),
+                                      (64, 5, 1531)])
 def test_ingest_bit_exact(D, Hkv, n):
     import position_agnostic_kv_paged_amd as L
     rng = np.random.default_rng(D + Hkv + n)
