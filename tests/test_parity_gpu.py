@@ -494,6 +494,29 @@ def test_shifted_document_is_detected():
     assert np.max(np.abs(got - good)) > 2e-2
 
 
+@pytest.mark.parametrize("kind", ["prefill", "decode"])
+def test_negative_control_rotation_compiled_out(kind):
+    """Negative control: the kernels with the key rotation compiled out (the materialised
+    baseline's entry points, which expect every key already rotated to its position) run on
+    the position-free pool must fail the tolerance against the oracle. The parity bar can
+    therefore see a missing rotation. The same call with the rotation passes."""
+    import torch
+    import position_agnostic_kv_paged_amd as L
+    wl = small(Hq=8, Hkv=2, D=128, seed=91, q_scale=4.0)
+    want = oracle_out(wl)
+    t = wl.to_device("cuda")
+    meta = torch.from_numpy(np.ascontiguousarray(words_for(wl)).view(np.int32)).to("cuda")
+    fn = L.prefill_rotated_pool if kind == "prefill" else L.decode_rotated_pool
+    say(f"negative control: rotation compiled out via {kind}")
+    out = fn(t["q"], t["k_pool"], t["v_pool"], t["block_table"], meta, t["kv_lens"],
+             t["q_indptr"], t["q_pos"], wl.rope_base, max(len(x) for x in wl.seq_block_ids))
+    torch.cuda.synchronize()
+    bad = out.float().cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(bad))
+    assert np.max(np.abs(bad - want)) > 2e-2 or np.mean(np.abs(bad - want)) > 2e-3
+    compare(run_hip(wl, kind), want, f"negative-control-reference/{kind}")
+
+
 # ------------------------------------------------------------------ full-size workloads
 
 def _sampled(wl, kind, seqs, rows_of, inv_freq=None, slopes=None, rotary_dim=None):
