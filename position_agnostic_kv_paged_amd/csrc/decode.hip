@@ -30,6 +30,7 @@
 // partial (o, m, l); merge_kernel combines the splits of a row.
 #include "lazyattn_common.h"
 #include "lazyattn_kernels.h"
+#include <atomic>
 
 namespace lazyattn {
 
@@ -493,18 +494,26 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 2) void decode_kernel(DecodePara
   }
 }
 
-static int g_num_cus = 0;
+// Compute units of each device, queried once per device. Host threads calling at the same
+// time may both fill an entry; they store the same value, and the atomics make that race
+// well-defined.
+constexpr int kMaxDevices = 64;
+static std::atomic<int> g_num_cus[kMaxDevices];
 
 static int num_cus() {
-  if (g_num_cus == 0) {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        n <= 0)
-      n = 256;                                       // MI355X (also when no device is visible)
-    g_num_cus = n;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = -1;
+  if (dev >= 0) {
+    const int known = g_num_cus[dev].load(std::memory_order_relaxed);
+    if (known > 0) return known;
   }
-  return g_num_cus;
+  int n = 0;
+  if (dev < 0 ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n <= 0)
+    n = 256;                                         // MI355X (also when no device is visible)
+  if (dev >= 0) g_num_cus[dev].store(n, std::memory_order_relaxed);
+  return n;
 }
 
 int decode_resident_waves() { return num_cus() * kDecodeWgPerCu * kDecodeWaves; }
