@@ -33,6 +33,21 @@
  *    L <= p. A query with no visible key outputs zeros.
  *  - Return value: LAZYATTN_OK (0) or a negative LAZYATTN_ERR_* code; no exception, abort
  *    or other failure leaves the ABI.
+ *  - Row arrays: q_indptr must be non-decreasing with q_indptr[0] = 0 and
+ *    q_indptr[num_seqs] = total_q. Rows the table places at or past total_q are neither
+ *    read nor written, and no partial buffer is written past its size, but their outputs
+ *    are then missing: such a call is a caller error the library cannot see (it never reads
+ *    device memory on the host).
+ *  - Operand range. Rotated queries and keys enter the score products as fp16 (11-bit
+ *    significands, 3 more than bf16, at the same matrix-core rate), so every rotate-half
+ *    pair (x_k, x_{k+D/2}) of a key must have Euclidean norm below 65504 (then every rotated
+ *    element is representable); so must every pair of a query row scaled by log2(e)/sqrt(D)
+ *    in the prefill kernel, and of the unscaled query row in the decode kernel. The prefill
+ *    kernel keeps its running score maximum (log2 domain, q.k log2(e)/sqrt(D)) as 256 times
+ *    an fp16 value: scores must stay below about 1.6e7 in magnitude. Values past these
+ *    bounds become inf and the affected rows NaN; bf16 inputs can exceed them, real model
+ *    activations (|x| < ~1e3) do not. Probabilities multiply bf16 values in P.V; sums,
+ *    maxima and accumulators are fp32.
  */
 #ifndef LAZYATTN_H
 #define LAZYATTN_H
@@ -358,6 +373,25 @@ size_t lazyattn_prefill_workspace_bytes(int32_t num_seqs, int32_t total_q, int32
                                         int32_t Hq, int32_t Hkv, int32_t D);
 size_t lazyattn_decode_workspace_bytes(int32_t num_seqs, int32_t total_q, int32_t max_entries,
                                        int32_t Hq, int32_t Hkv, int32_t D);
+
+/*
+ * lazyattn_llama31_inv_freq -- host helper: the frequency-scaled RoPE table of the Llama 3.1
+ * models, D/2 values theta_k (radians per position) for the *_freqs entry points (the
+ * summary only claims compatibility with RoPE variants; this is one such table).
+ * theta_k = base^(-2k/D); with wavelength w = 2 pi / theta_k, a pair with
+ * w < original_context / high_freq_factor keeps theta_k, one with
+ * w > original_context / low_freq_factor gets theta_k / factor, and in between
+ * s = (original_context / w - low_freq_factor) / (high_freq_factor - low_freq_factor)
+ * blends them: (1 - s) theta_k / factor + s theta_k. Llama 3.1 uses base 500000, factor 8,
+ * low 1, high 4, original_context 8192.
+ *  inv_freq_out  host double [D/2], written in full on success
+ * Errors: NULL output (ERR_NULL); D odd, <= 0 or above 128 (ERR_SHAPE); base <= 1,
+ * factor < 1, high_freq_factor <= low_freq_factor or a non-positive factor / context
+ * (ERR_ARG). Touches no device.
+ */
+int lazyattn_llama31_inv_freq(int32_t D, double base, double factor, double low_freq_factor,
+                              double high_freq_factor, double original_context,
+                              double* inv_freq_out);
 
 /*
  * lazyattn_encode_meta -- HOST function: pack per-entry (block id, logical offset) into

@@ -20,6 +20,7 @@ EXPORTED = [
     "lazyattn_pool_alloc_private", "lazyattn_pool_free_private", "lazyattn_pool_stats",
     "lazyattn_prefill_workspace_bytes",
     "lazyattn_decode_workspace_bytes", "lazyattn_encode_meta", "lazyattn_debug_decode_meta",
+    "lazyattn_llama31_inv_freq",
     "lazyattn_status_str", "lazyattn_version",
 ]
 
@@ -88,6 +89,8 @@ def lib():
                        ("lazyattn_pool_stats", [vp, ctypes.POINTER(PoolStats)])):
         f = getattr(L, name)
         f.argtypes, f.restype = args, ctypes.c_int
+    L.lazyattn_llama31_inv_freq.argtypes = [i32, dbl, dbl, dbl, dbl, dbl, vp]
+    L.lazyattn_llama31_inv_freq.restype = ctypes.c_int
     L.lazyattn_encode_meta.argtypes = [vp, vp, vp, i32, i32, vp, vp]
     L.lazyattn_encode_meta.restype = ctypes.c_int
     L.lazyattn_debug_decode_meta.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp]

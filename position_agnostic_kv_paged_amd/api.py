@@ -116,16 +116,14 @@ def decode(q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indptr, q_pos,
 
 def llama31_inv_freq(D, base=500000.0, factor=8.0, low_freq_factor=1.0, high_freq_factor=4.0,
                      original_context=8192):
-    """Frequency-scaled RoPE table of the Llama 3.1 models (host, float64, D/2 entries):
-    pairs whose wavelength 2 pi / theta is shorter than original_context / high_freq_factor
-    keep theta, those longer than original_context / low_freq_factor use theta / factor, and
-    in between theta is interpolated linearly in original_context / wavelength."""
-    theta = np.power(float(base), -np.arange(0, D, 2, dtype=np.float64) / D)
-    wavelen = 2.0 * np.pi / theta
-    smooth = (original_context / wavelen - low_freq_factor) / (high_freq_factor - low_freq_factor)
-    mid = (1.0 - smooth) * theta / factor + smooth * theta
-    out = np.where(wavelen < original_context / high_freq_factor, theta, mid)
-    return np.where(wavelen > original_context / low_freq_factor, theta / factor, out)
+    """lazyattn_llama31_inv_freq: the Llama 3.1 frequency-scaled RoPE table (host, float64,
+    D/2 radians per position) for the *_freqs entry points."""
+    out = np.zeros(D // 2 if D > 0 else 1, dtype=np.float64)
+    rc = lib().lazyattn_llama31_inv_freq(int(D), float(base), float(factor),
+                                         float(low_freq_factor), float(high_freq_factor),
+                                         float(original_context), out.ctypes.data)
+    check(rc, "lazyattn_llama31_inv_freq")
+    return out
 
 
 def prefill_rotated_pool(q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indptr, q_pos,

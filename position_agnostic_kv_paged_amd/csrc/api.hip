@@ -4,6 +4,7 @@
 #include "lazyattn_common.h"
 #include "lazyattn_kernels.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -138,17 +139,18 @@ int run(const void* q, const void* k_pool, const void* v_pool, const int32_t* bl
                     block_table, block_meta, kv_lens, q_indptr, q_positions,
                     (uint16_t*)out, pf_prefix, (const uint16_t*)zero, num_seqs, Hq, Hw,
                     num_blocks, (int)tiles, scale_log2, freqs, slopes, Hkv, kv_group, r / 16,
-                    stored_offsets};
+                    stored_offsets, total_q};
     if (launch_prefill(P, D, G, pe, st) != hipSuccess) return LAZYATTN_ERR_LAUNCH;
   }
   DecodeParams Dp{(const uint16_t*)q, (const uint16_t*)k_pool, (const uint16_t*)v_pool,
                   block_table, block_meta, kv_lens, q_indptr, q_positions, dec_prefix,
                   (const uint16_t*)zero, partials, num_seqs, Hq, Hw, num_blocks,
                   ds.bps, ds.smax, scale_log2, freqs, slopes, Hkv, kv_group, r / 16,
-                  stored_offsets};
+                  stored_offsets, total_q,
+                  (int)std::min<long long>((long long)rows_bound * ds.smax, INT32_MAX)};
   if (launch_decode(Dp, D, G, pe, st) != hipSuccess) return LAZYATTN_ERR_LAUNCH;
   MergeParams Mp{q_indptr, block_table, dec_prefix, partials, (uint16_t*)out,
-                 num_seqs, Hq, ds.bps, ds.smax, mode};
+                 num_seqs, Hq, ds.bps, ds.smax, mode, total_q};
   if (launch_merge(Mp, total_q, D, st) != hipSuccess) return LAZYATTN_ERR_LAUNCH;
   return LAZYATTN_OK;
 }
@@ -351,6 +353,37 @@ int lazyattn_encode_meta(const int32_t* block_ids, const int64_t* offsets,
     }
   }
   return rc;
+}
+
+int lazyattn_llama31_inv_freq(int32_t D, double base, double factor, double low_freq_factor,
+                              double high_freq_factor, double original_context,
+                              double* inv_freq_out) {
+  if (!inv_freq_out) return LAZYATTN_ERR_NULL;
+  if (D <= 0 || D % 2 || D / 2 > kMaxHalfDim) return LAZYATTN_ERR_SHAPE;
+  if (!(base > 1.0) || !(factor >= 1.0) || !(low_freq_factor > 0.0) ||
+      !(high_freq_factor > low_freq_factor) || !(original_context > 0.0) ||
+      !std::isfinite(base) || !std::isfinite(factor) || !std::isfinite(high_freq_factor) ||
+      !std::isfinite(original_context))
+    return LAZYATTN_ERR_ARG;
+  // wavelength 2 pi / theta against the context the model was trained on: short waves keep
+  // theta, long waves are slowed by `factor`, the band between is a linear blend in
+  // original_context / wavelength
+  const double short_wave = original_context / high_freq_factor;
+  const double long_wave = original_context / low_freq_factor;
+  for (int k = 0; k < D / 2; ++k) {
+    const double theta = std::pow(base, -2.0 * k / D);
+    const double wave = 2.0 * M_PI / theta;
+    double t = theta;
+    if (wave > long_wave) {
+      t = theta / factor;
+    } else if (wave >= short_wave) {
+      const double w = (original_context / wave - low_freq_factor) /
+                       (high_freq_factor - low_freq_factor);
+      t = (1.0 - w) * theta / factor + w * theta;
+    }
+    inv_freq_out[k] = t;
+  }
+  return LAZYATTN_OK;
 }
 
 int lazyattn_materialize_rotated(const void* k_pool, const void* v_pool,

@@ -101,8 +101,9 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 2) void decode_kernel(DecodePara
   __shared__ __align__(16) u32x2 slot_tab[HC * 4 * 4 * 16];   // fp16 (cos, cos), (sin, sin)
 
   // a call whose batch has no single-row sequence (a pure prefill batch) leaves no work:
-  // leave before the per-workgroup constants and the queue atomic
-  const int n_items = P.dec_prefix[P.num_seqs] * P.Hkv;
+  // leave before the per-workgroup constants. Row-splits past the partial buffer (only
+  // possible when q_indptr runs past total_q) are never started.
+  const int n_items = min(P.dec_prefix[P.num_seqs], P.rowsplit_cap) * P.Hkv;
   if (n_items == 0) return;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   uint8_t* lds = lds_all[w][0];
@@ -158,6 +159,10 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 2) void decode_kernel(DecodePara
         x_eb = sp * bpsr;
         x_ee = min(T, x_eb + bpsr);
         x_r = P.q_indptr[seq] + row;
+        if (x_r >= P.total_q) {                       // past the q array: no work, no partial
+          x_r = 0;
+          x_ee = x_eb;
+        }
         x_p = P.q_pos[x_r];
       }
     }

@@ -265,6 +265,15 @@ __device__ __forceinline__ uint32_t f16_bits(float x) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
 }
 
+// The smallest fp16 value >= x, as a float (x finite; values above 65504 give +inf).
+__device__ __forceinline__ float f16_round_up(float x) {
+  const _Float16 r = (_Float16)x;
+  if ((float)r >= x) return (float)r;
+  uint16_t b = __builtin_bit_cast(uint16_t, r);
+  b = (b & 0x8000u) ? (uint16_t)(b - 1u) : (uint16_t)(b + 1u);   // one ulp towards +inf
+  return (float)__builtin_bit_cast(_Float16, b);
+}
+
 // Plan modes.
 enum PlanMode : int { kPlanMixed = 0, kPlanDecodeOnly = 1 };
 

@@ -40,6 +40,7 @@ struct PrefillParams {
   int Hkv_pool, kv_group;    // pool KV heads; work heads per pool head (see below)
   int rot_chunks;            // rotary_dim / 16 (kRopePartial only; nat_chunk)
   const int32_t* stored;     // [entries] stored rotation offset of slot 0 (kDocRotated only)
+  int total_q;               // rows of q and out: rows at or past it are never touched
 };
 
 // More than 16 query heads per KV head (G = 16 S): the kernels run Hkv * S "work heads" of
@@ -65,6 +66,8 @@ struct DecodeParams {
   int Hkv_pool, kv_group;    // as in PrefillParams
   int rot_chunks;            // as in PrefillParams
   const int32_t* stored;     // as in PrefillParams
+  int total_q;               // as in PrefillParams
+  int rowsplit_cap;          // row-splits the partial buffer holds; items past it are skipped
 };
 
 struct MergeParams {
@@ -74,6 +77,7 @@ struct MergeParams {
   const float* partials;
   uint16_t* out;
   int num_seqs, Hq, bps, smax, mode;
+  int total_q;               // rows of out
 };
 
 hipError_t launch_plan(const PlanParams& p, hipStream_t st);

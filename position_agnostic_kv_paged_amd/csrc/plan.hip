@@ -76,7 +76,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams P) {
       const int seq = blockIdx.x;
       const int q0 = P.q_indptr[seq], qlen = P.q_indptr[seq + 1] - q0;
       const int T = P.block_table[seq + 1] - P.block_table[seq];
-      s_splits = qlen == 1 ? row_splits(T, P.bps, P.smax) : 0;
+      s_splits = (qlen == 1) & (q0 < P.total_q) ? row_splits(T, P.bps, P.smax) : 0;
       s_item0 = P.dec_prefix[seq];
       s_row = q0;
     }

@@ -187,7 +187,9 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
   const int e0 = __builtin_amdgcn_readfirstlane(P.block_table[seq]);
   const int T = __builtin_amdgcn_readfirstlane(P.block_table[seq + 1] - e0);
   const int kvlen = __builtin_amdgcn_readfirstlane(P.kv_lens[seq]);
-  const int p_ref = ROTATE ? __builtin_amdgcn_readfirstlane(P.q_pos[q0 + qt * POS]) : 0;
+  // (rows at or past total_q -- a q_indptr that runs past the q array -- are not touched)
+  const int p_ref =
+      ROTATE ? __builtin_amdgcn_readfirstlane(P.q_pos[min(q0 + qt * POS, P.total_q - 1)]) : 0;
 
   // ---- this lane's query row -------------------------------------------------------------
   const int col = lane & 31, hh = lane >> 5;
@@ -195,13 +197,13 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
   const int qi = qt * POS + rho / G;
   const int h = kvh * G + rho % G;
   const int kvp = kvh / P.kv_group;                          // pool head of this work head
-  const bool row_ok = qi < qlen;
+  const bool row_ok = (qi < qlen) & (q0 + qi < P.total_q);
   const int p = row_ok ? P.q_pos[q0 + qi] : INT_MIN;       // invalid rows see no key
   // raw query row (rotated below) and the words of key tiles 0 .. 3, in flight together
   // with the frequency table
   u32x4 qraw[NCH];
   {
-    const uint16_t* qrow = P.q + ((size_t)(q0 + (row_ok ? qi : 0)) * P.Hq + h) * D;
+    const uint16_t* qrow = P.q + ((size_t)(row_ok ? q0 + qi : 0) * P.Hq + h) * D;
 #pragma unroll
     for (int c = 0; c < NCH; ++c)
       qraw[c] = row_ok ? *(const u32x4*)(qrow + (PART ? 8 * nat_chunk(2 * c + hh, P.rot_chunks,
@@ -280,20 +282,22 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
   }
 
   // The running max m rides on the matrix cores: an extra 16-wide k-step with
-  // K~ = (1, 0, ...) and Q~ = (-m, 0, ...) makes S^T = K~ Q~^T - m directly. With ALiBi the
-  // same k-step also carries the bias within a block: K~ = (1, j, j, 0, ...) for slot j
-  // and Q~ = (-m, c_hi, c_lo, 0, ...) with c = slope_h log2(e) = c_hi + c_lo split into two
-  // fp16 values, so S^T gets + c j; the rest of the bias, c (off_b - p) per block b, is
-  // added on the vector ALUs in fp32.
+  // K~ = (256, 0, ...) and Q~ = (-m / 256, 0, ...) makes S^T = K~ Q~^T - m directly. m is
+  // kept a multiple of 256 times an fp16 value, so the product is exact in the fp32
+  // accumulator and m may reach 256 * 65504 (~1.7e7) in the log2 domain before it
+  // overflows. With ALiBi the same k-step also carries the bias within a block:
+  // K~ = (256, j, j, 0, ...) for slot j and Q~ = (-m / 256, c_hi, c_lo, 0, ...) with
+  // c = slope_h log2(e) = c_hi + c_lo split into two fp16 values, so S^T gets + c j; the
+  // rest of the bias, c (off_b - p) per block b, is added on the vector ALUs in fp32.
   const bool e0lane = hh == 0;
   const float cslope = ALIBI ? P.slopes[h] * 1.4426950408889634f : 0.f;
   const float c_hi = (float)(_Float16)cslope;
   const uint32_t slope_hi = ALIBI ? f16_bits(c_hi) << 16 : 0u;
   const uint32_t jbits = ALIBI ? f16_bits((float)(col & 15)) : 0u;
-  const u32x4 ones_a = e0lane ? u32x4{0x3C00u | (jbits << 16), jbits, 0u, 0u}
-                              : u32x4{0u, 0u, 0u, 0u};      // fp16 (1, j, j, 0, ...)
+  const u32x4 ones_a = e0lane ? u32x4{0x5C00u | (jbits << 16), jbits, 0u, 0u}
+                              : u32x4{0u, 0u, 0u, 0u};      // fp16 (256, j, j, 0, ...)
   float m = -INFINITY, l = 0.f;                              // l: this lane's half of the row sum
-  u32x4 qm = {e0lane ? slope_hi : 0u,                        // (-m, c_hi, c_lo, 0...) as fp16
+  u32x4 qm = {e0lane ? slope_hi : 0u,                        // (-m/256, c_hi, c_lo, 0...) fp16
               e0lane && ALIBI ? f16_bits(cslope - c_hi) : 0u, 0u, 0u};
   const int p_bias = row_ok ? p : 0;                         // rows past the tile see no key
   // ALiBi bias of score half t of the tile whose words are at window index 0 of wd
@@ -490,17 +494,18 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
       }
     }
     // the running max moves only when a row's max exceeds it by 2^8 (or on the row's first
-    // visible key), so P = exp2(S) stays below 256; m is kept as the exact fp16 value the
-    // matrix cores subtract, so the offset cancels in O / l
+    // visible key), so P = exp2(S) stays below 256; m is kept as the exact value the
+    // matrix cores subtract (256 times an fp16 number, rounded up so that m is never below
+    // the row max it is set from), so the offset cancels in O / l
     const bool first = (m == -INFINITY) & (mx != -INFINITY);
     if (__any(first | (mx > 8.f))) {
       const float m_old = m == -INFINITY ? 0.f : m;
       float m_new = m;
-      if (first | (mx > 0.f)) m_new = (float)(_Float16)(m_old + mx);
+      if (first | (mx > 0.f)) m_new = 256.f * f16_round_up((m_old + mx) * (1.f / 256.f));
       const float delta = m_new == -INFINITY ? 0.f : m_new - m_old;
       const float alpha = first ? 1.f : __builtin_amdgcn_exp2f(-delta);
       m = m_new;
-      qm[0] = e0lane ? f16_bits(m == -INFINITY ? 0.f : -m) | slope_hi : 0u;
+      qm[0] = e0lane ? f16_bits(m == -INFINITY ? 0.f : m * (-1.f / 256.f)) | slope_hi : 0u;
       l *= alpha;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;

@@ -1,9 +1,9 @@
 """Parity of the HIP path (through the C ABI) with the float64 oracle on the same inputs.
 
 Tolerance on bf16 outputs: max |diff| <= 2e-2 and mean |diff| <= 2e-3; packed-word
-decoding bit-exact. Small cases compare every output element; the full-size workloads
-compare sampled rows (every head and dim of each sampled row) and check that all outputs
-are finite (unreferenced pool blocks and padding slots hold NaN).
+decoding bit-exact. Every case, the full-size workloads included, compares every output
+element (all rows, heads and dims) with the oracle; unreferenced pool blocks and padding
+slots hold NaN, so a stray read shows up as a non-finite output.
 """
 import numpy as np
 import pytest
@@ -124,11 +124,16 @@ def test_mini_cases(name, kw, kind):
 
 
 def _freq_tables(D):
+    """name -> (table given to the HIP entry point, table given to the oracle). The Llama
+    3.1 table comes from the library's host helper on the HIP side and from the oracle's own
+    scaling on the oracle side, so the two sides share no arithmetic."""
     import position_agnostic_kv_paged_amd as L
     half_zero = oracle.rope.inv_freq(D, 10000.0).copy()
     half_zero[::2] = 0.0                                 # every other pair unrotated
     interp = oracle.rope.inv_freq(D, 10000.0) / 4.0      # position interpolation by 4
-    return {"llama31": L.llama31_inv_freq(D), "half-zero": half_zero, "interp4": interp}
+    llama = oracle.rope.llama31_scale(oracle.rope.inv_freq(D, 500000.0))
+    return {"llama31": (L.llama31_inv_freq(D), llama), "half-zero": (half_zero, half_zero),
+            "interp4": (interp, interp)}
 
 
 @pytest.mark.parametrize("kind", ["prefill", "decode"])
@@ -140,9 +145,10 @@ def test_frequency_tables(name, table, kind):
     table (Llama 3.1 scaling at base 500000, zero-frequency pairs, position interpolation)."""
     kw = dict(_mini_cases())[name]
     wl = small(**kw)
-    th = _freq_tables(wl.D)[table]
+    th_hip, th_oracle = _freq_tables(wl.D)[table]
     say(f"frequency table {table} on {name} via {kind}")
-    compare(run_hip(wl, kind, inv_freq=th), oracle_out(wl, base=th), f"{name}/{table}/{kind}")
+    compare(run_hip(wl, kind, inv_freq=th_hip), oracle_out(wl, base=th_oracle),
+            f"{name}/{table}/{kind}")
 
 
 _PARTIAL = [("gaps-D128-G4", 32), ("gaps-D128-G4", 64), ("gaps-D128-G4", 112),
@@ -164,17 +170,10 @@ def test_partial_rotary(name, r, kind):
 
 @pytest.mark.parametrize("kind", ["prefill", "decode"])
 def test_partial_rotary_full_size(kind):
-    """Partial rotary (r = 32 of 128) on the full-size Zipf batches, sampled rows."""
-    if kind == "decode":
-        wl = make("decode-32q8kv-b64-ctx4161")
-        g, w = _sampled(wl, "decode", [0, 33, 63], lambda s: np.array([wl.q_indptr[s]]),
-                        rotary_dim=32)
-    else:
-        wl = make("prefill-32q8kv-b16-ctx5376")
-        g, w = _sampled(wl, "prefill", [0, 15], lambda s: wl.q_indptr[s] + np.array([0, 129, 255]),
-                        rotary_dim=32)
+    """Partial rotary (r = 32 of 128) on the full-size Zipf batches, every row."""
+    wl = make("decode-32q8kv-b64-ctx4161" if kind == "decode" else "prefill-32q8kv-b16-ctx5376")
     say(f"partial rotary r = 32 on {wl.name} via {kind}")
-    compare(g, w, f"{wl.name}/r32")
+    _full_check(wl, kind, f"{wl.name}/r32", rotary_dim=32)
 
 
 _DOCROT = ["gaps-D128-G4", "gaps-D64-G2", "overlap-repeat-partial", "positions-above-2^15",
@@ -221,27 +220,13 @@ def test_doc_rotated_pool_at_logical_offsets(kind):
 
 def test_doc_rotated_pool_full_size_decode():
     """Document-rotated pool on the 64-request decode batch (Zipf documents reused at
-    per-request offsets), sampled rows."""
-    from oracle.docrot import doc_rotated_rows
+    per-request offsets), every row."""
     from tests.util import doc_stored_offsets
-    import dataclasses
-    from tests.util import doc_rotated_pool
     wl = make("decode-32q8kv-b64-ctx4161")
     st = doc_stored_offsets(wl)
-    kd = doc_rotated_pool(wl, st)
-    wd = dataclasses.replace(wl, k_bits=kd)
+    wd, want = _docrot_case(wl, st)
     say("document-rotated pool on decode-32q8kv-b64-ctx4161 via decode")
-    out = run_hip(wd, "decode", stored=st)
-    got, want = [], []
-    for s in (0, 31, 63):
-        rows = np.array([wl.q_indptr[s]])
-        got.append(out[rows])
-        want.append(doc_rotated_rows(wl.q_bits, kd, wl.v_bits,
-                                     [wl.compact_ids(x) if x == s else None
-                                      for x in range(wl.num_seqs)],
-                                     wl.seq_offsets, st, wl.kv_lens, wl.q_indptr, wl.q_pos,
-                                     wl.rope_base, wl.B, s, rows))
-    compare(np.concatenate(got), np.concatenate(want), "decode-b64/docrot")
+    compare(run_hip(wd, "decode", stored=st), want, "decode-b64/docrot")
 
 
 @pytest.mark.parametrize("variant", ["partial-r32", "doc-rotated"])
@@ -519,93 +504,94 @@ def test_negative_control_rotation_compiled_out(kind):
 
 # ------------------------------------------------------------------ full-size workloads
 
-def _sampled(wl, kind, seqs, rows_of, inv_freq=None, slopes=None, rotary_dim=None):
-    out = run_hip(wl, kind, inv_freq=inv_freq, slopes=slopes, rotary_dim=rotary_dim)
-    assert np.all(np.isfinite(out)), "non-finite outputs"
-    got, want = [], []
-    for s in seqs:
-        rows = rows_of(s)
-        got.append(out[rows])
-        if slopes is not None:
-            from oracle.alibi import alibi_rows
-            want.append(alibi_rows(wl.q_bits, wl.k_bits, wl.v_bits,
-                                   [wl.compact_ids(x) if x == s else None
-                                    for x in range(wl.num_seqs)],
-                                   wl.seq_offsets, wl.kv_lens, wl.q_indptr, wl.q_pos,
-                                   slopes, wl.B, s, rows))
-        else:
-            want.append(oracle_out(wl, rows=rows, seq=s, base=inv_freq, rotary_dim=rotary_dim))
-    return np.concatenate(got), np.concatenate(want)
+def _full_check(wl, kind, label, inv_freq=None, oracle_base=None, slopes=None,
+                rotary_dim=None):
+    """Every output element of a full-size call against the oracle on the same inputs."""
+    got = run_hip(wl, kind, inv_freq=inv_freq, slopes=slopes, rotary_dim=rotary_dim)
+    if slopes is not None:
+        want = _alibi_ref(wl, slopes)
+    else:
+        want = oracle_out(wl, base=oracle_base, rotary_dim=rotary_dim)
+    return compare(got, want, label)
 
 
-def test_decode_llama8b_batch64():
-    wl = make("decode-32q8kv-b64-ctx4161")
-    say("decode-32q8kv-b64-ctx4161 via decode")
-    seqs = [0, 9, 21, 40, 63]
-    g, w = _sampled(wl, "decode", seqs, lambda s: np.array([wl.q_indptr[s]]))
-    compare(g, w, "decode-b64")
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("q_scale", [1.0, 4.0])
+def test_decode_llama8b_batch64(q_scale):
+    wl = make("decode-32q8kv-b64-ctx4161", q_scale=q_scale)
+    say(f"{wl.name} via decode, every row")
+    _full_check(wl, "decode", wl.name)
 
 
-def test_prefill_llama8b_batch16():
-    wl = make("prefill-32q8kv-b16-ctx5376")
-    say("prefill-32q8kv-b16-ctx5376 via prefill")
-
-    def rows(s):
-        q0 = wl.q_indptr[s]
-        return q0 + np.array([0, 1, 63, 64, 127, 128, 200, 255])
-    g, w = _sampled(wl, "prefill", [0, 7, 15], rows)
-    compare(g, w, "prefill-b16")
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("q_scale", [1.0, 4.0])
+def test_prefill_llama8b_batch16(q_scale):
+    wl = make("prefill-32q8kv-b16-ctx5376", q_scale=q_scale)
+    say(f"{wl.name} via prefill, every row")
+    _full_check(wl, "prefill", wl.name)
 
 
-def test_long_decode_batch8():
-    wl = make("decode-32q8kv-b8-ctx32769")
-    say("decode-32q8kv-b8-ctx32769 via decode")
-    g, w = _sampled(wl, "decode", [0, 3, 7], lambda s: np.array([wl.q_indptr[s]]))
-    compare(g, w, "long-decode")
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("q_scale", [1.0, 4.0])
+def test_long_decode_batch8(q_scale):
+    wl = make("decode-32q8kv-b8-ctx32769", q_scale=q_scale)
+    say(f"{wl.name} via decode, every row")
+    _full_check(wl, "decode", wl.name)
 
 
-def test_mixed_70b_batch():
-    wl = make("mixed-64q8kv-4p96d")
-    say("mixed-64q8kv-4p96d via prefill (one call)")
-
-    def rows(s):
-        q0, q1 = wl.q_indptr[s], wl.q_indptr[s + 1]
-        if q1 - q0 == 1:
-            return np.array([q0])
-        return q0 + np.array([0, 31, 32, 255, 256, 511])
-    g, w = _sampled(wl, "prefill", [0, 3, 4, 50, 99], rows)
-    compare(g, w, "mixed")
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("q_scale", [1.0, 4.0])
+def test_mixed_70b_batch(q_scale):
+    """The 4-prefill + 96-decode batch in one lazyattn_prefill call, every row."""
+    wl = make("mixed-64q8kv-4p96d", q_scale=q_scale)
+    say(f"{wl.name} via prefill (one call), every row")
+    _full_check(wl, "prefill", wl.name)
 
 
+@pytest.mark.timeout(300)
+def test_shifted_document_is_detected_full_size():
+    """Detection at full size: the long-decode batch with peaky queries, one document of
+    every request placed one position later in the words the GPU gets. The GPU output must
+    match the oracle on the shifted layout and miss the tolerance against the unshifted one,
+    so the full-size comparison sees a one-position placement error."""
+    import dataclasses
+    wl = make("decode-32q8kv-b8-ctx32769", q_scale=4.0)
+    offs = [o.copy() for o in wl.seq_offsets]
+    for s in range(wl.num_seqs):
+        offs[s][32 * 20: 32 * 21] += 1                # document 20 of each request (32 blocks)
+    shifted = dataclasses.replace(wl, seq_offsets=offs)
+    say("long decode, peaky, document 20 of every request shifted by one position")
+    got = run_hip(shifted, "decode")
+    compare(got, oracle_out(shifted), "long-decode-shifted/vs-shifted")
+    want = oracle_out(wl)
+    d = np.abs(got - want)
+    say(f"  vs the unshifted layout: max_abs={d.max():.3e} mean_abs={d.mean():.3e}")
+    assert d.max() > MAX_ABS
+
+
+@pytest.mark.timeout(300)
 @pytest.mark.parametrize("variant", ["alibi", "llama31"])
 @pytest.mark.parametrize("name,kind", [("decode-32q8kv-b64-ctx4161", "decode"),
                                        ("prefill-32q8kv-b16-ctx5376", "prefill"),
                                        ("decode-32q8kv-b8-ctx32769", "decode")])
 def test_full_size_variants(name, kind, variant):
     """The ALiBi and frequency-table entry points on the full-size workloads (positions up
-    to ~35k), sampled rows against the oracle, all outputs finite."""
+    to ~35k), every row against the oracle."""
     import position_agnostic_kv_paged_amd as L
     from oracle.alibi import alibi_slopes
     wl = make(name)
     say(f"{name} via {kind}, {variant}")
-    opt = dict(slopes=alibi_slopes(wl.Hq)) if variant == "alibi" else \
-        dict(inv_freq=L.llama31_inv_freq(wl.D))
-    if kind == "prefill":
-        def rows(s):
-            return wl.q_indptr[s] + np.array([0, 63, 64, 200, 255])
-        seqs = [0, 15]
+    if variant == "alibi":
+        _full_check(wl, kind, f"{name}/{variant}", slopes=alibi_slopes(wl.Hq))
     else:
-        def rows(s):
-            return np.array([wl.q_indptr[s]])
-        seqs = [0, wl.num_seqs - 1]
-    g, w = _sampled(wl, kind, seqs, rows, **opt)
-    compare(g, w, f"{name}/{variant}")
+        _full_check(wl, kind, f"{name}/{variant}", inv_freq=L.llama31_inv_freq(wl.D),
+                    oracle_base=oracle.rope.llama31_scale(oracle.rope.inv_freq(wl.D, 500000.0)))
 
 
 @pytest.mark.parametrize("kind", ["prefill", "decode"])
 def test_gqa16_405b_shape(kind):
     """128 query heads over 8 KV heads (G = 16), head dim 128: 12 requests of 6 Zipf
-    documents x 512 tokens at per-request offsets plus a 48-token question; sampled rows."""
+    documents x 512 tokens at per-request offsets plus a 48-token question; every row."""
     rng = np.random.default_rng(31)
     reqs = []
     for r in range(12):
@@ -616,12 +602,46 @@ def test_gqa16_405b_shape(kind):
         reqs.append(RequestLayout(segs, 48 if kind == "prefill" else 1))
     wl = build("gqa16", 128, 8, 128, 16, 10000.0, 40, 512, reqs, seed=32)
     say(f"G = 16 (128 q / 8 kv heads) via {kind}")
+    _full_check(wl, kind, f"gqa16/{kind}")
 
-    def rows(s):
-        q0, q1 = wl.q_indptr[s], wl.q_indptr[s + 1]
-        return np.array([q0]) if q1 - q0 == 1 else q0 + np.array([0, 17, 47])
-    g, w = _sampled(wl, kind, [0, 5, 11], rows)
-    compare(g, w, f"gqa16/{kind}")
+
+@pytest.mark.parametrize("kind", ["prefill", "decode"])
+def test_operand_range_equal_huge_scores(kind):
+    """Scores near the stated range: with an all-zero frequency table nothing is rotated,
+    and every key and query element is 100, so every visible score is
+    128 * 100 * 100 / sqrt(128) (1.6e5 in the log2 domain, past fp16's 65504). All scores
+    are equal, so each row is the mean of its visible values (the oracle's float64 result);
+    a running maximum kept in fp16 would overflow to inf here."""
+    import dataclasses
+    wl = small(Hq=8, Hkv=2, D=128, seed=81)
+    hundred = np.uint16(0x42C8)                           # bf16 100.0
+    fin = wl.k_bits != np.uint16(0x7FC0)                  # keep the NaN padding
+    k = np.where(fin, hundred, wl.k_bits).astype(np.uint16)
+    q = np.full_like(wl.q_bits, hundred)
+    wz = dataclasses.replace(wl, k_bits=k, q_bits=q)
+    zero = np.zeros(wl.D // 2)
+    say(f"equal huge scores via {kind}")
+    got = run_hip(wz, kind, inv_freq=zero)
+    want = oracle_out(wz, base=zero)
+    compare(got, want, f"equal-huge-scores/{kind}")
+
+
+@pytest.mark.parametrize("kind", ["prefill", "decode"])
+def test_operand_range_large_keys(kind):
+    """Keys scaled to |k| ~ 1e4 (N(0, 1) x 1e4, elements up to ~5e4, below fp16's 65504)
+    with queries scaled by 1e-3, so scores stay moderate while the key operands sit near
+    the top of the fp16 range."""
+    import dataclasses
+    from oracle.attention import bf16_bits_to_f64
+    from workload import f32_to_bf16_bits
+    wl = small(Hq=8, Hkv=2, D=128, seed=82, q_scale=1e-3)
+    kf = bf16_bits_to_f64(wl.k_bits)
+    fin = np.isfinite(kf)
+    k = wl.k_bits.copy()
+    k[fin] = f32_to_bf16_bits((kf[fin] * 1e4).astype(np.float32))
+    wk = dataclasses.replace(wl, k_bits=k)
+    say(f"large keys via {kind}: max |k| = {np.abs(kf[fin]).max() * 1e4:.3g}")
+    compare(run_hip(wk, kind), oracle_out(wk), f"large-keys/{kind}")
 
 
 @pytest.mark.gpu

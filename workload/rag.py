@@ -383,8 +383,10 @@ def _tiny_layouts(decode: bool) -> List[RequestLayout]:
 
 
 def make(name: str, seed: Optional[int] = None, decode_variant: bool = False,
-         no_reuse: bool = False) -> Workload:
-    """Build a named configuration. Master seed defaults to 1000 + its 1-based index."""
+         no_reuse: bool = False, q_scale: float = 1.0) -> Workload:
+    """Build a named configuration. Master seed defaults to 1000 + its 1-based index.
+    q_scale multiplies the N(0, 1) queries before rounding (q_scale 4 gives the peaky
+    softmax of the stress variants)."""
     cfg = CONFIGS[name]
     if seed is None:
         seed = 1000 + CONFIG_ORDER.index(name) + 1
@@ -392,8 +394,9 @@ def make(name: str, seed: Optional[int] = None, decode_variant: bool = False,
         lays = _tiny_layouts(decode_variant)
     else:
         lays = layouts_for(cfg, seed, no_reuse)
-    suffix = ("-decode" if decode_variant else "") + ("-noreuse" if no_reuse else "")
+    suffix = ("-decode" if decode_variant else "") + ("-noreuse" if no_reuse else "") + \
+        (f"-q{q_scale:g}" if q_scale != 1.0 else "")
     wl = build(cfg.name + suffix, cfg.Hq, cfg.Hkv, cfg.D, cfg.B,
-               cfg.rope_base, cfg.n_docs, cfg.doc_tokens, lays, seed)
+               cfg.rope_base, cfg.n_docs, cfg.doc_tokens, lays, seed, q_scale=q_scale)
     wl.info["description"] = cfg.description
     return wl
