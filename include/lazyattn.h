@@ -136,6 +136,28 @@ int lazyattn_decode(const void* q, const void* k_pool, const void* v_pool,
                     void* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * lazyattn_decode_noalloc -- lazyattn_decode for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * same arguments, result and errors, minus the workspace. The split-K partials, plan
+ * prefixes and frequency table live in a fixed device buffer of
+ * LAZYATTN_NOALLOC_SCRATCH_BYTES inside the library, one per device, held until the process
+ * ends; nothing is allocated or freed by the call. The split is coarsened when the batch's
+ * partials would not fit (longer items, same result); a batch whose partials do not fit
+ * even with one split per row (about total_q * Hq * (D + 4) * 4 bytes plus 8 bytes per
+ * sequence and 1 KB) returns LAZYATTN_ERR_WORKSPACE before any launch. Every call on a
+ * device shares that device's buffer: calls that overlap on one device (two streams, or two
+ * host threads) race and must be serialised by the caller. The stream must belong to the
+ * current device. Returns LAZYATTN_ERR_LAUNCH if the buffer's device address cannot be had.
+ */
+#define LAZYATTN_NOALLOC_SCRATCH_BYTES (32u << 20)
+int lazyattn_decode_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                            const int32_t* block_table, const uint32_t* block_meta,
+                            const int32_t* kv_lens, const int32_t* q_indptr,
+                            const int32_t* q_positions, double rope_base, int32_t num_seqs,
+                            int32_t total_q, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
+                            int32_t num_blocks, int32_t max_entries, void* out, void* stream);
+
+/*
  * lazyattn_prefill_rotated_pool / lazyattn_decode_rotated_pool -- the materialised baseline
  * the method is measured against (technical summary: "Mathematical Equivalence"; the
  * "rotate keys twice" copy it avoids). Same arguments, layouts, workspace sizes and errors as

@@ -7,6 +7,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblazyattn
 OK, ERR_NULL, ERR_ALIGN, ERR_SHAPE, ERR_RANGE, ERR_WORKSPACE, ERR_LAUNCH, ERR_ARG = \
     0, -1, -2, -3, -4, -5, -6, -7
 ERR_NOSPACE, ERR_STATE = -8, -9
+NOALLOC_SCRATCH_BYTES = 32 << 20   # LAZYATTN_NOALLOC_SCRATCH_BYTES
 
 # every symbol include/lazyattn.h declares
 EXPORTED = [
@@ -20,7 +21,7 @@ EXPORTED = [
     "lazyattn_pool_alloc_private", "lazyattn_pool_free_private", "lazyattn_pool_stats",
     "lazyattn_prefill_workspace_bytes",
     "lazyattn_decode_workspace_bytes", "lazyattn_encode_meta", "lazyattn_debug_decode_meta",
-    "lazyattn_llama31_inv_freq",
+    "lazyattn_llama31_inv_freq", "lazyattn_decode_noalloc",
     "lazyattn_status_str", "lazyattn_version",
 ]
 
@@ -62,6 +63,8 @@ def lib():
                  "lazyattn_decode_alibi"):
         f = getattr(L, name)
         f.argtypes, f.restype = attn[:8] + [vp] + attn[9:], ctypes.c_int
+    L.lazyattn_decode_noalloc.argtypes = attn[:17] + [vp, vp]
+    L.lazyattn_decode_noalloc.restype = ctypes.c_int
     for name in ("lazyattn_prefill_workspace_bytes", "lazyattn_decode_workspace_bytes"):
         f = getattr(L, name)
         f.argtypes, f.restype = [i32] * 6, ctypes.c_size_t

@@ -114,6 +114,20 @@ def decode(q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indptr, q_pos,
                       stored_offsets=stored_offsets)
 
 
+def decode_noalloc(q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indptr, q_pos,
+                   rope_base, max_entries, out, stream=None):
+    """lazyattn_decode_noalloc: lazyattn_decode with the library's fixed per-device buffer in
+    place of a workspace (nothing is allocated; `out` must be given). Calls that overlap on
+    one device race."""
+    total_q, Hq, D, num_blocks, Hkv, B = _dims(q, k_pool)
+    rc = lib().lazyattn_decode_noalloc(
+        _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(block_meta),
+        _ptr(kv_lens), _ptr(q_indptr), _ptr(q_pos), float(rope_base), kv_lens.numel(), total_q,
+        Hq, Hkv, D, B, num_blocks, int(max_entries), _ptr(out), _stream(stream))
+    check(rc, "lazyattn_decode_noalloc")
+    return out
+
+
 def llama31_inv_freq(D, base=500000.0, factor=8.0, low_freq_factor=1.0, high_freq_factor=4.0,
                      original_context=8192):
     """lazyattn_llama31_inv_freq: the Llama 3.1 frequency-scaled RoPE table (host, float64,

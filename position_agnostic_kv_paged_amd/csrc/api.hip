@@ -5,6 +5,7 @@
 #include "lazyattn_kernels.h"
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 
@@ -66,6 +67,24 @@ size_t workspace_for(int num_seqs, int rows_bound, int max_entries, int Hq, int 
   return ws_layout(num_seqs, (long long)rows_bound * ds.smax, Hq, D).total;
 }
 
+// The split of decode_split, coarsened (longer items, fewer partials) until the workspace
+// fits `cap` bytes; smax = 0 if even one split per row does not fit.
+DecodeSplit decode_split_capped(int num_seqs, int rows_bound, int Hq, int Hkv, int D,
+                                int max_entries, size_t cap) {
+  DecodeSplit ds = decode_split(rows_bound, work_heads(Hq, Hkv), max_entries);
+  const long long T = max_entries > 0 ? max_entries : 1;
+  while (ws_layout(num_seqs, (long long)rows_bound * ds.smax, Hq, D).total > cap) {
+    if (ds.smax <= 1) {
+      ds.smax = 0;
+      return ds;
+    }
+    const long long b = std::min<long long>(2ll * ds.bps, INT32_MAX - 1);
+    ds.bps = (int)(b + (b & 1));
+    ds.smax = (int)((T + ds.bps - 1) / ds.bps);
+  }
+  return ds;
+}
+
 int run(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_table,
         const uint32_t* block_meta, const int32_t* kv_lens, const int32_t* q_indptr,
         const int32_t* q_positions, double rope_base, int32_t num_seqs, int32_t total_q,
@@ -73,7 +92,7 @@ int run(const void* q, const void* k_pool, const void* v_pool, const int32_t* bl
         int32_t max_entries, void* out, void* workspace, size_t workspace_bytes,
         void* stream, int mode, int pe, const double* inv_freq = nullptr,
         const float* slopes = nullptr, int rotary_dim = 0,
-        const int32_t* stored_offsets = nullptr) {
+        const int32_t* stored_offsets = nullptr, bool fit_workspace = false) {
   if (!q || !k_pool || !v_pool || !block_table || !block_meta || !kv_lens || !q_indptr ||
       !q_positions || !out || !workspace)
     return LAZYATTN_ERR_NULL;
@@ -101,13 +120,18 @@ int run(const void* q, const void* k_pool, const void* v_pool, const int32_t* bl
       !aligned(kv_lens, 4) || !aligned(q_indptr, 4) || !aligned(q_positions, 4))
     return LAZYATTN_ERR_ALIGN;
   const int rows_bound = mode == kPlanDecodeOnly ? total_q : num_seqs;
-  if (workspace_bytes < workspace_for(num_seqs, rows_bound, max_entries, Hq, Hkv, D))
+  // fit_workspace: the workspace is a fixed buffer, so the split is chosen to fit it
+  const DecodeSplit ds =
+      fit_workspace
+          ? decode_split_capped(num_seqs, rows_bound, Hq, Hkv, D, max_entries, workspace_bytes)
+          : decode_split(rows_bound, work_heads(Hq, Hkv), max_entries);
+  if (ds.smax <= 0 ||
+      workspace_bytes < ws_layout(num_seqs, (long long)rows_bound * ds.smax, Hq, D).total)
     return LAZYATTN_ERR_WORKSPACE;
   if (num_seqs == 0 || total_q == 0) return LAZYATTN_OK;
 
   hipStream_t st = (hipStream_t)stream;
   const int G = work_group(Hq, Hkv), Hw = work_heads(Hq, Hkv), kv_group = Hw / Hkv;
-  const DecodeSplit ds = decode_split(rows_bound, Hw, max_entries);
   const WsLayout L = ws_layout(num_seqs, (long long)rows_bound * ds.smax, Hq, D);
   char* ws = (char*)workspace;
   double* freqs = (double*)(ws + L.off_freqs);
@@ -155,9 +179,49 @@ int run(const void* q, const void* k_pool, const void* v_pool, const int32_t* bl
   return LAZYATTN_OK;
 }
 
+// ---- the decode entry point that allocates nothing ------------------------------------------
+// A fixed device buffer stands in for the workspace (plan prefixes, frequency table, zero
+// chunk, split-K partials). Each device that loads the library holds its own copy until the
+// process ends. In host code `scratch` names a host-side stand-in, never the device memory:
+// its device address comes from hipGetSymbolAddress, once per device, and only that
+// address is handed to kernels.
+constexpr size_t kNoAllocScratchBytes = (size_t)LAZYATTN_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+static std::atomic<void*> g_scratch_ptr[kMaxScratchDevices];
+
+// Device address of `scratch` on the current device (nullptr if it cannot be had). Host
+// threads racing on a device's first call both store the same address.
+void* scratch_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return nullptr;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  void* q = nullptr;
+  if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || q == nullptr)
+    return nullptr;
+  g_scratch_ptr[dev].store(q, std::memory_order_release);
+  return q;
+}
+
 }  // namespace
 
 extern "C" {
+
+int lazyattn_decode_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                            const int32_t* block_table, const uint32_t* block_meta,
+                            const int32_t* kv_lens, const int32_t* q_indptr,
+                            const int32_t* q_positions, double rope_base, int32_t num_seqs,
+                            int32_t total_q, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
+                            int32_t num_blocks, int32_t max_entries, void* out, void* stream) {
+  void* ws = scratch_ptr();
+  if (!ws) return LAZYATTN_ERR_LAUNCH;
+  return run(q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indptr, q_positions,
+             rope_base, num_seqs, total_q, Hq, Hkv, D, B, num_blocks, max_entries, out, ws,
+             kNoAllocScratchBytes, stream, kPlanDecodeOnly, kRope, nullptr, nullptr, 0, nullptr,
+             true);
+}
 
 int lazyattn_prefill(const void* q, const void* k_pool, const void* v_pool,
                      const int32_t* block_table, const uint32_t* block_meta,
