@@ -62,13 +62,65 @@ DecodeSplit decode_split(int rows_bound, int Hkv, int max_entries) {
   return d;
 }
 
-size_t workspace_for(int num_seqs, int rows_bound, int max_entries, int Hq, int Hkv, int D) {
+// Prefill KV split (mixed calls). Query tiles of 256 (position, head) rows are the natural
+// work items; when a batch has too few of them to keep every compute unit busy (one long
+// request, say), each tile's key range is cut into splits that run as separate items and
+// are merged by the tile's last split. The host cannot see the per-sequence lengths (no
+// device reads), so it sizes the split from total_q and the max_entries hint; plan_kernel
+// applies the same rule (pf_split) to each sequence's real length.
+constexpr int kPfItemsPerCu = 2;    // target prefill items per compute unit
+constexpr int kPfMinChunk = 8;      // key tiles (of 64 keys) per split, at least
+constexpr int kPfMaxSplits = 32;
+
+struct CallPlan {
+  DecodeSplit ds;
+  int rows_bound;
+  int pf_kc, pf_smax, pf_item_cap;  // prefill KV split (mixed calls)
+  long long n_counters, pf_slots;
+  WsLayout L;
+};
+
+CallPlan plan_call(int mode, int num_seqs, int total_q, int max_entries, int Hq, int Hkv,
+                   int D, const DecodeSplit& ds) {
+  CallPlan c;
+  c.ds = ds;
+  c.rows_bound = mode == kPlanDecodeOnly ? total_q : num_seqs;
+  c.pf_kc = INT32_MAX / 2;
+  c.pf_smax = 1;
+  c.pf_item_cap = 0;
+  c.n_counters = 0;
+  c.pf_slots = 0;
+  if (mode == kPlanMixed) {
+    const int G = work_group(Hq, Hkv), Hw = work_heads(Hq, Hkv);
+    const long long pos = prefill_positions_per_tile(G);
+    const long long tiles_est = ((long long)total_q + pos - 1) / pos;
+    const long long tiles_bound = tiles_est + num_seqs;
+    const long long max_kt = std::max(1, (max_entries + 3) / 4);
+    const long long target = (long long)kPfItemsPerCu * (decode_resident_waves() / 8);
+    if (tiles_est * Hw < target && max_kt > kPfMinChunk) {
+      const long long want = (target + tiles_est * Hw - 1) / std::max(1ll, tiles_est * Hw);
+      c.pf_smax = (int)std::min<long long>(kPfMaxSplits, std::max(2ll, want));
+      c.pf_kc = (int)std::max<long long>(kPfMinChunk, (max_kt + c.pf_smax - 1) / c.pf_smax);
+    }
+    c.pf_item_cap = (int)std::min<long long>(tiles_bound * c.pf_smax, INT32_MAX / 4);
+    if (c.pf_smax > 1) {
+      c.n_counters = (long long)Hw * c.pf_item_cap;
+      c.pf_slots = (long long)Hw * c.pf_item_cap;
+    }
+  }
+  c.L = ws_layout(num_seqs, (long long)c.rows_bound * ds.smax, Hq, D, c.n_counters, c.pf_slots);
+  return c;
+}
+
+size_t workspace_for(int mode, int num_seqs, int total_q, int max_entries, int Hq, int Hkv,
+                     int D) {
+  const int rows_bound = mode == kPlanDecodeOnly ? total_q : num_seqs;
   const DecodeSplit ds = decode_split(rows_bound, work_heads(Hq, Hkv), max_entries);
-  return ws_layout(num_seqs, (long long)rows_bound * ds.smax, Hq, D).total;
+  return plan_call(mode, num_seqs, total_q, max_entries, Hq, Hkv, D, ds).L.total;
 }
 
 // The split of decode_split, coarsened (longer items, fewer partials) until the workspace
-// fits `cap` bytes; smax = 0 if even one split per row does not fit.
+// of a decode call fits `cap` bytes; smax = 0 if even one split per row does not fit.
 DecodeSplit decode_split_capped(int num_seqs, int rows_bound, int Hq, int Hkv, int D,
                                 int max_entries, size_t cap) {
   DecodeSplit ds = decode_split(rows_bound, work_heads(Hq, Hkv), max_entries);
@@ -120,25 +172,28 @@ int run(const void* q, const void* k_pool, const void* v_pool, const int32_t* bl
       !aligned(kv_lens, 4) || !aligned(q_indptr, 4) || !aligned(q_positions, 4))
     return LAZYATTN_ERR_ALIGN;
   const int rows_bound = mode == kPlanDecodeOnly ? total_q : num_seqs;
-  // fit_workspace: the workspace is a fixed buffer, so the split is chosen to fit it
+  // fit_workspace: the workspace is a fixed buffer (decode calls), so the split is chosen to
+  // fit it
   const DecodeSplit ds =
       fit_workspace
           ? decode_split_capped(num_seqs, rows_bound, Hq, Hkv, D, max_entries, workspace_bytes)
           : decode_split(rows_bound, work_heads(Hq, Hkv), max_entries);
-  if (ds.smax <= 0 ||
-      workspace_bytes < ws_layout(num_seqs, (long long)rows_bound * ds.smax, Hq, D).total)
-    return LAZYATTN_ERR_WORKSPACE;
+  if (ds.smax <= 0) return LAZYATTN_ERR_WORKSPACE;
+  const CallPlan cp = plan_call(mode, num_seqs, total_q, max_entries, Hq, Hkv, D, ds);
+  if (workspace_bytes < cp.L.total) return LAZYATTN_ERR_WORKSPACE;
   if (num_seqs == 0 || total_q == 0) return LAZYATTN_OK;
 
   hipStream_t st = (hipStream_t)stream;
   const int G = work_group(Hq, Hkv), Hw = work_heads(Hq, Hkv), kv_group = Hw / Hkv;
-  const WsLayout L = ws_layout(num_seqs, (long long)rows_bound * ds.smax, Hq, D);
+  const WsLayout& L = cp.L;
   char* ws = (char*)workspace;
   double* freqs = (double*)(ws + L.off_freqs);
   uint32_t* zero = (uint32_t*)(ws + L.off_zero);
   int32_t* pf_prefix = (int32_t*)(ws + L.off_pf_prefix);
   int32_t* dec_prefix = (int32_t*)(ws + L.off_dec_prefix);
   float* partials = (float*)(ws + L.off_partials);
+  int* counters = (int*)(ws + L.off_counters);
+  float* pf_partials = (float*)(ws + L.off_pf_partials);
 
   // RoPE frequencies in revolutions per position (unused with ALiBi: all zero). Partial
   // rotary: theta_k = base^(-2k/r) for the r/2 rotated pairs, zero for the pass-through
@@ -151,19 +206,20 @@ int run(const void* q, const void* k_pool, const void* v_pool, const int32_t* bl
                         : 0.0;
   const float scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
 
+  if (mode == kPlanMixed && (long long)cp.pf_item_cap * Hw > INT32_MAX / 2)
+    return LAZYATTN_ERR_SHAPE;
   PlanParams pp{q_indptr, block_table, freqs, pf_prefix, dec_prefix, zero, num_seqs,
-                prefill_positions_per_tile(G), ds.bps, ds.smax, mode, D / 2, fr};
+                prefill_positions_per_tile(G), ds.bps, ds.smax, mode, D / 2,
+                cp.pf_kc, cp.pf_smax, counters, (int)cp.n_counters, fr};
   if (launch_plan(pp, st) != hipSuccess) return LAZYATTN_ERR_LAUNCH;
 
   if (mode == kPlanMixed) {
-    const int pos = prefill_positions_per_tile(G);
-    const long long tiles = ((long long)total_q + pos - 1) / pos + num_seqs;
-    if (tiles * Hw > INT32_MAX / 2) return LAZYATTN_ERR_SHAPE;
     PrefillParams P{(const uint16_t*)q, (const uint16_t*)k_pool, (const uint16_t*)v_pool,
                     block_table, block_meta, kv_lens, q_indptr, q_positions,
                     (uint16_t*)out, pf_prefix, (const uint16_t*)zero, num_seqs, Hq, Hw,
-                    num_blocks, (int)tiles, scale_log2, freqs, slopes, Hkv, kv_group, r / 16,
-                    stored_offsets, total_q};
+                    num_blocks, cp.pf_item_cap, scale_log2, freqs, slopes, Hkv, kv_group,
+                    r / 16, stored_offsets, total_q, cp.pf_kc, cp.pf_smax, pf_partials,
+                    counters};
     if (launch_prefill(P, D, G, pe, st) != hipSuccess) return LAZYATTN_ERR_LAUNCH;
   }
   DecodeParams Dp{(const uint16_t*)q, (const uint16_t*)k_pool, (const uint16_t*)v_pool,
@@ -380,13 +436,13 @@ int lazyattn_decode_doc_rotated(const void* q, const void* k_pool, const void* v
 size_t lazyattn_prefill_workspace_bytes(int32_t num_seqs, int32_t total_q, int32_t max_entries,
                                         int32_t Hq, int32_t Hkv, int32_t D) {
   if (num_seqs < 0 || total_q < 0 || max_entries < 0 || !shape_ok(Hq, Hkv, D, kBlock)) return 0;
-  return workspace_for(num_seqs, num_seqs, max_entries, Hq, Hkv, D);
+  return workspace_for(kPlanMixed, num_seqs, total_q, max_entries, Hq, Hkv, D);
 }
 
 size_t lazyattn_decode_workspace_bytes(int32_t num_seqs, int32_t total_q, int32_t max_entries,
                                        int32_t Hq, int32_t Hkv, int32_t D) {
   if (num_seqs < 0 || total_q < 0 || max_entries < 0 || !shape_ok(Hq, Hkv, D, kBlock)) return 0;
-  return workspace_for(num_seqs, total_q, max_entries, Hq, Hkv, D);
+  return workspace_for(kPlanDecodeOnly, num_seqs, total_q, max_entries, Hq, Hkv, D);
 }
 
 int lazyattn_encode_meta(const int32_t* block_ids, const int64_t* offsets,

@@ -207,23 +207,43 @@ __device__ __forceinline__ SeqFound wave_upper_seq(const int32_t* prefix, int n,
 // ---- workspace layout -----------------------------------------------------------------------
 // [0, 512)                RoPE frequency table, double [64] (revolutions per position)
 // [512, 768)              reserved; 16-byte zero rows at 576..767
-// [768, ...)              prefix arrays: prefill tiles, decode row-splits, each num_seqs + 1 int32
+// [768, ...)              prefix arrays: prefill items, decode row-splits, each num_seqs + 1 int32
+// aligned 256             counters: int32 [n_counters] (zeroed by the plan kernel)
 // aligned 256             split-K partials: float [row-splits][Hq][D + 4]  (o[D], m, l, -, -)
+// aligned 256             prefill KV-split partials: float [pf_slots][256 rows][D + 4]
 struct WsLayout {
-  size_t off_freqs, off_zero, off_pf_prefix, off_dec_prefix, off_partials, total;
+  size_t off_freqs, off_zero, off_pf_prefix, off_dec_prefix, off_counters, off_partials,
+      off_pf_partials, total;
 };
 
 __host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-__host__ __device__ inline WsLayout ws_layout(int num_seqs, long long max_rowsplits, int Hq, int D) {
+__host__ __device__ inline WsLayout ws_layout(int num_seqs, long long max_rowsplits, int Hq, int D,
+                                              long long n_counters = 0, long long pf_slots = 0) {
   WsLayout L;
   L.off_freqs = 0;
   L.off_zero = 576;
   L.off_pf_prefix = 768;
   L.off_dec_prefix = align_up(L.off_pf_prefix + 4ull * (num_seqs + 1), 256);
-  L.off_partials = align_up(L.off_dec_prefix + 4ull * (num_seqs + 1), 256);
-  L.total = L.off_partials + (size_t)max_rowsplits * Hq * (D + 4) * 4ull;
+  L.off_counters = align_up(L.off_dec_prefix + 4ull * (num_seqs + 1), 256);
+  L.off_partials = align_up(L.off_counters + 4ull * (size_t)n_counters, 256);
+  L.off_pf_partials =
+      align_up(L.off_partials + (size_t)max_rowsplits * Hq * (D + 4) * 4ull, 256);
+  L.total = L.off_pf_partials + (size_t)pf_slots * 256ull * (D + 4) * 4ull;
   return L;
+}
+
+// KV split of one prefill query tile over n_kt key tiles: at most smax splits of at least kc
+// key tiles (the last may be shorter), none empty. n_kt = 0 gives one empty split.
+struct PfSplit {
+  int splits, chunk;
+};
+__host__ __device__ inline PfSplit pf_split(int n_kt, int kc, int smax) {
+  if (n_kt <= 0) return PfSplit{1, 0};
+  int s = n_kt / kc + (n_kt % kc != 0);
+  s = s < 1 ? 1 : (s > smax ? smax : s);
+  const int chunk = (n_kt + s - 1) / s;
+  return PfSplit{(n_kt + chunk - 1) / chunk, chunk};
 }
 
 // Split-K of a decode row with T block-table entries: the host picks a base split size

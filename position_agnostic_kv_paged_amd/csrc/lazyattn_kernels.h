@@ -17,6 +17,9 @@ struct PlanParams {
   int bps, smax;             // decode split size (blocks) and splits-per-row cap
   int mode;                  // PlanMode
   int half_dim;
+  int pf_kc, pf_smax;        // prefill KV split: key tiles per split, splits-per-tile cap
+  int* counters;             // [n_counters] zeroed here (prefill tile counters)
+  int n_counters;
   RopeFreqs fr;              // host-computed table (kernel argument)
 };
 
@@ -30,10 +33,10 @@ struct PrefillParams {
   const int32_t* q_indptr;
   const int32_t* q_pos;
   uint16_t* out;
-  const int32_t* pf_prefix;
+  const int32_t* pf_prefix;  // [num_seqs + 1] prefill items (tiles x KV splits) per sequence
   const uint16_t* zero;      // zero bytes: source of V rows that must read as 0
   int num_seqs, Hq, Hkv, num_blocks;
-  int tiles_bound;           // upper bound of prefill tiles per KV head (grid sizing)
+  int pf_item_cap;           // upper bound of prefill items per KV head (grid / buffer sizing)
   float scale_log2;          // log2(e) / sqrt(D)
   const double* freqs;       // [D/2] RoPE frequencies (revolutions per position)
   const float* slopes;       // [Hq] ALiBi slopes (positional encoding kAlibi only)
@@ -41,6 +44,9 @@ struct PrefillParams {
   int rot_chunks;            // rotary_dim / 16 (kRopePartial only; nat_chunk)
   const int32_t* stored;     // [entries] stored rotation offset of slot 0 (kDocRotated only)
   int total_q;               // rows of q and out: rows at or past it are never touched
+  int pf_kc, pf_smax;        // KV split: key tiles per split, splits-per-tile cap (pf_split)
+  float* pf_partials;        // [Hkv * pf_item_cap][tile rows][D + 4]: split partials (o, m, l)
+  int* pf_counters;          // [Hkv * pf_item_cap]: finished splits of each tile (zeroed by plan)
 };
 
 // More than 16 query heads per KV head (G = 16 S): the kernels run Hkv * S "work heads" of

@@ -16,6 +16,7 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanParams P) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   if (tid < 48) P.zero[tid] = 0u;
   if (tid < P.half_dim) P.freqs_out[tid] = P.fr.f[tid];
+  for (int i = tid; i < P.n_counters; i += 256) P.counters[i] = 0;
   int carry_a = 0, carry_b = 0;                 // identical in every thread
   for (int base = 0; base < P.num_seqs; base += 256) {
     const int s = base + tid;
@@ -25,7 +26,8 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanParams P) {
       const int T = P.block_table[s + 1] - P.block_table[s];
       const bool dec = (P.mode == kPlanDecodeOnly) || qlen == 1;
       if (dec) b = qlen * row_splits(T, P.bps, P.smax);
-      else a = (qlen + P.pos_per_tile - 1) / P.pos_per_tile;
+      else a = (qlen + P.pos_per_tile - 1) / P.pos_per_tile *
+               pf_split((T + 3) / 4, P.pf_kc, P.pf_smax).splits;
     }
     int ia = a, ib = b;                          // inclusive scan within the wave
 #pragma unroll

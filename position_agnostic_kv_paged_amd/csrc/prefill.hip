@@ -126,8 +126,33 @@ __device__ __forceinline__ TileWords tile_words(const WinDec& wd) {
   return tw;
 }
 
+// LDS of one prefill work item (a workgroup of kPrefillWaves waves)
+template <int D>
+struct PrefillSmem {
+  static constexpr int NW = kPrefillWaves, NK = 64, HALF = D / 2, KS = D + 8;
+  static constexpr int VBYTES = NK * (D * 2 + 32);
+  alignas(16) uint16_t Ks[2][NK * KS];
+  alignas(16) uint8_t Vs[2][VBYTES];
+  // rotation tables as fp16 pairs, one 8-byte entry per two frequencies: {(cos, cos),
+  // (sin, sin)}, laid out [block or slot][pair][thread] so that the staging threads of a
+  // wave read consecutive 8-byte words
+  alignas(16) u32x2 tbl[2][4 * HALF / 2];   // (off_b - p_ref) theta_k
+  alignas(16) u32x2 slot_cs[16 * HALF / 2]; // j theta_k, j < 16
+  alignas(16) uint16_t Qs[NW][32 * KS];     // each wave's rotated queries (fp16)
+  double fr_s[HALF];
+  int pmax_s;
+  int last_s;                               // this split item completes its query tile
+};
+
+// One prefill work item: query tile qt of a sequence for KV (work) head kvh, over the key
+// tiles of one KV split. `item` numbers the items of a KV head: each sequence owns
+// tiles x splits consecutive items (plan_kernel's prefix sums), tile-major. An item that is
+// its tile's only split writes the bf16 output rows; otherwise it writes a partial
+// (o, m, l) per row, and the split that finishes its tile last merges the tile's partials
+// into the output (a per-tile counter; device-scope fences order the partial stores).
 template <int D, int G, int PE>
-__global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillParams P) {
+__device__ __forceinline__ void prefill_item(const PrefillParams& P, PrefillSmem<D>& SM,
+                                             const int kvh, const int item) {
   constexpr bool PART = PE == kRopePartial;   // dims in the permuted order of nat_chunk
   constexpr bool DOC = PE == kDocRotated;     // keys carry R(stored + j): rotate by off - stored
   constexpr bool ROTATE = PE == kRope || PART || DOC;   // keys rotated per tile
@@ -151,42 +176,34 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
   static_assert(FPT == 4 || FPT == 8, "staging unit = 4 or 8 frequencies of one key");
   using KRaw = typename std::conditional<FPT == 8, u32x4, u32x2>::type;
 
-  __shared__ __align__(16) uint16_t Ks[2][NK * KS];
-  __shared__ __align__(16) uint8_t Vs[2][VBYTES];
-  // (cos, sin) tables as float4 = two frequencies, laid out [block or slot][pair][thread]
-  // so that the staging threads of a wave read consecutive 16-byte words
-  // rotation tables as fp16 pairs, one 8-byte entry per two frequencies: {(cos, cos),
-  // (sin, sin)}, laid out [block or slot][pair][thread] so that the staging threads of a
-  // wave read consecutive 8-byte words
-  __shared__ __align__(16) u32x2 tbl[2][4 * HALF / 2];   // (off_b - p_ref) theta_k
-  __shared__ __align__(16) u32x2 slot_cs[16 * HALF / 2]; // j theta_k, j < 16
-  __shared__ __align__(16) uint16_t Qs[NW][32 * KS];     // each wave's rotated queries (fp16)
-  __shared__ double fr_s[HALF];
-  __shared__ int pmax_s;
+  auto& Ks = SM.Ks;
+  auto& Vs = SM.Vs;
+  auto& tbl = SM.tbl;
+  auto& slot_cs = SM.slot_cs;
+  auto& Qs = SM.Qs;
+  auto& fr_s = SM.fr_s;
+  auto& pmax_s = SM.pmax_s;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);    // wave index (uniform)
 
-  // XCD-aware order: consecutive workgroups land on different XCDs, so hand each XCD a
-  // contiguous range of tiles (tiles of one sequence and KV head share their key tiles).
-  const int nwg = gridDim.x;                                  // multiple of 8
-  const int Lb = blockIdx.x;
-  const int Lp = (Lb & 7) * (nwg >> 3) + (Lb >> 3);
-  const int tiles_bound = P.tiles_bound;
-  const int kvh = Lp / tiles_bound;
-  const int tile_id = Lp - kvh * tiles_bound;
-  if (kvh >= P.Hkv || tile_id >= P.pf_prefix[P.num_seqs]) return;   // uniform
   // The prologue is a chain of dependent memory round trips (sequence, its CSR entries,
   // then its queries, positions and words, then the first keys); independent loads are
   // issued together so that each link costs one trip.
-  const SeqFound sf = wave_upper_seq(P.pf_prefix, P.num_seqs, tile_id, lane);
+  const SeqFound sf = wave_upper_seq(P.pf_prefix, P.num_seqs, item, lane);
   const int seq = sf.s;
-  const int qt = __builtin_amdgcn_readfirstlane(tile_id - sf.start);
   const int q0 = __builtin_amdgcn_readfirstlane(P.q_indptr[seq]);
   const int qlen = __builtin_amdgcn_readfirstlane(P.q_indptr[seq + 1] - q0);
   const int e0 = __builtin_amdgcn_readfirstlane(P.block_table[seq]);
   const int T = __builtin_amdgcn_readfirstlane(P.block_table[seq + 1] - e0);
   const int kvlen = __builtin_amdgcn_readfirstlane(P.kv_lens[seq]);
+  // this item's query tile and key-tile range (KV split)
+  const PfSplit spl = pf_split((T + 3) / 4, P.pf_kc, P.pf_smax);
+  const int local = item - sf.start;
+  const int qt = __builtin_amdgcn_readfirstlane(local / spl.splits);
+  const int sp = __builtin_amdgcn_readfirstlane(local - qt * spl.splits);
+  const int kt_b = sp * spl.chunk;
+  const int kt_e = min((T + 3) / 4, kt_b + spl.chunk);
   // (rows at or past total_q -- a q_indptr that runs past the q array -- are not touched)
   const int p_ref =
       ROTATE ? __builtin_amdgcn_readfirstlane(P.q_pos[min(q0 + qt * POS, P.total_q - 1)]) : 0;
@@ -211,8 +228,8 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
                                                        : 16 * c + 8 * hh))
                        : u32x4{0, 0, 0, 0};
   }
-  uint32_t win = load_window(P, e0, T, 0, lane);           // words of tiles 0 .. 3
-  const int st0 = DOC ? load_stored(P, e0, T, 0, lane) : 0;
+  uint32_t win = load_window(P, e0, T, kt_b, lane);        // words of tiles kt_b .. kt_b+3
+  const int st0 = DOC ? load_stored(P, e0, T, kt_b, lane) : 0;
 
   for (int i = tid; i < HALF; i += NT) fr_s[i] = P.freqs[i];
   if (tid == 0) pmax_s = INT_MIN;
@@ -349,7 +366,6 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
   constexpr int VREM = VINST % NW;                          // + one more on waves < VREM
   static_assert(VPW >= 1 && VPW <= 3, "value loads are placed in the first score k-steps");
 
-  const int n_kt = (T + 3) / 4;
   KRaw klo{}, khi{};
   // raw keys of a tile into (klo, khi); empty slots read as zero
   // (key staging reads block kb of tile kt + d: lane 4 d + kb of the decoded window)
@@ -386,8 +402,8 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
   // vector work that hides under it, LDS operands are fetched one MFMA group ahead, and the
   // loads for later tiles are spread over A's k-steps so that the vector memory path
   // overlaps the matrix cores instead of stalling every wave right after the barrier.
-  if (n_kt > 0) {
-    const WinDec wd = decode_window(P, win, st0, T, kvlen, 0, lane);
+  if (kt_e > kt_b) {
+    const WinDec wd = decode_window(P, win, st0, T, kvlen, kt_b, lane);
     KRaw kraw[2][2];                                         // raw keys of tiles 0 and 1
     load_k_to(wd, 0, kraw[0][0], kraw[0][1]);
     load_k_to(wd, 1, kraw[1][0], kraw[1][1]);
@@ -450,8 +466,8 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
       }
     }
   };
-  if (n_kt > 0) qk(0, S0);
-  WinDec wdc = decode_window(P, win, st0, T, kvlen, 0, lane);
+  if (kt_e > kt_b) qk(0, S0);
+  WinDec wdc = decode_window(P, win, st0, T, kvlen, kt_b, lane);
   add_bias(S0[0], wdc, 0);
   add_bias(S0[1], wdc, 1);
   bool maskc = needs_mask(wdc);
@@ -465,7 +481,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
 
   // one pipeline iteration: S(kt) in Sc on entry, S(kt+1) left in Sn
   auto step = [&](const int kt, f32x16 (&Sc)[2], f32x16 (&Sn)[2]) {
-    const int cur = kt & 1, nxt = cur ^ 1;
+    const int cur = (kt - kt_b) & 1, nxt = cur ^ 1;          // buffers of tiles kt, kt+1
     // wdc (decoded words of tiles kt .. kt+3) and mxc (row max of S(kt) before masking)
     // were computed under the MFMAs of the previous iteration
     const WinDec wd = wdc;
@@ -694,34 +710,117 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillP
     __builtin_amdgcn_s_waitcnt(0x0F70);                      // vmcnt(0): values of tile kt+1
     __syncthreads();
   };
-  for (int kt = 0; kt < n_kt; kt += 2) {                     // unrolled x2: S0 <-> S1
+  for (int kt = kt_b; kt < kt_e; kt += 2) {                  // unrolled x2: S0 <-> S1
     step(kt, S0, S1);
-    if (kt + 1 < n_kt) step(kt + 1, S1, S0);
+    if (kt + 1 < kt_e) step(kt + 1, S1, S0);
   }
 
   // ---- epilogue: O / l -> bf16 ----------------------------------------------------------
   const float lt = xor32_add(l);
-  const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  if (row_ok) {
-    uint16_t* dst = P.out + ((size_t)(q0 + qi) * P.Hq + h) * D;
+  if (spl.splits == 1) {
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    if (row_ok) {
+      uint16_t* dst = P.out + ((size_t)(q0 + qi) * P.Hq + h) * D;
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) {
+      for (int dt = 0; dt < D / 32; ++dt) {
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        u32x2 v;
-        v[0] = pack_bf16(o[dt][4 * r4] * inv, o[dt][4 * r4 + 1] * inv);
-        v[1] = pack_bf16(o[dt][4 * r4 + 2] * inv, o[dt][4 * r4 + 3] * inv);
-        *(u32x2*)(dst + 32 * dt + 8 * r4 + 4 * hh) = v;
+        for (int r4 = 0; r4 < 4; ++r4) {
+          u32x2 v;
+          v[0] = pack_bf16(o[dt][4 * r4] * inv, o[dt][4 * r4 + 1] * inv);
+          v[1] = pack_bf16(o[dt][4 * r4 + 2] * inv, o[dt][4 * r4 + 3] * inv);
+          *(u32x2*)(dst + 32 * dt + 8 * r4 + 4 * hh) = v;
+        }
+      }
+    }
+    return;
+  }
+  // KV split: partial (o, m, l) of each row of the tile, [slot][row rho][D + 4] floats
+  constexpr int RS = D + 4;
+  const size_t cap = (size_t)P.pf_item_cap;
+  float* part = P.pf_partials + ((size_t)kvh * cap + item) * (size_t)(ROWS * RS);
+  {
+    float* pr = part + (size_t)rho * RS;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        *(f32x4*)(pr + 32 * dt + 8 * r4 + 4 * hh) =
+            f32x4{o[dt][4 * r4], o[dt][4 * r4 + 1], o[dt][4 * r4 + 2], o[dt][4 * r4 + 3]};
+    if (hh == 0) {
+      pr[D] = lt > 0.f ? m : -INFINITY;
+      pr[D + 1] = lt;
+    }
+  }
+  // the tile's counter: the split that brings it to `splits` merges every split's partial
+  __threadfence();                                           // partials visible device-wide
+  __syncthreads();
+  const int first = item - sp;                               // the tile's first split item
+  if (tid == 0) {
+    int* cnt = P.pf_counters + (size_t)kvh * cap + first;
+    SM.last_s = atomicAdd(cnt, 1) == spl.splits - 1;
+  }
+  __syncthreads();
+  if (!SM.last_s) return;
+  __threadfence();                                           // see the other splits' stores
+  // two threads per row, D/2 dims each: M = max m, L = sum l 2^(m - M), O = sum o 2^(m - M)
+  {
+    const int row = tid >> 1, half = tid & 1;
+    const int rq = qt * POS + row / G;                       // query row in the sequence
+    const int rh = kvh * G + row % G;                        // query head
+    if ((rq < qlen) & (q0 + rq < P.total_q)) {
+      const float* base = P.pf_partials + ((size_t)kvh * cap + first) * (size_t)(ROWS * RS) +
+                          (size_t)row * RS;
+      float M = -INFINITY;
+      for (int s2 = 0; s2 < spl.splits; ++s2)
+        M = fmaxf(M, base[(size_t)s2 * ROWS * RS + D]);
+      float L = 0.f;
+      f32x4 acc[D / 8];
+#pragma unroll
+      for (int i = 0; i < D / 8; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int s2 = 0; s2 < spl.splits; ++s2) {
+        const float* ps = base + (size_t)s2 * ROWS * RS;
+        const float ms = ps[D];
+        if (ms == -INFINITY) continue;                       // no visible key in this split
+        const float wgt = __builtin_amdgcn_exp2f(ms - M);
+        L += ps[D + 1] * wgt;
+#pragma unroll
+        for (int i = 0; i < D / 8; ++i)
+          acc[i] += *(const f32x4*)(ps + half * (D / 2) + 4 * i) * wgt;
+      }
+      const float inv = L > 0.f ? 1.f / L : 0.f;
+      uint16_t* dst = P.out + ((size_t)(q0 + rq) * P.Hq + rh) * D + half * (D / 2);
+#pragma unroll
+      for (int i = 0; i < D / 8; i += 2) {
+        u32x4 v;
+        v[0] = pack_bf16(acc[i][0] * inv, acc[i][1] * inv);
+        v[1] = pack_bf16(acc[i][2] * inv, acc[i][3] * inv);
+        v[2] = pack_bf16(acc[i + 1][0] * inv, acc[i + 1][1] * inv);
+        v[3] = pack_bf16(acc[i + 1][2] * inv, acc[i + 1][3] * inv);
+        *(u32x4*)(dst + 4 * i) = v;
       }
     }
   }
+}
+
+template <int D, int G, int PE>
+__global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillParams P) {
+  __shared__ PrefillSmem<D> SM;
+  // XCD-aware order: consecutive workgroups land on different XCDs, so hand each XCD a
+  // contiguous range of items (tiles of one sequence and KV head share their key tiles).
+  const int nwg = gridDim.x;                                  // multiple of 8
+  const int Lb = blockIdx.x;
+  const int Lp = (Lb & 7) * (nwg >> 3) + (Lb >> 3);
+  const int kvh = Lp / P.pf_item_cap;
+  const int item = Lp - kvh * P.pf_item_cap;
+  if (kvh >= P.Hkv || item >= P.pf_prefix[P.num_seqs]) return;   // uniform
+  prefill_item<D, G, PE>(P, SM, kvh, item);
 }
 
 int prefill_positions_per_tile(int G) { return 32 * kPrefillWaves / G; }
 
 template <int D, int G>
 static hipError_t launch_dg(const PrefillParams& p, int pe, hipStream_t st) {
-  const long long n = (long long)p.tiles_bound * p.Hkv;
+  const long long n = (long long)p.pf_item_cap * p.Hkv;
   dim3 grid((unsigned)((n + 7) / 8 * 8)), block(kPrefillWaves * 64);
   switch (pe) {
     case kRope: hipLaunchKernelGGL((prefill_kernel<D, G, kRope>), grid, block, 0, st, p); break;
@@ -751,7 +850,7 @@ static hipError_t launch_d(const PrefillParams& p, int G, int pe, hipStream_t st
 }
 
 hipError_t launch_prefill(const PrefillParams& p, int D, int G, int pe, hipStream_t st) {
-  if (p.tiles_bound <= 0) return hipSuccess;
+  if (p.pf_item_cap <= 0) return hipSuccess;
   return D == 128 ? launch_d<128>(p, G, pe, st) : launch_d<64>(p, G, pe, st);
 }
 

@@ -549,6 +549,58 @@ def test_mixed_70b_batch(q_scale):
 
 
 @pytest.mark.timeout(300)
+@pytest.mark.parametrize("q_scale", [1.0, 4.0])
+def test_kv_split_one_long_request(q_scale):
+    """One request, 256 queries over 32,512 keys: 32 query tiles in all (4 per KV head),
+    too few for the GPU, so each tile's key range is split and the splits are merged by the
+    tile's last one. Every row against the oracle."""
+    wl = make("prefill-32q8kv-b1-ctx32512", q_scale=q_scale)
+    say(f"{wl.name} via prefill (KV split), every row")
+    _full_check(wl, "prefill", wl.name)
+
+
+def _split_cases():
+    """Small layouts long enough (> 512 keys) to be KV-split: uneven split boundaries,
+    queries whose causal window ends inside an early split, a mixed batch with decode rows
+    and an entry-less request, G from 1 to 16."""
+    cases = []
+    segs = [Segment("doc", 5 + 40 * i, doc=i % 4) for i in range(25)] + \
+        [Segment("private", 5 + 40 * 25 + 3, tokens=300)]
+    cases.append(("split-one-request-G1-D64", dict(Hq=2, Hkv=2, D=64, segs=segs, q_len=300,
+                                                   n_docs=4, seed=51)))
+    cases.append(("split-one-request-G4-peaky", dict(Hq=8, Hkv=2, D=128, segs=segs, q_len=300,
+                                                     n_docs=4, seed=52, q_scale=4.0)))
+    early = np.concatenate([np.arange(40, 140), 1000 + np.arange(60), [1305]])
+    cases.append(("split-early-queries", dict(Hq=8, Hkv=1, D=128, segs=segs, q_len=161,
+                                              q_pos=early, n_docs=4, seed=53)))
+    cases.append(("split-G16", dict(Hq=16, Hkv=1, D=128, segs=segs, q_len=77, n_docs=4,
+                                    seed=54)))
+    reqs = [RequestLayout(segs, 130),
+            RequestLayout([Segment("doc", 0, doc=2), Segment("private", 32, tokens=5)], 1),
+            RequestLayout([], 1, np.array([3])),
+            RequestLayout([Segment("doc", 9 + 32 * i, doc=i % 4) for i in range(30)] +
+                          [Segment("private", 9 + 32 * 30, tokens=40)], 40)]
+    cases.append(("split-mixed-batch", dict(Hq=8, Hkv=2, D=128, requests=reqs, n_docs=4,
+                                            seed=55)))
+    return cases
+
+
+@pytest.mark.parametrize("name,kw", _split_cases(), ids=[c[0] for c in _split_cases()])
+def test_kv_split_cases(name, kw):
+    wl = small(**kw)
+    say(f"KV split case {name}: kv_lens {list(wl.kv_lens)}")
+    compare(run_hip(wl, "prefill"), oracle_out(wl), f"{name}/prefill")
+
+
+@pytest.mark.parametrize("bound", [1, 9, 100000])
+def test_kv_split_max_entries_hint(bound):
+    """A max_entries hint below or far above the real length changes only the KV split."""
+    wl = small(**dict(_split_cases())["split-mixed-batch"])
+    say(f"KV split, max_entries = {bound}")
+    compare(run_hip(wl, "prefill", max_entries=bound), oracle_out(wl), f"split-hint{bound}")
+
+
+@pytest.mark.timeout(300)
 def test_shifted_document_is_detected_full_size():
     """Detection at full size: the long-decode batch with peaky queries, one document of
     every request placed one position later in the words the GPU gets. The GPU output must

@@ -372,6 +372,18 @@ CONFIGS = {
 
 CONFIG_ORDER = list(CONFIGS)
 
+# Not one of the five named workloads: one long request whose 256-query prefill has too few
+# query tiles to fill the GPU, so the prefill key range is split (KV split). Seeded as if it
+# were the sixth configuration.
+EXTRA_CONFIGS = {
+    "prefill-32q8kv-b1-ctx32512": Config(
+        "prefill-32q8kv-b1-ctx32512", Hq=32, Hkv=8, D=128, B=16, rope_base=10000.0,
+        n_docs=4000, doc_tokens=512, zipf_s=1.2,
+        groups=(Group(1, 63, 256, 256, gap_max=63),),
+        description="1 request x (63 Zipf(1.2) docs x 512 with gaps + 256-token suffix "
+                    "prefill): 32,512 keys"),
+}
+
 
 def _tiny_layouts(decode: bool) -> List[RequestLayout]:
     segs = [Segment("doc", 0, doc=0), Segment("doc", 64, doc=1)]
@@ -387,9 +399,10 @@ def make(name: str, seed: Optional[int] = None, decode_variant: bool = False,
     """Build a named configuration. Master seed defaults to 1000 + its 1-based index.
     q_scale multiplies the N(0, 1) queries before rounding (q_scale 4 gives the peaky
     softmax of the stress variants)."""
-    cfg = CONFIGS[name]
+    cfg = CONFIGS[name] if name in CONFIGS else EXTRA_CONFIGS[name]
     if seed is None:
-        seed = 1000 + CONFIG_ORDER.index(name) + 1
+        seed = 1000 + (CONFIG_ORDER.index(name) + 1 if name in CONFIGS
+                       else len(CONFIG_ORDER) + 1 + list(EXTRA_CONFIGS).index(name))
     if name.startswith("tiny-prefill"):
         lays = _tiny_layouts(decode_variant)
     else:
