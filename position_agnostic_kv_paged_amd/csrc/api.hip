@@ -68,9 +68,9 @@ DecodeSplit decode_split(int rows_bound, int Hkv, int max_entries) {
 // are merged by the tile's last split. The host cannot see the per-sequence lengths (no
 // device reads), so it sizes the split from total_q and the max_entries hint; plan_kernel
 // applies the same rule (pf_split) to each sequence's real length.
-constexpr int kPfItemsPerCu = 2;    // target prefill items per compute unit
+constexpr int kPfItemsPerCu = 1;    // target prefill items per compute unit (one round)
 constexpr int kPfMinChunk = 8;      // key tiles (of 64 keys) per split, at least
-constexpr int kPfMaxSplits = 32;
+constexpr int kPfMaxSplits = kMaxPfSplits;
 
 struct CallPlan {
   DecodeSplit ds;

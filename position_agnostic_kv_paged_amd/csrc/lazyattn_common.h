@@ -235,6 +235,8 @@ __host__ __device__ inline WsLayout ws_layout(int num_seqs, long long max_rowspl
 
 // KV split of one prefill query tile over n_kt key tiles: at most smax splits of at least kc
 // key tiles (the last may be shorter), none empty. n_kt = 0 gives one empty split.
+constexpr int kMaxPfSplits = 32;   // splits per prefill tile, at most
+
 struct PfSplit {
   int splits, chunk;
 };

@@ -762,30 +762,43 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& P, PrefillSmem
   __syncthreads();
   if (!SM.last_s) return;
   __threadfence();                                           // see the other splits' stores
-  // two threads per row, D/2 dims each: M = max m, L = sum l 2^(m - M), O = sum o 2^(m - M)
+  // two threads per row, D/2 dims each: M = max m, L = sum l 2^(m - M), O = sum o 2^(m - M).
+  // Every split's m is loaded at once; then two splits' (o, l) per round of loads.
   {
     const int row = tid >> 1, half = tid & 1;
     const int rq = qt * POS + row / G;                       // query row in the sequence
     const int rh = kvh * G + row % G;                        // query head
     if ((rq < qlen) & (q0 + rq < P.total_q)) {
-      const float* base = P.pf_partials + ((size_t)kvh * cap + first) * (size_t)(ROWS * RS) +
+      constexpr size_t SPLIT = (size_t)ROWS * RS;            // floats per split partial
+      const float* base = P.pf_partials + ((size_t)kvh * cap + first) * SPLIT +
                           (size_t)row * RS;
+      const int ns = spl.splits;                             // <= kMaxPfSplits
       float M = -INFINITY;
-      for (int s2 = 0; s2 < spl.splits; ++s2)
-        M = fmaxf(M, base[(size_t)s2 * ROWS * RS + D]);
+#pragma unroll
+      for (int s2 = 0; s2 < kMaxPfSplits; ++s2)
+        if (s2 < ns) M = fmaxf(M, base[s2 * SPLIT + D]);
+      const float Mu = M == -INFINITY ? 0.f : M;             // all -inf: weights 0, row 0
       float L = 0.f;
       f32x4 acc[D / 8];
 #pragma unroll
       for (int i = 0; i < D / 8; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int s2 = 0; s2 < spl.splits; ++s2) {
-        const float* ps = base + (size_t)s2 * ROWS * RS;
-        const float ms = ps[D];
-        if (ms == -INFINITY) continue;                       // no visible key in this split
-        const float wgt = __builtin_amdgcn_exp2f(ms - M);
-        L += ps[D + 1] * wgt;
+      for (int s2 = 0; s2 < ns; s2 += 2) {
+        const bool two = s2 + 1 < ns;
+        const float* p0 = base + s2 * SPLIT;
+        const float* p1 = two ? p0 + SPLIT : p0;
+        f32x4 o0[D / 8], o1[D / 8];
+        const float m0 = p0[D], l0 = p0[D + 1], m1 = p1[D], l1 = p1[D + 1];
 #pragma unroll
-        for (int i = 0; i < D / 8; ++i)
-          acc[i] += *(const f32x4*)(ps + half * (D / 2) + 4 * i) * wgt;
+        for (int i = 0; i < D / 8; ++i) {
+          o0[i] = *(const f32x4*)(p0 + half * (D / 2) + 4 * i);
+          o1[i] = *(const f32x4*)(p1 + half * (D / 2) + 4 * i);
+        }
+        // a split with no visible key has m = -inf, l = 0, o = 0: weight exp2(-inf) = 0
+        const float w0 = __builtin_amdgcn_exp2f(m0 - Mu);
+        const float w1 = two ? __builtin_amdgcn_exp2f(m1 - Mu) : 0.f;
+        L += l0 * w0 + l1 * w1;
+#pragma unroll
+        for (int i = 0; i < D / 8; ++i) acc[i] += o0[i] * w0 + o1[i] * w1;
       }
       const float inv = L > 0.f ? 1.f / L : 0.f;
       uint16_t* dst = P.out + ((size_t)(q0 + rq) * P.Hq + rh) * D + half * (D / 2);
