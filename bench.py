@@ -4,18 +4,23 @@
 Workload: the mixed continuous batch "mixed-64q8kv-4p96d" (64 q / 8 KV heads, head dim
 128, bf16, block size 16, one 2000-document position-free pool): 4 prefill requests
 (16 Zipf(1.1) documents x 1024 tokens + 512-token suffix prefilled causally) and 96 decode
-requests (12 documents x 1024 tokens + 1 token). One step = the prefill half through
-lazyattn_prefill plus the decode half through lazyattn_decode, on the current HIP stream,
-each call bracketed by HIP events. Inputs are resident in HBM before timing.
+requests (12 documents x 1024 tokens + 1 token). One step = ONE lazyattn_prefill call over
+the whole batch (prefill tiles and decode items in one launch), on the current HIP stream,
+bracketed by HIP events. Inputs are resident in HBM before timing.
 
-Reported (one JSON line): prefill attention TFLOP/s (algorithmic: 4*D FLOP per visible
-(query, key, q-head) pair) as `value`, decode attention GB/s (algorithmic: K+V bytes of
-every (sequence, key) plus q, out and 4 B per block entry) in `decode`, also as unique-block
-bytes and counter-measured HBM bytes per second, p10/median/p90 call times, the roofline of
-the dominant kernel, and the float64 oracle timed on a bounded sample on the host cores.
-
-Other configurations (--workload), a no-reuse control (--no-reuse) and cold-cache steps
-(--cold) are for reference runs; the default line is the mixed batch, warm.
+Reported (one JSON line):
+  value        attention TFLOP/s of the whole step (algorithmic: 4*D FLOP per visible
+               (query, key, q-head) pair of every row, prefill and decode);
+  mixed_step   the step against the sum of its halves run as separate calls, and against
+               the overlapped roofline max(MFMA time, HBM time) of the whole batch;
+  prefill      the prefill half alone (same kernel): TFLOP/s, fraction of the MFMA peak --
+               the `roofline` object describes this launch;
+  decode       the decode half alone (lazyattn_decode): GB/s of logical K+V bytes, of
+               distinct blocks, counter-measured HBM bytes; cold-cache and no-reuse rates;
+  decode_controls  the two decode configurations (C2, C4): warm, cold (1 GiB written
+               before every repetition) and the no-reuse control of the same shape;
+plus p10/median/p90 of every timing, the rotation ablation, the measured ceilings and the
+float64 oracle timed on a bounded sample on the host cores.
 """
 import argparse
 import json
@@ -65,7 +70,8 @@ def kernel_source_hash(kernel):
     """Hash of the sources a kernel is built from (ties recorded counters to a kernel version)."""
     import hashlib
     csrc = os.path.join(ROOT, "position_agnostic_kv_paged_amd", "csrc")
-    files = {"prefill_kernel": ["prefill.hip"], "decode_kernel": ["decode.hip"]}[kernel]
+    files = {"prefill": ["prefill_body.h", "mixed.hip", "decode_body.h"],
+             "decode": ["decode.hip", "decode_body.h"]}[kernel]
     h = hashlib.sha256()
     for f in files + ["lazyattn_common.h", "lazyattn_kernels.h"]:
         with open(os.path.join(csrc, f), "rb") as fh:
@@ -154,11 +160,11 @@ def record_traffic(fetch_dir, write_dir):
                            "write_kib_on_copy": w[cal],
                            "fetch_factor": target_kib / f[cal],
                            "write_factor": target_kib / w[cal]}}
-    for kernel, tag in (("prefill_kernel", "lazyattn::prefill_kernel<"),
-                        ("decode_kernel", "lazyattn::decode_kernel<")):
-        # launches of the half under test: a prefill call also launches the decode kernel
-        # (for its single-row sequences, none here), which then finds no work
-        # the lazy (RoPE, mode 0) instantiation only; the materialised baseline's is mode 1
+    for kernel, tag in (("prefill", "lazyattn::mixed_kernel<"),
+                        ("decode", "lazyattn::decode_kernel<")):
+        # the counter runs use --counters: prefill-half calls (mixed_kernel with prefill items
+        # only) and decode-half calls (decode_kernel); the lazy (RoPE, mode 0) instantiation
+        # only, the materialised baseline's is mode 1
         keys = [k for k in f if tag in k[1] and ", 0>(" in k[1] and k in w]
         if not keys:
             continue
@@ -302,6 +308,64 @@ def measured_ceilings(torch, L, stream, reps=5):
                     "device-to-device copy of 1 GiB, read + write bytes"}
 
 
+def timed(torch, stream, fn, reps, warmup, flush=None):
+    """Median-style timing of fn on `stream`: warmup calls, then reps calls each bracketed
+    by HIP events (a flush fill before each one, outside the events, when given)."""
+    for _ in range(warmup):
+        fn()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps)]
+    for k in range(reps):
+        if flush is not None:
+            flush.fill_(1.0)
+        ev[2 * k].record(stream)
+        fn()
+        ev[2 * k + 1].record(stream)
+    torch.cuda.synchronize()
+    ts = [ev[2 * k].elapsed_time(ev[2 * k + 1]) for k in range(reps)]
+    st = pct(ts)
+    st["mean"] = float(np.mean(ts))
+    return st
+
+
+def attention_call(L, fn, wl, a, ws, stream):
+    return lambda: fn(a["q"], a["k_pool"], a["v_pool"], a["block_table"], a["block_meta"],
+                      a["kv_lens"], a["q_indptr"], a["q_pos"], wl.rope_base, a["max_entries"],
+                      out=a["out"], workspace=ws, stream=stream)
+
+
+def workspace_for(torch, L, kind, wl, a, dev):
+    return torch.empty(L.workspace_bytes(kind, a["kv_lens"].numel(), a["q"].shape[0],
+                                         a["max_entries"], wl.Hq, wl.Hkv, wl.D),
+                       dtype=torch.uint8, device=dev)
+
+
+def decode_control(torch, L, name, dev, stream, reps, warmup, flush):
+    """Warm, cold and no-reuse rates of a decode configuration (lazyattn_decode)."""
+    from workload import make
+    out = {}
+    for label, no_reuse in (("zipf", False), ("no_reuse", True)):
+        wl = make(name, no_reuse=no_reuse)
+        pool = wl.to_device(dev)
+        seqs = list(range(wl.num_seqs))
+        a = half_inputs(wl, seqs, dev, pool)
+        ws = workspace_for(torch, L, "decode", wl, a, dev)
+        f = attention_call(L, L.decode, wl, a, ws, stream)
+        nbytes = decode_bytes(wl, seqs)
+        runs = (("warm", None), ("cold", flush)) if not no_reuse else (("warm", None),)
+        for mode, fl in runs:
+            st = timed(torch, stream, f, reps, warmup, fl)
+            key = label if label == "no_reuse" else mode
+            out[key] = {"ms": st, "gbs": nbytes / (st["median"] / 1e3) / 1e9,
+                        "frac_hbm_peak": nbytes / (st["median"] / 1e3) / 1e9 / PEAK_HBM_GBS}
+        del pool, a, ws
+        torch.cuda.empty_cache()
+    out["algorithmic_gb"] = nbytes / 1e9
+    out["note"] = ("logical K+V bytes of every (sequence, key) plus q, out and words over the "
+                   "median call time; cold: 1 GiB written before each repetition (L2 and MALL "
+                   "flushed); no_reuse: every document appears once (no block read twice)")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -309,11 +373,11 @@ def main():
     # the first ~10 launches after the inputs are uploaded run up to 15% slower (the clock
     # ramps under load); the timed steps measure the steady state
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--reps", type=int, default=50,
+                    help="repetitions of every reference timing (halves, controls, ablation)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
-                    help="profiling aid: run only one half (the JSON line then reports it alone)")
     ap.add_argument("--workload", default=WORKLOAD,
-                    help="configuration to time (default: the mixed batch); the others are "
+                    help="configuration of the step (default: the mixed batch); the others are "
                          "the parity configurations, timed for reference")
     ap.add_argument("--no-reuse", action="store_true",
                     help="control of the same shape in which every document appears once")
@@ -321,11 +385,15 @@ def main():
                     help="overwrite a 1 GiB buffer before every step (flushes L2 and MALL; "
                          "outside the timed calls)")
     ap.add_argument("--no-ablation", action="store_true",
-                    help="skip the rotation ablation (the materialised-baseline entry points "
-                         "timed on the same inputs)")
+                    help="skip the rotation ablation and the variants")
+    ap.add_argument("--no-controls", action="store_true",
+                    help="skip the decode configurations' cold and no-reuse controls")
+    ap.add_argument("--counters", action="store_true",
+                    help="profiling pass for rocprofv3 --pmc: only prefill-half and decode-half "
+                         "calls, a few of each, then exit")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/traffic.json from two rocprofv3 --pmc runs of this "
-                         "script (FETCH_SIZE, then WRITE_SIZE) and exit; needs no GPU")
+                         "script with --counters (FETCH_SIZE, then WRITE_SIZE) and exit")
     args = ap.parse_args()
     if args.record_traffic:
         record_traffic(*args.record_traffic)
@@ -343,43 +411,27 @@ def main():
         sys.exit(2)
     L.lib()
     dev = "cuda:0"
+    stream = torch.cuda.current_stream()
     wl = make(args.workload, no_reuse=args.no_reuse)
     qlen = np.diff(wl.q_indptr)
-    pre_seqs = [s for s in range(wl.num_seqs) if qlen[s] > 1]
-    dec_seqs = [s for s in range(wl.num_seqs) if qlen[s] == 1]
-    if args.only == "prefill":
-        dec_seqs = []
-    if args.only == "decode":
-        pre_seqs = []
+    all_seqs = list(range(wl.num_seqs))
+    pre_seqs = [s for s in all_seqs if qlen[s] > 1]
+    dec_seqs = [s for s in all_seqs if qlen[s] == 1]
     pool = wl.to_device(dev)
-    halves = []
-    baseline = {"prefill": L.prefill_rotated_pool, "decode": L.decode_rotated_pool}
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
+    # the step: one lazyattn_prefill call over the whole batch (any mix of query lengths);
+    # a pure decode configuration runs lazyattn_decode
+    step_fn = L.prefill if pre_seqs else L.decode
+    step_kind = "prefill" if pre_seqs else "decode"
+    a_all = half_inputs(wl, all_seqs, dev, pool)
+    ws_all = workspace_for(torch, L, step_kind, wl, a_all, dev)
+    step = attention_call(L, step_fn, wl, a_all, ws_all, stream)
+    halves = {}
     for kind, seqs, fn in (("prefill", pre_seqs, L.prefill), ("decode", dec_seqs, L.decode)):
-        if not seqs:
-            continue
-        a = half_inputs(wl, seqs, dev, pool)
-        ws = torch.empty(L.workspace_bytes(kind, len(seqs), a["q"].shape[0], a["max_entries"],
-                                           wl.Hq, wl.Hkv, wl.D), dtype=torch.uint8, device=dev)
-        halves.append((kind, seqs, fn, a, ws))
-    stream = torch.cuda.current_stream()
-
-    def call(fn, a, ws):
-        fn(a["q"], a["k_pool"], a["v_pool"], a["block_table"], a["block_meta"], a["kv_lens"],
-           a["q_indptr"], a["q_pos"], wl.rope_base, a["max_entries"], out=a["out"],
-           workspace=ws, stream=stream)
-
-    nh = len(halves)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nh + 1)]
-          for _ in range(args.steps)]
-    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev) if args.cold else None
-
-    def step(e=None):
-        if flush is not None:
-            flush.fill_(1.0)
-        for i, (kind, seqs, fn, a, ws) in enumerate(halves):
-            if e: e[i].record(stream)
-            call(fn, a, ws)
-        if e: e[nh].record(stream)
+        if seqs:
+            a = half_inputs(wl, seqs, dev, pool)
+            ws = workspace_for(torch, L, kind, wl, a, dev)
+            halves[kind] = (seqs, fn, a, ws, attention_call(L, fn, wl, a, ws, stream))
 
     # a plain copy of known size, once, so that FETCH_SIZE / WRITE_SIZE counter runs over
     # this program can be scaled to bytes (the factor is recorded with the counters)
@@ -388,19 +440,40 @@ def main():
     dst.copy_(src)
     del src, dst
     torch.cuda.synchronize()
+    if args.counters:
+        for kind in ("prefill", "decode"):
+            if kind in halves:
+                for _ in range(5):
+                    halves[kind][4]()
+        torch.cuda.synchronize()
+        print(json.dumps({"counters_pass": sorted(halves)}), flush=True)
+        return
 
+    # ---- the timed step -------------------------------------------------------------------
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
+    cold = flush if args.cold else None
     t0 = time.perf_counter()
     for k in range(args.steps):
-        step(ev[k])
+        if cold is not None:
+            cold.fill_(1.0)
+        ev[2 * k].record(stream)
+        step()
+        ev[2 * k + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    ts = [ev[2 * k].elapsed_time(ev[2 * k + 1]) for k in range(args.steps)]
+    step_ms = float(np.mean(ts))
+    pre_flops = prefill_flops(wl, pre_seqs) if pre_seqs else 0.0
+    dec_flops = 4.0 * wl.D * wl.Hq * sum(int(wl.kv_lens[s]) for s in dec_seqs)
+    dbytes = decode_bytes(wl, dec_seqs) if dec_seqs else 0.0
+    value = (pre_flops + dec_flops) / (step_ms / 1e3) / 1e12
 
-    line = {"metric": METRIC, "value": 0.0, "unit": "TFLOP/s", "n_gpus": 1,
+    line = {"metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup,
-            "ms_per_step": wall / args.steps * 1e3, "higher_is_better": True,
+            "ms_per_step": step_ms, "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
             "data": "synthetic (seeded N(0,1) bf16, Zipf document reuse)"
                     + (", no-reuse control" if args.no_reuse else "")
@@ -409,65 +482,78 @@ def main():
                        "operands": "bf16 in/out, fp16 rotated q/k and bf16 p/v on MFMA, fp32 "
                                    "accumulation",
                        "block": wl.B, "prefill_requests": len(pre_seqs),
-                       "decode_requests": len(dec_seqs), "pool_blocks": wl.num_blocks}}
+                       "decode_requests": len(dec_seqs), "pool_blocks": wl.num_blocks,
+                       "step": f"one {'lazyattn_prefill' if pre_seqs else 'lazyattn_decode'} "
+                               f"call over the whole batch"},
+            "step_ms_pct": pct(ts),
+            "value_definition": "algorithmic attention FLOPs of the whole step (prefill and "
+                                "decode rows, 4*D per visible (query, key, q-head) pair) over "
+                                "the mean step time"}
+
+    # ---- the halves alone: per-kernel rooflines ----------------------------------------------
     roofs = []
-    for i, (kind, seqs, fn, a, ws) in enumerate(halves):
-        ts = [e[i].elapsed_time(e[i + 1]) / 1e3 for e in ev]
-        t = float(np.mean(ts))
-        stats = {k: v * 1e3 for k, v in pct(ts).items()}
-        if kind == "prefill":
-            flops = prefill_flops(wl, seqs)
-            val = flops / t / 1e12
-            line["prefill"] = {"value": val, "unit": "TFLOP/s", "ms": t * 1e3, "ms_pct": stats,
-                               "frac_mfma_peak": val / PEAK_MFMA_TFLOPS,
-                               "algorithmic_tflop": flops / 1e12}
-            roofs.append((t, {"kernel": "prefill_kernel", "bound": "mfma", "achieved": val,
-                              "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s"}))
-        else:
-            dbytes, ubytes = decode_bytes(wl, seqs), unique_decode_bytes(wl, seqs)
-            val = dbytes / t / 1e9
-            line["decode"] = {"value": val, "unit": "GB/s", "ms": t * 1e3, "ms_pct": stats,
-                              "frac_hbm_peak": val / PEAK_HBM_GBS,
-                              "algorithmic_gb": dbytes / 1e9,
-                              "unique_gb": ubytes / 1e9, "unique_gbs": ubytes / t / 1e9}
-            roofs.append((t, {"kernel": "decode_kernel", "bound": "hbm", "achieved": val,
-                              "peak": PEAK_HBM_GBS, "unit": "GB/s"}))
-    # `value` is the prefill half's TFLOP/s when the batch has one, else the decode GB/s
-    if "prefill" in line:
-        line["value"] = line["prefill"]["value"]
-    else:
-        line["metric"] = "decode attn HBM GB/s (logical K+V bytes), Zipf RAG batch"
-        line["value"], line["unit"] = line["decode"]["value"], "GB/s"
-    t_dom, roof = max(roofs, key=lambda r: r[0])
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = (recorded_traffic(roof["kernel"])
-                       if wl.name == WORKLOAD and not args.cold else None)
-    roof["launch_ms"] = t_dom * 1e3
-    line["roofline"] = roof
-    # decode GB/s three ways: logical (value), unique blocks, and counter-measured HBM bytes
-    # (from the committed counter record, while it matches this kernel and workload)
-    if "decode" in line and wl.name == WORKLOAD and not args.cold:
-        rec = recorded_traffic("decode_kernel")
+    if "prefill" in halves:
+        seqs, fn, a, ws, f = halves["prefill"]
+        st = timed(torch, stream, f, args.reps, args.warmup)
+        t = st["mean"] / 1e3
+        val = pre_flops / t / 1e12
+        line["prefill"] = {"value": val, "unit": "TFLOP/s", "ms": st["mean"], "ms_pct": st,
+                           "frac_mfma_peak": val / PEAK_MFMA_TFLOPS,
+                           "algorithmic_tflop": pre_flops / 1e12,
+                           "call": "lazyattn_prefill over the prefill requests alone"}
+        roofs.append((t, {"kernel": "mixed_kernel (prefill items)", "bound": "mfma",
+                          "achieved": val, "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
+                          "traffic_key": "prefill"}))
+    if "decode" in halves:
+        seqs, fn, a, ws, f = halves["decode"]
+        st = timed(torch, stream, f, args.reps, args.warmup)
+        stc = timed(torch, stream, f, args.reps, 3, flush)
+        t = st["mean"] / 1e3
+        ubytes = unique_decode_bytes(wl, seqs)
+        val = dbytes / t / 1e9
+        line["decode"] = {"value": val, "unit": "GB/s", "ms": st["mean"], "ms_pct": st,
+                          "frac_hbm_peak": val / PEAK_HBM_GBS,
+                          "algorithmic_gb": dbytes / 1e9,
+                          "unique_gb": ubytes / 1e9, "unique_gbs": ubytes / t / 1e9,
+                          "cold_ms_pct": stc,
+                          "cold_gbs": dbytes / (stc["median"] / 1e3) / 1e9,
+                          "call": "lazyattn_decode over the decode requests alone"}
+        roofs.append((t, {"kernel": "decode_kernel", "bound": "hbm", "achieved": val,
+                          "peak": PEAK_HBM_GBS, "unit": "GB/s", "traffic_key": "decode"}))
+    if pre_seqs and dec_seqs:
+        halves_ms = line["prefill"]["ms"] + line["decode"]["ms"]
+        roof_us = max(pre_flops / (PEAK_MFMA_TFLOPS * 1e12), dbytes / (PEAK_HBM_GBS * 1e9)) * 1e6
+        line["mixed_step"] = {"ms": step_ms, "sum_of_halves_ms": halves_ms,
+                              "speedup_vs_halves": halves_ms / step_ms,
+                              "overlapped_roofline_us": roof_us,
+                              "frac_overlapped_roofline": roof_us / 1e3 / step_ms,
+                              "serial_roofline_us": (pre_flops / (PEAK_MFMA_TFLOPS * 1e12)
+                                                     + dbytes / (PEAK_HBM_GBS * 1e9)) * 1e6}
+    if roofs:
+        t_dom, roof = max(roofs, key=lambda r: r[0])
+        roof["frac"] = roof["achieved"] / roof["peak"]
+        key = roof.pop("traffic_key")
+        rec = recorded_traffic(key) if wl.name == WORKLOAD and not args.no_reuse else None
+        roof["traffic"] = rec
+        roof["launch_ms"] = t_dom * 1e3
+        line["roofline"] = roof
+    if "decode" in line and wl.name == WORKLOAD and not args.no_reuse:
+        rec = recorded_traffic("decode")
         line["decode"]["hbm_counter_gbs"] = (rec / (line["decode"]["ms"] / 1e3) / 1e9
                                              if rec else None)
-    # rotation ablation: the same calls with the key rotation compiled out (the materialised
-    # baseline's kernels), timed on the same inputs -- only the time is used, the values
-    # differ because this pool is not pre-rotated
+
+    # ---- rotation ablation: the same calls with the key rotation compiled out (the
+    # materialised baseline's kernels), timed on the same inputs -- only the time is used ----
     if not args.no_ablation:
-        abl = {}
-        for kind, seqs, fn, a, ws in halves:
-            for _ in range(args.warmup):
-                call(baseline[kind], a, ws)
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
-            for k in range(args.steps):
-                e[2 * k].record(stream)
-                call(baseline[kind], a, ws)
-                e[2 * k + 1].record(stream)
-            torch.cuda.synchronize()
-            t_base = float(np.median([e[2 * k].elapsed_time(e[2 * k + 1])
-                                      for k in range(args.steps)]))
+        baseline = {"prefill": L.prefill_rotated_pool, "decode": L.decode_rotated_pool}
+        abl, var_a, var_d = {}, {}, {}
+        slopes = torch.tensor([2.0 ** (-8.0 * i / wl.Hq) for i in range(1, wl.Hq + 1)],
+                              dtype=torch.float32, device=dev)
+        st_all = wl.doc_stored_offsets()
+        for kind, (seqs, fn, a, ws, f) in halves.items():
             t_lazy = line[kind]["ms_pct"]["median"]
-            # the copy the method avoids: every entry's block rotated to its position
+            t_base = timed(torch, stream, attention_call(L, baseline[kind], wl, a, ws, stream),
+                           args.reps, args.warmup)["median"]
             n_ent = int(a["block_table"][-1].item())
             dk = torch.empty((n_ent, wl.Hkv, wl.B, wl.D), dtype=torch.bfloat16, device=dev)
             dv = torch.empty_like(dk)
@@ -477,68 +563,33 @@ def main():
                 L.materialize_rotated(pool["k_pool"], pool["v_pool"], a["block_table"],
                                       a["block_meta"], a["kv_lens"], wl.rope_base, n_ent,
                                       dk, dv, dm, stream=stream)
-            for _ in range(args.warmup):
-                mat()
-            for k in range(args.steps):
-                e[2 * k].record(stream)
-                mat()
-                e[2 * k + 1].record(stream)
-            torch.cuda.synchronize()
-            t_mat = float(np.median([e[2 * k].elapsed_time(e[2 * k + 1])
-                                     for k in range(args.steps)]))
+            t_mat = timed(torch, stream, mat, args.reps, args.warmup)["median"]
             del dk, dv, dm
             abl[kind] = {"baseline_ms": t_base, "lazy_ms": t_lazy,
                          "rotation_overhead": t_lazy / t_base - 1.0,
                          "materialize_ms": t_mat,
                          "materialize_then_attend_ms": t_mat + t_base,
                          "lazy_speedup_vs_materialize": (t_mat + t_base) / t_lazy}
-        line["rotation_ablation"] = abl
-        # the ALiBi variant on the same pool and rows (Press et al.'s slopes)
-        slopes = torch.tensor([2.0 ** (-8.0 * i / wl.Hq) for i in range(1, wl.Hq + 1)],
-                              dtype=torch.float32, device=dev)
-        var = {}
-        for kind, seqs, fn, a, ws in halves:
-            def run_alibi():
+
+            def alibi():
                 fn(a["q"], a["k_pool"], a["v_pool"], a["block_table"], a["block_meta"],
                    a["kv_lens"], a["q_indptr"], a["q_pos"], wl.rope_base, a["max_entries"],
                    out=a["out"], workspace=ws, stream=stream, slopes=slopes)
-            for _ in range(args.warmup):
-                run_alibi()
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
-            for k in range(args.steps):
-                e[2 * k].record(stream)
-                run_alibi()
-                e[2 * k + 1].record(stream)
-            torch.cuda.synchronize()
-            var[kind] = {"ms": float(np.median([e[2 * k].elapsed_time(e[2 * k + 1])
-                                                for k in range(args.steps)])),
-                         "rope_ms": line[kind]["ms_pct"]["median"]}
-        line["alibi"] = var
-        # the document-rotated pool variant: keys stored with RoPE at their positions inside
-        # their document, so decode needs no per-key rotation. Timed on the same pool and rows
-        # (only the time is used: this pool's keys are not stored rotated, the work is the
-        # same)
-        st_all = wl.doc_stored_offsets()
-        var = {}
-        for kind, seqs, fn, a, ws in halves:
-            st = torch.from_numpy(np.concatenate([st_all[s] for s in seqs]).astype(np.int32)).to(dev)
+            var_a[kind] = {"ms": timed(torch, stream, alibi, args.reps, args.warmup)["median"],
+                           "rope_ms": t_lazy}
+            stv = torch.from_numpy(np.concatenate([st_all[x] for x in seqs]).astype(np.int32)).to(dev)
 
-            def run_doc():
+            def doc():
                 fn(a["q"], a["k_pool"], a["v_pool"], a["block_table"], a["block_meta"],
                    a["kv_lens"], a["q_indptr"], a["q_pos"], wl.rope_base, a["max_entries"],
-                   out=a["out"], workspace=ws, stream=stream, stored_offsets=st)
-            for _ in range(args.warmup):
-                run_doc()
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
-            for k in range(args.steps):
-                e[2 * k].record(stream)
-                run_doc()
-                e[2 * k + 1].record(stream)
-            torch.cuda.synchronize()
-            var[kind] = {"ms": float(np.median([e[2 * k].elapsed_time(e[2 * k + 1])
-                                                for k in range(args.steps)])),
-                         "rope_ms": line[kind]["ms_pct"]["median"]}
-        line["doc_rotated_pool"] = var
+                   out=a["out"], workspace=ws, stream=stream, stored_offsets=stv)
+            var_d[kind] = {"ms": timed(torch, stream, doc, args.reps, args.warmup)["median"],
+                           "rope_ms": t_lazy}
+        line["rotation_ablation"] = abl
+        line["alibi"] = var_a
+        # the document-rotated pool variant (only the time is used: the pool's keys are not
+        # stored rotated here, the work is the same)
+        line["doc_rotated_pool"] = var_d
     # ingest of new tokens' K/V into pool slots (separate scratch pool; not part of a step)
     line["ingest"] = measure_ingest(torch, L, wl, stream, args.steps)
     # the same kernels' rates against what the chip sustains on plain probes
@@ -551,6 +602,24 @@ def main():
     line["ingest"]["frac_measured_copy"] = line["ingest"]["gbs"] / ceil["hbm_copy_gbs"]
     if not args.no_cpu_baseline and wl.name == WORKLOAD and pre_seqs and dec_seqs:
         line["cpu_baseline"] = cpu_baseline(wl, pre_seqs, dec_seqs)
+    # the C5 decode half without reuse, and the decode configurations' controls
+    if not args.no_controls and wl.name == WORKLOAD and not args.no_reuse:
+        del pool, a_all, ws_all, halves
+        torch.cuda.empty_cache()
+        wn = make(WORKLOAD, no_reuse=True)
+        pn = wn.to_device(dev)
+        dn = [x for x in range(wn.num_seqs) if wn.q_indptr[x + 1] - wn.q_indptr[x] == 1]
+        an = half_inputs(wn, dn, dev, pn)
+        wsn = workspace_for(torch, L, "decode", wn, an, dev)
+        stn = timed(torch, stream, attention_call(L, L.decode, wn, an, wsn, stream), args.reps,
+                    args.warmup)
+        line["decode"]["no_reuse_ms_pct"] = stn
+        line["decode"]["no_reuse_gbs"] = decode_bytes(wn, dn) / (stn["median"] / 1e3) / 1e9
+        del pn, an, wsn
+        torch.cuda.empty_cache()
+        line["decode_controls"] = {
+            name: decode_control(torch, L, name, dev, stream, args.reps, args.warmup, flush)
+            for name in ("decode-32q8kv-b64-ctx4161", "decode-32q8kv-b8-ctx32769")}
     print(json.dumps(line), flush=True)
 
 

@@ -29,36 +29,27 @@ bool shape_ok(int32_t Hq, int32_t Hkv, int32_t D, int32_t B) {
 int work_group(int Hq, int Hkv) { const int G = Hq / Hkv; return G > 16 ? 16 : G; }
 int work_heads(int Hq, int Hkv) { return Hq / work_group(Hq, Hkv); }
 
-// Decode split size (blocks per item, even, at least 8). The (row-split, kv-head) items are
-// dealt round-robin to the W resident decode waves, so the choice aims at an item count that
-// is a whole multiple of W -- every wave gets the same number of equal items -- assuming each
-// row holds about max_entries blocks. Among 1 .. 8 items per wave the candidate with the
-// least idle share wins; ties go to fewer, longer items (fewer partials to merge).
+// Decode split (host): decode_bps for rows_bound rows of about max_entries blocks.
 struct DecodeSplit {
   int bps, smax;
 };
 DecodeSplit decode_split(int rows_bound, int Hkv, int max_entries) {
-  const long long W = decode_resident_waves();
   const long long T = max_entries > 0 ? max_entries : 1;
-  const long long pairs = (long long)(rows_bound > 0 ? rows_bound : 1) * Hkv;
-  long long best_b = 0;
-  double best_eff = -1.0;
-  for (long long k = 1; k <= 8; ++k) {
-    long long s = k * W / pairs;                     // splits per row
-    if (s < 1) s = 1;
-    long long b = (T + s - 1) / s;
-    if (b < 8) b = 8;
-    b += b & 1;
-    const long long items = pairs * ((T + b - 1) / b);
-    const double eff = (double)items / (double)(((items + W - 1) / W) * W);
-    if (eff > best_eff + 1e-9) {
-      best_eff = eff;
-      best_b = b;
-    }
-  }
   DecodeSplit d;
-  d.bps = (int)best_b;
-  d.smax = (int)((T + best_b - 1) / best_b);
+  d.bps = decode_bps((long long)(rows_bound > 0 ? rows_bound : 1) * Hkv, T,
+                     decode_resident_waves());
+  d.smax = (int)((T + d.bps - 1) / d.bps);
+  return d;
+}
+
+// Mixed calls: plan_kernel chooses the decode split from the batch's real decode rows (the
+// host sees only num_seqs and the max_entries bound of every sequence); the host bounds
+// the splits per row so that the partial buffer holds any such choice.
+constexpr int kMixedDecodeMaxSplits = 16;
+DecodeSplit mixed_decode_split(int num_seqs, int Hkv, int max_entries) {
+  DecodeSplit d = decode_split(num_seqs, Hkv, max_entries);
+  const int T = max_entries > 0 ? max_entries : 1;
+  d.smax = std::max(d.smax, std::min(kMixedDecodeMaxSplits, (T + 7) / 8));
   return d;
 }
 
@@ -69,13 +60,13 @@ DecodeSplit decode_split(int rows_bound, int Hkv, int max_entries) {
 // device reads), so it sizes the split from total_q and the max_entries hint; plan_kernel
 // applies the same rule (pf_split) to each sequence's real length.
 constexpr int kPfItemsPerCu = 1;    // target prefill items per compute unit (one round)
-constexpr int kPfMinChunk = 8;      // key tiles (of 64 keys) per split, at least
 constexpr int kPfMaxSplits = kMaxPfSplits;
+constexpr int kDecChunkWaves = 1;   // decode items per wave in one mixed-kernel claim
 
 struct CallPlan {
   DecodeSplit ds;
   int rows_bound;
-  int pf_kc, pf_smax, pf_item_cap;  // prefill KV split (mixed calls)
+  int pf_smax, pf_item_cap;         // prefill KV split bound (mixed calls)
   long long n_counters, pf_slots;
   WsLayout L;
 };
@@ -85,25 +76,24 @@ CallPlan plan_call(int mode, int num_seqs, int total_q, int max_entries, int Hq,
   CallPlan c;
   c.ds = ds;
   c.rows_bound = mode == kPlanDecodeOnly ? total_q : num_seqs;
-  c.pf_kc = INT32_MAX / 2;
   c.pf_smax = 1;
   c.pf_item_cap = 0;
   c.n_counters = 0;
   c.pf_slots = 0;
   if (mode == kPlanMixed) {
+    // bound of the splits plan_kernel may choose: enough items for one round when the
+    // tiles are too few (estimated from total_q)
     const int G = work_group(Hq, Hkv), Hw = work_heads(Hq, Hkv);
     const long long pos = prefill_positions_per_tile(G);
     const long long tiles_est = ((long long)total_q + pos - 1) / pos;
     const long long tiles_bound = tiles_est + num_seqs;
-    const long long max_kt = std::max(1, (max_entries + 3) / 4);
     const long long target = (long long)kPfItemsPerCu * (decode_resident_waves() / 8);
-    if (tiles_est * Hw < target && max_kt > kPfMinChunk) {
-      const long long want = (target + tiles_est * Hw - 1) / std::max(1ll, tiles_est * Hw);
-      c.pf_smax = (int)std::min<long long>(kPfMaxSplits, std::max(2ll, want));
-      c.pf_kc = (int)std::max<long long>(kPfMinChunk, (max_kt + c.pf_smax - 1) / c.pf_smax);
-    }
+    long long smax = 1;
+    if (tiles_est * Hw < target)
+      smax = std::max(smax, (target + tiles_est * Hw - 1) / std::max(1ll, tiles_est * Hw));
+    c.pf_smax = (int)std::min<long long>(kPfMaxSplits, smax);
     c.pf_item_cap = (int)std::min<long long>(tiles_bound * c.pf_smax, INT32_MAX / 4);
-    if (c.pf_smax > 1) {
+    if (c.pf_smax > 1) {                  // tile counters and partials of split tiles
       c.n_counters = (long long)Hw * c.pf_item_cap;
       c.pf_slots = (long long)Hw * c.pf_item_cap;
     }
@@ -114,8 +104,9 @@ CallPlan plan_call(int mode, int num_seqs, int total_q, int max_entries, int Hq,
 
 size_t workspace_for(int mode, int num_seqs, int total_q, int max_entries, int Hq, int Hkv,
                      int D) {
-  const int rows_bound = mode == kPlanDecodeOnly ? total_q : num_seqs;
-  const DecodeSplit ds = decode_split(rows_bound, work_heads(Hq, Hkv), max_entries);
+  const DecodeSplit ds = mode == kPlanDecodeOnly
+                            ? decode_split(total_q, work_heads(Hq, Hkv), max_entries)
+                            : mixed_decode_split(num_seqs, work_heads(Hq, Hkv), max_entries);
   return plan_call(mode, num_seqs, total_q, max_entries, Hq, Hkv, D, ds).L.total;
 }
 
@@ -177,7 +168,8 @@ int run(const void* q, const void* k_pool, const void* v_pool, const int32_t* bl
   const DecodeSplit ds =
       fit_workspace
           ? decode_split_capped(num_seqs, rows_bound, Hq, Hkv, D, max_entries, workspace_bytes)
-          : decode_split(rows_bound, work_heads(Hq, Hkv), max_entries);
+      : mode == kPlanDecodeOnly ? decode_split(rows_bound, work_heads(Hq, Hkv), max_entries)
+                                : mixed_decode_split(num_seqs, work_heads(Hq, Hkv), max_entries);
   if (ds.smax <= 0) return LAZYATTN_ERR_WORKSPACE;
   const CallPlan cp = plan_call(mode, num_seqs, total_q, max_entries, Hq, Hkv, D, ds);
   if (workspace_bytes < cp.L.total) return LAZYATTN_ERR_WORKSPACE;
@@ -208,29 +200,37 @@ int run(const void* q, const void* k_pool, const void* v_pool, const int32_t* bl
 
   if (mode == kPlanMixed && (long long)cp.pf_item_cap * Hw > INT32_MAX / 2)
     return LAZYATTN_ERR_SHAPE;
+  const int ncu = decode_resident_waves() / 8;
+  int* pf_kc = (int*)(ws + L.off_zero - 64);                 // the reserved words at 512, 516
+  int* dec_bps = pf_kc + 1;
   PlanParams pp{q_indptr, block_table, freqs, pf_prefix, dec_prefix, zero, num_seqs,
                 prefill_positions_per_tile(G), ds.bps, ds.smax, mode, D / 2,
-                cp.pf_kc, cp.pf_smax, counters, (int)cp.n_counters, fr};
+                cp.pf_smax, kPfItemsPerCu * ncu, Hw, decode_resident_waves(),
+                pf_kc, dec_bps, counters, (int)cp.n_counters, fr};
   if (launch_plan(pp, st) != hipSuccess) return LAZYATTN_ERR_LAUNCH;
 
-  if (mode == kPlanMixed) {
-    PrefillParams P{(const uint16_t*)q, (const uint16_t*)k_pool, (const uint16_t*)v_pool,
-                    block_table, block_meta, kv_lens, q_indptr, q_positions,
-                    (uint16_t*)out, pf_prefix, (const uint16_t*)zero, num_seqs, Hq, Hw,
-                    num_blocks, cp.pf_item_cap, scale_log2, freqs, slopes, Hkv, kv_group,
-                    r / 16, stored_offsets, total_q, cp.pf_kc, cp.pf_smax, pf_partials,
-                    counters};
-    if (launch_prefill(P, D, G, pe, st) != hipSuccess) return LAZYATTN_ERR_LAUNCH;
-  }
   DecodeParams Dp{(const uint16_t*)q, (const uint16_t*)k_pool, (const uint16_t*)v_pool,
                   block_table, block_meta, kv_lens, q_indptr, q_positions, dec_prefix,
                   (const uint16_t*)zero, partials, num_seqs, Hq, Hw, num_blocks,
                   ds.bps, ds.smax, scale_log2, freqs, slopes, Hkv, kv_group, r / 16,
                   stored_offsets, total_q,
                   (int)std::min<long long>((long long)rows_bound * ds.smax, INT32_MAX)};
-  if (launch_decode(Dp, D, G, pe, st) != hipSuccess) return LAZYATTN_ERR_LAUNCH;
+  if (mode == kPlanMixed) {
+    // prefill tiles and decode chunks of any mix of query lengths: one persistent launch
+    PrefillParams P{(const uint16_t*)q, (const uint16_t*)k_pool, (const uint16_t*)v_pool,
+                    block_table, block_meta, kv_lens, q_indptr, q_positions,
+                    (uint16_t*)out, pf_prefix, (const uint16_t*)zero, num_seqs, Hq, Hw,
+                    num_blocks, cp.pf_item_cap, scale_log2, freqs, slopes, Hkv, kv_group,
+                    r / 16, stored_offsets, total_q, pf_kc, cp.pf_smax, pf_partials,
+                    counters};
+    MixedParams Mp{P, dec_prefix, partials, dec_bps, ds.smax, Dp.rowsplit_cap,
+                   8 * kDecChunkWaves};
+    if (launch_mixed(Mp, D, G, pe, st) != hipSuccess) return LAZYATTN_ERR_LAUNCH;
+  } else {
+    if (launch_decode(Dp, D, G, pe, st) != hipSuccess) return LAZYATTN_ERR_LAUNCH;
+  }
   MergeParams Mp{q_indptr, block_table, dec_prefix, partials, (uint16_t*)out,
-                 num_seqs, Hq, ds.bps, ds.smax, mode, total_q};
+                 num_seqs, Hq, dec_bps, ds.smax, mode, total_q};
   if (launch_merge(Mp, total_q, D, st) != hipSuccess) return LAZYATTN_ERR_LAUNCH;
   return LAZYATTN_OK;
 }

@@ -206,7 +206,8 @@ __device__ __forceinline__ SeqFound wave_upper_seq(const int32_t* prefix, int n,
 
 // ---- workspace layout -----------------------------------------------------------------------
 // [0, 512)                RoPE frequency table, double [64] (revolutions per position)
-// [512, 768)              reserved; 16-byte zero rows at 576..767
+// [512, 516)              prefill KV split: key tiles per split (int, written by plan_kernel)
+// [516, 768)              reserved; 16-byte zero rows at 576..767
 // [768, ...)              prefix arrays: prefill items, decode row-splits, each num_seqs + 1 int32
 // aligned 256             counters: int32 [n_counters] (zeroed by the plan kernel)
 // aligned 256             split-K partials: float [row-splits][Hq][D + 4]  (o[D], m, l, -, -)
@@ -236,6 +237,7 @@ __host__ __device__ inline WsLayout ws_layout(int num_seqs, long long max_rowspl
 // KV split of one prefill query tile over n_kt key tiles: at most smax splits of at least kc
 // key tiles (the last may be shorter), none empty. n_kt = 0 gives one empty split.
 constexpr int kMaxPfSplits = 32;   // splits per prefill tile, at most
+constexpr int kPfMinChunk = 8;     // key tiles (of 64 keys) per prefill split, at least
 
 struct PfSplit {
   int splits, chunk;
@@ -246,6 +248,32 @@ __host__ __device__ inline PfSplit pf_split(int n_kt, int kc, int smax) {
   s = s < 1 ? 1 : (s > smax ? smax : s);
   const int chunk = (n_kt + s - 1) / s;
   return PfSplit{(n_kt + chunk - 1) / chunk, chunk};
+}
+
+// Decode split size (blocks per item, even, at least 8) for `pairs` (row, KV head) pairs of
+// rows holding about T blocks on W resident waves: items are dealt round-robin to the waves,
+// so the choice aims at an item count that is a whole multiple of W -- every wave gets the
+// same number of equal items. Among 1 .. 8 items per wave the candidate with the least idle
+// share wins; ties go to fewer, longer items (fewer partials to merge).
+__host__ __device__ inline int decode_bps(long long pairs, long long T, long long W) {
+  if (T < 1) T = 1;
+  if (pairs < 1) pairs = 1;
+  long long best_b = 8;
+  double best_eff = -1.0;
+  for (long long k = 1; k <= 8; ++k) {
+    long long s = k * W / pairs;                     // splits per row
+    if (s < 1) s = 1;
+    long long b = (T + s - 1) / s;
+    if (b < 8) b = 8;
+    b += b & 1;
+    const long long items = pairs * ((T + b - 1) / b);
+    const double eff = (double)items / (double)(((items + W - 1) / W) * W);
+    if (eff > best_eff + 1e-9) {
+      best_eff = eff;
+      best_b = b;
+    }
+  }
+  return (int)best_b;
 }
 
 // Split-K of a decode row with T block-table entries: the host picks a base split size

@@ -17,7 +17,12 @@ struct PlanParams {
   int bps, smax;             // decode split size (blocks) and splits-per-row cap
   int mode;                  // PlanMode
   int half_dim;
-  int pf_kc, pf_smax;        // prefill KV split: key tiles per split, splits-per-tile cap
+  int pf_smax;               // prefill KV split: splits-per-tile cap (workspace bound)
+  int num_cus;               // prefill items fill one round of the GPU at least
+  int work_heads;            // KV (work) heads
+  int dec_waves;             // resident decode waves (decode split of mixed calls)
+  int* pf_kc;                // out: key tiles per split (device-chosen, read by prefill)
+  int* dec_bps;              // out: decode split size (mixed calls: device-chosen; else bps)
   int* counters;             // [n_counters] zeroed here (prefill tile counters)
   int n_counters;
   RopeFreqs fr;              // host-computed table (kernel argument)
@@ -44,7 +49,8 @@ struct PrefillParams {
   int rot_chunks;            // rotary_dim / 16 (kRopePartial only; nat_chunk)
   const int32_t* stored;     // [entries] stored rotation offset of slot 0 (kDocRotated only)
   int total_q;               // rows of q and out: rows at or past it are never touched
-  int pf_kc, pf_smax;        // KV split: key tiles per split, splits-per-tile cap (pf_split)
+  const int* pf_kc;          // KV split: key tiles per split (written by plan_kernel)
+  int pf_smax;               // KV split: splits-per-tile cap (pf_split)
   float* pf_partials;        // [Hkv * pf_item_cap][tile rows][D + 4]: split partials (o, m, l)
   int* pf_counters;          // [Hkv * pf_item_cap]: finished splits of each tile (zeroed by plan)
 };
@@ -82,16 +88,30 @@ struct MergeParams {
   const int32_t* dec_prefix;
   const float* partials;
   uint16_t* out;
-  int num_seqs, Hq, bps, smax, mode;
+  int num_seqs, Hq;
+  const int* bps;            // decode split size (written by plan_kernel)
+  int smax, mode;
   int total_q;               // rows of out
 };
+
+// One launch for a batch of any query lengths: prefill items (query tiles, KV split) and
+// decode chunks (dec_chunk consecutive decode items, one wave per item) on one grid, in
+// eight per-XCD queues (prefill items first, then decode chunks).
+struct MixedParams {
+  PrefillParams pf;          // shared fields (pointers, shapes, tables) and the prefill ones
+  const int32_t* dec_prefix; // decode-only fields of DecodeParams
+  float* partials;
+  const int* bps;            // decode split size (written by plan_kernel)
+  int smax, rowsplit_cap;
+  int dec_chunk;             // decode items per workgroup (a multiple of its 8 waves)
+};
+hipError_t launch_mixed(const MixedParams& p, int D, int G, int pe, hipStream_t st);
 
 hipError_t launch_plan(const PlanParams& p, hipStream_t st);
 hipError_t launch_merge(const MergeParams& p, int total_q, int D, hipStream_t st);
 hipError_t launch_debug_decode(const uint32_t* words, const int32_t* bt, int num_seqs, int n,
                                int32_t* ids, int32_t* offs, hipStream_t st);
-// p.tiles_bound: upper bound of prefill tiles (extra workgroups exit at once)
-hipError_t launch_prefill(const PrefillParams& p, int D, int G, int pe, hipStream_t st);
+// query positions per prefill tile (256 (position, head) rows)
 int prefill_positions_per_tile(int G);
 struct MaterializeParams {
   const uint16_t* k_pool;

@@ -5,6 +5,7 @@
 // prefix sums that the attention kernels binary-search to find their sequence.
 #include "lazyattn_common.h"
 #include "lazyattn_kernels.h"
+#include <limits.h>
 
 namespace lazyattn {
 
@@ -13,10 +14,71 @@ namespace lazyattn {
 // chunk).
 __global__ __launch_bounds__(256) void plan_kernel(PlanParams P) {
   __shared__ int wa[4], wb[4];
+  __shared__ int s_tiles, s_maxkt, s_kc, s_dec_rows, s_dec_maxT, s_bps;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   if (tid < 48) P.zero[tid] = 0u;
   if (tid < P.half_dim) P.freqs_out[tid] = P.fr.f[tid];
   for (int i = tid; i < P.n_counters; i += 256) P.counters[i] = 0;
+  if (tid == 0) {
+    s_tiles = 0;
+    s_maxkt = 0;
+    s_dec_rows = 0;
+    s_dec_maxT = 0;
+  }
+  __syncthreads();
+  // pass 1 (mixed calls): prefill query tiles, the longest prefill key range (in 64-key
+  // tiles), and the decode rows with their longest block table. The KV split follows:
+  // enough prefill items for one round of the GPU when the tiles are too few; and the
+  // decode split is sized from the real decode rows.
+  for (int base = 0; P.mode == kPlanMixed && base < P.num_seqs; base += 256) {
+    const int s = base + tid;
+    int tl = 0, kt = 0, dec = 0, dT = 0;
+    if (s < P.num_seqs) {
+      const int qlen = P.q_indptr[s + 1] - P.q_indptr[s];
+      const int T = P.block_table[s + 1] - P.block_table[s];
+      if (qlen == 1) {
+        dec = 1;
+        dT = T;
+      } else if (qlen > 1) {
+        tl = (qlen + P.pos_per_tile - 1) / P.pos_per_tile;
+        kt = (T + 3) / 4;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      tl += __shfl_xor(tl, o);
+      kt = max(kt, __shfl_xor(kt, o));
+      dec += __shfl_xor(dec, o);
+      dT = max(dT, __shfl_xor(dT, o));
+    }
+    if (lane == 0) {
+      atomicAdd(&s_tiles, tl);
+      atomicMax(&s_maxkt, kt);
+      atomicAdd(&s_dec_rows, dec);
+      atomicMax(&s_dec_maxT, dT);
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const long long wp = (long long)s_tiles * P.work_heads;
+    int sp = 1;
+    if (wp > 0 && wp < P.num_cus) sp = (int)((P.num_cus + wp - 1) / wp);
+    sp = min(sp, P.pf_smax);
+    const int kc = sp > 1 ? max(kPfMinChunk, (s_maxkt + sp - 1) / sp) : INT_MAX / 2;
+    s_kc = kc;
+    *P.pf_kc = kc;
+    // decode split: a mixed call sizes it from its real decode rows (the rows of the
+    // single-row sequences and their longest block table), a decode call takes the host's
+    const int bps = P.mode == kPlanMixed
+                        ? decode_bps((long long)s_dec_rows * P.work_heads, s_dec_maxT,
+                                     P.dec_waves)
+                        : P.bps;
+    s_bps = bps;
+    *P.dec_bps = bps;
+  }
+  __syncthreads();
+  const int kc = s_kc;
+  const int bps = s_bps;
   int carry_a = 0, carry_b = 0;                 // identical in every thread
   for (int base = 0; base < P.num_seqs; base += 256) {
     const int s = base + tid;
@@ -25,9 +87,9 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanParams P) {
       const int qlen = P.q_indptr[s + 1] - P.q_indptr[s];
       const int T = P.block_table[s + 1] - P.block_table[s];
       const bool dec = (P.mode == kPlanDecodeOnly) || qlen == 1;
-      if (dec) b = qlen * row_splits(T, P.bps, P.smax);
+      if (dec) b = qlen * row_splits(T, bps, P.smax);
       else a = (qlen + P.pos_per_tile - 1) / P.pos_per_tile *
-               pf_split((T + 3) / 4, P.pf_kc, P.pf_smax).splits;
+               pf_split((T + 3) / 4, kc, P.pf_smax).splits;
     }
     int ia = a, ib = b;                          // inclusive scan within the wave
 #pragma unroll
@@ -78,7 +140,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams P) {
       const int seq = blockIdx.x;
       const int q0 = P.q_indptr[seq], qlen = P.q_indptr[seq + 1] - q0;
       const int T = P.block_table[seq + 1] - P.block_table[seq];
-      s_splits = (qlen == 1) & (q0 < P.total_q) ? row_splits(T, P.bps, P.smax) : 0;
+      s_splits = (qlen == 1) & (q0 < P.total_q) ? row_splits(T, *P.bps, P.smax) : 0;
       s_item0 = P.dec_prefix[seq];
       s_row = q0;
     }
@@ -105,7 +167,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams P) {
       const int q0 = P.q_indptr[seq], qlen = P.q_indptr[seq + 1] - q0;
       const bool dec = (P.mode == kPlanDecodeOnly) || qlen == 1;
       const int T = P.block_table[seq + 1] - P.block_table[seq];
-      const int splits = row_splits(T, P.bps, P.smax);
+      const int splits = row_splits(T, *P.bps, P.smax);
       s_splits = dec ? splits : 0;            // prefill rows are written by the prefill kernel
       s_item0 = (long long)P.dec_prefix[seq] + (long long)(r - q0) * splits;
       s_row = r;

@@ -1,4 +1,5 @@
-// LazyAttention prefill kernel for gfx950 (MFMA, online softmax, pipelined key tiles).
+// LazyAttention prefill work item for gfx950 (MFMA, online softmax, pipelined key tiles),
+// run by mixed_kernel (mixed.hip).
 //
 // Technical summary of LazyAttention (arXiv 2606.04302), "Technical Implementation",
 // prefilling phase: cached KV blocks are loaded from the position-free cache and, instead
@@ -30,6 +31,7 @@
 // rotation); kAlibi (no rotation, linear bias); kRopePartial (kRope over the permuted dim
 // order of nat_chunk); kDocRotated (keys stored with R(stored_b + j): each key tile is
 // rotated by R(off_b - stored_b - p_ref) from the block phase table alone).
+#pragma once
 #include "lazyattn_common.h"
 #include "lazyattn_kernels.h"
 #include <limits.h>
@@ -126,23 +128,43 @@ __device__ __forceinline__ TileWords tile_words(const WinDec& wd) {
   return tw;
 }
 
-// LDS of one prefill work item (a workgroup of kPrefillWaves waves)
+// LDS of one prefill work item (a workgroup of kPrefillWaves waves): references to
+// separately declared __shared__ arrays. Keeping them separate variables lets the compiler
+// tell the direct-to-LDS value copies (into Vs) from the operand reads of Ks and Qs, so
+// operand reads do not wait for the copies in flight.
 template <int D>
-struct PrefillSmem {
+struct PrefillSmemDims {
   static constexpr int NW = kPrefillWaves, NK = 64, HALF = D / 2, KS = D + 8;
   static constexpr int VBYTES = NK * (D * 2 + 32);
-  alignas(16) uint16_t Ks[2][NK * KS];
-  alignas(16) uint8_t Vs[2][VBYTES];
+};
+template <int D>
+struct PrefillSmem {
+  using S = PrefillSmemDims<D>;
+  uint16_t (&Ks)[2][S::NK * S::KS];
+  uint8_t (&Vs)[2][S::VBYTES];
   // rotation tables as fp16 pairs, one 8-byte entry per two frequencies: {(cos, cos),
   // (sin, sin)}, laid out [block or slot][pair][thread] so that the staging threads of a
   // wave read consecutive 8-byte words
-  alignas(16) u32x2 tbl[2][4 * HALF / 2];   // (off_b - p_ref) theta_k
-  alignas(16) u32x2 slot_cs[16 * HALF / 2]; // j theta_k, j < 16
-  alignas(16) uint16_t Qs[NW][32 * KS];     // each wave's rotated queries (fp16)
-  double fr_s[HALF];
-  int pmax_s;
-  int last_s;                               // this split item completes its query tile
+  u32x2 (&tbl)[2][4 * S::HALF / 2];          // (off_b - p_ref) theta_k
+  u32x2 (&slot_cs)[16 * S::HALF / 2];        // j theta_k, j < 16
+  uint16_t (&Qs)[S::NW][32 * S::KS];         // each wave's rotated queries (fp16)
+  double (&fr_s)[S::HALF];
+  int& pmax_s;
+  int& last_s;                               // this split item completes its query tile
 };
+
+// Declares the arrays of a PrefillSmem in the calling kernel and binds `name` to them.
+#define LAZYATTN_PREFILL_SMEM(D, name)                                                       \
+  using name##_S = PrefillSmemDims<D>;                                                       \
+  __shared__ __align__(16) uint16_t name##_Ks[2][name##_S::NK * name##_S::KS];             \
+  __shared__ __align__(16) uint8_t name##_Vs[2][name##_S::VBYTES];                          \
+  __shared__ __align__(16) u32x2 name##_tbl[2][4 * name##_S::HALF / 2];                     \
+  __shared__ __align__(16) u32x2 name##_slot[16 * name##_S::HALF / 2];                      \
+  __shared__ __align__(16) uint16_t name##_Qs[name##_S::NW][32 * name##_S::KS];            \
+  __shared__ double name##_fr[name##_S::HALF];                                             \
+  __shared__ int name##_pmax, name##_last;                                                 \
+  PrefillSmem<D> name{name##_Ks, name##_Vs, name##_tbl, name##_slot, name##_Qs, name##_fr, \
+                      name##_pmax, name##_last}
 
 // One prefill work item: query tile qt of a sequence for KV (work) head kvh, over the key
 // tiles of one KV split. `item` numbers the items of a KV head: each sequence owns
@@ -151,7 +173,7 @@ struct PrefillSmem {
 // (o, m, l) per row, and the split that finishes its tile last merges the tile's partials
 // into the output (a per-tile counter; device-scope fences order the partial stores).
 template <int D, int G, int PE>
-__device__ __forceinline__ void prefill_item(const PrefillParams& P, PrefillSmem<D>& SM,
+__device__ __forceinline__ void prefill_item(const PrefillParams& P, const PrefillSmem<D>& SM,
                                              const int kvh, const int item) {
   constexpr bool PART = PE == kRopePartial;   // dims in the permuted order of nat_chunk
   constexpr bool DOC = PE == kDocRotated;     // keys carry R(stored + j): rotate by off - stored
@@ -198,7 +220,7 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& P, PrefillSmem
   const int T = __builtin_amdgcn_readfirstlane(P.block_table[seq + 1] - e0);
   const int kvlen = __builtin_amdgcn_readfirstlane(P.kv_lens[seq]);
   // this item's query tile and key-tile range (KV split)
-  const PfSplit spl = pf_split((T + 3) / 4, P.pf_kc, P.pf_smax);
+  const PfSplit spl = pf_split((T + 3) / 4, *P.pf_kc, P.pf_smax);
   const int local = item - sf.start;
   const int qt = __builtin_amdgcn_readfirstlane(local / spl.splits);
   const int sp = __builtin_amdgcn_readfirstlane(local - qt * spl.splits);
@@ -763,7 +785,7 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& P, PrefillSmem
   if (!SM.last_s) return;
   __threadfence();                                           // see the other splits' stores
   // two threads per row, D/2 dims each: M = max m, L = sum l 2^(m - M), O = sum o 2^(m - M).
-  // Every split's m is loaded at once; then two splits' (o, l) per round of loads.
+  // The m values are loaded eight at a time, then one split's (o, l) per round of loads.
   {
     const int row = tid >> 1, half = tid & 1;
     const int rq = qt * POS + row / G;                       // query row in the sequence
@@ -774,31 +796,29 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& P, PrefillSmem
                           (size_t)row * RS;
       const int ns = spl.splits;                             // <= kMaxPfSplits
       float M = -INFINITY;
+      for (int s0 = 0; s0 < ns; s0 += 8) {                   // eight m values per round
+        float mv[8];
 #pragma unroll
-      for (int s2 = 0; s2 < kMaxPfSplits; ++s2)
-        if (s2 < ns) M = fmaxf(M, base[s2 * SPLIT + D]);
+        for (int u = 0; u < 8; ++u) mv[u] = s0 + u < ns ? base[(s0 + u) * SPLIT + D] : -INFINITY;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) M = fmaxf(M, mv[u]);
+      }
       const float Mu = M == -INFINITY ? 0.f : M;             // all -inf: weights 0, row 0
       float L = 0.f;
       f32x4 acc[D / 8];
 #pragma unroll
       for (int i = 0; i < D / 8; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int s2 = 0; s2 < ns; s2 += 2) {
-        const bool two = s2 + 1 < ns;
-        const float* p0 = base + s2 * SPLIT;
-        const float* p1 = two ? p0 + SPLIT : p0;
-        f32x4 o0[D / 8], o1[D / 8];
-        const float m0 = p0[D], l0 = p0[D + 1], m1 = p1[D], l1 = p1[D + 1];
+      for (int s2 = 0; s2 < ns; ++s2) {                      // one split per round of loads
+        const float* ps = base + s2 * SPLIT;
+        f32x4 ov[D / 8];
+        const float ms = ps[D], ls = ps[D + 1];
 #pragma unroll
-        for (int i = 0; i < D / 8; ++i) {
-          o0[i] = *(const f32x4*)(p0 + half * (D / 2) + 4 * i);
-          o1[i] = *(const f32x4*)(p1 + half * (D / 2) + 4 * i);
-        }
+        for (int i = 0; i < D / 8; ++i) ov[i] = *(const f32x4*)(ps + half * (D / 2) + 4 * i);
         // a split with no visible key has m = -inf, l = 0, o = 0: weight exp2(-inf) = 0
-        const float w0 = __builtin_amdgcn_exp2f(m0 - Mu);
-        const float w1 = two ? __builtin_amdgcn_exp2f(m1 - Mu) : 0.f;
-        L += l0 * w0 + l1 * w1;
+        const float wgt = __builtin_amdgcn_exp2f(ms - Mu);
+        L += ls * wgt;
 #pragma unroll
-        for (int i = 0; i < D / 8; ++i) acc[i] += o0[i] * w0 + o1[i] * w1;
+        for (int i = 0; i < D / 8; ++i) acc[i] += ov[i] * wgt;
       }
       const float inv = L > 0.f ? 1.f / L : 0.f;
       uint16_t* dst = P.out + ((size_t)(q0 + rq) * P.Hq + rh) * D + half * (D / 2);
@@ -813,58 +833,6 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& P, PrefillSmem
       }
     }
   }
-}
-
-template <int D, int G, int PE>
-__global__ __launch_bounds__(kPrefillWaves * 64, 1) void prefill_kernel(PrefillParams P) {
-  __shared__ PrefillSmem<D> SM;
-  // XCD-aware order: consecutive workgroups land on different XCDs, so hand each XCD a
-  // contiguous range of items (tiles of one sequence and KV head share their key tiles).
-  const int nwg = gridDim.x;                                  // multiple of 8
-  const int Lb = blockIdx.x;
-  const int Lp = (Lb & 7) * (nwg >> 3) + (Lb >> 3);
-  const int kvh = Lp / P.pf_item_cap;
-  const int item = Lp - kvh * P.pf_item_cap;
-  if (kvh >= P.Hkv || item >= P.pf_prefix[P.num_seqs]) return;   // uniform
-  prefill_item<D, G, PE>(P, SM, kvh, item);
-}
-
-int prefill_positions_per_tile(int G) { return 32 * kPrefillWaves / G; }
-
-template <int D, int G>
-static hipError_t launch_dg(const PrefillParams& p, int pe, hipStream_t st) {
-  const long long n = (long long)p.pf_item_cap * p.Hkv;
-  dim3 grid((unsigned)((n + 7) / 8 * 8)), block(kPrefillWaves * 64);
-  switch (pe) {
-    case kRope: hipLaunchKernelGGL((prefill_kernel<D, G, kRope>), grid, block, 0, st, p); break;
-    case kStored: hipLaunchKernelGGL((prefill_kernel<D, G, kStored>), grid, block, 0, st, p); break;
-    case kAlibi: hipLaunchKernelGGL((prefill_kernel<D, G, kAlibi>), grid, block, 0, st, p); break;
-    case kRopePartial:
-      hipLaunchKernelGGL((prefill_kernel<D, G, kRopePartial>), grid, block, 0, st, p);
-      break;
-    case kDocRotated:
-      hipLaunchKernelGGL((prefill_kernel<D, G, kDocRotated>), grid, block, 0, st, p);
-      break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
-}
-
-template <int D>
-static hipError_t launch_d(const PrefillParams& p, int G, int pe, hipStream_t st) {
-  switch (G) {
-    case 1: return launch_dg<D, 1>(p, pe, st);
-    case 2: return launch_dg<D, 2>(p, pe, st);
-    case 4: return launch_dg<D, 4>(p, pe, st);
-    case 8: return launch_dg<D, 8>(p, pe, st);
-    case 16: return launch_dg<D, 16>(p, pe, st);
-  }
-  return hipErrorInvalidValue;
-}
-
-hipError_t launch_prefill(const PrefillParams& p, int D, int G, int pe, hipStream_t st) {
-  if (p.pf_item_cap <= 0) return hipSuccess;
-  return D == 128 ? launch_d<128>(p, G, pe, st) : launch_d<64>(p, G, pe, st);
 }
 
 }  // namespace lazyattn
