@@ -135,7 +135,7 @@ __device__ __forceinline__ TileWords tile_words(const WinDec& wd) {
 template <int D>
 struct PrefillSmemDims {
   static constexpr int NW = kPrefillWaves, NK = 64, HALF = D / 2, KS = D + 8;
-  static constexpr int VBYTES = NK * (D * 2 + 32);
+  static constexpr int VBYTES = NK * D * 2;
 };
 template <int D>
 struct PrefillSmem {
@@ -188,11 +188,13 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& P, const Prefi
   constexpr int NCH = D / 16;                 // 16-dim k-steps of QK^T
   constexpr int KS = D + 8;                   // K~ LDS row stride (16-bit elements)
   constexpr int ROWB = D * 2;                 // V row bytes
-  constexpr int VROW = ROWB + 32;             // padded LDS row: 4 consecutive rows -> disjoint banks
-  constexpr int SPR = VROW / 16;              // 16-byte slots per padded row
-  constexpr int VBYTES = NK * VROW;
+  // value tile in LDS: rows of ROWB bytes; 16-byte chunk c of row R sits at chunk
+  // c ^ 2 (R & 3), so the four rows one transposed read touches hit disjoint banks
+  constexpr int VBYTES = NK * ROWB;
   constexpr int VINST = VBYTES / 1024;        // wave-wide global_load_lds per tile
-  static_assert(VBYTES % 1024 == 0, "value tile = whole wave loads");
+  constexpr int RPI = 1024 / ROWB;            // rows per instruction (4 rows of one block)
+  constexpr int CPR = ROWB / 16;              // 16-byte chunks per row
+  static_assert(VBYTES % 1024 == 0 && 16 % RPI == 0, "value tile = whole wave loads");
   constexpr int FPT = NK * HALF / NT;         // frequencies each thread rotates per key tile
   constexpr int CPT = HALF / FPT;             // threads per key
   static_assert(FPT == 4 || FPT == 8, "staging unit = 4 or 8 frequencies of one key");
@@ -366,27 +368,26 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& P, const Prefi
     const int o = rl(DOC ? wd.sh : wd.off, 4 * d + tab_b);
     ((_Float16*)tbl[buf])[tab_pos] = (_Float16)rope_sin_rev(o - p_ref, tab_f, tab_quarter);
   };
-  // values of tile kt + d straight into LDS, wave-wide instruction i of this wave: slot
-  // (row R, chunk c) of the padded tile; pad slots and invalid rows read the zeroed chunk
-  auto issue_v = [&](const WinDec& wd, int d, int buf, int i) __attribute__((always_inline)) {
-    const int I = w + NW * i;
-    const int slot = I * 64 + lane;
-    const int R = slot / SPR, c = slot % SPR;
-    const int b = R >> 4, j = R & 15;
-    const int n0 = rl(wd.nv, 4 * d), n1 = rl(wd.nv, 4 * d + 1);
-    const int n2 = rl(wd.nv, 4 * d + 2), n3 = rl(wd.nv, 4 * d + 3);
-    const int i0 = rl(wd.id, 4 * d), i1 = rl(wd.id, 4 * d + 1);
-    const int i2 = rl(wd.id, 4 * d + 2), i3 = rl(wd.id, 4 * d + 3);
-    const int nv = b == 0 ? n0 : b == 1 ? n1 : b == 2 ? n2 : n3;
-    const int id = b == 0 ? i0 : b == 1 ? i1 : b == 2 ? i2 : i3;
-    const void* src = blend_ptr((c < D / 8) & (j < nv),
-                                P.v_pool + (((size_t)id * P.Hkv_pool + kvp) * kBlock + j) * D + 8 * c,
-                                P.zero);
-    g2lds16p(src, Vs[buf] + I * 1024);
-  };
+  // values of tile kt + d straight into LDS, wave-wide instruction i of this wave: rows
+  // R0 .. R0 + RPI - 1 of one block (block id and valid count are wave-uniform); lane l
+  // fetches the chunk that belongs at its LDS slot (swizzle above); rows past the block's
+  // valid keys read the zeroed chunk
   constexpr int VPW = VINST / NW;                           // value loads every wave issues
-  constexpr int VREM = VINST % NW;                          // + one more on waves < VREM
-  static_assert(VPW >= 1 && VPW <= 3, "value loads are placed in the first score k-steps");
+  static_assert(VPW >= 1 && VPW <= 3 && VINST % NW == 0,
+                "value loads are placed in the first score k-steps");
+  const int v_r = lane / CPR;                               // row within an instruction
+  const int v_lc = (lane % CPR) ^ (2 * (v_r & 3));          // logical chunk this lane fetches
+  auto issue_v = [&](const WinDec& wd, int d, int buf, int i) __attribute__((always_inline)) {
+    const int R0 = (w * VPW + i) * RPI;                     // uniform
+    const int b = R0 >> 4;
+    const int nv = rl(wd.nv, 4 * d + b), id = rl(wd.id, 4 * d + b);
+    const int j = (R0 & 15) + v_r;
+    const void* src = blend_ptr(j < nv,
+                                P.v_pool + (((size_t)id * P.Hkv_pool + kvp) * kBlock + j) * D +
+                                    8 * v_lc,
+                                P.zero);
+    g2lds16p(src, Vs[buf] + R0 * ROWB);
+  };
 
   KRaw klo{}, khi{};
   // raw keys of a tile into (klo, khi); empty slots read as zero
@@ -433,7 +434,6 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& P, const Prefi
     make_table(wd, 1, 1);
 #pragma unroll
     for (int i = 0; i < VPW; ++i) issue_v(wd, 0, 0, i);
-    if (w < VREM) issue_v(wd, 0, 0, VPW);
     __syncthreads();                                         // tables 0, 1 visible
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {                         // keys of tiles 0 and 1
@@ -496,8 +496,12 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& P, const Prefi
   float mxc = xor32_max(max32(S0[0], S0[1]));
 
   const int gi = lane >> 4, i16 = lane & 15;
-  const uint8_t* vlane = (const uint8_t*)Vs + (4 * hh + (i16 >> 2)) * VROW +
-                         16 * (2 * (gi & 1) + ((i16 & 3) >> 1)) + 8 * (i16 & 1);
+  // transposed value reads: this lane's row is 4 hh + i16 / 4 (+ 32 t + 16 kk, + 8), so its
+  // swizzle 2 (R & 3) = 2 (i16 / 4) is fixed; the chunk of dim step dt is
+  // (4 dt + 2 (gi & 1) + (i16 & 3) / 2) ^ 2 (i16 / 4)
+  const int v_sw = 2 * (i16 >> 2);
+  const uint8_t* vlane = (const uint8_t*)Vs + (4 * hh + (i16 >> 2)) * ROWB + 8 * (i16 & 1);
+  auto vchunk = [&](int dt) { return 16 * ((4 * dt + 2 * (gi & 1) + ((i16 & 3) >> 1)) ^ v_sw); };
   const uint16_t* klane = Ks[0] + col * KS + 8 * hh;        // + buf * NK * KS
   const uint16_t* qlane = qs + col * KS + 8 * hh;
 
@@ -512,7 +516,6 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& P, const Prefi
     WinDec wdn;
     bool maskn = false;
     float h0 = 0.f, h1 = 0.f;
-    if (w < VREM) issue_v(wd, 1, nxt, VPW);                   // the odd value loads
     float mx = mxc;
     // ---- rare paths: causal / ragged mask of S(kt) ------------------------------------
     if (maskc) {
@@ -628,9 +631,9 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& P, const Prefi
         const int t = g >> 1, kk = g & 1;
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
-          const uint8_t* a1 = vb + (32 * t + 16 * kk) * VROW + 64 * dt;
+          const uint8_t* a1 = vb + (32 * t + 16 * kk) * ROWB + vchunk(dt);
           const u32x2 r1 = lds_read_tr((const uint16_t*)a1);
-          const u32x2 r2 = lds_read_tr((const uint16_t*)(a1 + 8 * VROW));
+          const u32x2 r2 = lds_read_tr((const uint16_t*)(a1 + 8 * ROWB));
           va[dt] = u32x4{r1[0], r1[1], r2[0], r2[1]};
         }
       };
