@@ -23,7 +23,7 @@
 // G query heads of one KV head share every staged key/value tile (grouped-query packing).
 // Per wave, S^T = K~ Q~^T (fp16 operands) and O^T += V^T P^T (bf16) on 32x32x16 MFMA: each
 // lane owns one query row (MFMA column), so row max / row sum are in-lane plus one
-// cross-half exchange. Values go straight from global memory into a padded LDS tile
+// cross-half exchange. Values go straight from global memory into a swizzled LDS tile
 // (global_load_lds) and are transposed on read (ds_read_b64_tr_b16). The next key tile's
 // loads are in flight while the current one is multiplied; one barrier per key tile.
 //
