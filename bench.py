@@ -74,8 +74,12 @@ def kernel_source_hash(kernel):
              "decode": ["decode.hip", "decode_body.h"]}[kernel]
     h = hashlib.sha256()
     for f in files + ["lazyattn_common.h", "lazyattn_kernels.h"]:
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            # code only: comment-only lines and trailing // comments do not change a kernel
+            for line in fh:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 
