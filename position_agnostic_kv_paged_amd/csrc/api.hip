@@ -67,7 +67,7 @@ struct CallPlan {
   DecodeSplit ds;
   int rows_bound;
   int pf_smax, pf_item_cap;         // prefill KV split bound (mixed calls)
-  long long n_counters, pf_slots;
+  long long pf_slots;
   WsLayout L;
 };
 
@@ -78,7 +78,6 @@ CallPlan plan_call(int mode, int num_seqs, int total_q, int max_entries, int Hq,
   c.rows_bound = mode == kPlanDecodeOnly ? total_q : num_seqs;
   c.pf_smax = 1;
   c.pf_item_cap = 0;
-  c.n_counters = 0;
   c.pf_slots = 0;
   if (mode == kPlanMixed) {
     // bound of the splits plan_kernel may choose: enough items for one round when the
@@ -93,12 +92,9 @@ CallPlan plan_call(int mode, int num_seqs, int total_q, int max_entries, int Hq,
       smax = std::max(smax, (target + tiles_est * Hw - 1) / std::max(1ll, tiles_est * Hw));
     c.pf_smax = (int)std::min<long long>(kPfMaxSplits, smax);
     c.pf_item_cap = (int)std::min<long long>(tiles_bound * c.pf_smax, INT32_MAX / 4);
-    if (c.pf_smax > 1) {                  // tile counters and partials of split tiles
-      c.n_counters = (long long)Hw * c.pf_item_cap;
-      c.pf_slots = (long long)Hw * c.pf_item_cap;
-    }
+    if (c.pf_smax > 1) c.pf_slots = (long long)Hw * c.pf_item_cap;   // split partials
   }
-  c.L = ws_layout(num_seqs, (long long)c.rows_bound * ds.smax, Hq, D, c.n_counters, c.pf_slots);
+  c.L = ws_layout(num_seqs, (long long)c.rows_bound * ds.smax, Hq, D, c.pf_slots);
   return c;
 }
 
@@ -184,7 +180,6 @@ int run(const void* q, const void* k_pool, const void* v_pool, const int32_t* bl
   int32_t* pf_prefix = (int32_t*)(ws + L.off_pf_prefix);
   int32_t* dec_prefix = (int32_t*)(ws + L.off_dec_prefix);
   float* partials = (float*)(ws + L.off_partials);
-  int* counters = (int*)(ws + L.off_counters);
   float* pf_partials = (float*)(ws + L.off_pf_partials);
 
   // RoPE frequencies in revolutions per position (unused with ALiBi: all zero). Partial
@@ -206,7 +201,7 @@ int run(const void* q, const void* k_pool, const void* v_pool, const int32_t* bl
   PlanParams pp{q_indptr, block_table, freqs, pf_prefix, dec_prefix, zero, num_seqs,
                 prefill_positions_per_tile(G), ds.bps, ds.smax, mode, D / 2,
                 cp.pf_smax, kPfItemsPerCu * ncu, Hw, decode_resident_waves(),
-                pf_kc, dec_bps, counters, (int)cp.n_counters, fr};
+                pf_kc, dec_bps, fr};
   if (launch_plan(pp, st) != hipSuccess) return LAZYATTN_ERR_LAUNCH;
 
   DecodeParams Dp{(const uint16_t*)q, (const uint16_t*)k_pool, (const uint16_t*)v_pool,
@@ -221,11 +216,14 @@ int run(const void* q, const void* k_pool, const void* v_pool, const int32_t* bl
                     block_table, block_meta, kv_lens, q_indptr, q_positions,
                     (uint16_t*)out, pf_prefix, (const uint16_t*)zero, num_seqs, Hq, Hw,
                     num_blocks, cp.pf_item_cap, scale_log2, freqs, slopes, Hkv, kv_group,
-                    r / 16, stored_offsets, total_q, pf_kc, cp.pf_smax, pf_partials,
-                    counters};
+                    r / 16, stored_offsets, total_q, pf_kc, cp.pf_smax, pf_partials};
     MixedParams Mp{P, dec_prefix, partials, dec_bps, ds.smax, Dp.rowsplit_cap,
                    8 * kDecChunkWaves};
     if (launch_mixed(Mp, D, G, pe, st) != hipSuccess) return LAZYATTN_ERR_LAUNCH;
+    // split tiles: their partials are merged once every split has finished (the launch
+    // boundary orders the partial stores before the merge's loads)
+    if (cp.pf_smax > 1 && launch_pf_merge(P, D, G, st) != hipSuccess)
+      return LAZYATTN_ERR_LAUNCH;
   } else {
     if (launch_decode(Dp, D, G, pe, st) != hipSuccess) return LAZYATTN_ERR_LAUNCH;
   }

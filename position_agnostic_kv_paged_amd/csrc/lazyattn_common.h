@@ -209,25 +209,23 @@ __device__ __forceinline__ SeqFound wave_upper_seq(const int32_t* prefix, int n,
 // [512, 516)              prefill KV split: key tiles per split (int, written by plan_kernel)
 // [516, 768)              reserved; 16-byte zero rows at 576..767
 // [768, ...)              prefix arrays: prefill items, decode row-splits, each num_seqs + 1 int32
-// aligned 256             counters: int32 [n_counters] (zeroed by the plan kernel)
 // aligned 256             split-K partials: float [row-splits][Hq][D + 4]  (o[D], m, l, -, -)
 // aligned 256             prefill KV-split partials: float [pf_slots][256 rows][D + 4]
 struct WsLayout {
-  size_t off_freqs, off_zero, off_pf_prefix, off_dec_prefix, off_counters, off_partials,
-      off_pf_partials, total;
+  size_t off_freqs, off_zero, off_pf_prefix, off_dec_prefix, off_partials, off_pf_partials,
+      total;
 };
 
 __host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 __host__ __device__ inline WsLayout ws_layout(int num_seqs, long long max_rowsplits, int Hq, int D,
-                                              long long n_counters = 0, long long pf_slots = 0) {
+                                              long long pf_slots = 0) {
   WsLayout L;
   L.off_freqs = 0;
   L.off_zero = 576;
   L.off_pf_prefix = 768;
   L.off_dec_prefix = align_up(L.off_pf_prefix + 4ull * (num_seqs + 1), 256);
-  L.off_counters = align_up(L.off_dec_prefix + 4ull * (num_seqs + 1), 256);
-  L.off_partials = align_up(L.off_counters + 4ull * (size_t)n_counters, 256);
+  L.off_partials = align_up(L.off_dec_prefix + 4ull * (num_seqs + 1), 256);
   L.off_pf_partials =
       align_up(L.off_partials + (size_t)max_rowsplits * Hq * (D + 4) * 4ull, 256);
   L.total = L.off_pf_partials + (size_t)pf_slots * 256ull * (D + 4) * 4ull;

@@ -23,8 +23,6 @@ struct PlanParams {
   int dec_waves;             // resident decode waves (decode split of mixed calls)
   int* pf_kc;                // out: key tiles per split (device-chosen, read by prefill)
   int* dec_bps;              // out: decode split size (mixed calls: device-chosen; else bps)
-  int* counters;             // [n_counters] zeroed here (prefill tile counters)
-  int n_counters;
   RopeFreqs fr;              // host-computed table (kernel argument)
 };
 
@@ -52,7 +50,6 @@ struct PrefillParams {
   const int* pf_kc;          // KV split: key tiles per split (written by plan_kernel)
   int pf_smax;               // KV split: splits-per-tile cap (pf_split)
   float* pf_partials;        // [Hkv * pf_item_cap][tile rows][D + 4]: split partials (o, m, l)
-  int* pf_counters;          // [Hkv * pf_item_cap]: finished splits of each tile (zeroed by plan)
 };
 
 // More than 16 query heads per KV head (G = 16 S): the kernels run Hkv * S "work heads" of
@@ -106,6 +103,9 @@ struct MixedParams {
   int dec_chunk;             // decode items per workgroup (a multiple of its 8 waves)
 };
 hipError_t launch_mixed(const MixedParams& p, int D, int G, int pe, hipStream_t st);
+// merge of the prefill KV-split partials (launched after the mixed kernel when splits may
+// have been taken)
+hipError_t launch_pf_merge(const PrefillParams& p, int D, int G, hipStream_t st);
 
 hipError_t launch_plan(const PlanParams& p, hipStream_t st);
 hipError_t launch_merge(const MergeParams& p, int total_q, int D, hipStream_t st);

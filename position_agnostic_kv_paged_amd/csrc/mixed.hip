@@ -75,6 +75,37 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void mixed_kernel(MixedParam
 
 int prefill_positions_per_tile(int G) { return 32 * kPrefillWaves / G; }
 
+// Merge of the KV-split prefill tiles: workgroup (kvh, item) merges its slice of the item's
+// tile (pf_merge_slice); items past the batch's count and items of unsplit tiles leave.
+template <int D, int G>
+__global__ __launch_bounds__(256) void pf_merge_kernel(PrefillParams P) {
+  const int kvh = blockIdx.x / P.pf_item_cap, item = blockIdx.x - kvh * P.pf_item_cap;
+  if (item >= P.pf_prefix[P.num_seqs]) return;                   // uniform
+  pf_merge_slice<D, G>(P, kvh, item, 256);
+}
+
+template <int D>
+static hipError_t launch_pf_merge_d(const PrefillParams& p, int G, int nwg, hipStream_t st) {
+  dim3 grid(nwg), block(256);
+  switch (G) {
+    case 1: hipLaunchKernelGGL((pf_merge_kernel<D, 1>), grid, block, 0, st, p); break;
+    case 2: hipLaunchKernelGGL((pf_merge_kernel<D, 2>), grid, block, 0, st, p); break;
+    case 4: hipLaunchKernelGGL((pf_merge_kernel<D, 4>), grid, block, 0, st, p); break;
+    case 8: hipLaunchKernelGGL((pf_merge_kernel<D, 8>), grid, block, 0, st, p); break;
+    case 16: hipLaunchKernelGGL((pf_merge_kernel<D, 16>), grid, block, 0, st, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_pf_merge(const PrefillParams& p, int D, int G, hipStream_t st) {
+  const long long nwg = (long long)p.pf_item_cap * p.Hkv;        // every (KV head, item) slot
+  if (nwg <= 0) return hipSuccess;
+  if (nwg > INT32_MAX / 2) return hipErrorInvalidValue;
+  return D == 128 ? launch_pf_merge_d<128>(p, G, (int)nwg, st)
+                  : launch_pf_merge_d<64>(p, G, (int)nwg, st);
+}
+
 template <int D, int G>
 static hipError_t launch_dg(const MixedParams& p, int pe, int nwg, hipStream_t st) {
   dim3 grid(nwg), block(kPrefillWaves * 64);

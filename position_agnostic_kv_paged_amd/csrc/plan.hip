@@ -18,7 +18,6 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanParams P) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   if (tid < 48) P.zero[tid] = 0u;
   if (tid < P.half_dim) P.freqs_out[tid] = P.fr.f[tid];
-  for (int i = tid; i < P.n_counters; i += 256) P.counters[i] = 0;
   if (tid == 0) {
     s_tiles = 0;
     s_maxkt = 0;

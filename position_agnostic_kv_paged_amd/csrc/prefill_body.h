@@ -150,7 +150,6 @@ struct PrefillSmem {
   uint16_t (&Qs)[S::NW][32 * S::KS];         // each wave's rotated queries (fp16)
   double (&fr_s)[S::HALF];
   int& pmax_s;
-  int& last_s;                               // this split item completes its query tile
 };
 
 // Declares the arrays of a PrefillSmem in the calling kernel and binds `name` to them.
@@ -162,16 +161,15 @@ struct PrefillSmem {
   __shared__ __align__(16) u32x2 name##_slot[16 * name##_S::HALF / 2];                      \
   __shared__ __align__(16) uint16_t name##_Qs[name##_S::NW][32 * name##_S::KS];            \
   __shared__ double name##_fr[name##_S::HALF];                                             \
-  __shared__ int name##_pmax, name##_last;                                                 \
+  __shared__ int name##_pmax;                                                              \
   PrefillSmem<D> name{name##_Ks, name##_Vs, name##_tbl, name##_slot, name##_Qs, name##_fr, \
-                      name##_pmax, name##_last}
+                      name##_pmax}
 
 // One prefill work item: query tile qt of a sequence for KV (work) head kvh, over the key
 // tiles of one KV split. `item` numbers the items of a KV head: each sequence owns
 // tiles x splits consecutive items (plan_kernel's prefix sums), tile-major. An item that is
 // its tile's only split writes the bf16 output rows; otherwise it writes a partial
-// (o, m, l) per row, and the split that finishes its tile last merges the tile's partials
-// into the output (a per-tile counter; device-scope fences order the partial stores).
+// (o, m, l) per row, which pf_merge_slice folds into the output in a later launch.
 template <int D, int G, int PE>
 __device__ __forceinline__ void prefill_item(const PrefillParams& P, const PrefillSmem<D>& SM,
                                              const int kvh, const int item) {
@@ -776,65 +774,75 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& P, const Prefi
       pr[D + 1] = lt;
     }
   }
-  // the tile's counter: the split that brings it to `splits` merges every split's partial
-  __threadfence();                                           // partials visible device-wide
-  __syncthreads();
-  const int first = item - sp;                               // the tile's first split item
-  if (tid == 0) {
-    int* cnt = P.pf_counters + (size_t)kvh * cap + first;
-    SM.last_s = atomicAdd(cnt, 1) == spl.splits - 1;
-  }
-  __syncthreads();
-  if (!SM.last_s) return;
-  __threadfence();                                           // see the other splits' stores
-  // two threads per row, D/2 dims each: M = max m, L = sum l 2^(m - M), O = sum o 2^(m - M).
-  // The m values are loaded eight at a time, then one split's (o, l) per round of loads.
-  {
-    const int row = tid >> 1, half = tid & 1;
+}
+
+// Merge of a split query tile (after every split item has written its partial): the rows
+// of the tile are shared among its split items' slots, so item sp of a tile with s splits
+// merges rows [sp 256 / s, (sp + 1) 256 / s). One thread per (row, 4 dims) in turn:
+// M = max m, L = sum l 2^(m - M), O = sum o 2^(m - M), out = O / L (0 where L = 0). A split
+// with no visible key has m = -inf, l = 0, o = 0, weight 0. Every wave of the workgroup
+// calls it with the same (kvh, item).
+template <int D, int G>
+__device__ __forceinline__ void pf_merge_slice(const PrefillParams& P, const int kvh,
+                                               const int item, const int nthreads) {
+  constexpr int ROWS = 32 * kPrefillWaves;
+  constexpr int POS = ROWS / G;
+  constexpr int RS = D + 4;
+  constexpr int CH = D / 4;                                  // 4-dim chunks per row
+  constexpr size_t SPLIT = (size_t)ROWS * RS;                // floats per split partial
+  const int lane = threadIdx.x & 63;
+  const SeqFound sf = wave_upper_seq(P.pf_prefix, P.num_seqs, item, lane);
+  const int seq = sf.s;
+  const int q0 = P.q_indptr[seq], qlen = P.q_indptr[seq + 1] - q0;
+  const int T = P.block_table[seq + 1] - P.block_table[seq];
+  const PfSplit spl = pf_split((T + 3) / 4, *P.pf_kc, P.pf_smax);
+  const int ns = spl.splits;
+  if (ns == 1) return;                                       // written by the item itself
+  const int local = item - sf.start;
+  const int qt = local / ns, sp = local - qt * ns;
+  const int first = item - sp;
+  const int r0 = sp * ROWS / ns, r1 = (sp + 1) * ROWS / ns;
+  const float* tile = P.pf_partials + ((size_t)kvh * P.pf_item_cap + first) * SPLIT;
+  for (int x = threadIdx.x; x < (r1 - r0) * CH; x += nthreads) {
+    const int row = r0 + x / CH, c = x % CH;
     const int rq = qt * POS + row / G;                       // query row in the sequence
     const int rh = kvh * G + row % G;                        // query head
-    if ((rq < qlen) & (q0 + rq < P.total_q)) {
-      constexpr size_t SPLIT = (size_t)ROWS * RS;            // floats per split partial
-      const float* base = P.pf_partials + ((size_t)kvh * cap + first) * SPLIT +
-                          (size_t)row * RS;
-      const int ns = spl.splits;                             // <= kMaxPfSplits
-      float M = -INFINITY;
-      for (int s0 = 0; s0 < ns; s0 += 8) {                   // eight m values per round
-        float mv[8];
+    if (!((rq < qlen) & (q0 + rq < P.total_q))) continue;
+    const float* base = tile + (size_t)row * RS;
+    float M = -INFINITY;
+    for (int s0 = 0; s0 < ns; s0 += 8) {                     // eight m values per round
+      float mv[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) mv[u] = s0 + u < ns ? base[(s0 + u) * SPLIT + D] : -INFINITY;
+      for (int u = 0; u < 8; ++u) mv[u] = s0 + u < ns ? base[(s0 + u) * SPLIT + D] : -INFINITY;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) M = fmaxf(M, mv[u]);
+      for (int u = 0; u < 8; ++u) M = fmaxf(M, mv[u]);
+    }
+    const float Mu = M == -INFINITY ? 0.f : M;               // all -inf: weights 0, row 0
+    float L = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < ns; s0 += 4) {                     // four splits per round
+      f32x4 ov[4];
+      float ms[4], ls[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bool ok = s0 + u < ns;
+        const float* ps = base + (size_t)(ok ? s0 + u : s0) * SPLIT;
+        ov[u] = *(const f32x4*)(ps + 4 * c);
+        ms[u] = ok ? ps[D] : -INFINITY;
+        ls[u] = ps[D + 1];
       }
-      const float Mu = M == -INFINITY ? 0.f : M;             // all -inf: weights 0, row 0
-      float L = 0.f;
-      f32x4 acc[D / 8];
 #pragma unroll
-      for (int i = 0; i < D / 8; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int s2 = 0; s2 < ns; ++s2) {                      // one split per round of loads
-        const float* ps = base + s2 * SPLIT;
-        f32x4 ov[D / 8];
-        const float ms = ps[D], ls = ps[D + 1];
-#pragma unroll
-        for (int i = 0; i < D / 8; ++i) ov[i] = *(const f32x4*)(ps + half * (D / 2) + 4 * i);
-        // a split with no visible key has m = -inf, l = 0, o = 0: weight exp2(-inf) = 0
-        const float wgt = __builtin_amdgcn_exp2f(ms - Mu);
-        L += ls * wgt;
-#pragma unroll
-        for (int i = 0; i < D / 8; ++i) acc[i] += ov[i] * wgt;
-      }
-      const float inv = L > 0.f ? 1.f / L : 0.f;
-      uint16_t* dst = P.out + ((size_t)(q0 + rq) * P.Hq + rh) * D + half * (D / 2);
-#pragma unroll
-      for (int i = 0; i < D / 8; i += 2) {
-        u32x4 v;
-        v[0] = pack_bf16(acc[i][0] * inv, acc[i][1] * inv);
-        v[1] = pack_bf16(acc[i][2] * inv, acc[i][3] * inv);
-        v[2] = pack_bf16(acc[i + 1][0] * inv, acc[i + 1][1] * inv);
-        v[3] = pack_bf16(acc[i + 1][2] * inv, acc[i + 1][3] * inv);
-        *(u32x4*)(dst + 4 * i) = v;
+      for (int u = 0; u < 4; ++u) {
+        const float wgt = __builtin_amdgcn_exp2f(ms[u] - Mu);
+        L += ls[u] * wgt;
+        acc += ov[u] * wgt;
       }
     }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    u32x2 v;
+    v[0] = pack_bf16(acc[0] * inv, acc[1] * inv);
+    v[1] = pack_bf16(acc[2] * inv, acc[3] * inv);
+    *(u32x2*)(P.out + ((size_t)(q0 + rq) * P.Hq + rh) * D + 4 * c) = v;
   }
 }
 
