@@ -284,16 +284,23 @@ def measured_ceilings(torch, L, stream, reps=5):
     cyc = torch.empty(L.probe_cus() * 8, dtype=torch.int64, device="cuda")
     buf = torch.empty(1 << 29, dtype=torch.int32, device="cuda").fill_(7)
     half = buf.numel() // 2
-    mf, ghz, rd, cp = [], [], [], []
+    chunk = 4096                                           # one (block, KV head) of K at D = 128
+    n_chunks = buf.numel() * 4 // chunk
+    order = torch.randperm(n_chunks, generator=torch.Generator().manual_seed(11))
+    ids = order.to(torch.int32).to("cuda")
+    mf, ghz, rd, cp, ga = [], [], [], [], []
     for r in range(reps + 1):
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
         e[0].record(stream)
         _, flops = L.probe_mfma(iters, cycles=cyc, stream=stream)
         e[1].record(stream)
         e[2].record(stream)
         L.probe_read(buf, stream=stream)
         e[3].record(stream)
-        e[4].record(stream)
+        e[6].record(stream)
+        L.probe_gather(buf, ids, chunk, stream=stream)     # the same 2 GiB in random 4 KB chunks
+        e[7].record(stream)
+        e[4].record(stream)                                # (last: it leaves dirty lines behind)
         buf[half:].copy_(buf[:half])                       # plain device copy, 1 GiB each way
         e[5].record(stream)
         torch.cuda.synchronize()
@@ -304,17 +311,40 @@ def measured_ceilings(torch, L, stream, reps=5):
         ghz.append(float(cyc.max().item()) / t / 1e9)
         rd.append(buf.numel() * 4 / (e[2].elapsed_time(e[3]) / 1e3) / 1e9)
         cp.append(2 * half * 4 / (e[4].elapsed_time(e[5]) / 1e3) / 1e9)
-    del buf
+        ga.append(buf.numel() * 4 / (e[6].elapsed_time(e[7]) / 1e3) / 1e9)
+    del buf, ids
     return {"mfma_f16_tflops": float(np.median(mf)), "shader_ghz": float(np.median(ghz)),
             "hbm_read_gbs": float(np.median(rd)), "hbm_copy_gbs": float(np.median(cp)),
+            "hbm_gather_gbs": float(np.median(ga)),
             "note": "MFMA: 8 waves/CU of independent 32x32x16 fp16 products; read: 2 GiB, "
                     "16-byte non-temporal loads, 8 workgroups of 256 per CU; copy: torch "
-                    "device-to-device copy of 1 GiB, read + write bytes"}
+                    "device-to-device copy of 1 GiB, read + write bytes; gather: the same "
+                    "2 GiB as 4 KB chunks in a seeded random order, one wave per chunk, "
+                    "ordinary 16-byte loads"}
+
+
+SETTLE_S = 0.05
+
+
+def settle(torch, fn, seconds=SETTLE_S):
+    """Run fn back to back for `seconds` of wall time, untimed: the shader clock ramps up
+    over the first milliseconds of sustained load (a short call after an idle gap runs
+    slower than the same call under continuous load), so every timing starts from the
+    clock that steady work sees."""
+    t0 = time.perf_counter()
+    while True:
+        for _ in range(4):
+            fn()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            return
 
 
 def timed(torch, stream, fn, reps, warmup, flush=None):
-    """Median-style timing of fn on `stream`: warmup calls, then reps calls each bracketed
-    by HIP events (a flush fill before each one, outside the events, when given)."""
+    """Median-style timing of fn on `stream`: the clock settled (settle), warmup calls,
+    then reps calls each bracketed by HIP events (a flush fill before each one, outside the
+    events, when given)."""
+    settle(torch, fn)
     for _ in range(warmup):
         fn()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps)]
@@ -454,6 +484,7 @@ def main():
         return
 
     # ---- the timed step -------------------------------------------------------------------
+    settle(torch, step)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -490,6 +521,7 @@ def main():
                        "step": f"one {'lazyattn_prefill' if pre_seqs else 'lazyattn_decode'} "
                                f"call over the whole batch"},
             "step_ms_pct": pct(ts),
+            "clock_settle_s": SETTLE_S,
             "value_definition": "algorithmic attention FLOPs of the whole step (prefill and "
                                 "decode rows, 4*D per visible (query, key, q-head) pair) over "
                                 "the mean step time"}
@@ -619,6 +651,8 @@ def main():
                     args.warmup)
         line["decode"]["no_reuse_ms_pct"] = stn
         line["decode"]["no_reuse_gbs"] = decode_bytes(wn, dn) / (stn["median"] / 1e3) / 1e9
+        line["decode"]["no_reuse_frac_measured_gather"] = (line["decode"]["no_reuse_gbs"]
+                                                           / ceil["hbm_gather_gbs"])
         del pn, an, wsn
         torch.cuda.empty_cache()
         line["decode_controls"] = {

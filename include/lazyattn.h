@@ -384,11 +384,18 @@ int lazyattn_pool_stats(void* pool, LazyattnPoolStats* out);
  *    matrix-core rate reachable in practice; cycles / time is the sustained shader clock.
  *  lazyattn_probe_read -- reads `bytes` (a multiple of 16, 16-byte aligned) of device memory
  *    once with 16-byte non-temporal loads; scratch_out: uint32 [8 * probe_cus * 256].
- * Errors: NULL, ALIGN, ARG (iters <= 0), SHAPE (bytes), LAUNCH.
+ *  lazyattn_probe_gather -- reads the chunks chunk_ids[0 .. n_ids) (device int32; chunk c is
+ *    bytes [c * chunk_bytes, (c + 1) * chunk_bytes) of buf, chunk_bytes a multiple of 1024)
+ *    with ordinary 16-byte loads, one wave per chunk at a time, waves taking the list
+ *    round-robin: the access pattern of a paged kernel over randomly placed blocks. Ids
+ *    outside the buffer are skipped. scratch_out: uint32 [8 * probe_cus * 256].
+ * Errors: NULL, ALIGN, ARG (iters <= 0), SHAPE (bytes, chunk size), LAUNCH.
  */
 int32_t lazyattn_probe_cus(void);
 int lazyattn_probe_mfma(int32_t iters, void* cycles_out, void* scratch_out, void* stream);
 int lazyattn_probe_read(const void* buf, size_t bytes, void* scratch_out, void* stream);
+int lazyattn_probe_gather(const void* buf, size_t bytes, const int32_t* chunk_ids,
+                          int32_t n_ids, int32_t chunk_bytes, void* scratch_out, void* stream);
 
 /* Workspace sizes (bytes) for the calls above; 0 on invalid sizes. */
 size_t lazyattn_prefill_workspace_bytes(int32_t num_seqs, int32_t total_q, int32_t max_entries,

@@ -16,7 +16,8 @@ EXPORTED = [
     "lazyattn_prefill_alibi", "lazyattn_decode_alibi", "lazyattn_prefill_partial",
     "lazyattn_decode_partial", "lazyattn_prefill_doc_rotated", "lazyattn_decode_doc_rotated",
     "lazyattn_materialize_rotated", "lazyattn_probe_cus",
-    "lazyattn_probe_mfma", "lazyattn_probe_read", "lazyattn_ingest_kv", "lazyattn_pool_create",
+    "lazyattn_probe_mfma", "lazyattn_probe_read", "lazyattn_probe_gather", "lazyattn_ingest_kv",
+    "lazyattn_pool_create",
     "lazyattn_pool_destroy", "lazyattn_pool_acquire", "lazyattn_pool_release",
     "lazyattn_pool_alloc_private", "lazyattn_pool_free_private", "lazyattn_pool_stats",
     "lazyattn_prefill_workspace_bytes",
@@ -80,6 +81,8 @@ def lib():
     L.lazyattn_probe_cus.argtypes, L.lazyattn_probe_cus.restype = [], i32
     L.lazyattn_probe_mfma.argtypes, L.lazyattn_probe_mfma.restype = [i32, vp, vp, vp], ctypes.c_int
     L.lazyattn_probe_read.argtypes, L.lazyattn_probe_read.restype = [vp, u64, vp, vp], ctypes.c_int
+    L.lazyattn_probe_gather.argtypes = [vp, u64, vp, i32, i32, vp, vp]
+    L.lazyattn_probe_gather.restype = ctypes.c_int
     L.lazyattn_ingest_kv.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp]
     L.lazyattn_ingest_kv.restype = ctypes.c_int
     P32 = ctypes.POINTER(ctypes.c_int32)

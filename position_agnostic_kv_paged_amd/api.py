@@ -233,6 +233,20 @@ def probe_read(buf, scratch=None, stream=None):
     return scratch
 
 
+def probe_gather(buf, chunk_ids, chunk_bytes, scratch=None, stream=None):
+    """lazyattn_probe_gather: reads the chunk_bytes-sized chunks of the device tensor `buf`
+    listed in chunk_ids (device int32), one wave per chunk; returns the uint32 scratch
+    whose XOR is the XOR of the 32-bit words of the chunks read."""
+    import torch
+    if scratch is None:
+        scratch = torch.empty(8 * probe_cus() * 256, dtype=torch.int32, device=buf.device)
+    rc = lib().lazyattn_probe_gather(_ptr(buf), buf.numel() * buf.element_size(),
+                                     _ptr(chunk_ids), chunk_ids.numel(), int(chunk_bytes),
+                                     _ptr(scratch), _stream(stream))
+    check(rc, "lazyattn_probe_gather")
+    return scratch
+
+
 def ingest_kv(k_new, v_new, slot_mapping, k_pool, v_pool, stream=None):
     """lazyattn_ingest_kv: scatter new tokens' K/V (bf16 [n, Hkv, D], unrotated) into the pool
     slots slot_mapping (int32 [n], block_id * B + slot; negative = skip)."""

@@ -575,6 +575,21 @@ int lazyattn_probe_read(const void* buf, size_t bytes, void* scratch_out, void* 
   return LAZYATTN_OK;
 }
 
+int lazyattn_probe_gather(const void* buf, size_t bytes, const int32_t* chunk_ids,
+                          int32_t n_ids, int32_t chunk_bytes, void* scratch_out, void* stream) {
+  if (!buf || !chunk_ids || !scratch_out) return LAZYATTN_ERR_NULL;
+  if (!aligned(buf, 16) || !aligned(chunk_ids, 4) || !aligned(scratch_out, 4))
+    return LAZYATTN_ERR_ALIGN;
+  if (n_ids < 0 || chunk_bytes <= 0 || chunk_bytes % 1024 || bytes < (size_t)chunk_bytes ||
+      bytes / (size_t)chunk_bytes > (size_t)INT32_MAX)
+    return LAZYATTN_ERR_SHAPE;
+  if (n_ids == 0) return LAZYATTN_OK;
+  if (launch_probe_gather(buf, bytes, chunk_ids, n_ids, chunk_bytes, 8 * lazyattn_probe_cus(),
+                          (uint32_t*)scratch_out, (hipStream_t)stream) != hipSuccess)
+    return LAZYATTN_ERR_LAUNCH;
+  return LAZYATTN_OK;
+}
+
 int lazyattn_debug_decode_meta(const uint32_t* words, const int32_t* block_table,
                                int32_t num_seqs, int32_t n_entries, int32_t B,
                                int32_t* ids_out, int32_t* offsets_out, void* stream) {

@@ -141,6 +141,8 @@ hipError_t launch_probe_mfma(int num_cus, int iters, unsigned long long* cyc, fl
                              hipStream_t st);
 hipError_t launch_probe_read(const void* buf, size_t bytes, int num_wg, uint32_t* out,
                              hipStream_t st);
+hipError_t launch_probe_gather(const void* buf, size_t bytes, const int32_t* idx, int n_idx,
+                               int chunk_bytes, int num_wg, uint32_t* out, hipStream_t st);
 
 // waves of the decode grid (all resident at once); decode items are dealt round-robin to them
 int decode_resident_waves();

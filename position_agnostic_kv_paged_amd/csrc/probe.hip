@@ -1,6 +1,7 @@
 // Measured ceilings for reporting: an MFMA loop (the matrix-core rate the prefill kernel's
-// 32x32x16 fp16/bf16 products can reach, and the shader clock it runs at) and a plain
-// stream read of device memory (the HBM rate the decode kernel's traffic can reach).
+// 32x32x16 fp16/bf16 products can reach, and the shader clock it runs at), a plain stream
+// read of device memory and a random gather of fixed-size chunks (the rates the decode
+// kernel's traffic can reach, streamed and as a paged kernel reads it).
 #include "lazyattn_common.h"
 #include "lazyattn_kernels.h"
 
@@ -51,6 +52,35 @@ __global__ __launch_bounds__(256) void probe_read_kernel(const u32x4* buf, size_
     x ^= v[0] ^ v[1] ^ v[2] ^ v[3];
   }
   out[(size_t)blockIdx.x * 256 + threadIdx.x] = x;
+}
+
+// Random gather of whole chunks: wave w reads chunks idx[w], idx[w + W], ... (each
+// `c16` 16-byte units, read by the 64 lanes together), the access pattern of a paged
+// kernel over randomly placed blocks. Chunk ids outside [0, n_total) are skipped.
+__global__ __launch_bounds__(256) void probe_gather_kernel(const u32x4* buf, const int32_t* idx,
+                                                           int n_idx, int n_total, int c16,
+                                                           uint32_t* out) {
+  const int lane = threadIdx.x & 63;
+  const int wave = (int)((blockIdx.x * 256 + threadIdx.x) >> 6);
+  const int nw = (int)(gridDim.x * 4);
+  uint32_t x = 0;
+  for (int i = wave; i < n_idx; i += nw) {
+    const int id = idx[i];
+    if ((unsigned)id >= (unsigned)n_total) continue;
+    const u32x4* c = buf + (size_t)id * c16;
+    for (int k = lane; k < c16; k += 64) {
+      const u32x4 v = c[k];
+      x ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+    }
+  }
+  out[(size_t)blockIdx.x * 256 + threadIdx.x] = x;
+}
+
+hipError_t launch_probe_gather(const void* buf, size_t bytes, const int32_t* idx, int n_idx,
+                               int chunk_bytes, int num_wg, uint32_t* out, hipStream_t st) {
+  hipLaunchKernelGGL(probe_gather_kernel, dim3(num_wg), dim3(256), 0, st, (const u32x4*)buf,
+                     idx, n_idx, (int)(bytes / (size_t)chunk_bytes), chunk_bytes / 16, out);
+  return hipGetLastError();
 }
 
 hipError_t launch_probe_mfma(int num_cus, int iters, unsigned long long* cyc, float* out,

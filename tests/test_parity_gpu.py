@@ -712,6 +712,16 @@ def test_probes():
     cyc, flops = L.probe_mfma(4)
     torch.cuda.synchronize()
     assert flops > 0 and int(cyc.min().item()) > 0
+    # gather: the listed 1 KB chunks (one repeated, one id past the buffer, skipped)
+    words = host.numpy().view(np.uint32)[: 3 * 2**20]
+    chunks = words.reshape(-1, 256)                       # 1 KB each
+    ids = np.array([5, 0, chunks.shape[0] - 1, 17, 5, chunks.shape[0], 1200], dtype=np.int32)
+    got = L.probe_gather(buf[: 3 * 2**20], torch.from_numpy(ids).cuda(), 1024).cpu().numpy()
+    want = np.uint32(0)
+    for i in ids:
+        if i < chunks.shape[0]:
+            want ^= np.bitwise_xor.reduce(chunks[i])
+    assert np.bitwise_xor.reduce(got.view(np.uint32)) == want
 
 
 def _random_batch(seed):
