@@ -136,6 +136,60 @@ int lazyattn_decode(const void* q, const void* k_pool, const void* v_pool,
                     void* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Shared-document decode (technical summary, "Core Concept": cached keys carry no position,
+ * so one physical copy of a document's blocks serves every request that contains it).
+ *
+ * lazyattn_decode_share_plan -- HOST function. From host copies of a decode batch's tables
+ * it finds runs of blocks that several query rows read (the same block ids at consecutive
+ * entries, at least 4 blocks) and groups up to M = 16 / G rows (G = Hq / Hkv; M = 1 for
+ * G = 16 and above) into one work item that loads each block once; the remaining entries
+ * of every row become single-row items of at most max_chunk blocks (grouped runs are also
+ * cut at max_chunk). single_row_only = 1 plans only the rows of sequences with one query
+ * row (the decode rows of a mixed batch), 0 plans every row.
+ *  q_indptr, block_table  int32 [num_seqs + 1] (host), as for the attention calls
+ *  block_meta             uint32 [block_table[num_seqs]] (host) packed words
+ *  max_chunk              blocks per item, at most (>= 4; items are also at most 128 / M
+ *                         blocks long)
+ *  waves                  resident decode waves of the device (8 per compute unit; 0: keep
+ *                         the items in planning order). The kernel deals item i to wave
+ *                         i mod waves; the planner puts the longest items first on the least
+ *                         loaded waves and pads with empty items (no members) to balance them
+ *  plan_out               int32 [plan_cap] or NULL (size query); *plan_len_out receives the
+ *                         plan's length in int32 either way
+ * The plan (int32): [0] magic, [1] version 1, [2] M, [3] 2 + 4 M, [4] items, [5] partial
+ * slots, [6] total_q, [7] num_seqs, then total_q + 1 slot offsets (row r owns slots
+ * [p[r], p[r + 1])), then one record per item: length in blocks, member count, and per
+ * member (query row, sequence, first entry, slot); member 0's entries supply the block ids.
+ * Errors: NULL, SHAPE (tables not non-decreasing from 0, q_indptr[num_seqs] != total_q,
+ * Hq % Hkv), ARG (max_chunk < 4, waves < 0), NOSPACE (plan_cap too small; *plan_len_out is
+ * set).
+ *
+ * lazyattn_decode_shared -- lazyattn_decode (RoPE) over such a plan, copied to device
+ * memory (plan: int32, 4-byte aligned) together with its item and slot counts from the
+ * header. The plan must have been built from the same block table, block_meta and q_indptr;
+ * a plan whose header does not match the call (M, total_q, num_seqs) produces zero rows,
+ * and indices inside it are clamped to the call's arrays. Workspace:
+ * lazyattn_decode_shared_workspace_bytes(num_seqs, total_q, plan_slots, Hq, Hkv, D).
+ * Errors as lazyattn_decode, plus NULL plan and ARG for negative counts.
+ */
+int lazyattn_decode_share_plan(const int32_t* q_indptr, const int32_t* block_table,
+                               const uint32_t* block_meta, int32_t num_seqs, int32_t total_q,
+                               int32_t Hq, int32_t Hkv, int32_t single_row_only,
+                               int32_t max_chunk, int32_t waves, int32_t* plan_out,
+                               int64_t plan_cap, int64_t* plan_len_out);
+int lazyattn_decode_shared(const void* q, const void* k_pool, const void* v_pool,
+                           const int32_t* block_table, const uint32_t* block_meta,
+                           const int32_t* kv_lens, const int32_t* q_indptr,
+                           const int32_t* q_positions, double rope_base, int32_t num_seqs,
+                           int32_t total_q, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
+                           int32_t num_blocks, int32_t max_entries, const int32_t* plan,
+                           int32_t plan_items, int32_t plan_slots, void* out, void* workspace,
+                           size_t workspace_bytes, void* stream);
+size_t lazyattn_decode_shared_workspace_bytes(int32_t num_seqs, int32_t total_q,
+                                              int32_t plan_slots, int32_t Hq, int32_t Hkv,
+                                              int32_t D);
+
+/*
  * lazyattn_decode_noalloc -- lazyattn_decode for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
  * same arguments, result and errors, minus the workspace. The split-K partials, plan

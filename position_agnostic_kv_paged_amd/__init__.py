@@ -5,4 +5,5 @@ from .api import (prefill, decode, prefill_rotated_pool, decode_rotated_pool,  #
                   materialize_rotated, encode_meta, debug_decode_meta,
                   workspace_bytes, probe_cus, probe_mfma, probe_read, probe_gather,
                   ingest_kv,
-                  PoolIndex, llama31_inv_freq, decode_noalloc, BLOCK)
+                  PoolIndex, llama31_inv_freq, decode_noalloc, decode_share_plan,
+                  decode_shared, BLOCK)

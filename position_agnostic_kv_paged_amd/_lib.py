@@ -22,7 +22,8 @@ EXPORTED = [
     "lazyattn_pool_alloc_private", "lazyattn_pool_free_private", "lazyattn_pool_stats",
     "lazyattn_prefill_workspace_bytes",
     "lazyattn_decode_workspace_bytes", "lazyattn_encode_meta", "lazyattn_debug_decode_meta",
-    "lazyattn_llama31_inv_freq", "lazyattn_decode_noalloc",
+    "lazyattn_llama31_inv_freq", "lazyattn_decode_noalloc", "lazyattn_decode_share_plan",
+    "lazyattn_decode_shared", "lazyattn_decode_shared_workspace_bytes",
     "lazyattn_status_str", "lazyattn_version",
 ]
 
@@ -66,6 +67,13 @@ def lib():
         f.argtypes, f.restype = attn[:8] + [vp] + attn[9:], ctypes.c_int
     L.lazyattn_decode_noalloc.argtypes = attn[:17] + [vp, vp]
     L.lazyattn_decode_noalloc.restype = ctypes.c_int
+    L.lazyattn_decode_shared.argtypes = attn[:17] + [vp, i32, i32] + attn[17:]
+    L.lazyattn_decode_shared.restype = ctypes.c_int
+    L.lazyattn_decode_shared_workspace_bytes.argtypes = [i32] * 6
+    L.lazyattn_decode_shared_workspace_bytes.restype = ctypes.c_size_t
+    L.lazyattn_decode_share_plan.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp,
+                                             ctypes.c_int64, ctypes.POINTER(ctypes.c_int64)]
+    L.lazyattn_decode_share_plan.restype = ctypes.c_int
     for name in ("lazyattn_prefill_workspace_bytes", "lazyattn_decode_workspace_bytes"):
         f = getattr(L, name)
         f.argtypes, f.restype = [i32] * 6, ctypes.c_size_t

@@ -128,6 +128,52 @@ def decode_noalloc(q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indptr
     return out
 
 
+def decode_share_plan(q_indptr, block_table, block_meta, Hq, Hkv, single_row_only=False,
+                      max_chunk=16, waves=None):
+    """lazyattn_decode_share_plan on host (numpy) tables: returns the int32 plan (numpy); its
+    header holds the item count [4] and slot count [5]. waves defaults to the resident
+    decode waves of the device (8 per compute unit)."""
+    if waves is None:
+        waves = 8 * probe_cus()
+    qi = np.ascontiguousarray(q_indptr, dtype=np.int32)
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    bm = np.ascontiguousarray(block_meta, dtype=np.uint32)
+    n = ctypes.c_int64(0)
+    args = (qi.ctypes.data, bt.ctypes.data, bm.ctypes.data if bm.size else None, len(qi) - 1,
+            int(qi[-1]), int(Hq), int(Hkv), int(bool(single_row_only)), int(max_chunk),
+            int(waves))
+    check(lib().lazyattn_decode_share_plan(*args, None, 0, ctypes.byref(n)),
+          "lazyattn_decode_share_plan")
+    plan = np.zeros(n.value, dtype=np.int32)
+    check(lib().lazyattn_decode_share_plan(*args, plan.ctypes.data, n.value, ctypes.byref(n)),
+          "lazyattn_decode_share_plan")
+    return plan
+
+
+def decode_shared(q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indptr, q_pos,
+                  rope_base, max_entries, plan, plan_items, plan_slots, out=None,
+                  workspace=None, stream=None):
+    """lazyattn_decode_shared: decode over a shared-document plan (`plan` a device int32
+    copy of decode_share_plan's result, plan_items / plan_slots its header [4] / [5])."""
+    import torch
+    total_q, Hq, D, num_blocks, Hkv, B = _dims(q, k_pool)
+    num_seqs = kv_lens.numel()
+    if out is None:
+        out = torch.empty_like(q)
+    need = lib().lazyattn_decode_shared_workspace_bytes(num_seqs, total_q, int(plan_slots), Hq,
+                                                        Hkv, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    rc = lib().lazyattn_decode_shared(
+        _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(block_meta),
+        _ptr(kv_lens), _ptr(q_indptr), _ptr(q_pos), float(rope_base), num_seqs, total_q, Hq,
+        Hkv, D, B, num_blocks, int(max_entries), _ptr(plan), int(plan_items), int(plan_slots),
+        _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream))
+    check(rc, "lazyattn_decode_shared")
+    return out
+
+
 def llama31_inv_freq(D, base=500000.0, factor=8.0, low_freq_factor=1.0, high_freq_factor=4.0,
                      original_context=8192):
     """lazyattn_llama31_inv_freq: the Llama 3.1 frequency-scaled RoPE table (host, float64,

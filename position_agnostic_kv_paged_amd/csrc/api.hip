@@ -131,10 +131,18 @@ int run(const void* q, const void* k_pool, const void* v_pool, const int32_t* bl
         int32_t max_entries, void* out, void* workspace, size_t workspace_bytes,
         void* stream, int mode, int pe, const double* inv_freq = nullptr,
         const float* slopes = nullptr, int rotary_dim = 0,
-        const int32_t* stored_offsets = nullptr, bool fit_workspace = false) {
+        const int32_t* stored_offsets = nullptr, bool fit_workspace = false,
+        const int32_t* share_plan = nullptr, int32_t plan_items = 0, int32_t plan_slots = 0) {
   if (!q || !k_pool || !v_pool || !block_table || !block_meta || !kv_lens || !q_indptr ||
       !q_positions || !out || !workspace)
     return LAZYATTN_ERR_NULL;
+  const bool shared = share_plan != nullptr;  // shared-document decode over a host plan
+  if (shared) {
+    if (mode != kPlanDecodeOnly || pe != kRope || inv_freq || fit_workspace)
+      return LAZYATTN_ERR_ARG;
+    if (plan_items < 0 || plan_slots < 0) return LAZYATTN_ERR_ARG;
+    if (!aligned(share_plan, 4)) return LAZYATTN_ERR_ALIGN;
+  }
   if (num_seqs < 0 || total_q < 0 || num_blocks < 0 || max_entries < 0 ||
       num_blocks > (1 << kIdBits) || !shape_ok(Hq, Hkv, D, B))
     return LAZYATTN_ERR_SHAPE;
@@ -167,7 +175,8 @@ int run(const void* q, const void* k_pool, const void* v_pool, const int32_t* bl
       : mode == kPlanDecodeOnly ? decode_split(rows_bound, work_heads(Hq, Hkv), max_entries)
                                 : mixed_decode_split(num_seqs, work_heads(Hq, Hkv), max_entries);
   if (ds.smax <= 0) return LAZYATTN_ERR_WORKSPACE;
-  const CallPlan cp = plan_call(mode, num_seqs, total_q, max_entries, Hq, Hkv, D, ds);
+  CallPlan cp = plan_call(mode, num_seqs, total_q, max_entries, Hq, Hkv, D, ds);
+  if (shared) cp.L = ws_layout(num_seqs, plan_slots, Hq, D);    // one partial per plan slot
   if (workspace_bytes < cp.L.total) return LAZYATTN_ERR_WORKSPACE;
   if (num_seqs == 0 || total_q == 0) return LAZYATTN_OK;
 
@@ -224,11 +233,15 @@ int run(const void* q, const void* k_pool, const void* v_pool, const int32_t* bl
     // boundary orders the partial stores before the merge's loads)
     if (cp.pf_smax > 1 && launch_pf_merge(P, D, G, st) != hipSuccess)
       return LAZYATTN_ERR_LAUNCH;
+  } else if (shared) {
+    if (launch_decode_plan(Dp, share_plan, plan_items, plan_slots, D, G, st) != hipSuccess)
+      return LAZYATTN_ERR_LAUNCH;
   } else {
     if (launch_decode(Dp, D, G, pe, st) != hipSuccess) return LAZYATTN_ERR_LAUNCH;
   }
   MergeParams Mp{q_indptr, block_table, dec_prefix, partials, (uint16_t*)out,
-                 num_seqs, Hq, dec_bps, ds.smax, mode, total_q};
+                 num_seqs, Hq, dec_bps, ds.smax, mode, total_q,
+                 shared ? share_plan + 8 : nullptr, plan_slots, 16 / G};
   if (launch_merge(Mp, total_q, D, st) != hipSuccess) return LAZYATTN_ERR_LAUNCH;
   return LAZYATTN_OK;
 }
@@ -299,6 +312,28 @@ int lazyattn_decode(const void* q, const void* k_pool, const void* v_pool,
   return run(q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indptr, q_positions,
              rope_base, num_seqs, total_q, Hq, Hkv, D, B, num_blocks, max_entries, out,
              workspace, workspace_bytes, stream, kPlanDecodeOnly, kRope);
+}
+
+int lazyattn_decode_shared(const void* q, const void* k_pool, const void* v_pool,
+                           const int32_t* block_table, const uint32_t* block_meta,
+                           const int32_t* kv_lens, const int32_t* q_indptr,
+                           const int32_t* q_positions, double rope_base, int32_t num_seqs,
+                           int32_t total_q, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
+                           int32_t num_blocks, int32_t max_entries, const int32_t* plan,
+                           int32_t plan_items, int32_t plan_slots, void* out, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  if (!plan) return LAZYATTN_ERR_NULL;
+  return run(q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indptr, q_positions,
+             rope_base, num_seqs, total_q, Hq, Hkv, D, B, num_blocks, max_entries, out,
+             workspace, workspace_bytes, stream, kPlanDecodeOnly, kRope, nullptr, nullptr, 0,
+             nullptr, false, plan, plan_items, plan_slots);
+}
+
+size_t lazyattn_decode_shared_workspace_bytes(int32_t num_seqs, int32_t total_q,
+                                              int32_t plan_slots, int32_t Hq, int32_t Hkv,
+                                              int32_t D) {
+  if (num_seqs < 0 || total_q < 0 || plan_slots < 0 || !shape_ok(Hq, Hkv, D, kBlock)) return 0;
+  return ws_layout(num_seqs, plan_slots, Hq, D).total;
 }
 
 int lazyattn_prefill_rotated_pool(const void* q, const void* k_pool, const void* v_pool,

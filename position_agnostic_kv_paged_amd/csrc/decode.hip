@@ -29,6 +29,7 @@
 // from a zeroed workspace chunk so that 0 * NaN never enters the sum. Each item writes a
 // partial (o, m, l); merge_kernel combines the splits of a row.
 #include "decode_body.h"
+#include "decode_plan.h"
 #include <atomic>
 
 namespace lazyattn {
@@ -47,6 +48,27 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 2) void decode_kernel(DecodePara
   const int w = threadIdx.x >> 6;
   decode_items<D, G, PE>(P, TB, lds_all[w], blockIdx.x * kDecodeWaves + w,
                          gridDim.x * kDecodeWaves, n_items);
+}
+
+// Shared-document decode: items from a host plan (decode_plan.h), dealt round-robin to the
+// resident waves like decode_kernel's. A plan whose header does not match the call does
+// nothing here (and merge_kernel then writes zero rows).
+template <int D, int G>
+__global__ __launch_bounds__(kDecodeWaves * 64, 2) void decode_plan_kernel(DecodeParams P,
+                                                                          const int32_t* plan,
+                                                                          int n_plan,
+                                                                          int n_slots) {
+  __shared__ __align__(16) uint8_t lds_all[kDecodeWaves][decode_wave_lds_bytes<D>()];
+  __shared__ DecodeTables<D> TB;
+  if (!share_plan_ok(plan, 16 / G, P.total_q, P.num_seqs)) return;
+  n_plan = min(n_plan, plan[4]);
+  n_slots = min(n_slots, plan[5]);
+  if (n_plan <= 0) return;
+  decode_tables_init<D, 16, kRope>(P, TB, kDecodeWaves * 64);   // R(16): per-block advance
+  __syncthreads();
+  const int w = threadIdx.x >> 6;
+  decode_plan_items<D, G>(P, TB, lds_all[w], plan, n_plan, n_slots,
+                          blockIdx.x * kDecodeWaves + w, gridDim.x * kDecodeWaves);
 }
 
 // Compute units of each device, queried once per device. Host threads calling at the same
@@ -101,6 +123,27 @@ static hipError_t launch_d(const DecodeParams& p, int G, int pe, hipStream_t st)
 
 hipError_t launch_decode(const DecodeParams& p, int D, int G, int pe, hipStream_t st) {
   return D == 128 ? launch_d<128>(p, G, pe, st) : launch_d<64>(p, G, pe, st);
+}
+
+template <int D>
+static hipError_t launch_plan_d(const DecodeParams& p, const int32_t* plan, int n_plan,
+                                int n_slots, int G, hipStream_t st) {
+  dim3 grid(num_cus() * kDecodeWgPerCu), block(kDecodeWaves * 64);
+  switch (G) {
+    case 1: hipLaunchKernelGGL((decode_plan_kernel<D, 1>), grid, block, 0, st, p, plan, n_plan, n_slots); break;
+    case 2: hipLaunchKernelGGL((decode_plan_kernel<D, 2>), grid, block, 0, st, p, plan, n_plan, n_slots); break;
+    case 4: hipLaunchKernelGGL((decode_plan_kernel<D, 4>), grid, block, 0, st, p, plan, n_plan, n_slots); break;
+    case 8: hipLaunchKernelGGL((decode_plan_kernel<D, 8>), grid, block, 0, st, p, plan, n_plan, n_slots); break;
+    case 16: hipLaunchKernelGGL((decode_plan_kernel<D, 16>), grid, block, 0, st, p, plan, n_plan, n_slots); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_plan(const DecodeParams& p, const int32_t* plan, int n_plan,
+                              int n_slots, int D, int G, hipStream_t st) {
+  return D == 128 ? launch_plan_d<128>(p, plan, n_plan, n_slots, G, st)
+                  : launch_plan_d<64>(p, plan, n_plan, n_slots, G, st);
 }
 
 }  // namespace lazyattn

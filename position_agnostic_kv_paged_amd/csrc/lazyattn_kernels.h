@@ -89,6 +89,10 @@ struct MergeParams {
   const int* bps;            // decode split size (written by plan_kernel)
   int smax, mode;
   int total_q;               // rows of out
+  const int32_t* slot_prefix;  // shared-document plan: row r's partials are slots
+                               // [slot_prefix[r], slot_prefix[r + 1]) (else null)
+  int n_slots;                 // partial slots the plan's workspace holds
+  int plan_members;            // rows per plan item this call expects (16 / G, or 1)
 };
 
 // One launch for a batch of any query lengths: prefill items (query tiles, KV split) and
@@ -147,5 +151,8 @@ hipError_t launch_probe_gather(const void* buf, size_t bytes, const int32_t* idx
 // waves of the decode grid (all resident at once); decode items are dealt round-robin to them
 int decode_resident_waves();
 hipError_t launch_decode(const DecodeParams& p, int D, int G, int pe, hipStream_t st);
+// shared-document decode over a host plan (RoPE mode only)
+hipError_t launch_decode_plan(const DecodeParams& p, const int32_t* plan, int n_plan,
+                              int n_slots, int D, int G, hipStream_t st);
 
 }  // namespace lazyattn

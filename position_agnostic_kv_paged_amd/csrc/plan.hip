@@ -132,7 +132,22 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams P) {
   constexpr int CH = 16;                      // splits loaded together
   __shared__ long long s_item0;
   __shared__ int s_splits, s_row;
-  if (P.mode != kPlanDecodeOnly) {
+  if (P.slot_prefix) {
+    // shared-document plan: row x owns slots [prefix[x], prefix[x + 1]) (a plan whose
+    // header does not match gives every row zero slots, hence zero output)
+    if (threadIdx.x == 0) {
+      const int r = blockIdx.x;
+      const int32_t* hdr = P.slot_prefix - 8;
+      const bool ok = hdr[0] == 0x5053414C && hdr[1] == 1 && hdr[2] == P.plan_members &&
+                      hdr[3] == 2 + 4 * P.plan_members && hdr[6] == P.total_q &&
+                      hdr[7] == P.num_seqs;
+      const int a = ok ? max(P.slot_prefix[r], 0) : 0;
+      const int b = ok ? min(P.slot_prefix[r + 1], P.n_slots) : 0;
+      s_splits = max(b - a, 0);
+      s_item0 = a;
+      s_row = r;
+    }
+  } else if (P.mode != kPlanDecodeOnly) {
     // a batch of any query lengths: only single-row sequences have partials, so workgroup
     // x takes sequence x (no search) and prefill sequences leave at once
     if (threadIdx.x == 0) {
@@ -178,7 +193,12 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams P) {
   const long long item0 = s_item0;
   const int h = blockIdx.y * HPB + threadIdx.x / TPH;
   const int d0 = (threadIdx.x % TPH) * 4;
-  if (splits == 0 || h >= P.Hq) return;
+  if (h >= P.Hq) return;
+  if (splits == 0) {
+    if (P.slot_prefix)                        // a row without partials (no key): zero
+      *(u32x2*)(P.out + ((size_t)r * P.Hq + h) * D + d0) = u32x2{0u, 0u};
+    return;
+  }
   auto part = [&](int sp) { return P.partials + ((item0 + sp) * P.Hq + h) * (D + 4); };
   // one pass with online rescaling, CH splits per round of loads
   float M = -INFINITY, L = 0.f;
@@ -236,7 +256,8 @@ hipError_t launch_plan(const PlanParams& p, hipStream_t st) {
 hipError_t launch_merge(const MergeParams& p, int total_q, int D, hipStream_t st) {
   if (total_q == 0) return hipSuccess;
   // one workgroup per query row, or per sequence where only single-row sequences merge
-  const unsigned rows = p.mode == kPlanDecodeOnly ? (unsigned)total_q : (unsigned)p.num_seqs;
+  const unsigned rows = p.mode == kPlanDecodeOnly || p.slot_prefix ? (unsigned)total_q
+                                                                   : (unsigned)p.num_seqs;
   if (D == 128) {
     hipLaunchKernelGGL(merge_kernel<128>, dim3(rows, (p.Hq + 7) / 8), dim3(256), 0, st, p);
   } else {
