@@ -115,7 +115,9 @@ def half_inputs(wl, seqs, dev, pool):
                 kv_lens=i32(wl.kv_lens[seqs]),
                 q_indptr=i32(np.concatenate([[0], np.cumsum(qcnt)])),
                 q_pos=i32(wl.q_pos[rows]), max_entries=max(len(x) for x in ids),
-                out=torch.empty_like(q))
+                out=torch.empty_like(q),
+                host=dict(q_indptr=np.concatenate([[0], np.cumsum(qcnt)]).astype(np.int32),
+                          block_table=bt, words=words))
 
 
 def _counter_rows(run_dir):
@@ -367,6 +369,37 @@ def attention_call(L, fn, wl, a, ws, stream):
                       out=a["out"], workspace=ws, stream=stream)
 
 
+def shared_call(torch, L, kind, wl, a, dev, stream, max_chunk=64):
+    """The same call over a shared-document plan (lazyattn_{prefill,decode}_shared): the
+    plan is built on the host from the batch's tables before any timing (its build time is
+    reported, not part of the timed calls). Returns (call, plan facts)."""
+    h = a["host"]
+    t0 = time.perf_counter()
+    plan = L.decode_share_plan(h["q_indptr"], h["block_table"], h["words"], wl.Hq, wl.Hkv,
+                               single_row_only=kind == "prefill", max_chunk=max_chunk)
+    plan_ms = (time.perf_counter() - t0) * 1e3
+    n_items, n_slots = int(plan[4]), int(plan[5])
+    total_q = int(h["q_indptr"][-1])
+    recs = plan[8 + total_q + 1:].reshape(n_items, -1) if n_items else np.zeros((0, 2), np.int32)
+    n_entries = int(h["block_table"][-1]) if kind == "decode" else sum(
+        int(h["block_table"][s + 1] - h["block_table"][s])
+        for s in range(len(h["q_indptr"]) - 1) if h["q_indptr"][s + 1] - h["q_indptr"][s] == 1)
+    d_plan = torch.from_numpy(plan).to(dev)
+    ws = torch.empty(max(16, L.shared_workspace_bytes(kind, a["kv_lens"].numel(), total_q,
+                                                      a["max_entries"], n_slots, wl.Hq,
+                                                      wl.Hkv, wl.D)),
+                     dtype=torch.uint8, device=dev)
+    fn = L.prefill_shared if kind == "prefill" else L.decode_shared
+    call = lambda: fn(a["q"], a["k_pool"], a["v_pool"], a["block_table"], a["block_meta"],  # noqa
+                      a["kv_lens"], a["q_indptr"], a["q_pos"], wl.rope_base, a["max_entries"],
+                      d_plan, n_items, n_slots, out=a["out"], workspace=ws, stream=stream)
+    facts = {"plan_host_ms": plan_ms, "items": n_items,
+             "grouped_items": int((recs[:, 1] > 1).sum()) if n_items else 0,
+             "decode_blocks_read_frac": float(recs[:, 0].sum() / max(n_entries, 1))
+             if n_items else 0.0}
+    return call, facts
+
+
 def workspace_for(torch, L, kind, wl, a, dev):
     return torch.empty(L.workspace_bytes(kind, a["kv_lens"].numel(), a["q"].shape[0],
                                          a["max_entries"], wl.Hq, wl.Hkv, wl.D),
@@ -391,6 +424,11 @@ def decode_control(torch, L, name, dev, stream, reps, warmup, flush):
             key = label if label == "no_reuse" else mode
             out[key] = {"ms": st, "gbs": nbytes / (st["median"] / 1e3) / 1e9,
                         "frac_hbm_peak": nbytes / (st["median"] / 1e3) / 1e9 / PEAK_HBM_GBS}
+        if not no_reuse:                                  # over a shared-document plan
+            fs, facts = shared_call(torch, L, "decode", wl, a, dev, stream)
+            st = timed(torch, stream, fs, reps, warmup)
+            out["shared_plan"] = dict(facts, ms=st, gbs=nbytes / (st["median"] / 1e3) / 1e9,
+                                      speedup=out["warm"]["ms"]["median"] / st["median"])
         del pool, a, ws
         torch.cuda.empty_cache()
     out["algorithmic_gb"] = nbytes / 1e9
@@ -420,6 +458,8 @@ def main():
                          "outside the timed calls)")
     ap.add_argument("--no-ablation", action="store_true",
                     help="skip the rotation ablation and the variants")
+    ap.add_argument("--no-shared", action="store_true",
+                    help="skip the shared-document plan timings")
     ap.add_argument("--no-controls", action="store_true",
                     help="skip the decode configurations' cold and no-reuse controls")
     ap.add_argument("--counters", action="store_true",
@@ -565,6 +605,27 @@ def main():
                               "frac_overlapped_roofline": roof_us / 1e3 / step_ms,
                               "serial_roofline_us": (pre_flops / (PEAK_MFMA_TFLOPS * 1e12)
                                                      + dbytes / (PEAK_HBM_GBS * 1e9)) * 1e6}
+    # ---- the same step and decode half over a shared-document plan: the decode rows that
+    # read the same runs of blocks share their loads (lazyattn_*_shared). The plan is built
+    # on the host from the batch's tables before timing; its build time is reported ----
+    if dec_seqs and not args.no_shared:
+        fs, facts = shared_call(torch, L, step_kind, wl, a_all, dev, stream)
+        st = timed(torch, stream, fs, args.reps, args.warmup)
+        sh = dict(facts, call=f"{'lazyattn_prefill_shared' if pre_seqs else 'lazyattn_decode_shared'}"
+                              " over the whole batch", ms=st["mean"], ms_pct=st,
+                  value=(pre_flops + dec_flops) / (st["mean"] / 1e3) / 1e12,
+                  speedup_vs_step=step_ms / st["mean"])
+        if pre_seqs and "decode" in halves:
+            seqs, fn, a, ws, f = halves["decode"]
+            fd, fdf = shared_call(torch, L, "decode", wl, a, dev, stream)
+            std = timed(torch, stream, fd, args.reps, args.warmup)
+            sh["decode_half"] = dict(fdf, ms=std["mean"], ms_pct=std,
+                                     gbs=dbytes / (std["mean"] / 1e3) / 1e9,
+                                     speedup=line["decode"]["ms"] / std["mean"])
+        sh["note"] = ("the plan groups up to 16/G decode rows that read the same run of "
+                      "blocks into one item, so each block is loaded once for all of them; "
+                      "value and gbs count the same algorithmic work as the plain call")
+        line["shared_plan"] = sh
     if roofs:
         t_dom, roof = max(roofs, key=lambda r: r[0])
         roof["frac"] = roof["achieved"] / roof["peak"]

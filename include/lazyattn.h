@@ -171,6 +171,12 @@ int lazyattn_decode(const void* q, const void* k_pool, const void* v_pool,
  * and indices inside it are clamped to the call's arrays. Workspace:
  * lazyattn_decode_shared_workspace_bytes(num_seqs, total_q, plan_slots, Hq, Hkv, D).
  * Errors as lazyattn_decode, plus NULL plan and ARG for negative counts.
+ *
+ * lazyattn_prefill_shared -- lazyattn_prefill (RoPE) with the decode rows of the batch (the
+ * rows of single-row sequences) run over a plan built with single_row_only = 1; the prefill
+ * rows are computed as by lazyattn_prefill. Workspace:
+ * lazyattn_prefill_shared_workspace_bytes(num_seqs, total_q, max_entries, plan_slots, Hq,
+ * Hkv, D).
  */
 int lazyattn_decode_share_plan(const int32_t* q_indptr, const int32_t* block_table,
                                const uint32_t* block_meta, int32_t num_seqs, int32_t total_q,
@@ -188,6 +194,17 @@ int lazyattn_decode_shared(const void* q, const void* k_pool, const void* v_pool
 size_t lazyattn_decode_shared_workspace_bytes(int32_t num_seqs, int32_t total_q,
                                               int32_t plan_slots, int32_t Hq, int32_t Hkv,
                                               int32_t D);
+int lazyattn_prefill_shared(const void* q, const void* k_pool, const void* v_pool,
+                            const int32_t* block_table, const uint32_t* block_meta,
+                            const int32_t* kv_lens, const int32_t* q_indptr,
+                            const int32_t* q_positions, double rope_base, int32_t num_seqs,
+                            int32_t total_q, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
+                            int32_t num_blocks, int32_t max_entries, const int32_t* plan,
+                            int32_t plan_items, int32_t plan_slots, void* out,
+                            void* workspace, size_t workspace_bytes, void* stream);
+size_t lazyattn_prefill_shared_workspace_bytes(int32_t num_seqs, int32_t total_q,
+                                               int32_t max_entries, int32_t plan_slots,
+                                               int32_t Hq, int32_t Hkv, int32_t D);
 
 /*
  * lazyattn_decode_noalloc -- lazyattn_decode for callers that cannot allocate device memory

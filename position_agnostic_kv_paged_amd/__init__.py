@@ -6,4 +6,4 @@ from .api import (prefill, decode, prefill_rotated_pool, decode_rotated_pool,  #
                   workspace_bytes, probe_cus, probe_mfma, probe_read, probe_gather,
                   ingest_kv,
                   PoolIndex, llama31_inv_freq, decode_noalloc, decode_share_plan,
-                  decode_shared, BLOCK)
+                  decode_shared, prefill_shared, shared_workspace_bytes, BLOCK)

@@ -24,6 +24,7 @@ EXPORTED = [
     "lazyattn_decode_workspace_bytes", "lazyattn_encode_meta", "lazyattn_debug_decode_meta",
     "lazyattn_llama31_inv_freq", "lazyattn_decode_noalloc", "lazyattn_decode_share_plan",
     "lazyattn_decode_shared", "lazyattn_decode_shared_workspace_bytes",
+    "lazyattn_prefill_shared", "lazyattn_prefill_shared_workspace_bytes",
     "lazyattn_status_str", "lazyattn_version",
 ]
 
@@ -71,6 +72,10 @@ def lib():
     L.lazyattn_decode_shared.restype = ctypes.c_int
     L.lazyattn_decode_shared_workspace_bytes.argtypes = [i32] * 6
     L.lazyattn_decode_shared_workspace_bytes.restype = ctypes.c_size_t
+    L.lazyattn_prefill_shared.argtypes = attn[:17] + [vp, i32, i32] + attn[17:]
+    L.lazyattn_prefill_shared.restype = ctypes.c_int
+    L.lazyattn_prefill_shared_workspace_bytes.argtypes = [i32] * 7
+    L.lazyattn_prefill_shared_workspace_bytes.restype = ctypes.c_size_t
     L.lazyattn_decode_share_plan.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp,
                                              ctypes.c_int64, ctypes.POINTER(ctypes.c_int64)]
     L.lazyattn_decode_share_plan.restype = ctypes.c_int

@@ -150,28 +150,55 @@ def decode_share_plan(q_indptr, block_table, block_meta, Hq, Hkv, single_row_onl
     return plan
 
 
-def decode_shared(q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indptr, q_pos,
-                  rope_base, max_entries, plan, plan_items, plan_slots, out=None,
-                  workspace=None, stream=None):
-    """lazyattn_decode_shared: decode over a shared-document plan (`plan` a device int32
-    copy of decode_share_plan's result, plan_items / plan_slots its header [4] / [5])."""
+def shared_workspace_bytes(kind, num_seqs, total_q, max_entries, plan_slots, Hq, Hkv, D):
+    """lazyattn_{prefill,decode}_shared_workspace_bytes."""
+    if kind == "prefill":
+        return int(lib().lazyattn_prefill_shared_workspace_bytes(
+            num_seqs, total_q, int(max_entries), int(plan_slots), Hq, Hkv, D))
+    return int(lib().lazyattn_decode_shared_workspace_bytes(num_seqs, total_q, int(plan_slots),
+                                                            Hq, Hkv, D))
+
+
+def _shared(kind, q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indptr, q_pos,
+            rope_base, max_entries, plan, plan_items, plan_slots, out, workspace, stream):
     import torch
     total_q, Hq, D, num_blocks, Hkv, B = _dims(q, k_pool)
     num_seqs = kv_lens.numel()
     if out is None:
         out = torch.empty_like(q)
-    need = lib().lazyattn_decode_shared_workspace_bytes(num_seqs, total_q, int(plan_slots), Hq,
-                                                        Hkv, D)
     if workspace is None:
+        need = shared_workspace_bytes(kind, num_seqs, total_q, max_entries, plan_slots, Hq,
+                                      Hkv, D)
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    rc = lib().lazyattn_decode_shared(
+    name = f"lazyattn_{kind}_shared"
+    rc = getattr(lib(), name)(
         _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(block_meta),
         _ptr(kv_lens), _ptr(q_indptr), _ptr(q_pos), float(rope_base), num_seqs, total_q, Hq,
         Hkv, D, B, num_blocks, int(max_entries), _ptr(plan), int(plan_items), int(plan_slots),
         _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream))
-    check(rc, "lazyattn_decode_shared")
+    check(rc, name)
     return out
+
+
+def decode_shared(q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indptr, q_pos,
+                  rope_base, max_entries, plan, plan_items, plan_slots, out=None,
+                  workspace=None, stream=None):
+    """lazyattn_decode_shared: decode over a shared-document plan (`plan` a device int32
+    copy of decode_share_plan's result, plan_items / plan_slots its header [4] / [5])."""
+    return _shared("decode", q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indptr,
+                   q_pos, rope_base, max_entries, plan, plan_items, plan_slots, out, workspace,
+                   stream)
+
+
+def prefill_shared(q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indptr, q_pos,
+                   rope_base, max_entries, plan, plan_items, plan_slots, out=None,
+                   workspace=None, stream=None):
+    """lazyattn_prefill_shared: a batch of any query lengths, its decode rows over a plan
+    built with single_row_only=True."""
+    return _shared("prefill", q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indptr,
+                   q_pos, rope_base, max_entries, plan, plan_items, plan_slots, out, workspace,
+                   stream)
 
 
 def llama31_inv_freq(D, base=500000.0, factor=8.0, low_freq_factor=1.0, high_freq_factor=4.0,

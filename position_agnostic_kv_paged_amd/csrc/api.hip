@@ -138,8 +138,7 @@ int run(const void* q, const void* k_pool, const void* v_pool, const int32_t* bl
     return LAZYATTN_ERR_NULL;
   const bool shared = share_plan != nullptr;  // shared-document decode over a host plan
   if (shared) {
-    if (mode != kPlanDecodeOnly || pe != kRope || inv_freq || fit_workspace)
-      return LAZYATTN_ERR_ARG;
+    if (pe != kRope || inv_freq || fit_workspace) return LAZYATTN_ERR_ARG;
     if (plan_items < 0 || plan_slots < 0) return LAZYATTN_ERR_ARG;
     if (!aligned(share_plan, 4)) return LAZYATTN_ERR_ALIGN;
   }
@@ -176,7 +175,7 @@ int run(const void* q, const void* k_pool, const void* v_pool, const int32_t* bl
                                 : mixed_decode_split(num_seqs, work_heads(Hq, Hkv), max_entries);
   if (ds.smax <= 0) return LAZYATTN_ERR_WORKSPACE;
   CallPlan cp = plan_call(mode, num_seqs, total_q, max_entries, Hq, Hkv, D, ds);
-  if (shared) cp.L = ws_layout(num_seqs, plan_slots, Hq, D);    // one partial per plan slot
+  if (shared) cp.L = ws_layout(num_seqs, plan_slots, Hq, D, cp.pf_slots);   // a partial per slot
   if (workspace_bytes < cp.L.total) return LAZYATTN_ERR_WORKSPACE;
   if (num_seqs == 0 || total_q == 0) return LAZYATTN_OK;
 
@@ -227,7 +226,7 @@ int run(const void* q, const void* k_pool, const void* v_pool, const int32_t* bl
                     num_blocks, cp.pf_item_cap, scale_log2, freqs, slopes, Hkv, kv_group,
                     r / 16, stored_offsets, total_q, pf_kc, cp.pf_smax, pf_partials};
     MixedParams Mp{P, dec_prefix, partials, dec_bps, ds.smax, Dp.rowsplit_cap,
-                   8 * kDecChunkWaves};
+                   8 * kDecChunkWaves, share_plan, plan_items, plan_slots};
     if (launch_mixed(Mp, D, G, pe, st) != hipSuccess) return LAZYATTN_ERR_LAUNCH;
     // split tiles: their partials are merged once every split has finished (the launch
     // boundary orders the partial stores before the merge's loads)
@@ -327,6 +326,32 @@ int lazyattn_decode_shared(const void* q, const void* k_pool, const void* v_pool
              rope_base, num_seqs, total_q, Hq, Hkv, D, B, num_blocks, max_entries, out,
              workspace, workspace_bytes, stream, kPlanDecodeOnly, kRope, nullptr, nullptr, 0,
              nullptr, false, plan, plan_items, plan_slots);
+}
+
+int lazyattn_prefill_shared(const void* q, const void* k_pool, const void* v_pool,
+                            const int32_t* block_table, const uint32_t* block_meta,
+                            const int32_t* kv_lens, const int32_t* q_indptr,
+                            const int32_t* q_positions, double rope_base, int32_t num_seqs,
+                            int32_t total_q, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
+                            int32_t num_blocks, int32_t max_entries, const int32_t* plan,
+                            int32_t plan_items, int32_t plan_slots, void* out,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  if (!plan) return LAZYATTN_ERR_NULL;
+  return run(q, k_pool, v_pool, block_table, block_meta, kv_lens, q_indptr, q_positions,
+             rope_base, num_seqs, total_q, Hq, Hkv, D, B, num_blocks, max_entries, out,
+             workspace, workspace_bytes, stream, kPlanMixed, kRope, nullptr, nullptr, 0,
+             nullptr, false, plan, plan_items, plan_slots);
+}
+
+size_t lazyattn_prefill_shared_workspace_bytes(int32_t num_seqs, int32_t total_q,
+                                               int32_t max_entries, int32_t plan_slots,
+                                               int32_t Hq, int32_t Hkv, int32_t D) {
+  if (num_seqs < 0 || total_q < 0 || max_entries < 0 || plan_slots < 0 ||
+      !shape_ok(Hq, Hkv, D, kBlock))
+    return 0;
+  const DecodeSplit ds = mixed_decode_split(num_seqs, work_heads(Hq, Hkv), max_entries);
+  const CallPlan cp = plan_call(kPlanMixed, num_seqs, total_q, max_entries, Hq, Hkv, D, ds);
+  return ws_layout(num_seqs, plan_slots, Hq, D, cp.pf_slots).total;
 }
 
 size_t lazyattn_decode_shared_workspace_bytes(int32_t num_seqs, int32_t total_q,

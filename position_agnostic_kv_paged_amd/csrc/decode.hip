@@ -68,7 +68,8 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 2) void decode_plan_kernel(Decod
   __syncthreads();
   const int w = threadIdx.x >> 6;
   decode_plan_items<D, G>(P, TB, lds_all[w], plan, n_plan, n_slots,
-                          blockIdx.x * kDecodeWaves + w, gridDim.x * kDecodeWaves);
+                          blockIdx.x * kDecodeWaves + w, gridDim.x * kDecodeWaves,
+                          n_plan * P.Hkv);
 }
 
 // Compute units of each device, queried once per device. Host threads calling at the same

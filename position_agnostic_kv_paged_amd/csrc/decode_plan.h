@@ -29,13 +29,15 @@ __device__ __forceinline__ bool share_plan_ok(const int32_t* plan, int M, int to
          plan[6] == total_q && plan[7] == num_seqs;
 }
 
-// Items gw, gw + W, ... of the n_plan x Hkv (plan item, KV head) pairs, by the calling wave.
-// TB must hold R(16) in adv (decode_tables_init with G = 16). Only the RoPE mode.
+// Items gw, gw + W, ... below `end` of the n_plan x Hkv (plan item, KV head) pairs, by the
+// calling wave. TB must hold R(16) in adv (decode_tables_init with G = 16). Only the RoPE
+// mode.
 template <int D, int G>
 __device__ __forceinline__ void decode_plan_items(const DecodeParams& P,
                                                   const DecodeTables<D>& TB, uint8_t* lds,
                                                   const int32_t* plan, const int n_plan,
-                                                  const int n_slots, const int gw, const int W) {
+                                                  const int n_slots, const int gw, const int W,
+                                                  const int end) {
   constexpr int M = 16 / G;                    // member rows per item
   constexpr int REC = 2 + 4 * M;
   constexpr int NC = D / 32;
@@ -49,7 +51,7 @@ __device__ __forceinline__ void decode_plan_items(const DecodeParams& P,
   const int i16 = lane & 15, q4 = lane >> 4;
   const int mi = i16 / G, g = i16 % G;         // this lane's column: member mi, head g
   const int32_t* recs = plan + kSharePlanHeader + P.total_q + 1;
-  const int n_items = n_plan * P.Hkv;
+  const int n_items = min(n_plan * P.Hkv, end);
   int dofs[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) dofs[c] = 32 * c + 8 * q4;

@@ -105,6 +105,8 @@ struct MixedParams {
   const int* bps;            // decode split size (written by plan_kernel)
   int smax, rowsplit_cap;
   int dec_chunk;             // decode items per workgroup (a multiple of its 8 waves)
+  const int32_t* plan;       // shared-document plan for the decode rows (or null)
+  int plan_items, plan_slots;
 };
 hipError_t launch_mixed(const MixedParams& p, int D, int G, int pe, hipStream_t st);
 // merge of the prefill KV-split partials (launched after the mixed kernel when splits may

@@ -20,6 +20,7 @@
 // measured slower on the mixed 70B-shaped batch.) The grid is sized from host bounds;
 // workgroups past their queue's length leave at once.
 #include "decode_body.h"
+#include "decode_plan.h"
 #include "prefill_body.h"
 
 namespace lazyattn {
@@ -51,7 +52,13 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void mixed_kernel(MixedParam
                         M.rowsplit_cap};
   const int q = blockIdx.x & 7, c = blockIdx.x >> 3;
   const int n_pf = P.pf_prefix[P.num_seqs];                       // prefill items per KV head
-  const int n_dec = min(M.dec_prefix[P.num_seqs], M.rowsplit_cap) * P.Hkv;
+  // decode work: the plan's (item, KV head) pairs, or the row-splits of plan_kernel
+  const bool shared = M.plan != nullptr;
+  const bool plan_ok = shared && share_plan_ok(M.plan, 16 / G, P.total_q, P.num_seqs);
+  const int n_plan = plan_ok ? min(M.plan_items, M.plan[4]) : 0;
+  const int n_slots = plan_ok ? min(M.plan_slots, M.plan[5]) : 0;
+  const int n_dec = shared ? n_plan * P.Hkv
+                           : min(M.dec_prefix[P.num_seqs], M.rowsplit_cap) * P.Hkv;
   const int n_dchunks = (n_dec + M.dec_chunk - 1) / M.dec_chunk;
   const long long np_all = (long long)n_pf * P.Hkv;
   const int p_lo = (int)(np_all * q / 8), p_hi = (int)(np_all * (q + 1) / 8);
@@ -60,10 +67,19 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void mixed_kernel(MixedParam
   if (c >= n_p + n_d) return;                                     // uniform
   if (c >= n_p) {                                                 // decode chunk q + 8 dc
     const int dc = c - n_p;
-    decode_tables_init<D, G, PE>(Dp, TB, kPrefillWaves * 64);
-    __syncthreads();
     const int w = threadIdx.x >> 6;
     const int first = (q + 8 * dc) * M.dec_chunk;
+    if constexpr (PE == kRope) {
+      if (shared) {                                               // (uniform)
+        decode_tables_init<D, 16, kRope>(Dp, TB, kPrefillWaves * 64);   // R(16) advance
+        __syncthreads();
+        decode_plan_items<D, G>(Dp, TB, decode_wave_buf<D>(SM, w), M.plan, n_plan, n_slots,
+                                first + w, kPrefillWaves, min(first + M.dec_chunk, n_dec));
+        return;
+      }
+    }
+    decode_tables_init<D, G, PE>(Dp, TB, kPrefillWaves * 64);
+    __syncthreads();
     decode_items<D, G, PE>(Dp, TB, decode_wave_buf<D>(SM, w), first + w, kPrefillWaves,
                            min(first + M.dec_chunk, n_dec));
   } else {                                                       // prefill item
@@ -139,7 +155,8 @@ static hipError_t launch_d(const MixedParams& p, int G, int pe, int nwg, hipStre
 hipError_t launch_mixed(const MixedParams& p, int D, int G, int pe, hipStream_t st) {
   // bounds: every (KV head, prefill item) and every decode chunk, spread over 8 queues
   const long long np = (long long)p.pf.pf_item_cap * p.pf.Hkv;
-  const long long nd = ((long long)p.rowsplit_cap * p.pf.Hkv + p.dec_chunk - 1) / p.dec_chunk;
+  const long long nd = ((p.plan ? (long long)p.plan_items : (long long)p.rowsplit_cap) *
+                            p.pf.Hkv + p.dec_chunk - 1) / p.dec_chunk;
   const long long per_queue = (np + 7) / 8 + (nd + 7) / 8 + 1;
   if (per_queue * 8 > INT32_MAX / 2) return hipErrorInvalidValue;
   const int nwg = (int)(per_queue * 8);

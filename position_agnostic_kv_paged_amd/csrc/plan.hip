@@ -133,17 +133,25 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams P) {
   __shared__ long long s_item0;
   __shared__ int s_splits, s_row;
   if (P.slot_prefix) {
-    // shared-document plan: row x owns slots [prefix[x], prefix[x + 1]) (a plan whose
-    // header does not match gives every row zero slots, hence zero output)
+    // shared-document plan: row r owns slots [prefix[r], prefix[r + 1]) (a plan whose
+    // header does not match gives every row zero slots, hence zero output). A decode call
+    // runs one workgroup per row; a mixed call one per sequence, and only the row of a
+    // single-row sequence is merged here (s_splits = -1: nothing to do)
     if (threadIdx.x == 0) {
-      const int r = blockIdx.x;
+      int r = blockIdx.x;
+      bool mine = true;
+      if (P.mode != kPlanDecodeOnly) {
+        const int seq = blockIdx.x;
+        r = P.q_indptr[seq];
+        mine = (P.q_indptr[seq + 1] - r == 1) & (r < P.total_q);
+      }
       const int32_t* hdr = P.slot_prefix - 8;
       const bool ok = hdr[0] == 0x5053414C && hdr[1] == 1 && hdr[2] == P.plan_members &&
                       hdr[3] == 2 + 4 * P.plan_members && hdr[6] == P.total_q &&
                       hdr[7] == P.num_seqs;
-      const int a = ok ? max(P.slot_prefix[r], 0) : 0;
-      const int b = ok ? min(P.slot_prefix[r + 1], P.n_slots) : 0;
-      s_splits = max(b - a, 0);
+      const int a = ok && mine ? max(P.slot_prefix[r], 0) : 0;
+      const int b = ok && mine ? min(P.slot_prefix[r + 1], P.n_slots) : 0;
+      s_splits = mine ? max(b - a, 0) : -1;
       s_item0 = a;
       s_row = r;
     }
@@ -193,7 +201,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams P) {
   const long long item0 = s_item0;
   const int h = blockIdx.y * HPB + threadIdx.x / TPH;
   const int d0 = (threadIdx.x % TPH) * 4;
-  if (h >= P.Hq) return;
+  if (h >= P.Hq || splits < 0) return;
   if (splits == 0) {
     if (P.slot_prefix)                        // a row without partials (no key): zero
       *(u32x2*)(P.out + ((size_t)r * P.Hq + h) * D + d0) = u32x2{0u, 0u};
@@ -256,8 +264,7 @@ hipError_t launch_plan(const PlanParams& p, hipStream_t st) {
 hipError_t launch_merge(const MergeParams& p, int total_q, int D, hipStream_t st) {
   if (total_q == 0) return hipSuccess;
   // one workgroup per query row, or per sequence where only single-row sequences merge
-  const unsigned rows = p.mode == kPlanDecodeOnly || p.slot_prefix ? (unsigned)total_q
-                                                                   : (unsigned)p.num_seqs;
+  const unsigned rows = p.mode == kPlanDecodeOnly ? (unsigned)total_q : (unsigned)p.num_seqs;
   if (D == 128) {
     hipLaunchKernelGGL(merge_kernel<128>, dim3(rows, (p.Hq + 7) / 8), dim3(256), 0, st, p);
   } else {

@@ -13,14 +13,15 @@ from tests.gpu_util import compare, say, words_for  # noqa: E402
 from tests.test_parity_gpu import _mini_cases, _random_batch  # noqa: E402
 
 
-def run_shared(wl, max_chunk=64, plan_edit=None, repeat=1):
-    """Plan on the host, copy the plan to the device, call lazyattn_decode_shared."""
+def run_shared(wl, max_chunk=64, plan_edit=None, repeat=1, kind="decode"):
+    """Plan on the host, copy the plan to the device, call lazyattn_{decode,prefill}_shared
+    (a prefill call plans the rows of single-row sequences only)."""
     import torch
     import position_agnostic_kv_paged_amd as L
     t = wl.to_device("cuda")
     words = words_for(wl)
     plan = L.decode_share_plan(wl.q_indptr, wl.block_table, words, wl.Hq, wl.Hkv,
-                               max_chunk=max_chunk)
+                               single_row_only=kind == "prefill", max_chunk=max_chunk)
     n_items, n_slots = int(plan[4]), int(plan[5])
     if plan_edit is not None:
         plan = plan_edit(plan.copy())
@@ -29,7 +30,8 @@ def run_shared(wl, max_chunk=64, plan_edit=None, repeat=1):
     max_entries = max(len(x) for x in wl.seq_block_ids)
     outs = []
     for _ in range(repeat):
-        out = L.decode_shared(t["q"], t["k_pool"], t["v_pool"], t["block_table"], meta,
+        fn = L.prefill_shared if kind == "prefill" else L.decode_shared
+        out = fn(t["q"], t["k_pool"], t["v_pool"], t["block_table"], meta,
                               t["kv_lens"], t["q_indptr"], t["q_pos"], wl.rope_base,
                               max_entries, d_plan, n_items, n_slots)
         torch.cuda.synchronize()
@@ -117,3 +119,39 @@ def test_shared_mismatched_plan_gives_zero_rows(edit):
         return p
     got, _ = run_shared(wl, plan_edit=spoil)
     assert np.all(got == 0.0)
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("q_scale", [1.0, 4.0])
+def test_shared_prefill_call_mixed_batch(q_scale):
+    """The whole mixed batch in one lazyattn_prefill_shared call (prefill tiles plus the
+    decode rows over the plan), every row."""
+    wl = make("mixed-64q8kv-4p96d", q_scale=q_scale)
+    got, grouped = run_shared(wl, max_chunk=64, kind="prefill")
+    say(f"{wl.name} prefill_shared: {grouped} grouped decode items, every row")
+    assert grouped > 0
+    compare(got, oracle_out(wl), f"{wl.name}/prefill-shared")
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_shared_prefill_call_random_layouts(seed):
+    wl = _random_batch(seed)
+    if wl.total_q == 0:
+        return
+    got, _ = run_shared(wl, max_chunk=int(np.random.default_rng(seed).choice([4, 8, 64])),
+                        kind="prefill")
+    compare(got, oracle_out(wl), f"random{seed}/prefill-shared")
+
+
+def test_shared_prefill_call_small_mixed_and_empty():
+    """Prefill, decode and empty requests in one call; two decode rows share a document."""
+    d = [Segment("doc", 11, doc=0), Segment("doc", 60, doc=1), Segment("private", 120, tokens=9)]
+    reqs = [RequestLayout(d, 9), RequestLayout(d, 1), RequestLayout([], 0),
+            RequestLayout([Segment("doc", 300, doc=1), Segment("doc", 364, doc=0),
+                           Segment("private", 430, tokens=2)], 1),
+            RequestLayout([], 1, np.array([5]))]
+    wl = build("small-mixed-shared", 16, 2, 128, 16, 10000.0, 2, 64, reqs, seed=13,
+               q_scale=3.0)
+    got, grouped = run_shared(wl, max_chunk=4, kind="prefill")
+    assert grouped > 0
+    compare(got, oracle_out(wl), "small-mixed/prefill-shared")
