@@ -8,7 +8,7 @@ import ctypes
 
 import numpy as np
 
-from ._lib import lib, check, PoolStats
+from ._lib import lib, check, PoolStats, ERR_NOSPACE
 
 BLOCK = 16
 
@@ -142,12 +142,19 @@ def decode_share_plan(q_indptr, block_table, block_meta, Hq, Hkv, single_row_onl
     args = (qi.ctypes.data, bt.ctypes.data, bm.ctypes.data if bm.size else None, len(qi) - 1,
             int(qi[-1]), int(Hq), int(Hkv), int(bool(single_row_only)), int(max_chunk),
             int(waves))
-    check(lib().lazyattn_decode_share_plan(*args, None, 0, ctypes.byref(n)),
-          "lazyattn_decode_share_plan")
-    plan = np.zeros(n.value, dtype=np.int32)
-    check(lib().lazyattn_decode_share_plan(*args, plan.ctypes.data, n.value, ctypes.byref(n)),
-          "lazyattn_decode_share_plan")
-    return plan
+    # one planner call with a generous guess of the length; a second only if it was short
+    G = Hq // Hkv
+    rec = 2 + 4 * (16 // G if G <= 16 else 1)
+    lanes = max(1, int(waves) // max(1, Hkv if G <= 16 else Hq // 16))
+    guess = 8 + len(qi) + rec * (int(bt[-1]) // 4 + int(qi[-1]) + 2 * lanes + 64)
+    plan = np.zeros(guess, dtype=np.int32)
+    rc = lib().lazyattn_decode_share_plan(*args, plan.ctypes.data, guess, ctypes.byref(n))
+    if rc == ERR_NOSPACE:
+        plan = np.zeros(n.value, dtype=np.int32)
+        rc = lib().lazyattn_decode_share_plan(*args, plan.ctypes.data, n.value,
+                                              ctypes.byref(n))
+    check(rc, "lazyattn_decode_share_plan")
+    return plan[: n.value]
 
 
 def shared_workspace_bytes(kind, num_seqs, total_q, max_entries, plan_slots, Hq, Hkv, D):

@@ -23,7 +23,6 @@
 
 #include <algorithm>
 #include <cstdint>
-#include <unordered_map>
 #include <vector>
 
 namespace {
@@ -70,13 +69,32 @@ extern "C" int lazyattn_decode_share_plan(const int32_t* q_indptr, const int32_t
   }
   auto id_of = [&](const Row& r, int32_t e) { return (int32_t)(block_meta[r.e0 + e] & kIdMask); };
 
-  // block id -> (planned row, entry), in ascending (row, entry) order
-  std::unordered_map<int32_t, std::vector<std::pair<int32_t, int32_t>>> users;
-  std::vector<std::vector<uint8_t>> taken(rows.size());
-  for (size_t i = 0; i < rows.size(); ++i) {
-    taken[i].assign((size_t)rows[i].T, 0);
-    for (int32_t e = 0; e < rows[i].T; ++e) users[id_of(rows[i], e)].push_back({(int32_t)i, e});
+  // block id -> (planned row, entry) users, as CSR over the id range, each id's users in
+  // ascending (row, entry) order; taken[] flags entries already in an item (flat per row)
+  const size_t n_ids = (size_t)kIdMask + 2;
+  std::vector<int64_t> row_base(rows.size() + 1, 0);
+  for (size_t i = 0; i < rows.size(); ++i) row_base[i + 1] = row_base[i] + rows[i].T;
+  const int64_t n_ent = row_base[rows.size()];
+  std::vector<int32_t> first(n_ids, 0);
+  for (size_t i = 0; i < rows.size(); ++i)
+    for (int32_t e = 0; e < rows[i].T; ++e) first[(size_t)id_of(rows[i], e) + 1]++;
+  for (size_t k = 1; k < n_ids; ++k) first[k] += first[k - 1];
+  std::vector<int32_t> u_row((size_t)n_ent), u_ent((size_t)n_ent);
+  {
+    std::vector<int32_t> fill(first.begin(), first.end() - 1);
+    for (size_t i = 0; i < rows.size(); ++i)
+      for (int32_t e = 0; e < rows[i].T; ++e) {
+        const int32_t k = fill[(size_t)id_of(rows[i], e)]++;
+        u_row[(size_t)k] = (int32_t)i;
+        u_ent[(size_t)k] = e;
+      }
   }
+  std::vector<uint8_t> taken((size_t)n_ent, 0);
+  auto is_taken = [&](int32_t i, int32_t e) { return taken[(size_t)(row_base[i] + e)] != 0; };
+  // users before cursor[id] are taken (entries never become free again) or belong to rows
+  // already planned (an untaken entry of an earlier row found no partner for a run of
+  // kMinRun, and runs only shorten as entries are taken): the cursor only moves forward
+  std::vector<int32_t> cursor(first.begin(), first.end() - 1);
 
   struct Member {
     int32_t ri, e;
@@ -92,24 +110,28 @@ extern "C" int lazyattn_decode_share_plan(const int32_t* q_indptr, const int32_t
     const Row& a = rows[i];
     int32_t e = 0;
     while (e < a.T) {
-      if (taken[i][e]) {
+      if (is_taken(i, e)) {
         ++e;
         continue;
       }
+      const int32_t id = id_of(a, e);
+      int32_t& cur = cursor[(size_t)id];
+      const int32_t end = first[(size_t)id + 1];
+      while (cur < end && (u_row[(size_t)cur] < i || is_taken(u_row[(size_t)cur], u_ent[(size_t)cur])))
+        ++cur;
       std::vector<std::pair<Member, int32_t>> cand;   // (member, run length)
-      for (const auto& u : users[id_of(a, e)]) {
-        const int32_t j = u.first, f = u.second;
-        if (j == i || taken[j][f]) continue;
+      for (int32_t k = cur; k < end && (int)cand.size() < M - 1; ++k) {
+        const int32_t j = u_row[(size_t)k], f = u_ent[(size_t)k];
+        if (j <= i || is_taken(j, f)) continue;
         bool dup = false;
         for (const auto& c : cand) dup |= c.first.ri == j;
         if (dup) continue;
-        const Row& b = rows[j];
+        const Row& b = rows[(size_t)j];
         int32_t len = 0;
-        while (len < max_chunk && e + len < a.T && f + len < b.T && !taken[i][e + len] &&
-               !taken[j][f + len] && id_of(a, e + len) == id_of(b, f + len))
+        while (len < max_chunk && e + len < a.T && f + len < b.T && !is_taken(i, e + len) &&
+               !is_taken(j, f + len) && id_of(a, e + len) == id_of(b, f + len))
           ++len;
         if (len >= kMinRun) cand.push_back({Member{j, f}, len});
-        if ((int)cand.size() == M - 1) break;
       }
       if (cand.empty()) {
         ++e;
@@ -120,7 +142,7 @@ extern "C" int lazyattn_decode_share_plan(const int32_t* q_indptr, const int32_t
       Item it{len, {Member{i, e}}};
       for (const auto& c : cand) it.m.push_back(c.first);
       for (const auto& m : it.m)
-        for (int32_t k = 0; k < len; ++k) taken[m.ri][m.e + k] = 1;
+        for (int32_t k = 0; k < len; ++k) taken[(size_t)(row_base[m.ri] + m.e + k)] = 1;
       items.push_back(std::move(it));
       e += len;
     }
@@ -129,12 +151,12 @@ extern "C" int lazyattn_decode_share_plan(const int32_t* q_indptr, const int32_t
   for (int32_t i = 0; i < (int32_t)rows.size(); ++i) {
     int32_t e = 0;
     while (e < rows[i].T) {
-      if (taken[i][e]) {
+      if (is_taken(i, e)) {
         ++e;
         continue;
       }
       int32_t len = 0;
-      while (len < max_chunk && e + len < rows[i].T && !taken[i][e + len]) ++len;
+      while (len < max_chunk && e + len < rows[i].T && !is_taken(i, e + len)) ++len;
       items.push_back(Item{len, {Member{i, e}}});
       e += len;
     }
