@@ -70,7 +70,7 @@ def kernel_source_hash(kernel):
     """Hash of the sources a kernel is built from (ties recorded counters to a kernel version)."""
     import hashlib
     csrc = os.path.join(ROOT, "position_agnostic_kv_paged_amd", "csrc")
-    files = {"prefill": ["prefill_body.h", "mixed.hip", "decode_body.h"],
+    files = {"prefill": ["prefill_body.h", "mixed.hip", "decode_body.h", "decode_plan.h"],
              "decode": ["decode.hip", "decode_body.h"]}[kernel]
     h = hashlib.sha256()
     for f in files + ["lazyattn_common.h", "lazyattn_kernels.h"]:
