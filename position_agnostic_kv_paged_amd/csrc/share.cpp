@@ -167,20 +167,50 @@ extern "C" int lazyattn_decode_share_plan(const int32_t* q_indptr, const int32_t
   // each onto the least loaded of the waves / Hw lanes of work, then emitted round by round
   // so that lane k's r-th item lands at position r * lanes + k; lanes with fewer items get
   // empty items (no members). Without a wave count the items keep their order.
+  // Items of equal length are dealt in order of their blocks' ids (first, then last id),
+  // so that the waves of the chip read neighbouring pool blocks at the same time (a sorted
+  // gather runs faster than a random one). Items that read the same run of blocks are also
+  // kept on one XCD: lane k's items run on workgroups of XCD class k mod 8 in both decode
+  // launches (the standalone kernel deals waves 4 per workgroup with Hw = 8 work heads, the
+  // mixed kernel one plan item per workgroup), so the first item of a run fixes a class and
+  // the run's later items take the least loaded lane of that class when that costs at most
+  // half the item's length in balance. Sorted next to each other they start at about the
+  // same time, and the later ones find the blocks in that XCD's L2.
   const int Hw = G <= 16 ? Hkv : Hq / 16;
   const int64_t lanes = waves > 0 ? std::max<int64_t>(1, waves / Hw) : 0;
   if (lanes > 0 && (int64_t)items.size() > 1) {
+    const size_t classes = (size_t)std::min<int64_t>(8, lanes);
+    auto key = [&](const Item& it) {           // (first id, last id) of the item's blocks
+      const Row& r = rows[(size_t)it.m[0].ri];
+      return std::make_pair(id_of(r, it.m[0].e), id_of(r, it.m[0].e + it.len - 1));
+    };
     std::vector<size_t> order(items.size());
-    for (size_t k = 0; k < order.size(); ++k) order[k] = k;
-    std::stable_sort(order.begin(), order.end(),
-                     [&](size_t a, size_t b) { return items[a].len > items[b].len; });
+    std::vector<std::pair<int32_t, int32_t>> keys(items.size());
+    for (size_t k = 0; k < order.size(); ++k) {
+      order[k] = k;
+      keys[k] = key(items[k]);
+    }
+    std::stable_sort(order.begin(), order.end(), [&](size_t a, size_t b) {
+      if (items[a].len != items[b].len) return items[a].len > items[b].len;
+      return keys[a] < keys[b];
+    });
     std::vector<int64_t> load((size_t)lanes, 0);
     std::vector<std::vector<size_t>> per((size_t)lanes);
-    // least-loaded lane, ties to the lowest index (a linear scan: lanes is a few hundred)
+    std::pair<int32_t, int32_t> last_key{-1, -1};
+    size_t last_class = 0;
     for (size_t k : order) {
+      // least loaded lane, ties to the lowest index (a linear scan: lanes is a few hundred)
       size_t best = 0;
       for (size_t x = 1; x < (size_t)lanes; ++x)
         if (load[x] < load[best]) best = x;
+      if (keys[k] == last_key) {               // the run's class, if balance allows
+        size_t cb = last_class;
+        for (size_t x = cb; x < (size_t)lanes; x += classes)
+          if (load[x] < load[cb]) cb = x;
+        if (2 * (load[cb] - load[best]) <= items[k].len) best = cb;
+      }
+      last_key = keys[k];
+      last_class = best % classes;
       load[best] += items[k].len;
       per[best].push_back(k);
     }
