@@ -473,7 +473,7 @@ def main():
         record_traffic(*args.record_traffic)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build runs the attention path on a "
+        print("bench.py measures one GPU only: the library runs the attention path on a "
               "single MI355X (no multi-GPU sharding); use --gpus 1", file=sys.stderr)
         sys.exit(2)
 

@@ -52,8 +52,8 @@ def lib():
     if _lib is not None:
         return _lib
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
-                          "(hipcc, gfx950)")
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "python position_agnostic_kv_paged_amd/build.py (hipcc, gfx950)")
     L = ctypes.CDLL(LIB_PATH)
     vp, i32, u64, dbl = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_double
     attn = [vp, vp, vp, vp, vp, vp, vp, vp, dbl, i32, i32, i32, i32, i32, i32, i32, i32,
