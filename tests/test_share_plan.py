@@ -118,3 +118,33 @@ def test_plan_errors():
     bad[0] = 1                                   # CSR must start at 0
     with pytest.raises(LazyAttnError):
         L.decode_share_plan(bad, wl.block_table, words, wl.Hq, wl.Hkv)
+
+
+def test_plan_keeps_runs_of_one_document_on_one_xcd_class():
+    """Items that read the same run of blocks go to lanes of one class (lane mod 8, the XCD
+    both decode launches run that lane's items on), and the plan still covers every entry."""
+    L = _lib()
+    doc = [Segment("doc", 0, doc=0), Segment("private", 4096, tokens=40)]
+    reqs = [RequestLayout(doc, 1) for _ in range(20)]
+    wl = build("same-doc", 16, 2, 64, 16, 10000.0, 1, 4096, reqs, seed=3)
+    _check(wl, False, 12, waves=2048)
+    words = words_for(wl)
+    # 12-block runs: a row pair's 22 items would put the next pair's copies 22 lanes on
+    plan = L.decode_share_plan(wl.q_indptr, wl.block_table, words, wl.Hq, wl.Hkv,
+                               max_chunk=12, waves=2048)
+    M, n_items, _, _, recs = _parse(plan, wl.total_q)
+    lanes = 2048 // wl.Hkv
+    ids = (np.asarray(words).view(np.uint32) & ((1 << 17) - 1)).astype(np.int64)
+    bt = np.asarray(wl.block_table)
+    by_run = {}
+    for pos, it in enumerate(recs):
+        ln, nm = int(it[0]), int(it[1])
+        if nm == 0:
+            continue
+        seq, eb = int(it[3]), int(it[4])
+        run = tuple(ids[bt[seq] + eb: bt[seq] + eb + ln])
+        by_run.setdefault(run, []).append((pos % lanes) % 8)
+    shared = {r: c for r, c in by_run.items() if len(c) > 1}
+    assert shared, "the 20 rows of one document give repeated runs"
+    for run, classes in shared.items():
+        assert len(set(classes)) == 1, f"run of {len(run)} blocks spread over classes {classes}"
