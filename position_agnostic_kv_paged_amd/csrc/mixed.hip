@@ -8,8 +8,9 @@
 // Work items:
 //  - prefill: (KV head, item) with item = a query tile of 256 (position, head) rows over one
 //    KV split of its key range (prefill_item; splits chosen by plan_kernel);
-//  - decode: a chunk of dec_chunk consecutive decode items ((row-split, KV head) pairs), one
-//    wave per item (decode_items); their split-K partials are merged by merge_kernel.
+//  - decode: a chunk of dec_chunk consecutive decode items, one wave per item: (row-split,
+//    KV head) pairs (decode_items), or, over a shared-document plan, (plan item, KV head)
+//    pairs (decode_plan_items); their partials are merged by merge_kernel.
 // Order: workgroup b runs on XCD b mod 8 and the workgroups of an XCD are dispatched in
 // index order as compute units free up, so queue q = b mod 8 is worked through in the order
 // c = b / 8. Queue q holds a contiguous eighth of the (KV head, prefill item) space first
