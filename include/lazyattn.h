@@ -156,7 +156,7 @@ int lazyattn_decode(const void* q, const void* k_pool, const void* v_pool,
  *                         loaded waves and pads with empty items (no members) to balance them.
  *                         Items of equal length go in order of their block ids, and items
  *                         reading the same run of blocks onto waves of one XCD, balance
- *                         permitting (the order changes speed, never results)
+ *                         permitting (the order changes speed and rounding order only)
  *  plan_out               int32 [plan_cap] or NULL (size query); *plan_len_out receives the
  *                         plan's length in int32 either way
  * The plan (int32): [0] magic, [1] version 1, [2] M, [3] 2 + 4 M, [4] items, [5] partial
