@@ -1,7 +1,9 @@
-"""The host pool index (csrc/pool.cpp) under the compiler's sanitizers, on the CPU: a
-randomised model check built with AddressSanitizer + UndefinedBehaviorSanitizer, and a
-threaded stress of one handle built with ThreadSanitizer (tests/pool_sanitize_driver.cpp).
-The index is plain C++ with no device code, so g++ builds it on its own."""
+"""Host C++ of the library under the compiler's sanitizers, on the CPU: the pool index
+(csrc/pool.cpp) in a randomised model check built with AddressSanitizer +
+UndefinedBehaviorSanitizer and a threaded stress of one handle built with ThreadSanitizer
+(tests/pool_sanitize_driver.cpp); the shared-document planner (csrc/share.cpp) on random
+batches under AddressSanitizer + UndefinedBehaviorSanitizer (tests/share_sanitize_driver.cpp).
+Both are plain C++ with no device code, so g++ builds them on their own."""
 import os
 import shutil
 import subprocess
@@ -16,10 +18,14 @@ SRC = [os.path.join(HERE, "pool_sanitize_driver.cpp"),
 pytestmark = pytest.mark.skipif(shutil.which("g++") is None, reason="g++ not available")
 
 
-def _build_and_run(tmp_path, flags, arg, env_extra):
+SHARE_SRC = [os.path.join(HERE, "share_sanitize_driver.cpp"),
+             os.path.join(ROOT, "position_agnostic_kv_paged_amd", "csrc", "share.cpp")]
+
+
+def _build_and_run(tmp_path, flags, arg, env_extra, src=SRC):
     exe = str(tmp_path / "driver")
     cmd = ["g++", "-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer", *flags,
-           "-I", os.path.join(ROOT, "include"), *SRC, "-o", exe, "-pthread"]
+           "-I", os.path.join(ROOT, "include"), *src, "-o", exe, "-pthread"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         pytest.skip(f"sanitizer build unavailable: {r.stderr[-400:]}")
@@ -38,3 +44,9 @@ def test_pool_index_model_check_asan_ubsan(tmp_path):
 def test_pool_index_threaded_stress_tsan(tmp_path):
     _build_and_run(tmp_path, ["-fsanitize=thread"], "threads",
                    {"TSAN_OPTIONS": "halt_on_error=1"})
+
+
+def test_share_planner_random_batches_asan_ubsan(tmp_path):
+    _build_and_run(tmp_path, ["-fsanitize=address,undefined", "-fno-sanitize-recover=all"],
+                   "400", {"ASAN_OPTIONS": "detect_leaks=1:abort_on_error=0",
+                           "UBSAN_OPTIONS": "print_stacktrace=1"}, src=SHARE_SRC)
