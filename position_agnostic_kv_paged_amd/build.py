@@ -10,7 +10,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "liblazyattn.so")
-SOURCES = ["api.hip", "plan.hip", "decode.hip", "mixed.hip", "materialize.hip", "probe.hip", "ingest.hip", "pool.cpp", "share.cpp"]
+SOURCES = ["api.hip", "plan.hip", "decode.hip", "mixed.hip", "materialize.hip", "probe.hip", "ingest.hip", "pool.cpp", "share.cpp", "host.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-Wall",
          "-Wno-unused-result", "-Wno-unused-variable",

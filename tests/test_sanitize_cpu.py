@@ -2,8 +2,10 @@
 (csrc/pool.cpp) in a randomised model check built with AddressSanitizer +
 UndefinedBehaviorSanitizer and a threaded stress of one handle built with ThreadSanitizer
 (tests/pool_sanitize_driver.cpp); the shared-document planner (csrc/share.cpp) on random
-batches under AddressSanitizer + UndefinedBehaviorSanitizer (tests/share_sanitize_driver.cpp).
-Both are plain C++ with no device code, so g++ builds them on their own."""
+batches (tests/share_sanitize_driver.cpp) and the ABI's host helpers (csrc/host.cpp: word
+encoder, Llama 3.1 table, status strings; tests/host_sanitize_driver.cpp) under
+AddressSanitizer + UndefinedBehaviorSanitizer. All are plain C++ with no device code, so g++
+builds them on their own."""
 import os
 import shutil
 import subprocess
@@ -18,6 +20,8 @@ SRC = [os.path.join(HERE, "pool_sanitize_driver.cpp"),
 pytestmark = pytest.mark.skipif(shutil.which("g++") is None, reason="g++ not available")
 
 
+HOST_SRC = [os.path.join(HERE, "host_sanitize_driver.cpp"),
+            os.path.join(ROOT, "position_agnostic_kv_paged_amd", "csrc", "host.cpp")]
 SHARE_SRC = [os.path.join(HERE, "share_sanitize_driver.cpp"),
              os.path.join(ROOT, "position_agnostic_kv_paged_amd", "csrc", "share.cpp")]
 
@@ -50,3 +54,9 @@ def test_share_planner_random_batches_asan_ubsan(tmp_path):
     _build_and_run(tmp_path, ["-fsanitize=address,undefined", "-fno-sanitize-recover=all"],
                    "400", {"ASAN_OPTIONS": "detect_leaks=1:abort_on_error=0",
                            "UBSAN_OPTIONS": "print_stacktrace=1"}, src=SHARE_SRC)
+
+
+def test_host_helpers_random_tables_asan_ubsan(tmp_path):
+    _build_and_run(tmp_path, ["-fsanitize=address,undefined", "-fno-sanitize-recover=all"],
+                   "400", {"ASAN_OPTIONS": "detect_leaks=1:abort_on_error=0",
+                           "UBSAN_OPTIONS": "print_stacktrace=1"}, src=HOST_SRC)
