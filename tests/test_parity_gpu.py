@@ -468,6 +468,10 @@ def test_run_to_run_bitwise_determinism():
     say("determinism: decode workload twice")
     a, b = run_hip(wd, "decode", repeat=2)
     assert np.array_equal(a, b)
+    wm = make("mixed-64q8kv-4p96d")                   # G = 8, prefill tiles and decode rows
+    say("determinism: mixed batch three times (one call)")
+    outs = run_hip(wm, "prefill", repeat=3)
+    assert all(np.array_equal(outs[0], x) for x in outs[1:])
 
 
 def test_shifted_document_is_detected():
