@@ -106,11 +106,13 @@ __device__ __forceinline__ void decode_plan_items(const DecodeParams& P,
     return x;
   };
   struct Grp {
-    int id[2], nl[2];                          // uniform: block id, rows to load
+    int id[2], nl[2], kvp;                     // uniform: block id, rows to load, pool head
     int off[2], nv[2];                         // per lane: member offset, valid keys
   };
-  // loads of blocks t0, t0 + 1 of item x: keys into kreg, values into LDS buffer `bb`
-  auto issue = [&](const Desc& x, int t0, int bb, u32x4 (&kreg)[2][NC], Grp& gm) {
+  // blocks t0, t0 + 1 of item x: their description into gm and their values into LDS buffer
+  // `bb` (the keys follow with issue_k, once the registers they go to are free)
+  auto issue = [&](const Desc& x, int t0, int bb, Grp& gm) {
+    gm.kvp = x.kvp;
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       const int t = t0 + b;
@@ -133,11 +135,6 @@ __device__ __forceinline__ void decode_plan_items(const DecodeParams& P,
       for (int o = 1; o < 16; o <<= 1) nl = max(nl, __shfl_xor(nl, o));
       gm.nl[b] = __builtin_amdgcn_readfirstlane(nl);
       gm.id[b] = id;
-      const size_t kb = ((size_t)id * P.Hkv_pool + x.kvp) * kBlock;
-#pragma unroll
-      for (int c = 0; c < NC; ++c)
-        kreg[b][c] = i16 < gm.nl[b] ? *(const u32x4*)(P.k_pool + (kb + i16) * D + dofs[c])
-                                    : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
@@ -151,10 +148,23 @@ __device__ __forceinline__ void decode_plan_items(const DecodeParams& P,
       g2lds16(src, lds + bb * BUF + i * 1024);
     }
   };
+  // the keys of a described group into registers
+  auto issue_k = [&](const Grp& gm, u32x4 (&kreg)[2][NC]) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const size_t kb = ((size_t)gm.id[b] * P.Hkv_pool + gm.kvp) * kBlock;
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        kreg[b][c] = i16 < gm.nl[b] ? *(const u32x4*)(P.k_pool + (kb + i16) * D + dofs[c])
+                                    : u32x4{0, 0, 0, 0};
+    }
+  };
 
   int buf = 0;                                 // LDS buffer of the group in flight
   bool pre = false;                            // the item's first group already in flight
-  u32x4 kcur[2][NC], knext[2][NC];
+  // one set of key registers: a group's keys are scored first, then the next group's keys
+  // are loaded into the same registers while the softmax and value products run
+  u32x4 kreg[2][NC];
   Grp gcur, gnext;
   Desc cur = describe(min(gw, max(n_items - 1, 0)));
   for (int it = gw; it < n_items; it += W) {
@@ -216,8 +226,8 @@ __device__ __forceinline__ void decode_plan_items(const DecodeParams& P,
         for (int i = 0; i < 4; ++i) {
           qlo[i] = pack_f16(qr[c][2 * i], qr[c][2 * i + 1]);
           qhi[i] = pack_f16(qr[c + HC][2 * i], qr[c + HC][2 * i + 1]);
-          const float a0 = bf_lo(kcur[b][c][i]), a1 = bf_hi(kcur[b][c][i]);
-          const float b0 = bf_lo(kcur[b][c + HC][i]), b1 = bf_hi(kcur[b][c + HC][i]);
+          const float a0 = bf_lo(kreg[b][c][i]), a1 = bf_hi(kreg[b][c][i]);
+          const float b0 = bf_lo(kreg[b][c + HC][i]), b1 = bf_hi(kreg[b][c + HC][i]);
           const u32x2 t = slot_tab[((c * 4 + q4) * 4 + i) * 16 + i16];
           const u32x2 r = rot_h2(pack_f16(a0, a1), pack_f16(b0, b1), t[0], t[1]);
           lo[i] = r[0];
@@ -229,22 +239,24 @@ __device__ __forceinline__ void decode_plan_items(const DecodeParams& P,
       return S;
     };
 
-    if (!pre && cur.len > 0) issue(cur, 0, buf, knext, gnext);
+    if (!pre && cur.len > 0) {
+      issue(cur, 0, buf, gnext);
+      issue_k(gnext, kreg);
+    }
     pre = false;
     for (int t0 = 0; t0 < cur.len; t0 += 2) {
       __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0): this group's keys and values
       asm volatile("" ::: "memory");
       wave_sync();
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int c = 0; c < NC; ++c) kcur[b][c] = knext[b][c];
       gcur = gnext;
+      bool more = false;                       // a next group (this item's or the next's)
       if (t0 + 2 < cur.len) {
-        issue(cur, t0 + 2, buf ^ 1, knext, gnext);
+        issue(cur, t0 + 2, buf ^ 1, gnext);
+        more = true;
       } else if (has_next && nxt.len > 0) {    // the next item's first group
-        issue(nxt, 0, buf ^ 1, knext, gnext);
+        issue(nxt, 0, buf ^ 1, gnext);
         pre = true;
+        more = true;
       }
       const bool has1 = t0 + 1 < cur.len;
       set_q(gcur.off[0]);
@@ -254,6 +266,7 @@ __device__ __forceinline__ void decode_plan_items(const DecodeParams& P,
         set_q(gcur.off[1]);
         S1 = scores(1);
       }
+      if (more) issue_k(gnext, kreg);          // this group's keys are read: refill
       float sc[8];
       float mx = -INFINITY;
 #pragma unroll
