@@ -464,11 +464,15 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& P, const Prefi
   __builtin_amdgcn_s_waitcnt(0x0F70);                        // vmcnt(0)
   __syncthreads();
   const int pmax_g = __builtin_amdgcn_readfirstlane(pmax_s);
-  // does tile d of a decoded window need the causal / ragged mask for this wave's rows?
+  // does tile 0 of a decoded window (lanes 0..3) need the causal / ragged mask for this
+  // wave's rows? It does not when its four blocks are full, none reaches past the wave's
+  // first row, and at least one starts at or before the last row of the wave and of the
+  // workgroup. Two ballots over the window's lanes decide that (no per-block scalar reads).
+  const int pm_vis = min(pmax_w, pmax_g);
   auto needs_mask = [&](const WinDec& wd) __attribute__((always_inline)) {
-    const TileWords tw = tile_words<0>(wd);
-    const bool visible = tw.kmin <= pmax_w && tw.kmin <= pmax_g;
-    return !(visible && tw.full && tw.kmax <= pmin_w);
+    const uint64_t bad = __ballot((wd.nv != kBlock) | (wd.off + (kBlock - 1) > pmin_w));
+    const uint64_t late = __ballot(wd.off > pm_vis);
+    return ((bad & 0xFull) != 0) | ((late & 0xFull) == 0xFull);
   };
   f32x16 S0[2], S1[2];
 
