@@ -73,10 +73,12 @@ __device__ __forceinline__ const void* blend_ptr(bool c, const void* a, const vo
   return (const void*)(((uint64_t)a & m) | ((uint64_t)b & ~m));
 }
 
-// Words of key tiles kt .. kt+3 live in one VGPR ("window"): lane i < 16 holds the word of
-// entry 4 kt + i. The loop issues one small vector load per key tile (the next window);
-// each lane decodes its own word (block id, logical offset, valid keys) on the VALU, and
-// the scalars a step needs are read out of lanes 4d .. 4d+3 (tile kt + d) with readlane.
+// Words of key tiles kw .. kw+7 live in one VGPR ("window"): lane i < 32 holds the word of
+// entry 4 kw + i. A step needs the words of its tile and the next three, so a window serves
+// four steps: the loop loads the next window once per four key tiles, each lane decodes its
+// own word (block id, logical offset, valid keys) on the VALU, and the scalars a step needs
+// are read out of lanes 4d .. 4d+3 (tile kw + d) with readlane.
+constexpr int kWinLanes = 32;
 __device__ __forceinline__ uint32_t load_window(const PrefillParams& P, int e0, int T, int kt,
                                                 int lane) {
   // every lane loads (no branch): lanes past the table read its last word, which the
@@ -104,7 +106,7 @@ __device__ __forceinline__ WinDec decode_window(const PrefillParams& P, uint32_t
   d.id = word_id(win);
   d.off = word_offset(win, ent);
   d.sh = d.off - st;
-  d.nv = ((lane < 16) & (ent < T) & (d.id < P.num_blocks))   // out-of-pool id: never read
+  d.nv = ((lane < kWinLanes) & (ent < T) & (d.id < P.num_blocks))   // out-of-pool id: not read
              ? min(max(kvlen - ent * kBlock, 0), kBlock) : 0;
   return d;
 }
@@ -250,7 +252,7 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& P, const Prefi
                                                        : 16 * c + 8 * hh))
                        : u32x4{0, 0, 0, 0};
   }
-  uint32_t win = load_window(P, e0, T, kt_b, lane);        // words of tiles kt_b .. kt_b+3
+  uint32_t win = load_window(P, e0, T, kt_b, lane);        // words of tiles kt_b .. kt_b+7
   const int st0 = DOC ? load_stored(P, e0, T, kt_b, lane) : 0;
 
   for (int i = tid; i < HALF; i += NT) fr_s[i] = P.freqs[i];
@@ -339,11 +341,11 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& P, const Prefi
   u32x4 qm = {e0lane ? slope_hi : 0u,                        // (-m/256, c_hi, c_lo, 0...) fp16
               e0lane && ALIBI ? f16_bits(cslope - c_hi) : 0u, 0u, 0u};
   const int p_bias = row_ok ? p : 0;                         // rows past the tile see no key
-  // ALiBi bias of score half t of the tile whose words are at window index 0 of wd
-  auto add_bias = [&](f32x16& s, const WinDec& wd, int t) __attribute__((always_inline)) {
+  // ALiBi bias of score half t of the tile whose words are at window index d of wd
+  auto add_bias = [&](f32x16& s, const WinDec& wd, int d, int t) __attribute__((always_inline)) {
     if (!ALIBI) return;
-    const float b0 = cslope * (float)(rl(wd.off, 2 * t) - p_bias);
-    const float b1 = cslope * (float)(rl(wd.off, 2 * t + 1) - p_bias);
+    const float b0 = cslope * (float)(rl(wd.off, 4 * d + 2 * t) - p_bias);
+    const float b1 = cslope * (float)(rl(wd.off, 4 * d + 2 * t + 1) - p_bias);
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] += (r < 8) ? b0 : b1;
   };
@@ -464,15 +466,20 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& P, const Prefi
   __builtin_amdgcn_s_waitcnt(0x0F70);                        // vmcnt(0)
   __syncthreads();
   const int pmax_g = __builtin_amdgcn_readfirstlane(pmax_s);
-  // does tile 0 of a decoded window (lanes 0..3) need the causal / ragged mask for this
-  // wave's rows? It does not when its four blocks are full, none reaches past the wave's
-  // first row, and at least one starts at or before the last row of the wave and of the
-  // workgroup. Two ballots over the window's lanes decide that (no per-block scalar reads).
+  // Does tile d of a decoded window (lanes 4d .. 4d+3) need the causal / ragged mask for
+  // this wave's rows? It does not when its four blocks are full, none reaches past the
+  // wave's first row, and at least one starts at or before the last row of the wave and of
+  // the workgroup. Two ballots per window give every tile's answer (no per-block scalar
+  // reads): `bad` marks blocks not full or reaching past the first row, `late` blocks that
+  // start after the last row.
   const int pm_vis = min(pmax_w, pmax_g);
-  auto needs_mask = [&](const WinDec& wd) __attribute__((always_inline)) {
-    const uint64_t bad = __ballot((wd.nv != kBlock) | (wd.off + (kBlock - 1) > pmin_w));
-    const uint64_t late = __ballot(wd.off > pm_vis);
-    return ((bad & 0xFull) != 0) | ((late & 0xFull) == 0xFull);
+  struct WinMask { uint64_t bad, late; };
+  auto window_mask = [&](const WinDec& wd) __attribute__((always_inline)) {
+    return WinMask{__ballot((wd.nv != kBlock) | (wd.off + (kBlock - 1) > pmin_w)),
+                   __ballot(wd.off > pm_vis)};
+  };
+  auto needs_mask = [&](const WinMask& wm, int d) __attribute__((always_inline)) {
+    return (((wm.bad >> (4 * d)) & 0xFull) != 0) | (((wm.late >> (4 * d)) & 0xFull) == 0xFull);
   };
   f32x16 S0[2], S1[2];
 
@@ -492,9 +499,12 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& P, const Prefi
   };
   if (kt_e > kt_b) qk(0, S0);
   WinDec wdc = decode_window(P, win, st0, T, kvlen, kt_b, lane);
-  add_bias(S0[0], wdc, 0);
-  add_bias(S0[1], wdc, 1);
-  bool maskc = needs_mask(wdc);
+  WinMask wmc = window_mask(wdc);
+  add_bias(S0[0], wdc, 0, 0);
+  add_bias(S0[1], wdc, 0, 1);
+  bool maskc = needs_mask(wmc, 0);
+  uint32_t win_nx = 0;                                       // the next window, in flight
+  int st_nx = 0;
   float mxc = xor32_max(max32(S0[0], S0[1]));
 
   const int gi = lane >> 4, i16 = lane & 15;
@@ -507,21 +517,23 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& P, const Prefi
   const uint16_t* klane = Ks[0] + col * KS + 8 * hh;        // + buf * NK * KS
   const uint16_t* qlane = qs + col * KS + 8 * hh;
 
-  // one pipeline iteration: S(kt) in Sc on entry, S(kt+1) left in Sn
-  auto step = [&](const int kt, f32x16 (&Sc)[2], f32x16 (&Sn)[2]) {
-    const int cur = (kt - kt_b) & 1, nxt = cur ^ 1;          // buffers of tiles kt, kt+1
-    // wdc (decoded words of tiles kt .. kt+3) and mxc (row max of S(kt) before masking)
-    // were computed under the MFMAs of the previous iteration
+  // one pipeline iteration: S(kt) in Sc on entry, S(kt+1) left in Sn. PH = (kt - kt_b) % 4 is
+  // the step's place in its window: wdc holds the decoded words of tiles kt - PH .. kt - PH + 7
+  // (tile kt + d at window index PH + d); the next window is loaded in step PH = 0 and decoded
+  // in step PH = 3. mxc (row max of S(kt) before masking) was computed under the MFMAs of
+  // the previous iteration.
+  auto step = [&](auto ph, const int kt, f32x16 (&Sc)[2], f32x16 (&Sn)[2]) {
+    constexpr int PH = decltype(ph)::value;
+    const int cur = PH & 1, nxt = cur ^ 1;                   // buffers of tiles kt, kt+1
     const WinDec wd = wdc;
-    uint32_t win_next = 0;
-    int st_next = 0;
-    WinDec wdn;
+    WinDec wdn = wdc;
+    WinMask wmn = wmc;
     bool maskn = false;
     float h0 = 0.f, h1 = 0.f;
     float mx = mxc;
     // ---- rare paths: causal / ragged mask of S(kt) ------------------------------------
     if (maskc) {
-      const TileWords tw = tile_words<0>(wd);
+      const TileWords tw = tile_words<PH>(wd);
       const bool visible = tw.kmin <= pmax_w && tw.kmin <= pmax_g;
       {
 #pragma unroll
@@ -590,7 +602,7 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& P, const Prefi
       u32x4 b = *(const u32x4*)qlane;
       Sn[0] = mfma32h(as_f16x8(ones_a), as_f16x8(qm), f32x16{});
       exp_slot(0);
-      load_k(wd, 2);                                        // raw keys of tile kt+2
+      load_k(wd, PH + 2);                                   // raw keys of tile kt+2
       Sn[1] = mfma32h(as_f16x8(ones_a), as_f16x8(qm), f32x16{});
       exp_slot(1);
       __builtin_amdgcn_sched_barrier(0);
@@ -607,12 +619,12 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& P, const Prefi
         // staging for later tiles, spread over the k-steps so that the vector memory
         // path works while the matrix cores do: values of tile kt+1 (k-steps 0..2), the
         // next word window (k-step 2), the phase table of tile kt+3 (k-step 3)
-        if (c < VPW) issue_v(wd, 1, nxt, c);
-        if (c == 2) {
-          win_next = load_window(P, e0, T, kt + 1, lane);
-          if (DOC) st_next = load_stored(P, e0, T, kt + 1, lane);
+        if (c < VPW) issue_v(wd, PH + 1, nxt, c);
+        if (PH == 0 && c == 2) {                            // the window of tiles kt+4 ..
+          win_nx = load_window(P, e0, T, kt + 4, lane);
+          if (DOC) st_nx = load_stored(P, e0, T, kt + 4, lane);
         }
-        if (c == 3) make_table(wd, 3, nxt);
+        if (c == 3) make_table(wd, PH + 3, nxt);
         Sn[1] = mfma32h(as_f16x8(a1), as_f16x8(b), Sn[1]);
         exp_slot(3 + 2 * c);
         __builtin_amdgcn_sched_barrier(0);
@@ -689,20 +701,24 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& P, const Prefi
           }
         }
         __builtin_amdgcn_sched_barrier(0);
-        // next iteration's inputs, under these MFMAs: decoded words of tiles kt+1 ..
-        // kt+4 (group 1) and the row max of S(kt+1) (groups 2, 3)
+        // next iteration's inputs, under these MFMAs: the mask decision of tile kt+1 and,
+        // in the window's last step, the next window decoded (group 1); the row max of
+        // S(kt+1) (groups 2, 3)
         if (g == 1) {
-          wdn = decode_window(P, win_next, st_next, T, kvlen, kt + 1, lane);
-          asm volatile("" ::"v"(wdn.id), "v"(wdn.off), "v"(wdn.nv));
-          maskn = needs_mask(wdn);
+          maskn = needs_mask(wmc, PH + 1);
+          if (PH == 3) {
+            wdn = decode_window(P, win_nx, st_nx, T, kvlen, kt + 1, lane);
+            asm volatile("" ::"v"(wdn.id), "v"(wdn.off), "v"(wdn.nv));
+            wmn = window_mask(wdn);
+          }
         }
         if (g == 2) {
-          add_bias(Sn[0], wdn, 0);
+          add_bias(Sn[0], wd, PH + 1, 0);
           h0 = max16(Sn[0]);
           asm volatile("" ::"v"(h0));
         }
         if (g == 3) {
-          add_bias(Sn[1], wdn, 1);
+          add_bias(Sn[1], wd, PH + 1, 1);
           h1 = max16(Sn[1]);
           asm volatile("" ::"v"(h1));
         }
@@ -732,14 +748,21 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& P, const Prefi
     }
     __builtin_amdgcn_s_setprio(0);
     wdc = wdn;
+    wmc = wmn;
     maskc = maskn;
     mxc = xor32_max(max3f(h0, h1, h1));
     __builtin_amdgcn_s_waitcnt(0x0F70);                      // vmcnt(0): values of tile kt+1
     __syncthreads();
   };
-  for (int kt = kt_b; kt < kt_e; kt += 2) {                  // unrolled x2: S0 <-> S1
-    step(kt, S0, S1);
-    if (kt + 1 < kt_e) step(kt + 1, S1, S0);
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  using P2 = std::integral_constant<int, 2>;
+  using P3 = std::integral_constant<int, 3>;
+  for (int kt = kt_b; kt < kt_e; kt += 4) {                  // one window; S0 <-> S1
+    step(P0{}, kt, S0, S1);
+    if (kt + 1 < kt_e) step(P1{}, kt + 1, S1, S0);
+    if (kt + 2 < kt_e) step(P2{}, kt + 2, S0, S1);
+    if (kt + 3 < kt_e) step(P3{}, kt + 3, S1, S0);
   }
 
   // ---- epilogue: O / l -> bf16 ----------------------------------------------------------
