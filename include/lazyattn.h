@@ -144,7 +144,9 @@ int lazyattn_decode(const void* q, const void* k_pool, const void* v_pool,
  * entries, at least 4 blocks) and groups up to M = 16 / G rows (G = Hq / Hkv; M = 1 for
  * G = 16 and above) into one work item that loads each block once; the remaining entries
  * of every row become single-row items of at most max_chunk blocks (grouped runs are also
- * cut at max_chunk). single_row_only = 1 plans only the rows of sequences with one query
+ * cut at max_chunk). Every item is also cut where a member's offset delta changes, so
+ * inside an item each member's logical offsets advance by one block per entry (the kernel
+ * relies on it). single_row_only = 1 plans only the rows of sequences with one query
  * row (the decode rows of a mixed batch), 0 plans every row.
  *  q_indptr, block_table  int32 [num_seqs + 1] (host), as for the attention calls
  *  block_meta             uint32 [block_table[num_seqs]] (host) packed words
@@ -159,7 +161,7 @@ int lazyattn_decode(const void* q, const void* k_pool, const void* v_pool,
  *                         permitting (the order changes speed and rounding order only)
  *  plan_out               int32 [plan_cap] or NULL (size query); *plan_len_out receives the
  *                         plan's length in int32 either way
- * The plan (int32): [0] magic, [1] version 1, [2] M, [3] 2 + 4 M, [4] items, [5] partial
+ * The plan (int32): [0] magic, [1] version 2, [2] M, [3] 2 + 4 M, [4] items, [5] partial
  * slots, [6] total_q, [7] num_seqs, then total_q + 1 slot offsets (row r owns slots
  * [p[r], p[r + 1])), then one record per item: length in blocks, member count, and per
  * member (query row, sequence, first entry, slot); member 0's entries supply the block ids.
@@ -170,8 +172,8 @@ int lazyattn_decode(const void* q, const void* k_pool, const void* v_pool,
  * lazyattn_decode_shared -- lazyattn_decode (RoPE) over such a plan, copied to device
  * memory (plan: int32, 4-byte aligned) together with its item and slot counts from the
  * header. The plan must have been built from the same block table, block_meta and q_indptr;
- * a plan whose header does not match the call (M, total_q, num_seqs) produces zero rows,
- * and indices inside it are clamped to the call's arrays. Workspace:
+ * a plan whose header does not match the call (magic, version, M, total_q, num_seqs)
+ * produces zero rows, and indices inside it are clamped to the call's arrays. Workspace:
  * lazyattn_decode_shared_workspace_bytes(num_seqs, total_q, plan_slots, Hq, Hkv, D).
  * Errors as lazyattn_decode, plus NULL plan and ARG for negative counts.
  *

@@ -64,7 +64,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 2) void decode_plan_kernel(Decod
   n_plan = min(n_plan, plan[4]);
   n_slots = min(n_slots, plan[5]);
   if (n_plan <= 0) return;
-  decode_tables_init<D, 16, kRope>(P, TB, kDecodeWaves * 64);   // R(16): per-block advance
+  decode_pair_tables_init<D>(P, TB, kDecodeWaves * 64);          // R(j), R(16 + j), R(32)
   __syncthreads();
   const int w = threadIdx.x >> 6;
   decode_plan_items<D, G>(P, TB, lds_all[w], plan, n_plan, n_slots,

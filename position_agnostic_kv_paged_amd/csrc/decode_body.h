@@ -81,10 +81,13 @@ struct GroupMeta {
 // frequencies k = 32c + 8 q4 + 2 e2 + u as packed fp16 pairs (cos u = 0, 1; sin u = 0, 1)
 // at [c][q4][e2][j] -- the 16 slots of a 16-lane read are consecutive 8-byte words; and
 // R(32) (or R(16) for G = 16) for the per-group advance of q', (cos, sin) interleaved.
+// Shared-document decode also uses R(16 + j) (slot_tab16): the second block of a group is
+// scored with the first block's q'.
 template <int D>
 struct DecodeTables {
   alignas(16) float adv[D];
   alignas(16) u32x2 slot_tab[(D / 64) * 4 * 4 * 16];
+  alignas(16) u32x2 slot_tab16[(D / 64) * 4 * 4 * 16];
 };
 
 // One wave's double-buffered value staging (2 groups x 32 rows x D bf16)
@@ -111,6 +114,22 @@ __device__ __forceinline__ void decode_tables_init(const DecodeParams& P, Decode
     rope_cos_sin(PHC ? 32 : 16, P.freqs[threadIdx.x], cs, sn);
     TB.adv[2 * threadIdx.x] = cs;
     TB.adv[2 * threadIdx.x + 1] = sn;
+  }
+}
+
+// The tables of shared-document decode: R(j) and R(16 + j) per slot, R(32) per group.
+template <int D>
+__device__ __forceinline__ void decode_pair_tables_init(const DecodeParams& P,
+                                                        DecodeTables<D>& TB, int nthreads) {
+  decode_tables_init<D, 8, kRope>(P, TB, nthreads);   // R(j), R(32)
+  constexpr int HC = D / 64;
+  for (int i = threadIdx.x; i < HC * 4 * 4 * 16; i += nthreads) {
+    const int j = i & 15, e2 = (i >> 4) & 3, qq = (i >> 6) & 3, c = i >> 8;
+    const int f0 = 32 * c + 8 * qq + 2 * e2;
+    float c0, s0, c1, s1;
+    rope_cos_sin(16 + j, P.freqs[f0], c0, s0);
+    rope_cos_sin(16 + j, P.freqs[f0 + 1], c1, s1);
+    TB.slot_tab16[i] = u32x2{pack_f16(c0, c1), pack_f16(s0, s1)};
   }
 }
 

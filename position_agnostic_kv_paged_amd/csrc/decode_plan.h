@@ -12,8 +12,13 @@
 // word for that block (the same block sits at different entries and offsets in different
 // rows). q'_m is set for each block in turn: advanced by R(-16) from the previous block when
 // the member's offset moves by 16, recomputed exactly from the double-precision phase
-// otherwise. Masks, the online softmax and the partial (o, m, l) are per column; each
-// member writes its partial into its own slot, and merge_kernel folds a row's slots.
+// otherwise. Within an item every member's offset delta is constant (the planner cuts runs
+// where it changes), so the second block of a group sits 16 positions after the first for
+// every member: <R(p - off - 16) q, R(j) k> = <R(p - off) q, R(16 + j) k>, and that block is
+// scored with the first block's q' against keys rotated by R(16 + j). q' is therefore set
+// once per group, advanced by R(-32) from the previous group. Masks, the online softmax
+// and the partial (o, m, l) are per column; each member writes its partial into its own
+// slot, and merge_kernel folds a row's slots.
 #pragma once
 #include "decode_body.h"
 
@@ -21,17 +26,19 @@ namespace lazyattn {
 
 constexpr int kSharePlanMagic = 0x5053414C;
 constexpr int kSharePlanHeader = 8;
+constexpr int kSharePlanVersion = 2;         // 2: constant offset delta within an item
 
 // does the plan's header match this call (members per item, rows, sequences)?
 __device__ __forceinline__ bool share_plan_ok(const int32_t* plan, int M, int total_q,
                                               int num_seqs) {
-  return plan[0] == kSharePlanMagic && plan[1] == 1 && plan[2] == M && plan[3] == 2 + 4 * M &&
+  return plan[0] == kSharePlanMagic && plan[1] == kSharePlanVersion && plan[2] == M &&
+         plan[3] == 2 + 4 * M &&
          plan[6] == total_q && plan[7] == num_seqs;
 }
 
 // Items gw, gw + W, ... below `end` of the n_plan x Hkv (plan item, KV head) pairs, by the
-// calling wave. TB must hold R(16) in adv (decode_tables_init with G = 16). Only the RoPE
-// mode.
+// calling wave. TB must hold R(32) in adv and R(16 + j) in slot_tab16
+// (decode_pair_tables_init). Only the RoPE mode.
 template <int D, int G>
 __device__ __forceinline__ void decode_plan_items(const DecodeParams& P,
                                                   const DecodeTables<D>& TB, uint8_t* lds,
@@ -47,6 +54,7 @@ __device__ __forceinline__ void decode_plan_items(const DecodeParams& P,
   constexpr int LOADS = BUF / 1024;
   const float* adv_all = TB.adv;
   const u32x2* slot_tab = TB.slot_tab;
+  const u32x2* slot_tab16 = TB.slot_tab16;
   const int lane = threadIdx.x & 63;
   const int i16 = lane & 15, q4 = lane >> 4;
   const int mi = i16 / G, g = i16 % G;         // this lane's column: member mi, head g
@@ -197,11 +205,11 @@ __device__ __forceinline__ void decode_plan_items(const DecodeParams& P,
       }
     };
     auto set_q = [&](int off) {                // qr := R(p - off) q, per lane
-      if (have_q && off == cur_off + kBlock) {
+      if (have_q && off == cur_off + 2 * kBlock) {
 #pragma unroll
         for (int c = 0; c < HC; ++c)
 #pragma unroll
-          for (int e2 = 0; e2 < 4; ++e2) {     // R(-16)
+          for (int e2 = 0; e2 < 4; ++e2) {     // R(-32)
             const f32x4 cs = *(const f32x4*)(adv_all + 2 * (32 * c + 8 * q4 + 2 * e2));
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
@@ -217,7 +225,7 @@ __device__ __forceinline__ void decode_plan_items(const DecodeParams& P,
       have_q = true;
       cur_off = off;
     };
-    auto scores = [&](int b) {
+    auto scores = [&](int b, const u32x2* tab) {   // tab: R(j) (b = 0) or R(16 + j) (b = 1)
       f32x4 S = {};
 #pragma unroll
       for (int c = 0; c < HC; ++c) {
@@ -228,7 +236,7 @@ __device__ __forceinline__ void decode_plan_items(const DecodeParams& P,
           qhi[i] = pack_f16(qr[c + HC][2 * i], qr[c + HC][2 * i + 1]);
           const float a0 = bf_lo(kreg[b][c][i]), a1 = bf_hi(kreg[b][c][i]);
           const float b0 = bf_lo(kreg[b][c + HC][i]), b1 = bf_hi(kreg[b][c + HC][i]);
-          const u32x2 t = slot_tab[((c * 4 + q4) * 4 + i) * 16 + i16];
+          const u32x2 t = tab[((c * 4 + q4) * 4 + i) * 16 + i16];
           const u32x2 r = rot_h2(pack_f16(a0, a1), pack_f16(b0, b1), t[0], t[1]);
           lo[i] = r[0];
           hi[i] = r[1];
@@ -259,13 +267,10 @@ __device__ __forceinline__ void decode_plan_items(const DecodeParams& P,
         more = true;
       }
       const bool has1 = t0 + 1 < cur.len;
-      set_q(gcur.off[0]);
-      const f32x4 S0 = scores(0);
+      set_q(gcur.off[0]);                      // one q' per group (see above)
+      const f32x4 S0 = scores(0, slot_tab);
       f32x4 S1 = {};
-      if (has1) {
-        set_q(gcur.off[1]);
-        S1 = scores(1);
-      }
+      if (has1) S1 = scores(1, slot_tab16);
       if (more) issue_k(gnext, kreg);          // this group's keys are read: refill
       float sc[8];
       float mx = -INFINITY;

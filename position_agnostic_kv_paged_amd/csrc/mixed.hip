@@ -72,7 +72,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void mixed_kernel(MixedParam
     const int first = (q + 8 * dc) * M.dec_chunk;
     if constexpr (PE == kRope) {
       if (shared) {                                               // (uniform)
-        decode_tables_init<D, 16, kRope>(Dp, TB, kPrefillWaves * 64);   // R(16) advance
+        decode_pair_tables_init<D>(Dp, TB, kPrefillWaves * 64);   // R(j), R(16 + j), R(32)
         __syncthreads();
         decode_plan_items<D, G>(Dp, TB, decode_wave_buf<D>(SM, w), M.plan, n_plan, n_slots,
                                 first + w, kPrefillWaves, min(first + M.dec_chunk, n_dec));

@@ -146,7 +146,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams P) {
         mine = (P.q_indptr[seq + 1] - r == 1) & (r < P.total_q);
       }
       const int32_t* hdr = P.slot_prefix - 8;
-      const bool ok = hdr[0] == 0x5053414C && hdr[1] == 1 && hdr[2] == P.plan_members &&
+      const bool ok = hdr[0] == 0x5053414C && hdr[1] == 2 && hdr[2] == P.plan_members &&
                       hdr[3] == 2 + 4 * P.plan_members && hdr[6] == P.total_q &&
                       hdr[7] == P.num_seqs;
       const int a = ok && mine ? max(P.slot_prefix[r], 0) : 0;

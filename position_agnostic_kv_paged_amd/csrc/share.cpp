@@ -17,8 +17,9 @@
 //   [8 .. 8 + total_q]          row_slot_prefix: row r owns slots [p[r], p[r + 1])
 //   then n_items records        {len, n_members, (row, seq, entry_begin, slot) x M}
 // Member 0 leads: the item reads blocks entry_begin0 .. entry_begin0 + len - 1 of its
-// sequence's table; every member's entries entry_begin_m .. + len - 1 hold the same ids.
-// Items are at most min(max_chunk, 128 / M) blocks long.
+// sequence's table; every member's entries entry_begin_m .. + len - 1 hold the same ids, and
+// every member's offset delta is the same over its len entries (its logical offsets advance
+// by one block per entry). Items are at most min(max_chunk, 128 / M) blocks long.
 #include "lazyattn.h"
 
 #include <algorithm>
@@ -28,7 +29,7 @@
 namespace {
 
 constexpr int32_t kPlanMagic = 0x5053414C;   // "LASP"
-constexpr int32_t kPlanVersion = 1;
+constexpr int32_t kPlanVersion = 2;          // 2: constant offset delta within an item
 constexpr int kMinRun = 4;                   // blocks a shared run must span to be grouped
 constexpr uint32_t kIdMask = (1u << LAZYATTN_ID_BITS) - 1u;
 
@@ -68,6 +69,9 @@ extern "C" int lazyattn_decode_share_plan(const int32_t* q_indptr, const int32_t
       rows.push_back(Row{q_indptr[s] + i, s, block_table[s], block_table[s + 1] - block_table[s]});
   }
   auto id_of = [&](const Row& r, int32_t e) { return (int32_t)(block_meta[r.e0 + e] & kIdMask); };
+  // the offset delta field of an entry's word: within an item it must not change for any
+  // member (the kernel scores a group's second block with the first block's rotated query)
+  auto delta_of = [&](const Row& r, int32_t e) { return block_meta[r.e0 + e] >> LAZYATTN_ID_BITS; };
 
   // block id -> (planned row, entry) users, as CSR over the id range, each id's users in
   // ascending (row, entry) order; taken[] flags entries already in an item (flat per row)
@@ -129,7 +133,8 @@ extern "C" int lazyattn_decode_share_plan(const int32_t* q_indptr, const int32_t
         const Row& b = rows[(size_t)j];
         int32_t len = 0;
         while (len < max_chunk && e + len < a.T && f + len < b.T && !is_taken(i, e + len) &&
-               !is_taken(j, f + len) && id_of(a, e + len) == id_of(b, f + len))
+               !is_taken(j, f + len) && id_of(a, e + len) == id_of(b, f + len) &&
+               delta_of(a, e + len) == delta_of(a, e) && delta_of(b, f + len) == delta_of(b, f))
           ++len;
         if (len >= kMinRun) cand.push_back({Member{j, f}, len});
       }
@@ -147,7 +152,8 @@ extern "C" int lazyattn_decode_share_plan(const int32_t* q_indptr, const int32_t
       e += len;
     }
   }
-  // single-row items: each row's untaken entries in runs of at most max_chunk
+  // single-row items: each row's untaken entries in runs of at most max_chunk, cut where
+  // the offset delta changes
   for (int32_t i = 0; i < (int32_t)rows.size(); ++i) {
     int32_t e = 0;
     while (e < rows[i].T) {
@@ -156,7 +162,9 @@ extern "C" int lazyattn_decode_share_plan(const int32_t* q_indptr, const int32_t
         continue;
       }
       int32_t len = 0;
-      while (len < max_chunk && e + len < rows[i].T && !is_taken(i, e + len)) ++len;
+      while (len < max_chunk && e + len < rows[i].T && !is_taken(i, e + len) &&
+             delta_of(rows[i], e + len) == delta_of(rows[i], e))
+        ++len;
       items.push_back(Item{len, {Member{i, e}}});
       e += len;
     }

@@ -6,8 +6,8 @@
 // block ids) at random entries, plus private blocks, plans it with random members per item
 // (through Hq / Hkv), max_chunk and wave counts, and checks what any plan must satisfy:
 // every planned (row, entry) is covered exactly once, members of an item read the same ids,
-// each row's slots are exactly [prefix[r], prefix[r + 1]), and the header describes the
-// plan. Error paths: a size query, a too-small buffer (NOSPACE with the length still
+// every member's offset delta is constant inside an item, each row's slots are exactly
+// [prefix[r], prefix[r + 1]), and the header describes the plan. Error paths: a size query, a too-small buffer (NOSPACE with the length still
 // reported), and rejected arguments.
 #include "lazyattn.h"
 
@@ -101,7 +101,7 @@ void one_case(int case_no) {
   if (rc != LAZYATTN_OK) return;
 
   const int M = G <= 16 ? 16 / G : 1, REC = 2 + 4 * M;
-  CHECK(plan[0] == 0x5053414C && plan[1] == 1 && plan[2] == M && plan[3] == REC,
+  CHECK(plan[0] == 0x5053414C && plan[1] == 2 && plan[2] == M && plan[3] == REC,
         "case %d: header", case_no);
   const int n_items = plan[4], n_slots = plan[5];
   CHECK(plan[6] == total_q && plan[7] == num_seqs, "case %d: header sizes", case_no);
@@ -138,6 +138,9 @@ void one_case(int case_no) {
         const uint32_t a = meta[(size_t)(block_table[s] + e + t)] & kIdMask;
         const uint32_t b = meta[(size_t)(block_table[s0] + e0 + t)] & kIdMask;
         CHECK(a == b, "case %d: member ids differ", case_no);
+        CHECK(meta[(size_t)(block_table[s] + e + t)] >> LAZYATTN_ID_BITS ==
+                  meta[(size_t)(block_table[s] + e)] >> LAZYATTN_ID_BITS,
+              "case %d: member offset delta changes inside an item", case_no);
       }
       slots[row].push_back(slot);
     }

@@ -1,6 +1,7 @@
 """Host planner of shared-document decode (lazyattn_decode_share_plan), on the CPU: the plan
 covers every (row, entry) of the planned rows exactly once, grouped members read the same
-block ids, slots are consecutive per row, and the header describes the plan."""
+block ids, every member's logical offsets advance by one block per entry inside an item,
+slots are consecutive per row, and the header describes the plan."""
 import numpy as np
 import pytest
 
@@ -29,7 +30,7 @@ def _check(wl, single_row_only, max_chunk, waves=2048):
     plan = L.decode_share_plan(wl.q_indptr, wl.block_table, words, wl.Hq, wl.Hkv,
                                single_row_only=single_row_only, max_chunk=max_chunk,
                                waves=waves)
-    assert plan[0] == 0x5053414C and plan[1] == 1
+    assert plan[0] == 0x5053414C and plan[1] == 2
     assert plan[6] == wl.total_q and plan[7] == wl.num_seqs
     M, n_items, n_slots, prefix, recs = _parse(plan, wl.total_q)
     assert M == (16 // G if G <= 16 else 1) and plan[3] == 2 + 4 * M
@@ -57,6 +58,8 @@ def _check(wl, single_row_only, max_chunk, waves=2048):
             assert len(ids) == ln
             lead = ids if lead is None else lead
             assert np.array_equal(ids, lead), "members read the same blocks"
+            offs = np.asarray(wl.seq_offsets[seq][eb: eb + ln], dtype=np.int64)
+            assert np.all(np.diff(offs) == wl.B), "offsets contiguous inside an item"
             covered[row][eb: eb + ln] += 1
             slots_seen[row].append(slot)
         assert len({int(x) for x in it[2: 2 + 4 * nm: 4]}) == nm, "distinct member rows"
