@@ -60,14 +60,15 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 2) void decode_plan_kernel(Decod
                                                                           int n_slots) {
   __shared__ __align__(16) uint8_t lds_all[kDecodeWaves][decode_wave_lds_bytes<D>()];
   __shared__ DecodeTables<D> TB;
+  __shared__ PairTable<D> PT;
   if (!share_plan_ok(plan, 16 / G, P.total_q, P.num_seqs)) return;
   n_plan = min(n_plan, plan[4]);
   n_slots = min(n_slots, plan[5]);
   if (n_plan <= 0) return;
-  decode_pair_tables_init<D>(P, TB, kDecodeWaves * 64);          // R(j), R(16 + j), R(32)
+  decode_pair_tables_init<D>(P, TB, PT, kDecodeWaves * 64);      // R(j), R(16 + j), R(32)
   __syncthreads();
   const int w = threadIdx.x >> 6;
-  decode_plan_items<D, G>(P, TB, lds_all[w], plan, n_plan, n_slots,
+  decode_plan_items<D, G>(P, TB, PT, lds_all[w], plan, n_plan, n_slots,
                           blockIdx.x * kDecodeWaves + w, gridDim.x * kDecodeWaves,
                           n_plan * P.Hkv);
 }

@@ -81,12 +81,15 @@ struct GroupMeta {
 // frequencies k = 32c + 8 q4 + 2 e2 + u as packed fp16 pairs (cos u = 0, 1; sin u = 0, 1)
 // at [c][q4][e2][j] -- the 16 slots of a 16-lane read are consecutive 8-byte words; and
 // R(32) (or R(16) for G = 16) for the per-group advance of q', (cos, sin) interleaved.
-// Shared-document decode also uses R(16 + j) (slot_tab16): the second block of a group is
-// scored with the first block's q'.
 template <int D>
 struct DecodeTables {
   alignas(16) float adv[D];
   alignas(16) u32x2 slot_tab[(D / 64) * 4 * 4 * 16];
+};
+// Shared-document decode also uses R(16 + j), laid out as slot_tab: the second block of a
+// group is scored with the first block's q'.
+template <int D>
+struct PairTable {
   alignas(16) u32x2 slot_tab16[(D / 64) * 4 * 4 * 16];
 };
 
@@ -120,7 +123,8 @@ __device__ __forceinline__ void decode_tables_init(const DecodeParams& P, Decode
 // The tables of shared-document decode: R(j) and R(16 + j) per slot, R(32) per group.
 template <int D>
 __device__ __forceinline__ void decode_pair_tables_init(const DecodeParams& P,
-                                                        DecodeTables<D>& TB, int nthreads) {
+                                                        DecodeTables<D>& TB, PairTable<D>& PT,
+                                                        int nthreads) {
   decode_tables_init<D, 8, kRope>(P, TB, nthreads);   // R(j), R(32)
   constexpr int HC = D / 64;
   for (int i = threadIdx.x; i < HC * 4 * 4 * 16; i += nthreads) {
@@ -129,7 +133,7 @@ __device__ __forceinline__ void decode_pair_tables_init(const DecodeParams& P,
     float c0, s0, c1, s1;
     rope_cos_sin(16 + j, P.freqs[f0], c0, s0);
     rope_cos_sin(16 + j, P.freqs[f0 + 1], c1, s1);
-    TB.slot_tab16[i] = u32x2{pack_f16(c0, c1), pack_f16(s0, s1)};
+    PT.slot_tab16[i] = u32x2{pack_f16(c0, c1), pack_f16(s0, s1)};
   }
 }
 

@@ -37,11 +37,12 @@ __device__ __forceinline__ bool share_plan_ok(const int32_t* plan, int M, int to
 }
 
 // Items gw, gw + W, ... below `end` of the n_plan x Hkv (plan item, KV head) pairs, by the
-// calling wave. TB must hold R(32) in adv and R(16 + j) in slot_tab16
-// (decode_pair_tables_init). Only the RoPE mode.
+// calling wave. TB must hold R(j) and R(32), PT R(16 + j) (decode_pair_tables_init). Only
+// the RoPE mode.
 template <int D, int G>
 __device__ __forceinline__ void decode_plan_items(const DecodeParams& P,
-                                                  const DecodeTables<D>& TB, uint8_t* lds,
+                                                  const DecodeTables<D>& TB,
+                                                  const PairTable<D>& PT, uint8_t* lds,
                                                   const int32_t* plan, const int n_plan,
                                                   const int n_slots, const int gw, const int W,
                                                   const int end) {
@@ -54,7 +55,7 @@ __device__ __forceinline__ void decode_plan_items(const DecodeParams& P,
   constexpr int LOADS = BUF / 1024;
   const float* adv_all = TB.adv;
   const u32x2* slot_tab = TB.slot_tab;
-  const u32x2* slot_tab16 = TB.slot_tab16;
+  const u32x2* slot_tab16 = PT.slot_tab16;
   const int lane = threadIdx.x & 63;
   const int i16 = lane & 15, q4 = lane >> 4;
   const int mi = i16 / G, g = i16 % G;         // this lane's column: member mi, head g
@@ -185,8 +186,6 @@ __device__ __forceinline__ void decode_plan_items(const DecodeParams& P,
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4{};
     float qr[NC][8];
-    bool have_q = false;
-    int cur_off = 0;                           // the offset qr is anchored at (per lane)
 
     auto qexact = [&](int n) {                 // qr := R(n) q_row
 #pragma unroll
@@ -204,8 +203,12 @@ __device__ __forceinline__ void decode_plan_items(const DecodeParams& P,
         }
       }
     };
-    auto set_q = [&](int off) {                // qr := R(p - off) q, per lane
-      if (have_q && off == cur_off + 2 * kBlock) {
+    // qr := R(p - off) q for the group at entry t0, per lane: exact at the item's first group;
+    // otherwise every member's offset has moved on by two blocks since the previous group
+    // (constant delta inside an item), so qr advances by R(-32). t0 is wave-uniform, so the
+    // choice is a uniform branch and qr is updated in place.
+    auto set_q = [&](int t0, int off) {
+      if (t0 != 0) {
 #pragma unroll
         for (int c = 0; c < HC; ++c)
 #pragma unroll
@@ -219,11 +222,9 @@ __device__ __forceinline__ void decode_plan_items(const DecodeParams& P,
               qr[c + HC][e] = b * cs[2 * u] - a * cs[2 * u + 1];
             }
           }
-      } else if (!have_q || off != cur_off) {
+      } else {
         qexact(cur.p - off);
       }
-      have_q = true;
-      cur_off = off;
     };
     auto scores = [&](int b, const u32x2* tab) {   // tab: R(j) (b = 0) or R(16 + j) (b = 1)
       f32x4 S = {};
@@ -267,7 +268,7 @@ __device__ __forceinline__ void decode_plan_items(const DecodeParams& P,
         more = true;
       }
       const bool has1 = t0 + 1 < cur.len;
-      set_q(gcur.off[0]);                      // one q' per group (see above)
+      set_q(t0, gcur.off[0]);                  // one q' per group (see above)
       const f32x4 S0 = scores(0, slot_tab);
       f32x4 S1 = {};
       if (has1) S1 = scores(1, slot_tab16);

@@ -44,6 +44,7 @@ template <int D, int G, int PE>
 __global__ __launch_bounds__(kPrefillWaves * 64, 1) void mixed_kernel(MixedParams M) {
   LAZYATTN_PREFILL_SMEM(D, SM);
   __shared__ DecodeTables<D> TB;
+  __shared__ PairTable<D> PT;                                      // shared-document decode
   const PrefillParams& P = M.pf;
   // the decode view of the same call (kernel arguments are passed once)
   const DecodeParams Dp{P.q, P.k_pool, P.v_pool, P.block_table, P.block_meta, P.kv_lens,
@@ -72,9 +73,9 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void mixed_kernel(MixedParam
     const int first = (q + 8 * dc) * M.dec_chunk;
     if constexpr (PE == kRope) {
       if (shared) {                                               // (uniform)
-        decode_pair_tables_init<D>(Dp, TB, kPrefillWaves * 64);   // R(j), R(16 + j), R(32)
+        decode_pair_tables_init<D>(Dp, TB, PT, kPrefillWaves * 64);   // R(j), R(16+j), R(32)
         __syncthreads();
-        decode_plan_items<D, G>(Dp, TB, decode_wave_buf<D>(SM, w), M.plan, n_plan, n_slots,
+        decode_plan_items<D, G>(Dp, TB, PT, decode_wave_buf<D>(SM, w), M.plan, n_plan, n_slots,
                                 first + w, kPrefillWaves, min(first + M.dec_chunk, n_dec));
         return;
       }
