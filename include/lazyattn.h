@@ -161,8 +161,9 @@ int lazyattn_decode(const void* q, const void* k_pool, const void* v_pool,
  *                         permitting (the order changes speed and rounding order only)
  *  plan_out               int32 [plan_cap] or NULL (size query); *plan_len_out receives the
  *                         plan's length in int32 either way
- * The plan (int32): [0] magic, [1] version 2, [2] M, [3] 2 + 4 M, [4] items, [5] partial
- * slots, [6] total_q, [7] num_seqs, then total_q + 1 slot offsets (row r owns slots
+ * The plan (int32): [0] magic LAZYATTN_SHARE_PLAN_MAGIC, [1] version
+ * LAZYATTN_SHARE_PLAN_VERSION, [2] M, [3] 2 + 4 M, [4] items, [5] partial slots, [6]
+ * total_q, [7] num_seqs, then total_q + 1 slot offsets (row r owns slots
  * [p[r], p[r + 1])), then one record per item: length in blocks, member count, and per
  * member (query row, sequence, first entry, slot); member 0's entries supply the block ids.
  * Errors: NULL, SHAPE (tables not non-decreasing from 0, q_indptr[num_seqs] != total_q,
@@ -183,6 +184,8 @@ int lazyattn_decode(const void* q, const void* k_pool, const void* v_pool,
  * lazyattn_prefill_shared_workspace_bytes(num_seqs, total_q, max_entries, plan_slots, Hq,
  * Hkv, D).
  */
+#define LAZYATTN_SHARE_PLAN_MAGIC   0x5053414C  /* "LASP" */
+#define LAZYATTN_SHARE_PLAN_VERSION 2           /* 2: one offset delta per member and item */
 int lazyattn_decode_share_plan(const int32_t* q_indptr, const int32_t* block_table,
                                const uint32_t* block_meta, int32_t num_seqs, int32_t total_q,
                                int32_t Hq, int32_t Hkv, int32_t single_row_only,

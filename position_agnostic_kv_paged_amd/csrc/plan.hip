@@ -5,9 +5,16 @@
 // prefix sums that the attention kernels binary-search to find their sequence.
 #include "lazyattn_common.h"
 #include "lazyattn_kernels.h"
+#include "decode_plan.h"
+#include "lazyattn.h"
 #include <limits.h>
 
 namespace lazyattn {
+
+// the device-side plan check and the host planner agree on the header
+static_assert(kSharePlanMagic == LAZYATTN_SHARE_PLAN_MAGIC, "plan magic");
+static_assert(kSharePlanVersion == LAZYATTN_SHARE_PLAN_VERSION, "plan version");
+static_assert(kSharePlanHeader == 8, "plan header length");
 
 // One workgroup of 256 threads; exclusive scan over sequences in chunks of 256: each wave
 // scans its 64 counts with shuffles, the four wave totals go through LDS (two barriers per
@@ -145,8 +152,9 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams P) {
         r = P.q_indptr[seq];
         mine = (P.q_indptr[seq + 1] - r == 1) & (r < P.total_q);
       }
-      const int32_t* hdr = P.slot_prefix - 8;
-      const bool ok = hdr[0] == 0x5053414C && hdr[1] == 2 && hdr[2] == P.plan_members &&
+      const int32_t* hdr = P.slot_prefix - kSharePlanHeader;
+      const bool ok = hdr[0] == kSharePlanMagic && hdr[1] == kSharePlanVersion &&
+                      hdr[2] == P.plan_members &&
                       hdr[3] == 2 + 4 * P.plan_members && hdr[6] == P.total_q &&
                       hdr[7] == P.num_seqs;
       const int a = ok && mine ? max(P.slot_prefix[r], 0) : 0;

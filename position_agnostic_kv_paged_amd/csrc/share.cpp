@@ -28,8 +28,6 @@
 
 namespace {
 
-constexpr int32_t kPlanMagic = 0x5053414C;   // "LASP"
-constexpr int32_t kPlanVersion = 2;          // 2: constant offset delta within an item
 constexpr int kMinRun = 4;                   // blocks a shared run must span to be grouped
 constexpr uint32_t kIdMask = (1u << LAZYATTN_ID_BITS) - 1u;
 
@@ -248,8 +246,8 @@ extern "C" int lazyattn_decode_share_plan(const int32_t* q_indptr, const int32_t
   if (plan_cap < len_total) return LAZYATTN_ERR_NOSPACE;
 
   int32_t* p = plan_out;
-  p[0] = kPlanMagic;
-  p[1] = kPlanVersion;
+  p[0] = LAZYATTN_SHARE_PLAN_MAGIC;
+  p[1] = LAZYATTN_SHARE_PLAN_VERSION;
   p[2] = M;
   p[3] = REC;
   p[4] = (int32_t)items.size();

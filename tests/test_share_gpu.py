@@ -106,14 +106,18 @@ def test_shared_run_to_run_bitwise():
     assert np.array_equal(a, b)
 
 
-@pytest.mark.parametrize("edit", ["magic", "members"])
+@pytest.mark.parametrize("edit", ["magic", "version", "members"])
 def test_shared_mismatched_plan_gives_zero_rows(edit):
-    """A plan whose header does not match the call is not followed: every row is zero."""
+    """A plan whose header does not match the call is not followed: every row is zero. A plan
+    of the earlier layout (version 1, items not cut where a member's offset delta changes)
+    is refused the same way."""
     wl = small(Hq=8, Hkv=2, D=128, seed=9)
 
     def spoil(p):
         if edit == "magic":
             p[0] ^= 1
+        elif edit == "version":
+            p[1] = 1
         else:
             p[2] += 1
         return p
@@ -155,3 +159,26 @@ def test_shared_prefill_call_small_mixed_and_empty():
     got, grouped = run_shared(wl, max_chunk=4, kind="prefill")
     assert grouped > 0
     compare(got, oracle_out(wl), "small-mixed/prefill-shared")
+
+
+def test_shared_prefill_call_mismatched_plan():
+    """lazyattn_prefill_shared with a plan of another version: the decode rows (single-row
+    sequences) are zero, the prefill rows are still computed as by lazyattn_prefill."""
+    d = [Segment("doc", 11, doc=0), Segment("doc", 60, doc=1), Segment("private", 120, tokens=9)]
+    reqs = [RequestLayout(d, 9), RequestLayout(d, 1),
+            RequestLayout([Segment("doc", 300, doc=1), Segment("private", 364, tokens=20)], 20),
+            RequestLayout([Segment("doc", 300, doc=1), Segment("doc", 364, doc=0),
+                           Segment("private", 430, tokens=2)], 1)]
+    wl = build("small-mixed-spoiled", 16, 2, 128, 16, 10000.0, 2, 64, reqs, seed=17)
+
+    def spoil(p):
+        p[1] = 1
+        return p
+    got, _ = run_shared(wl, max_chunk=4, kind="prefill", plan_edit=spoil)
+    qlen = np.diff(wl.q_indptr)
+    dec = [int(wl.q_indptr[s]) for s in range(wl.num_seqs) if qlen[s] == 1]
+    pre = [r for s in range(wl.num_seqs) if qlen[s] > 1
+           for r in range(int(wl.q_indptr[s]), int(wl.q_indptr[s + 1]))]
+    assert len(dec) == 2 and len(pre) == 29
+    assert np.all(got[dec] == 0.0)
+    compare(got[pre], oracle_out(wl)[pre], "small-mixed/prefill-shared, spoiled plan")
