@@ -17,8 +17,10 @@
 // boundary) and at the start of each work item q' is recomputed exactly from the
 // double-precision phase.
 //
-// Work: (row-split, kv-head) items are dealt round-robin to the waves of a grid that is
-// exactly resident (item i goes to wave i mod W). Each wave first describes all of its items
+// Work: (row-split, kv-head) items, numbered head-major, are cut into 8 contiguous ranges,
+// one per XCD (workgroup b runs on XCD b mod 8), and dealt round-robin to the waves of that
+// XCD's workgroups; the grid is exactly resident. With 8 KV heads each XCD reads one head,
+// so rows that share a document share that head's blocks in one L2. Each wave first describes all of its items
 // at once, one item per lane (sequence, query row and position, entry range), so starting
 // an item costs no dependent memory round trips; the first key/value group of the next
 // item is fetched while the last group of the current one is multiplied. Keys are
@@ -46,8 +48,13 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 2) void decode_kernel(DecodePara
   decode_tables_init<D, G, PE>(P, TB, kDecodeWaves * 64);
   __syncthreads();
   const int w = threadIdx.x >> 6;
-  decode_items<D, G, PE>(P, TB, lds_all[w], blockIdx.x * kDecodeWaves + w,
-                         gridDim.x * kDecodeWaves, n_items);
+  // XCD x (of X = 8, or fewer for a grid below 8) takes items [n x / X, n (x + 1) / X)
+  const int X = min(8, (int)gridDim.x), x = blockIdx.x % X, bx = blockIdx.x / X;
+  const int nbx = ((int)gridDim.x - x + X - 1) / X;              // workgroups on XCD x
+  const int lo = (int)((long long)n_items * x / X);
+  const int hi = (int)((long long)n_items * (x + 1) / X);
+  decode_items<D, G, PE>(P, TB, lds_all[w], lo + bx * kDecodeWaves + w, nbx * kDecodeWaves,
+                         hi);
 }
 
 // Shared-document decode: items from a host plan (decode_plan.h), dealt round-robin to the

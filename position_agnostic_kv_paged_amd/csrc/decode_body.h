@@ -138,8 +138,10 @@ __device__ __forceinline__ void decode_pair_tables_init(const DecodeParams& P,
 }
 
 // Decode items gw, gw + W, gw + 2W, ... below n_items, by the calling wave. An item is a
-// (row-split, KV head) pair: item = row_split * Hkv + kvh. `lds` is this wave's value
-// staging (decode_wave_lds_bytes).
+// (row-split, KV head) pair, numbered head-major: item = kvh * R + row_split over the R
+// row-splits of the batch, so that a contiguous range of items given to the workgroups of
+// one XCD holds one KV head's reads of every row (rows sharing a document then find its
+// blocks in that XCD's L2). `lds` is this wave's value staging (decode_wave_lds_bytes).
 template <int D, int G, int PE>
 __device__ __forceinline__ void decode_items(const DecodeParams& P, const DecodeTables<D>& TB,
                                              uint8_t* lds, const int gw, const int W,
@@ -172,6 +174,7 @@ __device__ __forceinline__ void decode_items(const DecodeParams& P, const Decode
   for (int c = 0; c < NC; ++c)
     dofs[c] = PART ? 8 * nat_chunk(4 * c + q4, P.rot_chunks, D / 16) : 32 * c + 8 * q4;
 
+  const int nrs = min(P.dec_prefix[P.num_seqs], P.rowsplit_cap);   // row-splits R
   // items gw + i W, i = 0, 1, ...; described 64 at a time, item gw + (64 rd + k) W by lane k
   for (int base = gw; base < n_items; base += 64 * W) {
     int x_rs = 0, x_kvh = 0, x_kvp = 0, x_r = 0, x_p = 0, x_e0 = 0, x_kvlen = 0, x_eb = 0,
@@ -179,8 +182,8 @@ __device__ __forceinline__ void decode_items(const DecodeParams& P, const Decode
     {
       const int itl = base + lane * W;
       if (itl < n_items) {
-        x_rs = itl / P.Hkv;
-        x_kvh = itl - x_rs * P.Hkv;
+        x_kvh = itl / nrs;
+        x_rs = itl - x_kvh * nrs;
         x_kvp = x_kvh / P.kv_group;                   // pool head of this work head
         const int seq = upper_seq(P.dec_prefix, P.num_seqs, x_rs);
         const int local = x_rs - P.dec_prefix[seq];

@@ -65,12 +65,18 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void mixed_kernel(MixedParam
   const long long np_all = (long long)n_pf * P.Hkv;
   const int p_lo = (int)(np_all * q / 8), p_hi = (int)(np_all * (q + 1) / 8);
   const int n_p = p_hi - p_lo;                                    // this queue's prefill items
-  const int n_d = q < n_dchunks ? (n_dchunks - q + 7) / 8 : 0;    // and decode chunks
+  // and decode chunks. Row-splits: a contiguous range per queue (items are numbered
+  // head-major, so with 8 KV heads queue q reads head q, as its prefill items do). Plan
+  // items: chunk q + 8 dc (the planner puts items that read the same blocks in one class
+  // mod 8).
+  const int d_lo = shared ? 0 : (int)((long long)n_dchunks * q / 8);
+  const int n_d = shared ? (q < n_dchunks ? (n_dchunks - q + 7) / 8 : 0)
+                         : (int)((long long)n_dchunks * (q + 1) / 8) - d_lo;
   if (c >= n_p + n_d) return;                                     // uniform
-  if (c >= n_p) {                                                 // decode chunk q + 8 dc
+  if (c >= n_p) {                                                 // decode chunk
     const int dc = c - n_p;
     const int w = threadIdx.x >> 6;
-    const int first = (q + 8 * dc) * M.dec_chunk;
+    const int first = (shared ? q + 8 * dc : d_lo + dc) * M.dec_chunk;
     if constexpr (PE == kRope) {
       if (shared) {                                               // (uniform)
         decode_pair_tables_init<D>(Dp, TB, PT, kPrefillWaves * 64);   // R(j), R(16+j), R(32)
