@@ -17,8 +17,9 @@
 // boundary) and at the start of each work item q' is recomputed exactly from the
 // double-precision phase.
 //
-// Work: (row-split, kv-head) items are dealt round-robin to the waves of a grid that is
-// exactly resident (item i goes to wave i mod W). Each wave first describes all of its items
+// Work: (row-split, kv-head) items, numbered head-major, go in one contiguous range per XCD
+// and round-robin to that XCD's waves (decode_kernel; the mixed kernel deals its decode
+// chunks the same way); the grid is exactly resident. Each wave first describes all of its items
 // at once, one item per lane (sequence, query row and position, entry range), so starting
 // an item costs no dependent memory round trips; the first key/value group of the next
 // item is fetched while the last group of the current one is multiplied. Keys are

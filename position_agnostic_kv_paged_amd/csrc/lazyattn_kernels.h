@@ -150,7 +150,8 @@ hipError_t launch_probe_read(const void* buf, size_t bytes, int num_wg, uint32_t
 hipError_t launch_probe_gather(const void* buf, size_t bytes, const int32_t* idx, int n_idx,
                                int chunk_bytes, int num_wg, uint32_t* out, hipStream_t st);
 
-// waves of the decode grid (all resident at once); decode items are dealt round-robin to them
+// waves of the decode grid (all resident at once); decode items are dealt round-robin to them,
+// one contiguous range of items per XCD
 int decode_resident_waves();
 hipError_t launch_decode(const DecodeParams& p, int D, int G, int pe, hipStream_t st);
 // shared-document decode over a host plan (RoPE mode only)
