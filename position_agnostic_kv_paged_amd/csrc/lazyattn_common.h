@@ -251,9 +251,9 @@ __host__ __device__ inline PfSplit pf_split(int n_kt, int kc, int smax) {
 // Decode split size (blocks per item, even, at least 8) for `pairs` (row, KV head) pairs of
 // rows holding about T blocks on W resident waves: items are dealt round-robin to the waves
 // (within each XCD's eighth of them), so the choice aims at an item count that is a whole
-// multiple of W -- every wave gets the
-// same number of equal items. Among 1 .. 8 items per wave the candidate with the least idle
-// share wins; ties go to fewer, longer items (fewer partials to merge).
+// multiple of W -- every wave gets the same number of equal items. Among 1 .. 8 items per
+// wave the candidate with the least idle share wins; ties go to fewer, longer items (fewer
+// partials to merge).
 __host__ __device__ inline int decode_bps(long long pairs, long long T, long long W) {
   if (T < 1) T = 1;
   if (pairs < 1) pairs = 1;
