@@ -324,6 +324,23 @@ def test_mixed_batch_small():
     compare(run_hip(wl, "decode"), oracle_out(wl), "mixed-small/decode")
 
 
+@pytest.mark.parametrize("Hkv,G", [(3, 4), (6, 2)])
+def test_kv_heads_straddling_xcd_ranges(Hkv, G):
+    """Decode items are numbered head-major and cut into eight contiguous ranges, one per XCD
+    (the mixed kernel cuts its decode chunks the same way). With 3 or 6 KV heads the ranges
+    start inside heads. Every row against the oracle: a decode batch, and the same rows with
+    prefill requests between them in one mixed call."""
+    dec = [RequestLayout([Segment("doc", 5 + i, doc=i % 4), Segment("doc", 100 + 2 * i, doc=(i + 1) % 4),
+                          Segment("private", 240 + 3 * i, tokens=3 + i % 5)], 1) for i in range(40)]
+    pre = RequestLayout([Segment("doc", 17, doc=2), Segment("private", 90, tokens=20)], 20)
+    for name, reqs, kind in (("decode", dec, "decode"),
+                             ("mixed", [pre] + dec[:20] + [pre] + dec[20:], "prefill")):
+        wl = build(f"straddle-{Hkv}kv-{name}", Hkv * G, Hkv, 128, 16, 10000.0, 4, 48, reqs,
+                   seed=31 + Hkv)
+        say(f"KV heads {Hkv}, {name} batch via {kind}")
+        compare(run_hip(wl, kind), oracle_out(wl), f"straddle-{Hkv}kv/{name}")
+
+
 def _distinct_cases():
     """Layouts in which every pool block is referenced once (a rotated pool can hold it)."""
     segs = [Segment("doc", 7 + 32 * i + 3 * (i % 2), doc=i) for i in range(9)] + \
